@@ -1,0 +1,128 @@
+"""CPU fp64 oracle for gated linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library
+(``chunkwise_linear_rnn_amd``) never imports it and it never imports the
+product; the two share no code.
+
+The arithmetic lives in ``gla_oracle.c`` (plain C, fp64, the token-by-token
+recurrence of "Gated Linear Attention Transformers with Hardware-Efficient
+Training", Section 4.1, Eq. 3, and its reverse-mode gradient).  This module
+only builds that file with gcc and marshals numpy arrays to it.
+
+Parity status of each function is recorded in its docstring; both are pinned by
+the ``-m "not gpu"`` tests (``tests/test_oracle_*.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``gla_oracle.c`` into ``liboracle.so`` with gcc (fp64, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+           "-std=c99", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.oracle_gla_fwd.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp]
+    lib.oracle_gla_fwd.restype = ctypes.c_int
+    lib.oracle_gla_bwd.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.oracle_gla_bwd.restype = ctypes.c_int
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _as_f64(x) -> np.ndarray:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor -> exact upcast on the CPU
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    """Threads the OpenMP runtime of the oracle will use (OMP_NUM_THREADS)."""
+    return int(_load().oracle_num_threads())
+
+
+def gla_fwd(q, k, v, g, s0=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward recurrence in fp64: returns (o [B,T,H,V], s_final [B,H,K,V]).
+
+    Follows "Gated Linear Attention Transformers with Hardware-Efficient
+    Training", Section 4.1, Eq. 3 (S_t = Diag(exp g_t) S_{t-1} + k_t^T v_t,
+    o_t = q_t S_t), with S_0 = s0 or zero (Section 2.2).
+    Pinned by: brute-force Eq. 4 parallel form, the ungated Eq. 1 reduction,
+    the scalar-gate decay-mask form, chunk-size invariance, segment invariance,
+    linearity, and a hand-computed golden fixture.
+    """
+    q, k, v, g = (_as_f64(x) for x in (q, k, v, g))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, T, H, K) and g.shape == (B, T, H, K) and v.shape == (B, T, H, V)
+    s0 = _as_f64(s0)
+    if s0 is not None:
+        assert s0.shape == (B, H, K, V)
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    sf = np.zeros((B, H, K, V), dtype=np.float64)
+    rc = _load().oracle_gla_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o), _ptr(sf))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_fwd failed with code %d" % rc)
+    return o, sf
+
+
+def gla_bwd(q, k, v, g, d_o, s0=None, dht=None):
+    """Reverse-mode gradient of the fp64 recurrence for loss <o,do> + <S_T,dht>.
+
+    Returns (dq, dk, dv, dg, ds0).  dg is the gradient with respect to the log
+    gate g, taken through d(exp(g_t) S_{t-1})/dg_t -- independent of the
+    paper's closed form (Section 4.3), which the tests check against it.
+    Pinned by: central finite differences, torch float64 autograd of the
+    parallel form (Eq. 4), the closed-form gate gradient, the closed-form
+    dS_0, dg_1 = 0 when S_0 = 0, and a hand-computed T = 2 fixture.
+    """
+    q, k, v, g, d_o = (_as_f64(x) for x in (q, k, v, g, d_o))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    s0 = _as_f64(s0)
+    dht = _as_f64(dht)
+    dq = np.zeros((B, T, H, K)); dk = np.zeros((B, T, H, K)); dg = np.zeros((B, T, H, K))
+    dv = np.zeros((B, T, H, V)); ds0 = np.zeros((B, H, K, V))
+    rc = _load().oracle_gla_bwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(d_o),
+                                _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ds0))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_bwd failed with code %d" % rc)
+    return dq, dk, dv, dg, ds0

@@ -1,0 +1,226 @@
+/*
+ * Reference oracle for gated linear attention (GLA) -- TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the slow, obviously-correct CPU definition that the GPU path is
+ * checked against.  Only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it; the product library never links it, and it
+ * shares no code, header or table with the HIP kernels.
+ *
+ * Arithmetic is IEEE fp64 throughout, token by token, exactly as the
+ * recurrence is written -- no chunking, no blocking, no reordering:
+ *
+ *   "Gated Linear Attention Transformers with Hardware-Efficient Training"
+ *   (Yang, Wang, Shen, Panda, Kim), Section 4.1, Eq. (3):
+ *       S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t ,   o_t = q_t S_t
+ *   with alpha_t = exp(g_t) given as the log forget gate g_t (Section 4.3 and
+ *   the chapter summary's Knowl 3 take the gate in log space).  S_0 is zero or
+ *   the previous segment's state (Section 2.2, "initialized to zero or from the
+ *   previous segment's hidden state"); the final state S_T is returned so that
+ *   segments can be chained (truncated BPTT, Section 5.2).
+ *
+ * The backward pass is reverse-mode differentiation of that same loop (the
+ * hand-computed gradient of the recurrence).  It does NOT use the paper's
+ * closed-form gate gradient (Section 4.3, "Memory-efficient dalpha_t
+ * computation"); the gate gradient here comes from dS_t and S_{t-1} directly,
+ * which is the quantity the paper says earlier work had to materialise.  The
+ * agreement of the two routes is itself one of the tests.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, k, g, dq, dk, dg : [B, T, H, K]
+ *   v, o, do, dv        : [B, T, H, V]
+ *   s0, s_final, dht, ds0 : [B, H, K, V]
+ * Heads are independent (Section 4.4, multi-head GLA), so (b, h) pairs are
+ * processed in parallel with OpenMP when it is available.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define IDX_TOK(b, t, h, d, T, H, D) ((((size_t)(b) * (T) + (t)) * (H) + (h)) * (D) + (d))
+#define IDX_ST(b, h, i, j, H, K, V) ((((size_t)(b) * (H) + (h)) * (K) + (i)) * (V) + (j))
+
+/* Length of the recompute segments used by the backward pass.  States are
+ * checkpointed at every multiple of this many tokens and recomputed forward
+ * inside a segment; they are never obtained by dividing by the gate. */
+#define ORACLE_CKPT 64
+
+int oracle_version(void) { return 1; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* One recurrence step on a single head: S <- Diag(exp(g_t)) S + k_t^T v_t. */
+static void step_state(double *S, const double *k_t, const double *g_t, const double *v_t,
+                       long K, long V) {
+    for (long i = 0; i < K; ++i) {
+        const double a = exp(g_t[i]);
+        const double ki = k_t[i];
+        double *row = S + i * V;
+        for (long j = 0; j < V; ++j) row[j] = a * row[j] + ki * v_t[j];
+    }
+}
+
+/* Forward: o_t = q_t S_t with S_t the state AFTER token t's update (the causal
+ * mask of Section 2.1 has M_tt = 1, so token t attends to itself). */
+int oracle_gla_fwd(long B, long T, long H, long K, long V,
+                   const double *q, const double *k, const double *v, const double *g,
+                   const double *s0, double *o, double *s_final) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return 1;
+    long nbh = B * H;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        long b = bh / H, h = bh % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)K * (size_t)V);
+        double *qt = (double *)malloc(sizeof(double) * (size_t)K);
+        double *kt = (double *)malloc(sizeof(double) * (size_t)K);
+        double *gt = (double *)malloc(sizeof(double) * (size_t)K);
+        double *vt = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!S || !qt || !kt || !gt || !vt) {
+#pragma omp atomic write
+            err = 2;
+            free(S); free(qt); free(kt); free(gt); free(vt);
+            continue;
+        }
+        for (long i = 0; i < K; ++i)
+            for (long j = 0; j < V; ++j)
+                S[i * V + j] = s0 ? s0[IDX_ST(b, h, i, j, H, K, V)] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            for (long i = 0; i < K; ++i) {
+                qt[i] = q[IDX_TOK(b, t, h, i, T, H, K)];
+                kt[i] = k[IDX_TOK(b, t, h, i, T, H, K)];
+                gt[i] = g[IDX_TOK(b, t, h, i, T, H, K)];
+            }
+            for (long j = 0; j < V; ++j) vt[j] = v[IDX_TOK(b, t, h, j, T, H, V)];
+            step_state(S, kt, gt, vt, K, V);
+            for (long j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < K; ++i) acc += qt[i] * S[i * V + j];
+                o[IDX_TOK(b, t, h, j, T, H, V)] = acc;
+            }
+        }
+        if (s_final)
+            for (long i = 0; i < K; ++i)
+                for (long j = 0; j < V; ++j) s_final[IDX_ST(b, h, i, j, H, K, V)] = S[i * V + j];
+        free(S); free(qt); free(kt); free(gt); free(vt);
+    }
+    return err;
+}
+
+/* Backward of the same loop.  With S_t the post-update state and dS the
+ * running gradient with respect to it, for t = T..1:
+ *   dS      += q_t^T do_t                       (o_t = q_t S_t)
+ *   dq_t[i]  = sum_j do_t[j] S_t[i,j]
+ *   dk_t[i]  = sum_j dS[i,j] v_t[j]             (S_t contains k_t^T v_t)
+ *   dv_t[j]  = sum_i k_t[i] dS[i,j]
+ *   dg_t[i]  = exp(g_t[i]) sum_j dS[i,j] S_{t-1}[i,j]   (d/dg of exp(g) S_{t-1})
+ *   dS      <- Diag(exp(g_t)) dS                (gradient flowing into S_{t-1})
+ * The loss is <o, do> + <S_T, dht>, so dS starts at dht (zero when absent),
+ * and after t = 1 it is the gradient with respect to S_0. */
+int oracle_gla_bwd(long B, long T, long H, long K, long V,
+                   const double *q, const double *k, const double *v, const double *g,
+                   const double *s0, const double *d_o, const double *dht,
+                   double *dq, double *dk, double *dv, double *dg, double *ds0) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return 1;
+    const long KV = K * V;
+    const long nseg = (T + ORACLE_CKPT - 1) / ORACLE_CKPT;
+    long nbh = B * H;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        long b = bh / H, h = bh % H;
+        /* ckpt[m] = state before token m*ORACLE_CKPT (i.e. S_{m*CKPT}). */
+        double *ckpt = (double *)malloc(sizeof(double) * (size_t)KV * (size_t)(nseg > 0 ? nseg : 1));
+        /* seg[u] = state after token (segment start + u), u = 0..CKPT-1,
+         * plus seg_prev = state before the segment. */
+        double *seg = (double *)malloc(sizeof(double) * (size_t)KV * (ORACLE_CKPT + 1));
+        double *dS = (double *)malloc(sizeof(double) * (size_t)KV);
+        double *kt = (double *)malloc(sizeof(double) * (size_t)K);
+        double *gt = (double *)malloc(sizeof(double) * (size_t)K);
+        double *vt = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!ckpt || !seg || !dS || !kt || !gt || !vt) {
+#pragma omp atomic write
+            err = 2;
+            free(ckpt); free(seg); free(dS); free(kt); free(gt); free(vt);
+            continue;
+        }
+        /* Forward sweep storing checkpoints. */
+        double *S = seg; /* scratch for the sweep */
+        for (long i = 0; i < K; ++i)
+            for (long j = 0; j < V; ++j)
+                S[i * V + j] = s0 ? s0[IDX_ST(b, h, i, j, H, K, V)] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            if (t % ORACLE_CKPT == 0) memcpy(ckpt + (t / ORACLE_CKPT) * KV, S, sizeof(double) * KV);
+            for (long i = 0; i < K; ++i) {
+                kt[i] = k[IDX_TOK(b, t, h, i, T, H, K)];
+                gt[i] = g[IDX_TOK(b, t, h, i, T, H, K)];
+            }
+            for (long j = 0; j < V; ++j) vt[j] = v[IDX_TOK(b, t, h, j, T, H, V)];
+            step_state(S, kt, gt, vt, K, V);
+        }
+        for (long i = 0; i < K; ++i)
+            for (long j = 0; j < V; ++j)
+                dS[i * V + j] = dht ? dht[IDX_ST(b, h, i, j, H, K, V)] : 0.0;
+        /* Reverse sweep, one checkpoint segment at a time. */
+        for (long m = nseg - 1; m >= 0; --m) {
+            long t0 = m * ORACLE_CKPT;
+            long t1 = t0 + ORACLE_CKPT < T ? t0 + ORACLE_CKPT : T;
+            /* seg[0] = S before token t0; seg[u+1] = S after token t0+u. */
+            memcpy(seg, ckpt + m * KV, sizeof(double) * KV);
+            for (long t = t0; t < t1; ++t) {
+                double *dst = seg + (t - t0 + 1) * KV;
+                memcpy(dst, seg + (t - t0) * KV, sizeof(double) * KV);
+                for (long i = 0; i < K; ++i) {
+                    kt[i] = k[IDX_TOK(b, t, h, i, T, H, K)];
+                    gt[i] = g[IDX_TOK(b, t, h, i, T, H, K)];
+                }
+                for (long j = 0; j < V; ++j) vt[j] = v[IDX_TOK(b, t, h, j, T, H, V)];
+                step_state(dst, kt, gt, vt, K, V);
+            }
+            for (long t = t1 - 1; t >= t0; --t) {
+                const double *St = seg + (t - t0 + 1) * KV;
+                const double *Sp = seg + (t - t0) * KV;
+                /* dS += q_t^T do_t */
+                for (long i = 0; i < K; ++i) {
+                    const double qi = q[IDX_TOK(b, t, h, i, T, H, K)];
+                    for (long j = 0; j < V; ++j) dS[i * V + j] += qi * d_o[IDX_TOK(b, t, h, j, T, H, V)];
+                }
+                for (long i = 0; i < K; ++i) {
+                    double aq = 0.0, ak = 0.0, ag = 0.0;
+                    for (long j = 0; j < V; ++j) {
+                        aq += d_o[IDX_TOK(b, t, h, j, T, H, V)] * St[i * V + j];
+                        ak += dS[i * V + j] * v[IDX_TOK(b, t, h, j, T, H, V)];
+                        ag += dS[i * V + j] * Sp[i * V + j];
+                    }
+                    const double a = exp(g[IDX_TOK(b, t, h, i, T, H, K)]);
+                    dq[IDX_TOK(b, t, h, i, T, H, K)] = aq;
+                    dk[IDX_TOK(b, t, h, i, T, H, K)] = ak;
+                    dg[IDX_TOK(b, t, h, i, T, H, K)] = a * ag;
+                }
+                for (long j = 0; j < V; ++j) {
+                    double av = 0.0;
+                    for (long i = 0; i < K; ++i) av += k[IDX_TOK(b, t, h, i, T, H, K)] * dS[i * V + j];
+                    dv[IDX_TOK(b, t, h, j, T, H, V)] = av;
+                }
+                for (long i = 0; i < K; ++i) {
+                    const double a = exp(g[IDX_TOK(b, t, h, i, T, H, K)]);
+                    for (long j = 0; j < V; ++j) dS[i * V + j] *= a;
+                }
+            }
+        }
+        if (ds0)
+            for (long i = 0; i < K; ++i)
+                for (long j = 0; j < V; ++j) ds0[IDX_ST(b, h, i, j, H, K, V)] = dS[i * V + j];
+        free(ckpt); free(seg); free(dS); free(kt); free(gt); free(vt);
+    }
+    return err;
+}
