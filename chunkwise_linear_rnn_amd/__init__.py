@@ -1,0 +1,177 @@
+"""Chunkwise gated linear attention (GLA) for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libgla.so`` (declared in
+``include/gla.h``).  PyTorch is used only to own device memory and to name the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Functions mirror the ABI:
+  gla_fwd(q, k, v, g, s0=None, ...)         -> (o, s_final)
+  gla_bwd(q, k, v, g, d_o, s0=None, dht=None) -> (dq, dk, dv, dg, ds0)
+  gla_fwd_workspace_size / gla_bwd_workspace_size
+Layouts: q, k, g [B,T,H,K]; v, o, d_o [B,T,H,V]; states [B,H,K,V] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgla.so")
+
+GLA_DTYPE_FP32 = 0
+GLA_DTYPE_BF16 = 1
+CHUNK = 64
+
+
+class GlaShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("chunk", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status: int, detail: str, message: str):
+        super().__init__("%s (%s)" % (message, detail) if detail else message)
+        self.status = status
+
+
+EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size",
+           "gla_status_string", "gla_last_error_detail", "gla_abi_version"]
+
+_lib = None
+
+
+def lib():
+    """Load libgla.so (built by ``build.build()``); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgla.so not built: run `python -m chunkwise_linear_rnn_amd.build` "
+                           "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    sh = ctypes.POINTER(GlaShape)
+    L.gla_fwd.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gla_fwd.restype = ctypes.c_int
+    L.gla_bwd.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gla_bwd.restype = ctypes.c_int
+    L.gla_fwd_workspace_size.argtypes = [sh]
+    L.gla_fwd_workspace_size.restype = ctypes.c_size_t
+    L.gla_bwd_workspace_size.argtypes = [sh]
+    L.gla_bwd_workspace_size.restype = ctypes.c_size_t
+    L.gla_status_string.argtypes = [ctypes.c_int]
+    L.gla_status_string.restype = ctypes.c_char_p
+    L.gla_last_error_detail.argtypes = []
+    L.gla_last_error_detail.restype = ctypes.c_char_p
+    L.gla_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def make_shape(B, T, H, K, V, dtype) -> GlaShape:
+    if isinstance(dtype, torch.dtype):
+        dtype = GLA_DTYPE_BF16 if dtype == torch.bfloat16 else (GLA_DTYPE_FP32 if dtype == torch.float32 else -1)
+    return GlaShape(B, T, H, K, V, CHUNK, dtype, 0)
+
+
+def _check(rc: int):
+    if rc != 0:
+        L = lib()
+        raise GlaError(rc, L.gla_last_error_detail().decode(), L.gla_status_string(rc).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gla_fwd_workspace_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_fwd_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
+
+
+def gla_bwd_workspace_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_bwd_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
+
+
+def _dims(q, v):
+    B, T, H, K = q.shape
+    return B, T, H, K, v.shape[-1]
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gla_fwd_into(q, k, v, g, s0, o, s_final, ws, stream=None):
+    """Call the ABI with caller-owned outputs and workspace (nothing allocated)."""
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib().gla_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o),
+                         _ptr(s_final), _ptr(ws), nbytes, _stream(stream)))
+
+
+def gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream=None):
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib().gla_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(d_o),
+                         _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ds0), _ptr(ws), nbytes,
+                         _stream(stream)))
+
+
+def gla_fwd(q, k, v, g, s0=None, output_final_state=True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """o, S_T = GLA forward.  q, k, g: [B,T,H,K]; v: [B,T,H,V]; s0: [B,H,K,V] fp32 or None."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(q, "q", (B, T, H, K), dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    ws = workspace(gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+    gla_fwd_into(q, k, v, g, s0, o, sf, ws, stream)
+    return o, sf
+
+
+def gla_bwd(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
+    """dq, dk, dv, dg, dS0 of <o, d_o> + <S_T, dht> (states recomputed inside)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("d_o", d_o, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    _need(dht, "dht", (B, H, K, V), torch.float32, dev)
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dg = torch.empty_like(g); dv = torch.empty_like(v)
+    ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
+    ws = workspace(gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
+    gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream)
+    return dq, dk, dv, dg, ds0

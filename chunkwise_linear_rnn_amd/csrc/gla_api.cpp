@@ -1,0 +1,217 @@
+// C ABI of the gfx950 GLA library: argument validation, launch planning and
+// dispatch.  Every check runs on the host before the first HIP call, so an
+// invalid call enqueues nothing (see include/gla.h for the contract).
+#include "../../include/gla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gla_launch.hpp"
+#include "gla_plan.hpp"
+
+namespace {
+
+thread_local std::string g_detail;
+
+gla_status_t fail(gla_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gla_status_t fail(gla_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return st;
+}
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_kv(int64_t K, int64_t V, bool bf16) {
+    if (bf16) return (K == 64 || K == 128 || K == 256) && (V == 64 || V == 128 || V == 256 || V == 512);
+    return (K == 64 || K == 128) && (V == 64 || V == 128 || V == 256);
+}
+
+// Shape checks shared by forward and backward.  On success fills `out`.
+gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out) {
+    if (!s) return fail(GLA_ERR_NULL, "shape is NULL");
+    if (s->reserved != 0) return fail(GLA_ERR_UNSUPPORTED, "shape.reserved must be 0 (got %d)", s->reserved);
+    if (s->B < 0 || s->T < 0 || s->H < 0)
+        return fail(GLA_ERR_SHAPE, "negative size: B=%lld T=%lld H=%lld", (long long)s->B, (long long)s->T,
+                    (long long)s->H);
+    if (s->K <= 0 || s->V <= 0)
+        return fail(GLA_ERR_SHAPE, "head dims must be positive: K=%lld V=%lld", (long long)s->K, (long long)s->V);
+    if (s->chunk != 64) return fail(GLA_ERR_UNSUPPORTED, "chunk must be 64 (got %lld)", (long long)s->chunk);
+    if (s->dtype != GLA_DTYPE_BF16 && s->dtype != GLA_DTYPE_FP32)
+        return fail(GLA_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+    const bool bf16 = s->dtype == GLA_DTYPE_BF16;
+    if (!supported_kv(s->K, s->V, bf16))
+        return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for %s", (long long)s->K,
+                    (long long)s->V, bf16 ? "bf16" : "fp32");
+    if (s->T % 64 != 0) return fail(GLA_ERR_SHAPE, "T=%lld is not a multiple of the chunk 64", (long long)s->T);
+    // kernel index arithmetic: per-tensor element counts and the sizes passed as int
+    const int64_t lim = (int64_t)1 << 31;
+    if (s->T >= lim || s->H >= lim || s->B >= lim || s->B * s->H >= lim)
+        return fail(GLA_ERR_SHAPE, "size too large for this library");
+    out->B = s->B;
+    out->T = s->T;
+    out->H = s->H;
+    out->K = s->K;
+    out->V = s->V;
+    out->bf16 = bf16;
+    return GLA_OK;
+}
+
+size_t bwd_workspace_bytes(const gla::Shape& s);
+
+}  // namespace
+
+extern "C" {
+
+int gla_abi_version(void) { return GLA_ABI_VERSION; }
+
+const char* gla_status_string(gla_status_t st) {
+    switch (st) {
+        case GLA_OK: return "GLA_OK: success";
+        case GLA_ERR_NULL: return "GLA_ERR_NULL: a required pointer is NULL";
+        case GLA_ERR_SHAPE: return "GLA_ERR_SHAPE: invalid problem size";
+        case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED: head dims, chunk or dtype not supported";
+        case GLA_ERR_ALIGN: return "GLA_ERR_ALIGN: pointer not 16-byte aligned";
+        case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace missing or too small";
+        case GLA_ERR_HIP: return "GLA_ERR_HIP: HIP runtime error";
+    }
+    return "unknown gla_status_t";
+}
+
+const char* gla_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s) != GLA_OK) return 0;
+    return gla::fwd_workspace_bytes(s);
+}
+
+size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s) != GLA_OK) return 0;
+    return bwd_workspace_bytes(s);
+}
+
+gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                     const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s);
+    if (st != GLA_OK) return st;
+    const bool empty = s.B * s.H == 0 || s.T == 0;
+    if (!empty && (!q || !k || !v || !g || !o)) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
+    const void* ptrs[] = {q, k, v, g, s0, o, s_final, workspace};
+    const char* names[] = {"q", "k", "v", "g", "s0", "o", "s_final", "workspace"};
+    for (int i = 0; i < 8; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t need = empty ? 0 : gla::fwd_workspace_bytes(s);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (empty) {
+        // no tokens: the final state is the initial state (Section 2.2)
+        err = s_final ? gla::launch_state_copy(s0, s_final, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else {
+        gla::Plan p = gla::make_fwd_plan(s);
+        gla::FwdLaunch a{};
+        a.bf16 = s.bf16;
+        a.K = (int)s.K;
+        a.V = (int)s.V;
+        a.BV = p.BV;
+        a.T = (int)s.T;
+        a.H = (int)s.H;
+        a.N = (int)p.N;
+        a.P = p.P;
+        a.seg_len = p.seg_len;
+        a.BH = p.BH;
+        a.q = q; a.k = k; a.v = v; a.g = g;
+        a.s0 = s0;
+        a.o = o;
+        a.s_final = s_final;
+        if (p.P > 1) {
+            a.ws_state = static_cast<float*>(workspace);
+            a.ws_gate = a.ws_state + (size_t)p.BH * p.P * s.K * s.V;
+        }
+        a.stream = strm;
+        err = gla::launch_fwd(a);
+    }
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
+gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                     const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                     float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s);
+    if (st != GLA_OK) return st;
+    const bool empty = s.B * s.H == 0 || s.T == 0;
+    if (!empty && (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg))
+        return fail(GLA_ERR_NULL, "q, k, v, g, d_o, dq, dk, dv and dg are required");
+    const void* ptrs[] = {q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace};
+    const char* names[] = {"q", "k", "v", "g", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "ds0", "workspace"};
+    for (int i = 0; i < 13; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t need = empty ? 0 : bwd_workspace_bytes(s);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (empty) {
+        // no tokens: dS_0 = dht (the state passes through unchanged)
+        err = ds0 ? gla::launch_state_copy(dht, ds0, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else {
+        gla::BwdLaunch a{};
+        gla::Plan p = gla::make_bwd_plan(s);
+        a.bf16 = s.bf16;
+        a.K = (int)s.K;
+        a.V = (int)s.V;
+        a.BV = p.BV;
+        a.BK = p.BK;
+        a.T = (int)s.T;
+        a.H = (int)s.H;
+        a.N = (int)p.N;
+        a.P = p.P;
+        a.seg_len = p.seg_len;
+        a.BH = p.BH;
+        a.q = q; a.k = k; a.v = v; a.g = g; a.d_o = d_o;
+        a.s0 = s0; a.dht = dht;
+        a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.ds0 = ds0;
+        const size_t kv = (size_t)p.BH * p.P * s.K * s.V;
+        const size_t kk = (size_t)p.BH * p.P * s.K;
+        float* ws = static_cast<float*>(workspace);
+        a.ws_state = ws;
+        a.ws_dstate = ws + kv;
+        a.ws_gate = ws + 2 * kv;
+        a.ws_carry = ws + 2 * kv + kk;
+        a.stream = strm;
+        err = gla::launch_bwd(a);
+    }
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+size_t bwd_workspace_bytes(const gla::Shape& s) {
+    gla::Plan p = gla::make_bwd_plan(s);
+    if (p.BH == 0) return 0;
+    const size_t kv = (size_t)p.BH * p.P * s.K * s.V;
+    const size_t kk = (size_t)p.BH * p.P * s.K;
+    return (2 * kv + 2 * kk) * sizeof(float);
+}
+}  // namespace

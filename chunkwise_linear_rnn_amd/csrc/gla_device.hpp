@@ -1,0 +1,212 @@
+// Device-side building blocks of the gfx950 GLA kernels.
+//
+// Everything here is written for CDNA4 wave64 and its matrix cores:
+//   * one MFMA "k-step" contracts 32 indices: v_mfma_f32_16x16x32_bf16 for
+//     bf16 operands, eight v_mfma_f32_16x16x4_f32 for fp32 operands;
+//   * every operand fragment is "16 free x 16 contraction" with lane l holding
+//     free index (l % 16) and contraction indices 4*(l/16) + e, e = 0..3 --
+//     the same placement as the 16x16 accumulator (lane holds rows
+//     4*(l/16)+e of column l%16).  A k-step pairs two such fragments.  A and
+//     B fragments use the same (lane group, slot) -> contraction-index map, so
+//     the product is the intended contraction, and an accumulator tile can be
+//     fed straight back as an operand that contracts over its rows.
+//   * all LDS tiles are row-major with 16 bytes of padding per row; operands
+//     that contract along the row are read with one 8/16-byte load per lane
+//     ("rm" fragments), operands that contract down a column with four
+//     element loads ("cm" fragments).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef float __attribute__((ext_vector_type(4))) f32x4;
+typedef __bf16 __attribute__((ext_vector_type(4))) bf16x4;
+typedef __bf16 __attribute__((ext_vector_type(8))) bf16x8;
+
+constexpr int kChunk = 64;      // chunk length C (Section 4.2)
+constexpr int kSub = 16;        // sub-chunk length c (Section 4.3) = MFMA tile edge
+constexpr float kLog2e = 1.4426950408889634f;
+// Within a chunk the intra-chunk products use one reference row (the chunk's
+// last row), so the query side carries factors in [1, 2^R] and the key side
+// factors in [2^-R, 1], R = the chunk's gate range in log2 units.  For R up to
+// this bound every factor is a normal number in fp32 and bf16 and no product
+// can overflow; chunks beyond it take the exact element-wise path (Eq. 4).
+constexpr float kRangeLimit = 64.0f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    using vec4 = f32x4;
+    static constexpr int pad = 4;  // 16 bytes of row padding in LDS tiles
+    __device__ static __forceinline__ float to_f(float x) { return x; }
+    __device__ static __forceinline__ float from_f(float x) { return x; }
+};
+template <> struct Elem<bf16> {
+    using vec4 = bf16x4;
+    static constexpr int pad = 8;
+    __device__ static __forceinline__ float to_f(bf16 x) { return (float)x; }
+    __device__ static __forceinline__ bf16 from_f(float x) { return (bf16)x; }
+};
+
+template <typename T> using vec4_t = typename Elem<T>::vec4;
+
+// ---------------------------------------------------------------------------
+// MFMA k-step: acc += A(16x32) * B(32x16), operands given as (lo, hi) pairs of
+// 16-contraction fragments.
+__device__ __forceinline__ f32x4 mma32(f32x4 acc, bf16x4 alo, bf16x4 ahi, bf16x4 blo, bf16x4 bhi) {
+    bf16x8 a = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x8 b = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(f32x4 acc, f32x4 alo, f32x4 ahi, f32x4 blo, f32x4 bhi) {
+    // fp32 operands: step r of a 16-block contracts index 4*(l/16) + r.
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(alo[0], blo[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(alo[1], blo[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(alo[2], blo[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(alo[3], blo[3], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ahi[0], bhi[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ahi[1], bhi[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ahi[2], bhi[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ahi[3], bhi[3], acc, 0, 0, 0);
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Fragment loads from row-major LDS tiles (element (r, c) at base[r*pitch + c]).
+
+// free index = row (r0 + l%16), contraction = columns c0 + 4*(l/16) + e.
+template <typename T>
+__device__ __forceinline__ vec4_t<T> frag_rm(const T* base, int pitch, int r0, int c0) {
+    const int l = lane_id();
+    return *reinterpret_cast<const vec4_t<T>*>(base + (r0 + (l & 15)) * pitch + c0 + 4 * (l >> 4));
+}
+
+// contraction = rows r0 + 4*(l/16) + e, free index = column c0 + l%16.
+template <typename T>
+__device__ __forceinline__ vec4_t<T> frag_cm(const T* base, int pitch, int r0, int c0) {
+    const int l = lane_id();
+    const T* p = base + (r0 + 4 * (l >> 4)) * pitch + c0 + (l & 15);
+    vec4_t<T> v;
+    v[0] = p[0];
+    v[1] = p[pitch];
+    v[2] = p[2 * pitch];
+    v[3] = p[3 * pitch];
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ vec4_t<T> to_vec4(f32x4 x) {
+    vec4_t<T> v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = Elem<T>::from_f(x[e]);
+    return v;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// A 64-row x W-column tile held in registers between its global load and its
+// use, 16 bytes per vector.  Thread `tid` owns vectors tid, tid+NT, ...; vector
+// idx covers row idx / (W/VEC), columns (idx % (W/VEC))*VEC .. +VEC-1.
+template <typename T, int W, int NT>
+struct TileRegs {
+    static constexpr int VEC = 16 / (int)sizeof(T);
+    static constexpr int VPR = W / VEC;           // vectors per row
+    static constexpr int NV = kChunk * VPR;       // vectors per tile
+    static constexpr int PER = (NV + NT - 1) / NT;
+    static_assert(W % VEC == 0, "tile width must be a whole number of 16-byte vectors");
+    uint4 r[PER];
+
+    __device__ __forceinline__ static bool owns(int p, int tid) { return (NV % NT == 0) || (tid + p * NT < NV); }
+    __device__ __forceinline__ static int row_of(int p, int tid) { return (tid + p * NT) / VPR; }
+    __device__ __forceinline__ static int col_of(int p, int tid) { return ((tid + p * NT) % VPR) * VEC; }
+
+    // `g` points at element (row 0, col 0) of the tile; rows are `rs` elements apart.
+    __device__ __forceinline__ void load(const T* __restrict__ g, long rs, int tid) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+            if (owns(p, tid))
+                r[p] = *reinterpret_cast<const uint4*>(g + (long)row_of(p, tid) * rs + col_of(p, tid));
+    }
+    __device__ __forceinline__ void store_lds(T* s, int pitch, int tid) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+            if (owns(p, tid))
+                *reinterpret_cast<uint4*>(s + row_of(p, tid) * pitch + col_of(p, tid)) = r[p];
+    }
+    // element e (0..VEC-1) of vector p as float
+    __device__ __forceinline__ float get(int p, int e) const {
+        const T* v = reinterpret_cast<const T*>(&r[p]);
+        return Elem<T>::to_f(v[e]);
+    }
+};
+
+// Pack VEC floats into one 16-byte vector of T and store it to LDS.
+template <typename T>
+__device__ __forceinline__ void store_vec_lds(T* dst, const float* x) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    uint4 u;
+    T* v = reinterpret_cast<T*>(&u);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = Elem<T>::from_f(x[e]);
+    *reinterpret_cast<uint4*>(dst) = u;
+}
+
+// ---------------------------------------------------------------------------
+// Intra-chunk inclusive cumulative log gate (Section 4.2: b_{iC+j}/b_{iC} in
+// log space; Knowl 3 of the chapter summary: "intra-chunk cumulative log
+// gates"), in log2 units:  sB[t][i] = log2(e) * sum_{u<=t} g[u][i].
+//
+// On entry the raw gate tile is in registers; on exit sB holds the cumsum,
+// sLast[i] = sB[63][i], and *sFlag is set if some column's chunk range
+// sB[0][i] - sB[63][i] exceeds kRangeLimit.  NT threads; KD columns.
+// Three barriers inside.  The caller clears *sFlag before the first barrier.
+template <typename T, int KD, int NT>
+__device__ __forceinline__ void chunk_log_cumsum(const TileRegs<T, KD, NT>& graw, float* sB, int pitchB,
+                                                 float* sTot, float* sLast, int* sFlag, int tid) {
+    using TR = TileRegs<T, KD, NT>;
+#pragma unroll
+    for (int p = 0; p < TR::PER; ++p) {
+        if (!TR::owns(p, tid)) continue;
+        float* dst = sB + TR::row_of(p, tid) * pitchB + TR::col_of(p, tid);
+#pragma unroll
+        for (int e = 0; e < TR::VEC; ++e) dst[e] = graw.get(p, e) * kLog2e;
+    }
+    __syncthreads();
+    static_assert(NT % KD == 0, "threads must tile the gate columns");
+    constexpr int NPART = NT / KD;          // threads per column
+    constexpr int R = kChunk / NPART;       // rows per thread
+    const int col = tid % KD, part = tid / KD;
+    float run = 0.f;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        float* p = sB + (part * R + u) * pitchB + col;
+        run += *p;
+        *p = run;
+    }
+    sTot[part * KD + col] = run;
+    __syncthreads();
+    if (part > 0) {
+        float off = 0.f;
+        for (int p = 0; p < part; ++p) off += sTot[p * KD + col];
+#pragma unroll
+        for (int u = 0; u < R; ++u) sB[(part * R + u) * pitchB + col] += off;
+        if (part == NPART - 1) {
+            const float last = run + off;
+            sLast[col] = last;
+            if (sB[col] - last > kRangeLimit) *sFlag = 1;
+        }
+    } else if (NPART == 1) {
+        sLast[col] = run;
+        if (sB[col] - run > kRangeLimit) *sFlag = 1;
+    }
+    __syncthreads();
+}
+
+}  // namespace gla

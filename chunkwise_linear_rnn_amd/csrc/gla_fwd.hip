@@ -1,0 +1,481 @@
+// Forward kernels of chunkwise gated linear attention on gfx950.
+//
+// Source of the method: "Gated Linear Attention Transformers with
+// Hardware-Efficient Training", Section 4.2 (chunkwise form: Lambda, Gamma,
+// gamma, the inter-chunk state recurrence and O_inter = (Q*Lambda) S) and
+// Section 4.3 (secondary chunking of the intra-chunk attention).  Section 3.3
+// describes the two ways of exposing parallelism over the sequence; here the
+// sequence of each head is cut into P segments:
+//
+//   1. gla_seg_state   (parallel over head x segment x column block)
+//        S*_p = sum over the segment's chunks of the decayed K^T V products,
+//        starting from zero, plus the segment's total log decay.
+//   2. gla_seg_combine (parallel over head x state element; serial over P)
+//        S_init(p+1) = Diag(decay_p) S_init(p) + S*_p,  S_init(0) = S_0.
+//   3. gla_fwd_walk    (parallel over head x segment x column block)
+//        walks the segment's chunks from S_init(p) with the state resident in
+//        VGPRs, producing O = (Q*Lambda) S + P V chunk by chunk, and the
+//        final state for the last segment.
+// With P = 1 only step 3 runs (the non-materialised form of Section 3.3).
+#include "gla_device.hpp"
+#include "gla_launch.hpp"
+
+namespace gla {
+
+// ---------------------------------------------------------------------------
+// Shared-memory layout of one chunk for the column-split kernels.
+template <typename T, int KD, int BV, int NT>
+struct ChunkSmem {
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int pB = KD + 4;      // fp32 cumulative log gate
+    static constexpr int pQ = KD + PT;     // q-side operand, row-major [t][i]
+    static constexpr int pK = KD + PT;     // k-side operand, row-major [s][i]
+    static constexpr int pV = BV + PT;     // value (or d_o) tile, row-major [s][j]
+    static constexpr int pA = kChunk + PT; // intra-chunk attention A[t][s]
+    float B[kChunk * pB];
+    T Q[kChunk * pQ];
+    T K[kChunk * pK];
+    T V[kChunk * pV];
+    T A[kChunk * pA];
+    float tot[NT];
+    float last[KD];
+    int flag;
+};
+
+// One wave's share of the state: rows 0..KD-1, columns col0 .. col0+16*CB-1,
+// as KD/16 x CB accumulator tiles.
+template <int KD, int CB>
+struct StateRegs {
+    f32x4 s[KD / 16][CB];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a)
+#pragma unroll
+            for (int c = 0; c < CB; ++c) s[a][c] = zero4();
+    }
+    // element (i, j) of tile (a, c) for accumulator slot r: i = 16a + 4*(l/16) + r, j = col0 + 16c + l%16
+    __device__ __forceinline__ void load(const float* __restrict__ src, long ld, int col0) {
+        const int l = lane_id();
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a)
+#pragma unroll
+            for (int c = 0; c < CB; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s[a][c][r] = src[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)];
+    }
+    __device__ __forceinline__ void store(float* __restrict__ dst, long ld, int col0) const {
+        const int l = lane_id();
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a)
+#pragma unroll
+            for (int c = 0; c < CB; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)] = s[a][c][r];
+    }
+};
+
+// S <- Diag(gamma) S + X^T Y over the 64 rows of the chunk (Section 4.2:
+// S_[i+1] = (gamma^T 1) * S_[i] + (K*Gamma)^T V).  X (row-major [t][i], the
+// already-decayed key/query tile) and Y (row-major [t][j]) are in LDS;
+// gamma = exp2(last[i]).  Columns of this wave: col0 .. col0 + 16*CB - 1.
+template <typename T, int KD, int CB>
+__device__ __forceinline__ void state_update(StateRegs<KD, CB>& S, const T* X, int pX, const T* Y, int pY,
+                                             const float* last, int col0) {
+    const int l = lane_id();
+#pragma unroll
+    for (int a = 0; a < KD / 16; ++a) {
+        f32x4 gam;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gam[r] = exp2_fast(last[16 * a + 4 * (l >> 4) + r]);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) S.s[a][c] *= gam;
+    }
+    vec4_t<T> yf[4][CB];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) yf[sb][c] = frag_cm<T>(Y, pY, 16 * sb, col0 + 16 * c);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a) {
+            vec4_t<T> xlo = frag_cm<T>(X, pX, 32 * ks, 16 * a);
+            vec4_t<T> xhi = frag_cm<T>(X, pX, 32 * ks + 16, 16 * a);
+#pragma unroll
+            for (int c = 0; c < CB; ++c) S.s[a][c] = mma32(S.s[a][c], xlo, xhi, yf[2 * ks][c], yf[2 * ks + 1][c]);
+        }
+    }
+}
+
+__device__ __forceinline__ void decode_tile(int tile, int& is, int& js) {
+    // lower-triangular 16x16 tiles of the 64x64 chunk, row by row
+    constexpr int tis[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int tjs[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    is = tis[tile];
+    js = tjs[tile];
+}
+
+// ---------------------------------------------------------------------------
+// Step 1: segment-local states.  REV = false: S*_p from the keys and values of
+// the segment walked forwards (decay Gamma = exp2(B_63 - B_t) on the keys).
+// REV = true: the backward pass's dS*_p from queries and d_o walked backwards
+// (decay Lambda = exp2(B_t) on the queries; dS_[n-1] = gamma dS_[n] + (Q*Lambda)^T dO).
+template <typename T, int KD, int BV, int NW, bool REV>
+__global__ void __launch_bounds__(NW * 64)
+gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
+              float* __restrict__ ws_state, float* __restrict__ ws_gate,
+              int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg) {
+    constexpr int NT = NW * 64;
+    constexpr int CB = BV / NW / 16;
+    using Sm = ChunkSmem<T, KD, BV, NT>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id();
+    const int nvb = V / BV;
+    int bid = blockIdx.x;
+    const int vb = bid % nvb; bid /= nvb;
+    const int seg = seg_first + bid % nseg; bid /= nseg;
+    const int bh = bid;
+    const int b = bh / H, h = bh % H;
+    const int v0 = vb * BV;
+    const int c_begin = seg * seg_len;
+    const int c_end = min(N, c_begin + seg_len);
+    const int nchunks = c_end - c_begin;
+    const long rsK = (long)H * KD, rsV = (long)H * V;
+    const int col0 = w * (BV / NW);
+
+    StateRegs<KD, CB> S;
+    S.zero();
+    float gate_total = 0.f;
+
+    TileRegs<T, KD, NT> rx, rg;
+    TileRegs<T, BV, NT> ry;
+    auto issue = [&](int c) {
+        const long tok0 = (long)b * T_ + (long)c * kChunk;
+        rx.load(x + (tok0 * H + h) * KD, rsK, tid);
+        rg.load(g + (tok0 * H + h) * KD, rsK, tid);
+        ry.load(y + (tok0 * H + h) * V + v0, rsV, tid);
+    };
+    issue(REV ? c_end - 1 : c_begin);
+    for (int it = 0; it < nchunks; ++it) {
+        if (tid == 0) sm.flag = 0;
+        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        if (tid < KD) gate_total += sm.last[tid];
+        // decayed operand: K*Gamma (forward) or Q*Lambda (reverse)
+        using TR = TileRegs<T, KD, NT>;
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+            float vals[TR::VEC];
+#pragma unroll
+            for (int e = 0; e < TR::VEC; ++e) {
+                const float bt = sm.B[row * Sm::pB + c0 + e];
+                const float ex = REV ? bt : (sm.last[c0 + e] - bt);
+                vals[e] = rx.get(p, e) * exp2_fast(ex);
+            }
+            store_vec_lds<T>(sm.K + row * Sm::pK + c0, vals);
+        }
+        ry.store_lds(sm.V, Sm::pV, tid);
+        if (it + 1 < nchunks) issue(REV ? c_end - 2 - it : c_begin + it + 1);
+        __syncthreads();
+        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.last, col0);
+        __syncthreads();
+    }
+    float* dst = ws_state + ((long)bh * P + seg) * (long)KD * V + v0;
+    S.store(dst, V, col0);
+    if (vb == 0 && tid < KD) ws_gate[((long)bh * P + seg) * KD + tid] = gate_total;
+}
+
+// ---------------------------------------------------------------------------
+// Step 2 (forward): S_init(0) = S_0 (or 0); S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p.
+// ws_state[p] holds S*_p on entry and S_init(p) on exit.  One thread per state element.
+__global__ void __launch_bounds__(256)
+gla_seg_combine_fwd(const float* __restrict__ s0, float* __restrict__ ws_state, const float* __restrict__ ws_gate,
+                    int K, int V, int P) {
+    const long KV = (long)K * V;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long bh = blockIdx.y;
+    if (e >= KV) return;
+    const int i = (int)(e / V);
+    float cur = s0 ? s0[bh * KV + e] : 0.f;
+    float* st = ws_state + bh * P * KV + e;
+    const float* gt = ws_gate + bh * P * (long)K + i;
+    for (int p = 0; p < P; ++p) {
+        const float sp = (p + 1 < P) ? st[p * KV] : 0.f;
+        st[p * KV] = cur;
+        if (p + 1 < P) cur = exp2_fast(gt[p * (long)K]) * cur + sp;
+    }
+}
+
+// Copy (or zero) a [BH][K][V] fp32 state: final state of an empty sequence.
+__global__ void __launch_bounds__(256) gla_state_copy(const float* __restrict__ src, float* __restrict__ dst, long n) {
+    long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e < n) dst[e] = src ? src[e] : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Step 3: walk the chunks of one segment for one block of BV value columns.
+//
+// Per chunk (64 tokens, B = intra-chunk cumulative log2 gate, reference row
+// 63; Section 4.2 with the sub-chunk tiling of Section 4.3 at c = 16):
+//   Qh = q * exp2(B_t - B_63)   Kt = k * exp2(B_63 - B_s)   (row-major LDS)
+//   A[t][s] = sum_i Qh[t][i] Kt[s][i]  for s <= t: ten 16x16 MFMA tiles
+//   Ql = q * exp2(B_t)                                       (Q * Lambda)
+//   O  = Ql S + A V                                         (inter + intra)
+//   S  = Diag(exp2 B_63) S + Kt^T V                          (state passing)
+// Chunks whose gate range exceeds kRangeLimit compute A element by element
+// (Eq. 4, fp32, exp2 of the log-gate difference) instead.
+template <typename T, int KD, int BV, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
+             const float* __restrict__ s_init, long s_init_seg_stride, long s_init_bh_stride,
+             T* __restrict__ o, float* __restrict__ s_final,
+             int T_, int H, int V, int N, int P, int seg_len) {
+    constexpr int NT = NW * 64;
+    constexpr int CB = BV / NW / 16;
+    using Sm = ChunkSmem<T, KD, BV, NT>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nvb = V / BV;
+    int bid = blockIdx.x;
+    const int vb = bid % nvb; bid /= nvb;
+    const int seg = bid % P; bid /= P;
+    const int bh = bid;
+    const int b = bh / H, h = bh % H;
+    const int v0 = vb * BV;
+    const int c_begin = seg * seg_len;
+    const int c_end = min(N, c_begin + seg_len);
+    const long rsK = (long)H * KD, rsV = (long)H * V;
+    const int col0 = w * (BV / NW);
+
+    // zero the strictly-upper 16x16 tiles of A once; they are never written
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int t = e / kChunk, s = e % kChunk;
+        if ((s >> 4) > (t >> 4)) sm.A[t * Sm::pA + s] = Elem<T>::from_f(0.f);
+    }
+
+    StateRegs<KD, CB> S;
+    if (s_init) S.load(s_init + (long)bh * s_init_bh_stride + (long)seg * s_init_seg_stride + v0, V, col0);
+    else S.zero();
+
+    TileRegs<T, KD, NT> rq, rk, rg;
+    TileRegs<T, BV, NT> rv;
+    using TR = TileRegs<T, KD, NT>;
+    auto tok_base = [&](int c) { return (long)b * T_ + (long)c * kChunk; };
+    {
+        const long t0 = tok_base(c_begin);
+        rq.load(q + (t0 * H + h) * KD, rsK, tid);
+        rk.load(k + (t0 * H + h) * KD, rsK, tid);
+        rg.load(g + (t0 * H + h) * KD, rsK, tid);
+        rv.load(v + (t0 * H + h) * V + v0, rsV, tid);
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        const bool more = c + 1 < c_end;
+        if (tid == 0) sm.flag = 0;
+        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        const bool exact = sm.flag != 0;
+        // (b) operands of the intra-chunk tiles
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+            float qv[TR::VEC], kv[TR::VEC];
+#pragma unroll
+            for (int e = 0; e < TR::VEC; ++e) {
+                const float bt = sm.B[row * Sm::pB + c0 + e], bl = sm.last[c0 + e];
+                qv[e] = rq.get(p, e);
+                kv[e] = rk.get(p, e);
+                if (!exact) {
+                    qv[e] *= exp2_fast(bt - bl);
+                    kv[e] *= exp2_fast(bl - bt);
+                }
+            }
+            store_vec_lds<T>(sm.Q + row * Sm::pQ + c0, qv);
+            store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
+        }
+        rv.store_lds(sm.V, Sm::pV, tid);
+        if (more) {
+            const long t1 = tok_base(c + 1);
+            rk.load(k + (t1 * H + h) * KD, rsK, tid);
+            rg.load(g + (t1 * H + h) * KD, rsK, tid);
+            rv.load(v + (t1 * H + h) * V + v0, rsV, tid);
+        }
+        __syncthreads();
+        // (c) A tiles, and Q*Lambda into registers
+        for (int tile = w; tile < 10; tile += NW) {
+            int is, js;
+            decode_tile(tile, is, js);
+            f32x4 acc = zero4();
+            if (!exact) {
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks) {
+                    vec4_t<T> alo = frag_rm<T>(sm.K, Sm::pK, 16 * js, 32 * ks);
+                    vec4_t<T> ahi = frag_rm<T>(sm.K, Sm::pK, 16 * js, 32 * ks + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks);
+                    vec4_t<T> bhi = frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks + 16);
+                    acc = mma32(acc, alo, ahi, blo, bhi);
+                }
+            } else {
+                const int t = 16 * is + (l & 15);
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * js + 4 * (l >> 4) + r;
+                    float sum = 0.f;
+                    if (s <= t)
+                        for (int i = 0; i < KD; ++i)
+                            sum += Elem<T>::to_f(sm.Q[t * Sm::pQ + i]) * Elem<T>::to_f(sm.K[s * Sm::pK + i]) *
+                                   exp2_fast(sm.B[t * Sm::pB + i] - sm.B[s * Sm::pB + i]);
+                    acc[r] = sum;
+                }
+            }
+            // acc holds A^T[s][t] for s = 16js + 4(l/16) + r, t = 16is + l%16
+            if (is == js) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * (l >> 4) + r > (l & 15)) acc[r] = 0.f;
+            }
+            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
+                to_vec4<T>(acc);
+        }
+        float ql[TR::PER][TR::VEC];
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+#pragma unroll
+            for (int e = 0; e < TR::VEC; ++e) ql[p][e] = rq.get(p, e) * exp2_fast(sm.B[row * Sm::pB + c0 + e]);
+        }
+        __syncthreads();
+        // (d) Q*Lambda over the q tile; K*Gamma in place for exact-path chunks
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+            store_vec_lds<T>(sm.Q + row * Sm::pQ + c0, ql[p]);
+            if (exact) {
+                float kv[TR::VEC];
+#pragma unroll
+                for (int e = 0; e < TR::VEC; ++e)
+                    kv[e] = Elem<T>::to_f(sm.K[row * Sm::pK + c0 + e]) *
+                            exp2_fast(sm.last[c0 + e] - sm.B[row * Sm::pB + c0 + e]);
+                store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
+            }
+        }
+        if (more) {
+            const long t1 = tok_base(c + 1);
+            rq.load(q + (t1 * H + h) * KD, rsK, tid);
+        }
+        __syncthreads();
+        // (e) outputs from the state before this chunk, then the state update
+        {
+            vec4_t<T> sf[KD / 32][CB][2];
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    sf[ks][cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
+                    sf[ks][cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                }
+            vec4_t<T> vf[4][CB];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(sm.V, Sm::pV, 16 * sb, col0 + 16 * cb);
+            const long t0 = tok_base(c);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4 acc[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[cb] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks) {
+                    vec4_t<T> alo = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks);
+                    vec4_t<T> ahi = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], alo, ahi, sf[ks][cb][0], sf[ks][cb][1]);
+                }
+#pragma unroll
+                for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
+                    vec4_t<T> alo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
+                    vec4_t<T> ahi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[cb] = mma32(acc[cb], alo, ahi, vf[2 * ks2][cb], vf[2 * ks2 + 1][cb]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const long t = t0 + 16 * rb + 4 * (l >> 4) + r;
+                        o[(t * H + h) * V + v0 + col0 + 16 * cb + (l & 15)] = Elem<T>::from_f(acc[cb][r]);
+                    }
+            }
+        }
+        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.last, col0);
+    }
+    if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V + v0, V, col0);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+template <typename T, int KD, int BV>
+static hipError_t launch_fwd_t(const FwdLaunch& a) {
+    constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
+    constexpr int NT = NW * 64;
+    static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
+    const int nvb = a.V / BV;
+    const long KV = (long)KD * a.V;
+    if (a.P > 1) {
+        // segments 0..P-2 feed the combine; the last segment's S* is never needed
+        const int nseg = a.P - 1;
+        dim3 grid((unsigned)(nvb * nseg * a.BH));
+        hipLaunchKernelGGL((gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), 0, a.stream,
+                           (const T*)a.k, (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate,
+                           a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg);
+        dim3 g2((unsigned)((KV + 255) / 256), (unsigned)a.BH);
+        hipLaunchKernelGGL(gla_seg_combine_fwd, g2, dim3(256), 0, a.stream, a.s0, a.ws_state, a.ws_gate,
+                           KD, a.V, a.P);
+    }
+    const float* sinit = a.P > 1 ? a.ws_state : a.s0;
+    const long seg_stride = a.P > 1 ? KV : 0;
+    const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
+    dim3 grid((unsigned)(nvb * a.P * a.BH));
+    hipLaunchKernelGGL((gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
+                       (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gla_state_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdLaunch& a) {
+    if (a.bf16) {
+        if (a.K == 64) {
+            if (a.BV == 64) return launch_fwd_t<bf16, 64, 64>(a);
+            if (a.BV == 128) return launch_fwd_t<bf16, 64, 128>(a);
+            if (a.BV == 256) return launch_fwd_t<bf16, 64, 256>(a);
+        } else if (a.K == 128) {
+            if (a.BV == 64) return launch_fwd_t<bf16, 128, 64>(a);
+            if (a.BV == 128) return launch_fwd_t<bf16, 128, 128>(a);
+            if (a.BV == 256) return launch_fwd_t<bf16, 128, 256>(a);
+        } else if (a.K == 256) {
+            if (a.BV == 64) return launch_fwd_t<bf16, 256, 64>(a);
+        }
+    } else {
+        if (a.K == 64) {
+            if (a.BV == 64) return launch_fwd_t<float, 64, 64>(a);
+            if (a.BV == 128) return launch_fwd_t<float, 64, 128>(a);
+        } else if (a.K == 128) {
+            if (a.BV == 64) return launch_fwd_t<float, 128, 64>(a);
+            if (a.BV == 128) return launch_fwd_t<float, 128, 128>(a);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gla

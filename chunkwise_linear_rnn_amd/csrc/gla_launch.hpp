@@ -1,0 +1,44 @@
+// Internal interface between the ABI layer (gla_api.cpp) and the kernel
+// launchers (gla_fwd.hip, gla_bwd.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+struct FwdLaunch {
+    bool bf16;
+    int K, V, BV;
+    int T, H, N, P, seg_len;
+    long BH;
+    const void *q, *k, *v, *g;
+    const float* s0;
+    void* o;
+    float* s_final;
+    float* ws_state;  // [BH][P][K][V] fp32
+    float* ws_gate;   // [BH][P][K]    fp32 (log2 of the segment decay)
+    hipStream_t stream;
+};
+
+struct BwdLaunch {
+    bool bf16;
+    int K, V, BV, BK;
+    int T, H, N, P, seg_len;
+    long BH;
+    const void *q, *k, *v, *g, *d_o;
+    const float *s0, *dht;
+    void *dq, *dk, *dv, *dg;
+    float* ds0;
+    float* ws_state;   // [BH][P][K][V] fp32: S*_p, then S_init(p)
+    float* ws_dstate;  // [BH][P][K][V] fp32: dS*_p, then dS_end(p)
+    float* ws_gate;    // [BH][P][K]
+    float* ws_carry;   // [BH][P][K]: gate-gradient carry into segment p from later tokens
+    hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdLaunch& a);
+hipError_t launch_bwd(const BwdLaunch& a);
+hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream);
+
+}  // namespace gla

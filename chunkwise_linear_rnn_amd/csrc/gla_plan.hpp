@@ -1,0 +1,87 @@
+// Host-side launch plan shared by the ABI layer and the kernel launchers.
+//
+// The plan is a pure function of the problem shape (no device query), so the
+// workspace size can be computed without a GPU.  It is sized for MI355X: 256
+// compute units, one 512-thread workgroup per CU for the chunk walks.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gla {
+
+constexpr int kTargetWorkgroups = 256;  // MI355X compute units
+
+struct Shape {
+    int64_t B, T, H, K, V;
+    bool bf16;
+};
+
+struct Plan {
+    int64_t BH;      // B*H independent recurrences (Section 4.4)
+    int64_t N;       // chunks per sequence, T / 64
+    int P;           // sequence segments per recurrence
+    int seg_len;     // chunks per segment (the last segment may be shorter)
+    int BV;          // state columns held by one workgroup in column-split kernels
+    int NW;          // waves per workgroup for column-split kernels
+    int BK;          // state rows held by one workgroup in row-split kernels
+    int NWK;         // waves per workgroup for row-split kernels
+};
+
+// State columns per workgroup: the K x BV fp32 state lives in VGPRs (64 per
+// lane at 512 threads) and the chunk tiles in LDS (160 KiB per CU).
+inline int plan_bv(const Shape& s) {
+    int cap;
+    if (s.bf16) cap = (s.K <= 64) ? 256 : (s.K <= 128 ? 256 : 64);
+    else cap = 128;
+    return (int)(s.V < cap ? s.V : cap);
+}
+
+// State rows per workgroup in the backward kernels that contract over V.
+inline int plan_bk(const Shape& s) {
+    // K-block x full V state in VGPRs: keep K_blk * V <= 32768 (64 regs/lane at 512 threads).
+    int64_t bk = 32768 / s.V;
+    if (!s.bf16) bk = 8192 / s.V;  // fp32 LDS tiles are twice as large
+    if (bk > s.K) bk = s.K;
+    if (bk < 16) bk = 16;
+    return (int)bk;
+}
+
+inline Plan make_plan(const Shape& s, int col_blocks_hint) {
+    Plan p;
+    p.BH = s.B * s.H;
+    p.N = s.T / 64;
+    p.BV = plan_bv(s);
+    p.NW = p.BV / 16 < 8 ? p.BV / 16 : 8;
+    p.BK = plan_bk(s);
+    p.NWK = p.BK / 16 < 8 ? p.BK / 16 : 8;
+    int64_t per_seg = p.BH * (int64_t)col_blocks_hint;
+    int64_t P = per_seg > 0 ? kTargetWorkgroups / per_seg : 1;
+    if (P < 1) P = 1;
+    if (P > p.N) P = p.N > 0 ? p.N : 1;
+    int64_t len = p.N > 0 ? (p.N + P - 1) / P : 1;
+    p.seg_len = (int)len;
+    p.P = (int)(p.N > 0 ? (p.N + len - 1) / len : 1);
+    return p;
+}
+
+inline Plan make_fwd_plan(const Shape& s) {
+    int bv = plan_bv(s);
+    return make_plan(s, (int)(s.V / bv));
+}
+
+inline Plan make_bwd_plan(const Shape& s) {
+    const int bv = plan_bv(s), bk = plan_bk(s);
+    const int nvb = (int)(s.V / bv), nkb = (int)(s.K / bk);
+    return make_plan(s, nvb > nkb ? nvb : nkb);
+}
+
+inline size_t fwd_workspace_bytes(const Shape& s) {
+    Plan p = make_fwd_plan(s);
+    if (p.P <= 1 || p.BH == 0) return 0;
+    size_t st = (size_t)p.BH * p.P * (size_t)s.K * (size_t)s.V * sizeof(float);
+    size_t gt = (size_t)p.BH * p.P * (size_t)s.K * sizeof(float);
+    return st + ((gt + 255) / 256) * 256;
+}
+
+}  // namespace gla

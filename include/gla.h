@@ -1,0 +1,139 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunkwise gated linear attention library.
+ *
+ * The operator is the gated linear attention recurrence of "Gated Linear
+ * Attention Transformers with Hardware-Efficient Training" (Yang, Wang, Shen,
+ * Panda, Kim), Section 4.1, Eq. 3, per head:
+ *
+ *     S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t ,     o_t = q_t S_t ,
+ *
+ * with the forget gate passed in log space, g_t = log(alpha_t) <= 0, and the
+ * initial state S_0 either zero or a caller-supplied state (Section 2.2: "zero
+ * or from the previous segment's hidden state").  The library computes it in
+ * the chunkwise form of Section 4.2 (chunk C = 64) with the secondary
+ * sub-chunking of Section 4.3 (sub-chunk c = 16), on hand-written HIP kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout (row-major, fully contiguous, no padding):
+ *      q, k, g, dq, dk, dg        [B, T, H, K]
+ *      v, o, d_o, dv              [B, T, H, V]
+ *      s0, s_final, dht, ds0      [B, H, K, V]   (always float32)
+ *  dtype: GLA_DTYPE_BF16 or GLA_DTYPE_FP32 applies to q, k, v, g, o, d_o and
+ *      to the gradients dq, dk, dv, dg.  Accumulation is always float32.
+ *  Pointers are DEVICE pointers (hipMalloc'd or equivalent), 16-byte aligned.
+ *  Ownership: the caller allocates every buffer including the workspace; the
+ *      library allocates nothing, frees nothing and keeps no pointer after
+ *      the call returns.
+ *  Execution: stream-ordered and asynchronous.  A call validates its
+ *      arguments on the host, then only enqueues kernels on `stream` (a
+ *      hipStream_t; NULL = the default stream) and returns.  Inputs must stay
+ *      alive and unmodified until the stream has passed the call.  Results are
+ *      deterministic: no atomics take part in any sum.
+ *  Errors: every argument is validated before anything is enqueued, so on
+ *      any error other than GLA_ERR_HIP nothing has been launched.  Detail
+ *      text for the last error of the calling thread is available from
+ *      gla_last_error_detail().  No C++ exception crosses this interface.
+ *  Preconditions not checked (checking would cost a pass over the data):
+ *      all inputs finite and g <= 0 (alpha in (0, 1], as the gate's
+ *      definition in Section 4.1 requires; g = 0 is ungated linear attention,
+ *      Eq. 1).  Violations give unspecified values, never an out-of-bounds
+ *      access.
+ *  Supported sizes: chunk == 64; T a multiple of 64; K in {64, 128, 256} and
+ *      V in {64, 128, 256, 512} for bf16; K in {64, 128} and V in
+ *      {64, 128, 256} for fp32.  B, H >= 0 and T >= 0; B*H == 0 or T == 0 is a
+ *      valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_ABI_VERSION 1
+
+typedef enum {
+    GLA_OK = 0,
+    GLA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    GLA_ERR_SHAPE = 2,       /* negative size, or T not a multiple of the chunk     */
+    GLA_ERR_UNSUPPORTED = 3, /* K, V, chunk or dtype outside the supported set      */
+    GLA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+    GLA_ERR_WORKSPACE = 5,   /* workspace smaller than the *_workspace_size() value */
+    GLA_ERR_HIP = 6          /* the HIP runtime rejected a launch (see detail text) */
+} gla_status_t;
+
+typedef enum { GLA_DTYPE_FP32 = 0, GLA_DTYPE_BF16 = 1 } gla_dtype_t;
+
+/* Problem description.  chunk must be 64 (the chunk size C of Section 4.2). */
+typedef struct {
+    int64_t B, T, H, K, V;
+    int64_t chunk;
+    int32_t dtype; /* gla_dtype_t */
+    int32_t reserved; /* must be 0 */
+} gla_shape_t;
+
+/*
+ * gla_fwd -- forward pass (Section 4.2 chunkwise form of Eq. 3).
+ *   q, k, g : [B,T,H,K] dtype        (g = log forget gate, <= 0)
+ *   v       : [B,T,H,V] dtype
+ *   s0      : [B,H,K,V] float32 initial state, or NULL for a zero state
+ *   o       : [B,T,H,V] dtype output, o_t = q_t S_t (S_t after token t)
+ *   s_final : [B,H,K,V] float32 final state S_T, or NULL to skip
+ *   workspace / workspace_bytes : device scratch of at least
+ *             gla_fwd_workspace_size(shape) bytes (may be NULL when that is 0)
+ *   stream  : hipStream_t to enqueue on (NULL = default stream)
+ * Returns GLA_OK or an error code (see above).
+ */
+gla_status_t gla_fwd(const gla_shape_t* shape,
+                     const void* q, const void* k, const void* v, const void* g,
+                     const float* s0, void* o, float* s_final,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gla_fwd needs for `shape` (0 for an invalid shape).
+ * A pure function of the shape: it makes no HIP call. */
+size_t gla_fwd_workspace_size(const gla_shape_t* shape);
+
+/*
+ * gla_bwd -- gradients of the loss L = <o, d_o> + <S_T, dht> with respect to
+ * q, k, v, g and S_0, for the same forward as gla_fwd.  States are recomputed
+ * (Section 3.3: hidden states are discarded after the forward pass and
+ * recomputed in the backward pass).  The gate gradient uses the closed form of
+ * Section 4.3, dlog b_t = q_t*dq_t - k_t*dk_t, dg_t = sum_{i>=t} dlog b_i, plus
+ * the final-state term sum_j S_T[i,j] dht[i,j] added to every dg_t.
+ *   q, k, g, v, s0 : as for gla_fwd (s0 may be NULL)
+ *   d_o     : [B,T,H,V] dtype upstream gradient of o
+ *   dht     : [B,H,K,V] float32 gradient of S_T, or NULL for zero
+ *             (truncated BPTT passes no gradient across segments, Section 5.2)
+ *   dq, dk, dg : [B,T,H,K] dtype outputs;  dv : [B,T,H,V] dtype output
+ *   ds0     : [B,H,K,V] float32 gradient of S_0, or NULL to skip
+ *   workspace : at least gla_bwd_workspace_size(shape) bytes
+ * Returns GLA_OK or an error code.
+ */
+gla_status_t gla_bwd(const gla_shape_t* shape,
+                     const void* q, const void* k, const void* v, const void* g,
+                     const float* s0, const void* d_o, const float* dht,
+                     void* dq, void* dk, void* dv, void* dg, float* ds0,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gla_bwd needs for `shape` (0 for an invalid shape). */
+size_t gla_bwd_workspace_size(const gla_shape_t* shape);
+
+/* Static description of a status code (never NULL). */
+const char* gla_status_string(gla_status_t status);
+
+/* Detail text of the last error reported on the calling thread ("" if none).
+ * The pointer stays valid until the next gla_* call on that thread. */
+const char* gla_last_error_detail(void);
+
+/* GLA_ABI_VERSION of the loaded library. */
+int gla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

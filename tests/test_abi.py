@@ -1,0 +1,101 @@
+"""C-ABI contract checks that need no GPU.
+
+The library must load without a device, export every symbol include/gla.h
+declares, and reject every invalid argument with its status code before making
+any HIP call (the pointers used below are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_linear_rnn_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gla.LIB_PATH):
+        from chunkwise_linear_rnn_amd import build
+        build.build()
+    return gla.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert set(declared) == set(gla.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.gla_abi_version() == 1
+
+
+def test_status_strings_total(L):
+    for code in range(-1, 9):
+        s = L.gla_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def _shape(B=2, T=128, H=3, K=64, V=64, chunk=64, dtype=gla.GLA_DTYPE_BF16, reserved=0):
+    return gla.GlaShape(B, T, H, K, V, chunk, dtype, reserved)
+
+
+P = ctypes.c_void_p(0x10000)  # aligned fake device pointer: validation never dereferences it
+
+
+def _fwd(L, shape, q=P, k=P, v=P, g=P, s0=None, o=P, sf=None, ws=P, wsb=1 << 40):
+    return L.gla_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, g, s0, o, sf, ws, wsb, None)
+
+
+def _bwd(L, shape, dq=P, ws=P, wsb=1 << 40, dht=None):
+    return L.gla_bwd(ctypes.byref(shape), P, P, P, P, None, P, dht, dq, P, P, P, None, ws, wsb, None)
+
+
+def test_validation_codes(L):
+    assert _fwd(L, None) == ERR_NULL
+    assert _fwd(L, _shape(), q=None) == ERR_NULL
+    assert _fwd(L, _shape(B=-1)) == ERR_SHAPE
+    assert _fwd(L, _shape(K=0)) == ERR_SHAPE
+    assert _fwd(L, _shape(T=100)) == ERR_SHAPE
+    assert _fwd(L, _shape(chunk=32)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(K=96)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(V=1024)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(dtype=7)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(K=256, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(reserved=1)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(), k=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert _fwd(L, _shape(), s0=ctypes.c_void_p(0x10004)) == ERR_ALIGN
+    assert b"16-byte" in L.gla_last_error_detail()
+    big = _shape(B=1, H=1, T=64 * 64)
+    need = L.gla_fwd_workspace_size(ctypes.byref(big))
+    if need > 0:
+        assert _fwd(L, big, wsb=need - 1) == ERR_WORKSPACE
+        assert _fwd(L, big, ws=None, wsb=need) == ERR_WORKSPACE
+    assert _bwd(L, _shape(), dq=None) == ERR_NULL
+    assert _bwd(L, _shape(T=65)) == ERR_SHAPE
+    need_b = L.gla_bwd_workspace_size(ctypes.byref(_shape()))
+    assert need_b > 0
+    assert _bwd(L, _shape(), wsb=need_b - 1) == ERR_WORKSPACE
+
+
+def test_workspace_sizes(L):
+    # invalid shapes report 0; sizes are a pure function of the shape
+    assert L.gla_fwd_workspace_size(ctypes.byref(_shape(T=100))) == 0
+    s = _shape(B=2, H=4, T=8192, K=128, V=256)
+    a = L.gla_fwd_workspace_size(ctypes.byref(s))
+    b = L.gla_fwd_workspace_size(ctypes.byref(s))
+    assert a == b and a % 4 == 0
+    # per-segment fp32 states dominate: at least one [K, V] state per head when segmented
+    assert a == 0 or a >= 2 * 4 * 128 * 256 * 4
+    bw = L.gla_bwd_workspace_size(ctypes.byref(s))
+    assert bw >= 2 * 2 * 4 * 128 * 256 * 4
