@@ -30,13 +30,20 @@ gla_status_t fail(gla_status_t st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool supported_kv(int64_t K, int64_t V, bool bf16) {
-    if (bf16) return (K == 64 || K == 128 || K == 256) && (V == 64 || V == 128 || V == 256 || V == 512);
-    return (K == 64 || K == 128) && (V == 64 || V == 128 || V == 256);
+// Head dims with kernel instantiations.  The limits come from the 160 KiB of
+// LDS per CU: fp32 tiles are twice the size of bf16 ones, and the backward
+// holds both the value and d_o tiles at full V.
+bool supported_kv(int64_t K, int64_t V, bool bf16, bool backward) {
+    if (bf16) {
+        const bool k_ok = K == 64 || K == 128 || K == 256;
+        const bool v_ok = V == 64 || V == 128 || V == 256 || (!backward && V == 512);
+        return k_ok && v_ok;
+    }
+    return (K == 64 || K == 128) && (V == 64 || V == 128);
 }
 
 // Shape checks shared by forward and backward.  On success fills `out`.
-gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out) {
+gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out, bool backward) {
     if (!s) return fail(GLA_ERR_NULL, "shape is NULL");
     if (s->reserved != 0) return fail(GLA_ERR_UNSUPPORTED, "shape.reserved must be 0 (got %d)", s->reserved);
     if (s->B < 0 || s->T < 0 || s->H < 0)
@@ -48,9 +55,9 @@ gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out) {
     if (s->dtype != GLA_DTYPE_BF16 && s->dtype != GLA_DTYPE_FP32)
         return fail(GLA_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
     const bool bf16 = s->dtype == GLA_DTYPE_BF16;
-    if (!supported_kv(s->K, s->V, bf16))
-        return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for %s", (long long)s->K,
-                    (long long)s->V, bf16 ? "bf16" : "fp32");
+    if (!supported_kv(s->K, s->V, bf16, backward))
+        return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for %s %s", (long long)s->K,
+                    (long long)s->V, bf16 ? "bf16" : "fp32", backward ? "backward" : "forward");
     if (s->T % 64 != 0) return fail(GLA_ERR_SHAPE, "T=%lld is not a multiple of the chunk 64", (long long)s->T);
     // kernel index arithmetic: per-tensor element counts and the sizes passed as int
     const int64_t lim = (int64_t)1 << 31;
@@ -90,13 +97,13 @@ const char* gla_last_error_detail(void) { return g_detail.c_str(); }
 
 size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
-    if (check_shape(shape, &s) != GLA_OK) return 0;
+    if (check_shape(shape, &s, false) != GLA_OK) return 0;
     return gla::fwd_workspace_bytes(s);
 }
 
 size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
-    if (check_shape(shape, &s) != GLA_OK) return 0;
+    if (check_shape(shape, &s, true) != GLA_OK) return 0;
     return bwd_workspace_bytes(s);
 }
 
@@ -105,7 +112,7 @@ gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, con
                      void* stream) {
     g_detail.clear();
     gla::Shape s;
-    gla_status_t st = check_shape(shape, &s);
+    gla_status_t st = check_shape(shape, &s, false);
     if (st != GLA_OK) return st;
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !o)) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
@@ -155,7 +162,7 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
                      float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
     g_detail.clear();
     gla::Shape s;
-    gla_status_t st = check_shape(shape, &s);
+    gla_status_t st = check_shape(shape, &s, true);
     if (st != GLA_OK) return st;
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg))
@@ -196,7 +203,7 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.ws_state = ws;
         a.ws_dstate = ws + kv;
         a.ws_gate = ws + 2 * kv;
-        a.ws_carry = ws + 2 * kv + kk;
+        a.ws_hs = ws + 2 * kv + ((kk + 63) / 64) * 64;
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
@@ -212,6 +219,7 @@ size_t bwd_workspace_bytes(const gla::Shape& s) {
     if (p.BH == 0) return 0;
     const size_t kv = (size_t)p.BH * p.P * s.K * s.V;
     const size_t kk = (size_t)p.BH * p.P * s.K;
-    return (2 * kv + 2 * kk) * sizeof(float);
+    const size_t hs = (size_t)p.BH * p.N * s.K * s.V * (s.bf16 ? 2 : 4);
+    return (2 * kv + ((kk + 63) / 64) * 64) * sizeof(float) + hs;
 }
 }  // namespace

@@ -1,12 +1,876 @@
-// Backward kernels of chunkwise gated linear attention on gfx950 (in progress).
-#include "gla_device.hpp"
+// Backward kernels of chunkwise gated linear attention on gfx950.
+//
+// Gradients of L = <o, d_o> + <S_T, dht> for the chunkwise form of "Gated
+// Linear Attention Transformers with Hardware-Efficient Training", Section 4.2,
+// with the hidden states recomputed (Section 3.3) and the gate gradient in the
+// closed form of Section 4.3 (dlog b_t = q_t*dq_t - k_t*dk_t, summed in reverse).
+// Per chunk (B = intra-chunk cumulative log2 gate, reference row 63,
+// Lambda_t = exp2(B_t), Gamma_s = exp2(B_63 - B_s), gamma = exp2(B_63)):
+//
+//   dP  = (dO V^T) * M                                  (causal, within the chunk)
+//   dq  = Lambda * (dO S_in^T) + sum_{s<=t} dP_ts k_s * exp2(B_t - B_s)
+//   dk  = Gamma * (V dS_out^T) + sum_{t>=s} dP_ts q_t * exp2(B_t - B_s)
+//   dv  = A^T dO + (K*Gamma) dS_out,   A the forward's intra-chunk matrix
+//   dS_in = Diag(gamma) dS_out + (Q*Lambda)^T dO
+//   dg_t = sum_{r>=t, r in chunk} (q_r*dq_r - k_r*dk_r) + rowsum(S_out * dS_out)
+//
+// S_in / S_out are the states before / after the chunk and dS_out the gradient
+// with respect to S_out.  The last term is the closed form's sum over all
+// later tokens, taken from the identity dg_t = rowsum(S_{t-1} * dL/dS_{t-1})
+// at the chunk boundary, so the reverse cumulative sum never runs over more
+// than one chunk and rounding errors of dq, dk cannot accumulate along the
+// sequence.  The sequence of each head is cut into P segments as in the
+// forward: segment-local states S*_p (forwards) and dS*_p (backwards) are
+// combined into S_init(p) and dS_end(p).  Then three walks run per segment:
+// dq forwards (state S^T split by rows of K; it also stores S_out of every
+// chunk), dk + dg backwards (dS^T split by rows of K), dv backwards (dS split
+// by columns of V).  Each walk contracts only over dimensions it holds whole.
+#include "gla_chunk.hpp"
 #include "gla_launch.hpp"
 
 namespace gla {
 
+// ---------------------------------------------------------------------------
+// LDS of the row-split kernels: a BK-column slice of the key-side tiles and
+// full-width value / d_o tiles.
+template <typename T, int BK, int V, int NT>
+struct RowSmem {
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int pB = BK + 4;
+    static constexpr int pX = BK + PT;
+    static constexpr int pV = V + PT;
+    static constexpr int pP = kChunk + PT;
+    float B[kChunk * pB];   // cumulative log2 gate; later d k (fp32) and dA
+    T X[kChunk * pX];       // K*Gamma (dq walk) or q-side operand (dk walk)
+    T Vt[kChunk * pV];      // value tile, row-major [s][j]
+    T dO[kChunk * pV];      // d_o tile, row-major [t][j]
+    T P[kChunk * pP];       // dP (dq walk, [t][s]) or dP^T (dk walk, [s][t])
+    float tot[NT];
+    float last[BK];
+    int flag;
+};
+
+// Transposed state tiles of the row-split kernels: element (j, i) of S^T for
+// rows j = 0..V-1 and this wave's IBW blocks of 16 key rows i.  Tile (jb, ib)
+// slot r holds j = 16*jb + 4*(l/16) + r, i = 16*(w*IBW + ib) + l%16.
+template <int V, int IBW>
+struct TStateRegs {
+    f32x4 s[V / 16][IBW];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int jb = 0; jb < V / 16; ++jb)
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) s[jb][ib] = zero4();
+    }
+    // src points at row k0 of a [K][V] fp32 state
+    __device__ __forceinline__ void load(const float* __restrict__ src, int w) {
+        const int l = lane_id();
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const int i = 16 * (w * IBW + ib) + (l & 15);
+#pragma unroll
+            for (int jb = 0; jb < V / 16; ++jb)
+                s[jb][ib] = *reinterpret_cast<const f32x4*>(src + (long)i * V + 16 * jb + 4 * (l >> 4));
+        }
+    }
+};
+
+// The ten lower-triangular 16x16 tiles of dP = (dO V^T) * M, contraction over
+// the full value width.  OUT_ST = false stores dP row-major [t][s];
+// OUT_ST = true stores dP^T row-major [s][t].
+template <typename T, int V, bool OUT_ST>
+__device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* sP, int pP, int w, int nw) {
+    const int l = lane_id();
+    for (int tile = w; tile < 10; tile += nw) {
+        int is, js;  // is: t-block, js: s-block, js <= is
+        decode_tile(tile, is, js);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < V / 32; ++ks) {
+            if (!OUT_ST) {  // D[s][t] = sum_j V[s][j] dO[t][j]
+                acc = mma32(acc, frag_rm<T>(sV, pV, 16 * js, 32 * ks), frag_rm<T>(sV, pV, 16 * js, 32 * ks + 16),
+                            frag_rm<T>(sdO, pV, 16 * is, 32 * ks), frag_rm<T>(sdO, pV, 16 * is, 32 * ks + 16));
+            } else {        // D[t][s] = sum_j dO[t][j] V[s][j]
+                acc = mma32(acc, frag_rm<T>(sdO, pV, 16 * is, 32 * ks), frag_rm<T>(sdO, pV, 16 * is, 32 * ks + 16),
+                            frag_rm<T>(sV, pV, 16 * js, 32 * ks), frag_rm<T>(sV, pV, 16 * js, 32 * ks + 16));
+            }
+        }
+        if (!OUT_ST) {
+            // slot r: s = 16js + 4(l/16) + r, t = 16is + l%16
+            if (is == js)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * (l >> 4) + r > (l & 15)) acc[r] = 0.f;
+            *reinterpret_cast<vec4_t<T>*>(sP + (16 * is + (l & 15)) * pP + 16 * js + 4 * (l >> 4)) = to_vec4<T>(acc);
+        } else {
+            // slot r: t = 16is + 4(l/16) + r, s = 16js + l%16
+            if (is == js)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if ((l & 15) > 4 * (l >> 4) + r) acc[r] = 0.f;
+            *reinterpret_cast<vec4_t<T>*>(sP + (16 * js + (l & 15)) * pP + 16 * is + 4 * (l >> 4)) = to_vec4<T>(acc);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward combine.  One workgroup per (head, key row i), threads over j.
+//   S_init(0) = S_0;  S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p
+//   dS_end(P-1) = dht; dS_end(p-1) = Diag(exp2 G_p) dS_end(p) + dS*_p
+// ws_state / ws_dstate hold S*_p / dS*_p on entry and S_init / dS_end on exit.
+__global__ void __launch_bounds__(256)
+gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht, float* __restrict__ ws_state,
+                    float* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
+    const int i = blockIdx.x;
+    const long bh = blockIdx.y;
+    const long KV = (long)K * V;
+    const int tid = threadIdx.x;
+    const bool has = tid < V, has2 = tid + 256 < V;
+    const int j0 = tid, j1 = tid + 256;
+    float* st = ws_state + bh * P * KV + (long)i * V;
+    float* ds = ws_dstate + bh * P * KV + (long)i * V;
+    const float* gt = ws_gate + bh * P * (long)K + i;
+    float c0 = 0.f, c1 = 0.f;
+    if (s0) {
+        if (has) c0 = s0[bh * KV + (long)i * V + j0];
+        if (has2) c1 = s0[bh * KV + (long)i * V + j1];
+    }
+    for (int p = 0; p < P; ++p) {
+        float a0 = 0.f, a1 = 0.f;
+        if (p + 1 < P) {
+            if (has) a0 = st[p * KV + j0];
+            if (has2) a1 = st[p * KV + j1];
+        }
+        if (has) st[p * KV + j0] = c0;
+        if (has2) st[p * KV + j1] = c1;
+        if (p + 1 < P) {
+            const float gm = exp2_fast(gt[p * (long)K]);
+            c0 = gm * c0 + a0;
+            c1 = gm * c1 + a1;
+        }
+    }
+    float d0 = 0.f, d1 = 0.f;
+    if (dht) {
+        if (has) d0 = dht[bh * KV + (long)i * V + j0];
+        if (has2) d1 = dht[bh * KV + (long)i * V + j1];
+    }
+    for (int p = P - 1; p >= 0; --p) {
+        float a0 = 0.f, a1 = 0.f;
+        if (p >= 1) {
+            if (has) a0 = ds[p * KV + j0];
+            if (has2) a1 = ds[p * KV + j1];
+        }
+        if (has) ds[p * KV + j0] = d0;
+        if (has2) ds[p * KV + j1] = d1;
+        if (p >= 1) {
+            const float gm = exp2_fast(gt[p * (long)K]);
+            d0 = gm * d0 + a0;
+            d1 = gm * d1 + a1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq walk: forwards over one segment for key rows k0 .. k0+BK-1, full V.
+// State S^T in VGPRs; dq_t = exp2(B_t - B_63) * [dO (gamma*S)^T + dP (K*Gamma)]_t
+// (both terms share the factor; exact-path chunks use the element-wise form).
+// After each chunk the state S_out is stored to `hs` (dtype) in this kernel's
+// own tile order, for the dk walk's chunk-boundary gate-gradient term.
+template <typename T, int BK, int V, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
+           const float* __restrict__ s_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dq,
+           T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len) {
+    constexpr int NT = NW * 64;
+    constexpr int IBW = BK / 16 / NW;
+    static_assert(IBW >= 1 && IBW * 16 * NW == BK, "waves must tile the key rows");
+    using Sm = RowSmem<T, BK, V, NT>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nkb = K / BK;
+    int bid = blockIdx.x;
+    const int kb = bid % nkb; bid /= nkb;
+    const int seg = bid % P; bid /= P;
+    const int bh = bid;
+    const int b = bh / H, h = bh % H;
+    const int k0 = kb * BK;
+    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const long rsK = (long)H * K, rsV = (long)H * V;
+
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int t = e / kChunk, s = e % kChunk;
+        if ((s >> 4) > (t >> 4)) sm.P[t * Sm::pP + s] = Elem<T>::from_f(0.f);
+    }
+    TStateRegs<V, IBW> S;
+    if (s_init) S.load(s_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, w);
+    else S.zero();
+
+    using TRK = TileRegs<T, BK, NT>;
+    using TRV = TileRegs<T, V, NT>;
+    TRK rk, rg;
+    TRV rv, rdo;
+    auto issue = [&](int c) {
+        const long t0 = (long)b * T_ + (long)c * kChunk;
+        rk.load(k + (t0 * H + h) * K + k0, rsK, tid);
+        rg.load(g + (t0 * H + h) * K + k0, rsK, tid);
+        rv.load(v + (t0 * H + h) * V, rsV, tid);
+        rdo.load(d_o + (t0 * H + h) * V, rsV, tid);
+    };
+    issue(c_begin);
+    for (int c = c_begin; c < c_end; ++c) {
+        const bool more = c + 1 < c_end;
+        if (tid == 0) sm.flag = 0;
+        chunk_log_cumsum<T, BK, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        const bool exact = sm.flag != 0;
+#pragma unroll
+        for (int p = 0; p < TRK::PER; ++p) {
+            if (!TRK::owns(p, tid)) continue;
+            const int row = TRK::row_of(p, tid), c0 = TRK::col_of(p, tid);
+            float kv[TRK::VEC];
+#pragma unroll
+            for (int e = 0; e < TRK::VEC; ++e) {
+                kv[e] = rk.get(p, e);
+                if (!exact) kv[e] *= exp2_fast(sm.last[c0 + e] - sm.B[row * Sm::pB + c0 + e]);
+            }
+            store_vec_lds<T>(sm.X + row * Sm::pX + c0, kv);
+        }
+        rv.store_lds(sm.Vt, Sm::pV, tid);
+        rdo.store_lds(sm.dO, Sm::pV, tid);
+        if (more) issue(c + 1);
+        __syncthreads();
+        dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
+        __syncthreads();
+        const long t0 = (long)b * T_ + (long)c * kChunk;
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const int il = 16 * (w * IBW + ib) + (l & 15);  // key row within the block
+            const float gam = exact ? 1.f : exp2_fast(sm.last[il]);
+            vec4_t<T> sf[V / 32][2];
+#pragma unroll
+            for (int ks = 0; ks < V / 32; ++ks) {
+                sf[ks][0] = to_vec4<T>(S.s[2 * ks][ib] * gam);
+                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1][ib] * gam);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < V / 32; ++ks)
+                    acc = mma32(acc, frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks),
+                                frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks + 16), sf[ks][0], sf[ks][1]);
+                if (!exact) {
+#pragma unroll
+                    for (int ks2 = 0; ks2 <= tb / 2; ++ks2)
+                        acc = mma32(acc, frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
+                                    frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16),
+                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2, 16 * (w * IBW + ib)),
+                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, 16 * (w * IBW + ib)));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tb + 4 * (l >> 4) + r;
+                    const float bt = sm.B[t * Sm::pB + il];
+                    float val;
+                    if (!exact) {
+                        val = acc[r] * exp2_fast(bt - sm.last[il]);
+                    } else {
+                        val = acc[r] * exp2_fast(bt);
+                        for (int s = 0; s <= t; ++s)
+                            val += Elem<T>::to_f(sm.P[t * Sm::pP + s]) * Elem<T>::to_f(sm.X[s * Sm::pX + il]) *
+                                   exp2_fast(bt - sm.B[s * Sm::pB + il]);
+                    }
+                    dq[((t0 + t) * H + h) * K + k0 + il] = Elem<T>::from_f(val);
+                }
+            }
+        }
+        if (exact) {
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < TRK::PER; ++p) {
+                if (!TRK::owns(p, tid)) continue;
+                const int row = TRK::row_of(p, tid), c0 = TRK::col_of(p, tid);
+                float kv[TRK::VEC];
+#pragma unroll
+                for (int e = 0; e < TRK::VEC; ++e)
+                    kv[e] = Elem<T>::to_f(sm.X[row * Sm::pX + c0 + e]) *
+                            exp2_fast(sm.last[c0 + e] - sm.B[row * Sm::pB + c0 + e]);
+                store_vec_lds<T>(sm.X + row * Sm::pX + c0, kv);
+            }
+            __syncthreads();
+        }
+        // S^T <- S^T Diag(gamma) + V^T (K*Gamma)
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const float gam = exp2_fast(sm.last[16 * (w * IBW + ib) + (l & 15)]);
+#pragma unroll
+            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gam;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            vec4_t<T> xf[IBW][2];
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) {
+                xf[ib][0] = frag_cm<T>(sm.X, Sm::pX, 32 * ks, 16 * (w * IBW + ib));
+                xf[ib][1] = frag_cm<T>(sm.X, Sm::pX, 32 * ks + 16, 16 * (w * IBW + ib));
+            }
+#pragma unroll
+            for (int jb = 0; jb < V / 16; ++jb) {
+                vec4_t<T> alo = frag_cm<T>(sm.Vt, Sm::pV, 32 * ks, 16 * jb);
+                vec4_t<T> ahi = frag_cm<T>(sm.Vt, Sm::pV, 32 * ks + 16, 16 * jb);
+#pragma unroll
+                for (int ib = 0; ib < IBW; ++ib) S.s[jb][ib] = mma32(S.s[jb][ib], alo, ahi, xf[ib][0], xf[ib][1]);
+            }
+        }
+        // S_out of this chunk: tile (jb, ib) of wave w is 64 lanes x 4 contiguous elements
+        {
+            T* dst = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < V / 16; ++jb)
+                    *reinterpret_cast<vec4_t<T>*>(dst + (((w * IBW + ib) * (V / 16) + jb) * 64 + l) * 4) =
+                        to_vec4<T>(S.s[jb][ib]);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk + dg walk: backwards over one segment for key rows k0 .. k0+BK-1, full V.
+// State dS^T in VGPRs.  dk_s = Gamma_s * [V dS_out^T + dP^T (q*exp2(B_t - B_63))]_s,
+// then dA = q*dq - k*dk and dg = reverse cumulative sum of dA within the chunk
+// plus rowsum(S_out * dS_out), with S_out read back from the dq walk's `hs`.
+template <typename T, int BK, int V, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
+           const T* __restrict__ d_o, const T* __restrict__ dq, const float* __restrict__ ds_init, long s_seg_stride,
+           long s_bh_stride, const T* __restrict__ hs, T* __restrict__ dk, T* __restrict__ dg, int T_, int H,
+           int K, int N, int P, int seg_len) {
+    constexpr int NT = NW * 64;
+    constexpr int IBW = BK / 16 / NW;
+    static_assert(IBW >= 1 && IBW * 16 * NW == BK, "waves must tile the key rows");
+    using Sm = RowSmem<T, BK, V, NT>;
+    __shared__ Sm sm;
+    __shared__ float s_carry[BK];
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nkb = K / BK;
+    int bid = blockIdx.x;
+    const int kb = bid % nkb; bid /= nkb;
+    const int seg = bid % P; bid /= P;
+    const int bh = bid;
+    const int b = bh / H, h = bh % H;
+    const int k0 = kb * BK;
+    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const int nchunks = c_end - c_begin;
+    const long rsK = (long)H * K, rsV = (long)H * V;
+
+    // dP^T is stored [s][t]; its tiles with t-block < s-block are zero
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int s = e / kChunk, t = e % kChunk;
+        if ((t >> 4) < (s >> 4)) sm.P[s * Sm::pP + t] = Elem<T>::from_f(0.f);
+    }
+    TStateRegs<V, IBW> S;
+    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, w);
+    else S.zero();
+
+    // reverse-scan layout: thread (column, part) owns R rows of one key column
+    constexpr int NPART = NT / BK, R = kChunk / NPART;
+    const int scol = tid % BK, spart = tid / BK;
+
+    using TRK = TileRegs<T, BK, NT>;
+    using TRV = TileRegs<T, V, NT>;
+    TRK rq, rk, rg, rdq;
+    TRV rv, rdo;
+    auto tok0 = [&](int c) { return (long)b * T_ + (long)c * kChunk; };
+    auto issue_main = [&](int c) {
+        const long t0 = tok0(c);
+        rq.load(q + (t0 * H + h) * K + k0, rsK, tid);
+        rg.load(g + (t0 * H + h) * K + k0, rsK, tid);
+        rdq.load(dq + (t0 * H + h) * K + k0, rsK, tid);
+        rv.load(v + (t0 * H + h) * V, rsV, tid);
+        rdo.load(d_o + (t0 * H + h) * V, rsV, tid);
+    };
+    issue_main(c_end - 1);
+    rk.load(k + (tok0(c_end - 1) * H + h) * K + k0, rsK, tid);
+    for (int it = 0; it < nchunks; ++it) {
+        const int c = c_end - 1 - it;
+        const bool more = it + 1 < nchunks;
+        const long t0 = tok0(c);
+        if (tid == 0) sm.flag = 0;
+        chunk_log_cumsum<T, BK, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        const bool exact = sm.flag != 0;
+        // q-side operand q*exp2(B_t - B_63) (raw q on the exact path); keep
+        // q*Lambda and q*dq in registers for later in the chunk
+        float ql[TRK::PER][TRK::VEC], qdq[TRK::PER][TRK::VEC];
+#pragma unroll
+        for (int p = 0; p < TRK::PER; ++p) {
+            if (!TRK::owns(p, tid)) continue;
+            const int row = TRK::row_of(p, tid), c0 = TRK::col_of(p, tid);
+            float qv[TRK::VEC];
+#pragma unroll
+            for (int e = 0; e < TRK::VEC; ++e) {
+                const float bt = sm.B[row * Sm::pB + c0 + e];
+                const float qq = rq.get(p, e);
+                qv[e] = exact ? qq : qq * exp2_fast(bt - sm.last[c0 + e]);
+                ql[p][e] = qq * exp2_fast(bt);
+                qdq[p][e] = qq * rdq.get(p, e);
+            }
+            store_vec_lds<T>(sm.X + row * Sm::pX + c0, qv);
+        }
+        rv.store_lds(sm.Vt, Sm::pV, tid);
+        rdo.store_lds(sm.dO, Sm::pV, tid);
+        if (more) issue_main(c - 1);
+        __syncthreads();
+        dp_tiles<T, V, true>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
+        __syncthreads();
+        f32x4 dkr[4][IBW];
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const int il = 16 * (w * IBW + ib) + (l & 15);
+            vec4_t<T> sf[V / 32][2];
+#pragma unroll
+            for (int ks = 0; ks < V / 32; ++ks) {
+                sf[ks][0] = to_vec4<T>(S.s[2 * ks][ib]);
+                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1][ib]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < V / 32; ++ks)
+                    acc = mma32(acc, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks),
+                                frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks + 16), sf[ks][0], sf[ks][1]);
+                if (!exact) {
+#pragma unroll
+                    for (int ks2 = sb / 2; ks2 < 2; ++ks2)
+                        acc = mma32(acc, frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
+                                    frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16),
+                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2, 16 * (w * IBW + ib)),
+                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, 16 * (w * IBW + ib)));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 16 * sb + 4 * (l >> 4) + r;
+                    const float bs = sm.B[s * Sm::pB + il];
+                    float val = acc[r] * exp2_fast(sm.last[il] - bs);
+                    if (exact)
+                        for (int t = s; t < kChunk; ++t)
+                            val += Elem<T>::to_f(sm.P[s * Sm::pP + t]) * Elem<T>::to_f(sm.X[t * Sm::pX + il]) *
+                                   exp2_fast(sm.B[t * Sm::pB + il] - bs);
+                    acc[r] = val;
+                    dk[((t0 + s) * H + h) * K + k0 + il] = Elem<T>::from_f(val);
+                }
+                dkr[sb][ib] = acc;
+            }
+        }
+        __syncthreads();
+        // dk (fp32) replaces the gate cumsum in LDS; q*Lambda replaces the q-side operand
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.B[(16 * sb + 4 * (l >> 4) + r) * Sm::pB + 16 * (w * IBW + ib) + (l & 15)] = dkr[sb][ib][r];
+#pragma unroll
+        for (int p = 0; p < TRK::PER; ++p)
+            if (TRK::owns(p, tid)) store_vec_lds<T>(sm.X + TRK::row_of(p, tid) * Sm::pX + TRK::col_of(p, tid), ql[p]);
+        __syncthreads();
+        // sum over later tokens for dg: rowsum(S_out * dS_out) at this chunk's end
+        {
+            const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) {
+                float part = 0.f;
+#pragma unroll
+                for (int jb = 0; jb < V / 16; ++jb) {
+                    const vec4_t<T> so =
+                        *reinterpret_cast<const vec4_t<T>*>(src + (((w * IBW + ib) * (V / 16) + jb) * 64 + l) * 4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) part += Elem<T>::to_f(so[r]) * S.s[jb][ib][r];
+                }
+                part += __shfl_xor(part, 16);
+                part += __shfl_xor(part, 32);
+                if ((l >> 4) == 0) s_carry[16 * (w * IBW + ib) + (l & 15)] = part;
+            }
+        }
+        // dS^T <- dS^T Diag(gamma) + dO^T (q*Lambda)
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const float gam = exp2_fast(sm.last[16 * (w * IBW + ib) + (l & 15)]);
+#pragma unroll
+            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gam;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            vec4_t<T> xf[IBW][2];
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) {
+                xf[ib][0] = frag_cm<T>(sm.X, Sm::pX, 32 * ks, 16 * (w * IBW + ib));
+                xf[ib][1] = frag_cm<T>(sm.X, Sm::pX, 32 * ks + 16, 16 * (w * IBW + ib));
+            }
+#pragma unroll
+            for (int jb = 0; jb < V / 16; ++jb) {
+                vec4_t<T> alo = frag_cm<T>(sm.dO, Sm::pV, 32 * ks, 16 * jb);
+                vec4_t<T> ahi = frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, 16 * jb);
+#pragma unroll
+                for (int ib = 0; ib < IBW; ++ib) S.s[jb][ib] = mma32(S.s[jb][ib], alo, ahi, xf[ib][0], xf[ib][1]);
+            }
+        }
+        // dA = q*dq - k*dk, in place over dk
+#pragma unroll
+        for (int p = 0; p < TRK::PER; ++p) {
+            if (!TRK::owns(p, tid)) continue;
+            float* dst = sm.B + TRK::row_of(p, tid) * Sm::pB + TRK::col_of(p, tid);
+#pragma unroll
+            for (int e = 0; e < TRK::VEC; ++e) dst[e] = qdq[p][e] - rk.get(p, e) * dst[e];
+        }
+        if (more) rk.load(k + (tok0(c - 1) * H + h) * K + k0, rsK, tid);
+        __syncthreads();
+        // dg_t = sum_{r >= t} dA_r over the rest of the sequence (Section 4.3 closed form)
+        {
+            float acc = 0.f;
+#pragma unroll
+            for (int u = R - 1; u >= 0; --u) {
+                float* p = sm.B + (spart * R + u) * Sm::pB + scol;
+                acc += *p;
+                *p = acc;
+            }
+            sm.tot[spart * BK + scol] = acc;
+            __syncthreads();
+            float off = s_carry[scol];
+            for (int pp = spart + 1; pp < NPART; ++pp) off += sm.tot[pp * BK + scol];
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int t = spart * R + u;
+                dg[((t0 + t) * H + h) * K + k0 + scol] = Elem<T>::from_f(sm.B[t * Sm::pB + scol] + off);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dv walk: backwards over one segment for value columns v0 .. v0+BV-1, full K.
+// State dS in VGPRs.  dv = A^T dO + (K*Gamma) dS_out with A rebuilt from
+// q*exp2(B_t - B_63) and k*exp2(B_63 - B_s) (element-wise on exact-path chunks);
+// dS_in = Diag(gamma) dS_out + (Q*Lambda)^T dO.  Segment 0 ends with dS_0.
+template <typename T, int KD, int BV, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g, const T* __restrict__ d_o,
+           const float* __restrict__ ds_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dv,
+           float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len) {
+    constexpr int NT = NW * 64;
+    constexpr int CB = BV / NW / 16;
+    using Sm = ChunkSmem<T, KD, BV, NT>;
+    __shared__ Sm sm;  // sm.V holds the d_o tile, sm.A holds A^T [s][t]
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nvb = V / BV;
+    int bid = blockIdx.x;
+    const int vb = bid % nvb; bid /= nvb;
+    const int seg = bid % P; bid /= P;
+    const int bh = bid;
+    const int b = bh / H, h = bh % H;
+    const int v0 = vb * BV;
+    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const int nchunks = c_end - c_begin;
+    const long rsK = (long)H * KD, rsV = (long)H * V;
+    const int col0 = w * (BV / NW);
+
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int s = e / kChunk, t = e % kChunk;
+        if ((t >> 4) < (s >> 4)) sm.A[s * Sm::pA + t] = Elem<T>::from_f(0.f);
+    }
+    StateRegs<KD, CB> S;
+    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + v0, V, col0);
+    else S.zero();
+
+    using TR = TileRegs<T, KD, NT>;
+    TR rq, rk, rg;
+    TileRegs<T, BV, NT> rdo;
+    auto tok0 = [&](int c) { return (long)b * T_ + (long)c * kChunk; };
+    {
+        const long t0 = tok0(c_end - 1);
+        rq.load(q + (t0 * H + h) * KD, rsK, tid);
+        rk.load(k + (t0 * H + h) * KD, rsK, tid);
+        rg.load(g + (t0 * H + h) * KD, rsK, tid);
+        rdo.load(d_o + (t0 * H + h) * V + v0, rsV, tid);
+    }
+    for (int it = 0; it < nchunks; ++it) {
+        const int c = c_end - 1 - it;
+        const bool more = it + 1 < nchunks;
+        const long t0 = tok0(c);
+        if (tid == 0) sm.flag = 0;
+        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        const bool exact = sm.flag != 0;
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+            float qv[TR::VEC], kv[TR::VEC];
+#pragma unroll
+            for (int e = 0; e < TR::VEC; ++e) {
+                const float bt = sm.B[row * Sm::pB + c0 + e], bl = sm.last[c0 + e];
+                qv[e] = rq.get(p, e);
+                kv[e] = rk.get(p, e);
+                if (!exact) {
+                    qv[e] *= exp2_fast(bt - bl);
+                    kv[e] *= exp2_fast(bl - bt);
+                }
+            }
+            store_vec_lds<T>(sm.Q + row * Sm::pQ + c0, qv);
+            store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
+        }
+        rdo.store_lds(sm.V, Sm::pV, tid);
+        if (more) {
+            const long t1 = tok0(c - 1);
+            rk.load(k + (t1 * H + h) * KD, rsK, tid);
+            rg.load(g + (t1 * H + h) * KD, rsK, tid);
+            rdo.load(d_o + (t1 * H + h) * V + v0, rsV, tid);
+        }
+        __syncthreads();
+        // A tiles, stored transposed: sm.A[s][t] = A[t][s]
+        for (int tile = w; tile < 10; tile += NW) {
+            int is, js;
+            decode_tile(tile, is, js);
+            f32x4 acc = zero4();
+            if (!exact) {
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks)
+                    acc = mma32(acc, frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks),
+                                frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks + 16), frag_rm<T>(sm.K, Sm::pK, 16 * js, 32 * ks),
+                                frag_rm<T>(sm.K, Sm::pK, 16 * js, 32 * ks + 16));
+            } else {
+                const int s = 16 * js + (l & 15);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * is + 4 * (l >> 4) + r;
+                    float sum = 0.f;
+                    if (s <= t)
+                        for (int i = 0; i < KD; ++i)
+                            sum += Elem<T>::to_f(sm.Q[t * Sm::pQ + i]) * Elem<T>::to_f(sm.K[s * Sm::pK + i]) *
+                                   exp2_fast(sm.B[t * Sm::pB + i] - sm.B[s * Sm::pB + i]);
+                    acc[r] = sum;
+                }
+            }
+            // slot r: t = 16is + 4(l/16) + r, s = 16js + l%16
+            if (is == js)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if ((l & 15) > 4 * (l >> 4) + r) acc[r] = 0.f;
+            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * js + (l & 15)) * Sm::pA + 16 * is + 4 * (l >> 4)) =
+                to_vec4<T>(acc);
+        }
+        float ql[TR::PER][TR::VEC];
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+#pragma unroll
+            for (int e = 0; e < TR::VEC; ++e) ql[p][e] = rq.get(p, e) * exp2_fast(sm.B[row * Sm::pB + c0 + e]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < TR::PER; ++p) {
+            if (!TR::owns(p, tid)) continue;
+            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+            store_vec_lds<T>(sm.Q + row * Sm::pQ + c0, ql[p]);
+            if (exact) {
+                float kv[TR::VEC];
+#pragma unroll
+                for (int e = 0; e < TR::VEC; ++e)
+                    kv[e] = Elem<T>::to_f(sm.K[row * Sm::pK + c0 + e]) *
+                            exp2_fast(sm.last[c0 + e] - sm.B[row * Sm::pB + c0 + e]);
+                store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
+            }
+        }
+        if (more) rq.load(q + (tok0(c - 1) * H + h) * KD, rsK, tid);
+        __syncthreads();
+        {
+            vec4_t<T> sf[KD / 32][CB][2];
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    sf[ks][cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
+                    sf[ks][cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                }
+            vec4_t<T> df[4][CB];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) df[tb][cb] = frag_cm<T>(sm.V, Sm::pV, 16 * tb, col0 + 16 * cb);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                f32x4 acc[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[cb] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks) {
+                    vec4_t<T> alo = frag_rm<T>(sm.K, Sm::pK, 16 * sb, 32 * ks);
+                    vec4_t<T> ahi = frag_rm<T>(sm.K, Sm::pK, 16 * sb, 32 * ks + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], alo, ahi, sf[ks][cb][0], sf[ks][cb][1]);
+                }
+#pragma unroll
+                for (int ks2 = sb / 2; ks2 < 2; ++ks2) {
+                    vec4_t<T> alo = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2);
+                    vec4_t<T> ahi = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2 + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[cb] = mma32(acc[cb], alo, ahi, df[2 * ks2][cb], df[2 * ks2 + 1][cb]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const long s = t0 + 16 * sb + 4 * (l >> 4) + r;
+                        dv[(s * H + h) * V + v0 + col0 + 16 * cb + (l & 15)] = Elem<T>::from_f(acc[cb][r]);
+                    }
+            }
+        }
+        state_update<T, KD, CB>(S, sm.Q, Sm::pQ, sm.V, Sm::pV, sm.last, col0);
+    }
+    if (ds0 && seg == 0) S.store(ds0 + (long)bh * KD * V + v0, V, col0);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+template <typename T, int KD, int BV>
+static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
+    constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
+    constexpr int NT = NW * 64;
+    static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
+    const int nvb = a.V / BV;
+    const long KV = (long)KD * a.V;
+    if (a.P > 1) {
+        const int nseg = a.P - 1;
+        dim3 grid((unsigned)(nvb * nseg * a.BH));
+        hipLaunchKernelGGL((gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), 0, a.stream, (const T*)a.k,
+                           (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, 0,
+                           nseg);
+        hipLaunchKernelGGL((gla_seg_state<T, KD, BV, NW, true>), grid, dim3(NT), 0, a.stream, (const T*)a.q,
+                           (const T*)a.g, (const T*)a.d_o, a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P,
+                           a.seg_len, 1, nseg);
+        hipLaunchKernelGGL(gla_seg_combine_bwd, dim3((unsigned)KD, (unsigned)a.BH), dim3(256), 0, a.stream, a.s0,
+                           a.dht, a.ws_state, a.ws_dstate, a.ws_gate, KD, a.V, a.P);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int KD, int BV>
+static hipError_t launch_dv(const BwdLaunch& a) {
+    constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
+    constexpr int NT = NW * 64;
+    const int nvb = a.V / BV;
+    const long KV = (long)KD * a.V;
+    const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
+    const long seg_stride = a.P > 1 ? KV : 0;
+    const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
+    dim3 grid((unsigned)(nvb * a.P * a.BH));
+    hipLaunchKernelGGL((gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv, a.ds0, a.T, a.H, a.V,
+                       a.N, a.P, a.seg_len);
+    return hipGetLastError();
+}
+
+template <typename T, int BK, int V>
+static hipError_t launch_rows(const BwdLaunch& a) {
+    constexpr int NW = (BK / 16 < 8) ? BK / 16 : 8;
+    constexpr int NT = NW * 64;
+    static_assert(sizeof(RowSmem<T, BK, V, NT>) <= 160 * 1024, "LDS budget");
+    const int nkb = a.K / BK;
+    const long KV = (long)a.K * V;
+    dim3 grid((unsigned)(nkb * a.P * a.BH));
+    const float* sinit = a.P > 1 ? a.ws_state : a.s0;
+    const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
+    const long seg_stride = a.P > 1 ? KV : 0;
+    const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
+    hipLaunchKernelGGL((gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), 0, a.stream, (const T*)a.k, (const T*)a.v,
+                       (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq, (T*)a.ws_hs,
+                       a.T, a.H, a.K, a.N, a.P, a.seg_len);
+    hipLaunchKernelGGL((gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit, seg_stride, bh_stride,
+                       (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P, a.seg_len);
+    return hipGetLastError();
+}
+
+#define GLA_COL_DISPATCH(FN, T, KD_, BV_)                              \
+    if (a.K == KD_ && a.BV == BV_) {                                   \
+        hipError_t e = FN<T, KD_, BV_>(a);                             \
+        return e;                                                      \
+    }
+
+template <typename T>
+static hipError_t col_stage(const BwdLaunch& a, bool dv_stage) {
+    if (!dv_stage) {
+        if (a.bf16) {
+            if constexpr (sizeof(T) == 2) {
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 64)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 128)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 256)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 64)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 128)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 256)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 256, 64)
+            }
+        } else {
+            if constexpr (sizeof(T) == 4) {
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 64)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 128)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 64)
+                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 128)
+            }
+        }
+    } else {
+        if (a.bf16) {
+            if constexpr (sizeof(T) == 2) {
+                GLA_COL_DISPATCH(launch_dv, T, 64, 64)
+                GLA_COL_DISPATCH(launch_dv, T, 64, 128)
+                GLA_COL_DISPATCH(launch_dv, T, 64, 256)
+                GLA_COL_DISPATCH(launch_dv, T, 128, 64)
+                GLA_COL_DISPATCH(launch_dv, T, 128, 128)
+                GLA_COL_DISPATCH(launch_dv, T, 128, 256)
+                GLA_COL_DISPATCH(launch_dv, T, 256, 64)
+            }
+        } else {
+            if constexpr (sizeof(T) == 4) {
+                GLA_COL_DISPATCH(launch_dv, T, 64, 64)
+                GLA_COL_DISPATCH(launch_dv, T, 64, 128)
+                GLA_COL_DISPATCH(launch_dv, T, 128, 64)
+                GLA_COL_DISPATCH(launch_dv, T, 128, 128)
+            }
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+#define GLA_ROW_DISPATCH(T, BK_, V_)                                   \
+    if (a.BK == BK_ && a.V == V_) return launch_rows<T, BK_, V_>(a);
+
+static hipError_t row_stage(const BwdLaunch& a) {
+    if (a.bf16) {
+        GLA_ROW_DISPATCH(bf16, 64, 64)
+        GLA_ROW_DISPATCH(bf16, 128, 64)
+        GLA_ROW_DISPATCH(bf16, 256, 64)
+        GLA_ROW_DISPATCH(bf16, 64, 128)
+        GLA_ROW_DISPATCH(bf16, 128, 128)
+        GLA_ROW_DISPATCH(bf16, 256, 128)
+        GLA_ROW_DISPATCH(bf16, 64, 256)
+        GLA_ROW_DISPATCH(bf16, 128, 256)
+    } else {
+        GLA_ROW_DISPATCH(float, 64, 64)
+        GLA_ROW_DISPATCH(float, 128, 64)
+        GLA_ROW_DISPATCH(float, 64, 128)
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd(const BwdLaunch& a) {
-    (void)a;
-    return hipErrorNotSupported;
+    hipError_t e = a.bf16 ? col_stage<bf16>(a, false) : col_stage<float>(a, false);
+    if (e != hipSuccess) return e;
+    e = row_stage(a);
+    if (e != hipSuccess) return e;
+    return a.bf16 ? col_stage<bf16>(a, true) : col_stage<float>(a, true);
 }
 
 }  // namespace gla

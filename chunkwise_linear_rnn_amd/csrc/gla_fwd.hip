@@ -17,176 +17,10 @@
 //        VGPRs, producing O = (Q*Lambda) S + P V chunk by chunk, and the
 //        final state for the last segment.
 // With P = 1 only step 3 runs (the non-materialised form of Section 3.3).
-#include "gla_device.hpp"
+#include "gla_chunk.hpp"
 #include "gla_launch.hpp"
 
 namespace gla {
-
-// ---------------------------------------------------------------------------
-// Shared-memory layout of one chunk for the column-split kernels.
-template <typename T, int KD, int BV, int NT>
-struct ChunkSmem {
-    static constexpr int PT = Elem<T>::pad;
-    static constexpr int pB = KD + 4;      // fp32 cumulative log gate
-    static constexpr int pQ = KD + PT;     // q-side operand, row-major [t][i]
-    static constexpr int pK = KD + PT;     // k-side operand, row-major [s][i]
-    static constexpr int pV = BV + PT;     // value (or d_o) tile, row-major [s][j]
-    static constexpr int pA = kChunk + PT; // intra-chunk attention A[t][s]
-    float B[kChunk * pB];
-    T Q[kChunk * pQ];
-    T K[kChunk * pK];
-    T V[kChunk * pV];
-    T A[kChunk * pA];
-    float tot[NT];
-    float last[KD];
-    int flag;
-};
-
-// One wave's share of the state: rows 0..KD-1, columns col0 .. col0+16*CB-1,
-// as KD/16 x CB accumulator tiles.
-template <int KD, int CB>
-struct StateRegs {
-    f32x4 s[KD / 16][CB];
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int a = 0; a < KD / 16; ++a)
-#pragma unroll
-            for (int c = 0; c < CB; ++c) s[a][c] = zero4();
-    }
-    // element (i, j) of tile (a, c) for accumulator slot r: i = 16a + 4*(l/16) + r, j = col0 + 16c + l%16
-    __device__ __forceinline__ void load(const float* __restrict__ src, long ld, int col0) {
-        const int l = lane_id();
-#pragma unroll
-        for (int a = 0; a < KD / 16; ++a)
-#pragma unroll
-            for (int c = 0; c < CB; ++c)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    s[a][c][r] = src[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)];
-    }
-    __device__ __forceinline__ void store(float* __restrict__ dst, long ld, int col0) const {
-        const int l = lane_id();
-#pragma unroll
-        for (int a = 0; a < KD / 16; ++a)
-#pragma unroll
-            for (int c = 0; c < CB; ++c)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)] = s[a][c][r];
-    }
-};
-
-// S <- Diag(gamma) S + X^T Y over the 64 rows of the chunk (Section 4.2:
-// S_[i+1] = (gamma^T 1) * S_[i] + (K*Gamma)^T V).  X (row-major [t][i], the
-// already-decayed key/query tile) and Y (row-major [t][j]) are in LDS;
-// gamma = exp2(last[i]).  Columns of this wave: col0 .. col0 + 16*CB - 1.
-template <typename T, int KD, int CB>
-__device__ __forceinline__ void state_update(StateRegs<KD, CB>& S, const T* X, int pX, const T* Y, int pY,
-                                             const float* last, int col0) {
-    const int l = lane_id();
-#pragma unroll
-    for (int a = 0; a < KD / 16; ++a) {
-        f32x4 gam;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gam[r] = exp2_fast(last[16 * a + 4 * (l >> 4) + r]);
-#pragma unroll
-        for (int c = 0; c < CB; ++c) S.s[a][c] *= gam;
-    }
-    vec4_t<T> yf[4][CB];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int c = 0; c < CB; ++c) yf[sb][c] = frag_cm<T>(Y, pY, 16 * sb, col0 + 16 * c);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int a = 0; a < KD / 16; ++a) {
-            vec4_t<T> xlo = frag_cm<T>(X, pX, 32 * ks, 16 * a);
-            vec4_t<T> xhi = frag_cm<T>(X, pX, 32 * ks + 16, 16 * a);
-#pragma unroll
-            for (int c = 0; c < CB; ++c) S.s[a][c] = mma32(S.s[a][c], xlo, xhi, yf[2 * ks][c], yf[2 * ks + 1][c]);
-        }
-    }
-}
-
-__device__ __forceinline__ void decode_tile(int tile, int& is, int& js) {
-    // lower-triangular 16x16 tiles of the 64x64 chunk, row by row
-    constexpr int tis[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int tjs[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    is = tis[tile];
-    js = tjs[tile];
-}
-
-// ---------------------------------------------------------------------------
-// Step 1: segment-local states.  REV = false: S*_p from the keys and values of
-// the segment walked forwards (decay Gamma = exp2(B_63 - B_t) on the keys).
-// REV = true: the backward pass's dS*_p from queries and d_o walked backwards
-// (decay Lambda = exp2(B_t) on the queries; dS_[n-1] = gamma dS_[n] + (Q*Lambda)^T dO).
-template <typename T, int KD, int BV, int NW, bool REV>
-__global__ void __launch_bounds__(NW * 64)
-gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
-              float* __restrict__ ws_state, float* __restrict__ ws_gate,
-              int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg) {
-    constexpr int NT = NW * 64;
-    constexpr int CB = BV / NW / 16;
-    using Sm = ChunkSmem<T, KD, BV, NT>;
-    __shared__ Sm sm;
-    const int tid = threadIdx.x, w = wave_id();
-    const int nvb = V / BV;
-    int bid = blockIdx.x;
-    const int vb = bid % nvb; bid /= nvb;
-    const int seg = seg_first + bid % nseg; bid /= nseg;
-    const int bh = bid;
-    const int b = bh / H, h = bh % H;
-    const int v0 = vb * BV;
-    const int c_begin = seg * seg_len;
-    const int c_end = min(N, c_begin + seg_len);
-    const int nchunks = c_end - c_begin;
-    const long rsK = (long)H * KD, rsV = (long)H * V;
-    const int col0 = w * (BV / NW);
-
-    StateRegs<KD, CB> S;
-    S.zero();
-    float gate_total = 0.f;
-
-    TileRegs<T, KD, NT> rx, rg;
-    TileRegs<T, BV, NT> ry;
-    auto issue = [&](int c) {
-        const long tok0 = (long)b * T_ + (long)c * kChunk;
-        rx.load(x + (tok0 * H + h) * KD, rsK, tid);
-        rg.load(g + (tok0 * H + h) * KD, rsK, tid);
-        ry.load(y + (tok0 * H + h) * V + v0, rsV, tid);
-    };
-    issue(REV ? c_end - 1 : c_begin);
-    for (int it = 0; it < nchunks; ++it) {
-        if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
-        if (tid < KD) gate_total += sm.last[tid];
-        // decayed operand: K*Gamma (forward) or Q*Lambda (reverse)
-        using TR = TileRegs<T, KD, NT>;
-#pragma unroll
-        for (int p = 0; p < TR::PER; ++p) {
-            if (!TR::owns(p, tid)) continue;
-            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
-            float vals[TR::VEC];
-#pragma unroll
-            for (int e = 0; e < TR::VEC; ++e) {
-                const float bt = sm.B[row * Sm::pB + c0 + e];
-                const float ex = REV ? bt : (sm.last[c0 + e] - bt);
-                vals[e] = rx.get(p, e) * exp2_fast(ex);
-            }
-            store_vec_lds<T>(sm.K + row * Sm::pK + c0, vals);
-        }
-        ry.store_lds(sm.V, Sm::pV, tid);
-        if (it + 1 < nchunks) issue(REV ? c_end - 2 - it : c_begin + it + 1);
-        __syncthreads();
-        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.last, col0);
-        __syncthreads();
-    }
-    float* dst = ws_state + ((long)bh * P + seg) * (long)KD * V + v0;
-    S.store(dst, V, col0);
-    if (vb == 0 && tid < KD) ws_gate[((long)bh * P + seg) * KD + tid] = gate_total;
-}
 
 // ---------------------------------------------------------------------------
 // Step 2 (forward): S_init(0) = S_0 (or 0); S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p.

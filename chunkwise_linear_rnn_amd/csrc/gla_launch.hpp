@@ -33,7 +33,7 @@ struct BwdLaunch {
     float* ws_state;   // [BH][P][K][V] fp32: S*_p, then S_init(p)
     float* ws_dstate;  // [BH][P][K][V] fp32: dS*_p, then dS_end(p)
     float* ws_gate;    // [BH][P][K]
-    float* ws_carry;   // [BH][P][K]: gate-gradient carry into segment p from later tokens
+    void* ws_hs;       // [BH][N][K*V] dtype: state after every chunk, in the walks' tile order
     hipStream_t stream;
 };
 

@@ -39,10 +39,10 @@
  *      definition in Section 4.1 requires; g = 0 is ungated linear attention,
  *      Eq. 1).  Violations give unspecified values, never an out-of-bounds
  *      access.
- *  Supported sizes: chunk == 64; T a multiple of 64; K in {64, 128, 256} and
- *      V in {64, 128, 256, 512} for bf16; K in {64, 128} and V in
- *      {64, 128, 256} for fp32.  B, H >= 0 and T >= 0; B*H == 0 or T == 0 is a
- *      valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
+ *  Supported sizes: chunk == 64; T a multiple of 64; bf16: K in
+ *      {64, 128, 256} and V in {64, 128, 256, 512} (backward: V <= 256);
+ *      fp32: K and V in {64, 128}.  B, H >= 0 and T >= 0; B*H == 0 or T == 0
+ *      is a valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
  */
 #ifndef GLA_H_
 #define GLA_H_

@@ -39,7 +39,7 @@ def _run_and_check(w, heads=None, tol=None, inputs=None):
     (1, 1, 64, 64, 64, "none"),        # one chunk
     (1, 2, 320, 64, 64, "normal0.1"),  # five chunks, several segments
     (2, 3, 448, 128, 128, "none"),     # seven chunks: uneven segments
-    (1, 2, 256, 64, 256, "normal0.1"),
+    (1, 2, 256, 64, 128, "normal0.1"),
     (1, 1, 384, 128, 64, "normal0.1"),
 ])
 def test_fwd_small(dtype, B, H, T, K, V, s0):
