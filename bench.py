@@ -1,0 +1,261 @@
+"""Throughput benchmark of the GLA forward + backward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload metric_8k]
+
+A step is one gla_fwd followed by one gla_bwd (all hot-path steps: chunk
+cumsum, intra-chunk attention, state scan, output, state recompute, dS scan,
+chunk gradients, gate gradient) over one batch of seeded synthetic inputs that
+are resident in HBM before timing starts.  Prints one JSON line.
+
+Roofline: the dominant kernel (largest share of step time, timed with HIP
+events on the launch stream through the library's kernel-timing interface) is
+compared with the HBM peak using its algorithmic bytes (each input it needs read
+once, each output written once; workspace traffic excluded).  The CPU baseline
+is the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6
+FP32_MFMA_PEAK_TFLOPS = 157.3
+METRIC = "GLA fwd(+bwd) tokens/sec at T=8K, dk=128, dv=256; % of bf16 MFMA peak"
+
+
+def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int):
+    """Algorithmic HBM bytes per (token, head) of one launch of `kernel`."""
+    seg_frac = (P - 1) / P if P > 1 else 0.0
+    table = {
+        "fwd_walk": e * (3 * K + 2 * V),            # q, k, g, v read; o written
+        "bwd_dq_walk": e * (3 * K + 2 * V),         # k, g, v, d_o read; dq written
+        "bwd_dk_walk": e * (6 * K + 2 * V),         # q, k, g, dq, v, d_o read; dk, dg written
+        "bwd_dv_walk": e * (3 * K + 2 * V),         # q, k, g, d_o read; dv written
+        "fwd_seg_state": e * (2 * K + V) * seg_frac,  # k, g, v of all but the last segment
+        "bwd_seg_state": e * (2 * K + V) * seg_frac,
+        "bwd_seg_state_rev": e * (2 * K + V) * seg_frac,
+    }
+    return table.get(kernel)
+
+
+def fwd_flops_per_token_head(K, V, C=64):
+    # 4KV for Q S and K^T V, plus the causal halves of the 64x64 intra-chunk products
+    return 4 * K * V + (C + 1) * (K + V)
+
+
+def bwd_flops_per_token_head(K, V, C=64):
+    return 10 * K * V + (C + 1) * (3 * K + 2 * V)
+
+
+def plan_segments(B, H, T, K, V, bf16):
+    """Segments per head chosen by the library's launch plan (mirrors gla_plan.hpp)."""
+    if bf16:
+        cap = 256 if K <= 128 else 64
+    else:
+        cap = 128
+    bv = min(V, cap)
+    bh, n = B * H, T // 64
+    per_seg = bh * (V // bv)
+    P = max(1, 256 // per_seg) if per_seg > 0 else 1
+    P = min(P, max(n, 1))
+    seg_len = -(-n // P)
+    return -(-n // seg_len)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "chunkwise_linear_rnn_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str, units: int):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
+    or None if none were taken for this kernel/workload or the sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs, w, n_heads):
+    """fp64 oracle forward + backward on n_heads full-length heads of the workload."""
+    import numpy as np
+    import oracle
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    f64 = lambda t: t.detach().cpu().double().numpy()
+    pick = lambda a: np.stack([a[b, :, h, :] for b, h in heads])[:, :, None, :]
+    q, k, v, g, do = (pick(f64(inputs[n])) for n in ("q", "k", "v", "g", "do"))
+    threads = min(oracle.num_threads(), len(heads))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    t0 = time.perf_counter()
+    oracle.gla_fwd(q, k, v, g, None)
+    oracle.gla_bwd(q, k, v, g, do, None, None)
+    dt = time.perf_counter() - t0
+    tokens_equiv = len(heads) * w.T / w.H  # a token of the workload carries H heads
+    return {
+        "value": tokens_equiv / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "fp64 oracle fwd+bwd on %d of %d heads, full T=%d (%.1f s wall)" % (len(heads), w.B * w.H,
+                                                                                  w.T, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="metric_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; the multi-GPU sharding of the path is "
+              "described in DESIGN.md and not run (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunkwise_linear_rnn_amd as gla
+    import gla_inputs as gi
+
+    w = gi.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
+    dt = w.torch_dtype
+    e = 2 if w.dtype == "bf16" else 4
+    cpu_inputs = gi.make_inputs(w)
+    if "do" not in cpu_inputs:
+        raise SystemExit("workload %s has no backward inputs" % w.name)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in cpu_inputs.items()}
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    dq, dk, dg = (torch.empty(B, T, H, K, dtype=dt, device=dev) for _ in range(3))
+    dv = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    wsf = gla.workspace(gla.gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+    wsb = gla.workspace(gla.gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
+
+    def fwd():
+        gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, wsf)
+
+    def bwd():
+        gla.gla_bwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], d["do"], None, dq, dk, dv, dg, ds0, wsb)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ms_step = timed(step, args.steps)
+    wall = time.perf_counter() - wall0
+    ms_fwd = timed(fwd, args.steps)
+    ms_bwd = timed(bwd, args.steps)
+    # cold-cache variant: overwrite a 512 MiB buffer between steps (not part of value)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 10)):
+        scrub.fill_(1)
+        torch.cuda.synchronize()
+        cold.append(timed(step, 1))
+    del scrub
+
+    # per-kernel HIP-event timing over another K steps
+    gla.gla_kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = gla.gla_kernel_timing_read()
+    gla.gla_kernel_timing(False)
+    kern = {n: {"launches": c, "avg_us": 1e3 * ms / c, "share": ms / max(1e-9, sum(x[1] for x in kt.values()))}
+            for n, (c, ms) in kt.items()}
+    dom = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches"])
+    P = plan_segments(B, H, T, K, V, w.dtype == "bf16")
+    units = B * T * H
+    bpt = alg_bytes_per_token_head(dom, K, V, e, P)
+    roofline = None
+    if bpt is not None:
+        ach = bpt * units / (kern[dom]["avg_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic(w.name, dom, units),
+                    "alg_bytes_per_launch": bpt * units}
+
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    fwd_flops = fwd_flops_per_token_head(K, V) * units
+    peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, gla_fwd + gla_bwd per step" % (
+            w.name, B, H, T, K, V, w.dtype), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
+            "chunk": 64, "segments": P},
+        "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
+        "bwd_tokens_per_s": tokens / (ms_bwd * 1e-3),
+        "ms_fwd": ms_fwd,
+        "ms_bwd": ms_bwd,
+        "ms_per_step_cold": sorted(cold)[len(cold) // 2] if cold else None,
+        "fwd_mfma_frac": fwd_flops / (ms_fwd * 1e-3) / (peak_tf * 1e12),
+        "fwdbwd_mfma_frac": (fwd_flops + bwd_flops_per_token_head(K, V) * units) / (ms_step * 1e-3) /
+                            (peak_tf * 1e12),
+        "fwd_hbm_frac": e * (3 * K + 2 * V) * units / (ms_fwd * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "kernels": kern,
+        "roofline": roofline,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cpu_inputs, w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,7 +41,8 @@ class GlaError(RuntimeError):
 
 
 EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size",
-           "gla_status_string", "gla_last_error_detail", "gla_abi_version"]
+           "gla_status_string", "gla_last_error_detail", "gla_abi_version",
+           "gla_kernel_timing", "gla_kernel_timing_read"]
 
 _lib = None
 
@@ -70,6 +71,10 @@ def lib():
     L.gla_last_error_detail.argtypes = []
     L.gla_last_error_detail.restype = ctypes.c_char_p
     L.gla_abi_version.restype = ctypes.c_int
+    L.gla_kernel_timing.argtypes = [ctypes.c_int]
+    L.gla_kernel_timing.restype = ctypes.c_int
+    L.gla_kernel_timing_read.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+    L.gla_kernel_timing_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -175,3 +180,21 @@ def gla_bwd(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
     ws = workspace(gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
     gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream)
     return dq, dk, dv, dg, ds0
+
+
+def gla_kernel_timing(enable: bool) -> None:
+    """Turn per-kernel HIP-event timing of library launches on or off."""
+    lib().gla_kernel_timing(1 if enable else 0)
+
+
+def gla_kernel_timing_read() -> dict:
+    """{kernel: (launches, total_ms)} recorded since the previous read."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().gla_kernel_timing_read(buf, len(buf))
+    if n < 0:
+        raise RuntimeError("gla_kernel_timing_read: HIP event query failed")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out

@@ -27,6 +27,7 @@
 // by columns of V).  Each walk contracts only over dimensions it holds whole.
 #include "gla_chunk.hpp"
 #include "gla_launch.hpp"
+#include "gla_timing.hpp"
 
 namespace gla {
 
@@ -745,13 +746,13 @@ static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
     if (a.P > 1) {
         const int nseg = a.P - 1;
         dim3 grid((unsigned)(nvb * nseg * a.BH));
-        hipLaunchKernelGGL((gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), 0, a.stream, (const T*)a.k,
+        GLA_LAUNCH("bwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, 0,
                            nseg);
-        hipLaunchKernelGGL((gla_seg_state<T, KD, BV, NW, true>), grid, dim3(NT), 0, a.stream, (const T*)a.q,
+        GLA_LAUNCH("bwd_seg_state_rev", (gla_seg_state<T, KD, BV, NW, true>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.g, (const T*)a.d_o, a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P,
                            a.seg_len, 1, nseg);
-        hipLaunchKernelGGL(gla_seg_combine_bwd, dim3((unsigned)KD, (unsigned)a.BH), dim3(256), 0, a.stream, a.s0,
+        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd, dim3((unsigned)KD, (unsigned)a.BH), dim3(256), a.stream, a.s0,
                            a.dht, a.ws_state, a.ws_dstate, a.ws_gate, KD, a.V, a.P);
     }
     return hipGetLastError();
@@ -767,7 +768,7 @@ static hipError_t launch_dv(const BwdLaunch& a) {
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)(nvb * a.P * a.BH));
-    hipLaunchKernelGGL((gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), 0, a.stream, (const T*)a.q, (const T*)a.k,
+    GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv, a.ds0, a.T, a.H, a.V,
                        a.N, a.P, a.seg_len);
     return hipGetLastError();
@@ -785,10 +786,10 @@ static hipError_t launch_rows(const BwdLaunch& a) {
     const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
-    hipLaunchKernelGGL((gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), 0, a.stream, (const T*)a.k, (const T*)a.v,
+    GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k, (const T*)a.v,
                        (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq, (T*)a.ws_hs,
                        a.T, a.H, a.K, a.N, a.P, a.seg_len);
-    hipLaunchKernelGGL((gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), 0, a.stream, (const T*)a.q, (const T*)a.k,
+    GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit, seg_stride, bh_stride,
                        (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P, a.seg_len);
     return hipGetLastError();

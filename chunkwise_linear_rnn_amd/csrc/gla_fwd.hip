@@ -19,6 +19,7 @@
 // With P = 1 only step 3 runs (the non-materialised form of Section 3.3).
 #include "gla_chunk.hpp"
 #include "gla_launch.hpp"
+#include "gla_timing.hpp"
 
 namespace gla {
 
@@ -264,18 +265,18 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
         // segments 0..P-2 feed the combine; the last segment's S* is never needed
         const int nseg = a.P - 1;
         dim3 grid((unsigned)(nvb * nseg * a.BH));
-        hipLaunchKernelGGL((gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), 0, a.stream,
+        GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate,
                            a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg);
         dim3 g2((unsigned)((KV + 255) / 256), (unsigned)a.BH);
-        hipLaunchKernelGGL(gla_seg_combine_fwd, g2, dim3(256), 0, a.stream, a.s0, a.ws_state, a.ws_gate,
+        GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd, g2, dim3(256), a.stream, a.s0, a.ws_state, a.ws_gate,
                            KD, a.V, a.P);
     }
     const float* sinit = a.P > 1 ? a.ws_state : a.s0;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)(nvb * a.P * a.BH));
-    hipLaunchKernelGGL((gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), 0, a.stream,
+    GLA_LAUNCH("fwd_walk", (gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
                        (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
     return hipGetLastError();
@@ -283,7 +284,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
 
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gla_state_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, dst, n);
+    GLA_LAUNCH("state_copy", gla_state_copy, dim3((unsigned)((n + 255) / 256)), dim3(256), stream, src, dst, n);
     return hipGetLastError();
 }
 

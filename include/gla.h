@@ -132,6 +132,23 @@ const char* gla_last_error_detail(void);
 /* GLA_ABI_VERSION of the loaded library. */
 int gla_abi_version(void);
 
+/*
+ * Kernel timing, for benchmarks and profiling (off by default).
+ * gla_kernel_timing(1): every later gla_fwd / gla_bwd call, on any thread,
+ *   brackets each kernel it enqueues with two HIP events recorded on the
+ *   call's stream (so the measured interval is that kernel on that stream).
+ *   gla_kernel_timing(0) stops recording.  Returns 0.
+ * gla_kernel_timing_read(buf, len): waits for every recorded event, then
+ *   writes one line "<kernel> <launches> <total_ms>" per kernel name, summed
+ *   since the previous read, into buf (NUL-terminated, truncated to len
+ *   bytes; buf may be NULL to just discard), and clears the record.  Returns
+ *   the number of kernel names, or -1 if a HIP event query failed.
+ * The events come from a library-owned pool that is kept for the life of the
+ * process; recording costs two hipEventRecord calls per launch.
+ */
+int gla_kernel_timing(int enable);
+int gla_kernel_timing_read(char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif
