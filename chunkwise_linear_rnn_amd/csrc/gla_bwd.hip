@@ -48,6 +48,7 @@ struct RowSmem {
     T P[kChunk * pP];       // dP (dq walk, [t][s]) or dP^T (dk walk, [s][t])
     float tot[NT];
     float last[BK];
+    float gam[BK];
     int flag;
 };
 
@@ -174,7 +175,8 @@ gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht,
 // ---------------------------------------------------------------------------
 // dq walk: forwards over one segment for key rows k0 .. k0+BK-1, full V.
 // State S^T in VGPRs; dq_t = exp2(B_t - B_63) * [dO (gamma*S)^T + dP (K*Gamma)]_t
-// (both terms share the factor; exact-path chunks use the element-wise form).
+// (both terms share the factor; exact-path chunks use the element-wise form),
+// accumulated transposed so each lane stores four consecutive key columns.
 // After each chunk the state S_out is stored to `hs` (dtype) in this kernel's
 // own tile order, for the dk walk's chunk-boundary gate-gradient term.
 template <typename T, int BK, int V, int NW>
@@ -196,7 +198,7 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
     const int b = bh / H, h = bh % H;
     const int k0 = kb * BK;
     const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
-    const long rsK = (long)H * K, rsV = (long)H * V;
+    const int rsK = H * K, rsV = H * V;
 
     for (int e = tid; e < kChunk * kChunk; e += NT) {
         const int t = e / kChunk, s = e % kChunk;
@@ -210,18 +212,19 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
     using TRV = TileRegs<T, V, NT>;
     TRK rk, rg;
     TRV rv, rdo;
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
     auto issue = [&](int c) {
-        const long t0 = (long)b * T_ + (long)c * kChunk;
-        rk.load(k + (t0 * H + h) * K + k0, rsK, tid);
-        rg.load(g + (t0 * H + h) * K + k0, rsK, tid);
-        rv.load(v + (t0 * H + h) * V, rsV, tid);
-        rdo.load(d_o + (t0 * H + h) * V, rsV, tid);
+        rk.load(kbase(k, c), rsK, tid);
+        rg.load(kbase(g, c), rsK, tid);
+        rv.load(vbase(v, c), rsV, tid);
+        rdo.load(vbase(d_o, c), rsV, tid);
     };
     issue(c_begin);
     for (int c = c_begin; c < c_end; ++c) {
         const bool more = c + 1 < c_end;
         if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, BK, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        chunk_log_cumsum<T, BK, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
         const bool exact = sm.flag != 0;
 #pragma unroll
         for (int p = 0; p < TRK::PER; ++p) {
@@ -241,47 +244,51 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
         __syncthreads();
         dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         __syncthreads();
-        const long t0 = (long)b * T_ + (long)c * kChunk;
+        T* dqbase = const_cast<T*>(kbase(dq, c));
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
-            const int il = 16 * (w * IBW + ib) + (l & 15);  // key row within the block
-            const float gam = exact ? 1.f : exp2_fast(sm.last[il]);
+            const int i0 = 16 * (w * IBW + ib);
+            const float gl = exact ? 1.f : sm.gam[i0 + (l & 15)];
             vec4_t<T> sf[V / 32][2];
 #pragma unroll
             for (int ks = 0; ks < V / 32; ++ks) {
-                sf[ks][0] = to_vec4<T>(S.s[2 * ks][ib] * gam);
-                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1][ib] * gam);
+                sf[ks][0] = to_vec4<T>(S.s[2 * ks][ib] * gl);
+                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1][ib] * gl);
             }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
+                // dq^T[i][t] = sum_j (gamma S)[i][j] dO[t][j] + sum_s Kt[s][i] dP[t][s]
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < V / 32; ++ks)
-                    acc = mma32(acc, frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks),
-                                frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks + 16), sf[ks][0], sf[ks][1]);
+                    acc = mma32(acc, sf[ks][0], sf[ks][1], frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks),
+                                frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks + 16));
                 if (!exact) {
 #pragma unroll
                     for (int ks2 = 0; ks2 <= tb / 2; ++ks2)
-                        acc = mma32(acc, frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
-                                    frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16),
-                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2, 16 * (w * IBW + ib)),
-                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, 16 * (w * IBW + ib)));
+                        acc = mma32(acc, frag_cm<T>(sm.X, Sm::pX, 32 * ks2, i0),
+                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, i0),
+                                    frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
+                                    frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16));
                 }
+                // slot r: key row i = i0 + 4(l/16) + r, token t = 16tb + l%16
+                const int t = 16 * tb + (l & 15), ic = i0 + 4 * (l >> 4);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.B + t * Sm::pB + ic);
+                f32x4 val;
+                if (!exact) {
+                    const f32x4 bl = *reinterpret_cast<const f32x4*>(sm.last + ic);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * tb + 4 * (l >> 4) + r;
-                    const float bt = sm.B[t * Sm::pB + il];
-                    float val;
-                    if (!exact) {
-                        val = acc[r] * exp2_fast(bt - sm.last[il]);
-                    } else {
-                        val = acc[r] * exp2_fast(bt);
+                    for (int r = 0; r < 4; ++r) val[r] = acc[r] * exp2_fast(bt[r] - bl[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        val[r] = acc[r] * exp2_fast(bt[r]);
                         for (int s = 0; s <= t; ++s)
-                            val += Elem<T>::to_f(sm.P[t * Sm::pP + s]) * Elem<T>::to_f(sm.X[s * Sm::pX + il]) *
-                                   exp2_fast(bt - sm.B[s * Sm::pB + il]);
+                            val[r] += Elem<T>::to_f(sm.P[t * Sm::pP + s]) * Elem<T>::to_f(sm.X[s * Sm::pX + ic + r]) *
+                                      exp2_fast(bt[r] - sm.B[s * Sm::pB + ic + r]);
                     }
-                    dq[((t0 + t) * H + h) * K + k0 + il] = Elem<T>::from_f(val);
                 }
+                *reinterpret_cast<vec4_t<T>*>(dqbase + t * rsK + ic) = to_vec4<T>(val);
             }
         }
         if (exact) {
@@ -302,9 +309,9 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
         // S^T <- S^T Diag(gamma) + V^T (K*Gamma)
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
-            const float gam = exp2_fast(sm.last[16 * (w * IBW + ib) + (l & 15)]);
+            const float gl = sm.gam[16 * (w * IBW + ib) + (l & 15)];
 #pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gam;
+            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gl;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -338,9 +345,10 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
 
 // ---------------------------------------------------------------------------
 // dk + dg walk: backwards over one segment for key rows k0 .. k0+BK-1, full V.
-// State dS^T in VGPRs.  dk_s = Gamma_s * [V dS_out^T + dP^T (q*exp2(B_t - B_63))]_s,
-// then dA = q*dq - k*dk and dg = reverse cumulative sum of dA within the chunk
-// plus rowsum(S_out * dS_out), with S_out read back from the dq walk's `hs`.
+// State dS^T in VGPRs.  dk_s = Gamma_s * [V dS_out^T + dP^T (q*exp2(B_t - B_63))]_s
+// (accumulated transposed), then dA = q*dq - k*dk and dg = reverse cumulative
+// sum of dA within the chunk plus rowsum(S_out * dS_out), with S_out read back
+// from the dq walk's `hs`.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
@@ -353,6 +361,7 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     using Sm = RowSmem<T, BK, V, NT>;
     __shared__ Sm sm;
     __shared__ float s_carry[BK];
+    __shared__ T s_ql[kChunk * Sm::pX];  // q*Lambda for the dS update
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int nkb = K / BK;
     int bid = blockIdx.x;
@@ -363,7 +372,7 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     const int k0 = kb * BK;
     const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
     const int nchunks = c_end - c_begin;
-    const long rsK = (long)H * K, rsV = (long)H * V;
+    const int rsK = H * K, rsV = H * V;
 
     // dP^T is stored [s][t]; its tiles with t-block < s-block are zero
     for (int e = tid; e < kChunk * kChunk; e += NT) {
@@ -382,41 +391,41 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     using TRV = TileRegs<T, V, NT>;
     TRK rq, rk, rg, rdq;
     TRV rv, rdo;
-    auto tok0 = [&](int c) { return (long)b * T_ + (long)c * kChunk; };
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
     auto issue_main = [&](int c) {
-        const long t0 = tok0(c);
-        rq.load(q + (t0 * H + h) * K + k0, rsK, tid);
-        rg.load(g + (t0 * H + h) * K + k0, rsK, tid);
-        rdq.load(dq + (t0 * H + h) * K + k0, rsK, tid);
-        rv.load(v + (t0 * H + h) * V, rsV, tid);
-        rdo.load(d_o + (t0 * H + h) * V, rsV, tid);
+        rq.load(kbase(q, c), rsK, tid);
+        rg.load(kbase(g, c), rsK, tid);
+        rdq.load(kbase(dq, c), rsK, tid);
+        rv.load(vbase(v, c), rsV, tid);
+        rdo.load(vbase(d_o, c), rsV, tid);
     };
     issue_main(c_end - 1);
-    rk.load(k + (tok0(c_end - 1) * H + h) * K + k0, rsK, tid);
+    rk.load(kbase(k, c_end - 1), rsK, tid);
     for (int it = 0; it < nchunks; ++it) {
         const int c = c_end - 1 - it;
         const bool more = it + 1 < nchunks;
-        const long t0 = tok0(c);
         if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, BK, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        chunk_log_cumsum<T, BK, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
         const bool exact = sm.flag != 0;
-        // q-side operand q*exp2(B_t - B_63) (raw q on the exact path); keep
-        // q*Lambda and q*dq in registers for later in the chunk
-        float ql[TRK::PER][TRK::VEC], qdq[TRK::PER][TRK::VEC];
+        // q-side operands q*exp2(B_t - B_63) (raw q on the exact path) and
+        // q*Lambda to LDS; q*dq stays in registers until dk is known
+        float qdq[TRK::PER][TRK::VEC];
 #pragma unroll
         for (int p = 0; p < TRK::PER; ++p) {
             if (!TRK::owns(p, tid)) continue;
             const int row = TRK::row_of(p, tid), c0 = TRK::col_of(p, tid);
-            float qv[TRK::VEC];
+            float qv[TRK::VEC], ql[TRK::VEC];
 #pragma unroll
             for (int e = 0; e < TRK::VEC; ++e) {
                 const float bt = sm.B[row * Sm::pB + c0 + e];
                 const float qq = rq.get(p, e);
                 qv[e] = exact ? qq : qq * exp2_fast(bt - sm.last[c0 + e]);
-                ql[p][e] = qq * exp2_fast(bt);
+                ql[e] = qq * exp2_fast(bt);
                 qdq[p][e] = qq * rdq.get(p, e);
             }
             store_vec_lds<T>(sm.X + row * Sm::pX + c0, qv);
+            store_vec_lds<T>(s_ql + row * Sm::pX + c0, ql);
         }
         rv.store_lds(sm.Vt, Sm::pV, tid);
         rdo.store_lds(sm.dO, Sm::pV, tid);
@@ -424,59 +433,53 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         __syncthreads();
         dp_tiles<T, V, true>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         __syncthreads();
-        f32x4 dkr[4][IBW];
+        T* dkbase = const_cast<T*>(kbase(dk, c));
+        f32x4 dkr[IBW][4];
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
-            const int il = 16 * (w * IBW + ib) + (l & 15);
-            vec4_t<T> sf[V / 32][2];
+            const int i0 = 16 * (w * IBW + ib);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) dkr[ib][sb] = zero4();
+            // dk^T[i][s] = sum_j dS[i][j] V[s][j] + sum_t Qh[t][i] dP^T[s][t]
 #pragma unroll
             for (int ks = 0; ks < V / 32; ++ks) {
-                sf[ks][0] = to_vec4<T>(S.s[2 * ks][ib]);
-                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1][ib]);
+                const vec4_t<T> alo = to_vec4<T>(S.s[2 * ks][ib]);
+                const vec4_t<T> ahi = to_vec4<T>(S.s[2 * ks + 1][ib]);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+                    dkr[ib][sb] = mma32(dkr[ib][sb], alo, ahi, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks),
+                                        frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks + 16));
+            }
+            if (!exact) {
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
+                    const vec4_t<T> alo = frag_cm<T>(sm.X, Sm::pX, 32 * ks2, i0);
+                    const vec4_t<T> ahi = frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, i0);
+#pragma unroll
+                    for (int sb = 0; sb <= 2 * ks2 + 1; ++sb)
+                        dkr[ib][sb] = mma32(dkr[ib][sb], alo, ahi, frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
+                                            frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16));
+                }
             }
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < V / 32; ++ks)
-                    acc = mma32(acc, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks),
-                                frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks + 16), sf[ks][0], sf[ks][1]);
-                if (!exact) {
-#pragma unroll
-                    for (int ks2 = sb / 2; ks2 < 2; ++ks2)
-                        acc = mma32(acc, frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
-                                    frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16),
-                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2, 16 * (w * IBW + ib)),
-                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, 16 * (w * IBW + ib)));
-                }
+                // slot r: key row i = i0 + 4(l/16) + r, token s = 16sb + l%16
+                const int s = 16 * sb + (l & 15), ic = i0 + 4 * (l >> 4);
+                const f32x4 bs = *reinterpret_cast<const f32x4*>(sm.B + s * Sm::pB + ic);
+                const f32x4 bl = *reinterpret_cast<const f32x4*>(sm.last + ic);
+                f32x4 val;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int s = 16 * sb + 4 * (l >> 4) + r;
-                    const float bs = sm.B[s * Sm::pB + il];
-                    float val = acc[r] * exp2_fast(sm.last[il] - bs);
+                    val[r] = dkr[ib][sb][r] * exp2_fast(bl[r] - bs[r]);
                     if (exact)
                         for (int t = s; t < kChunk; ++t)
-                            val += Elem<T>::to_f(sm.P[s * Sm::pP + t]) * Elem<T>::to_f(sm.X[t * Sm::pX + il]) *
-                                   exp2_fast(sm.B[t * Sm::pB + il] - bs);
-                    acc[r] = val;
-                    dk[((t0 + s) * H + h) * K + k0 + il] = Elem<T>::from_f(val);
+                            val[r] += Elem<T>::to_f(sm.P[s * Sm::pP + t]) * Elem<T>::to_f(sm.X[t * Sm::pX + ic + r]) *
+                                      exp2_fast(sm.B[t * Sm::pB + ic + r] - bs[r]);
                 }
-                dkr[sb][ib] = acc;
+                dkr[ib][sb] = val;
+                *reinterpret_cast<vec4_t<T>*>(dkbase + s * rsK + ic) = to_vec4<T>(val);
             }
         }
-        __syncthreads();
-        // dk (fp32) replaces the gate cumsum in LDS; q*Lambda replaces the q-side operand
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib)
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.B[(16 * sb + 4 * (l >> 4) + r) * Sm::pB + 16 * (w * IBW + ib) + (l & 15)] = dkr[sb][ib][r];
-#pragma unroll
-        for (int p = 0; p < TRK::PER; ++p)
-            if (TRK::owns(p, tid)) store_vec_lds<T>(sm.X + TRK::row_of(p, tid) * Sm::pX + TRK::col_of(p, tid), ql[p]);
-        __syncthreads();
         // sum over later tokens for dg: rowsum(S_out * dS_out) at this chunk's end
         {
             const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
@@ -495,20 +498,29 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
                 if ((l >> 4) == 0) s_carry[16 * (w * IBW + ib) + (l & 15)] = part;
             }
         }
+        __syncthreads();
+        // dk (fp32) replaces the gate cumsum in LDS
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+                *reinterpret_cast<f32x4*>(sm.B + (16 * sb + (l & 15)) * Sm::pB + 16 * (w * IBW + ib) + 4 * (l >> 4)) =
+                    dkr[ib][sb];
+        __syncthreads();
         // dS^T <- dS^T Diag(gamma) + dO^T (q*Lambda)
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
-            const float gam = exp2_fast(sm.last[16 * (w * IBW + ib) + (l & 15)]);
+            const float gl = sm.gam[16 * (w * IBW + ib) + (l & 15)];
 #pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gam;
+            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gl;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             vec4_t<T> xf[IBW][2];
 #pragma unroll
             for (int ib = 0; ib < IBW; ++ib) {
-                xf[ib][0] = frag_cm<T>(sm.X, Sm::pX, 32 * ks, 16 * (w * IBW + ib));
-                xf[ib][1] = frag_cm<T>(sm.X, Sm::pX, 32 * ks + 16, 16 * (w * IBW + ib));
+                xf[ib][0] = frag_cm<T>(s_ql, Sm::pX, 32 * ks, 16 * (w * IBW + ib));
+                xf[ib][1] = frag_cm<T>(s_ql, Sm::pX, 32 * ks + 16, 16 * (w * IBW + ib));
             }
 #pragma unroll
             for (int jb = 0; jb < V / 16; ++jb) {
@@ -526,10 +538,11 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 #pragma unroll
             for (int e = 0; e < TRK::VEC; ++e) dst[e] = qdq[p][e] - rk.get(p, e) * dst[e];
         }
-        if (more) rk.load(k + (tok0(c - 1) * H + h) * K + k0, rsK, tid);
+        if (more) rk.load(kbase(k, c - 1), rsK, tid);
         __syncthreads();
         // dg_t = sum_{r >= t} dA_r over the rest of the sequence (Section 4.3 closed form)
         {
+            T* dgbase = const_cast<T*>(kbase(dg, c));
             float acc = 0.f;
 #pragma unroll
             for (int u = R - 1; u >= 0; --u) {
@@ -544,7 +557,7 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const int t = spart * R + u;
-                dg[((t0 + t) * H + h) * K + k0 + scol] = Elem<T>::from_f(sm.B[t * Sm::pB + scol] + off);
+                dgbase[t * rsK + scol] = Elem<T>::from_f(sm.B[t * Sm::pB + scol] + off);
             }
         }
         __syncthreads();
@@ -554,8 +567,9 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 // ---------------------------------------------------------------------------
 // dv walk: backwards over one segment for value columns v0 .. v0+BV-1, full K.
 // State dS in VGPRs.  dv = A^T dO + (K*Gamma) dS_out with A rebuilt from
-// q*exp2(B_t - B_63) and k*exp2(B_63 - B_s) (element-wise on exact-path chunks);
-// dS_in = Diag(gamma) dS_out + (Q*Lambda)^T dO.  Segment 0 ends with dS_0.
+// q*exp2(B_t - B_63) and k*exp2(B_63 - B_s) (element-wise on exact-path
+// chunks), accumulated transposed; dS_in = Diag(gamma) dS_out + (Q*Lambda)^T dO.
+// Segment 0 ends with dS_0.
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g, const T* __restrict__ d_o,
@@ -575,7 +589,7 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     const int v0 = vb * BV;
     const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
     const int nchunks = c_end - c_begin;
-    const long rsK = (long)H * KD, rsV = (long)H * V;
+    const int rsK = H * KD, rsV = H * V;
     const int col0 = w * (BV / NW);
 
     for (int e = tid; e < kChunk * kChunk; e += NT) {
@@ -589,20 +603,17 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     using TR = TileRegs<T, KD, NT>;
     TR rq, rk, rg;
     TileRegs<T, BV, NT> rdo;
-    auto tok0 = [&](int c) { return (long)b * T_ + (long)c * kChunk; };
-    {
-        const long t0 = tok0(c_end - 1);
-        rq.load(q + (t0 * H + h) * KD, rsK, tid);
-        rk.load(k + (t0 * H + h) * KD, rsK, tid);
-        rg.load(g + (t0 * H + h) * KD, rsK, tid);
-        rdo.load(d_o + (t0 * H + h) * V + v0, rsV, tid);
-    }
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + v0; };
+    rq.load(kbase(q, c_end - 1), rsK, tid);
+    rk.load(kbase(k, c_end - 1), rsK, tid);
+    rg.load(kbase(g, c_end - 1), rsK, tid);
+    rdo.load(vbase(d_o, c_end - 1), rsV, tid);
     for (int it = 0; it < nchunks; ++it) {
         const int c = c_end - 1 - it;
         const bool more = it + 1 < nchunks;
-        const long t0 = tok0(c);
         if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
         const bool exact = sm.flag != 0;
 #pragma unroll
         for (int p = 0; p < TR::PER; ++p) {
@@ -624,10 +635,9 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         }
         rdo.store_lds(sm.V, Sm::pV, tid);
         if (more) {
-            const long t1 = tok0(c - 1);
-            rk.load(k + (t1 * H + h) * KD, rsK, tid);
-            rg.load(g + (t1 * H + h) * KD, rsK, tid);
-            rdo.load(d_o + (t1 * H + h) * V + v0, rsV, tid);
+            rk.load(kbase(k, c - 1), rsK, tid);
+            rg.load(kbase(g, c - 1), rsK, tid);
+            rdo.load(vbase(d_o, c - 1), rsV, tid);
         }
         __syncthreads();
         // A tiles, stored transposed: sm.A[s][t] = A[t][s]
@@ -684,7 +694,7 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
                 store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
             }
         }
-        if (more) rq.load(q + (tok0(c - 1) * H + h) * KD, rsK, tid);
+        if (more) rq.load(kbase(q, c - 1), rsK, tid);
         __syncthreads();
         {
             vec4_t<T> sf[KD / 32][CB][2];
@@ -700,36 +710,36 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) df[tb][cb] = frag_cm<T>(sm.V, Sm::pV, 16 * tb, col0 + 16 * cb);
+            T* dvbase = const_cast<T*>(vbase(dv, c));
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
+                // dv^T[j][s] = sum_i dS[i][j] Kt[s][i] + sum_t dO[t][j] A^T[s][t]
                 f32x4 acc[CB];
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) acc[cb] = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks) {
-                    vec4_t<T> alo = frag_rm<T>(sm.K, Sm::pK, 16 * sb, 32 * ks);
-                    vec4_t<T> ahi = frag_rm<T>(sm.K, Sm::pK, 16 * sb, 32 * ks + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.K, Sm::pK, 16 * sb, 32 * ks);
+                    vec4_t<T> bhi = frag_rm<T>(sm.K, Sm::pK, 16 * sb, 32 * ks + 16);
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], alo, ahi, sf[ks][cb][0], sf[ks][cb][1]);
+                    for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], sf[ks][cb][0], sf[ks][cb][1], blo, bhi);
                 }
 #pragma unroll
                 for (int ks2 = sb / 2; ks2 < 2; ++ks2) {
-                    vec4_t<T> alo = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2);
-                    vec4_t<T> ahi = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2 + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2);
+                    vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2 + 16);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
-                        acc[cb] = mma32(acc[cb], alo, ahi, df[2 * ks2][cb], df[2 * ks2 + 1][cb]);
+                        acc[cb] = mma32(acc[cb], df[2 * ks2][cb], df[2 * ks2 + 1][cb], blo, bhi);
                 }
+                // slot r: value column j = col0 + 16cb + 4(l/16) + r, token s = 16sb + l%16
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const long s = t0 + 16 * sb + 4 * (l >> 4) + r;
-                        dv[(s * H + h) * V + v0 + col0 + 16 * cb + (l & 15)] = Elem<T>::from_f(acc[cb][r]);
-                    }
+                    *reinterpret_cast<vec4_t<T>*>(dvbase + (16 * sb + (l & 15)) * rsV + col0 + 16 * cb +
+                                                  4 * (l >> 4)) = to_vec4<T>(acc[cb]);
             }
         }
-        state_update<T, KD, CB>(S, sm.Q, Sm::pQ, sm.V, Sm::pV, sm.last, col0);
+        state_update<T, KD, CB>(S, sm.Q, Sm::pQ, sm.V, Sm::pV, sm.gam, col0);
     }
     if (ds0 && seg == 0) S.store(ds0 + (long)bh * KD * V + v0, V, col0);
 }
@@ -778,7 +788,10 @@ template <typename T, int BK, int V>
 static hipError_t launch_rows(const BwdLaunch& a) {
     constexpr int NW = (BK / 16 < 8) ? BK / 16 : 8;
     constexpr int NT = NW * 64;
-    static_assert(sizeof(RowSmem<T, BK, V, NT>) <= 160 * 1024, "LDS budget");
+    // dk walk: the row-split tiles plus its carry and q*Lambda tiles
+    static_assert(sizeof(RowSmem<T, BK, V, NT>) + sizeof(float) * BK +
+                      sizeof(T) * kChunk * RowSmem<T, BK, V, NT>::pX <= 160 * 1024,
+                  "LDS budget");
     const int nkb = a.K / BK;
     const long KV = (long)a.K * V;
     dim3 grid((unsigned)(nkb * a.P * a.BH));
@@ -852,15 +865,10 @@ static hipError_t row_stage(const BwdLaunch& a) {
     if (a.bf16) {
         GLA_ROW_DISPATCH(bf16, 64, 64)
         GLA_ROW_DISPATCH(bf16, 128, 64)
-        GLA_ROW_DISPATCH(bf16, 256, 64)
         GLA_ROW_DISPATCH(bf16, 64, 128)
-        GLA_ROW_DISPATCH(bf16, 128, 128)
-        GLA_ROW_DISPATCH(bf16, 256, 128)
         GLA_ROW_DISPATCH(bf16, 64, 256)
-        GLA_ROW_DISPATCH(bf16, 128, 256)
     } else {
         GLA_ROW_DISPATCH(float, 64, 64)
-        GLA_ROW_DISPATCH(float, 128, 64)
         GLA_ROW_DISPATCH(float, 64, 128)
     }
     return hipErrorInvalidValue;

@@ -24,6 +24,7 @@ struct ChunkSmem {
     T A[kChunk * pA];
     float tot[NT];
     float last[KD];
+    float gam[KD];
     int flag;
 };
 
@@ -63,17 +64,15 @@ struct StateRegs {
 
 // S <- Diag(gamma) S + X^T Y over the 64 rows of the chunk (Section 4.2:
 // S_[i+1] = (gamma^T 1) * S_[i] + (K*Gamma)^T V).  X (row-major [t][i], the
-// already-decayed key/query tile) and Y (row-major [t][j]) are in LDS;
-// gamma = exp2(last[i]).  Columns of this wave: col0 .. col0 + 16*CB - 1.
+// already-decayed key/query tile) and Y (row-major [t][j]) are in LDS, and so
+// is gamma.  Columns of this wave: col0 .. col0 + 16*CB - 1.
 template <typename T, int KD, int CB>
 __device__ __forceinline__ void state_update(StateRegs<KD, CB>& S, const T* X, int pX, const T* Y, int pY,
-                                             const float* last, int col0) {
+                                             const float* gamma, int col0) {
     const int l = lane_id();
 #pragma unroll
     for (int a = 0; a < KD / 16; ++a) {
-        f32x4 gam;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gam[r] = exp2_fast(last[16 * a + 4 * (l >> 4) + r]);
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(gamma + 16 * a + 4 * (l >> 4));
 #pragma unroll
         for (int c = 0; c < CB; ++c) S.s[a][c] *= gam;
     }
@@ -127,7 +126,7 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
     const int c_begin = seg * seg_len;
     const int c_end = min(N, c_begin + seg_len);
     const int nchunks = c_end - c_begin;
-    const long rsK = (long)H * KD, rsV = (long)H * V;
+    const int rsK = H * KD, rsV = H * V;
     const int col0 = w * (BV / NW);
 
     StateRegs<KD, CB> S;
@@ -145,7 +144,7 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
     issue(REV ? c_end - 1 : c_begin);
     for (int it = 0; it < nchunks; ++it) {
         if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
         if (tid < KD) gate_total += sm.last[tid];
         // decayed operand: K*Gamma (forward) or Q*Lambda (reverse)
         using TR = TileRegs<T, KD, NT>;
@@ -165,7 +164,7 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
         ry.store_lds(sm.V, Sm::pV, tid);
         if (it + 1 < nchunks) issue(REV ? c_end - 2 - it : c_begin + it + 1);
         __syncthreads();
-        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.last, col0);
+        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.gam, col0);
         __syncthreads();
     }
     float* dst = ws_state + ((long)bh * P + seg) * (long)KD * V + v0;

@@ -12,8 +12,10 @@
 //     fed straight back as an operand that contracts over its rows.
 //   * all LDS tiles are row-major with 16 bytes of padding per row; operands
 //     that contract along the row are read with one 8/16-byte load per lane
-//     ("rm" fragments), operands that contract down a column with four
-//     element loads ("cm" fragments).
+//     ("rm" fragments), operands that contract down a column with one LDS
+//     transpose read for bf16 or four element loads for fp32 ("cm" fragments);
+//   * global memory is addressed from a per-chunk uniform base plus 32-bit
+//     lane offsets.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -88,6 +90,11 @@ __device__ __forceinline__ vec4_t<T> frag_rm(const T* base, int pitch, int r0, i
 }
 
 // contraction = rows r0 + 4*(l/16) + e, free index = column c0 + l%16.
+// fp32: four element loads.  bf16: one gfx950 LDS transpose read
+// (ds_read_b64_tr_b16).  Within each 16-lane group that instruction hands lane
+// p element (p % 4) of the 8-byte vectors read by lanes 4e + p/4, e = 0..3; so
+// lane s of the group reads row r0 + 4*(l/16) + s/4 at columns c0 + 4*(s%4)..+3
+// and every lane ends up holding its column for four consecutive rows.
 template <typename T>
 __device__ __forceinline__ vec4_t<T> frag_cm(const T* base, int pitch, int r0, int c0) {
     const int l = lane_id();
@@ -98,6 +105,15 @@ __device__ __forceinline__ vec4_t<T> frag_cm(const T* base, int pitch, int r0, i
     v[2] = p[2 * pitch];
     v[3] = p[3 * pitch];
     return v;
+}
+typedef short __attribute__((ext_vector_type(4))) i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+template <>
+__device__ __forceinline__ bf16x4 frag_cm<bf16>(const bf16* base, int pitch, int r0, int c0) {
+    const int l = lane_id(), s = l & 15;
+    const bf16* p = base + (r0 + 4 * (l >> 4) + (s >> 2)) * pitch + c0 + 4 * (s & 3);
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
 template <typename T>
@@ -127,12 +143,13 @@ struct TileRegs {
     __device__ __forceinline__ static int row_of(int p, int tid) { return (tid + p * NT) / VPR; }
     __device__ __forceinline__ static int col_of(int p, int tid) { return ((tid + p * NT) % VPR) * VEC; }
 
-    // `g` points at element (row 0, col 0) of the tile; rows are `rs` elements apart.
-    __device__ __forceinline__ void load(const T* __restrict__ g, long rs, int tid) {
+    // `g` (uniform) points at element (row 0, col 0) of the tile; rows are `rs`
+    // elements apart.  Offsets stay 32-bit so the loads use a scalar base.
+    __device__ __forceinline__ void load(const T* __restrict__ g, int rs, int tid) {
 #pragma unroll
         for (int p = 0; p < PER; ++p)
             if (owns(p, tid))
-                r[p] = *reinterpret_cast<const uint4*>(g + (long)row_of(p, tid) * rs + col_of(p, tid));
+                r[p] = *reinterpret_cast<const uint4*>(g + (row_of(p, tid) * rs + col_of(p, tid)));
     }
     __device__ __forceinline__ void store_lds(T* s, int pitch, int tid) const {
 #pragma unroll
@@ -164,12 +181,13 @@ __device__ __forceinline__ void store_vec_lds(T* dst, const float* x) {
 // gates"), in log2 units:  sB[t][i] = log2(e) * sum_{u<=t} g[u][i].
 //
 // On entry the raw gate tile is in registers; on exit sB holds the cumsum,
-// sLast[i] = sB[63][i], and *sFlag is set if some column's chunk range
-// sB[0][i] - sB[63][i] exceeds kRangeLimit.  NT threads; KD columns.
-// Three barriers inside.  The caller clears *sFlag before the first barrier.
+// sLast[i] = sB[63][i], sGam[i] = exp2(sLast[i]) (the chunk decay gamma), and
+// *sFlag is set if some column's chunk range sB[0][i] - sB[63][i] exceeds
+// kRangeLimit.  NT threads; KD columns.  Three barriers inside.  The caller
+// clears *sFlag before the first barrier.
 template <typename T, int KD, int NT>
 __device__ __forceinline__ void chunk_log_cumsum(const TileRegs<T, KD, NT>& graw, float* sB, int pitchB,
-                                                 float* sTot, float* sLast, int* sFlag, int tid) {
+                                                 float* sTot, float* sLast, float* sGam, int* sFlag, int tid) {
     using TR = TileRegs<T, KD, NT>;
 #pragma unroll
     for (int p = 0; p < TR::PER; ++p) {
@@ -200,10 +218,12 @@ __device__ __forceinline__ void chunk_log_cumsum(const TileRegs<T, KD, NT>& graw
         if (part == NPART - 1) {
             const float last = run + off;
             sLast[col] = last;
+            sGam[col] = exp2_fast(last);
             if (sB[col] - last > kRangeLimit) *sFlag = 1;
         }
     } else if (NPART == 1) {
         sLast[col] = run;
+        sGam[col] = exp2_fast(run);
         if (sB[col] - run > kRangeLimit) *sFlag = 1;
     }
     __syncthreads();

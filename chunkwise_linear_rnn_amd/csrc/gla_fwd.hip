@@ -60,6 +60,8 @@ __global__ void __launch_bounds__(256) gla_state_copy(const float* __restrict__ 
 //   Ql = q * exp2(B_t)                                       (Q * Lambda)
 //   O  = Ql S + A V                                         (inter + intra)
 //   S  = Diag(exp2 B_63) S + Kt^T V                          (state passing)
+// O is accumulated transposed (O^T = S^T Ql^T + V^T A^T) so that every lane
+// owns four consecutive output columns and stores them in one 8-byte write.
 // Chunks whose gate range exceeds kRangeLimit compute A element by element
 // (Eq. 4, fp32, exp2 of the log-gate difference) instead.
 template <typename T, int KD, int BV, int NW>
@@ -82,7 +84,7 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     const int v0 = vb * BV;
     const int c_begin = seg * seg_len;
     const int c_end = min(N, c_begin + seg_len);
-    const long rsK = (long)H * KD, rsV = (long)H * V;
+    const int rsK = H * KD, rsV = H * V;
     const int col0 = w * (BV / NW);
 
     // zero the strictly-upper 16x16 tiles of A once; they are never written
@@ -98,18 +100,18 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     TileRegs<T, KD, NT> rq, rk, rg;
     TileRegs<T, BV, NT> rv;
     using TR = TileRegs<T, KD, NT>;
-    auto tok_base = [&](int c) { return (long)b * T_ + (long)c * kChunk; };
-    {
-        const long t0 = tok_base(c_begin);
-        rq.load(q + (t0 * H + h) * KD, rsK, tid);
-        rk.load(k + (t0 * H + h) * KD, rsK, tid);
-        rg.load(g + (t0 * H + h) * KD, rsK, tid);
-        rv.load(v + (t0 * H + h) * V + v0, rsV, tid);
-    }
+    // uniform per-chunk bases: element (token 0 of chunk c, head h)
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + v0; };
+    auto obase_of = [&](int c) { return o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + v0; };
+    rq.load(kbase(q, c_begin), rsK, tid);
+    rk.load(kbase(k, c_begin), rsK, tid);
+    rg.load(kbase(g, c_begin), rsK, tid);
+    rv.load(vbase(v, c_begin), rsV, tid);
     for (int c = c_begin; c < c_end; ++c) {
         const bool more = c + 1 < c_end;
         if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, &sm.flag, tid);
+        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
         const bool exact = sm.flag != 0;
         // (b) operands of the intra-chunk tiles
 #pragma unroll
@@ -132,10 +134,9 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
         }
         rv.store_lds(sm.V, Sm::pV, tid);
         if (more) {
-            const long t1 = tok_base(c + 1);
-            rk.load(k + (t1 * H + h) * KD, rsK, tid);
-            rg.load(g + (t1 * H + h) * KD, rsK, tid);
-            rv.load(v + (t1 * H + h) * V + v0, rsV, tid);
+            rk.load(kbase(k, c + 1), rsK, tid);
+            rg.load(kbase(g, c + 1), rsK, tid);
+            rv.load(vbase(v, c + 1), rsV, tid);
         }
         __syncthreads();
         // (c) A tiles, and Q*Lambda into registers
@@ -197,10 +198,7 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                 store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
             }
         }
-        if (more) {
-            const long t1 = tok_base(c + 1);
-            rq.load(q + (t1 * H + h) * KD, rsK, tid);
-        }
+        if (more) rq.load(kbase(q, c + 1), rsK, tid);
         __syncthreads();
         // (e) outputs from the state before this chunk, then the state update
         {
@@ -217,37 +215,36 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(sm.V, Sm::pV, 16 * sb, col0 + 16 * cb);
-            const long t0 = tok_base(c);
+            T* obase = obase_of(c);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 f32x4 acc[CB];
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) acc[cb] = zero4();
+                // O^T[j][t] = sum_i S[i][j] Ql[t][i] + sum_s V[s][j] A[t][s]
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks) {
-                    vec4_t<T> alo = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks);
-                    vec4_t<T> ahi = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks);
+                    vec4_t<T> bhi = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks + 16);
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], alo, ahi, sf[ks][cb][0], sf[ks][cb][1]);
+                    for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], sf[ks][cb][0], sf[ks][cb][1], blo, bhi);
                 }
 #pragma unroll
                 for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
-                    vec4_t<T> alo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
-                    vec4_t<T> ahi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
+                    vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
-                        acc[cb] = mma32(acc[cb], alo, ahi, vf[2 * ks2][cb], vf[2 * ks2 + 1][cb]);
+                        acc[cb] = mma32(acc[cb], vf[2 * ks2][cb], vf[2 * ks2 + 1][cb], blo, bhi);
                 }
+                // slot r: column j = col0 + 16cb + 4(l/16) + r, token t = 16rb + l%16
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const long t = t0 + 16 * rb + 4 * (l >> 4) + r;
-                        o[(t * H + h) * V + v0 + col0 + 16 * cb + (l & 15)] = Elem<T>::from_f(acc[cb][r]);
-                    }
+                    *reinterpret_cast<vec4_t<T>*>(obase + (16 * rb + (l & 15)) * rsV + col0 + 16 * cb +
+                                                  4 * (l >> 4)) = to_vec4<T>(acc[cb]);
             }
         }
-        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.last, col0);
+        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.gam, col0);
     }
     if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V + v0, V, col0);
 }

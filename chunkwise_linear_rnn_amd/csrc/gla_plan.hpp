@@ -37,14 +37,14 @@ inline int plan_bv(const Shape& s) {
     return (int)(s.V < cap ? s.V : cap);
 }
 
-// State rows per workgroup in the backward kernels that contract over V.
+// State rows per workgroup in the backward kernels that contract over V.  The
+// K-block x full-V state lives in VGPRs next to the chunk's prefetched tiles:
+// at V >= 128 (and for fp32) a 64-row block with four waves, which may use the
+// whole 512-entry register file per lane; otherwise up to 128 rows over eight
+// waves.
 inline int plan_bk(const Shape& s) {
-    // K-block x full V state in VGPRs: keep K_blk * V <= 32768 (64 regs/lane at 512 threads).
-    int64_t bk = 32768 / s.V;
-    if (!s.bf16) bk = 8192 / s.V;  // fp32 LDS tiles are twice as large
-    if (bk > s.K) bk = s.K;
-    if (bk < 16) bk = 16;
-    return (int)bk;
+    if (!s.bf16 || s.V >= 128) return 64;
+    return (int)(s.K < 128 ? s.K : 128);
 }
 
 inline Plan make_plan(const Shape& s, int col_blocks_hint) {
