@@ -20,9 +20,13 @@ LIB = os.path.join(HERE, "libgla.so")
 SOURCES = ["gla_api.cpp", "gla_timing.cpp", "gla_fwd.hip", "gla_bwd.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
 
-# Packed-fp32 VALU forms are kept out of the generated code on purpose.
+# Packed-fp32 VALU forms are kept out of the generated code on purpose.  The
+# register tiles that carry the next chunk's prefetch are private arrays; LLVM's
+# promote-alloca pass would otherwise move them into LDS (a global load, a wait
+# and an LDS write at the prefetch point), which defeats the prefetch.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-disable-promote-alloca-to-lds",
           "-I", os.path.join(ROOT, "include")]
 
 

@@ -130,6 +130,8 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // A 64-row x W-column tile held in registers between its global load and its
 // use, 16 bytes per vector.  Thread `tid` owns vectors tid, tid+NT, ...; vector
 // idx covers row idx / (W/VEC), columns (idx % (W/VEC))*VEC .. +VEC-1.
+typedef unsigned int __attribute__((ext_vector_type(4))) u32x4;
+
 template <typename T, int W, int NT>
 struct TileRegs {
     static constexpr int VEC = 16 / (int)sizeof(T);
@@ -137,7 +139,7 @@ struct TileRegs {
     static constexpr int NV = kChunk * VPR;       // vectors per tile
     static constexpr int PER = (NV + NT - 1) / NT;
     static_assert(W % VEC == 0, "tile width must be a whole number of 16-byte vectors");
-    uint4 r[PER];
+    u32x4 r[PER];
 
     __device__ __forceinline__ static bool owns(int p, int tid) { return (NV % NT == 0) || (tid + p * NT < NV); }
     __device__ __forceinline__ static int row_of(int p, int tid) { return (tid + p * NT) / VPR; }
@@ -149,13 +151,13 @@ struct TileRegs {
 #pragma unroll
         for (int p = 0; p < PER; ++p)
             if (owns(p, tid))
-                r[p] = *reinterpret_cast<const uint4*>(g + (row_of(p, tid) * rs + col_of(p, tid)));
+                r[p] = *reinterpret_cast<const u32x4*>(g + (row_of(p, tid) * rs + col_of(p, tid)));
     }
     __device__ __forceinline__ void store_lds(T* s, int pitch, int tid) const {
 #pragma unroll
         for (int p = 0; p < PER; ++p)
             if (owns(p, tid))
-                *reinterpret_cast<uint4*>(s + row_of(p, tid) * pitch + col_of(p, tid)) = r[p];
+                *reinterpret_cast<u32x4*>(s + row_of(p, tid) * pitch + col_of(p, tid)) = r[p];
     }
     // element e (0..VEC-1) of vector p as float
     __device__ __forceinline__ float get(int p, int e) const {
@@ -163,6 +165,43 @@ struct TileRegs {
         return Elem<T>::to_f(v[e]);
     }
 };
+
+// One wave's slab of a 64-row chunk tile, one token row per lane: lane l holds
+// row l, columns c0 .. c0+NC-1 (NC a whole number of 16-byte vectors).
+template <typename T, int NC>
+struct RowSlab {
+    static constexpr int VEC = 16 / (int)sizeof(T);
+    static constexpr int NV = NC / VEC;
+    static_assert(NC % VEC == 0, "slab width must be a whole number of 16-byte vectors");
+    u32x4 r[NV];
+    // `base` (uniform) points at element (row 0, col 0) of the tile; rows are `rs` apart.
+    __device__ __forceinline__ void load(const T* __restrict__ base, int rs, int c0) {
+        const T* p = base + (lane_id() * rs + c0);
+#pragma unroll
+        for (int m = 0; m < NV; ++m) r[m] = *reinterpret_cast<const u32x4*>(p + m * VEC);
+    }
+    __device__ __forceinline__ float get(int c) const {
+        const T* v = reinterpret_cast<const T*>(&r[c / VEC]);
+        return Elem<T>::to_f(v[c % VEC]);
+    }
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane = token): four
+// row_shr steps within each 16-lane row, then row_bcast:15 into rows 1 and 3
+// and row_bcast:31 into rows 2 and 3 (GFX9 DPP).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x111, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x112, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x114, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x118, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+
+__device__ __forceinline__ float lane_bcast(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
 
 // Pack VEC floats into one 16-byte vector of T and store it to LDS.
 template <typename T>

@@ -55,15 +55,36 @@ __global__ void __launch_bounds__(256) gla_state_copy(const float* __restrict__ 
 //
 // Per chunk (64 tokens, B = intra-chunk cumulative log2 gate, reference row
 // 63; Section 4.2 with the sub-chunk tiling of Section 4.3 at c = 16):
-//   Qh = q * exp2(B_t - B_63)   Kt = k * exp2(B_63 - B_s)   (row-major LDS)
+//   Qh = q * exp2(B_t - B_63)   Kt = k * exp2(B_63 - B_s)   Ql = q * exp2(B_t)
 //   A[t][s] = sum_i Qh[t][i] Kt[s][i]  for s <= t: ten 16x16 MFMA tiles
-//   Ql = q * exp2(B_t)                                       (Q * Lambda)
 //   O  = Ql S + A V                                         (inter + intra)
 //   S  = Diag(exp2 B_63) S + Kt^T V                          (state passing)
-// O is accumulated transposed (O^T = S^T Ql^T + V^T A^T) so that every lane
-// owns four consecutive output columns and stores them in one 8-byte write.
-// Chunks whose gate range exceeds kRangeLimit compute A element by element
-// (Eq. 4, fp32, exp2 of the log-gate difference) instead.
+// The operands are prepared without LDS round trips: each wave owns KD/NW key
+// columns with one token row per lane, scans the gate down the 64 lanes with
+// DPP, and writes Qh, Kt and Ql straight to LDS.  O is accumulated transposed
+// (O^T = S^T Ql^T + V^T A^T) so each lane stores four consecutive columns.
+// Chunks whose gate range exceeds kRangeLimit rebuild A element by element
+// (Eq. 4, fp32, exp2 of the log-gate difference).
+template <typename T, int KD, int BV>
+struct WalkSmem {
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int pB = KD + 4;       // fp32 gate cumsum (exact-path chunks only)
+    static constexpr int pQ = KD + PT;
+    static constexpr int pV = BV + PT;
+    static constexpr int pA = kChunk + PT;
+    union {
+        float B[kChunk * pB];
+        T Ql[kChunk * pQ];                  // q * Lambda
+    };
+    T Q[kChunk * pQ];                       // q * exp2(B_t - B_63), raw q on exact-path chunks
+    T K[kChunk * pQ];                       // k * exp2(B_63 - B_s), raw k while A is rebuilt exactly
+    T V[kChunk * pV];
+    T A[kChunk * pA];
+    float last[KD];
+    float gam[KD];
+    int flag[2];
+};
+
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
@@ -72,7 +93,8 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
              int T_, int H, int V, int N, int P, int seg_len) {
     constexpr int NT = NW * 64;
     constexpr int CB = BV / NW / 16;
-    using Sm = ChunkSmem<T, KD, BV, NT>;
+    constexpr int CPK = KD / NW;            // key columns per wave in the row-slab preparation
+    using Sm = WalkSmem<T, KD, BV>;
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int nvb = V / BV;
@@ -86,121 +108,159 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     const int c_end = min(N, c_begin + seg_len);
     const int rsK = H * KD, rsV = H * V;
     const int col0 = w * (BV / NW);
+    const int kc0 = w * CPK;
 
     // zero the strictly-upper 16x16 tiles of A once; they are never written
     for (int e = tid; e < kChunk * kChunk; e += NT) {
         const int t = e / kChunk, s = e % kChunk;
         if ((s >> 4) > (t >> 4)) sm.A[t * Sm::pA + s] = Elem<T>::from_f(0.f);
     }
+    if (tid < 2) sm.flag[tid] = 0;
 
     StateRegs<KD, CB> S;
     if (s_init) S.load(s_init + (long)bh * s_init_bh_stride + (long)seg * s_init_seg_stride + v0, V, col0);
     else S.zero();
 
-    TileRegs<T, KD, NT> rq, rk, rg;
+    RowSlab<T, CPK> rq, rk, rg;
     TileRegs<T, BV, NT> rv;
-    using TR = TileRegs<T, KD, NT>;
-    // uniform per-chunk bases: element (token 0 of chunk c, head h)
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
     auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + v0; };
     auto obase_of = [&](int c) { return o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + v0; };
-    rq.load(kbase(q, c_begin), rsK, tid);
-    rk.load(kbase(k, c_begin), rsK, tid);
-    rg.load(kbase(g, c_begin), rsK, tid);
+    rq.load(kbase(q, c_begin), rsK, kc0);
+    rk.load(kbase(k, c_begin), rsK, kc0);
+    rg.load(kbase(g, c_begin), rsK, kc0);
     rv.load(vbase(v, c_begin), rsV, tid);
+    __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         const bool more = c + 1 < c_end;
-        if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
-        const bool exact = sm.flag != 0;
-        // (b) operands of the intra-chunk tiles
+        // (a) gate cumsum down the lanes, decays, operands
+        {
+            float bt[CPK], bl[CPK];
+            float rng = -3.0e38f;
 #pragma unroll
-        for (int p = 0; p < TR::PER; ++p) {
-            if (!TR::owns(p, tid)) continue;
-            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
-            float qv[TR::VEC], kv[TR::VEC];
+            for (int j = 0; j < CPK; ++j) {
+                bt[j] = wave_incl_scan(rg.get(j) * kLog2e);
+                bl[j] = lane_bcast(bt[j], 63);
+                rng = fmaxf(rng, lane_bcast(bt[j], 0) - bl[j]);
+            }
+            if (l == 0) {
+                if (rng > kRangeLimit) sm.flag[c & 1] = 1;
 #pragma unroll
-            for (int e = 0; e < TR::VEC; ++e) {
-                const float bt = sm.B[row * Sm::pB + c0 + e], bl = sm.last[c0 + e];
-                qv[e] = rq.get(p, e);
-                kv[e] = rk.get(p, e);
-                if (!exact) {
-                    qv[e] *= exp2_fast(bt - bl);
-                    kv[e] *= exp2_fast(bl - bt);
+                for (int j = 0; j < CPK; ++j) {
+                    sm.last[kc0 + j] = bl[j];
+                    sm.gam[kc0 + j] = exp2_fast(bl[j]);
                 }
             }
-            store_vec_lds<T>(sm.Q + row * Sm::pQ + c0, qv);
-            store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
+            constexpr int VEC = 16 / (int)sizeof(T);
+#pragma unroll
+            for (int j0 = 0; j0 < CPK; j0 += VEC) {
+                float qh[VEC], kt[VEC], ql[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int j = j0 + e;
+                    const float qq = rq.get(j), kk = rk.get(j);
+                    qh[e] = qq * exp2_fast(bt[j] - bl[j]);
+                    kt[e] = kk * exp2_fast(bl[j] - bt[j]);
+                    ql[e] = qq * exp2_fast(bt[j]);
+                }
+                store_vec_lds<T>(sm.Q + l * Sm::pQ + kc0 + j0, qh);
+                store_vec_lds<T>(sm.K + l * Sm::pQ + kc0 + j0, kt);
+                store_vec_lds<T>(sm.Ql + l * Sm::pQ + kc0 + j0, ql);
+            }
         }
         rv.store_lds(sm.V, Sm::pV, tid);
         if (more) {
-            rk.load(kbase(k, c + 1), rsK, tid);
-            rg.load(kbase(g, c + 1), rsK, tid);
+            rq.load(kbase(q, c + 1), rsK, kc0);
+            rk.load(kbase(k, c + 1), rsK, kc0);
+            rg.load(kbase(g, c + 1), rsK, kc0);
             rv.load(vbase(v, c + 1), rsV, tid);
         }
         __syncthreads();
-        // (c) A tiles, and Q*Lambda into registers
-        for (int tile = w; tile < 10; tile += NW) {
-            int is, js;
-            decode_tile(tile, is, js);
-            f32x4 acc = zero4();
-            if (!exact) {
+        const bool exact = sm.flag[c & 1] != 0;
+        if (tid == 0) sm.flag[(c + 1) & 1] = 0;
+        if (exact) {
+            // rebuild A from raw q, k and the fp32 cumsum (element-wise Eq. 4)
+            RowSlab<T, CPK> xq, xk, xg;
+            xq.load(kbase(q, c), rsK, kc0);
+            xk.load(kbase(k, c), rsK, kc0);
+            xg.load(kbase(g, c), rsK, kc0);
+            float bt[CPK], bl[CPK];
 #pragma unroll
-                for (int ks = 0; ks < KD / 32; ++ks) {
-                    vec4_t<T> alo = frag_rm<T>(sm.K, Sm::pK, 16 * js, 32 * ks);
-                    vec4_t<T> ahi = frag_rm<T>(sm.K, Sm::pK, 16 * js, 32 * ks + 16);
-                    vec4_t<T> blo = frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks);
-                    vec4_t<T> bhi = frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks + 16);
-                    acc = mma32(acc, alo, ahi, blo, bhi);
+            for (int j = 0; j < CPK; ++j) {
+                bt[j] = wave_incl_scan(xg.get(j) * kLog2e);
+                bl[j] = lane_bcast(bt[j], 63);
+            }
+            __syncthreads();
+            constexpr int VEC = 16 / (int)sizeof(T);
+#pragma unroll
+            for (int j0 = 0; j0 < CPK; j0 += VEC) {
+                float qq[VEC], kk[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    qq[e] = xq.get(j0 + e);
+                    kk[e] = xk.get(j0 + e);
+                    sm.B[l * Sm::pB + kc0 + j0 + e] = bt[j0 + e];
                 }
-            } else {
+                store_vec_lds<T>(sm.Q + l * Sm::pQ + kc0 + j0, qq);
+                store_vec_lds<T>(sm.K + l * Sm::pQ + kc0 + j0, kk);
+            }
+            __syncthreads();
+            for (int tile = w; tile < 10; tile += NW) {
+                int is, js;
+                decode_tile(tile, is, js);
                 const int t = 16 * is + (l & 15);
+                f32x4 acc;
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * js + 4 * (l >> 4) + r;
                     float sum = 0.f;
                     if (s <= t)
                         for (int i = 0; i < KD; ++i)
-                            sum += Elem<T>::to_f(sm.Q[t * Sm::pQ + i]) * Elem<T>::to_f(sm.K[s * Sm::pK + i]) *
+                            sum += Elem<T>::to_f(sm.Q[t * Sm::pQ + i]) * Elem<T>::to_f(sm.K[s * Sm::pQ + i]) *
                                    exp2_fast(sm.B[t * Sm::pB + i] - sm.B[s * Sm::pB + i]);
                     acc[r] = sum;
                 }
+                *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
+                    to_vec4<T>(acc);
             }
-            // acc holds A^T[s][t] for s = 16js + 4(l/16) + r, t = 16is + l%16
-            if (is == js) {
+            __syncthreads();
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * (l >> 4) + r > (l & 15)) acc[r] = 0.f;
+            for (int j0 = 0; j0 < CPK; j0 += VEC) {
+                float kt[VEC], ql[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int j = j0 + e;
+                    kt[e] = xk.get(j) * exp2_fast(bl[j] - bt[j]);
+                    ql[e] = xq.get(j) * exp2_fast(bt[j]);
+                }
+                store_vec_lds<T>(sm.K + l * Sm::pQ + kc0 + j0, kt);
+                store_vec_lds<T>(sm.Ql + l * Sm::pQ + kc0 + j0, ql);
             }
-            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
-                to_vec4<T>(acc);
-        }
-        float ql[TR::PER][TR::VEC];
+        } else {
+            // (b) A tiles from Qh and Kt
+            for (int tile = w; tile < 10; tile += NW) {
+                int is, js;
+                decode_tile(tile, is, js);
+                f32x4 acc = zero4();
 #pragma unroll
-        for (int p = 0; p < TR::PER; ++p) {
-            if (!TR::owns(p, tid)) continue;
-            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
+                for (int ks = 0; ks < KD / 32; ++ks) {
+                    vec4_t<T> alo = frag_rm<T>(sm.K, Sm::pQ, 16 * js, 32 * ks);
+                    vec4_t<T> ahi = frag_rm<T>(sm.K, Sm::pQ, 16 * js, 32 * ks + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks);
+                    vec4_t<T> bhi = frag_rm<T>(sm.Q, Sm::pQ, 16 * is, 32 * ks + 16);
+                    acc = mma32(acc, alo, ahi, blo, bhi);
+                }
+                // acc holds A^T[s][t] for s = 16js + 4(l/16) + r, t = 16is + l%16
+                if (is == js) {
 #pragma unroll
-            for (int e = 0; e < TR::VEC; ++e) ql[p][e] = rq.get(p, e) * exp2_fast(sm.B[row * Sm::pB + c0 + e]);
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * (l >> 4) + r > (l & 15)) acc[r] = 0.f;
+                }
+                *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
+                    to_vec4<T>(acc);
+            }
         }
         __syncthreads();
-        // (d) Q*Lambda over the q tile; K*Gamma in place for exact-path chunks
-#pragma unroll
-        for (int p = 0; p < TR::PER; ++p) {
-            if (!TR::owns(p, tid)) continue;
-            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
-            store_vec_lds<T>(sm.Q + row * Sm::pQ + c0, ql[p]);
-            if (exact) {
-                float kv[TR::VEC];
-#pragma unroll
-                for (int e = 0; e < TR::VEC; ++e)
-                    kv[e] = Elem<T>::to_f(sm.K[row * Sm::pK + c0 + e]) *
-                            exp2_fast(sm.last[c0 + e] - sm.B[row * Sm::pB + c0 + e]);
-                store_vec_lds<T>(sm.K + row * Sm::pK + c0, kv);
-            }
-        }
-        if (more) rq.load(kbase(q, c + 1), rsK, tid);
-        __syncthreads();
-        // (e) outputs from the state before this chunk, then the state update
+        // (c) outputs from the state before this chunk, then the state update
         {
             vec4_t<T> sf[KD / 32][CB][2];
 #pragma unroll
@@ -224,8 +284,8 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                 // O^T[j][t] = sum_i S[i][j] Ql[t][i] + sum_s V[s][j] A[t][s]
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks) {
-                    vec4_t<T> blo = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks);
-                    vec4_t<T> bhi = frag_rm<T>(sm.Q, Sm::pQ, 16 * rb, 32 * ks + 16);
+                    vec4_t<T> blo = frag_rm<T>(sm.Ql, Sm::pQ, 16 * rb, 32 * ks);
+                    vec4_t<T> bhi = frag_rm<T>(sm.Ql, Sm::pQ, 16 * rb, 32 * ks + 16);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) acc[cb] = mma32(acc[cb], sf[ks][cb][0], sf[ks][cb][1], blo, bhi);
                 }
@@ -244,7 +304,8 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                                                   4 * (l >> 4)) = to_vec4<T>(acc[cb]);
             }
         }
-        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.gam, col0);
+        state_update<T, KD, CB>(S, sm.K, Sm::pQ, sm.V, Sm::pV, sm.gam, col0);
+        __syncthreads();
     }
     if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V + v0, V, col0);
 }
@@ -256,6 +317,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
+    static_assert(sizeof(WalkSmem<T, KD, BV>) <= 160 * 1024, "LDS budget");
     const int nvb = a.V / BV;
     const long KV = (long)KD * a.V;
     if (a.P > 1) {
