@@ -52,29 +52,36 @@ struct RowSmem {
     int flag;
 };
 
-// Transposed state tiles of the row-split kernels: element (j, i) of S^T for
-// rows j = 0..V-1 and this wave's IBW blocks of 16 key rows i.  Tile (jb, ib)
-// slot r holds j = 16*jb + 4*(l/16) + r, i = 16*(w*IBW + ib) + l%16.
-template <int V, int IBW>
+// Transposed state tiles of the row-split kernels.  A wave owns 16 key rows
+// i0..i0+15 and VW value rows j0..j0+VW-1 of S^T: tile jb slot r holds
+// j = j0 + 16*jb + 4*(l/16) + r, i = i0 + l%16.
+template <int VW>
 struct TStateRegs {
-    f32x4 s[V / 16][IBW];
+    f32x4 s[VW / 16];
     __device__ __forceinline__ void zero() {
 #pragma unroll
-        for (int jb = 0; jb < V / 16; ++jb)
-#pragma unroll
-            for (int ib = 0; ib < IBW; ++ib) s[jb][ib] = zero4();
+        for (int jb = 0; jb < VW / 16; ++jb) s[jb] = zero4();
     }
-    // src points at row k0 of a [K][V] fp32 state
-    __device__ __forceinline__ void load(const float* __restrict__ src, int w) {
+    // src points at element (0, 0) of a [K][ld] fp32 state block
+    __device__ __forceinline__ void load(const float* __restrict__ src, int ld, int i0, int j0) {
         const int l = lane_id();
+        const float* p = src + (long)(i0 + (l & 15)) * ld + j0 + 4 * (l >> 4);
 #pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const int i = 16 * (w * IBW + ib) + (l & 15);
-#pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb)
-                s[jb][ib] = *reinterpret_cast<const f32x4*>(src + (long)i * V + 16 * jb + 4 * (l >> 4));
-        }
+        for (int jb = 0; jb < VW / 16; ++jb) s[jb] = *reinterpret_cast<const f32x4*>(p + 16 * jb);
     }
+};
+
+// Wave roles of the row-split kernels: NW waves cover BK/16 key blocks times
+// VS (1 or 2) value slices.  With two slices, contractions over V are summed
+// through LDS and the slice-0 wave of a key block finishes its outputs.
+template <int BK, int V, int NW>
+struct RowRoles {
+    static constexpr int NKQ = BK / 16;
+    static constexpr int VS = NW / NKQ;
+    static constexpr int VW = V / VS;
+    static_assert(NKQ * VS == NW, "waves must tile key blocks x value slices");
+    static_assert(VS == 1 || VS == 2, "one or two value slices");
+    static_assert(VW % 32 == 0, "value slice must be a whole number of 32-wide MFMA steps");
 };
 
 // The ten lower-triangular 16x16 tiles of dP = (dO V^T) * M, contraction over
@@ -116,80 +123,47 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
 }
 
 // ---------------------------------------------------------------------------
-// Backward combine.  One workgroup per (head, key row i), threads over j.
+// Backward combine, one thread per state element; blockIdx.z = 0 combines the
+// states, 1 the state gradients:
 //   S_init(0) = S_0;  S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p
 //   dS_end(P-1) = dht; dS_end(p-1) = Diag(exp2 G_p) dS_end(p) + dS*_p
 // ws_state / ws_dstate hold S*_p / dS*_p on entry and S_init / dS_end on exit.
 __global__ void __launch_bounds__(256)
 gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht, float* __restrict__ ws_state,
                     float* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
-    const int i = blockIdx.x;
-    const long bh = blockIdx.y;
     const long KV = (long)K * V;
-    const int tid = threadIdx.x;
-    const bool has = tid < V, has2 = tid + 256 < V;
-    const int j0 = tid, j1 = tid + 256;
-    float* st = ws_state + bh * P * KV + (long)i * V;
-    float* ds = ws_dstate + bh * P * KV + (long)i * V;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long bh = blockIdx.y;
+    if (e >= KV) return;
+    const int i = (int)(e / V);
     const float* gt = ws_gate + bh * P * (long)K + i;
-    float c0 = 0.f, c1 = 0.f;
-    if (s0) {
-        if (has) c0 = s0[bh * KV + (long)i * V + j0];
-        if (has2) c1 = s0[bh * KV + (long)i * V + j1];
-    }
-    for (int p = 0; p < P; ++p) {
-        float a0 = 0.f, a1 = 0.f;
-        if (p + 1 < P) {
-            if (has) a0 = st[p * KV + j0];
-            if (has2) a1 = st[p * KV + j1];
-        }
-        if (has) st[p * KV + j0] = c0;
-        if (has2) st[p * KV + j1] = c1;
-        if (p + 1 < P) {
-            const float gm = exp2_fast(gt[p * (long)K]);
-            c0 = gm * c0 + a0;
-            c1 = gm * c1 + a1;
-        }
-    }
-    float d0 = 0.f, d1 = 0.f;
-    if (dht) {
-        if (has) d0 = dht[bh * KV + (long)i * V + j0];
-        if (has2) d1 = dht[bh * KV + (long)i * V + j1];
-    }
-    for (int p = P - 1; p >= 0; --p) {
-        float a0 = 0.f, a1 = 0.f;
-        if (p >= 1) {
-            if (has) a0 = ds[p * KV + j0];
-            if (has2) a1 = ds[p * KV + j1];
-        }
-        if (has) ds[p * KV + j0] = d0;
-        if (has2) ds[p * KV + j1] = d1;
-        if (p >= 1) {
-            const float gm = exp2_fast(gt[p * (long)K]);
-            d0 = gm * d0 + a0;
-            d1 = gm * d1 + a1;
-        }
-    }
+    if (blockIdx.z == 0)
+        combine_element<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0[bh * KV + e] : 0.f);
+    else
+        combine_element<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht[bh * KV + e] : 0.f);
 }
 
 // ---------------------------------------------------------------------------
 // dq walk: forwards over one segment for key rows k0 .. k0+BK-1, full V.
-// State S^T in VGPRs; dq_t = exp2(B_t - B_63) * [dO (gamma*S)^T + dP (K*Gamma)]_t
+// State S^T in VGPRs.  dq_t = exp2(B_t - B_63) * [dO (gamma*S)^T + dP (K*Gamma)]_t
 // (both terms share the factor; exact-path chunks use the element-wise form),
 // accumulated transposed so each lane stores four consecutive key columns.
-// After each chunk the state S_out is stored to `hs` (dtype) in this kernel's
-// own tile order, for the dk walk's chunk-boundary gate-gradient term.
+// After each chunk the state S_out is stored to `hs` (dtype) tile by tile, in
+// an order the dk walk reads back for its chunk-boundary gate-gradient term.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
            const float* __restrict__ s_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dq,
            T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len) {
     constexpr int NT = NW * 64;
-    constexpr int IBW = BK / 16 / NW;
-    static_assert(IBW >= 1 && IBW * 16 * NW == BK, "waves must tile the key rows");
+    using RR = RowRoles<BK, V, NW>;
+    constexpr int VW = RR::VW;
     using Sm = RowSmem<T, BK, V, NT>;
     __shared__ Sm sm;
+    __shared__ f32x4 s_red[RR::VS > 1 ? RR::NKQ * 4 * 64 : 1];  // partial dq^T of value slice 1
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int kq = w % RR::NKQ, vs = w / RR::NKQ;
+    const int i0 = 16 * kq, j0 = vs * VW;
     const int nkb = K / BK;
     int bid = blockIdx.x;
     const int kb = bid % nkb; bid /= nkb;
@@ -204,8 +178,8 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
         const int t = e / kChunk, s = e % kChunk;
         if ((s >> 4) > (t >> 4)) sm.P[t * Sm::pP + s] = Elem<T>::from_f(0.f);
     }
-    TStateRegs<V, IBW> S;
-    if (s_init) S.load(s_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, w);
+    TStateRegs<VW> S;
+    if (s_init) S.load(s_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, V, i0, j0);
     else S.zero();
 
     using TRK = TileRegs<T, BK, NT>;
@@ -244,33 +218,44 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
         __syncthreads();
         dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         __syncthreads();
-        T* dqbase = const_cast<T*>(kbase(dq, c));
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const int i0 = 16 * (w * IBW + ib);
+        // dq^T[i][t] = sum_j (gamma S)[i][j] dO[t][j] + sum_s Kt[s][i] dP[t][s], this wave's j range
+        f32x4 acc[4];
+        {
             const float gl = exact ? 1.f : sm.gam[i0 + (l & 15)];
-            vec4_t<T> sf[V / 32][2];
+            vec4_t<T> sf[VW / 32][2];
 #pragma unroll
-            for (int ks = 0; ks < V / 32; ++ks) {
-                sf[ks][0] = to_vec4<T>(S.s[2 * ks][ib] * gl);
-                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1][ib] * gl);
+            for (int ks = 0; ks < VW / 32; ++ks) {
+                sf[ks][0] = to_vec4<T>(S.s[2 * ks] * gl);
+                sf[ks][1] = to_vec4<T>(S.s[2 * ks + 1] * gl);
             }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                // dq^T[i][t] = sum_j (gamma S)[i][j] dO[t][j] + sum_s Kt[s][i] dP[t][s]
-                f32x4 acc = zero4();
+                acc[tb] = zero4();
 #pragma unroll
-                for (int ks = 0; ks < V / 32; ++ks)
-                    acc = mma32(acc, sf[ks][0], sf[ks][1], frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks),
-                                frag_rm<T>(sm.dO, Sm::pV, 16 * tb, 32 * ks + 16));
-                if (!exact) {
+                for (int ks = 0; ks < VW / 32; ++ks)
+                    acc[tb] = mma32(acc[tb], sf[ks][0], sf[ks][1], frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks),
+                                    frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks + 16));
+                if (!exact && vs == 0) {
 #pragma unroll
                     for (int ks2 = 0; ks2 <= tb / 2; ++ks2)
-                        acc = mma32(acc, frag_cm<T>(sm.X, Sm::pX, 32 * ks2, i0),
-                                    frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, i0),
-                                    frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
-                                    frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16));
+                        acc[tb] = mma32(acc[tb], frag_cm<T>(sm.X, Sm::pX, 32 * ks2, i0),
+                                        frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, i0),
+                                        frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
+                                        frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16));
                 }
+            }
+        }
+        if (RR::VS > 1) {
+            if (vs == 1)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) s_red[(kq * 4 + tb) * 64 + l] = acc[tb];
+            __syncthreads();
+        }
+        if (vs == 0) {
+            T* dqbase = const_cast<T*>(kbase(dq, c));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                if (RR::VS > 1) acc[tb] += s_red[(kq * 4 + tb) * 64 + l];
                 // slot r: key row i = i0 + 4(l/16) + r, token t = 16tb + l%16
                 const int t = 16 * tb + (l & 15), ic = i0 + 4 * (l >> 4);
                 const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.B + t * Sm::pB + ic);
@@ -278,11 +263,11 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
                 if (!exact) {
                     const f32x4 bl = *reinterpret_cast<const f32x4*>(sm.last + ic);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) val[r] = acc[r] * exp2_fast(bt[r] - bl[r]);
+                    for (int r = 0; r < 4; ++r) val[r] = acc[tb][r] * exp2_fast(bt[r] - bl[r]);
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        val[r] = acc[r] * exp2_fast(bt[r]);
+                        val[r] = acc[tb][r] * exp2_fast(bt[r]);
                         for (int s = 0; s <= t; ++s)
                             val[r] += Elem<T>::to_f(sm.P[t * Sm::pP + s]) * Elem<T>::to_f(sm.X[s * Sm::pX + ic + r]) *
                                       exp2_fast(bt[r] - sm.B[s * Sm::pB + ic + r]);
@@ -307,37 +292,27 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
             __syncthreads();
         }
         // S^T <- S^T Diag(gamma) + V^T (K*Gamma)
+        {
+            const float gl = sm.gam[i0 + (l & 15)];
 #pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const float gl = sm.gam[16 * (w * IBW + ib) + (l & 15)];
-#pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gl;
+            for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= gl;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            vec4_t<T> xf[IBW][2];
+            const vec4_t<T> x0 = frag_cm<T>(sm.X, Sm::pX, 32 * ks, i0);
+            const vec4_t<T> x1 = frag_cm<T>(sm.X, Sm::pX, 32 * ks + 16, i0);
 #pragma unroll
-            for (int ib = 0; ib < IBW; ++ib) {
-                xf[ib][0] = frag_cm<T>(sm.X, Sm::pX, 32 * ks, 16 * (w * IBW + ib));
-                xf[ib][1] = frag_cm<T>(sm.X, Sm::pX, 32 * ks + 16, 16 * (w * IBW + ib));
-            }
-#pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb) {
-                vec4_t<T> alo = frag_cm<T>(sm.Vt, Sm::pV, 32 * ks, 16 * jb);
-                vec4_t<T> ahi = frag_cm<T>(sm.Vt, Sm::pV, 32 * ks + 16, 16 * jb);
-#pragma unroll
-                for (int ib = 0; ib < IBW; ++ib) S.s[jb][ib] = mma32(S.s[jb][ib], alo, ahi, xf[ib][0], xf[ib][1]);
-            }
+            for (int jb = 0; jb < VW / 16; ++jb)
+                S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.Vt, Sm::pV, 32 * ks, j0 + 16 * jb),
+                                frag_cm<T>(sm.Vt, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
         }
-        // S_out of this chunk: tile (jb, ib) of wave w is 64 lanes x 4 contiguous elements
+        // S_out of this chunk: tile (key block kq, value block J) is 64 lanes x 4 contiguous elements
         {
             T* dst = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
 #pragma unroll
-            for (int ib = 0; ib < IBW; ++ib)
-#pragma unroll
-                for (int jb = 0; jb < V / 16; ++jb)
-                    *reinterpret_cast<vec4_t<T>*>(dst + (((w * IBW + ib) * (V / 16) + jb) * 64 + l) * 4) =
-                        to_vec4<T>(S.s[jb][ib]);
+            for (int jb = 0; jb < VW / 16; ++jb)
+                *reinterpret_cast<vec4_t<T>*>(dst + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4) =
+                    to_vec4<T>(S.s[jb]);
         }
         __syncthreads();
     }
@@ -356,13 +331,16 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
            long s_bh_stride, const T* __restrict__ hs, T* __restrict__ dk, T* __restrict__ dg, int T_, int H,
            int K, int N, int P, int seg_len) {
     constexpr int NT = NW * 64;
-    constexpr int IBW = BK / 16 / NW;
-    static_assert(IBW >= 1 && IBW * 16 * NW == BK, "waves must tile the key rows");
+    using RR = RowRoles<BK, V, NW>;
+    constexpr int VW = RR::VW;
     using Sm = RowSmem<T, BK, V, NT>;
     __shared__ Sm sm;
-    __shared__ float s_carry[BK];
+    __shared__ float s_carry[RR::VS * BK];
     __shared__ T s_ql[kChunk * Sm::pX];  // q*Lambda for the dS update
+    __shared__ f32x4 s_red[RR::VS > 1 ? RR::NKQ * 4 * 64 : 1];  // partial dk^T of value slice 1
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int kq = w % RR::NKQ, vs = w / RR::NKQ;
+    const int i0 = 16 * kq, j0 = vs * VW;
     const int nkb = K / BK;
     int bid = blockIdx.x;
     const int kb = bid % nkb; bid /= nkb;
@@ -379,8 +357,8 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         const int s = e / kChunk, t = e % kChunk;
         if ((t >> 4) < (s >> 4)) sm.P[s * Sm::pP + t] = Elem<T>::from_f(0.f);
     }
-    TStateRegs<V, IBW> S;
-    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, w);
+    TStateRegs<VW> S;
+    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, V, i0, j0);
     else S.zero();
 
     // reverse-scan layout: thread (column, part) owns R rows of one key column
@@ -433,36 +411,56 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         __syncthreads();
         dp_tiles<T, V, true>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         __syncthreads();
-        T* dkbase = const_cast<T*>(kbase(dk, c));
-        f32x4 dkr[IBW][4];
+        // dk^T[i][s] = sum_j dS[i][j] V[s][j] (this wave's j range) + sum_t Qh[t][i] dP^T[s][t]
+        f32x4 dkr[4];
 #pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const int i0 = 16 * (w * IBW + ib);
+        for (int sb = 0; sb < 4; ++sb) dkr[sb] = zero4();
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) dkr[ib][sb] = zero4();
-            // dk^T[i][s] = sum_j dS[i][j] V[s][j] + sum_t Qh[t][i] dP^T[s][t]
+        for (int ks = 0; ks < VW / 32; ++ks) {
+            const vec4_t<T> alo = to_vec4<T>(S.s[2 * ks]);
+            const vec4_t<T> ahi = to_vec4<T>(S.s[2 * ks + 1]);
 #pragma unroll
-            for (int ks = 0; ks < V / 32; ++ks) {
-                const vec4_t<T> alo = to_vec4<T>(S.s[2 * ks][ib]);
-                const vec4_t<T> ahi = to_vec4<T>(S.s[2 * ks + 1][ib]);
+            for (int sb = 0; sb < 4; ++sb)
+                dkr[sb] = mma32(dkr[sb], alo, ahi, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks),
+                                frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks + 16));
+        }
+        if (!exact && vs == 0) {
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    dkr[ib][sb] = mma32(dkr[ib][sb], alo, ahi, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks),
-                                        frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, 32 * ks + 16));
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                const vec4_t<T> alo = frag_cm<T>(sm.X, Sm::pX, 32 * ks2, i0);
+                const vec4_t<T> ahi = frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, i0);
+#pragma unroll
+                for (int sb = 0; sb <= 2 * ks2 + 1; ++sb)
+                    dkr[sb] = mma32(dkr[sb], alo, ahi, frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
+                                    frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16));
             }
-            if (!exact) {
+        }
+        // sum over later tokens for dg: rowsum(S_out * dS_out) at this chunk's end, this wave's j range
+        {
+            const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+            float part = 0.f;
 #pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2) {
-                    const vec4_t<T> alo = frag_cm<T>(sm.X, Sm::pX, 32 * ks2, i0);
-                    const vec4_t<T> ahi = frag_cm<T>(sm.X, Sm::pX, 32 * ks2 + 16, i0);
+            for (int jb = 0; jb < VW / 16; ++jb) {
+                const vec4_t<T> so =
+                    *reinterpret_cast<const vec4_t<T>*>(src + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4);
 #pragma unroll
-                    for (int sb = 0; sb <= 2 * ks2 + 1; ++sb)
-                        dkr[ib][sb] = mma32(dkr[ib][sb], alo, ahi, frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
-                                            frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16));
-                }
+                for (int r = 0; r < 4; ++r) part += Elem<T>::to_f(so[r]) * S.s[jb][r];
             }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if ((l >> 4) == 0) s_carry[vs * BK + i0 + (l & 15)] = part;
+        }
+        if (RR::VS > 1) {
+            if (vs == 1)
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) s_red[(kq * 4 + sb) * 64 + l] = dkr[sb];
+            __syncthreads();
+        }
+        if (vs == 0) {
+            T* dkbase = const_cast<T*>(kbase(dk, c));
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
+                if (RR::VS > 1) dkr[sb] += s_red[(kq * 4 + sb) * 64 + l];
                 // slot r: key row i = i0 + 4(l/16) + r, token s = 16sb + l%16
                 const int s = 16 * sb + (l & 15), ic = i0 + 4 * (l >> 4);
                 const f32x4 bs = *reinterpret_cast<const f32x4*>(sm.B + s * Sm::pB + ic);
@@ -470,65 +468,37 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
                 f32x4 val;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    val[r] = dkr[ib][sb][r] * exp2_fast(bl[r] - bs[r]);
+                    val[r] = dkr[sb][r] * exp2_fast(bl[r] - bs[r]);
                     if (exact)
                         for (int t = s; t < kChunk; ++t)
                             val[r] += Elem<T>::to_f(sm.P[s * Sm::pP + t]) * Elem<T>::to_f(sm.X[t * Sm::pX + ic + r]) *
                                       exp2_fast(sm.B[t * Sm::pB + ic + r] - bs[r]);
                 }
-                dkr[ib][sb] = val;
+                dkr[sb] = val;
                 *reinterpret_cast<vec4_t<T>*>(dkbase + s * rsK + ic) = to_vec4<T>(val);
-            }
-        }
-        // sum over later tokens for dg: rowsum(S_out * dS_out) at this chunk's end
-        {
-            const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
-#pragma unroll
-            for (int ib = 0; ib < IBW; ++ib) {
-                float part = 0.f;
-#pragma unroll
-                for (int jb = 0; jb < V / 16; ++jb) {
-                    const vec4_t<T> so =
-                        *reinterpret_cast<const vec4_t<T>*>(src + (((w * IBW + ib) * (V / 16) + jb) * 64 + l) * 4);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) part += Elem<T>::to_f(so[r]) * S.s[jb][ib][r];
-                }
-                part += __shfl_xor(part, 16);
-                part += __shfl_xor(part, 32);
-                if ((l >> 4) == 0) s_carry[16 * (w * IBW + ib) + (l & 15)] = part;
             }
         }
         __syncthreads();
         // dk (fp32) replaces the gate cumsum in LDS
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib)
+        if (vs == 0)
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb)
-                *reinterpret_cast<f32x4*>(sm.B + (16 * sb + (l & 15)) * Sm::pB + 16 * (w * IBW + ib) + 4 * (l >> 4)) =
-                    dkr[ib][sb];
+                *reinterpret_cast<f32x4*>(sm.B + (16 * sb + (l & 15)) * Sm::pB + i0 + 4 * (l >> 4)) = dkr[sb];
         __syncthreads();
         // dS^T <- dS^T Diag(gamma) + dO^T (q*Lambda)
+        {
+            const float gl = sm.gam[i0 + (l & 15)];
 #pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const float gl = sm.gam[16 * (w * IBW + ib) + (l & 15)];
-#pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb) S.s[jb][ib] *= gl;
+            for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= gl;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            vec4_t<T> xf[IBW][2];
+            const vec4_t<T> x0 = frag_cm<T>(s_ql, Sm::pX, 32 * ks, i0);
+            const vec4_t<T> x1 = frag_cm<T>(s_ql, Sm::pX, 32 * ks + 16, i0);
 #pragma unroll
-            for (int ib = 0; ib < IBW; ++ib) {
-                xf[ib][0] = frag_cm<T>(s_ql, Sm::pX, 32 * ks, 16 * (w * IBW + ib));
-                xf[ib][1] = frag_cm<T>(s_ql, Sm::pX, 32 * ks + 16, 16 * (w * IBW + ib));
-            }
-#pragma unroll
-            for (int jb = 0; jb < V / 16; ++jb) {
-                vec4_t<T> alo = frag_cm<T>(sm.dO, Sm::pV, 32 * ks, 16 * jb);
-                vec4_t<T> ahi = frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, 16 * jb);
-#pragma unroll
-                for (int ib = 0; ib < IBW; ++ib) S.s[jb][ib] = mma32(S.s[jb][ib], alo, ahi, xf[ib][0], xf[ib][1]);
-            }
+            for (int jb = 0; jb < VW / 16; ++jb)
+                S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.dO, Sm::pV, 32 * ks, j0 + 16 * jb),
+                                frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
         }
         // dA = q*dq - k*dk, in place over dk
 #pragma unroll
@@ -553,6 +523,7 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
             sm.tot[spart * BK + scol] = acc;
             __syncthreads();
             float off = s_carry[scol];
+            if (RR::VS > 1) off += s_carry[BK + scol];
             for (int pp = spart + 1; pp < NPART; ++pp) off += sm.tot[pp * BK + scol];
 #pragma unroll
             for (int u = 0; u < R; ++u) {
@@ -762,7 +733,8 @@ static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
         GLA_LAUNCH("bwd_seg_state_rev", (gla_seg_state<T, KD, BV, NW, true>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.g, (const T*)a.d_o, a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P,
                            a.seg_len, 1, nseg);
-        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd, dim3((unsigned)KD, (unsigned)a.BH), dim3(256), a.stream, a.s0,
+        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd, dim3((unsigned)((KV + 255) / 256), (unsigned)a.BH, 2u),
+                           dim3(256), a.stream, a.s0,
                            a.dht, a.ws_state, a.ws_dstate, a.ws_gate, KD, a.V, a.P);
     }
     return hipGetLastError();
@@ -786,11 +758,13 @@ static hipError_t launch_dv(const BwdLaunch& a) {
 
 template <typename T, int BK, int V>
 static hipError_t launch_rows(const BwdLaunch& a) {
-    constexpr int NW = (BK / 16 < 8) ? BK / 16 : 8;
+    constexpr int NW = 8;
     constexpr int NT = NW * 64;
-    // dk walk: the row-split tiles plus its carry and q*Lambda tiles
-    static_assert(sizeof(RowSmem<T, BK, V, NT>) + sizeof(float) * BK +
-                      sizeof(T) * kChunk * RowSmem<T, BK, V, NT>::pX <= 160 * 1024,
+    using RR = RowRoles<BK, V, NW>;
+    // dk walk: the row-split tiles plus its carry, q*Lambda and partial-sum tiles
+    static_assert(sizeof(RowSmem<T, BK, V, NT>) + sizeof(float) * RR::VS * BK +
+                      sizeof(T) * kChunk * RowSmem<T, BK, V, NT>::pX +
+                      (RR::VS > 1 ? sizeof(f32x4) * RR::NKQ * 4 * 64 : 0) <= 160 * 1024,
                   "LDS budget");
     const int nkb = a.K / BK;
     const long KV = (long)a.K * V;

@@ -102,6 +102,37 @@ __device__ __forceinline__ void decode_tile(int tile, int& is, int& js) {
 }
 
 // ---------------------------------------------------------------------------
+// Step 2: the linear recurrence across segments for one state element.
+//   forwards  (REV = false): out[0] = init, out[p+1] = exp2(G_p) out[p] + in[p]
+//   backwards (REV = true):  out[P-1] = init, out[p-1] = exp2(G_p) out[p] + in[p]
+// `st` holds in[] on entry and out[] on exit (stride KV), `gt` the segment gate
+// totals G_p in log2 units (stride K).  The loads of U segments are issued
+// before any of their results is needed, so one thread keeps U independent
+// requests in flight rather than one per step.
+template <bool REV>
+__device__ __forceinline__ void combine_element(float* st, const float* gt, long KV, long K, int P, float cur) {
+    constexpr int U = 8;
+    for (int b0 = 0; b0 < P; b0 += U) {
+        float a[U], gm[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = REV ? P - 1 - (b0 + u) : b0 + u;
+            const bool feeds = b0 + u < P && (REV ? p >= 1 : p + 1 < P);
+            a[u] = feeds ? st[p * KV] : 0.f;
+            gm[u] = feeds ? exp2_fast(gt[p * K]) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = REV ? P - 1 - (b0 + u) : b0 + u;
+            if (b0 + u < P) {
+                st[p * KV] = cur;
+                cur = gm[u] * cur + a[u];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Step 1: segment-local states.  REV = false: S*_p from the keys and values of
 // the segment walked forwards (decay Gamma = exp2(B_63 - B_t) on the keys).
 // REV = true: the backward pass's dS*_p from queries and d_o walked backwards

@@ -34,14 +34,8 @@ gla_seg_combine_fwd(const float* __restrict__ s0, float* __restrict__ ws_state, 
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
-    float cur = s0 ? s0[bh * KV + e] : 0.f;
-    float* st = ws_state + bh * P * KV + e;
-    const float* gt = ws_gate + bh * P * (long)K + i;
-    for (int p = 0; p < P; ++p) {
-        const float sp = (p + 1 < P) ? st[p * KV] : 0.f;
-        st[p * KV] = cur;
-        if (p + 1 < P) cur = exp2_fast(gt[p * (long)K]) * cur + sp;
-    }
+    combine_element<false>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                           s0 ? s0[bh * KV + e] : 0.f);
 }
 
 // Copy (or zero) a [BH][K][V] fp32 state: final state of an empty sequence.

@@ -38,10 +38,9 @@ inline int plan_bv(const Shape& s) {
 }
 
 // State rows per workgroup in the backward kernels that contract over V.  The
-// K-block x full-V state lives in VGPRs next to the chunk's prefetched tiles:
-// at V >= 128 (and for fp32) a 64-row block with four waves, which may use the
-// whole 512-entry register file per lane; otherwise up to 128 rows over eight
-// waves.
+// workgroup has eight waves; a 64-row block splits V between two waves per
+// 16-row key block, which keeps the state slice and the chunk's prefetched
+// tiles within 256 registers per lane.  Narrow V takes up to 128 rows whole.
 inline int plan_bk(const Shape& s) {
     if (!s.bf16 || s.V >= 128) return 64;
     return (int)(s.K < 128 ? s.K : 128);
@@ -54,7 +53,7 @@ inline Plan make_plan(const Shape& s, int col_blocks_hint) {
     p.BV = plan_bv(s);
     p.NW = p.BV / 16 < 8 ? p.BV / 16 : 8;
     p.BK = plan_bk(s);
-    p.NWK = p.BK / 16 < 8 ? p.BK / 16 : 8;
+    p.NWK = 8;
     int64_t per_seg = p.BH * (int64_t)col_blocks_hint;
     int64_t P = per_seg > 0 ? kTargetWorkgroups / per_seg : 1;
     if (P < 1) P = 1;
@@ -70,10 +69,20 @@ inline Plan make_fwd_plan(const Shape& s) {
     return make_plan(s, (int)(s.V / bv));
 }
 
+// The backward's column-split kernels take as many value blocks as the
+// row-split kernels take key blocks (never narrower than 64 columns), so both
+// kinds launch the same number of workgroups over the same segments.
 inline Plan make_bwd_plan(const Shape& s) {
-    const int bv = plan_bv(s), bk = plan_bk(s);
-    const int nvb = (int)(s.V / bv), nkb = (int)(s.K / bk);
-    return make_plan(s, nvb > nkb ? nvb : nkb);
+    const int bk = plan_bk(s);
+    const int nkb = (int)(s.K / bk);
+    int bv = plan_bv(s);
+    if (nkb > 1 && s.V / nkb < bv) bv = (int)(s.V / nkb);
+    if (bv < 64) bv = s.V < 64 ? (int)s.V : 64;
+    const int nvb = (int)(s.V / bv);
+    Plan p = make_plan(s, nvb > nkb ? nvb : nkb);
+    p.BV = bv;
+    p.NW = bv / 16 < 8 ? bv / 16 : 8;
+    return p;
 }
 
 inline size_t fwd_workspace_bytes(const Shape& s) {
