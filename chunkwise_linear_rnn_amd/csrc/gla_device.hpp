@@ -180,6 +180,13 @@ struct RowSlab {
 #pragma unroll
         for (int m = 0; m < NV; ++m) r[m] = *reinterpret_cast<const u32x4*>(p + m * VEC);
     }
+    // only the 16-byte vectors m0 .. m1-1 (columns c0 + m*VEC ..)
+    __device__ __forceinline__ void load_part(const T* __restrict__ base, int rs, int c0, int m0, int m1) {
+        const T* p = base + (lane_id() * rs + c0);
+#pragma unroll
+        for (int m = 0; m < NV; ++m)
+            if (m >= m0 && m < m1) r[m] = *reinterpret_cast<const u32x4*>(p + m * VEC);
+    }
     __device__ __forceinline__ float get(int c) const {
         const T* v = reinterpret_cast<const T*>(&r[c / VEC]);
         return Elem<T>::to_f(v[c % VEC]);
@@ -197,6 +204,24 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x142, 0xA, 0xF, false);
     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x143, 0xC, 0xF, false);
     return x;
+}
+
+// The same scan over N independent values per lane, step by step across the
+// values, so no DPP step waits on the one before it of the same value.
+template <int N>
+__device__ __forceinline__ void wave_incl_scan_n(float* x) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __builtin_amdgcn_update_dpp(0.0f, x[e], 0x111, 0xF, 0xF, false);
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __builtin_amdgcn_update_dpp(0.0f, x[e], 0x112, 0xF, 0xF, false);
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __builtin_amdgcn_update_dpp(0.0f, x[e], 0x114, 0xF, 0xF, false);
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __builtin_amdgcn_update_dpp(0.0f, x[e], 0x118, 0xF, 0xF, false);
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __builtin_amdgcn_update_dpp(0.0f, x[e], 0x142, 0xA, 0xF, false);
+#pragma unroll
+    for (int e = 0; e < N; ++e) x[e] += __builtin_amdgcn_update_dpp(0.0f, x[e], 0x143, 0xC, 0xF, false);
 }
 
 __device__ __forceinline__ float lane_bcast(float x, int lane) {

@@ -305,13 +305,341 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Step 3, software-pipelined (16-bit operands).  Same mathematics as
+// gla_fwd_walk, with the operands in the chunk-start basis
+//   Ql = q * exp2(B_t)   Kt = k * exp2(-B_s)   A[t][s] = sum_i Ql[t][i] Kt[s][i]
+//   S  <- Diag(gamma) (S + Kt^T V)
+// so two exp2 per element build both the intra and the inter operands.  A
+// column whose chunk decay exceeds kBasisLimit (log2 units) keeps the
+// reference-row key factor instead, Kt = k * exp2(B_63 - B_s), with the
+// state update S <- Diag(gamma) S + Kt^T V; such a chunk builds A element by
+// element (Eq. 4).  The state update is written as S <- post * (pre * S +
+// Kt^T V) with per-column (pre, post) = (1, gamma) or (gamma, 1).
+//
+// Two phases per chunk, one barrier after each:
+//   phase 1: A(c) from Ql(c), Kt(c);  preparation of chunk c+1 into the other
+//            buffer (DPP cumsum down the lanes, exp2, bf16 packing)
+//   phase 2: O(c) = Ql(c) S + A(c) V(c);  state update;  V(c+1) into the
+//            wave's own LDS slice
+// so the vector-ALU preparation of the next chunk overlaps the matrix work of
+// this one.  Each wave owns BV/NW value columns: its slice of V never needs a
+// workgroup barrier.
+constexpr float kBasisLimit = 96.0f;
+
+template <typename T, int KD, int BV, int NW>
+struct PipeSmem {
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int CW = BV / NW;      // value columns per wave
+    static constexpr int pQ = KD + PT;
+    static constexpr int pA = kChunk + PT;
+    static constexpr int pF = kChunk + 4;   // fp32 A of exact-path chunks
+    // wave-private V slices, read with ds_read_b64_tr_b16: the four rows a
+    // 16-lane group reads fall on disjoint banks at a pitch of 8 or 16 dwords
+    // (CW = 16 or 32 two-byte columns), and rows stay 16-byte aligned.  Two
+    // slices per wave when they fit, so the next chunk's V is written during
+    // phase 1 instead of being held in registers through phase 2.
+    static constexpr int pW = (sizeof(T) == 2 && (CW == 16 || CW == 32)) ? CW : CW + PT;
+    static constexpr int VB =
+        (2 * (2 * sizeof(T) * kChunk * pQ + 2 * sizeof(float) * KD + 16) + sizeof(T) * kChunk * pA +
+             2 * sizeof(T) * NW * kChunk * pW <= 160 * 1024) ? 2 : 1;
+    struct alignas(16) Buf {
+        T Ql[kChunk * pQ];
+        T Kt[kChunk * pQ];
+        float pre[KD];
+        float post[KD];
+        int flag[4];
+    };
+    static_assert(2 * sizeof(T) * kChunk * pQ >= sizeof(float) * kChunk * pF, "exact-path scratch");
+    Buf buf[2];
+    alignas(16) T A[kChunk * pA];
+    alignas(16) T Vw[VB * NW * kChunk * pW];
+};
+
+// One wave prepares 16-byte column groups m0 .. m1-1 of its key columns
+// kc0 .. kc0+NC-1 (lane = token row) from its register slabs of q, k and the
+// raw log gate.  Lane j collects B_63 of column kc0 + j and the factors are
+// formed once per lane at the end, so the column loop has no branches and the
+// scans of a group's VEC columns interleave.
+template <typename T, int NC, typename Buf>
+__device__ __forceinline__ void pipe_prep(Buf& bf, int pQ, const RowSlab<T, NC>& rq, const RowSlab<T, NC>& rk,
+                                          const RowSlab<T, NC>& rg, int kc0, int m0, int m1) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    static_assert(NC <= 64, "one lane per prepared column");
+    const int l = lane_id();
+    float last_l = 0.f;
+    bool wide = false;
+#pragma unroll
+    for (int m = 0; m < NC / VEC; ++m) {
+        if (m < m0 || m >= m1) continue;
+        const int j0 = m * VEC;
+        float bt[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
+        wave_incl_scan_n<VEC>(bt);
+        float ql[VEC], kt[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float bl = lane_bcast(bt[e], 63);
+            const bool in = -bl <= kBasisLimit;
+            wide |= !in;
+            last_l = (l == j0 + e) ? bl : last_l;
+            ql[e] = rq.get(j0 + e) * exp2_fast(bt[e]);
+            kt[e] = rk.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
+        }
+        store_vec_lds<T>(bf.Ql + l * pQ + kc0 + j0, ql);
+        store_vec_lds<T>(bf.Kt + l * pQ + kc0 + j0, kt);
+    }
+    if (l >= m0 * VEC && l < m1 * VEC) {
+        const float gm = exp2_fast(last_l);
+        const bool in = -last_l <= kBasisLimit;
+        bf.pre[kc0 + l] = in ? 1.f : gm;
+        bf.post[kc0 + l] = in ? gm : 1.f;
+    }
+    if (wide && l == 0) bf.flag[0] = 1;
+}
+
+template <typename T, int KD, int BV, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                  const T* __restrict__ g, const float* __restrict__ s_init, long s_init_seg_stride,
+                  long s_init_bh_stride, T* __restrict__ o, float* __restrict__ s_final, int T_, int H, int V, int N,
+                  int P, int seg_len) {
+    constexpr int NT = NW * 64;
+    using Sm = PipeSmem<T, KD, BV, NW>;
+    constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
+    static_assert(CW % 16 == 0 && CPK % (16 / (int)sizeof(T)) == 0, "wave tiling");
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nvb = V / BV;
+    int bid = blockIdx.x;
+    const int vb = bid % nvb; bid /= nvb;
+    const int seg = bid % P; bid /= P;
+    const int bh = bid;
+    const int b = bh / H, h = bh % H;
+    const int c_begin = seg * seg_len;
+    const int c_end = min(N, c_begin + seg_len);
+    const int rsK = H * KD, rsV = H * V;
+    const int col0 = vb * BV + w * CW;      // first value column of this wave
+    const int kc0 = w * CPK;                // first key column this wave prepares
+    auto vslice = [&](int c) { return sm.Vw + ((Sm::VB == 2 ? (c & 1) : 0) * NW + w) * kChunk * Sm::pW; };
+
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int t = e / kChunk, s = e % kChunk;
+        if ((s >> 4) > (t >> 4)) sm.A[t * Sm::pA + s] = Elem<T>::from_f(0.f);
+    }
+    if (tid < 2) sm.buf[tid].flag[0] = 0;
+
+    StateRegs<KD, CB> S;
+    if (s_init) S.load(s_init + (long)bh * s_init_bh_stride + (long)seg * s_init_seg_stride, V, col0);
+    else S.zero();
+
+    RowSlab<T, CPK> rq, rk, rg;
+    TileRegs<T, CW, 64> rv;
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto vrow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
+    auto load_slabs = [&](int c) {
+        rq.load(kbase(q, c), rsK, kc0);
+        rk.load(kbase(k, c), rsK, kc0);
+        rg.load(kbase(g, c), rsK, kc0);
+    };
+    // column groups of the preparation done in phase 1 (m < MG) and phase 2
+    constexpr int NG = CPK / (16 / (int)sizeof(T)), MG = (NG + 1) / 2;
+    auto load_groups = [&](int c, int m0, int m1) {
+        rq.load_part(kbase(q, c), rsK, kc0, m0, m1);
+        rk.load_part(kbase(k, c), rsK, kc0, m0, m1);
+        rg.load_part(kbase(g, c), rsK, kc0, m0, m1);
+    };
+    load_slabs(c_begin);
+    rv.load(vrow(v, c_begin), rsV, l);
+    __syncthreads();
+    pipe_prep<T, CPK>(sm.buf[c_begin & 1], Sm::pQ, rq, rk, rg, kc0, 0, NG);
+    rv.store_lds(vslice(c_begin), Sm::pW, l);
+    if (c_begin + 1 < c_end) {
+        load_slabs(c_begin + 1);
+        if (Sm::VB == 1) rv.load(vrow(v, c_begin + 1), rsV, l);
+    }
+    __syncthreads();
+    for (int c = c_begin; c < c_end; ++c) {
+        auto& cur = sm.buf[c & 1];
+        auto& nxt = sm.buf[(c + 1) & 1];
+        const bool more = c + 1 < c_end;
+        const bool exact = cur.flag[0] != 0;
+        if (Sm::VB == 2 && more) rv.load(vrow(v, c + 1), rsV, l);
+        // ---- phase 1: A(c), preparation of chunk c+1
+        if (!exact) {
+            for (int tile = w; tile < 10; tile += NW) {
+                int is, js;
+                decode_tile(tile, is, js);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks)
+                    acc = mma32(acc, frag_rm<T>(cur.Kt, Sm::pQ, 16 * js, 32 * ks),
+                                frag_rm<T>(cur.Kt, Sm::pQ, 16 * js, 32 * ks + 16),
+                                frag_rm<T>(cur.Ql, Sm::pQ, 16 * is, 32 * ks),
+                                frag_rm<T>(cur.Ql, Sm::pQ, 16 * is, 32 * ks + 16));
+                // acc holds A^T[s][t] for s = 16js + 4(l/16) + r, t = 16is + l%16
+                if (is == js) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * (l >> 4) + r > (l & 15)) acc[r] = 0.f;
+                }
+                *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
+                    to_vec4<T>(acc);
+            }
+        } else {
+            // Eq. 4 element by element: each wave adds its key columns' share of
+            // A[t][s] = sum_i q_ti k_si exp2(B_ti - B_si) into an fp32 tile
+            // (the spare buffer, refilled below once A is final).
+            float* Af = reinterpret_cast<float*>(nxt.Ql);
+            for (int e = tid; e < kChunk * Sm::pF; e += NT) Af[e] = 0.f;
+            __syncthreads();
+            constexpr int VEC = 16 / (int)sizeof(T);
+            for (int j0 = 0; j0 < CPK; j0 += VEC) {
+                RowSlab<T, VEC> xq, xk, xg;
+                xq.load(kbase(q, c), rsK, kc0 + j0);
+                xk.load(kbase(k, c), rsK, kc0 + j0);
+                xg.load(kbase(g, c), rsK, kc0 + j0);
+                float bt[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
+                wave_incl_scan_n<VEC>(bt);
+                for (int s = 0; s < kChunk; ++s) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j)
+                        part += xq.get(j) * lane_bcast(xk.get(j), s) * exp2_fast(bt[j] - lane_bcast(bt[j], s));
+                    if (l >= s) atomicAdd(Af + l * Sm::pF + s, part);
+                }
+            }
+            __syncthreads();
+            for (int e = tid; e < kChunk * kChunk; e += NT) {
+                const int t = e / kChunk, s = e % kChunk;
+                if ((s >> 4) == (t >> 4) || s < t)
+                    sm.A[t * Sm::pA + s] = Elem<T>::from_f(s <= t ? Af[t * Sm::pF + s] : 0.f);
+            }
+            __syncthreads();
+        }
+        // Inter-chunk outputs O^T[j][t] = sum_i S[i][j] Ql[t][i] need no A, so they
+        // share phase 1 with the next chunk's preparation.  Waves w and w + NW/2
+        // run on the same SIMD and take the two pieces in opposite order, so
+        // one's matrix work overlaps the other's vector work.  On the last chunk
+        // the preparation runs on stale registers into the unused buffer.
+        f32x4 acc[4][CB];
+        auto inter = [&]() {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                vec4_t<T> sf[CB][2];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
+                    sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const vec4_t<T> blo = frag_rm<T>(cur.Ql, Sm::pQ, 16 * rb, 32 * ks);
+                    const vec4_t<T> bhi = frag_rm<T>(cur.Ql, Sm::pQ, 16 * rb, 32 * ks + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], blo, bhi);
+                }
+            }
+        };
+        if (w < NW / 2) {
+            inter();
+            __builtin_amdgcn_sched_barrier(0);
+            pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, 0, MG);
+        } else {
+            pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, 0, MG);
+            __builtin_amdgcn_sched_barrier(0);
+            inter();
+        }
+        if (c + 2 < c_end) load_groups(c + 2, 0, MG);
+        if (Sm::VB == 2 && more) rv.store_lds(vslice(c + 1), Sm::pW, l);
+        __syncthreads();
+        // ---- phase 2: intra-chunk outputs, then the state update
+        {
+            const T* Vw = vslice(c);
+            vec4_t<T> vf[4][CB];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
+            T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                // O^T[j][t] += sum_s V[s][j] A[t][s]
+#pragma unroll
+                for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
+                    const vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
+                    const vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[rb][cb] = mma32(acc[rb][cb], vf[2 * ks2][cb], vf[2 * ks2 + 1][cb], blo, bhi);
+                }
+                // slot r: column j = col0 + 16cb + 4(l/16) + r, token t = 16rb + l%16
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    *reinterpret_cast<vec4_t<T>*>(obase + (16 * rb + (l & 15)) * rsV + 16 * cb + 4 * (l >> 4)) =
+                        to_vec4<T>(acc[rb][cb]);
+            }
+            // S <- post * (pre * S + Kt^T V); slot r of tile (a, cb) is key row 16a + 4(l/16) + r
+            auto update = [&]() {
+#pragma unroll
+                for (int a = 0; a < KD / 16; ++a) {
+                    const f32x4 pre = *reinterpret_cast<const f32x4*>(cur.pre + 16 * a + 4 * (l >> 4));
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= pre;
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int a = 0; a < KD / 16; ++a) {
+                        const vec4_t<T> xlo = frag_cm<T>(cur.Kt, Sm::pQ, 32 * ks, 16 * a);
+                        const vec4_t<T> xhi = frag_cm<T>(cur.Kt, Sm::pQ, 32 * ks + 16, 16 * a);
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            S.s[a][cb] = mma32(S.s[a][cb], xlo, xhi, vf[2 * ks][cb], vf[2 * ks + 1][cb]);
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < KD / 16; ++a) {
+                    const f32x4 post = *reinterpret_cast<const f32x4*>(cur.post + 16 * a + 4 * (l >> 4));
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= post;
+                }
+            };
+            if (w < NW / 2) {
+                update();
+                __builtin_amdgcn_sched_barrier(0);
+                pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, MG, NG);
+            } else {
+                pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, MG, NG);
+                __builtin_amdgcn_sched_barrier(0);
+                update();
+            }
+            if (c + 2 < c_end) load_groups(c + 2, MG, NG);
+        }
+        if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
+        if (Sm::VB == 1 && more) {
+            rv.store_lds(vslice(c + 1), Sm::pW, l);
+            if (c + 2 < c_end) rv.load(vrow(v, c + 2), rsV, l);
+        }
+        __syncthreads();
+    }
+    if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V, V, col0);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers.
 template <typename T, int KD, int BV>
 static hipError_t launch_fwd_t(const FwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
-    static_assert(sizeof(WalkSmem<T, KD, BV>) <= 160 * 1024, "LDS budget");
     const int nvb = a.V / BV;
     const long KV = (long)KD * a.V;
     if (a.P > 1) {
@@ -329,9 +657,17 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)(nvb * a.P * a.BH));
-    GLA_LAUNCH("fwd_walk", (gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
-                       (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
+    if constexpr (sizeof(T) == 2) {
+        static_assert(sizeof(PipeSmem<T, KD, BV, NW>) <= 160 * 1024, "LDS budget");
+        GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
+                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
+    } else {
+        static_assert(sizeof(WalkSmem<T, KD, BV>) <= 160 * 1024, "LDS budget");
+        GLA_LAUNCH("fwd_walk", (gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
+                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
+    }
     return hipGetLastError();
 }
 
