@@ -93,9 +93,11 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
     for (int tile = w; tile < 10; tile += nw) {
         int is, js;  // is: t-block, js: s-block, js <= is
         decode_tile(tile, is, js);
-        f32x4 acc = zero4();
+        // two independent accumulation chains over the value width
+        f32x4 acc2[2] = {zero4(), zero4()};
 #pragma unroll
         for (int ks = 0; ks < V / 32; ++ks) {
+            f32x4& acc = acc2[ks & 1];
             if (!OUT_ST) {  // D[s][t] = sum_j V[s][j] dO[t][j]
                 acc = mma32(acc, frag_rm<T>(sV, pV, 16 * js, 32 * ks), frag_rm<T>(sV, pV, 16 * js, 32 * ks + 16),
                             frag_rm<T>(sdO, pV, 16 * is, 32 * ks), frag_rm<T>(sdO, pV, 16 * is, 32 * ks + 16));
@@ -104,6 +106,7 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
                             frag_rm<T>(sV, pV, 16 * js, 32 * ks), frag_rm<T>(sV, pV, 16 * js, 32 * ks + 16));
             }
         }
+        f32x4 acc = acc2[0] + acc2[1];
         if (!OUT_ST) {
             // slot r: s = 16js + 4(l/16) + r, t = 16is + l%16
             if (is == js)
@@ -154,7 +157,7 @@ template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
            const float* __restrict__ s_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dq,
-           T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len) {
+           T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW;
@@ -165,10 +168,11 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
     const int i0 = 16 * kq, j0 = vs * VW;
     const int nkb = K / BK;
-    int bid = blockIdx.x;
-    const int kb = bid % nkb; bid /= nkb;
-    const int seg = bid % P; bid /= P;
-    const int bh = bid;
+    int unit, kb;
+    xcd_decode(nkb, unit, kb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
     const int b = bh / H, h = bh % H;
     const int k0 = kb * BK;
     const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
@@ -329,7 +333,7 @@ __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
            const T* __restrict__ d_o, const T* __restrict__ dq, const float* __restrict__ ds_init, long s_seg_stride,
            long s_bh_stride, const T* __restrict__ hs, T* __restrict__ dk, T* __restrict__ dg, int T_, int H,
-           int K, int N, int P, int seg_len) {
+           int K, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW;
@@ -342,10 +346,11 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
     const int i0 = 16 * kq, j0 = vs * VW;
     const int nkb = K / BK;
-    int bid = blockIdx.x;
-    const int kb = bid % nkb; bid /= nkb;
-    const int seg = bid % P; bid /= P;
-    const int bh = bid;
+    int unit, kb;
+    xcd_decode(nkb, unit, kb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
     const int b = bh / H, h = bh % H;
     const int k0 = kb * BK;
     const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
@@ -407,8 +412,16 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         }
         rv.store_lds(sm.Vt, Sm::pV, tid);
         rdo.store_lds(sm.dO, Sm::pV, tid);
-        if (more) issue_main(c - 1);
         __syncthreads();
+        // S_out of this chunk (stored by the dq walk) for the dg anchor, in flight
+        // while the dP tiles are formed
+        vec4_t<T> so[VW / 16];
+        {
+            const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb)
+                so[jb] = *reinterpret_cast<const vec4_t<T>*>(src + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4);
+        }
         dp_tiles<T, V, true>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         __syncthreads();
         // dk^T[i][s] = sum_j dS[i][j] V[s][j] (this wave's j range) + sum_t Qh[t][i] dP^T[s][t]
@@ -437,15 +450,11 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         }
         // sum over later tokens for dg: rowsum(S_out * dS_out) at this chunk's end, this wave's j range
         {
-            const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
             float part = 0.f;
 #pragma unroll
-            for (int jb = 0; jb < VW / 16; ++jb) {
-                const vec4_t<T> so =
-                    *reinterpret_cast<const vec4_t<T>*>(src + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4);
+            for (int jb = 0; jb < VW / 16; ++jb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part += Elem<T>::to_f(so[r]) * S.s[jb][r];
-            }
+                for (int r = 0; r < 4; ++r) part += Elem<T>::to_f(so[jb][r]) * S.s[jb][r];
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
             if ((l >> 4) == 0) s_carry[vs * BK + i0 + (l & 15)] = part;
@@ -478,6 +487,9 @@ gla_bwd_dk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
                 *reinterpret_cast<vec4_t<T>*>(dkbase + s * rsK + ic) = to_vec4<T>(val);
             }
         }
+        // next chunk's tiles: issued once this chunk's dP and dk are formed, so
+        // their registers are free at this chunk's peak
+        if (more) issue_main(c - 1);
         __syncthreads();
         // dk (fp32) replaces the gate cumsum in LDS
         if (vs == 0)
@@ -545,17 +557,18 @@ template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g, const T* __restrict__ d_o,
            const float* __restrict__ ds_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dv,
-           float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len) {
+           float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     constexpr int CB = BV / NW / 16;
     using Sm = ChunkSmem<T, KD, BV, NT>;
     __shared__ Sm sm;  // sm.V holds the d_o tile, sm.A holds A^T [s][t]
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int nvb = V / BV;
-    int bid = blockIdx.x;
-    const int vb = bid % nvb; bid /= nvb;
-    const int seg = bid % P; bid /= P;
-    const int bh = bid;
+    int unit, vb;
+    xcd_decode(nvb, unit, vb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
     const int b = bh / H, h = bh % H;
     const int v0 = vb * BV;
     const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
@@ -726,13 +739,13 @@ static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
     const long KV = (long)KD * a.V;
     if (a.P > 1) {
         const int nseg = a.P - 1;
-        dim3 grid((unsigned)(nvb * nseg * a.BH));
+        dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
         GLA_LAUNCH("bwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, 0,
-                           nseg);
+                           nseg, (int)a.BH);
         GLA_LAUNCH("bwd_seg_state_rev", (gla_seg_state<T, KD, BV, NW, true>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.g, (const T*)a.d_o, a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P,
-                           a.seg_len, 1, nseg);
+                           a.seg_len, 1, nseg, (int)a.BH);
         GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd, dim3((unsigned)((KV + 255) / 256), (unsigned)a.BH, 2u),
                            dim3(256), a.stream, a.s0,
                            a.dht, a.ws_state, a.ws_dstate, a.ws_gate, KD, a.V, a.P);
@@ -749,10 +762,10 @@ static hipError_t launch_dv(const BwdLaunch& a) {
     const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
-    dim3 grid((unsigned)(nvb * a.P * a.BH));
+    dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv, a.ds0, a.T, a.H, a.V,
-                       a.N, a.P, a.seg_len);
+                       a.N, a.P, a.seg_len, (int)a.BH);
     return hipGetLastError();
 }
 
@@ -768,17 +781,17 @@ static hipError_t launch_rows(const BwdLaunch& a) {
                   "LDS budget");
     const int nkb = a.K / BK;
     const long KV = (long)a.K * V;
-    dim3 grid((unsigned)(nkb * a.P * a.BH));
+    dim3 grid((unsigned)xcd_grid(a.P * a.BH, nkb));
     const float* sinit = a.P > 1 ? a.ws_state : a.s0;
     const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k, (const T*)a.v,
                        (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq, (T*)a.ws_hs,
-                       a.T, a.H, a.K, a.N, a.P, a.seg_len);
+                       a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit, seg_stride, bh_stride,
-                       (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P, a.seg_len);
+                       (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     return hipGetLastError();
 }
 

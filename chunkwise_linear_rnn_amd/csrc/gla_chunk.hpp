@@ -106,9 +106,9 @@ __device__ __forceinline__ void decode_tile(int tile, int& is, int& js) {
 //   forwards  (REV = false): out[0] = init, out[p+1] = exp2(G_p) out[p] + in[p]
 //   backwards (REV = true):  out[P-1] = init, out[p-1] = exp2(G_p) out[p] + in[p]
 // `st` holds in[] on entry and out[] on exit (stride KV), `gt` the segment gate
-// totals G_p in log2 units (stride K).  The loads of U segments are issued
-// before any of their results is needed, so one thread keeps U independent
-// requests in flight rather than one per step.
+// totals G_p in log2 units (stride K).  The loads of up to U segments are
+// issued before any of their results is needed, so one thread keeps them all
+// in flight rather than one request per step.
 template <bool REV>
 __device__ __forceinline__ void combine_element(float* st, const float* gt, long KV, long K, int P, float cur) {
     constexpr int U = 8;
@@ -134,73 +134,152 @@ __device__ __forceinline__ void combine_element(float* st, const float* gt, long
 
 // ---------------------------------------------------------------------------
 // Step 1: segment-local states.  REV = false: S*_p from the keys and values of
-// the segment walked forwards (decay Gamma = exp2(B_63 - B_t) on the keys).
-// REV = true: the backward pass's dS*_p from queries and d_o walked backwards
-// (decay Lambda = exp2(B_t) on the queries; dS_[n-1] = gamma dS_[n] + (Q*Lambda)^T dO).
+// the segment walked forwards, S <- Diag(gamma) S + (K*Gamma)^T V with
+// Gamma_s = exp2(B_63 - B_s).  REV = true: the backward pass's dS*_p from
+// queries and d_o walked backwards, dS <- Diag(gamma) dS + (Q*Lambda)^T dO with
+// Lambda_t = exp2(B_t).  Both decay factors are at most 1, so no chunk needs
+// an exact path.
+//
+// One barrier per chunk: while a wave applies chunk c to its state columns it
+// also prepares its key columns of chunk c+1 (register slabs, lane = token,
+// DPP scan of the log gate) into the other buffer.  Waves w and w + NW/2 share
+// a SIMD and take the two pieces in opposite order.  Each wave's value (or
+// d_o) slice is private and double-buffered.
+template <typename T, int KD, int BV, int NW>
+struct SegSmem {
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int CW = BV / NW;  // value columns per wave
+    // decayed operand, read only with column fragments: a pitch of 8 mod 64
+    // dwords (bf16) keeps the four rows of a transposed read on separate banks
+    static constexpr int pX = sizeof(T) == 2 ? KD + 16 : KD + 4;
+    static constexpr int pW = (sizeof(T) == 2 && (CW == 16 || CW == 32)) ? CW : CW + PT;
+    struct alignas(16) Buf {
+        T X[kChunk * pX];
+        float gam[KD];
+    };
+    Buf buf[2];
+    alignas(16) T Yw[2 * NW * kChunk * pW];
+};
+
 template <typename T, int KD, int BV, int NW, bool REV>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
               float* __restrict__ ws_state, float* __restrict__ ws_gate,
-              int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg) {
-    constexpr int NT = NW * 64;
-    constexpr int CB = BV / NW / 16;
-    using Sm = ChunkSmem<T, KD, BV, NT>;
+              int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg, int BH) {
+    using Sm = SegSmem<T, KD, BV, NW>;
+    constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
+    constexpr int VEC = 16 / (int)sizeof(T);
+    static_assert(CW % 16 == 0 && CPK % VEC == 0 && CPK <= 64, "wave tiling");
+    static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
     __shared__ Sm sm;
-    const int tid = threadIdx.x, w = wave_id();
+    const int w = wave_id(), l = lane_id();
     const int nvb = V / BV;
-    int bid = blockIdx.x;
-    const int vb = bid % nvb; bid /= nvb;
-    const int seg = seg_first + bid % nseg; bid /= nseg;
-    const int bh = bid;
+    int unit, vb;
+    xcd_decode(nvb, unit, vb);
+    if (unit >= BH * nseg) return;
+    const int seg = seg_first + unit % nseg;
+    const int bh = unit / nseg;
     const int b = bh / H, h = bh % H;
-    const int v0 = vb * BV;
     const int c_begin = seg * seg_len;
     const int c_end = min(N, c_begin + seg_len);
     const int nchunks = c_end - c_begin;
     const int rsK = H * KD, rsV = H * V;
-    const int col0 = w * (BV / NW);
+    const int col0 = vb * BV + w * CW;  // first value column of this wave
+    const int kc0 = w * CPK;            // first key column this wave prepares
 
     StateRegs<KD, CB> S;
     S.zero();
-    float gate_total = 0.f;
+    float gtot = 0.f;  // lane j: sum of B_63 over the segment for key column kc0 + j
 
-    TileRegs<T, KD, NT> rx, rg;
-    TileRegs<T, BV, NT> ry;
-    auto issue = [&](int c) {
-        const long tok0 = (long)b * T_ + (long)c * kChunk;
-        rx.load(x + (tok0 * H + h) * KD, rsK, tid);
-        rg.load(g + (tok0 * H + h) * KD, rsK, tid);
-        ry.load(y + (tok0 * H + h) * V + v0, rsV, tid);
-    };
-    issue(REV ? c_end - 1 : c_begin);
-    for (int it = 0; it < nchunks; ++it) {
-        if (tid == 0) sm.flag = 0;
-        chunk_log_cumsum<T, KD, NT>(rg, sm.B, Sm::pB, sm.tot, sm.last, sm.gam, &sm.flag, tid);
-        if (tid < KD) gate_total += sm.last[tid];
-        // decayed operand: K*Gamma (forward) or Q*Lambda (reverse)
-        using TR = TileRegs<T, KD, NT>;
+    RowSlab<T, CPK> rx, rg;
+    TileRegs<T, CW, 64> ry;
+    auto chunk_of = [&](int it) { return REV ? c_end - 1 - it : c_begin + it; };
+    auto krow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto vrow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
+    auto yslice = [&](int it) { return sm.Yw + ((it & 1) * NW + w) * kChunk * Sm::pW; };
+    auto prep = [&](typename Sm::Buf& bf) {
+        float last_l = 0.f;
 #pragma unroll
-        for (int p = 0; p < TR::PER; ++p) {
-            if (!TR::owns(p, tid)) continue;
-            const int row = TR::row_of(p, tid), c0 = TR::col_of(p, tid);
-            float vals[TR::VEC];
+        for (int j0 = 0; j0 < CPK; j0 += VEC) {
+            float bt[VEC];
 #pragma unroll
-            for (int e = 0; e < TR::VEC; ++e) {
-                const float bt = sm.B[row * Sm::pB + c0 + e];
-                const float ex = REV ? bt : (sm.last[c0 + e] - bt);
-                vals[e] = rx.get(p, e) * exp2_fast(ex);
+            for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
+            wave_incl_scan_n<VEC>(bt);
+            float xv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float bl = lane_bcast(bt[e], 63);
+                last_l = (l == j0 + e) ? bl : last_l;
+                xv[e] = rx.get(j0 + e) * exp2_fast(REV ? bt[e] : bl - bt[e]);
             }
-            store_vec_lds<T>(sm.K + row * Sm::pK + c0, vals);
+            store_vec_lds<T>(bf.X + l * Sm::pX + kc0 + j0, xv);
         }
-        ry.store_lds(sm.V, Sm::pV, tid);
-        if (it + 1 < nchunks) issue(REV ? c_end - 2 - it : c_begin + it + 1);
-        __syncthreads();
-        state_update<T, KD, CB>(S, sm.K, Sm::pK, sm.V, Sm::pV, sm.gam, col0);
+        if (l < CPK) {
+            bf.gam[kc0 + l] = exp2_fast(last_l);
+            gtot += last_l;
+        }
+    };
+    auto update = [&](const typename Sm::Buf& bf, const T* Yw) {
+        vec4_t<T> yf[4][CB];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) yf[sb][cb] = frag_cm<T>(Yw, Sm::pW, 16 * sb, 16 * cb);
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(bf.gam + 16 * a + 4 * (l >> 4));
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= gm;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int a = 0; a < KD / 16; ++a) {
+                const vec4_t<T> xlo = frag_cm<T>(bf.X, Sm::pX, 32 * ks, 16 * a);
+                const vec4_t<T> xhi = frag_cm<T>(bf.X, Sm::pX, 32 * ks + 16, 16 * a);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) S.s[a][cb] = mma32(S.s[a][cb], xlo, xhi, yf[2 * ks][cb], yf[2 * ks + 1][cb]);
+            }
+    };
+
+    if (nchunks > 0) {
+        rx.load(krow(x, chunk_of(0)), rsK, kc0);
+        rg.load(krow(g, chunk_of(0)), rsK, kc0);
+        ry.load(vrow(y, chunk_of(0)), rsV, l);
+        prep(sm.buf[0]);
+        ry.store_lds(yslice(0), Sm::pW, l);
+        if (nchunks > 1) {
+            rx.load(krow(x, chunk_of(1)), rsK, kc0);
+            rg.load(krow(g, chunk_of(1)), rsK, kc0);
+            ry.load(vrow(y, chunk_of(1)), rsV, l);
+        }
+    }
+    __syncthreads();
+    for (int it = 0; it < nchunks; ++it) {
+        const bool more = it + 1 < nchunks;
+        const auto& cur = sm.buf[it & 1];
+        auto& nxt = sm.buf[(it + 1) & 1];
+        if (w < NW / 2) {
+            update(cur, yslice(it));
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) prep(nxt);
+        } else {
+            if (more) prep(nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            update(cur, yslice(it));
+        }
+        if (more) {
+            ry.store_lds(yslice(it + 1), Sm::pW, l);
+            if (it + 2 < nchunks) {
+                rx.load(krow(x, chunk_of(it + 2)), rsK, kc0);
+                rg.load(krow(g, chunk_of(it + 2)), rsK, kc0);
+                ry.load(vrow(y, chunk_of(it + 2)), rsV, l);
+            }
+        }
         __syncthreads();
     }
-    float* dst = ws_state + ((long)bh * P + seg) * (long)KD * V + v0;
-    S.store(dst, V, col0);
-    if (vb == 0 && tid < KD) ws_gate[((long)bh * P + seg) * KD + tid] = gate_total;
+    S.store(ws_state + ((long)bh * P + seg) * (long)KD * V, V, col0);
+    if (vb == 0 && l < CPK) ws_gate[((long)bh * P + seg) * KD + kc0 + l] = gtot;
 }
 
 }  // namespace gla

@@ -39,6 +39,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRangeLimit = 64.0f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Workgroups are dispatched to the eight XCDs round-robin by block index, and
+// each XCD has its own L2.  Kernels whose G sibling workgroups (column or row
+// blocks of one head and segment) read the same chunk tiles give the siblings
+// block indices eight apart, so they share an L2.  Decodes this workgroup's
+// (unit, sibling); the grid is xcd_grid(units, G) and surplus workgroups
+// (unit >= units) must exit at once.
+constexpr int kXcds = 8;
+__host__ __device__ inline long xcd_grid(long units, int G) { return (units + kXcds - 1) / kXcds * kXcds * G; }
+__device__ __forceinline__ void xcd_decode(int G, int& unit, int& sib) {
+    const int bid = blockIdx.x;
+    const int rest = bid / kXcds;
+    sib = rest % G;
+    unit = (rest / G) * kXcds + bid % kXcds;
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
              const float* __restrict__ s_init, long s_init_seg_stride, long s_init_bh_stride,
              T* __restrict__ o, float* __restrict__ s_final,
-             int T_, int H, int V, int N, int P, int seg_len) {
+             int T_, int H, int V, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     constexpr int CB = BV / NW / 16;
     constexpr int CPK = KD / NW;            // key columns per wave in the row-slab preparation
@@ -92,10 +92,11 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int nvb = V / BV;
-    int bid = blockIdx.x;
-    const int vb = bid % nvb; bid /= nvb;
-    const int seg = bid % P; bid /= P;
-    const int bh = bid;
+    int unit, vb;
+    xcd_decode(nvb, unit, vb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
     const int b = bh / H, h = bh % H;
     const int v0 = vb * BV;
     const int c_begin = seg * seg_len;
@@ -403,7 +404,7 @@ __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const float* __restrict__ s_init, long s_init_seg_stride,
                   long s_init_bh_stride, T* __restrict__ o, float* __restrict__ s_final, int T_, int H, int V, int N,
-                  int P, int seg_len) {
+                  int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW>;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
@@ -411,10 +412,11 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
     const int nvb = V / BV;
-    int bid = blockIdx.x;
-    const int vb = bid % nvb; bid /= nvb;
-    const int seg = bid % P; bid /= P;
-    const int bh = bid;
+    int unit, vb;
+    xcd_decode(nvb, unit, vb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
     const int b = bh / H, h = bh % H;
     const int c_begin = seg * seg_len;
     const int c_end = min(N, c_begin + seg_len);
@@ -645,10 +647,10 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     if (a.P > 1) {
         // segments 0..P-2 feed the combine; the last segment's S* is never needed
         const int nseg = a.P - 1;
-        dim3 grid((unsigned)(nvb * nseg * a.BH));
+        dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
         GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate,
-                           a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg);
+                           a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg, (int)a.BH);
         dim3 g2((unsigned)((KV + 255) / 256), (unsigned)a.BH);
         GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd, g2, dim3(256), a.stream, a.s0, a.ws_state, a.ws_gate,
                            KD, a.V, a.P);
@@ -656,17 +658,17 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     const float* sinit = a.P > 1 ? a.ws_state : a.s0;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
-    dim3 grid((unsigned)(nvb * a.P * a.BH));
+    dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
-                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
+                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
         static_assert(sizeof(WalkSmem<T, KD, BV>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("fwd_walk", (gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
-                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len);
+                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
     }
     return hipGetLastError();
 }
