@@ -729,6 +729,248 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// dv walk, software-pipelined (16-bit operands): backwards over one segment for
+// value columns v0 .. v0+BV-1, full K, with the forward walk's chunk-start basis
+// (Ql = q * exp2(B_t), Kt = k * exp2(-B_s), A = Ql Kt^T; per-column factors
+// (pre, post) = (1, gamma) in range, (gamma, 1) beyond kBasisLimit, where Kt
+// holds k * exp2(B_63 - B_s)).  With dS = dS_out of the chunk:
+//   dv^T[j][s] = sum_i (post_i dS[i][j]) Kt[s][i] + sum_{t>=s} dO[t][j] A[t][s]
+//   dS_in     = Diag(gamma) dS + Ql^T dO,     gamma = pre * post
+// Phase 1: A^T(c), the inter-chunk part of dv, preparation of chunk c-1 (first
+// column groups).  Phase 2: the intra-chunk part of dv, the dS update, the rest
+// of the preparation.  Segment 0 ends with dS_0.
+template <typename T, int KD, int BV, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
+                const T* __restrict__ d_o, const float* __restrict__ ds_init, long s_seg_stride, long s_bh_stride,
+                T* __restrict__ dv, float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH) {
+    constexpr int NT = NW * 64;
+    using Sm = PipeSmem<T, KD, BV, NW, true>;  // sm.A holds A^T [s][t]; sm.Vw the d_o slices
+    constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
+    constexpr int VEC = 16 / (int)sizeof(T);
+    static_assert(CW % 16 == 0 && CPK % VEC == 0, "wave tiling");
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nvb = V / BV;
+    int unit, vb;
+    xcd_decode(nvb, unit, vb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
+    const int b = bh / H, h = bh % H;
+    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const int nchunks = c_end - c_begin;
+    const int rsK = H * KD, rsV = H * V;
+    const int col0 = vb * BV + w * CW;
+    const int kc0 = w * CPK;
+    auto chunk_of = [&](int it) { return c_end - 1 - it; };
+    auto dslice = [&](int it) { return sm.Vw + ((Sm::VB == 2 ? (it & 1) : 0) * NW + w) * kChunk * Sm::pW; };
+
+    // A^T is stored [s][t]; its tiles with t-block < s-block are zero
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int s = e / kChunk, t = e % kChunk;
+        if ((t >> 4) < (s >> 4)) sm.A[s * Sm::pA + t] = Elem<T>::from_f(0.f);
+    }
+    if (tid < 2) sm.buf[tid].flag[0] = 0;
+
+    StateRegs<KD, CB> S;  // dS
+    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride, V, col0);
+    else S.zero();
+
+    RowSlab<T, CPK> rq, rk, rg;
+    TileRegs<T, CW, 64> rdo;
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto vrow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
+    auto load_slabs = [&](int c) {
+        rq.load(kbase(q, c), rsK, kc0);
+        rk.load(kbase(k, c), rsK, kc0);
+        rg.load(kbase(g, c), rsK, kc0);
+    };
+    constexpr int NG = CPK / VEC, MG = (NG + 1) / 2;
+    auto load_groups = [&](int c, int m0, int m1) {
+        rq.load_part(kbase(q, c), rsK, kc0, m0, m1);
+        rk.load_part(kbase(k, c), rsK, kc0, m0, m1);
+        rg.load_part(kbase(g, c), rsK, kc0, m0, m1);
+    };
+    if (nchunks > 0) {
+        load_slabs(chunk_of(0));
+        rdo.load(vrow(d_o, chunk_of(0)), rsV, l);
+    }
+    __syncthreads();
+    if (nchunks > 0) {
+        pipe_prep<T, CPK>(sm.buf[0], Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, NG);
+        rdo.store_lds(dslice(0), Sm::pW, l);
+        if (nchunks > 1) {
+            load_slabs(chunk_of(1));
+            if (Sm::VB == 1) rdo.load(vrow(d_o, chunk_of(1)), rsV, l);
+        }
+    }
+    __syncthreads();
+    for (int it = 0; it < nchunks; ++it) {
+        const int c = chunk_of(it);
+        auto& cur = sm.buf[it & 1];
+        auto& nxt = sm.buf[(it + 1) & 1];
+        const bool more = it + 1 < nchunks;
+        const bool exact = cur.flag[0] != 0;
+        if (Sm::VB == 2 && more) rdo.load(vrow(d_o, chunk_of(it + 1)), rsV, l);
+        // ---- phase 1: A^T(c)
+        if (!exact) {
+            for (int tile = w; tile < 10; tile += NW) {
+                int is, js;  // is: t-block, js: s-block, js <= is
+                decode_tile(tile, is, js);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks)
+                    acc = mma32(acc, frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks),
+                                frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks + 16),
+                                frag_rm<T>(cur.Kt, Sm::pKt, 16 * js, 32 * ks),
+                                frag_rm<T>(cur.Kt, Sm::pKt, 16 * js, 32 * ks + 16));
+                // slot r: t = 16is + 4(l/16) + r, s = 16js + l%16
+                if (is == js) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if ((l & 15) > 4 * (l >> 4) + r) acc[r] = 0.f;
+                }
+                *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * js + (l & 15)) * Sm::pA + 16 * is + 4 * (l >> 4)) =
+                    to_vec4<T>(acc);
+            }
+        } else {
+            // Eq. 4 element by element into an fp32 tile (the spare buffer, refilled
+            // below once A^T is final); each wave adds its key columns' share
+            float* Af = reinterpret_cast<float*>(nxt.Ql);
+            for (int e = tid; e < kChunk * Sm::pF; e += NT) Af[e] = 0.f;
+            __syncthreads();
+            for (int j0 = 0; j0 < CPK; j0 += VEC) {
+                RowSlab<T, VEC> xq, xk, xg;
+                xq.load(kbase(q, c), rsK, kc0 + j0);
+                xk.load(kbase(k, c), rsK, kc0 + j0);
+                xg.load(kbase(g, c), rsK, kc0 + j0);
+                float bt[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
+                wave_incl_scan_n<VEC>(bt);
+                for (int s = 0; s < kChunk; ++s) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j)
+                        part += xq.get(j) * lane_bcast(xk.get(j), s) * exp2_fast(bt[j] - lane_bcast(bt[j], s));
+                    if (l >= s) atomicAdd(Af + l * Sm::pF + s, part);
+                }
+            }
+            __syncthreads();
+            for (int e = tid; e < kChunk * kChunk; e += NT) {
+                const int s = e / kChunk, t = e % kChunk;
+                if ((t >> 4) >= (s >> 4)) sm.A[s * Sm::pA + t] = Elem<T>::from_f(t >= s ? Af[t * Sm::pF + s] : 0.f);
+            }
+            __syncthreads();
+        }
+        // inter-chunk part of dv^T (no A needed), alongside the next preparation
+        f32x4 acc[4][CB];
+        auto inter = [&]() {
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[sb][cb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                const f32x4 p0 = *reinterpret_cast<const f32x4*>(cur.post + 32 * ks + 4 * (l >> 4));
+                const f32x4 p1 = *reinterpret_cast<const f32x4*>(cur.post + 32 * ks + 16 + 4 * (l >> 4));
+                vec4_t<T> sf[CB][2];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb] * p0);
+                    sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb] * p1);
+                }
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    const vec4_t<T> blo = frag_rm<T>(cur.Kt, Sm::pKt, 16 * sb, 32 * ks);
+                    const vec4_t<T> bhi = frag_rm<T>(cur.Kt, Sm::pKt, 16 * sb, 32 * ks + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) acc[sb][cb] = mma32(acc[sb][cb], sf[cb][0], sf[cb][1], blo, bhi);
+                }
+            }
+        };
+        if (w < NW / 2) {
+            inter();
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
+        } else {
+            if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
+            __builtin_amdgcn_sched_barrier(0);
+            inter();
+        }
+        if (it + 2 < nchunks) load_groups(chunk_of(it + 2), 0, MG);
+        if (Sm::VB == 2 && more) rdo.store_lds(dslice(it + 1), Sm::pW, l);
+        __syncthreads();
+        // ---- phase 2: intra-chunk part of dv, then the dS update
+        {
+            const T* Dw = dslice(it);
+            vec4_t<T> df[4][CB];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) df[tb][cb] = frag_cm<T>(Dw, Sm::pW, 16 * tb, 16 * cb);
+            T* dvbase = dv + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                // dv^T[j][s] += sum_t dO[t][j] A^T[s][t], t-blocks >= sb
+#pragma unroll
+                for (int ks2 = sb / 2; ks2 < 2; ++ks2) {
+                    const vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2);
+                    const vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * sb, 32 * ks2 + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[sb][cb] = mma32(acc[sb][cb], df[2 * ks2][cb], df[2 * ks2 + 1][cb], blo, bhi);
+                }
+                // slot r: value column j = col0 + 16cb + 4(l/16) + r, token s = 16sb + l%16
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    *reinterpret_cast<vec4_t<T>*>(dvbase + (16 * sb + (l & 15)) * rsV + 16 * cb + 4 * (l >> 4)) =
+                        to_vec4<T>(acc[sb][cb]);
+            }
+            // dS <- Diag(gamma) dS + Ql^T dO; slot r of tile (a, cb) is key row 16a + 4(l/16) + r
+            auto update = [&]() {
+#pragma unroll
+                for (int a = 0; a < KD / 16; ++a) {
+                    const f32x4 pre = *reinterpret_cast<const f32x4*>(cur.pre + 16 * a + 4 * (l >> 4));
+                    const f32x4 post = *reinterpret_cast<const f32x4*>(cur.post + 16 * a + 4 * (l >> 4));
+                    const f32x4 gm = pre * post;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= gm;
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int a = 0; a < KD / 16; ++a) {
+                        const vec4_t<T> xlo = frag_cm<T>(cur.Ql, Sm::pQl, 32 * ks, 16 * a);
+                        const vec4_t<T> xhi = frag_cm<T>(cur.Ql, Sm::pQl, 32 * ks + 16, 16 * a);
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            S.s[a][cb] = mma32(S.s[a][cb], xlo, xhi, df[2 * ks][cb], df[2 * ks + 1][cb]);
+                    }
+            };
+            if (w < NW / 2) {
+                update();
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
+            } else {
+                if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
+                __builtin_amdgcn_sched_barrier(0);
+                update();
+            }
+            if (it + 2 < nchunks) load_groups(chunk_of(it + 2), MG, NG);
+        }
+        if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
+        if (Sm::VB == 1 && more) {
+            rdo.store_lds(dslice(it + 1), Sm::pW, l);
+            if (it + 2 < nchunks) rdo.load(vrow(d_o, chunk_of(it + 2)), rsV, l);
+        }
+        __syncthreads();
+    }
+    if (ds0 && seg == 0) S.store(ds0 + (long)bh * KD * V, V, col0);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers.
 template <typename T, int KD, int BV>
 static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
@@ -763,9 +1005,16 @@ static hipError_t launch_dv(const BwdLaunch& a) {
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
-    GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv, a.ds0, a.T, a.H, a.V,
-                       a.N, a.P, a.seg_len, (int)a.BH);
+    if constexpr (sizeof(T) == 2) {
+        static_assert(sizeof(PipeSmem<T, KD, BV, NW, true>) <= 160 * 1024, "LDS budget");
+        GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv,
+                           a.ds0, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
+    } else {
+        GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv,
+                           a.ds0, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
+    }
     return hipGetLastError();
 }
 

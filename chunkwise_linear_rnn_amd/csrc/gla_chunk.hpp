@@ -102,6 +102,101 @@ __device__ __forceinline__ void decode_tile(int tile, int& is, int& js) {
 }
 
 // ---------------------------------------------------------------------------
+// Pieces of the software-pipelined walks (forward output walk, backward dv
+// walk): operands in the chunk-start basis Ql = q * exp2(B_t), Kt = k *
+// exp2(-B_s) (reference-row key factor k * exp2(B_63 - B_s) for columns beyond
+// kBasisLimit), double-buffered per chunk, plus wave-private value slices.
+constexpr float kBasisLimit = 96.0f;
+
+// Pitch (elements) of a 64-row tile with KD columns.  Two-byte tiles read with
+// row fragments (8 bytes per lane down 16 rows) are conflict-free at 4 mod 64
+// dwords; tiles also read with transposed column fragments (ds_read_b64_tr_b16:
+// 4 rows x 4 pieces per 16 lanes) need 36 mod 64 dwords for both patterns.
+// The wider pitch is used for KD <= 128 only.
+template <typename T, int KD, bool COLS>
+constexpr int tile_pitch() {
+    if (sizeof(T) != 2) return KD + Elem<T>::pad;
+    if (!COLS || KD > 128) return KD + 8;
+    const int dw = KD / 2;
+    return 2 * (dw + ((36 - dw % 64) % 64 + 64) % 64);
+}
+
+// QL_COLS: the Ql tile is also read with column fragments (the backward's dS update).
+template <typename T, int KD, int BV, int NW, bool QL_COLS>
+struct PipeSmem {
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int CW = BV / NW;      // value columns per wave
+    static constexpr int pQl = tile_pitch<T, KD, QL_COLS>();
+    static constexpr int pKt = tile_pitch<T, KD, false>();
+    static constexpr int pA = kChunk + PT;
+    static constexpr int pF = kChunk + 4;   // fp32 A of exact-path chunks
+    // wave-private V slices, read with ds_read_b64_tr_b16: the four rows a
+    // 16-lane group reads fall on disjoint banks at a pitch of 8 or 16 dwords
+    // (CW = 16 or 32 two-byte columns), and rows stay 16-byte aligned.  Two
+    // slices per wave when they fit, so the next chunk's V is written during
+    // phase 1 instead of being held in registers through phase 2.
+    static constexpr int pW = (sizeof(T) == 2 && (CW == 16 || CW == 32)) ? CW : CW + PT;
+    static constexpr int VB =
+        (2 * (sizeof(T) * kChunk * (pQl + pKt) + 2 * sizeof(float) * KD + 16) + sizeof(T) * kChunk * pA +
+             2 * sizeof(T) * NW * kChunk * pW <= 160 * 1024) ? 2 : 1;
+    struct alignas(16) Buf {
+        T Ql[kChunk * pQl];
+        T Kt[kChunk * pKt];
+        float pre[KD];
+        float post[KD];
+        int flag[4];
+    };
+    static_assert(sizeof(T) * kChunk * (pQl + pKt) >= sizeof(float) * kChunk * pF, "exact-path scratch");
+    Buf buf[2];
+    alignas(16) T A[kChunk * pA];
+    alignas(16) T Vw[VB * NW * kChunk * pW];
+};
+
+// One wave prepares 16-byte column groups m0 .. m1-1 of its key columns
+// kc0 .. kc0+NC-1 (lane = token row) from its register slabs of q, k and the
+// raw log gate.  Lane j collects B_63 of column kc0 + j and the factors are
+// formed once per lane at the end, so the column loop has no branches and the
+// scans of a group's VEC columns interleave.
+template <typename T, int NC, typename Buf>
+__device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSlab<T, NC>& rq,
+                                          const RowSlab<T, NC>& rk, const RowSlab<T, NC>& rg, int kc0, int m0,
+                                          int m1) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    static_assert(NC <= 64, "one lane per prepared column");
+    const int l = lane_id();
+    float last_l = 0.f;
+    bool wide = false;
+#pragma unroll
+    for (int m = 0; m < NC / VEC; ++m) {
+        if (m < m0 || m >= m1) continue;
+        const int j0 = m * VEC;
+        float bt[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
+        wave_incl_scan_n<VEC>(bt);
+        float ql[VEC], kt[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float bl = lane_bcast(bt[e], 63);
+            const bool in = -bl <= kBasisLimit;
+            wide |= !in;
+            last_l = (l == j0 + e) ? bl : last_l;
+            ql[e] = rq.get(j0 + e) * exp2_fast(bt[e]);
+            kt[e] = rk.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
+        }
+        store_vec_lds<T>(bf.Ql + l * pQl + kc0 + j0, ql);
+        store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
+    }
+    if (l >= m0 * VEC && l < m1 * VEC) {
+        const float gm = exp2_fast(last_l);
+        const bool in = -last_l <= kBasisLimit;
+        bf.pre[kc0 + l] = in ? 1.f : gm;
+        bf.post[kc0 + l] = in ? gm : 1.f;
+    }
+    if (wide && l == 0) bf.flag[0] = 1;
+}
+
+// ---------------------------------------------------------------------------
 // Step 2: the linear recurrence across segments for one state element.
 //   forwards  (REV = false): out[0] = init, out[p+1] = exp2(G_p) out[p] + in[p]
 //   backwards (REV = true):  out[P-1] = init, out[p-1] = exp2(G_p) out[p] + in[p]

@@ -325,80 +325,6 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 // so the vector-ALU preparation of the next chunk overlaps the matrix work of
 // this one.  Each wave owns BV/NW value columns: its slice of V never needs a
 // workgroup barrier.
-constexpr float kBasisLimit = 96.0f;
-
-template <typename T, int KD, int BV, int NW>
-struct PipeSmem {
-    static constexpr int PT = Elem<T>::pad;
-    static constexpr int CW = BV / NW;      // value columns per wave
-    static constexpr int pQ = KD + PT;
-    static constexpr int pA = kChunk + PT;
-    static constexpr int pF = kChunk + 4;   // fp32 A of exact-path chunks
-    // wave-private V slices, read with ds_read_b64_tr_b16: the four rows a
-    // 16-lane group reads fall on disjoint banks at a pitch of 8 or 16 dwords
-    // (CW = 16 or 32 two-byte columns), and rows stay 16-byte aligned.  Two
-    // slices per wave when they fit, so the next chunk's V is written during
-    // phase 1 instead of being held in registers through phase 2.
-    static constexpr int pW = (sizeof(T) == 2 && (CW == 16 || CW == 32)) ? CW : CW + PT;
-    static constexpr int VB =
-        (2 * (2 * sizeof(T) * kChunk * pQ + 2 * sizeof(float) * KD + 16) + sizeof(T) * kChunk * pA +
-             2 * sizeof(T) * NW * kChunk * pW <= 160 * 1024) ? 2 : 1;
-    struct alignas(16) Buf {
-        T Ql[kChunk * pQ];
-        T Kt[kChunk * pQ];
-        float pre[KD];
-        float post[KD];
-        int flag[4];
-    };
-    static_assert(2 * sizeof(T) * kChunk * pQ >= sizeof(float) * kChunk * pF, "exact-path scratch");
-    Buf buf[2];
-    alignas(16) T A[kChunk * pA];
-    alignas(16) T Vw[VB * NW * kChunk * pW];
-};
-
-// One wave prepares 16-byte column groups m0 .. m1-1 of its key columns
-// kc0 .. kc0+NC-1 (lane = token row) from its register slabs of q, k and the
-// raw log gate.  Lane j collects B_63 of column kc0 + j and the factors are
-// formed once per lane at the end, so the column loop has no branches and the
-// scans of a group's VEC columns interleave.
-template <typename T, int NC, typename Buf>
-__device__ __forceinline__ void pipe_prep(Buf& bf, int pQ, const RowSlab<T, NC>& rq, const RowSlab<T, NC>& rk,
-                                          const RowSlab<T, NC>& rg, int kc0, int m0, int m1) {
-    constexpr int VEC = 16 / (int)sizeof(T);
-    static_assert(NC <= 64, "one lane per prepared column");
-    const int l = lane_id();
-    float last_l = 0.f;
-    bool wide = false;
-#pragma unroll
-    for (int m = 0; m < NC / VEC; ++m) {
-        if (m < m0 || m >= m1) continue;
-        const int j0 = m * VEC;
-        float bt[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
-        wave_incl_scan_n<VEC>(bt);
-        float ql[VEC], kt[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float bl = lane_bcast(bt[e], 63);
-            const bool in = -bl <= kBasisLimit;
-            wide |= !in;
-            last_l = (l == j0 + e) ? bl : last_l;
-            ql[e] = rq.get(j0 + e) * exp2_fast(bt[e]);
-            kt[e] = rk.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
-        }
-        store_vec_lds<T>(bf.Ql + l * pQ + kc0 + j0, ql);
-        store_vec_lds<T>(bf.Kt + l * pQ + kc0 + j0, kt);
-    }
-    if (l >= m0 * VEC && l < m1 * VEC) {
-        const float gm = exp2_fast(last_l);
-        const bool in = -last_l <= kBasisLimit;
-        bf.pre[kc0 + l] = in ? 1.f : gm;
-        bf.post[kc0 + l] = in ? gm : 1.f;
-    }
-    if (wide && l == 0) bf.flag[0] = 1;
-}
-
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -406,7 +332,7 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                   long s_init_bh_stride, T* __restrict__ o, float* __restrict__ s_final, int T_, int H, int V, int N,
                   int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
-    using Sm = PipeSmem<T, KD, BV, NW>;
+    using Sm = PipeSmem<T, KD, BV, NW, false>;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
     static_assert(CW % 16 == 0 && CPK % (16 / (int)sizeof(T)) == 0, "wave tiling");
     __shared__ Sm sm;
@@ -454,7 +380,7 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     load_slabs(c_begin);
     rv.load(vrow(v, c_begin), rsV, l);
     __syncthreads();
-    pipe_prep<T, CPK>(sm.buf[c_begin & 1], Sm::pQ, rq, rk, rg, kc0, 0, NG);
+    pipe_prep<T, CPK>(sm.buf[c_begin & 1], Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, NG);
     rv.store_lds(vslice(c_begin), Sm::pW, l);
     if (c_begin + 1 < c_end) {
         load_slabs(c_begin + 1);
@@ -475,10 +401,10 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks)
-                    acc = mma32(acc, frag_rm<T>(cur.Kt, Sm::pQ, 16 * js, 32 * ks),
-                                frag_rm<T>(cur.Kt, Sm::pQ, 16 * js, 32 * ks + 16),
-                                frag_rm<T>(cur.Ql, Sm::pQ, 16 * is, 32 * ks),
-                                frag_rm<T>(cur.Ql, Sm::pQ, 16 * is, 32 * ks + 16));
+                    acc = mma32(acc, frag_rm<T>(cur.Kt, Sm::pKt, 16 * js, 32 * ks),
+                                frag_rm<T>(cur.Kt, Sm::pKt, 16 * js, 32 * ks + 16),
+                                frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks),
+                                frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks + 16));
                 // acc holds A^T[s][t] for s = 16js + 4(l/16) + r, t = 16is + l%16
                 if (is == js) {
 #pragma unroll
@@ -542,8 +468,8 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                 }
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    const vec4_t<T> blo = frag_rm<T>(cur.Ql, Sm::pQ, 16 * rb, 32 * ks);
-                    const vec4_t<T> bhi = frag_rm<T>(cur.Ql, Sm::pQ, 16 * rb, 32 * ks + 16);
+                    const vec4_t<T> blo = frag_rm<T>(cur.Ql, Sm::pQl, 16 * rb, 32 * ks);
+                    const vec4_t<T> bhi = frag_rm<T>(cur.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
                         acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], blo, bhi);
@@ -553,9 +479,9 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         if (w < NW / 2) {
             inter();
             __builtin_amdgcn_sched_barrier(0);
-            pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, 0, MG);
+            pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
         } else {
-            pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, 0, MG);
+            pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
             __builtin_amdgcn_sched_barrier(0);
             inter();
         }
@@ -600,8 +526,8 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                 for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                     for (int a = 0; a < KD / 16; ++a) {
-                        const vec4_t<T> xlo = frag_cm<T>(cur.Kt, Sm::pQ, 32 * ks, 16 * a);
-                        const vec4_t<T> xhi = frag_cm<T>(cur.Kt, Sm::pQ, 32 * ks + 16, 16 * a);
+                        const vec4_t<T> xlo = frag_cm<T>(cur.Kt, Sm::pKt, 32 * ks, 16 * a);
+                        const vec4_t<T> xhi = frag_cm<T>(cur.Kt, Sm::pKt, 32 * ks + 16, 16 * a);
 #pragma unroll
                         for (int cb = 0; cb < CB; ++cb)
                             S.s[a][cb] = mma32(S.s[a][cb], xlo, xhi, vf[2 * ks][cb], vf[2 * ks + 1][cb]);
@@ -617,9 +543,9 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
             if (w < NW / 2) {
                 update();
                 __builtin_amdgcn_sched_barrier(0);
-                pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, MG, NG);
+                pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
             } else {
-                pipe_prep<T, CPK>(nxt, Sm::pQ, rq, rk, rg, kc0, MG, NG);
+                pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
                 __builtin_amdgcn_sched_barrier(0);
                 update();
             }
@@ -660,7 +586,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
-        static_assert(sizeof(PipeSmem<T, KD, BV, NW>) <= 160 * 1024, "LDS budget");
+        static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
                            (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
