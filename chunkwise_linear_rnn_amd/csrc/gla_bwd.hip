@@ -323,6 +323,274 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// LDS of the software-pipelined row-split walks (16-bit operands): full-width
+// value and d_o tiles, the 64x64 dP tile, the value-slice partial sums, and a
+// double-buffered key-side slice of BK columns per chunk (the decayed operand
+// read with column fragments, the fp32 cumulative log gate, the per-column
+// state-update factors).
+template <typename T, int BK, int V, int NW>
+struct RowPipeSmem {
+    using RR = RowRoles<BK, V, NW>;
+    static constexpr int PT = Elem<T>::pad;
+    static constexpr int pV = V + PT;
+    static constexpr int pP = kChunk + PT;
+    // column fragments only: 8 mod 64 dwords keeps a transposed read's four rows apart
+    static constexpr int pK = sizeof(T) == 2 ? BK + 16 : BK + 4;
+    static constexpr int pB = BK + 4;
+    struct alignas(16) Buf {
+        T K[kChunk * pK];
+        float B[kChunk * pB];
+        float pre[BK];
+        float post[BK];
+        int flag[4];
+    };
+    Buf buf[2];
+    union {
+        struct {
+            alignas(16) T Vt[kChunk * pV];
+            alignas(16) T dO[kChunk * pV];
+        };
+        alignas(16) float X[kChunk * BK];  // exact-path intra sums, phase 2 only
+    };
+    alignas(16) T P[kChunk * pP];
+    alignas(16) f32x4 red[RR::VS > 1 ? RR::NKQ * 4 * 64 : 1];
+    float carry[RR::VS * BK];
+};
+
+// One wave prepares key columns kc0 .. kc0+NC-1 of a chunk (lane = token row)
+// for the row-split walks: the fp32 cumulative log gate B, the decayed operand
+// X = x * exp2(sgn * B_t) (QL: sgn = +1, X = q * Lambda; else the key factor of
+// the chunk-start basis, k * exp2(-B_s), or k * exp2(B_63 - B_s) beyond
+// kBasisLimit) and the state-update factors.  QL operands never exceed 1 in
+// magnitude factor, so (pre, post) = (gamma, 1) for them.
+template <typename T, int NC, bool QL, typename Buf>
+__device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<T, NC>& rx, const RowSlab<T, NC>& rg,
+                                         int kc0) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    static_assert(NC <= 64, "one lane per prepared column");
+    const int l = lane_id();
+    float last_l = 0.f;
+    bool wide = false;
+#pragma unroll
+    for (int j0 = 0; j0 < NC; j0 += VEC) {
+        float bt[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
+        wave_incl_scan_n<VEC>(bt);
+        float xv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float bl = lane_bcast(bt[e], 63);
+            last_l = (l == j0 + e) ? bl : last_l;
+            if (QL) {
+                xv[e] = rx.get(j0 + e) * exp2_fast(bt[e]);
+            } else {
+                const bool in = -bl <= kBasisLimit;
+                wide |= !in;
+                xv[e] = rx.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
+            }
+        }
+        store_vec_lds<T>(bf.K + l * pK + kc0 + j0, xv);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<f32x4*>(bf.B + l * pB + kc0 + j0 + e) = f32x4{bt[e], bt[e + 1], bt[e + 2], bt[e + 3]};
+    }
+    if (l < NC) {
+        const float gm = exp2_fast(last_l);
+        const bool in = QL || -last_l <= kBasisLimit;
+        bf.pre[kc0 + l] = in && !QL ? 1.f : gm;
+        bf.post[kc0 + l] = in && !QL ? gm : 1.f;
+    }
+    if (wide && l == 0) bf.flag[0] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// dq walk, software-pipelined (16-bit operands): forwards over one segment for
+// key rows k0 .. k0+BK-1, full V, in the chunk-start basis:
+//   dq_t = exp2(B_t) * [dO S_in^T + dP Kt]_t,   Kt = k * exp2(-B_s)
+// (exact-path chunks: the intra part element by element from raw k and B).
+// Phase 1: dP, the value-slice partial of dO S^T, the state update
+// S^T <- post * (pre * S^T + V^T Kt), the store of S_out to `hs`, the next
+// chunk's key-side preparation.  Phase 2: dP Kt, the slice reduction, the
+// factor exp2(B_t) and the store of dq; the next chunk's V and d_o tiles.
+template <typename T, int BK, int V, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
+                const float* __restrict__ s_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dq,
+                T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len, int BH) {
+    constexpr int NT = NW * 64;
+    using RR = RowRoles<BK, V, NW>;
+    constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
+    static_assert(CPK % VEC == 0, "wave tiling");
+    using Sm = RowPipeSmem<T, BK, V, NW>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int kq = w % RR::NKQ, vs = w / RR::NKQ;
+    const int i0 = 16 * kq, j0 = vs * VW;
+    const int kc0 = w * CPK;
+    const int nkb = K / BK;
+    int unit, kb;
+    xcd_decode(nkb, unit, kb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
+    const int b = bh / H, h = bh % H;
+    const int k0 = kb * BK;
+    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const int rsK = H * K, rsV = H * V;
+
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int t = e / kChunk, s = e % kChunk;
+        if ((s >> 4) > (t >> 4)) sm.P[t * Sm::pP + s] = Elem<T>::from_f(0.f);
+    }
+    if (tid < 2) sm.buf[tid].flag[0] = 0;
+    TStateRegs<VW> S;
+    if (s_init) S.load(s_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, V, i0, j0);
+    else S.zero();
+
+    RowSlab<T, CPK> rk, rg;
+    using TRV = TileRegs<T, V, NT>;
+    TRV rv, rdo;
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
+    rk.load(kbase(k, c_begin), rsK, kc0);
+    rg.load(kbase(g, c_begin), rsK, kc0);
+    rv.load(vbase(v, c_begin), rsV, tid);
+    rdo.load(vbase(d_o, c_begin), rsV, tid);
+    __syncthreads();
+    row_prep<T, CPK, false>(sm.buf[c_begin & 1], Sm::pK, Sm::pB, rk, rg, kc0);
+    rv.store_lds(sm.Vt, Sm::pV, tid);
+    rdo.store_lds(sm.dO, Sm::pV, tid);
+    if (c_begin + 1 < c_end) {
+        rk.load(kbase(k, c_begin + 1), rsK, kc0);
+        rg.load(kbase(g, c_begin + 1), rsK, kc0);
+        rv.load(vbase(v, c_begin + 1), rsV, tid);
+        rdo.load(vbase(d_o, c_begin + 1), rsV, tid);
+    }
+    __syncthreads();
+    for (int c = c_begin; c < c_end; ++c) {
+        auto& cur = sm.buf[c & 1];
+        auto& nxt = sm.buf[(c + 1) & 1];
+        const bool more = c + 1 < c_end;
+        const bool exact = cur.flag[0] != 0;
+        // ---- phase 1
+        dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
+        // dq^T[i][t] partial = sum_{j in slice} S^T[j][i] dO[t][j]
+        f32x4 acc[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[tb] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < VW / 32; ++ks) {
+            const vec4_t<T> s0 = to_vec4<T>(S.s[2 * ks]);
+            const vec4_t<T> s1 = to_vec4<T>(S.s[2 * ks + 1]);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[tb] = mma32(acc[tb], s0, s1, frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks),
+                                frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks + 16));
+        }
+        if (RR::VS > 1 && vs == 1)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) sm.red[(kq * 4 + tb) * 64 + l] = acc[tb];
+        // S^T <- post * (pre * S^T + V^T Kt); this lane's key column is i0 + l%16
+        {
+            const float pre = cur.pre[i0 + (l & 15)], post = cur.post[i0 + (l & 15)];
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= pre;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const vec4_t<T> x0 = frag_cm<T>(cur.K, Sm::pK, 32 * ks, i0);
+                const vec4_t<T> x1 = frag_cm<T>(cur.K, Sm::pK, 32 * ks + 16, i0);
+#pragma unroll
+                for (int jb = 0; jb < VW / 16; ++jb)
+                    S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.Vt, Sm::pV, 32 * ks, j0 + 16 * jb),
+                                    frag_cm<T>(sm.Vt, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
+            }
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= post;
+            T* dst = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb)
+                *reinterpret_cast<vec4_t<T>*>(dst + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4) =
+                    to_vec4<T>(S.s[jb]);
+        }
+        if (more) {
+            row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
+            if (c + 2 < c_end) {
+                rk.load(kbase(k, c + 2), rsK, kc0);
+                rg.load(kbase(g, c + 2), rsK, kc0);
+            }
+        }
+        __syncthreads();
+        // ---- phase 2
+        if (!exact) {
+            if (vs == 0) {
+                // dq^T[i][t] += sum_s Kt[s][i] dP[t][s]
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                    for (int ks2 = 0; ks2 <= tb / 2; ++ks2)
+                        acc[tb] = mma32(acc[tb], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
+                                        frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
+                                        frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
+                                        frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16));
+                }
+            }
+        } else {
+            // intra part element by element, sum_{s<=t} dP[t][s] k_s exp2(B_t - B_s),
+            // into an fp32 [t][i] tile over the (now unused) value tiles
+            float* Xf = sm.X;
+            RowSlab<T, CPK> xk;
+            xk.load(kbase(k, c), rsK, kc0);
+            float bt[CPK], sum[CPK];
+#pragma unroll
+            for (int j = 0; j < CPK; ++j) {
+                bt[j] = cur.B[l * Sm::pB + kc0 + j];
+                sum[j] = 0.f;
+            }
+            for (int s = 0; s < kChunk; ++s) {
+                const float dp = Elem<T>::to_f(sm.P[l * Sm::pP + s]);
+#pragma unroll
+                for (int j = 0; j < CPK; ++j) {
+                    // s > t: dP is zero there and exp2 may overflow, so the term is selected away
+                    const float term = dp * lane_bcast(xk.get(j), s) * exp2_fast(bt[j] - lane_bcast(bt[j], s));
+                    sum[j] += s <= l ? term : 0.f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CPK; ++j) Xf[l * BK + kc0 + j] = sum[j];
+            __syncthreads();
+        }
+        if (vs == 0) {
+            const float* Xf = sm.X;
+            T* dqbase = const_cast<T*>(kbase(dq, c));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                if (RR::VS > 1) acc[tb] += sm.red[(kq * 4 + tb) * 64 + l];
+                // slot r: key row i = i0 + 4(l/16) + r, token t = 16tb + l%16
+                const int t = 16 * tb + (l & 15), ic = i0 + 4 * (l >> 4);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(cur.B + t * Sm::pB + ic);
+                f32x4 val;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) val[r] = acc[tb][r] * exp2_fast(bt[r]);
+                if (exact) val += *reinterpret_cast<const f32x4*>(Xf + t * BK + ic);
+                *reinterpret_cast<vec4_t<T>*>(dqbase + t * rsK + ic) = to_vec4<T>(val);
+            }
+        }
+        if (exact) __syncthreads();
+        if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
+        if (more) {
+            rv.store_lds(sm.Vt, Sm::pV, tid);
+            rdo.store_lds(sm.dO, Sm::pV, tid);
+            if (c + 2 < c_end) {
+                rv.load(vbase(v, c + 2), rsV, tid);
+                rdo.load(vbase(d_o, c + 2), rsV, tid);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dk + dg walk: backwards over one segment for key rows k0 .. k0+BK-1, full V.
 // State dS^T in VGPRs.  dk_s = Gamma_s * [V dS_out^T + dP^T (q*exp2(B_t - B_63))]_s
 // (accumulated transposed), then dA = q*dq - k*dk and dg = reverse cumulative
@@ -1035,9 +1303,16 @@ static hipError_t launch_rows(const BwdLaunch& a) {
     const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
-    GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k, (const T*)a.v,
-                       (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq, (T*)a.ws_hs,
-                       a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+    if constexpr (sizeof(T) == 2) {
+        static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
+        GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
+                           (const T*)a.v, (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq,
+                           (T*)a.ws_hs, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+    } else {
+        GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
+                           (const T*)a.v, (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq,
+                           (T*)a.ws_hs, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+    }
     GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit, seg_stride, bh_stride,
                        (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
