@@ -362,7 +362,8 @@ struct RowPipeSmem {
 // X = x * exp2(sgn * B_t) (QL: sgn = +1, X = q * Lambda; else the key factor of
 // the chunk-start basis, k * exp2(-B_s), or k * exp2(B_63 - B_s) beyond
 // kBasisLimit) and the state-update factors.  QL operands never exceed 1 in
-// magnitude factor, so (pre, post) = (gamma, 1) for them.
+// magnitude factor, so (pre, post) = (gamma, 1) for them.  The chunk is flagged
+// for the exact path if a column's decay exceeds kBasisLimit.
 template <typename T, int NC, bool QL, typename Buf>
 __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<T, NC>& rx, const RowSlab<T, NC>& rg,
                                          int kc0) {
@@ -382,13 +383,10 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
         for (int e = 0; e < VEC; ++e) {
             const float bl = lane_bcast(bt[e], 63);
             last_l = (l == j0 + e) ? bl : last_l;
-            if (QL) {
-                xv[e] = rx.get(j0 + e) * exp2_fast(bt[e]);
-            } else {
-                const bool in = -bl <= kBasisLimit;
-                wide |= !in;
-                xv[e] = rx.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
-            }
+            const bool in = -bl <= kBasisLimit;
+            wide |= !in;
+            if (QL) xv[e] = rx.get(j0 + e) * exp2_fast(bt[e]);
+            else xv[e] = rx.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
         }
         store_vec_lds<T>(bf.K + l * pK + kc0 + j0, xv);
 #pragma unroll
@@ -584,6 +582,268 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
             if (c + 2 < c_end) {
                 rv.load(vbase(v, c + 2), rsV, tid);
                 rdo.load(vbase(d_o, c + 2), rsV, tid);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk + dg walk, software-pipelined (16-bit operands): backwards over one
+// segment for key rows k0 .. k0+BK-1, full V.  With dS = dS_out of the chunk,
+// Ql = q * exp2(B_t) and Gamma_s = exp2(B_63 - B_s):
+//   dk_s = exp2(-B_s) * [V (gamma dS)^T + dP^T Ql]_s            (in range)
+//        = Gamma_s * [V dS^T]_s + sum_{t>=s} dP_ts q_t exp2(B_t - B_s)  (exact path)
+//   dA   = q*dq - k*dk (fp32 dk),  dg_t = sum_{r>=t in chunk} dA_r + rowsum(S_out * dS)
+//   dS_in = Diag(gamma) dS + Ql^T dO
+// Phase 1: dP^T, the value-slice partials of V dS^T and of the dg anchor (S_out
+// read back from `hs`), the dS update, the previous chunk's query-side
+// preparation.  Phase 2: dP^T Ql, the slice reduction and the factors, dk, dA
+// and its reverse cumulative sum down the 16-lane rows (DPP) and across the
+// four token blocks, dg; the next value and d_o tiles.
+template <typename T, int BK, int V, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
+                const T* __restrict__ d_o, const T* __restrict__ dq, const float* __restrict__ ds_init,
+                long s_seg_stride, long s_bh_stride, const T* __restrict__ hs, T* __restrict__ dk,
+                T* __restrict__ dg, int T_, int H, int K, int N, int P, int seg_len, int BH) {
+    constexpr int NT = NW * 64;
+    using RR = RowRoles<BK, V, NW>;
+    constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
+    static_assert(CPK % VEC == 0, "wave tiling");
+    using Sm = RowPipeSmem<T, BK, V, NW>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int kq = w % RR::NKQ, vs = w / RR::NKQ;
+    const int i0 = 16 * kq, j0 = vs * VW;
+    const int kc0 = w * CPK;
+    const int nkb = K / BK;
+    int unit, kb;
+    xcd_decode(nkb, unit, kb);
+    if (unit >= BH * P) return;
+    const int seg = unit % P;
+    const int bh = unit / P;
+    const int b = bh / H, h = bh % H;
+    const int k0 = kb * BK;
+    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const int nchunks = c_end - c_begin;
+    const int rsK = H * K, rsV = H * V;
+    auto chunk_of = [&](int it) { return c_end - 1 - it; };
+
+    // dP^T is stored [s][t]; its tiles with t-block < s-block are zero
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+        const int s = e / kChunk, t = e % kChunk;
+        if ((t >> 4) < (s >> 4)) sm.P[s * Sm::pP + t] = Elem<T>::from_f(0.f);
+    }
+    if (tid < 2) sm.buf[tid].flag[0] = 0;
+    TStateRegs<VW> S;  // dS^T
+    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, V, i0, j0);
+    else S.zero();
+
+    RowSlab<T, CPK> rq, rg;
+    using TRV = TileRegs<T, V, NT>;
+    TRV rv, rdo;
+    auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
+    if (nchunks > 0) {
+        rq.load(kbase(q, chunk_of(0)), rsK, kc0);
+        rg.load(kbase(g, chunk_of(0)), rsK, kc0);
+        rv.load(vbase(v, chunk_of(0)), rsV, tid);
+        rdo.load(vbase(d_o, chunk_of(0)), rsV, tid);
+    }
+    __syncthreads();
+    if (nchunks > 0) {
+        row_prep<T, CPK, true>(sm.buf[0], Sm::pK, Sm::pB, rq, rg, kc0);
+        rv.store_lds(sm.Vt, Sm::pV, tid);
+        rdo.store_lds(sm.dO, Sm::pV, tid);
+        if (nchunks > 1) {
+            rq.load(kbase(q, chunk_of(1)), rsK, kc0);
+            rg.load(kbase(g, chunk_of(1)), rsK, kc0);
+            rv.load(vbase(v, chunk_of(1)), rsV, tid);
+            rdo.load(vbase(d_o, chunk_of(1)), rsV, tid);
+        }
+    }
+    __syncthreads();
+    for (int it = 0; it < nchunks; ++it) {
+        const int c = chunk_of(it);
+        auto& cur = sm.buf[it & 1];
+        auto& nxt = sm.buf[(it + 1) & 1];
+        const bool more = it + 1 < nchunks;
+        const bool exact = cur.flag[0] != 0;
+        // ---- phase 1
+        // loads for later in this chunk: S_out tiles (dg anchor); q, dq, k in the
+        // accumulator layout (slot r of token block sb: token 16sb + l%16, key
+        // column i0 + 4(l/16) + r) for dA
+        vec4_t<T> so[VW / 16];
+        {
+            const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb)
+                so[jb] = *reinterpret_cast<const vec4_t<T>*>(src + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4);
+        }
+        vec4_t<T> aq[4], adq[4], ak[4];
+        if (vs == 0) {
+            const long off = (long)(l & 15) * rsK + i0 + 4 * (l >> 4);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                aq[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(q, c) + off + 16 * sb * rsK);
+                adq[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(dq, c) + off + 16 * sb * rsK);
+                ak[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(k, c) + off + 16 * sb * rsK);
+            }
+        }
+        dp_tiles<T, V, true>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
+        const float gl = cur.pre[i0 + (l & 15)];  // gamma of this lane's key column
+        // dk^T[i][s] partial = sum_{j in slice} (gamma dS)[i][j] V[s][j] (exact path: dS unscaled)
+        f32x4 acc[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4();
+        {
+            const float sc = exact ? 1.f : gl;
+#pragma unroll
+            for (int ks = 0; ks < VW / 32; ++ks) {
+                const vec4_t<T> s0 = to_vec4<T>(S.s[2 * ks] * sc);
+                const vec4_t<T> s1 = to_vec4<T>(S.s[2 * ks + 1] * sc);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+                    acc[sb] = mma32(acc[sb], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks),
+                                    frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks + 16));
+            }
+        }
+        // anchor partial: sum_{j in slice} S_out[i][j] dS[i][j]
+        {
+            float part = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part += Elem<T>::to_f(so[jb][r]) * S.s[jb][r];
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if ((l >> 4) == 0) sm.carry[vs * BK + i0 + (l & 15)] = part;
+        }
+        if (RR::VS > 1 && vs == 1)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) sm.red[(kq * 4 + sb) * 64 + l] = acc[sb];
+        // dS^T <- gamma dS^T + dO^T Ql
+#pragma unroll
+        for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= gl;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const vec4_t<T> x0 = frag_cm<T>(cur.K, Sm::pK, 32 * ks, i0);
+            const vec4_t<T> x1 = frag_cm<T>(cur.K, Sm::pK, 32 * ks + 16, i0);
+#pragma unroll
+            for (int jb = 0; jb < VW / 16; ++jb)
+                S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.dO, Sm::pV, 32 * ks, j0 + 16 * jb),
+                                frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
+        }
+        if (more) {
+            row_prep<T, CPK, true>(nxt, Sm::pK, Sm::pB, rq, rg, kc0);
+            if (it + 2 < nchunks) {
+                rq.load(kbase(q, chunk_of(it + 2)), rsK, kc0);
+                rg.load(kbase(g, chunk_of(it + 2)), rsK, kc0);
+            }
+        }
+        __syncthreads();
+        // ---- phase 2
+        if (exact) {
+            // intra part element by element, sum_{t>=s} dP^T[s][t] q_t exp2(B_t - B_s),
+            // into an fp32 [s][i] tile over the (now unused) value tiles
+            RowSlab<T, CPK> xq;
+            xq.load(kbase(q, c), rsK, kc0);
+            float bs[CPK], sum[CPK];
+#pragma unroll
+            for (int j = 0; j < CPK; ++j) {
+                bs[j] = cur.B[l * Sm::pB + kc0 + j];
+                sum[j] = 0.f;
+            }
+            for (int t = 0; t < kChunk; ++t) {
+                const float dp = Elem<T>::to_f(sm.P[l * Sm::pP + t]);
+#pragma unroll
+                for (int j = 0; j < CPK; ++j) {
+                    // t < s: dP^T is zero there and exp2 may overflow, so the term is selected away
+                    const float term = dp * lane_bcast(xq.get(j), t) * exp2_fast(lane_bcast(bs[j], t) - bs[j]);
+                    sum[j] += t >= l ? term : 0.f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CPK; ++j) sm.X[l * BK + kc0 + j] = sum[j];
+            __syncthreads();
+        }
+        if (vs == 0) {
+            if (!exact) {
+                // dk^T[i][s] += sum_t Ql[t][i] dP^T[s][t], t-blocks >= sb
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int ks2 = sb / 2; ks2 < 2; ++ks2)
+                        acc[sb] = mma32(acc[sb], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
+                                        frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
+                                        frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
+                                        frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16));
+            }
+            const int ic = i0 + 4 * (l >> 4);
+            const f32x4 blast = *reinterpret_cast<const f32x4*>(cur.B + 63 * Sm::pB + ic);
+            T* dkbase = const_cast<T*>(kbase(dk, c));
+            f32x4 da[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                if (RR::VS > 1) acc[sb] += sm.red[(kq * 4 + sb) * 64 + l];
+                // slot r: key column ic + r, token s = 16sb + l%16
+                const int s = 16 * sb + (l & 15);
+                const f32x4 bs = *reinterpret_cast<const f32x4*>(cur.B + s * Sm::pB + ic);
+                f32x4 val;
+                if (!exact) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) val[r] = acc[sb][r] * exp2_fast(-bs[r]);
+                } else {
+                    const f32x4 xs = *reinterpret_cast<const f32x4*>(sm.X + s * BK + ic);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) val[r] = acc[sb][r] * exp2_fast(blast[r] - bs[r]) + xs[r];
+                }
+                *reinterpret_cast<vec4_t<T>*>(dkbase + s * rsK + ic) = to_vec4<T>(val);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    da[sb][r] = Elem<T>::to_f(aq[sb][r]) * Elem<T>::to_f(adq[sb][r]) -
+                                Elem<T>::to_f(ak[sb][r]) * val[r];
+            }
+            // reverse cumulative sum over the chunk's tokens: within each 16-token
+            // block down the 16-lane rows (DPP row_shl), then across the blocks
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = da[sb][r];
+                    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x101, 0xF, 0xF, false);
+                    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x102, 0xF, 0xF, false);
+                    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x104, 0xF, 0xF, false);
+                    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x108, 0xF, 0xF, false);
+                    da[sb][r] = x;
+                }
+            }
+            f32x4 run;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) run[r] = sm.carry[ic + r] + (RR::VS > 1 ? sm.carry[BK + ic + r] : 0.f);
+            T* dgbase = const_cast<T*>(kbase(dg, c));
+#pragma unroll
+            for (int sb = 3; sb >= 0; --sb) {
+                const int s = 16 * sb + (l & 15);
+                f32x4 out, tot;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    out[r] = da[sb][r] + run[r];
+                    tot[r] = __shfl(da[sb][r], l & 48);  // the block's total sits in its row's first lane
+                }
+                *reinterpret_cast<vec4_t<T>*>(dgbase + s * rsK + ic) = to_vec4<T>(out);
+                run += tot;
+            }
+        }
+        if (exact) __syncthreads();
+        if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
+        if (more) {
+            rv.store_lds(sm.Vt, Sm::pV, tid);
+            rdo.store_lds(sm.dO, Sm::pV, tid);
+            if (it + 2 < nchunks) {
+                rv.load(vbase(v, chunk_of(it + 2)), rsV, tid);
+                rdo.load(vbase(d_o, chunk_of(it + 2)), rsV, tid);
             }
         }
         __syncthreads();
@@ -1313,9 +1573,17 @@ static hipError_t launch_rows(const BwdLaunch& a) {
                            (const T*)a.v, (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq,
                            (T*)a.ws_hs, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     }
-    GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit, seg_stride, bh_stride,
-                       (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+    if constexpr (sizeof(T) == 2) {
+        GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit,
+                           seg_stride, bh_stride, (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P,
+                           a.seg_len, (int)a.BH);
+    } else {
+        GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit,
+                           seg_stride, bh_stride, (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P,
+                           a.seg_len, (int)a.BH);
+    }
     return hipGetLastError();
 }
 
