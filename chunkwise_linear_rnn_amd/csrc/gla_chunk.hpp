@@ -94,11 +94,11 @@ __device__ __forceinline__ void state_update(StateRegs<KD, CB>& S, const T* X, i
 }
 
 __device__ __forceinline__ void decode_tile(int tile, int& is, int& js) {
-    // lower-triangular 16x16 tiles of the 64x64 chunk, row by row
-    constexpr int tis[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int tjs[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    is = tis[tile];
-    js = tjs[tile];
+    // lower-triangular 16x16 tiles of the 64x64 chunk, row by row.  Computed, not
+    // looked up: a table indexed at run time becomes a global load, and waiting
+    // for it would also wait for every prefetch issued before it.
+    is = (tile >= 1) + (tile >= 3) + (tile >= 6);
+    js = tile - (is * (is + 1)) / 2;
 }
 
 // ---------------------------------------------------------------------------
