@@ -32,17 +32,18 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = "GLA fwd(+bwd) tokens/sec at T=8K, dk=128, dv=256; % of bf16 MFMA peak"
 
 
-def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int):
+def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int):
     """Algorithmic HBM bytes per (token, head) of one launch of `kernel`."""
     seg_frac = (P - 1) / P if P > 1 else 0.0
+    seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
     table = {
         "fwd_walk": e * (3 * K + 2 * V),            # q, k, g, v read; o written
         "bwd_dq_walk": e * (3 * K + 2 * V),         # k, g, v, d_o read; dq written
         "bwd_dk_walk": e * (6 * K + 2 * V),         # q, k, g, dq, v, d_o read; dk, dg written
         "bwd_dv_walk": e * (3 * K + 2 * V),         # q, k, g, d_o read; dv written
         "fwd_seg_state": e * (2 * K + V) * seg_frac,  # k, g, v of all but the last segment
-        "bwd_seg_state": e * (2 * K + V) * seg_frac,
-        "bwd_seg_state_rev": e * (2 * K + V) * seg_frac,
+        # k, g, v of all but the last segment and q, g, d_o of all but the first
+        "bwd_seg_states": 2 * e * (2 * K + V) * seg_frac_bwd,
     }
     return table.get(kernel)
 
@@ -56,19 +57,35 @@ def bwd_flops_per_token_head(K, V, C=64):
     return 10 * K * V + (C + 1) * (3 * K + 2 * V)
 
 
+def _segments(bh, n, blocks):
+    P = max(1, 256 // (bh * blocks)) if bh * blocks > 0 else 1
+    P = min(P, max(n, 1))
+    seg_len = -(-n // P)
+    return -(-n // seg_len)
+
+
 def plan_segments(B, H, T, K, V, bf16):
-    """Segments per head chosen by the library's launch plan (mirrors gla_plan.hpp)."""
+    """Forward segments per head chosen by the library's launch plan (mirrors gla_plan.hpp)."""
     if bf16:
         cap = 256 if K <= 128 else 64
     else:
         cap = 128
     bv = min(V, cap)
-    bh, n = B * H, T // 64
-    per_seg = bh * (V // bv)
-    P = max(1, 256 // per_seg) if per_seg > 0 else 1
-    P = min(P, max(n, 1))
-    seg_len = -(-n // P)
-    return -(-n // seg_len)
+    return _segments(B * H, T // 64, V // bv)
+
+
+def plan_segments_bwd(B, H, T, K, V, bf16):
+    """Backward segments per head (gla_plan.hpp's make_bwd_plan)."""
+    bk = 64 if (not bf16 or V >= 128) else min(K, 128)
+    nkb = K // bk
+    cap = (256 if K <= 128 else 64) if bf16 else 128
+    bv = min(V, cap)
+    if nkb > 1 and V // nkb < bv:
+        bv = V // nkb
+    if bv < 64:
+        bv = V if V < 64 else 64
+    nvb = V // bv
+    return _segments(B * H, T // 64, max(nvb, nkb))
 
 
 def source_digest() -> str:
@@ -222,8 +239,9 @@ def main():
             for n, (c, ms) in kt.items()}
     dom = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches"])
     P = plan_segments(B, H, T, K, V, w.dtype == "bf16")
+    P_bwd = plan_segments_bwd(B, H, T, K, V, w.dtype == "bf16")
     units = B * T * H
-    bpt = alg_bytes_per_token_head(dom, K, V, e, P)
+    bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd)
     roofline = None
     if bpt is not None:
         ach = bpt * units / (kern[dom]["avg_us"] * 1e-6) / 1e9

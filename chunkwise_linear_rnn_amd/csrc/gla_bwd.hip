@@ -1510,12 +1510,11 @@ static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
     if (a.P > 1) {
         const int nseg = a.P - 1;
         dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
-        GLA_LAUNCH("bwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream, (const T*)a.k,
-                           (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, 0,
-                           nseg, (int)a.BH);
-        GLA_LAUNCH("bwd_seg_state_rev", (gla_seg_state<T, KD, BV, NW, true>), grid, dim3(NT), a.stream, (const T*)a.q,
-                           (const T*)a.g, (const T*)a.d_o, a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P,
-                           a.seg_len, 1, nseg, (int)a.BH);
+        const long nfwd = xcd_grid(nseg * a.BH, nvb);
+        dim3 grid2((unsigned)(2 * nfwd));
+        GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW>), grid2, dim3(NT), a.stream, (const T*)a.k,
+                           (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, a.ws_state, a.ws_dstate,
+                           a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd);
         GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd, dim3((unsigned)((KV + 255) / 256), (unsigned)a.BH, 2u),
                            dim3(256), a.stream, a.s0,
                            a.dht, a.ws_state, a.ws_dstate, a.ws_gate, KD, a.V, a.P);

@@ -256,21 +256,22 @@ struct SegSmem {
     alignas(16) T Yw[2 * NW * kChunk * pW];
 };
 
+// One workgroup's segment; `bid` is its block index within its own grid.
 template <typename T, int KD, int BV, int NW, bool REV>
-__global__ void __launch_bounds__(NW * 64)
-gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
-              float* __restrict__ ws_state, float* __restrict__ ws_gate,
-              int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg, int BH) {
+__device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int bid, const T* __restrict__ x,
+                                               const T* __restrict__ g, const T* __restrict__ y,
+                                               float* __restrict__ ws_state, float* __restrict__ ws_gate, int T_,
+                                               int H, int V, int N, int P, int seg_len, int seg_first, int nseg,
+                                               int BH, int gate_first) {
     using Sm = SegSmem<T, KD, BV, NW>;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
     constexpr int VEC = 16 / (int)sizeof(T);
     static_assert(CW % 16 == 0 && CPK % VEC == 0 && CPK <= 64, "wave tiling");
     static_assert(sizeof(Sm) <= 160 * 1024, "LDS budget");
-    __shared__ Sm sm;
     const int w = wave_id(), l = lane_id();
     const int nvb = V / BV;
     int unit, vb;
-    xcd_decode(nvb, unit, vb);
+    xcd_decode(nvb, unit, vb, bid);
     if (unit >= BH * nseg) return;
     const int seg = seg_first + unit % nseg;
     const int bh = unit / nseg;
@@ -374,7 +375,38 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
         __syncthreads();
     }
     S.store(ws_state + ((long)bh * P + seg) * (long)KD * V, V, col0);
-    if (vb == 0 && l < CPK) ws_gate[((long)bh * P + seg) * KD + kc0 + l] = gtot;
+    // each segment's gate total is written by one workgroup only (segments >= gate_first)
+    if (vb == 0 && seg >= gate_first && l < CPK) ws_gate[((long)bh * P + seg) * KD + kc0 + l] = gtot;
+}
+
+template <typename T, int KD, int BV, int NW, bool REV>
+__global__ void __launch_bounds__(NW * 64)
+gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
+              float* __restrict__ ws_state, float* __restrict__ ws_gate,
+              int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg, int BH) {
+    __shared__ SegSmem<T, KD, BV, NW> sm;
+    seg_state_body<T, KD, BV, NW, REV>(sm, blockIdx.x, x, g, y, ws_state, ws_gate, T_, H, V, N, P, seg_len,
+                                       seg_first, nseg, BH, 0);
+}
+
+// Both directions of the backward's segment states in one grid (they are
+// independent): blocks [0, nfwd) take S*_p of segments 0 .. P-2 from k, v; the
+// rest take dS*_p of segments 1 .. P-1 from q, d_o.  Two workgroups fit a CU,
+// so the directions share the machine instead of running back to back.
+template <typename T, int KD, int BV, int NW>
+__global__ void __launch_bounds__(NW * 64)
+gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ q,
+                   const T* __restrict__ d_o, const T* __restrict__ g, float* __restrict__ ws_state,
+                   float* __restrict__ ws_dstate, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
+                   int seg_len, int nseg, int BH, int nfwd) {
+    __shared__ SegSmem<T, KD, BV, NW> sm;
+    const int bid = blockIdx.x;
+    if (bid < nfwd)
+        seg_state_body<T, KD, BV, NW, false>(sm, bid, k, g, v, ws_state, ws_gate, T_, H, V, N, P, seg_len, 0, nseg,
+                                             BH, 0);
+    else  // only segment P-1 is not covered by the forward direction
+        seg_state_body<T, KD, BV, NW, true>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P, seg_len,
+                                            1, nseg, BH, P - 1);
 }
 
 }  // namespace gla

@@ -48,12 +48,12 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // (unit >= units) must exit at once.
 constexpr int kXcds = 8;
 __host__ __device__ inline long xcd_grid(long units, int G) { return (units + kXcds - 1) / kXcds * kXcds * G; }
-__device__ __forceinline__ void xcd_decode(int G, int& unit, int& sib) {
-    const int bid = blockIdx.x;
+__device__ __forceinline__ void xcd_decode(int G, int& unit, int& sib, int bid) {
     const int rest = bid / kXcds;
     sib = rest % G;
     unit = (rest / G) * kXcds + bid % kXcds;
 }
+__device__ __forceinline__ void xcd_decode(int G, int& unit, int& sib) { xcd_decode(G, unit, sib, blockIdx.x); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
