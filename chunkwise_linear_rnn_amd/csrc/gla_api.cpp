@@ -147,8 +147,8 @@ gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.o = o;
         a.s_final = s_final;
         if (p.P > 1) {
-            a.ws_state = static_cast<float*>(workspace);
-            a.ws_gate = a.ws_state + (size_t)p.BH * p.P * s.K * s.V;
+            a.ws_state = workspace;
+            a.ws_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + gla::state_bytes(s, p));
         }
         a.stream = strm;
         err = gla::launch_fwd(a);
@@ -197,13 +197,13 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.q = q; a.k = k; a.v = v; a.g = g; a.d_o = d_o;
         a.s0 = s0; a.dht = dht;
         a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.ds0 = ds0;
-        const size_t kv = (size_t)p.BH * p.P * s.K * s.V;
+        const size_t sb = gla::state_bytes(s, p);
         const size_t kk = (size_t)p.BH * p.P * s.K;
-        float* ws = static_cast<float*>(workspace);
+        char* ws = static_cast<char*>(workspace);
         a.ws_state = ws;
-        a.ws_dstate = ws + kv;
-        a.ws_gate = ws + 2 * kv;
-        a.ws_hs = ws + 2 * kv + ((kk + 63) / 64) * 64;
+        a.ws_dstate = ws + sb;
+        a.ws_gate = reinterpret_cast<float*>(ws + 2 * sb);
+        a.ws_hs = ws + 2 * sb + gla::round256(kk * sizeof(float));
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
@@ -217,9 +217,8 @@ namespace {
 size_t bwd_workspace_bytes(const gla::Shape& s) {
     gla::Plan p = gla::make_bwd_plan(s);
     if (p.BH == 0) return 0;
-    const size_t kv = (size_t)p.BH * p.P * s.K * s.V;
     const size_t kk = (size_t)p.BH * p.P * s.K;
     const size_t hs = (size_t)p.BH * p.N * s.K * s.V * (s.bf16 ? 2 : 4);
-    return (2 * kv + ((kk + 63) / 64) * 64) * sizeof(float) + hs;
+    return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + hs;
 }
 }  // namespace

@@ -62,12 +62,21 @@ struct TStateRegs {
 #pragma unroll
         for (int jb = 0; jb < VW / 16; ++jb) s[jb] = zero4();
     }
-    // src points at element (0, 0) of a [K][ld] fp32 state block
+    // src points at element (0, 0) of a [K][ld] state block (fp32, or the input dtype)
     __device__ __forceinline__ void load(const float* __restrict__ src, int ld, int i0, int j0) {
         const int l = lane_id();
         const float* p = src + (long)(i0 + (l & 15)) * ld + j0 + 4 * (l >> 4);
 #pragma unroll
         for (int jb = 0; jb < VW / 16; ++jb) s[jb] = *reinterpret_cast<const f32x4*>(p + 16 * jb);
+    }
+    __device__ __forceinline__ void load(const bf16* __restrict__ src, int ld, int i0, int j0) {
+        const int l = lane_id();
+        const bf16* p = src + (long)(i0 + (l & 15)) * ld + j0 + 4 * (l >> 4);
+#pragma unroll
+        for (int jb = 0; jb < VW / 16; ++jb) {
+            const bf16x4 x = *reinterpret_cast<const bf16x4*>(p + 16 * jb);
+            s[jb] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        }
     }
 };
 
@@ -126,24 +135,25 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
 }
 
 // ---------------------------------------------------------------------------
-// Backward combine, one thread per state element; blockIdx.z = 0 combines the
-// states, 1 the state gradients:
+// Backward combine, one thread per kCombineVec adjacent elements of a state
+// row; blockIdx.z = 0 combines the states, 1 the state gradients:
 //   S_init(0) = S_0;  S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p
 //   dS_end(P-1) = dht; dS_end(p-1) = Diag(exp2 G_p) dS_end(p) + dS*_p
 // ws_state / ws_dstate hold S*_p / dS*_p on entry and S_init / dS_end on exit.
+template <typename ST>
 __global__ void __launch_bounds__(256)
-gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht, float* __restrict__ ws_state,
-                    float* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
+gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
+                    ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
     const long KV = (long)K * V;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long e = ((long)blockIdx.x * 256 + threadIdx.x) * kCombineVec;
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
     const float* gt = ws_gate + bh * P * (long)K + i;
     if (blockIdx.z == 0)
-        combine_element<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0[bh * KV + e] : 0.f);
+        combine_row<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr);
     else
-        combine_element<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht[bh * KV + e] : 0.f);
+        combine_row<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,7 +424,7 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
-                const float* __restrict__ s_init, long s_seg_stride, long s_bh_stride, T* __restrict__ dq,
+                const T* __restrict__ ws_init, const float* __restrict__ s0, T* __restrict__ dq,
                 T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
@@ -442,8 +452,10 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         if ((s >> 4) > (t >> 4)) sm.P[t * Sm::pP + s] = Elem<T>::from_f(0.f);
     }
     if (tid < 2) sm.buf[tid].flag[0] = 0;
+    // segment 0 starts from the caller's fp32 S_0, later ones from the combined states
     TStateRegs<VW> S;
-    if (s_init) S.load(s_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, V, i0, j0);
+    if (seg > 0) S.load(ws_init + ((long)bh * P + seg) * (long)K * V + (long)k0 * V, V, i0, j0);
+    else if (s0) S.load(s0 + (long)bh * K * V + (long)k0 * V, V, i0, j0);
     else S.zero();
 
     RowSlab<T, CPK> rk, rg;
@@ -604,9 +616,9 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
-                const T* __restrict__ d_o, const T* __restrict__ dq, const float* __restrict__ ds_init,
-                long s_seg_stride, long s_bh_stride, const T* __restrict__ hs, T* __restrict__ dk,
-                T* __restrict__ dg, int T_, int H, int K, int N, int P, int seg_len, int BH) {
+                const T* __restrict__ d_o, const T* __restrict__ dq, const T* __restrict__ ws_dinit,
+                const float* __restrict__ dht, const T* __restrict__ hs, T* __restrict__ dk, T* __restrict__ dg,
+                int T_, int H, int K, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
@@ -636,8 +648,10 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         if ((t >> 4) < (s >> 4)) sm.P[s * Sm::pP + t] = Elem<T>::from_f(0.f);
     }
     if (tid < 2) sm.buf[tid].flag[0] = 0;
+    // the last segment starts from the caller's fp32 dht, earlier ones from the combined gradients
     TStateRegs<VW> S;  // dS^T
-    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride + (long)k0 * V, V, i0, j0);
+    if (seg < P - 1) S.load(ws_dinit + ((long)bh * P + seg) * (long)K * V + (long)k0 * V, V, i0, j0);
+    else if (dht) S.load(dht + (long)bh * K * V + (long)k0 * V, V, i0, j0);
     else S.zero();
 
     RowSlab<T, CPK> rq, rg;
@@ -1270,7 +1284,7 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
-                const T* __restrict__ d_o, const float* __restrict__ ds_init, long s_seg_stride, long s_bh_stride,
+                const T* __restrict__ d_o, const T* __restrict__ ws_dinit, const float* __restrict__ dht,
                 T* __restrict__ dv, float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, true>;  // sm.A holds A^T [s][t]; sm.Vw the d_o slices
@@ -1301,8 +1315,11 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     }
     if (tid < 2) sm.buf[tid].flag[0] = 0;
 
+    // the last segment starts from the caller's fp32 dht, earlier ones from the
+    // combined segment gradients ([BH][P][K][V], input dtype)
     StateRegs<KD, CB> S;  // dS
-    if (ds_init) S.load(ds_init + (long)bh * s_bh_stride + (long)seg * s_seg_stride, V, col0);
+    if (seg < P - 1) S.load(ws_dinit + ((long)bh * P + seg) * KD * V, V, col0);
+    else if (dht) S.load(dht + (long)bh * KD * V, V, col0);
     else S.zero();
 
     RowSlab<T, CPK> rq, rk, rg;
@@ -1513,11 +1530,11 @@ static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
         const long nfwd = xcd_grid(nseg * a.BH, nvb);
         dim3 grid2((unsigned)(2 * nfwd));
         GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW>), grid2, dim3(NT), a.stream, (const T*)a.k,
-                           (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, a.ws_state, a.ws_dstate,
-                           a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd);
-        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd, dim3((unsigned)((KV + 255) / 256), (unsigned)a.BH, 2u),
-                           dim3(256), a.stream, a.s0,
-                           a.dht, a.ws_state, a.ws_dstate, a.ws_gate, KD, a.V, a.P);
+                           (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, (T*)a.ws_state,
+                           (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd);
+        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>, dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, 2u),
+                           dim3(256), a.stream, a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V,
+                           a.P);
     }
     return hipGetLastError();
 }
@@ -1528,16 +1545,16 @@ static hipError_t launch_dv(const BwdLaunch& a) {
     constexpr int NT = NW * 64;
     const int nvb = a.V / BV;
     const long KV = (long)KD * a.V;
-    const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
-    const long seg_stride = a.P > 1 ? KV : 0;
-    const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, true>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
-                           (const T*)a.k, (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv,
+                           (const T*)a.k, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_dstate, a.dht, (T*)a.dv,
                            a.ds0, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
+        const float* dinit = a.P > 1 ? (const float*)a.ws_dstate : a.dht;
+        const long seg_stride = a.P > 1 ? KV : 0;
+        const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
         GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.g, (const T*)a.d_o, dinit, seg_stride, bh_stride, (T*)a.dv,
                            a.ds0, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
@@ -1558,14 +1575,14 @@ static hipError_t launch_rows(const BwdLaunch& a) {
     const int nkb = a.K / BK;
     const long KV = (long)a.K * V;
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nkb));
-    const float* sinit = a.P > 1 ? a.ws_state : a.s0;
-    const float* dinit = a.P > 1 ? a.ws_dstate : a.dht;
+    const float* sinit = a.P > 1 ? (const float*)a.ws_state : a.s0;
+    const float* dinit = a.P > 1 ? (const float*)a.ws_dstate : a.dht;
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
-                           (const T*)a.v, (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq,
+                           (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0, (T*)a.dq,
                            (T*)a.ws_hs, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
         GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
@@ -1574,9 +1591,9 @@ static hipError_t launch_rows(const BwdLaunch& a) {
     }
     if constexpr (sizeof(T) == 2) {
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
-                           (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit,
-                           seg_stride, bh_stride, (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P,
-                           a.seg_len, (int)a.BH);
+                           (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq,
+                           (const T*)a.ws_dstate, a.dht, (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N,
+                           a.P, a.seg_len, (int)a.BH);
     } else {
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit,

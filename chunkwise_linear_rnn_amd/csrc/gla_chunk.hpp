@@ -40,7 +40,9 @@ struct StateRegs {
             for (int c = 0; c < CB; ++c) s[a][c] = zero4();
     }
     // element (i, j) of tile (a, c) for accumulator slot r: i = 16a + 4*(l/16) + r, j = col0 + 16c + l%16
-    __device__ __forceinline__ void load(const float* __restrict__ src, long ld, int col0) {
+    // (U: fp32 caller states or the workspace's segment states in the input dtype)
+    template <typename U>
+    __device__ __forceinline__ void load(const U* __restrict__ src, long ld, int col0) {
         const int l = lane_id();
 #pragma unroll
         for (int a = 0; a < KD / 16; ++a)
@@ -48,9 +50,10 @@ struct StateRegs {
             for (int c = 0; c < CB; ++c)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    s[a][c][r] = src[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)];
+                    s[a][c][r] = Elem<U>::to_f(src[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)]);
     }
-    __device__ __forceinline__ void store(float* __restrict__ dst, long ld, int col0) const {
+    template <typename U>
+    __device__ __forceinline__ void store(U* __restrict__ dst, long ld, int col0) const {
         const int l = lane_id();
 #pragma unroll
         for (int a = 0; a < KD / 16; ++a)
@@ -58,7 +61,7 @@ struct StateRegs {
             for (int c = 0; c < CB; ++c)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    dst[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)] = s[a][c][r];
+                    dst[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)] = Elem<U>::from_f(s[a][c][r]);
     }
 };
 
@@ -197,31 +200,54 @@ __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSl
 }
 
 // ---------------------------------------------------------------------------
-// Step 2: the linear recurrence across segments for one state element.
+// Step 2: the linear recurrence across segments for CE adjacent elements of
+// one state row.
 //   forwards  (REV = false): out[0] = init, out[p+1] = exp2(G_p) out[p] + in[p]
 //   backwards (REV = true):  out[P-1] = init, out[p-1] = exp2(G_p) out[p] + in[p]
-// `st` holds in[] on entry and out[] on exit (stride KV), `gt` the segment gate
-// totals G_p in log2 units (stride K).  The loads of up to U segments are
-// issued before any of their results is needed, so one thread keeps them all
-// in flight rather than one request per step.
-template <bool REV>
-__device__ __forceinline__ void combine_element(float* st, const float* gt, long KV, long K, int P, float cur) {
-    constexpr int U = 8;
-    for (int b0 = 0; b0 < P; b0 += U) {
-        float a[U], gm[U];
+// `st` holds in[] on entry and out[] on exit (stride KV, input dtype or fp32),
+// `gt` the row's segment gate totals G_p in log2 units (stride K), `init` the
+// CE fp32 starting values (null: zero).  The loads of up to CU segments are
+// issued before any of their results is needed, and each is CE elements wide,
+// so a thread keeps CU * CE * sizeof(ST) bytes in flight.  The running value
+// stays fp32; only the stored states are rounded.
+constexpr int kCombineVec = 4;  // elements per thread
+template <typename ST> using combine_vec_t = ST __attribute__((ext_vector_type(kCombineVec)));
+
+template <bool REV, typename ST>
+__device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, long K, int P, const float* init) {
+    constexpr int CE = kCombineVec;
+    constexpr int CU = 32;
+    using VT = combine_vec_t<ST>;
+    f32x4 cur = init ? *reinterpret_cast<const f32x4*>(init) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < P; b0 += CU) {
+        VT a[CU];
+        float gm[CU];
+        // unconditional loads from a clamped (always valid) segment, then a
+        // select: a conditional load becomes a branch with its own wait
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = REV ? P - 1 - (b0 + u) : b0 + u;
-            const bool feeds = b0 + u < P && (REV ? p >= 1 : p + 1 < P);
-            a[u] = feeds ? st[p * KV] : 0.f;
-            gm[u] = feeds ? exp2_fast(gt[p * K]) : 0.f;
+        for (int u = 0; u < CU; ++u) {
+            const int j = b0 + u < P ? b0 + u : P - 1;
+            const int p = REV ? P - 1 - j : j;
+            a[u] = *reinterpret_cast<const VT*>(st + p * KV);
+            gm[u] = gt[p * K];
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < CU; ++u) {
+            const int p = REV ? P - 1 - (b0 + u) : b0 + u;
+            const bool feeds = b0 + u < P && (REV ? p >= 1 : p + 1 < P);
+            gm[u] = feeds ? exp2_fast(gm[u]) : 0.f;
+            if (!feeds) a[u] = VT{};
+        }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
             const int p = REV ? P - 1 - (b0 + u) : b0 + u;
             if (b0 + u < P) {
-                st[p * KV] = cur;
-                cur = gm[u] * cur + a[u];
+                VT o;
+#pragma unroll
+                for (int c = 0; c < CE; ++c) o[c] = Elem<ST>::from_f(cur[c]);
+                *reinterpret_cast<VT*>(st + p * KV) = o;
+#pragma unroll
+                for (int c = 0; c < CE; ++c) cur[c] = gm[u] * cur[c] + Elem<ST>::to_f(a[u][c]);
             }
         }
     }
@@ -260,7 +286,7 @@ struct SegSmem {
 template <typename T, int KD, int BV, int NW, bool REV>
 __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int bid, const T* __restrict__ x,
                                                const T* __restrict__ g, const T* __restrict__ y,
-                                               float* __restrict__ ws_state, float* __restrict__ ws_gate, int T_,
+                                               T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_,
                                                int H, int V, int N, int P, int seg_len, int seg_first, int nseg,
                                                int BH, int gate_first) {
     using Sm = SegSmem<T, KD, BV, NW>;
@@ -382,7 +408,7 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
 template <typename T, int KD, int BV, int NW, bool REV>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
-              float* __restrict__ ws_state, float* __restrict__ ws_gate,
+              T* __restrict__ ws_state, float* __restrict__ ws_gate,
               int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg, int BH) {
     __shared__ SegSmem<T, KD, BV, NW> sm;
     seg_state_body<T, KD, BV, NW, REV>(sm, blockIdx.x, x, g, y, ws_state, ws_gate, T_, H, V, N, P, seg_len,
@@ -396,8 +422,8 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ q,
-                   const T* __restrict__ d_o, const T* __restrict__ g, float* __restrict__ ws_state,
-                   float* __restrict__ ws_dstate, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
+                   const T* __restrict__ d_o, const T* __restrict__ g, T* __restrict__ ws_state,
+                   T* __restrict__ ws_dstate, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
                    int seg_len, int nseg, int BH, int nfwd) {
     __shared__ SegSmem<T, KD, BV, NW> sm;
     const int bid = blockIdx.x;

@@ -25,17 +25,19 @@ namespace gla {
 
 // ---------------------------------------------------------------------------
 // Step 2 (forward): S_init(0) = S_0 (or 0); S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p.
-// ws_state[p] holds S*_p on entry and S_init(p) on exit.  One thread per state element.
+// ws_state[p] holds S*_p on entry and S_init(p) on exit.  One thread per
+// kCombineVec adjacent elements of a state row (V is a multiple of 64).
+template <typename ST>
 __global__ void __launch_bounds__(256)
-gla_seg_combine_fwd(const float* __restrict__ s0, float* __restrict__ ws_state, const float* __restrict__ ws_gate,
+gla_seg_combine_fwd(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
                     int K, int V, int P) {
     const long KV = (long)K * V;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long e = ((long)blockIdx.x * 256 + threadIdx.x) * kCombineVec;
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
-    combine_element<false>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
-                           s0 ? s0[bh * KV + e] : 0.f);
+    combine_row<false>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                       s0 ? s0 + bh * KV + e : nullptr);
 }
 
 // Copy (or zero) a [BH][K][V] fp32 state: final state of an empty sequence.
@@ -328,9 +330,9 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                  const T* __restrict__ g, const float* __restrict__ s_init, long s_init_seg_stride,
-                  long s_init_bh_stride, T* __restrict__ o, float* __restrict__ s_final, int T_, int H, int V, int N,
-                  int P, int seg_len, int BH) {
+                  const T* __restrict__ g, const T* __restrict__ ws_init, const float* __restrict__ s0,
+                  T* __restrict__ o, float* __restrict__ s_final, int T_, int H, int V, int N, int P, int seg_len,
+                  int BH) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, false>;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
@@ -357,8 +359,11 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     }
     if (tid < 2) sm.buf[tid].flag[0] = 0;
 
+    // segment 0 starts from the caller's fp32 S_0, later ones from the combined
+    // segment states ([BH][P][K][V], input dtype)
     StateRegs<KD, CB> S;
-    if (s_init) S.load(s_init + (long)bh * s_init_bh_stride + (long)seg * s_init_seg_stride, V, col0);
+    if (seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
+    else if (s0) S.load(s0 + (long)bh * KD * V, V, col0);
     else S.zero();
 
     RowSlab<T, CPK> rq, rk, rg;
@@ -575,22 +580,23 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
         const int nseg = a.P - 1;
         dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
         GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream,
-                           (const T*)a.k, (const T*)a.g, (const T*)a.v, a.ws_state, a.ws_gate,
+                           (const T*)a.k, (const T*)a.g, (const T*)a.v, (T*)a.ws_state, a.ws_gate,
                            a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg, (int)a.BH);
-        dim3 g2((unsigned)((KV + 255) / 256), (unsigned)a.BH);
-        GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd, g2, dim3(256), a.stream, a.s0, a.ws_state, a.ws_gate,
-                           KD, a.V, a.P);
+        dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
+        GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
+                           a.ws_gate, KD, a.V, a.P);
     }
-    const float* sinit = a.P > 1 ? a.ws_state : a.s0;
-    const long seg_stride = a.P > 1 ? KV : 0;
-    const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream,
-                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
                            (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
+        // fp32: the workspace states are fp32 and hold S_init(0) = S_0 after the combine
+        const float* sinit = a.P > 1 ? (const float*)a.ws_state : a.s0;
+        const long seg_stride = a.P > 1 ? KV : 0;
+        const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
         static_assert(sizeof(WalkSmem<T, KD, BV>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("fwd_walk", (gla_fwd_walk<T, KD, BV, NW>), grid, dim3(NT), a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, sinit, seg_stride, bh_stride,

@@ -16,7 +16,7 @@ struct FwdLaunch {
     const float* s0;
     void* o;
     float* s_final;
-    float* ws_state;  // [BH][P][K][V] fp32
+    void* ws_state;   // [BH][P][K][V] in the input dtype
     float* ws_gate;   // [BH][P][K]    fp32 (log2 of the segment decay)
     hipStream_t stream;
 };
@@ -30,8 +30,8 @@ struct BwdLaunch {
     const float *s0, *dht;
     void *dq, *dk, *dv, *dg;
     float* ds0;
-    float* ws_state;   // [BH][P][K][V] fp32: S*_p, then S_init(p)
-    float* ws_dstate;  // [BH][P][K][V] fp32: dS*_p, then dS_end(p)
+    void* ws_state;    // [BH][P][K][V] input dtype: S*_p, then S_init(p)
+    void* ws_dstate;   // [BH][P][K][V] input dtype: dS*_p, then dS_end(p)
     float* ws_gate;    // [BH][P][K]
     void* ws_hs;       // [BH][N][K*V] dtype: state after every chunk, in the walks' tile order
     hipStream_t stream;

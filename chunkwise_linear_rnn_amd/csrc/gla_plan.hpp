@@ -85,12 +85,18 @@ inline Plan make_bwd_plan(const Shape& s) {
     return p;
 }
 
+inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Segment states are kept in the input dtype (2 or 4 bytes per element).
+inline size_t state_bytes(const Shape& s, const Plan& p) {
+    return round256((size_t)p.BH * p.P * (size_t)s.K * (size_t)s.V * (s.bf16 ? 2 : 4));
+}
+
 inline size_t fwd_workspace_bytes(const Shape& s) {
     Plan p = make_fwd_plan(s);
     if (p.P <= 1 || p.BH == 0) return 0;
-    size_t st = (size_t)p.BH * p.P * (size_t)s.K * (size_t)s.V * sizeof(float);
     size_t gt = (size_t)p.BH * p.P * (size_t)s.K * sizeof(float);
-    return st + ((gt + 255) / 256) * 256;
+    return state_bytes(s, p) + round256(gt);
 }
 
 }  // namespace gla

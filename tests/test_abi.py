@@ -95,7 +95,7 @@ def test_workspace_sizes(L):
     a = L.gla_fwd_workspace_size(ctypes.byref(s))
     b = L.gla_fwd_workspace_size(ctypes.byref(s))
     assert a == b and a % 4 == 0
-    # per-segment fp32 states dominate: at least one [K, V] state per head when segmented
+    # per-segment states dominate: at least one [K, V] state per head when segmented
     assert a == 0 or a >= 2 * 4 * 128 * 256 * 4
     bw = L.gla_bwd_workspace_size(ctypes.byref(s))
     assert bw >= 2 * 2 * 4 * 128 * 256 * 4
