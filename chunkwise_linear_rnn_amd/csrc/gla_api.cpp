@@ -204,6 +204,7 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.ws_dstate = ws + sb;
         a.ws_gate = reinterpret_cast<float*>(ws + 2 * sb);
         a.ws_hs = ws + 2 * sb + gla::round256(kk * sizeof(float));
+        a.ws_dp = s.bf16 ? static_cast<char*>(a.ws_hs) + gla::round256(gla::hs_bytes(s, p)) : nullptr;
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
@@ -218,7 +219,8 @@ size_t bwd_workspace_bytes(const gla::Shape& s) {
     gla::Plan p = gla::make_bwd_plan(s);
     if (p.BH == 0) return 0;
     const size_t kk = (size_t)p.BH * p.P * s.K;
-    const size_t hs = (size_t)p.BH * p.N * s.K * s.V * (s.bf16 ? 2 : 4);
-    return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + hs;
+    // 16-bit inputs: the dq walk's dP tiles for the dk walk
+    const size_t dp = s.bf16 ? (size_t)p.BH * p.N * 64 * 64 * 2 : 0;
+    return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + gla::round256(gla::hs_bytes(s, p)) + dp;
 }
 }  // namespace

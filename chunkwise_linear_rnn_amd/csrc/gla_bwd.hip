@@ -419,13 +419,14 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
 // (exact-path chunks: the intra part element by element from raw k and B).
 // Phase 1: dP, the value-slice partial of dO S^T, the state update
 // S^T <- post * (pre * S^T + V^T Kt), the store of S_out to `hs`, the next
-// chunk's key-side preparation.  Phase 2: dP Kt, the slice reduction, the
-// factor exp2(B_t) and the store of dq; the next chunk's V and d_o tiles.
+// chunk's key-side preparation.  Phase 2: dP to `dp_out` for the dk walk (first
+// key block only), dP Kt, the slice reduction, the factor exp2(B_t) and the
+// store of dq; the next chunk's V and d_o tiles.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
                 const T* __restrict__ ws_init, const float* __restrict__ s0, T* __restrict__ dq,
-                T* __restrict__ hs, int T_, int H, int K, int N, int P, int seg_len, int BH) {
+                T* __restrict__ hs, T* __restrict__ dp_out, int T_, int H, int K, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
@@ -532,6 +533,16 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         }
         __syncthreads();
         // ---- phase 2
+        // the first key block hands the chunk's dP ([t][s], zero above the
+        // diagonal blocks) to the dk walk, which then need not form it again
+        if (kb == 0) {
+            T* dst = dp_out + ((long)bh * N + c) * (kChunk * kChunk);
+            for (int e = tid; e < kChunk * kChunk / 8; e += NT) {
+                const int row = e >> 3, col = (e & 7) * 8;
+                *reinterpret_cast<u32x4*>(dst + row * kChunk + col) =
+                    *reinterpret_cast<const u32x4*>(sm.P + row * Sm::pP + col);
+            }
+        }
         if (!exact) {
             if (vs == 0) {
                 // dq^T[i][t] += sum_s Kt[s][i] dP[t][s]
@@ -608,17 +619,19 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 //        = Gamma_s * [V dS^T]_s + sum_{t>=s} dP_ts q_t exp2(B_t - B_s)  (exact path)
 //   dA   = q*dq - k*dk (fp32 dk),  dg_t = sum_{r>=t in chunk} dA_r + rowsum(S_out * dS)
 //   dS_in = Diag(gamma) dS + Ql^T dO
-// Phase 1: dP^T, the value-slice partials of V dS^T and of the dg anchor (S_out
-// read back from `hs`), the dS update, the previous chunk's query-side
-// preparation.  Phase 2: dP^T Ql, the slice reduction and the factors, dk, dA
-// and its reverse cumulative sum down the 16-lane rows (DPP) and across the
-// four token blocks, dg; the next value and d_o tiles.
+// dP = dO V^T of the chunk is the dq walk's (`dp_in`, [t][s] per chunk), read
+// with transposed fragments.  Phase 1: the value-slice partials of V dS^T and
+// of the dg anchor (S_out read back from `hs`), the dS update, dP to LDS, the
+// previous chunk's query-side preparation.  Phase 2: dP^T Ql, the slice
+// reduction and the factors, dk, dA and its reverse cumulative sum down the
+// 16-lane rows (DPP) and across the four token blocks, dg; the next value and
+// d_o tiles.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
                 const T* __restrict__ d_o, const T* __restrict__ dq, const T* __restrict__ ws_dinit,
-                const float* __restrict__ dht, const T* __restrict__ hs, T* __restrict__ dk, T* __restrict__ dg,
-                int T_, int H, int K, int N, int P, int seg_len, int BH) {
+                const float* __restrict__ dht, const T* __restrict__ hs, const T* __restrict__ dp_in,
+                T* __restrict__ dk, T* __restrict__ dg, int T_, int H, int K, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
@@ -642,11 +655,6 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     const int rsK = H * K, rsV = H * V;
     auto chunk_of = [&](int it) { return c_end - 1 - it; };
 
-    // dP^T is stored [s][t]; its tiles with t-block < s-block are zero
-    for (int e = tid; e < kChunk * kChunk; e += NT) {
-        const int s = e / kChunk, t = e % kChunk;
-        if ((t >> 4) < (s >> 4)) sm.P[s * Sm::pP + t] = Elem<T>::from_f(0.f);
-    }
     if (tid < 2) sm.buf[tid].flag[0] = 0;
     // the last segment starts from the caller's fp32 dht, earlier ones from the combined gradients
     TStateRegs<VW> S;  // dS^T
@@ -657,6 +665,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     RowSlab<T, CPK> rq, rg;
     using TRV = TileRegs<T, V, NT>;
     TRV rv, rdo;
+    TileRegs<T, kChunk, NT> rp;  // the chunk's dP [t][s] from the dq walk
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
     auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
     if (nchunks > 0) {
@@ -685,9 +694,10 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         const bool more = it + 1 < nchunks;
         const bool exact = cur.flag[0] != 0;
         // ---- phase 1
-        // loads for later in this chunk: S_out tiles (dg anchor); q, dq, k in the
-        // accumulator layout (slot r of token block sb: token 16sb + l%16, key
-        // column i0 + 4(l/16) + r) for dA
+        // loads for later in this chunk: dP (to LDS before the barrier), S_out
+        // tiles (dg anchor); q, dq, k in the accumulator layout (slot r of token
+        // block sb: token 16sb + l%16, key column i0 + 4(l/16) + r) for dA
+        rp.load(dp_in + ((long)bh * N + c) * (kChunk * kChunk), kChunk, tid);
         vec4_t<T> so[VW / 16];
         {
             const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
@@ -705,7 +715,6 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 ak[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(k, c) + off + 16 * sb * rsK);
             }
         }
-        dp_tiles<T, V, true>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         const float gl = cur.pre[i0 + (l & 15)];  // gamma of this lane's key column
         // dk^T[i][s] partial = sum_{j in slice} (gamma dS)[i][j] V[s][j] (exact path: dS unscaled)
         f32x4 acc[4];
@@ -749,6 +758,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.dO, Sm::pV, 32 * ks, j0 + 16 * jb),
                                 frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
         }
+        rp.store_lds(sm.P, Sm::pP, tid);
         if (more) {
             row_prep<T, CPK, true>(nxt, Sm::pK, Sm::pB, rq, rg, kc0);
             if (it + 2 < nchunks) {
@@ -770,7 +780,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 sum[j] = 0.f;
             }
             for (int t = 0; t < kChunk; ++t) {
-                const float dp = Elem<T>::to_f(sm.P[l * Sm::pP + t]);
+                const float dp = Elem<T>::to_f(sm.P[t * Sm::pP + l]);
 #pragma unroll
                 for (int j = 0; j < CPK; ++j) {
                     // t < s: dP^T is zero there and exp2 may overflow, so the term is selected away
@@ -784,15 +794,15 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
         if (vs == 0) {
             if (!exact) {
-                // dk^T[i][s] += sum_t Ql[t][i] dP^T[s][t], t-blocks >= sb
+                // dk^T[i][s] += sum_t Ql[t][i] dP[t][s], t-blocks >= sb
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
                     for (int ks2 = sb / 2; ks2 < 2; ++ks2)
                         acc[sb] = mma32(acc[sb], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
                                         frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
-                                        frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2),
-                                        frag_rm<T>(sm.P, Sm::pP, 16 * sb, 32 * ks2 + 16));
+                                        frag_cm<T>(sm.P, Sm::pP, 32 * ks2, 16 * sb),
+                                        frag_cm<T>(sm.P, Sm::pP, 32 * ks2 + 16, 16 * sb));
             }
             const int ic = i0 + 4 * (l >> 4);
             const f32x4 blast = *reinterpret_cast<const f32x4*>(cur.B + 63 * Sm::pB + ic);
@@ -1583,7 +1593,7 @@ static hipError_t launch_rows(const BwdLaunch& a) {
         static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
         GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0, (T*)a.dq,
-                           (T*)a.ws_hs, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+                           (T*)a.ws_hs, (T*)a.ws_dp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
         GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq,
@@ -1592,8 +1602,8 @@ static hipError_t launch_rows(const BwdLaunch& a) {
     if constexpr (sizeof(T) == 2) {
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq,
-                           (const T*)a.ws_dstate, a.dht, (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N,
-                           a.P, a.seg_len, (int)a.BH);
+                           (const T*)a.ws_dstate, a.dht, (const T*)a.ws_hs, (const T*)a.ws_dp, (T*)a.dk, (T*)a.dg,
+                           a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit,

@@ -34,6 +34,7 @@ struct BwdLaunch {
     void* ws_dstate;   // [BH][P][K][V] input dtype: dS*_p, then dS_end(p)
     float* ws_gate;    // [BH][P][K]
     void* ws_hs;       // [BH][N][K*V] dtype: state after every chunk, in the walks' tile order
+    void* ws_dp;       // [BH][N][64][64] dtype (16-bit inputs): each chunk's dP = dO V^T, [t][s]
     hipStream_t stream;
 };
 

@@ -92,6 +92,11 @@ inline size_t state_bytes(const Shape& s, const Plan& p) {
     return round256((size_t)p.BH * p.P * (size_t)s.K * (size_t)s.V * (s.bf16 ? 2 : 4));
 }
 
+// the backward's chunk-end states for the gate-gradient anchors
+inline size_t hs_bytes(const Shape& s, const Plan& p) {
+    return (size_t)p.BH * p.N * (size_t)s.K * (size_t)s.V * (s.bf16 ? 2 : 4);
+}
+
 inline size_t fwd_workspace_bytes(const Shape& s) {
     Plan p = make_fwd_plan(s);
     if (p.P <= 1 || p.BH == 0) return 0;
