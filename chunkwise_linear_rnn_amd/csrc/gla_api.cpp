@@ -187,6 +187,7 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.K = (int)s.K;
         a.V = (int)s.V;
         a.BV = p.BV;
+        a.BVS = gla::plan_bv(s);
         a.BK = p.BK;
         a.T = (int)s.T;
         a.H = (int)s.H;

@@ -1527,8 +1527,11 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 
 // ---------------------------------------------------------------------------
 // Host launchers.
+// Segment states of both directions and their combine.  The workgroups span
+// the forward's value width (BV = a.BVS), so the key-side preparation and its
+// loads are not repeated across value blocks.
 template <typename T, int KD, int BV>
-static hipError_t launch_seg_and_dv(const BwdLaunch& a) {
+static hipError_t launch_seg_states(const BwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
@@ -1614,7 +1617,7 @@ static hipError_t launch_rows(const BwdLaunch& a) {
 }
 
 #define GLA_COL_DISPATCH(FN, T, KD_, BV_)                              \
-    if (a.K == KD_ && a.BV == BV_) {                                   \
+    if (a.K == KD_ && (dv_stage ? a.BV : a.BVS) == BV_) {              \
         hipError_t e = FN<T, KD_, BV_>(a);                             \
         return e;                                                      \
     }
@@ -1624,20 +1627,20 @@ static hipError_t col_stage(const BwdLaunch& a, bool dv_stage) {
     if (!dv_stage) {
         if (a.bf16) {
             if constexpr (sizeof(T) == 2) {
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 64)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 128)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 256)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 64)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 128)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 256)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 256, 64)
+                GLA_COL_DISPATCH(launch_seg_states, T, 64, 64)
+                GLA_COL_DISPATCH(launch_seg_states, T, 64, 128)
+                GLA_COL_DISPATCH(launch_seg_states, T, 64, 256)
+                GLA_COL_DISPATCH(launch_seg_states, T, 128, 64)
+                GLA_COL_DISPATCH(launch_seg_states, T, 128, 128)
+                GLA_COL_DISPATCH(launch_seg_states, T, 128, 256)
+                GLA_COL_DISPATCH(launch_seg_states, T, 256, 64)
             }
         } else {
             if constexpr (sizeof(T) == 4) {
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 64)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 64, 128)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 64)
-                GLA_COL_DISPATCH(launch_seg_and_dv, T, 128, 128)
+                GLA_COL_DISPATCH(launch_seg_states, T, 64, 64)
+                GLA_COL_DISPATCH(launch_seg_states, T, 64, 128)
+                GLA_COL_DISPATCH(launch_seg_states, T, 128, 64)
+                GLA_COL_DISPATCH(launch_seg_states, T, 128, 128)
             }
         }
     } else {

@@ -24,6 +24,7 @@ struct FwdLaunch {
 struct BwdLaunch {
     bool bf16;
     int K, V, BV, BK;
+    int BVS;  // value columns per workgroup of the segment-state pass (the forward's)
     int T, H, N, P, seg_len;
     long BH;
     const void *q, *k, *v, *g, *d_o;
