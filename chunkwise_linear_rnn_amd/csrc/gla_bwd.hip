@@ -31,6 +31,14 @@
 
 namespace gla {
 
+// The 16-bit walks anchor the gate gradient at every kAnchorStride-th chunk
+// end, counted back from each segment's end: the dq walk stores those chunks'
+// S_out, and the dk walk carries the offset rowsum(S_out * dS_out) across the
+// chunks in between by adding their dA totals.  Each carry spans one chunk
+// (64 tokens) of bf16-operand rounding; longer carries let that rounding grow
+// with the length summed over.
+constexpr int kAnchorStride = 2;
+
 // ---------------------------------------------------------------------------
 // LDS of the row-split kernels: a BK-column slice of the key-side tiles and
 // full-width value / d_o tiles.
@@ -418,10 +426,10 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
 //   dq_t = exp2(B_t) * [dO S_in^T + dP Kt]_t,   Kt = k * exp2(-B_s)
 // (exact-path chunks: the intra part element by element from raw k and B).
 // Phase 1: dP, the value-slice partial of dO S^T, the state update
-// S^T <- post * (pre * S^T + V^T Kt), the store of S_out to `hs`, the next
-// chunk's key-side preparation.  Phase 2: dP to `dp_out` for the dk walk (first
-// key block only), dP Kt, the slice reduction, the factor exp2(B_t) and the
-// store of dq; the next chunk's V and d_o tiles.
+// S^T <- post * (pre * S^T + V^T Kt), the store of S_out to `hs` (anchor chunks
+// only), the next chunk's key-side preparation.  Phase 2: dP to `dp_out` for
+// the dk walk (first key block only), dP Kt, the slice reduction, the factor
+// exp2(B_t) and the store of dq; the next chunk's V and d_o tiles.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
@@ -519,6 +527,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 #pragma unroll
             for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= post;
             T* dst = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
+            if ((c_end - 1 - c) % kAnchorStride == 0)
 #pragma unroll
             for (int jb = 0; jb < VW / 16; ++jb)
                 *reinterpret_cast<vec4_t<T>*>(dst + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4) =
@@ -617,15 +626,16 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 // Ql = q * exp2(B_t) and Gamma_s = exp2(B_63 - B_s):
 //   dk_s = exp2(-B_s) * [V (gamma dS)^T + dP^T Ql]_s            (in range)
 //        = Gamma_s * [V dS^T]_s + sum_{t>=s} dP_ts q_t exp2(B_t - B_s)  (exact path)
-//   dA   = q*dq - k*dk (fp32 dk),  dg_t = sum_{r>=t in chunk} dA_r + rowsum(S_out * dS)
+//   dA   = q*dq - k*dk (fp32 dk),  dg_t = sum_{r>=t in chunk} dA_r + off,
+//   off  = rowsum(S_out * dS) on anchor chunks, else the later chunk's off plus its dA total
 //   dS_in = Diag(gamma) dS + Ql^T dO
 // dP = dO V^T of the chunk is the dq walk's (`dp_in`, [t][s] per chunk), read
 // with transposed fragments.  Phase 1: the value-slice partials of V dS^T and
-// of the dg anchor (S_out read back from `hs`), the dS update, dP to LDS, the
-// previous chunk's query-side preparation.  Phase 2: dP^T Ql, the slice
-// reduction and the factors, dk, dA and its reverse cumulative sum down the
-// 16-lane rows (DPP) and across the four token blocks, dg; the next value and
-// d_o tiles.
+// (anchor chunks) of the dg anchor (S_out read back from `hs`), the dS update,
+// dP to LDS, the previous chunk's query-side preparation.  Phase 2: dP^T Ql,
+// the slice reduction and the factors, dk, dA and its reverse cumulative sum
+// down the 16-lane rows (DPP) and across the four token blocks, dg; the next
+// value and d_o tiles.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
@@ -687,8 +697,10 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
     }
     __syncthreads();
+    f32x4 run_carry = zero4();
     for (int it = 0; it < nchunks; ++it) {
         const int c = chunk_of(it);
+        const bool anc = it % kAnchorStride == 0;
         auto& cur = sm.buf[it & 1];
         auto& nxt = sm.buf[(it + 1) & 1];
         const bool more = it + 1 < nchunks;
@@ -699,7 +711,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         // block sb: token 16sb + l%16, key column i0 + 4(l/16) + r) for dA
         rp.load(dp_in + ((long)bh * N + c) * (kChunk * kChunk), kChunk, tid);
         vec4_t<T> so[VW / 16];
-        {
+        if (anc) {
             const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
 #pragma unroll
             for (int jb = 0; jb < VW / 16; ++jb)
@@ -733,7 +745,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             }
         }
         // anchor partial: sum_{j in slice} S_out[i][j] dS[i][j]
-        {
+        if (anc) {
             float part = 0.f;
 #pragma unroll
             for (int jb = 0; jb < VW / 16; ++jb)
@@ -843,9 +855,10 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                     da[sb][r] = x;
                 }
             }
-            f32x4 run;
+            f32x4 run = run_carry;
+            if (anc)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) run[r] = sm.carry[ic + r] + (RR::VS > 1 ? sm.carry[BK + ic + r] : 0.f);
+                for (int r = 0; r < 4; ++r) run[r] = sm.carry[ic + r] + (RR::VS > 1 ? sm.carry[BK + ic + r] : 0.f);
             T* dgbase = const_cast<T*>(kbase(dg, c));
 #pragma unroll
             for (int sb = 3; sb >= 0; --sb) {
@@ -859,6 +872,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 *reinterpret_cast<vec4_t<T>*>(dgbase + s * rsK + ic) = to_vec4<T>(out);
                 run += tot;
             }
+            run_carry = run;
         }
         if (exact) __syncthreads();
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
