@@ -1,6 +1,7 @@
 """Throughput benchmark of the GLA forward + backward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload metric_8k]
+    python bench.py --decode            (the recurrent decode step, its own JSON line)
 
 A step is one gla_fwd followed by one gla_bwd (all hot-path steps: chunk
 cumsum, intra-chunk attention, state scan, output, state recompute, dS scan,
@@ -140,6 +141,58 @@ def cpu_baseline(inputs, w, n_heads):
     }
 
 
+def decode_bench(args, torch, gla, gi):
+    """gla_decode at serving shape: B sequences, one new token each per call.
+
+    The state round-trips through HBM every call (fp32 read and write), so the
+    kernel is HBM-bound: algorithmic bytes per call = B*H*(8*K*V + e*(3K + 2V))."""
+    B, H, K, V = 64, 4, 128, 256
+    w = gi.custom(B, H, 1, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=False, seed=6)
+    cpu = gi.make_inputs(w)
+    dev = "cuda:0"
+    d = {k: (v.to(dev) if v is not None else None) for k, v in cpu.items()}
+    state = d["s0"].clone()
+    o = torch.empty(B, 1, H, V, dtype=torch.bfloat16, device=dev)
+    call = lambda: gla.gla_decode_into(d["q"], d["k"], d["v"], d["g"], state, o)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    gla.gla_kernel_timing(True)
+    gla.gla_kernel_timing_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(args.steps, 1) * 10
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    kt = gla.gla_kernel_timing_read()
+    gla.gla_kernel_timing(False)
+    kern_ms = kt["decode"][1] / kt["decode"][0]
+    alg = B * H * (8 * K * V + 2 * (3 * K + 2 * V))
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    line = {"metric": "GLA decode tokens/sec (recurrent form, one token per sequence per call)",
+            "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "calls": n, "ms_per_call": ms,
+            "kernel_us": kern_ms * 1e3, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "decode: B=64 H=4 dk=128 dv=256 bf16, fp32 state, 1 token per call"},
+            "roofline": {"bound": "hbm", "kernel": "decode", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": alg}}
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 2.0:
+            oracle.gla_fwd(*(cpu[x].to(torch.float64).numpy() for x in ("q", "k", "v", "g")),
+                           cpu["s0"].to(torch.float64).numpy())
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {"value": B / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
+                                "kind": "oracle", "sample": "fp64 oracle, the full call (%d repetitions)" % reps}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +201,8 @@ def main():
     ap.add_argument("--workload", default="metric_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--decode", action="store_true",
+                    help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (to calibrate rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -172,6 +227,10 @@ def main():
 
     import chunkwise_linear_rnn_amd as gla
     import gla_inputs as gi
+
+    if args.decode:
+        decode_bench(args, torch, gla, gi)
+        return
 
     w = gi.WORKLOADS[args.workload]
     dev = "cuda:0"

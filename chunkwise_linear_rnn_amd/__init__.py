@@ -9,6 +9,7 @@ exception is raised.
 Functions mirror the ABI:
   gla_fwd(q, k, v, g, s0=None, ...)         -> (o, s_final)
   gla_bwd(q, k, v, g, d_o, s0=None, dht=None) -> (dq, dk, dv, dg, ds0)
+  gla_decode(q, k, v, g, state)              -> o   (recurrent form; state updated in place)
   gla_fwd_workspace_size / gla_bwd_workspace_size
 Layouts: q, k, g [B,T,H,K]; v, o, d_o [B,T,H,V]; states [B,H,K,V] float32.
 """
@@ -40,7 +41,7 @@ class GlaError(RuntimeError):
         self.status = status
 
 
-EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size",
+EXPORTS = ["gla_fwd", "gla_bwd", "gla_decode", "gla_fwd_workspace_size", "gla_bwd_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
            "gla_kernel_timing", "gla_kernel_timing_read"]
 
@@ -62,6 +63,8 @@ def lib():
     L.gla_fwd.restype = ctypes.c_int
     L.gla_bwd.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gla_bwd.restype = ctypes.c_int
+    L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
+    L.gla_decode.restype = ctypes.c_int
     L.gla_fwd_workspace_size.argtypes = [sh]
     L.gla_fwd_workspace_size.restype = ctypes.c_size_t
     L.gla_bwd_workspace_size.argtypes = [sh]
@@ -180,6 +183,30 @@ def gla_bwd(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
     ws = workspace(gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
     gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream)
     return dq, dk, dv, dg, ds0
+
+
+def gla_decode_into(q, k, v, g, state, o, stream=None):
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    _check(lib().gla_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(o),
+                            _stream(stream)))
+
+
+def gla_decode(q, k, v, g, state, stream=None) -> torch.Tensor:
+    """o for T tokens of the recurrent form; `state` [B,H,K,V] fp32 is updated in place.
+
+    q, k, g: [B,T,H,K]; v: [B,T,H,V].  T is any count (no chunk constraint)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(q, "q", (B, T, H, K), dt, dev)
+    if state is None:
+        raise ValueError("state is required (it is read and updated in place)")
+    _need(state, "state", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    gla_decode_into(q, k, v, g, state, o, stream)
+    return o
 
 
 def gla_kernel_timing(enable: bool) -> None:

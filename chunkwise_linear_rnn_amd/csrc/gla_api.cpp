@@ -74,6 +74,32 @@ gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out, bool backward) {
 
 size_t bwd_workspace_bytes(const gla::Shape& s);
 
+// The recurrent decode step: any T >= 0, the chunk field unused.
+gla_status_t check_decode_shape(const gla_shape_t* s, gla::Shape* out) {
+    if (!s) return fail(GLA_ERR_NULL, "shape is NULL");
+    if (s->reserved != 0) return fail(GLA_ERR_UNSUPPORTED, "shape.reserved must be 0 (got %d)", s->reserved);
+    if (s->B < 0 || s->T < 0 || s->H < 0)
+        return fail(GLA_ERR_SHAPE, "negative size: B=%lld T=%lld H=%lld", (long long)s->B, (long long)s->T,
+                    (long long)s->H);
+    if (s->dtype != GLA_DTYPE_BF16 && s->dtype != GLA_DTYPE_FP32)
+        return fail(GLA_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+    const bool k_ok = s->K == 64 || s->K == 128 || s->K == 256;
+    const bool v_ok = s->V == 64 || s->V == 128 || s->V == 256 || s->V == 512;
+    if (!k_ok || !v_ok)
+        return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for decode", (long long)s->K,
+                    (long long)s->V);
+    const int64_t lim = (int64_t)1 << 31;
+    if (s->T >= lim || s->H >= lim || s->B >= lim || s->B * s->H * (s->V / 64) >= lim)
+        return fail(GLA_ERR_SHAPE, "size too large for this library");
+    out->B = s->B;
+    out->T = s->T;
+    out->H = s->H;
+    out->K = s->K;
+    out->V = s->V;
+    out->bf16 = s->dtype == GLA_DTYPE_BF16;
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +235,34 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
+gla_status_t gla_decode(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                        float* state, void* o, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_decode_shape(shape, &s);
+    if (st != GLA_OK) return st;
+    if (s.B * s.H == 0 || s.T == 0) return GLA_OK;
+    if (!q || !k || !v || !g || !state || !o) return fail(GLA_ERR_NULL, "q, k, v, g, state and o are required");
+    const void* ptrs[] = {q, k, v, g, state, o};
+    const char* names[] = {"q", "k", "v", "g", "state", "o"};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    gla::DecodeLaunch a{};
+    a.bf16 = s.bf16;
+    a.K = (int)s.K;
+    a.V = (int)s.V;
+    a.T = (int)s.T;
+    a.H = (int)s.H;
+    a.BH = s.B * s.H;
+    a.q = q; a.k = k; a.v = v; a.g = g;
+    a.state = state;
+    a.o = o;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t err = gla::launch_decode(a);
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
 }

@@ -39,7 +39,18 @@ struct BwdLaunch {
     hipStream_t stream;
 };
 
+struct DecodeLaunch {
+    bool bf16;
+    int K, V, T, H;
+    long BH;
+    const void *q, *k, *v, *g;
+    float* state;  // [BH][K][V] fp32, read and written in place
+    void* o;
+    hipStream_t stream;
+};
+
 hipError_t launch_fwd(const FwdLaunch& a);
+hipError_t launch_decode(const DecodeLaunch& a);
 hipError_t launch_bwd(const BwdLaunch& a);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream);
 

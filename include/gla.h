@@ -122,6 +122,24 @@ gla_status_t gla_bwd(const gla_shape_t* shape,
 /* Bytes of device workspace gla_bwd needs for `shape` (0 for an invalid shape). */
 size_t gla_bwd_workspace_size(const gla_shape_t* shape);
 
+/*
+ * gla_decode -- the recurrent form of Eq. 3 (Section 3.1), for token-by-token
+ * inference with the state carried between calls: for t = 1..T,
+ *     S <- Diag(exp g_t) S + k_t^T v_t ,   o_t = q_t S ,
+ * starting from and ending in `state`.  O(K V) work per token and head, no
+ * chunking, so T need not be a multiple of 64 (shape.chunk is not used; it is
+ * meant for a few tokens per call, the state staying on chip between them).
+ *   q, k, g : [B,T,H,K] dtype;  v : [B,T,H,V] dtype
+ *   state   : [B,H,K,V] float32, read and overwritten in place (required)
+ *   o       : [B,T,H,V] dtype output
+ *   stream  : as for gla_fwd.  No workspace.
+ * Supported: K in {64, 128, 256}, V in {64, 128, 256, 512}, bf16 or fp32.
+ * T == 0 or B*H == 0 is a no-op.  Returns GLA_OK or an error code.
+ */
+gla_status_t gla_decode(const gla_shape_t* shape,
+                        const void* q, const void* k, const void* v, const void* g,
+                        float* state, void* o, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* gla_status_string(gla_status_t status);
 

@@ -99,3 +99,23 @@ def test_workspace_sizes(L):
     assert a == 0 or a >= 2 * 4 * 128 * 256 * 4
     bw = L.gla_bwd_workspace_size(ctypes.byref(s))
     assert bw >= 2 * 2 * 4 * 128 * 256 * 4
+
+
+def _dec(L, shape, q=P, k=P, v=P, g=P, state=P, o=P):
+    return L.gla_decode(ctypes.byref(shape) if shape is not None else None, q, k, v, g, state, o, None)
+
+
+def test_decode_validation_codes(L):
+    # the recurrent form takes any T (no chunk constraint) and needs the state
+    assert _dec(L, None) == ERR_NULL
+    assert _dec(L, _shape(T=0)) == OK
+    assert _dec(L, _shape(B=0, T=5)) == OK
+    assert _dec(L, _shape(T=5), state=None) == ERR_NULL
+    assert _dec(L, _shape(T=5), o=None) == ERR_NULL
+    assert _dec(L, _shape(T=-1)) == ERR_SHAPE
+    assert _dec(L, _shape(T=5, K=96)) == ERR_UNSUPPORTED
+    assert _dec(L, _shape(T=5, V=1024)) == ERR_UNSUPPORTED
+    assert _dec(L, _shape(T=5, dtype=7)) == ERR_UNSUPPORTED
+    assert _dec(L, _shape(T=5, reserved=1)) == ERR_UNSUPPORTED
+    assert _dec(L, _shape(T=5), state=ctypes.c_void_p(0x10004)) == ERR_ALIGN
+    assert b"state" in L.gla_last_error_detail()
