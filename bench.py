@@ -89,10 +89,14 @@ def plan_segments_bwd(B, H, T, K, V, bf16):
     return _segments(B * H, T // 64, max(nvb, nkb))
 
 
+# sources of the forward and backward step kernels (the recorded traffic is theirs)
+STEP_SOURCES = ["gla_bwd.hip", "gla_chunk.hpp", "gla_device.hpp", "gla_fwd.hip", "gla_launch.hpp", "gla_plan.hpp"]
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "chunkwise_linear_rnn_amd", "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in STEP_SOURCES:
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
