@@ -214,6 +214,10 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.V = (int)s.V;
         a.BV = p.BV;
         a.BVS = gla::plan_bv(s);
+        // 16-bit: the dv walk takes the forward's value width and covers each
+        // segment as two halves (same workgroup count, no repeated key-side work)
+        a.dv_split = gla::dv_split(s, p);
+        a.BVD = a.dv_split == 2 ? a.BVS : a.BV;
         a.BK = p.BK;
         a.T = (int)s.T;
         a.H = (int)s.H;
@@ -232,6 +236,11 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         a.ws_gate = reinterpret_cast<float*>(ws + 2 * sb);
         a.ws_hs = ws + 2 * sb + gla::round256(kk * sizeof(float));
         a.ws_dp = s.bf16 ? static_cast<char*>(a.ws_hs) + gla::round256(gla::hs_bytes(s, p)) : nullptr;
+        if (a.dv_split == 2) {
+            char* mid = static_cast<char*>(a.ws_dp) + gla::round256((size_t)p.BH * p.N * 64 * 64 * 2);
+            a.ws_dmid = mid;
+            a.ws_gmid = reinterpret_cast<float*>(mid + sb);
+        }
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
@@ -274,8 +283,11 @@ size_t bwd_workspace_bytes(const gla::Shape& s) {
     gla::Plan p = gla::make_bwd_plan(s);
     if (p.BH == 0) return 0;
     const size_t kk = (size_t)p.BH * p.P * s.K;
-    // 16-bit inputs: the dq walk's dP tiles for the dk walk
-    const size_t dp = s.bf16 ? (size_t)p.BH * p.N * 64 * 64 * 2 : 0;
-    return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + gla::round256(gla::hs_bytes(s, p)) + dp;
+    // 16-bit inputs: the dq walk's dP tiles for the dk walk, and (split dv
+    // walk) the segments' midpoint states and half gate totals
+    const size_t dp = s.bf16 ? gla::round256((size_t)p.BH * p.N * 64 * 64 * 2) : 0;
+    const size_t mid = gla::dv_split(s, p) == 2 ? gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) : 0;
+    return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + gla::round256(gla::hs_bytes(s, p)) + dp +
+           mid;
 }
 }  // namespace

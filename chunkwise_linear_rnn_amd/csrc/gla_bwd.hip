@@ -1309,6 +1309,7 @@ template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
                 const T* __restrict__ d_o, const T* __restrict__ ws_dinit, const float* __restrict__ dht,
+                const T* __restrict__ ws_dmid, const float* __restrict__ ws_gmid, int split, int nhalf,
                 T* __restrict__ dv, float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, true>;  // sm.A holds A^T [s][t]; sm.Vw the d_o slices
@@ -1320,11 +1321,16 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     const int nvb = V / BV;
     int unit, vb;
     xcd_decode(nvb, unit, vb);
-    if (unit >= BH * P) return;
-    const int seg = unit % P;
-    const int bh = unit / P;
+    // nhalf == 2: each segment is walked as two halves, [c0, c0+split) and
+    // [c0+split, c0+seg_len), the first one starting from the midpoint state
+    if (unit >= BH * P * nhalf) return;
+    const int half = unit % nhalf;
+    const int seg = (unit / nhalf) % P;
+    const int bh = unit / nhalf / P;
     const int b = bh / H, h = bh % H;
-    const int c_begin = seg * seg_len, c_end = min(N, c_begin + seg_len);
+    const int s_begin = seg * seg_len, s_end = min(N, s_begin + seg_len);
+    const int c_begin = nhalf == 2 && half == 1 ? min(s_end, s_begin + split) : s_begin;
+    const int c_end = nhalf == 2 && half == 0 ? min(s_end, s_begin + split) : s_end;
     const int nchunks = c_end - c_begin;
     const int rsK = H * KD, rsV = H * V;
     const int col0 = vb * BV + w * CW;
@@ -1345,6 +1351,21 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     if (seg < P - 1) S.load(ws_dinit + ((long)bh * P + seg) * KD * V, V, col0);
     else if (dht) S.load(dht + (long)bh * KD * V, V, col0);
     else S.zero();
+    if (nhalf == 2 && half == 0) {
+        // dS at the midpoint = Diag(exp2 G_half) dS_end + the second half's local dS*;
+        // slot r of tile (a, cb) is key row 16a + 4(l/16) + r
+        StateRegs<KD, CB> D;
+        D.load(ws_dmid + ((long)bh * P + seg) * KD * V, V, col0);
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a) {
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(ws_gmid + ((long)bh * P + seg) * KD + 16 * a + 4 * (l >> 4));
+            f32x4 gm;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gm[r] = exp2_fast(gt[r]);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) S.s[a][cb] = S.s[a][cb] * gm + D.s[a][cb];
+        }
+    }
 
     RowSlab<T, CPK> rq, rk, rg;
     TileRegs<T, CW, 64> rdo;
@@ -1536,7 +1557,7 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
         __syncthreads();
     }
-    if (ds0 && seg == 0) S.store(ds0 + (long)bh * KD * V, V, col0);
+    if (ds0 && seg == 0 && half == 0) S.store(ds0 + (long)bh * KD * V, V, col0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1553,12 +1574,14 @@ static hipError_t launch_seg_states(const BwdLaunch& a) {
     const long KV = (long)KD * a.V;
     if (a.P > 1) {
         const int nseg = a.P - 1;
-        dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
+        const bool mid = a.dv_split == 2;
         const long nfwd = xcd_grid(nseg * a.BH, nvb);
-        dim3 grid2((unsigned)(2 * nfwd));
+        const long nrev = xcd_grid((nseg + (mid ? 1 : 0)) * a.BH, nvb);
+        dim3 grid2((unsigned)(nfwd + nrev));
         GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW>), grid2, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, (T*)a.ws_state,
-                           (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd);
+                           (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd,
+                           mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2);
         GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>, dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, 2u),
                            dim3(256), a.stream, a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V,
                            a.P);
@@ -1575,9 +1598,12 @@ static hipError_t launch_dv(const BwdLaunch& a) {
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, true>) <= 160 * 1024, "LDS budget");
-        GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
-                           (const T*)a.k, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_dstate, a.dht, (T*)a.dv,
-                           a.ds0, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
+        const int nhalf = a.dv_split == 2 && a.P > 1 ? 2 : 1;
+        dim3 gridh((unsigned)xcd_grid(a.P * a.BH * nhalf, nvb));
+        GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW>), gridh, dim3(NT), a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_dstate, a.dht,
+                           (const T*)a.ws_dmid, a.ws_gmid, (a.seg_len + 1) / 2, nhalf, (T*)a.dv, a.ds0, a.T, a.H, a.V,
+                           a.N, a.P, a.seg_len, (int)a.BH);
     } else {
         const float* dinit = a.P > 1 ? (const float*)a.ws_dstate : a.dht;
         const long seg_stride = a.P > 1 ? KV : 0;
@@ -1631,7 +1657,7 @@ static hipError_t launch_rows(const BwdLaunch& a) {
 }
 
 #define GLA_COL_DISPATCH(FN, T, KD_, BV_)                              \
-    if (a.K == KD_ && (dv_stage ? a.BV : a.BVS) == BV_) {              \
+    if (a.K == KD_ && (dv_stage ? a.BVD : a.BVS) == BV_) {             \
         hipError_t e = FN<T, KD_, BV_>(a);                             \
         return e;                                                      \
     }

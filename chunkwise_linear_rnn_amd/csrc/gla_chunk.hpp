@@ -288,7 +288,8 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
                                                const T* __restrict__ g, const T* __restrict__ y,
                                                T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_,
                                                int H, int V, int N, int P, int seg_len, int seg_first, int nseg,
-                                               int BH, int gate_first) {
+                                               int BH, int gate_first, T* __restrict__ ws_mid = nullptr,
+                                               float* __restrict__ ws_gmid = nullptr, int split = 0) {
     using Sm = SegSmem<T, KD, BV, NW>;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
     constexpr int VEC = 16 / (int)sizeof(T);
@@ -364,11 +365,23 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
             }
     };
 
+    // Optional midpoint output (ws_mid != null): the state after the first m2
+    // chunks walked (for REV, the local dS* of the segment's chunks from
+    // c_begin + split on) and the gate total of those chunks.  The prep of
+    // walk step j runs in step j-1, so the gate total is taken right after it.
+    const int m2 = ws_mid ? max(0, nchunks - split) : -1;
+    float gmid = 0.f;
+    auto store_mid = [&]() {
+        S.store(ws_mid + ((long)bh * P + seg) * (long)KD * V, V, col0);
+        if (vb == 0 && l < CPK) ws_gmid[((long)bh * P + seg) * KD + kc0 + l] = gmid;
+    };
+    if (m2 == 0) store_mid();
     if (nchunks > 0) {
         rx.load(krow(x, chunk_of(0)), rsK, kc0);
         rg.load(krow(g, chunk_of(0)), rsK, kc0);
         ry.load(vrow(y, chunk_of(0)), rsV, l);
         prep(sm.buf[0]);
+        if (m2 == 1) gmid = gtot;
         ry.store_lds(yslice(0), Sm::pW, l);
         if (nchunks > 1) {
             rx.load(krow(x, chunk_of(1)), rsK, kc0);
@@ -377,7 +390,7 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
         }
     }
     __syncthreads();
-    for (int it = 0; it < nchunks; ++it) {
+    auto step = [&](int it) {
         const bool more = it + 1 < nchunks;
         const auto& cur = sm.buf[it & 1];
         auto& nxt = sm.buf[(it + 1) & 1];
@@ -390,6 +403,7 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
             __builtin_amdgcn_sched_barrier(0);
             update(cur, yslice(it));
         }
+        if (it + 2 == m2) gmid = gtot;
         if (more) {
             ry.store_lds(yslice(it + 1), Sm::pW, l);
             if (it + 2 < nchunks) {
@@ -399,7 +413,15 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
             }
         }
         __syncthreads();
+    };
+    // the midpoint store sits between two loops: inside one, the compiler would
+    // keep its per-element addresses live across every step
+    int it = 0;
+    if (m2 > 0) {
+        for (; it < m2; ++it) step(it);
+        store_mid();
     }
+    for (; it < nchunks; ++it) step(it);
     S.store(ws_state + ((long)bh * P + seg) * (long)KD * V, V, col0);
     // each segment's gate total is written by one workgroup only (segments >= gate_first)
     if (vb == 0 && seg >= gate_first && l < CPK) ws_gate[((long)bh * P + seg) * KD + kc0 + l] = gtot;
@@ -417,22 +439,28 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
 
 // Both directions of the backward's segment states in one grid (they are
 // independent): blocks [0, nfwd) take S*_p of segments 0 .. P-2 from k, v; the
-// rest take dS*_p of segments 1 .. P-1 from q, d_o.  Two workgroups fit a CU,
-// so the directions share the machine instead of running back to back.
+// rest take dS*_p of segments 1 .. P-1 from q, d_o, or, with ws_dmid, of every
+// segment together with its midpoint state (the local dS* of the chunks from
+// c_begin + split on) and that half's gate total, from which the dv walk
+// starts a segment's first half.
 template <typename T, int KD, int BV, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ q,
                    const T* __restrict__ d_o, const T* __restrict__ g, T* __restrict__ ws_state,
                    T* __restrict__ ws_dstate, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
-                   int seg_len, int nseg, int BH, int nfwd) {
+                   int seg_len, int nseg, int BH, int nfwd, T* __restrict__ ws_dmid, float* __restrict__ ws_gmid,
+                   int split) {
     __shared__ SegSmem<T, KD, BV, NW> sm;
     const int bid = blockIdx.x;
     if (bid < nfwd)
         seg_state_body<T, KD, BV, NW, false>(sm, bid, k, g, v, ws_state, ws_gate, T_, H, V, N, P, seg_len, 0, nseg,
                                              BH, 0);
-    else  // only segment P-1 is not covered by the forward direction
+    else if (!ws_dmid)  // only segment P-1 is not covered by the forward direction
         seg_state_body<T, KD, BV, NW, true>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P, seg_len,
                                             1, nseg, BH, P - 1);
+    else  // every segment, for its midpoint state (segment 0's total is not needed)
+        seg_state_body<T, KD, BV, NW, true>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P, seg_len,
+                                            0, nseg + 1, BH, P - 1, ws_dmid, ws_gmid, split);
 }
 
 }  // namespace gla

@@ -25,6 +25,8 @@ struct BwdLaunch {
     bool bf16;
     int K, V, BV, BK;
     int BVS;  // value columns per workgroup of the segment-state pass (the forward's)
+    int BVD;  // value columns per workgroup of the dv walk
+    int dv_split;  // 2: the dv walk takes each segment in two halves (from the midpoint states)
     int T, H, N, P, seg_len;
     long BH;
     const void *q, *k, *v, *g, *d_o;
@@ -36,6 +38,8 @@ struct BwdLaunch {
     float* ws_gate;    // [BH][P][K]
     void* ws_hs;       // [BH][N][K*V] dtype: state after every chunk, in the walks' tile order
     void* ws_dp;       // [BH][N][64][64] dtype (16-bit inputs): each chunk's dP = dO V^T, [t][s]
+    void* ws_dmid;     // [BH][P][K][V] dtype (dv_split == 2): local dS* of each segment's second half
+    float* ws_gmid;    // [BH][P][K] fp32: that half's gate total (log2)
     hipStream_t stream;
 };
 

@@ -92,6 +92,12 @@ inline size_t state_bytes(const Shape& s, const Plan& p) {
     return round256((size_t)p.BH * p.P * (size_t)s.K * (size_t)s.V * (s.bf16 ? 2 : 4));
 }
 
+// 2 when the 16-bit dv walk runs at the forward's (twice wider) value width and
+// covers each segment as two halves; 1 otherwise.
+inline int dv_split(const Shape& s, const Plan& p) {
+    return s.bf16 && p.P > 1 && plan_bv(s) == 2 * p.BV ? 2 : 1;
+}
+
 // the backward's chunk-end states for the gate-gradient anchors
 inline size_t hs_bytes(const Shape& s, const Plan& p) {
     return (size_t)p.BH * p.N * (size_t)s.K * (size_t)s.V * (s.bf16 ? 2 : 4);
