@@ -33,8 +33,12 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = "GLA fwd(+bwd) tokens/sec at T=8K, dk=128, dv=256; % of bf16 MFMA peak"
 
 
-def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int):
-    """Algorithmic HBM bytes per (token, head) of one launch of `kernel`."""
+def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int, dv_split: bool = False):
+    """Algorithmic HBM bytes per (token, head) of one launch of `kernel`.
+
+    The backward's segment-state pass reads q, g, d_o of every segment instead of
+    all but the first when the dv walk takes segments in halves (it then also
+    needs each segment's midpoint state)."""
     seg_frac = (P - 1) / P if P > 1 else 0.0
     seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
     table = {
@@ -43,8 +47,8 @@ def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd:
         "bwd_dk_walk": e * (6 * K + 2 * V),         # q, k, g, dq, v, d_o read; dk, dg written
         "bwd_dv_walk": e * (3 * K + 2 * V),         # q, k, g, d_o read; dv written
         "fwd_seg_state": e * (2 * K + V) * seg_frac,  # k, g, v of all but the last segment
-        # k, g, v of all but the last segment and q, g, d_o of all but the first
-        "bwd_seg_states": 2 * e * (2 * K + V) * seg_frac_bwd,
+        # k, g, v of all but the last segment and q, g, d_o of all but the first (or all)
+        "bwd_seg_states": e * (2 * K + V) * (seg_frac_bwd + (1.0 if dv_split else seg_frac_bwd)),
     }
     return table.get(kernel)
 
@@ -87,6 +91,20 @@ def plan_segments_bwd(B, H, T, K, V, bf16):
         bv = V if V < 64 else 64
     nvb = V // bv
     return _segments(B * H, T // 64, max(nvb, nkb))
+
+
+def plan_dv_split(B, H, T, K, V, bf16):
+    """Whether the dv walk covers each segment in two halves (gla_plan.hpp's dv_split)."""
+    bk = 64 if (not bf16 or V >= 128) else min(K, 128)
+    nkb = K // bk
+    cap = (256 if K <= 128 else 64) if bf16 else 128
+    bvs = min(V, cap)
+    bv = bvs
+    if nkb > 1 and V // nkb < bv:
+        bv = V // nkb
+    if bv < 64:
+        bv = V if V < 64 else 64
+    return bool(bf16) and plan_segments_bwd(B, H, T, K, V, bf16) > 1 and bvs == 2 * bv
 
 
 # sources of the forward and backward step kernels (the recorded traffic is theirs)
@@ -304,7 +322,7 @@ def main():
     P = plan_segments(B, H, T, K, V, w.dtype == "bf16")
     P_bwd = plan_segments_bwd(B, H, T, K, V, w.dtype == "bf16")
     units = B * T * H
-    bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd)
+    bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd, plan_dv_split(B, H, T, K, V, w.dtype == "bf16"))
     roofline = None
     if bpt is not None:
         ach = bpt * units / (kern[dom]["avg_us"] * 1e-6) / 1e9
