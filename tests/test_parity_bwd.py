@@ -109,3 +109,14 @@ def test_bwd_deterministic():
 def test_bwd_named_workloads(name, heads):
     w = gi.WORKLOADS[name]
     _check_bwd(w, heads=heads)
+
+
+@pytest.mark.parametrize("B,H,T", [
+    (4, 16, 64 * 13),   # two segments of 7 and 6 chunks: halves of 4+3 and 4+2 chunks
+    (2, 16, 64 * 21),   # segments of 6, 6, 6, 3 chunks: the last one has an empty second half
+])
+def test_bwd_half_segment_walks_ragged(B, H, T):
+    # dk=128, dv=256 bf16 takes the value-width dv walk over half segments, started
+    # from the midpoint states of the reverse segment-state pass
+    w = gi.custom(B, H, T, 128, 256, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=500 + T)
+    _check_bwd(w, heads=[(0, 0), (B - 1, H - 1)], with_dht=True)
