@@ -90,7 +90,8 @@ struct TStateRegs {
 
 // Wave roles of the row-split kernels: NW waves cover BK/16 key blocks times
 // VS (1 or 2) value slices.  With two slices, contractions over V are summed
-// through LDS and the slice-0 wave of a key block finishes its outputs.
+// through LDS; the slice-0 wave of a key block finishes its outputs in the
+// fp32 walks, and the pipelined walks split the token blocks (NB, block()).
 template <int BK, int V, int NW>
 struct RowRoles {
     static constexpr int NKQ = BK / 16;
@@ -99,6 +100,21 @@ struct RowRoles {
     static_assert(NKQ * VS == NW, "waves must tile key blocks x value slices");
     static_assert(VS == 1 || VS == 2, "one or two value slices");
     static_assert(VW % 32 == 0, "value slice must be a whole number of 32-wide MFMA steps");
+    // Token blocks (16 rows of the chunk) whose outputs a wave finishes: NB per
+    // wave, slot m.  With two slices, slice 0 takes blocks 0 and 3 and slice 1
+    // blocks 1 and 2, so the causal intra products left after the slice sum
+    // split evenly (blocks 0-1 and 2-3 differ in depth by one 32-row step); slot
+    // m covers the 32-row half half(m) of the chunk for both slices.
+    static constexpr int NB = 4 / VS;
+    __device__ __forceinline__ static int block(int m, int vs) {
+        return VS == 1 ? m : (m == 0 ? (vs ? 1 : 0) : (vs ? 2 : 3));
+    }
+    __host__ __device__ static constexpr int half(int m) { return VS == 1 ? m / 2 : m; }
+    // a[block(m, vs)] for an unrolled (constant) m: a select on the uniform vs
+    __device__ __forceinline__ static f32x4 pick(const f32x4* a, int m, int vs) {
+        if (VS == 1) return a[m];
+        return vs ? a[m == 0 ? 1 : 2] : a[m == 0 ? 0 : 3];
+    }
 };
 
 // The ten lower-triangular 16x16 tiles of dP = (dO V^T) * M, contraction over
@@ -371,8 +387,9 @@ struct RowPipeSmem {
         alignas(16) float X[kChunk * BK];  // exact-path intra sums, phase 2 only
     };
     alignas(16) T P[kChunk * pP];
-    alignas(16) f32x4 red[RR::VS > 1 ? RR::NKQ * 4 * 64 : 1];
+    alignas(16) f32x4 red[RR::VS > 1 ? RR::NKQ * RR::VS * RR::NB * 64 : 1];  // [key block][reader slice][slot][lane]
     float carry[RR::VS * BK];
+    alignas(16) float tot[4 * BK];  // dk walk: per token block, the column totals of dA
 };
 
 // One wave prepares key columns kc0 .. kc0+NC-1 of a chunk (lane = token row)
@@ -428,8 +445,9 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
 // Phase 1: dP, the value-slice partial of dO S^T, the state update
 // S^T <- post * (pre * S^T + V^T Kt), the store of S_out to `hs` (anchor chunks
 // only), the next chunk's key-side preparation.  Phase 2: dP to `dp_out` for
-// the dk walk (first key block only), dP Kt, the slice reduction, the factor
-// exp2(B_t) and the store of dq; the next chunk's V and d_o tiles.
+// the dk walk (first key block only); then each wave, for its two token blocks
+// (RowRoles::block), dP Kt, the slice reduction, the factor exp2(B_t) and the
+// store of dq; the next chunk's V and d_o tiles.
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
@@ -441,7 +459,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     static_assert(CPK % VEC == 0, "wave tiling");
     using Sm = RowPipeSmem<T, BK, V, NW>;
     __shared__ Sm sm;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
     const int i0 = 16 * kq, j0 = vs * VW;
     const int kc0 = w * CPK;
@@ -494,22 +512,31 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         const bool exact = cur.flag[0] != 0;
         // ---- phase 1
         dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
-        // dq^T[i][t] partial = sum_{j in slice} S^T[j][i] dO[t][j]
-        f32x4 acc[4];
+        // dq^T[i][t] partial = sum_{j in slice} S^T[j][i] dO[t][j], for this
+        // wave's token blocks (own, slot m = block RR::block(m, vs)) and for
+        // the partner slice's (oth), which go to LDS in the partner's area
+        f32x4 own[RR::NB], oth[RR::NB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[tb] = zero4();
+        for (int m = 0; m < RR::NB; ++m) own[m] = oth[m] = zero4();
 #pragma unroll
         for (int ks = 0; ks < VW / 32; ++ks) {
             const vec4_t<T> s0 = to_vec4<T>(S.s[2 * ks]);
             const vec4_t<T> s1 = to_vec4<T>(S.s[2 * ks + 1]);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                acc[tb] = mma32(acc[tb], s0, s1, frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks),
-                                frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks + 16));
+            for (int m = 0; m < RR::NB; ++m) {
+                const int tb = RR::block(m, vs);
+                own[m] = mma32(own[m], s0, s1, frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks),
+                               frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks + 16));
+                if (RR::VS > 1) {
+                    const int tp = RR::block(m, vs ^ 1);
+                    oth[m] = mma32(oth[m], s0, s1, frag_rm<T>(sm.dO, Sm::pV, 16 * tp, j0 + 32 * ks),
+                                   frag_rm<T>(sm.dO, Sm::pV, 16 * tp, j0 + 32 * ks + 16));
+                }
+            }
         }
-        if (RR::VS > 1 && vs == 1)
+        if (RR::VS > 1)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) sm.red[(kq * 4 + tb) * 64 + l] = acc[tb];
+            for (int m = 0; m < RR::NB; ++m) sm.red[((kq * 2 + (vs ^ 1)) * RR::NB + m) * 64 + l] = oth[m];
         // S^T <- post * (pre * S^T + V^T Kt); this lane's key column is i0 + l%16
         {
             const float pre = cur.pre[i0 + (l & 15)], post = cur.post[i0 + (l & 15)];
@@ -552,18 +579,18 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
                     *reinterpret_cast<const u32x4*>(sm.P + row * Sm::pP + col);
             }
         }
+        f32x4* fin = own;
         if (!exact) {
-            if (vs == 0) {
-                // dq^T[i][t] += sum_s Kt[s][i] dP[t][s]
+            // dq^T[i][t] += sum_s Kt[s][i] dP[t][s], s-halves up to t's
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
+            for (int m = 0; m < RR::NB; ++m) {
+                const int tb = RR::block(m, vs);
 #pragma unroll
-                    for (int ks2 = 0; ks2 <= tb / 2; ++ks2)
-                        acc[tb] = mma32(acc[tb], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
-                                        frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
-                                        frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
-                                        frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16));
-                }
+                for (int ks2 = 0; ks2 <= RR::half(m); ++ks2)
+                    fin[m] = mma32(fin[m], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
+                                   frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
+                                   frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2),
+                                   frag_rm<T>(sm.P, Sm::pP, 16 * tb, 32 * ks2 + 16));
             }
         } else {
             // intra part element by element, sum_{s<=t} dP[t][s] k_s exp2(B_t - B_s),
@@ -590,18 +617,18 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
             for (int j = 0; j < CPK; ++j) Xf[l * BK + kc0 + j] = sum[j];
             __syncthreads();
         }
-        if (vs == 0) {
+        {
             const float* Xf = sm.X;
             T* dqbase = const_cast<T*>(kbase(dq, c));
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                if (RR::VS > 1) acc[tb] += sm.red[(kq * 4 + tb) * 64 + l];
-                // slot r: key row i = i0 + 4(l/16) + r, token t = 16tb + l%16
-                const int t = 16 * tb + (l & 15), ic = i0 + 4 * (l >> 4);
+            for (int m = 0; m < RR::NB; ++m) {
+                if (RR::VS > 1) fin[m] += sm.red[((kq * 2 + vs) * RR::NB + m) * 64 + l];
+                // slot r: key row i = i0 + 4(l/16) + r, token t = 16 block + l%16
+                const int t = 16 * RR::block(m, vs) + (l & 15), ic = i0 + 4 * (l >> 4);
                 const f32x4 bt = *reinterpret_cast<const f32x4*>(cur.B + t * Sm::pB + ic);
                 f32x4 val;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) val[r] = acc[tb][r] * exp2_fast(bt[r]);
+                for (int r = 0; r < 4; ++r) val[r] = fin[m][r] * exp2_fast(bt[r]);
                 if (exact) val += *reinterpret_cast<const f32x4*>(Xf + t * BK + ic);
                 *reinterpret_cast<vec4_t<T>*>(dqbase + t * rsK + ic) = to_vec4<T>(val);
             }
@@ -630,12 +657,16 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 //   off  = rowsum(S_out * dS) on anchor chunks, else the later chunk's off plus its dA total
 //   dS_in = Diag(gamma) dS + Ql^T dO
 // dP = dO V^T of the chunk is the dq walk's (`dp_in`, [t][s] per chunk), read
-// with transposed fragments.  Phase 1: the value-slice partials of V dS^T and
-// (anchor chunks) of the dg anchor (S_out read back from `hs`), the dS update,
-// dP to LDS, the previous chunk's query-side preparation.  Phase 2: dP^T Ql,
-// the slice reduction and the factors, dk, dA and its reverse cumulative sum
-// down the 16-lane rows (DPP) and across the four token blocks, dg; the next
-// value and d_o tiles.
+// with transposed fragments.  Phase 1: dg of the previous chunk (below), the
+// value-slice partials of V dS^T and (anchor chunks) of the dg anchor (S_out
+// read back from `hs`), the dS update, dP to LDS, the next chunk's query-side
+// preparation.  Phase 2, each wave for its two token blocks (RowRoles::block):
+// dP^T Ql, the slice reduction and the factors, dk, dA and its reverse
+// cumulative sum down the 16-lane rows (DPP), the block totals to LDS; the
+// next value and d_o tiles.  dg of a block adds the totals of the chunk's later
+// blocks, which the other slice's wave may own, so it is stored after the
+// step's closing barrier, at the start of the next step (after the loop for
+// the last chunk).
 template <typename T, int BK, int V, int NW>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
@@ -648,7 +679,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     static_assert(CPK % VEC == 0, "wave tiling");
     using Sm = RowPipeSmem<T, BK, V, NW>;
     __shared__ Sm sm;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
     const int i0 = 16 * kq, j0 = vs * VW;
     const int kc0 = w * CPK;
@@ -698,6 +729,27 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     }
     __syncthreads();
     f32x4 run_carry = zero4();
+    // dg of a chunk: the in-block reverse sums dA_scan of this wave's blocks,
+    // the carry into the chunk, and the chunk's dg rows
+    f32x4 da[RR::NB];
+    f32x4 cin = zero4();
+    T* dg_rows = nullptr;
+    const int ic = i0 + 4 * (l >> 4);  // slot r of a finishing tile: key column ic + r
+    auto store_dg = [&]() {
+        f32x4 tot[4], run[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) tot[sb] = *reinterpret_cast<const f32x4*>(sm.tot + sb * BK + ic);
+        // token block sb adds the totals of blocks sb+1 .. 3
+        run[3] = cin;
+#pragma unroll
+        for (int sb = 2; sb >= 0; --sb) run[sb] = run[sb + 1] + tot[sb + 1];
+#pragma unroll
+        for (int m = 0; m < RR::NB; ++m) {
+            const int s = 16 * RR::block(m, vs) + (l & 15);
+            *reinterpret_cast<vec4_t<T>*>(dg_rows + s * rsK + ic) = to_vec4<T>(da[m] + RR::pick(run, m, vs));
+        }
+        run_carry = run[0] + tot[0];
+    };
     for (int it = 0; it < nchunks; ++it) {
         const int c = chunk_of(it);
         const bool anc = it % kAnchorStride == 0;
@@ -710,6 +762,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         // tiles (dg anchor); q, dq, k in the accumulator layout (slot r of token
         // block sb: token 16sb + l%16, key column i0 + 4(l/16) + r) for dA
         rp.load(dp_in + ((long)bh * N + c) * (kChunk * kChunk), kChunk, tid);
+        if (it > 0) store_dg();
         vec4_t<T> so[VW / 16];
         if (anc) {
             const T* src = hs + (((long)bh * N + c) * nkb + kb) * (long)(BK * V);
@@ -717,21 +770,21 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             for (int jb = 0; jb < VW / 16; ++jb)
                 so[jb] = *reinterpret_cast<const vec4_t<T>*>(src + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4);
         }
-        vec4_t<T> aq[4], adq[4], ak[4];
-        if (vs == 0) {
-            const long off = (long)(l & 15) * rsK + i0 + 4 * (l >> 4);
+        vec4_t<T> aq[RR::NB], adq[RR::NB], ak[RR::NB];
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                aq[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(q, c) + off + 16 * sb * rsK);
-                adq[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(dq, c) + off + 16 * sb * rsK);
-                ak[sb] = *reinterpret_cast<const vec4_t<T>*>(kbase(k, c) + off + 16 * sb * rsK);
-            }
+        for (int m = 0; m < RR::NB; ++m) {
+            const long off = (long)(16 * RR::block(m, vs) + (l & 15)) * rsK + ic;
+            aq[m] = *reinterpret_cast<const vec4_t<T>*>(kbase(q, c) + off);
+            adq[m] = *reinterpret_cast<const vec4_t<T>*>(kbase(dq, c) + off);
+            ak[m] = *reinterpret_cast<const vec4_t<T>*>(kbase(k, c) + off);
         }
         const float gl = cur.pre[i0 + (l & 15)];  // gamma of this lane's key column
         // dk^T[i][s] partial = sum_{j in slice} (gamma dS)[i][j] V[s][j] (exact path: dS unscaled)
-        f32x4 acc[4];
+        // for this wave's token blocks (own, slot m = block RR::block(m, vs)) and
+        // the partner slice's (oth)
+        f32x4 own[RR::NB], oth[RR::NB];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4();
+        for (int m = 0; m < RR::NB; ++m) own[m] = oth[m] = zero4();
         {
             const float sc = exact ? 1.f : gl;
 #pragma unroll
@@ -739,9 +792,16 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 const vec4_t<T> s0 = to_vec4<T>(S.s[2 * ks] * sc);
                 const vec4_t<T> s1 = to_vec4<T>(S.s[2 * ks + 1] * sc);
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    acc[sb] = mma32(acc[sb], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks),
-                                    frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks + 16));
+                for (int m = 0; m < RR::NB; ++m) {
+                    const int sb = RR::block(m, vs);
+                    own[m] = mma32(own[m], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks),
+                                   frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks + 16));
+                    if (RR::VS > 1) {
+                        const int sp = RR::block(m, vs ^ 1);
+                        oth[m] = mma32(oth[m], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks),
+                                       frag_rm<T>(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks + 16));
+                    }
+                }
             }
         }
         // anchor partial: sum_{j in slice} S_out[i][j] dS[i][j]
@@ -755,9 +815,10 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             part += __shfl_xor(part, 32);
             if ((l >> 4) == 0) sm.carry[vs * BK + i0 + (l & 15)] = part;
         }
-        if (RR::VS > 1 && vs == 1)
+        // the partner slice's token blocks go to LDS, in its area
+        if (RR::VS > 1)
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) sm.red[(kq * 4 + sb) * 64 + l] = acc[sb];
+            for (int m = 0; m < RR::NB; ++m) sm.red[((kq * 2 + (vs ^ 1)) * RR::NB + m) * 64 + l] = oth[m];
         // dS^T <- gamma dS^T + dO^T Ql
 #pragma unroll
         for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= gl;
@@ -804,75 +865,66 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             for (int j = 0; j < CPK; ++j) sm.X[l * BK + kc0 + j] = sum[j];
             __syncthreads();
         }
-        if (vs == 0) {
+        {
+            f32x4* fin = own;
             if (!exact) {
-                // dk^T[i][s] += sum_t Ql[t][i] dP[t][s], t-blocks >= sb
+                // dk^T[i][s] += sum_t Ql[t][i] dP[t][s], t-halves from s's
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
+                for (int m = 0; m < RR::NB; ++m) {
+                    const int sb = RR::block(m, vs);
 #pragma unroll
-                    for (int ks2 = sb / 2; ks2 < 2; ++ks2)
-                        acc[sb] = mma32(acc[sb], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
-                                        frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
-                                        frag_cm<T>(sm.P, Sm::pP, 32 * ks2, 16 * sb),
-                                        frag_cm<T>(sm.P, Sm::pP, 32 * ks2 + 16, 16 * sb));
+                    for (int ks2 = RR::half(m); ks2 < 2; ++ks2)
+                        fin[m] = mma32(fin[m], frag_cm<T>(cur.K, Sm::pK, 32 * ks2, i0),
+                                       frag_cm<T>(cur.K, Sm::pK, 32 * ks2 + 16, i0),
+                                       frag_cm<T>(sm.P, Sm::pP, 32 * ks2, 16 * sb),
+                                       frag_cm<T>(sm.P, Sm::pP, 32 * ks2 + 16, 16 * sb));
+                }
             }
-            const int ic = i0 + 4 * (l >> 4);
             const f32x4 blast = *reinterpret_cast<const f32x4*>(cur.B + 63 * Sm::pB + ic);
             T* dkbase = const_cast<T*>(kbase(dk, c));
-            f32x4 da[4];
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                if (RR::VS > 1) acc[sb] += sm.red[(kq * 4 + sb) * 64 + l];
-                // slot r: key column ic + r, token s = 16sb + l%16
-                const int s = 16 * sb + (l & 15);
+            for (int m = 0; m < RR::NB; ++m) {
+                if (RR::VS > 1) fin[m] += sm.red[((kq * 2 + vs) * RR::NB + m) * 64 + l];
+                // slot r: key column ic + r, token s = 16 block + l%16
+                const int s = 16 * RR::block(m, vs) + (l & 15);
                 const f32x4 bs = *reinterpret_cast<const f32x4*>(cur.B + s * Sm::pB + ic);
                 f32x4 val;
                 if (!exact) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) val[r] = acc[sb][r] * exp2_fast(-bs[r]);
+                    for (int r = 0; r < 4; ++r) val[r] = fin[m][r] * exp2_fast(-bs[r]);
                 } else {
                     const f32x4 xs = *reinterpret_cast<const f32x4*>(sm.X + s * BK + ic);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) val[r] = acc[sb][r] * exp2_fast(blast[r] - bs[r]) + xs[r];
+                    for (int r = 0; r < 4; ++r) val[r] = fin[m][r] * exp2_fast(blast[r] - bs[r]) + xs[r];
                 }
                 *reinterpret_cast<vec4_t<T>*>(dkbase + s * rsK + ic) = to_vec4<T>(val);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    da[sb][r] = Elem<T>::to_f(aq[sb][r]) * Elem<T>::to_f(adq[sb][r]) -
-                                Elem<T>::to_f(ak[sb][r]) * val[r];
+                    da[m][r] = Elem<T>::to_f(aq[m][r]) * Elem<T>::to_f(adq[m][r]) - Elem<T>::to_f(ak[m][r]) * val[r];
             }
-            // reverse cumulative sum over the chunk's tokens: within each 16-token
-            // block down the 16-lane rows (DPP row_shl), then across the blocks
+            // reverse cumulative sum within each 16-token block, down the
+            // 16-lane rows (DPP row_shl); the row's first lane ends with the
+            // block total, which goes to LDS for the blocks before it
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
+            for (int m = 0; m < RR::NB; ++m) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float x = da[sb][r];
+                    float x = da[m][r];
                     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x101, 0xF, 0xF, false);
                     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x102, 0xF, 0xF, false);
                     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x104, 0xF, 0xF, false);
                     x += __builtin_amdgcn_update_dpp(0.0f, x, 0x108, 0xF, 0xF, false);
-                    da[sb][r] = x;
+                    da[m][r] = x;
                 }
+                if ((l & 15) == 0) *reinterpret_cast<f32x4*>(sm.tot + RR::block(m, vs) * BK + ic) = da[m];
             }
-            f32x4 run = run_carry;
-            if (anc)
+            if (anc) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) run[r] = sm.carry[ic + r] + (RR::VS > 1 ? sm.carry[BK + ic + r] : 0.f);
-            T* dgbase = const_cast<T*>(kbase(dg, c));
-#pragma unroll
-            for (int sb = 3; sb >= 0; --sb) {
-                const int s = 16 * sb + (l & 15);
-                f32x4 out, tot;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    out[r] = da[sb][r] + run[r];
-                    tot[r] = __shfl(da[sb][r], l & 48);  // the block's total sits in its row's first lane
-                }
-                *reinterpret_cast<vec4_t<T>*>(dgbase + s * rsK + ic) = to_vec4<T>(out);
-                run += tot;
+                for (int r = 0; r < 4; ++r) cin[r] = sm.carry[ic + r] + (RR::VS > 1 ? sm.carry[BK + ic + r] : 0.f);
+            } else {
+                cin = run_carry;
             }
-            run_carry = run;
+            dg_rows = const_cast<T*>(kbase(dg, c));
         }
         if (exact) __syncthreads();
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
@@ -886,6 +938,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
         __syncthreads();
     }
+    if (nchunks > 0) store_dg();
 }
 
 // ---------------------------------------------------------------------------
