@@ -215,6 +215,73 @@ def decode_bench(args, torch, gla, gi):
     print(json.dumps(line), flush=True)
 
 
+def out_gate_bench(args, torch, gla, gi):
+    """gla_out_gate and gla_out_gate_bwd on the metric workload's output rows
+    (B=2, T=8192, H=4, V=256, bf16: 65536 rows of one head each).
+
+    Both are HBM-bound.  Algorithmic bytes per call: forward e*V*R*3 (o, z read,
+    y written); backward e*V*R*5 (o, z, dy read, d_o, dz written)."""
+    B, T, H, V = 2, 8192, 4, 256
+    R = B * T * H
+    cpu = gi.make_gate_inputs(B, T, H, V, "bf16", seed=6)
+    dev = "cuda:0"
+    d = {k: (v.to(dev) if v is not None else None) for k, v in cpu.items()}
+    eps = 1e-5
+    y = torch.empty_like(d["o"]); dx = torch.empty_like(d["o"]); dz = torch.empty_like(d["o"])
+    dw = torch.empty(V, device=dev); db = torch.empty(V, device=dev)
+    ws = gla.workspace(gla.gla_out_gate_bwd_workspace_size(B, T, H, V, torch.bfloat16), dev)
+    fwd = lambda: gla.gla_out_gate_into(d["o"], d["z"], d["ln_w"], d["ln_b"], eps, y)
+    bwd = lambda: gla.gla_out_gate_bwd_into(d["o"], d["z"], d["ln_w"], d["ln_b"], eps, d["dy"], dx, dz, dw, db, ws)
+    step = lambda: (fwd(), bwd())
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n = max(args.steps, 1) * 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    gla.gla_kernel_timing(True)
+    gla.gla_kernel_timing_read()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    kt = gla.gla_kernel_timing_read()
+    gla.gla_kernel_timing(False)
+    kern = {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}
+    alg_f, alg_b = 2 * V * R * 3, 2 * V * R * 5
+    bwd_us = kern["out_gate_bwd"]["avg_us"]
+    achieved = alg_b / (bwd_us * 1e-6) / 1e9
+    line = {"metric": "GLA output epilogue rows/sec (per-head LayerNorm + Swish gate, forward + backward)",
+            "value": R / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": n, "ms_per_step": ms,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "out_gate: B=2 T=8192 H=4 V=256 bf16 (the metric workload's output), eps 1e-5"},
+            "kernels": kern,
+            "fwd_GBps": alg_f / (kern["out_gate_fwd"]["avg_us"] * 1e-6) / 1e9,
+            "roofline": {"bound": "hbm", "kernel": "out_gate_bwd", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": alg_b}}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 4096  # a bounded sample of the rows (they are independent)
+        f64 = lambda t: t.reshape(R, V)[:rows].to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 2.0:
+            oracle.out_gate(f64(cpu["o"]), f64(cpu["z"]), cpu["ln_w"].double().numpy(), cpu["ln_b"].double().numpy(),
+                            eps)
+            oracle.out_gate_bwd(f64(cpu["o"]), f64(cpu["z"]), cpu["ln_w"].double().numpy(),
+                                cpu["ln_b"].double().numpy(), eps, f64(cpu["dy"]))
+            reps += 1
+        sec = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {"value": rows / sec, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                "sample": "fp64 oracle forward + backward on %d of %d rows (%d repetitions)" % (
+                                    rows, R, reps)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +292,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--decode", action="store_true",
                     help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
+    ap.add_argument("--out-gate", action="store_true",
+                    help="measure the output epilogue (LayerNorm + Swish gate, fwd + bwd) on the metric "
+                         "workload's output rows instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (to calibrate rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -252,6 +322,9 @@ def main():
 
     if args.decode:
         decode_bench(args, torch, gla, gi)
+        return
+    if args.out_gate:
+        out_gate_bench(args, torch, gla, gi)
         return
 
     w = gi.WORKLOADS[args.workload]

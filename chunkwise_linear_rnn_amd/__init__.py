@@ -10,8 +10,10 @@ Functions mirror the ABI:
   gla_fwd(q, k, v, g, s0=None, ...)         -> (o, s_final)
   gla_bwd(q, k, v, g, d_o, s0=None, dht=None) -> (dq, dk, dv, dg, ds0)
   gla_decode(q, k, v, g, state)              -> o   (recurrent form; state updated in place)
-  gla_fwd_workspace_size / gla_bwd_workspace_size
-Layouts: q, k, g [B,T,H,K]; v, o, d_o [B,T,H,V]; states [B,H,K,V] float32.
+  gla_out_gate(o, z, ln_w, ln_b, eps)        -> y   (per-head LayerNorm, Swish output gate)
+  gla_out_gate_bwd(o, z, ln_w, ln_b, eps, dy) -> (d_o, dz, dln_w, dln_b)
+  gla_fwd_workspace_size / gla_bwd_workspace_size / gla_out_gate_bwd_workspace_size
+Layouts: q, k, g [B,T,H,K]; v, o, d_o, z, y [B,T,H,V]; states [B,H,K,V] float32.
 """
 from __future__ import annotations
 
@@ -41,7 +43,8 @@ class GlaError(RuntimeError):
         self.status = status
 
 
-EXPORTS = ["gla_fwd", "gla_bwd", "gla_decode", "gla_fwd_workspace_size", "gla_bwd_workspace_size",
+EXPORTS = ["gla_fwd", "gla_bwd", "gla_decode", "gla_out_gate", "gla_out_gate_bwd",
+           "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_out_gate_bwd_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
            "gla_kernel_timing", "gla_kernel_timing_read"]
 
@@ -65,6 +68,13 @@ def lib():
     L.gla_bwd.restype = ctypes.c_int
     L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
     L.gla_decode.restype = ctypes.c_int
+    fl = ctypes.c_float
+    L.gla_out_gate.argtypes = [sh, vp, vp, vp, vp, fl, vp, vp]
+    L.gla_out_gate.restype = ctypes.c_int
+    L.gla_out_gate_bwd.argtypes = [sh, vp, vp, vp, vp, fl, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gla_out_gate_bwd.restype = ctypes.c_int
+    L.gla_out_gate_bwd_workspace_size.argtypes = [sh]
+    L.gla_out_gate_bwd_workspace_size.restype = ctypes.c_size_t
     L.gla_fwd_workspace_size.argtypes = [sh]
     L.gla_fwd_workspace_size.restype = ctypes.c_size_t
     L.gla_bwd_workspace_size.argtypes = [sh]
@@ -207,6 +217,61 @@ def gla_decode(q, k, v, g, state, stream=None) -> torch.Tensor:
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
     gla_decode_into(q, k, v, g, state, o, stream)
     return o
+
+
+def _gate_args(o, z, ln_w, ln_b):
+    if o.dim() != 4:
+        raise ValueError("o must be [B,T,H,V]")
+    B, T, H, V = o.shape
+    dev, dt = o.device, o.dtype
+    _need(o, "o", (B, T, H, V), dt, dev)
+    _need(z, "z", (B, T, H, V), dt, dev)
+    if ln_w is None:
+        raise ValueError("ln_w is required")
+    _need(ln_w, "ln_w", (V,), torch.float32, dev)
+    _need(ln_b, "ln_b", (V,), torch.float32, dev)
+    return B, T, H, V, dev, dt
+
+
+def gla_out_gate_bwd_workspace_size(B, T, H, V, dtype) -> int:
+    return int(lib().gla_out_gate_bwd_workspace_size(ctypes.byref(make_shape(B, T, H, 0, V, dtype))))
+
+
+def gla_out_gate_into(o, z, ln_w, ln_b, eps, y, stream=None):
+    B, T, H, V = o.shape
+    shape = make_shape(B, T, H, 0, V, o.dtype)
+    _check(lib().gla_out_gate(ctypes.byref(shape), _ptr(o), _ptr(z), _ptr(ln_w), _ptr(ln_b), float(eps), _ptr(y),
+                              _stream(stream)))
+
+
+def gla_out_gate(o, z, ln_w, ln_b=None, eps=1e-5, stream=None) -> torch.Tensor:
+    """y = Swish(z) * (LayerNorm_V(o) * ln_w + ln_b), per head row (GLA layer output, Section 4.4).
+
+    o, z: [B,T,H,V] (bf16 or fp32); ln_w, ln_b: [V] float32 shared by the heads."""
+    B, T, H, V, dev, dt = _gate_args(o, z, ln_w, ln_b)
+    y = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    gla_out_gate_into(o, z, ln_w, ln_b, eps, y, stream)
+    return y
+
+
+def gla_out_gate_bwd_into(o, z, ln_w, ln_b, eps, dy, d_o, dz, dln_w, dln_b, ws, stream=None):
+    B, T, H, V = o.shape
+    shape = make_shape(B, T, H, 0, V, o.dtype)
+    _check(lib().gla_out_gate_bwd(ctypes.byref(shape), _ptr(o), _ptr(z), _ptr(ln_w), _ptr(ln_b), float(eps),
+                                  _ptr(dy), _ptr(d_o), _ptr(dz), _ptr(dln_w), _ptr(dln_b), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def gla_out_gate_bwd(o, z, ln_w, ln_b, eps, dy, stream=None):
+    """Gradients of <y, dy> for gla_out_gate: (d_o, dz, dln_w, dln_b); dln_b is None when ln_b is."""
+    B, T, H, V, dev, dt = _gate_args(o, z, ln_w, ln_b)
+    _need(dy, "dy", (B, T, H, V), dt, dev)
+    d_o = torch.empty_like(o); dz = torch.empty_like(z)
+    dln_w = torch.empty(V, dtype=torch.float32, device=dev)
+    dln_b = torch.empty(V, dtype=torch.float32, device=dev) if ln_b is not None else None
+    ws = workspace(gla_out_gate_bwd_workspace_size(B, T, H, V, dt), dev)
+    gla_out_gate_bwd_into(o, z, ln_w, ln_b, eps, dy, d_o, dz, dln_w, dln_b, ws, stream)
+    return d_o, dz, dln_w, dln_b
 
 
 def gla_kernel_timing(enable: bool) -> None:

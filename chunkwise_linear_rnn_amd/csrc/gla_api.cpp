@@ -10,6 +10,7 @@
 #include <cstring>
 #include <string>
 
+#include "gla_gate.hpp"
 #include "gla_launch.hpp"
 #include "gla_plan.hpp"
 
@@ -99,6 +100,31 @@ gla_status_t check_decode_shape(const gla_shape_t* s, gla::Shape* out) {
     out->bf16 = s->dtype == GLA_DTYPE_BF16;
     return GLA_OK;
 }
+
+// The output epilogue: rows of V channels, T any length; K and chunk unused.
+gla_status_t check_gate_shape(const gla_shape_t* s, gla::Shape* out) {
+    if (!s) return fail(GLA_ERR_NULL, "shape is NULL");
+    if (s->reserved != 0) return fail(GLA_ERR_UNSUPPORTED, "shape.reserved must be 0 (got %d)", s->reserved);
+    if (s->B < 0 || s->T < 0 || s->H < 0)
+        return fail(GLA_ERR_SHAPE, "negative size: B=%lld T=%lld H=%lld", (long long)s->B, (long long)s->T,
+                    (long long)s->H);
+    if (s->dtype != GLA_DTYPE_BF16 && s->dtype != GLA_DTYPE_FP32)
+        return fail(GLA_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+    if (s->V != 64 && s->V != 128 && s->V != 256 && s->V != 512)
+        return fail(GLA_ERR_UNSUPPORTED, "unsupported head dim V=%lld for the output gate", (long long)s->V);
+    const int64_t lim = (int64_t)1 << 31;
+    if (s->T >= lim || s->H >= lim || s->B >= lim || (s->B * s->H >= lim) || s->B * s->H * s->T >= lim)
+        return fail(GLA_ERR_SHAPE, "size too large for this library");
+    out->B = s->B;
+    out->T = s->T;
+    out->H = s->H;
+    out->K = s->K;
+    out->V = s->V;
+    out->bf16 = s->dtype == GLA_DTYPE_BF16;
+    return GLA_OK;
+}
+
+bool eps_ok(float eps) { return eps >= 0.f && eps <= 3.0e38f; }  // false for NaN and infinities
 
 }  // namespace
 
@@ -272,6 +298,87 @@ gla_status_t gla_decode(const gla_shape_t* shape, const void* q, const void* k, 
     a.o = o;
     a.stream = reinterpret_cast<hipStream_t>(stream);
     const hipError_t err = gla::launch_decode(a);
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
+gla_status_t gla_out_gate(const gla_shape_t* shape, const void* o, const void* z, const float* ln_w,
+                          const float* ln_b, float eps, void* y, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_gate_shape(shape, &s);
+    if (st != GLA_OK) return st;
+    if (!eps_ok(eps)) return fail(GLA_ERR_UNSUPPORTED, "eps must be finite and >= 0 (got %g)", (double)eps);
+    const long R = (long)(s.B * s.T * s.H);
+    if (R == 0) return GLA_OK;
+    if (!o || !z || !ln_w || !y) return fail(GLA_ERR_NULL, "o, z, ln_w and y are required");
+    const void* ptrs[] = {o, z, ln_w, ln_b, y};
+    const char* names[] = {"o", "z", "ln_w", "ln_b", "y"};
+    for (int i = 0; i < 5; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    gla::GateLaunch a{};
+    a.bf16 = s.bf16;
+    a.backward = false;
+    a.V = (int)s.V;
+    a.R = R;
+    a.o = o; a.z = z; a.w = ln_w; a.b = ln_b; a.eps = eps;
+    a.y = y;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t err = gla::launch_out_gate(a);
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
+size_t gla_out_gate_bwd_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_gate_shape(shape, &s) != GLA_OK) return 0;
+    return gla::round256((size_t)2 * gla::kGateMaxBlocks * (size_t)s.V * sizeof(float));
+}
+
+gla_status_t gla_out_gate_bwd(const gla_shape_t* shape, const void* o, const void* z, const float* ln_w,
+                              const float* ln_b, float eps, const void* dy, void* d_o, void* dz, float* dln_w,
+                              float* dln_b, void* workspace, size_t workspace_bytes, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_gate_shape(shape, &s);
+    if (st != GLA_OK) return st;
+    if (!eps_ok(eps)) return fail(GLA_ERR_UNSUPPORTED, "eps must be finite and >= 0 (got %g)", (double)eps);
+    const long R = (long)(s.B * s.T * s.H);
+    const size_t need = gla::round256((size_t)2 * gla::kGateMaxBlocks * (size_t)s.V * sizeof(float));
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    if (R == 0) {
+        // no rows: the column sums are zero (written by a kernel, not a memset,
+        // so that the call can be captured in a graph)
+        if (!aligned16(dln_w) || !aligned16(dln_b)) return fail(GLA_ERR_ALIGN, "dln_w or dln_b is not 16-byte aligned");
+        gla::GateLaunch a{};
+        a.backward = true;
+        a.V = (int)s.V;
+        a.R = 0;
+        a.dw = dln_w; a.db = dln_b;
+        a.stream = strm;
+        const hipError_t err = gla::launch_out_gate(a);
+        if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+        return GLA_OK;
+    }
+    if (!o || !z || !ln_w || !dy || !d_o || !dz)
+        return fail(GLA_ERR_NULL, "o, z, ln_w, dy, d_o and dz are required");
+    const void* ptrs[] = {o, z, ln_w, ln_b, dy, d_o, dz, dln_w, dln_b, workspace};
+    const char* names[] = {"o", "z", "ln_w", "ln_b", "dy", "d_o", "dz", "dln_w", "dln_b", "workspace"};
+    for (int i = 0; i < 10; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    if (!workspace || workspace_bytes < need)
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    gla::GateLaunch a{};
+    a.bf16 = s.bf16;
+    a.backward = true;
+    a.V = (int)s.V;
+    a.R = R;
+    a.o = o; a.z = z; a.w = ln_w; a.b = ln_b; a.eps = eps;
+    a.dy = dy; a.dx = d_o; a.dz = dz; a.dw = dln_w; a.db = dln_b;
+    a.ws = static_cast<float*>(workspace);
+    a.stream = strm;
+    const hipError_t err = gla::launch_out_gate(a);
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
 }

@@ -109,3 +109,26 @@ def make_inputs(w: Workload, device: Optional[str] = None, dht: bool = False) ->
     if device is not None:
         out = {kk: (vv.to(device) if vv is not None else None) for kk, vv in out.items()}
     return out
+
+
+def make_gate_inputs(B: int, T: int, H: int, V: int, dtype: str = "bf16", seed: int = 0, bias: bool = True,
+                     device: Optional[str] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs of the GLA layer's output epilogue (per-head LayerNorm, Swish gate).
+
+    Drawn in float32 on the CPU in the order o, z, ln_w, ln_b, dy:
+      o  ~ N(0,1) / sqrt(V)   [B,T,H,V]  (the scale of an attention output row)
+      z  ~ N(0,1)             [B,T,H,V]  (the gate's pre-activation x W_r + b_r)
+      ln_w ~ 1 + N(0,1)/10, ln_b ~ N(0,1)/10   [V] float32 (never cast)
+      dy ~ N(0,1)             [B,T,H,V]
+    o, z and dy are cast to ``dtype``; ln_b is None when ``bias`` is false."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    o = (torch.randn(B, T, H, V, generator=gen) / V ** 0.5).to(dt)
+    z = torch.randn(B, T, H, V, generator=gen).to(dt)
+    w = 1.0 + torch.randn(V, generator=gen) / 10
+    b = torch.randn(V, generator=gen) / 10
+    dy = torch.randn(B, T, H, V, generator=gen).to(dt)
+    out = {"o": o, "z": z, "ln_w": w, "ln_b": b if bias else None, "dy": dy}
+    if device is not None:
+        out = {k: (v.to(device) if v is not None else None) for k, v in out.items()}
+    return out

@@ -140,6 +140,48 @@ gla_status_t gla_decode(const gla_shape_t* shape,
                         const void* q, const void* k, const void* v, const void* g,
                         float* state, void* o, void* stream);
 
+/*
+ * gla_out_gate -- the output epilogue of the multi-head GLA layer (Section 4.4,
+ * "GLA Transformer"): every head's output row is normalised by LayerNorm on its
+ * own, then multiplied elementwise by the Swish output gate r = Swish(z),
+ *     y[b,t,h,:] = Swish(z[b,t,h,:]) * (LN(o[b,t,h,:]) * ln_w + ln_b),
+ *     LN(x) = (x - mean(x)) / sqrt(var(x) + eps)   (mean and biased variance
+ *             over the row's V channels),   Swish(z) = z / (1 + exp(-z)).
+ * z is the gate's pre-activation x W_r + b_r; that projection is a plain GEMM
+ * and not part of this call.  Only B, T, H, V and dtype of `shape` are used
+ * (K and chunk are ignored; T need not be a multiple of 64).
+ *   o, z    : [B,T,H,V] dtype inputs;  y : [B,T,H,V] dtype output
+ *   ln_w    : [V] float32 scale shared by the heads (required)
+ *   ln_b    : [V] float32 shift, or NULL for zero
+ *   eps     : finite, >= 0 (a row with zero variance and eps == 0 gives
+ *             non-finite values)
+ *   stream  : as for gla_fwd.  No workspace.
+ * Supported: V in {64, 128, 256, 512}, bf16 or fp32.  B*T*H == 0 is a no-op.
+ * Returns GLA_OK or an error code.
+ */
+gla_status_t gla_out_gate(const gla_shape_t* shape, const void* o, const void* z,
+                          const float* ln_w, const float* ln_b, float eps, void* y, void* stream);
+
+/*
+ * gla_out_gate_bwd -- gradients of <y, dy> for gla_out_gate with respect to o,
+ * z, ln_w and ln_b.  The ln_w and ln_b gradients are sums over all B*T*H rows,
+ * formed per workgroup and then added in a fixed order (deterministic).
+ *   o, z, ln_w, ln_b, eps : as for gla_out_gate
+ *   dy      : [B,T,H,V] dtype upstream gradient of y
+ *   d_o, dz : [B,T,H,V] dtype outputs (required)
+ *   dln_w, dln_b : [V] float32 outputs, either may be NULL to skip
+ *   workspace : at least gla_out_gate_bwd_workspace_size(shape) bytes
+ * B*T*H == 0 writes zero column sums.  Returns GLA_OK or an error code.
+ */
+gla_status_t gla_out_gate_bwd(const gla_shape_t* shape, const void* o, const void* z,
+                              const float* ln_w, const float* ln_b, float eps, const void* dy,
+                              void* d_o, void* dz, float* dln_w, float* dln_b,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gla_out_gate_bwd needs (depends on V only; 0 for an
+ * invalid shape).  A pure function of the shape: it makes no HIP call. */
+size_t gla_out_gate_bwd_workspace_size(const gla_shape_t* shape);
+
 /* Static description of a status code (never NULL). */
 const char* gla_status_string(gla_status_t status);
 

@@ -54,6 +54,11 @@ def _load():
     lib.oracle_gla_bwd.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_gla_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_out_gate_fwd.argtypes = [L, L, dp, dp, dp, dp, D, dp]
+    lib.oracle_out_gate_fwd.restype = ctypes.c_int
+    lib.oracle_out_gate_bwd.argtypes = [L, L, dp, dp, dp, dp, D, dp, dp, dp, dp, dp]
+    lib.oracle_out_gate_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -126,3 +131,46 @@ def gla_bwd(q, k, v, g, d_o, s0=None, dht=None):
     if rc != 0:
         raise RuntimeError("oracle_gla_bwd failed with code %d" % rc)
     return dq, dk, dv, dg, ds0
+
+
+def out_gate(o, z, w, b=None, eps=1e-5) -> np.ndarray:
+    """GLA layer output epilogue in fp64: y = Swish(z) * (LN(o) * w + b), per row.
+
+    Follows "Gated Linear Attention Transformers with Hardware-Efficient
+    Training", Section 4.4: LayerNorm of each head's output row over its V
+    channels (mean, biased variance, eps inside the square root), per-channel
+    scale w and shift b shared by the heads, times r = Swish(z), z the gate's
+    pre-activation.  o, z: [..., V]; w, b: [V].
+    Pinned by: torch float64 layer_norm and silu (library routines), shift
+    invariance, a constant row giving y = b * Swish(z), unit row moments with
+    w = 1, b = 0.
+    """
+    o, z, w = _as_f64(o), _as_f64(z), _as_f64(w)
+    b = _as_f64(b)
+    V = o.shape[-1]
+    assert z.shape == o.shape and w.shape == (V,) and (b is None or b.shape == (V,))
+    R = o.size // V
+    y = np.zeros_like(o)
+    rc = _load().oracle_out_gate_fwd(R, V, _ptr(o), _ptr(z), _ptr(w), _ptr(b), float(eps), _ptr(y))
+    if rc != 0:
+        raise RuntimeError("oracle_out_gate_fwd failed with code %d" % rc)
+    return y
+
+
+def out_gate_bwd(o, z, w, b, eps, dy):
+    """Reverse-mode gradient of <y, dy> for out_gate: (do, dz, dw, db), fp64.
+
+    The chain rule taken step by step through the forward as written.  Pinned
+    by: central finite differences and torch float64 autograd of layer_norm and
+    silu.
+    """
+    o, z, w, dy = _as_f64(o), _as_f64(z), _as_f64(w), _as_f64(dy)
+    b = _as_f64(b)
+    V = o.shape[-1]
+    R = o.size // V
+    dx = np.zeros_like(o); dz = np.zeros_like(o); dw = np.zeros(V); db = np.zeros(V)
+    rc = _load().oracle_out_gate_bwd(R, V, _ptr(o), _ptr(z), _ptr(w), _ptr(b), float(eps), _ptr(dy), _ptr(dx),
+                                     _ptr(dz), _ptr(dw), _ptr(db))
+    if rc != 0:
+        raise RuntimeError("oracle_out_gate_bwd failed with code %d" % rc)
+    return dx, dz, dw, db

@@ -224,3 +224,84 @@ int oracle_gla_bwd(long B, long T, long H, long K, long V,
     }
     return err;
 }
+
+/* ------------------------------------------------------------------------
+ * Output epilogue of the multi-head GLA layer (Section 4.4, "GLA
+ * Transformer"): each head's output row o (V channels) goes through
+ * LayerNorm on its own, and the result is multiplied elementwise by the
+ * output gate r = Swish(z), z being the gate's pre-activation x W_r + b_r:
+ *     mu = mean_j o_j,  var = mean_j (o_j - mu)^2,  n_j = (o_j - mu) / sqrt(var + eps),
+ *     a_j = n_j w_j + b_j,  y_j = a_j * z_j * sigmoid(z_j).
+ * w and b (length V) are shared by every row; b may be NULL (zero).
+ * Rows are R = B*T*H contiguous runs of V values.
+ */
+static double sigmoid_d(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+int oracle_out_gate_fwd(long R, long V, const double *o, const double *z, const double *w, const double *b,
+                        double eps, double *y) {
+    if (R < 0 || V <= 0 || !o || !z || !w || !y) return 1;
+    for (long r = 0; r < R; ++r) {
+        const double *x = o + r * V;
+        double mu = 0.0, var = 0.0;
+        for (long j = 0; j < V; ++j) mu += x[j];
+        mu /= (double)V;
+        for (long j = 0; j < V; ++j) var += (x[j] - mu) * (x[j] - mu);
+        var /= (double)V;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (long j = 0; j < V; ++j) {
+            const double a = (x[j] - mu) * inv * w[j] + (b ? b[j] : 0.0);
+            const double zj = z[r * V + j];
+            y[r * V + j] = a * zj * sigmoid_d(zj);
+        }
+    }
+    return 0;
+}
+
+/* Reverse-mode gradient of the loss sum_{r,j} dy_{r,j} y_{r,j} for the function
+ * above, by the chain rule through each step as written:
+ *   y = a * s with s = z sigmoid(z):   da = dy s,   dz = dy a s'(z),
+ *       s'(z) = sigmoid(z) + z sigmoid(z) (1 - sigmoid(z));
+ *   a = n w + b:                        dw += da n,  db += da,  dn = da w;
+ *   n = (x - mu) inv, inv = (var + eps)^(-1/2):
+ *       dinv = sum_j dn_j (x_j - mu),   dvar = -dinv inv^3 / 2,
+ *       dx_j = dn_j inv + dvar 2 (x_j - mu) / V + dmu / V,
+ *       dmu = -inv sum_j dn_j - dvar 2 sum_j (x_j - mu) / V  (the last sum is 0).
+ * dw and db are summed over all rows (either may be NULL). */
+int oracle_out_gate_bwd(long R, long V, const double *o, const double *z, const double *w, const double *b,
+                        double eps, const double *dy, double *dx, double *dz, double *dw, double *db) {
+    if (R < 0 || V <= 0 || !o || !z || !w || !dy || !dx || !dz) return 1;
+    if (dw) for (long j = 0; j < V; ++j) dw[j] = 0.0;
+    if (db) for (long j = 0; j < V; ++j) db[j] = 0.0;
+    double *dn = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!dn) return 2;
+    for (long r = 0; r < R; ++r) {
+        const double *x = o + r * V;
+        double mu = 0.0, var = 0.0;
+        for (long j = 0; j < V; ++j) mu += x[j];
+        mu /= (double)V;
+        for (long j = 0; j < V; ++j) var += (x[j] - mu) * (x[j] - mu);
+        var /= (double)V;
+        const double inv = 1.0 / sqrt(var + eps);
+        double dinv = 0.0, sdn = 0.0;
+        for (long j = 0; j < V; ++j) {
+            const double n = (x[j] - mu) * inv;
+            const double a = n * w[j] + (b ? b[j] : 0.0);
+            const double zj = z[r * V + j], sg = sigmoid_d(zj);
+            const double s = zj * sg;
+            const double g = dy[r * V + j];
+            const double da = g * s;
+            dz[r * V + j] = g * a * (sg + zj * sg * (1.0 - sg));
+            if (dw) dw[j] += da * n;
+            if (db) db[j] += da;
+            dn[j] = da * w[j];
+            dinv += dn[j] * (x[j] - mu);
+            sdn += dn[j];
+        }
+        const double dvar = -0.5 * dinv * inv * inv * inv;
+        const double dmu = -inv * sdn;
+        for (long j = 0; j < V; ++j)
+            dx[r * V + j] = dn[j] * inv + dvar * 2.0 * (x[j] - mu) / (double)V + dmu / (double)V;
+    }
+    free(dn);
+    return 0;
+}

@@ -119,3 +119,38 @@ def test_decode_validation_codes(L):
     assert _dec(L, _shape(T=5, reserved=1)) == ERR_UNSUPPORTED
     assert _dec(L, _shape(T=5), state=ctypes.c_void_p(0x10004)) == ERR_ALIGN
     assert b"state" in L.gla_last_error_detail()
+
+
+def _gate(L, shape, o=P, z=P, w=P, b=None, eps=1e-5, y=P):
+    return L.gla_out_gate(ctypes.byref(shape) if shape is not None else None, o, z, w, b, eps, y, None)
+
+
+def _gate_bwd(L, shape, o=P, z=P, w=P, b=None, eps=1e-5, dy=P, dx=P, dz=P, dw=P, db=None, ws=P, wsb=1 << 30):
+    return L.gla_out_gate_bwd(ctypes.byref(shape) if shape is not None else None, o, z, w, b, eps, dy, dx, dz, dw,
+                              db, ws, wsb, None)
+
+
+def test_out_gate_validation_codes(L):
+    # rows of V channels; K and chunk are not used, T need not be a multiple of 64
+    assert _gate(L, None) == ERR_NULL
+    assert _gate(L, _shape(T=0)) == OK
+    assert _gate(L, _shape(B=0, T=5, chunk=7, K=3)) == OK
+    assert _gate(L, _shape(T=5), z=None) == ERR_NULL
+    assert _gate(L, _shape(T=5), w=None) == ERR_NULL
+    assert _gate(L, _shape(T=-1)) == ERR_SHAPE
+    assert _gate(L, _shape(T=5, V=96)) == ERR_UNSUPPORTED
+    assert _gate(L, _shape(T=5, dtype=7)) == ERR_UNSUPPORTED
+    assert _gate(L, _shape(T=5), eps=-1.0) == ERR_UNSUPPORTED
+    assert _gate(L, _shape(T=5), eps=float("nan")) == ERR_UNSUPPORTED
+    assert _gate(L, _shape(T=5), y=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert b"y" in L.gla_last_error_detail()
+    # backward: inputs, outputs and the workspace are checked before any launch
+    ws = L.gla_out_gate_bwd_workspace_size(ctypes.byref(_shape(T=5, V=256)))
+    assert ws >= 2 * 256 * 256 * 4
+    assert L.gla_out_gate_bwd_workspace_size(ctypes.byref(_shape(T=5, V=96))) == 0
+    assert _gate_bwd(L, _shape(T=0), dw=None) == OK
+    assert _gate_bwd(L, _shape(T=5), dz=None) == ERR_NULL
+    assert _gate_bwd(L, _shape(T=5), ws=None) == ERR_WORKSPACE
+    assert _gate_bwd(L, _shape(T=5), wsb=16) == ERR_WORKSPACE
+    assert _gate_bwd(L, _shape(T=5), dw=ctypes.c_void_p(0x10004)) == ERR_ALIGN
+    assert _gate_bwd(L, _shape(T=5, V=1024)) == ERR_UNSUPPORTED
