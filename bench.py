@@ -31,24 +31,29 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6
 FP32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = "GLA fwd(+bwd) tokens/sec at T=8K, dk=128, dv=256; % of bf16 MFMA peak"
+METRIC_SCALAR = "GLA scalar-gate fwd+bwd tokens/sec at T=8K, dk=128, dv=256"
 
 
-def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int, dv_split: bool = False):
+def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int, dv_split: bool = False,
+                             G: int = None):
     """Algorithmic HBM bytes per (token, head) of one launch of `kernel`.
 
-    The backward's segment-state pass reads q, g, d_o of every segment instead of
-    all but the first when the dv walk takes segments in halves (it then also
-    needs each segment's midpoint state)."""
+    G is the number of log-gate values per token and head (K for per-column
+    gates, 1 for a scalar gate; g and dg have G elements).  The backward's
+    segment-state pass reads q, g, d_o of every segment instead of all but the
+    first when the dv walk takes segments in halves (it then also needs each
+    segment's midpoint state)."""
+    G = K if G is None else G
     seg_frac = (P - 1) / P if P > 1 else 0.0
     seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
     table = {
-        "fwd_walk": e * (3 * K + 2 * V),            # q, k, g, v read; o written
-        "bwd_dq_walk": e * (3 * K + 2 * V),         # k, g, v, d_o read; dq written
-        "bwd_dk_walk": e * (6 * K + 2 * V),         # q, k, g, dq, v, d_o read; dk, dg written
-        "bwd_dv_walk": e * (3 * K + 2 * V),         # q, k, g, d_o read; dv written
-        "fwd_seg_state": e * (2 * K + V) * seg_frac,  # k, g, v of all but the last segment
+        "fwd_walk": e * (2 * K + G + 2 * V),            # q, k, g, v read; o written
+        "bwd_dq_walk": e * (2 * K + G + 2 * V),         # k, g, v, d_o read; dq written
+        "bwd_dk_walk": e * (4 * K + 2 * G + 2 * V),     # q, k, g, dq, v, d_o read; dk, dg written
+        "bwd_dv_walk": e * (2 * K + G + 2 * V),         # q, k, g, d_o read; dv written
+        "fwd_seg_state": e * (K + G + V) * seg_frac,    # k, g, v of all but the last segment
         # k, g, v of all but the last segment and q, g, d_o of all but the first (or all)
-        "bwd_seg_states": e * (2 * K + V) * (seg_frac_bwd + (1.0 if dv_split else seg_frac_bwd)),
+        "bwd_seg_states": e * (K + G + V) * (seg_frac_bwd + (1.0 if dv_split else seg_frac_bwd)),
     }
     return table.get(kernel)
 
@@ -137,20 +142,25 @@ def load_traffic(workload: str, kernel: str, units: int):
     return k.get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, w, n_heads):
+def cpu_baseline(inputs, w, n_heads, scalar_gate=False):
     """fp64 oracle forward + backward on n_heads full-length heads of the workload."""
     import numpy as np
     import oracle
 
     heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
     f64 = lambda t: t.detach().cpu().double().numpy()
-    pick = lambda a: np.stack([a[b, :, h, :] for b, h in heads])[:, :, None, :]
+    pick = lambda a: (np.stack([a[b, :, h] for b, h in heads])[:, :, None] if a.ndim == 3 else
+                      np.stack([a[b, :, h, :] for b, h in heads])[:, :, None, :])
     q, k, v, g, do = (pick(f64(inputs[n])) for n in ("q", "k", "v", "g", "do"))
     threads = min(oracle.num_threads(), len(heads))
     os.environ["OMP_NUM_THREADS"] = str(threads)
     t0 = time.perf_counter()
-    oracle.gla_fwd(q, k, v, g, None)
-    oracle.gla_bwd(q, k, v, g, do, None, None)
+    if scalar_gate:
+        oracle.gla_fwd_scalar(q, k, v, g, None)
+        oracle.gla_bwd_scalar(q, k, v, g, do, None, None)
+    else:
+        oracle.gla_fwd(q, k, v, g, None)
+        oracle.gla_bwd(q, k, v, g, do, None, None)
     dt = time.perf_counter() - t0
     tokens_equiv = len(heads) * w.T / w.H  # a token of the workload carries H heads
     return {
@@ -292,6 +302,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--decode", action="store_true",
                     help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
+    ap.add_argument("--scalar-gate", action="store_true",
+                    help="the workload with one log gate per token and head (gla_fwd_scalar / gla_bwd_scalar)")
     ap.add_argument("--out-gate", action="store_true",
                     help="measure the output epilogue (LayerNorm + Swish gate, fwd + bwd) on the metric "
                          "workload's output rows instead")
@@ -328,6 +340,9 @@ def main():
         return
 
     w = gi.WORKLOADS[args.workload]
+    sg = args.scalar_gate
+    if sg:  # same shape, seed and draws, with the scalar gate recipe
+        w = gi.Workload(w.name, w.B, w.H, w.T, w.K, w.V, w.dtype, "scalar", w.v_scale, w.s0, w.backward, w.seed)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
@@ -339,17 +354,20 @@ def main():
     d = {k: (v.to(dev) if v is not None else None) for k, v in cpu_inputs.items()}
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
     sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
-    dq, dk, dg = (torch.empty(B, T, H, K, dtype=dt, device=dev) for _ in range(3))
+    dq, dk = (torch.empty(B, T, H, K, dtype=dt, device=dev) for _ in range(2))
+    dg = torch.empty(*d["g"].shape, dtype=dt, device=dev)
     dv = torch.empty(B, T, H, V, dtype=dt, device=dev)
     ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
     wsf = gla.workspace(gla.gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
-    wsb = gla.workspace(gla.gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
+    wsb = gla.workspace((gla.gla_bwd_scalar_workspace_size if sg else gla.gla_bwd_workspace_size)(
+        B, T, H, K, V, dt), dev)
 
     def fwd():
-        gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, wsf)
+        gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, wsf, scalar_gate=sg)
 
     def bwd():
-        gla.gla_bwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], d["do"], None, dq, dk, dv, dg, ds0, wsb)
+        gla.gla_bwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], d["do"], None, dq, dk, dv, dg, ds0, wsb,
+                         scalar_gate=sg)
 
     def step():
         fwd()
@@ -395,12 +413,13 @@ def main():
     P = plan_segments(B, H, T, K, V, w.dtype == "bf16")
     P_bwd = plan_segments_bwd(B, H, T, K, V, w.dtype == "bf16")
     units = B * T * H
-    bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd, plan_dv_split(B, H, T, K, V, w.dtype == "bf16"))
+    bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd, plan_dv_split(B, H, T, K, V, w.dtype == "bf16"),
+                                   G=1 if sg else K)
     roofline = None
     if bpt is not None:
         ach = bpt * units / (kern[dom]["avg_us"] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic(w.name, dom, units),
+                    "frac": ach / HBM_PEAK_GBS, "traffic": None if sg else load_traffic(w.name, dom, units),
                     "alg_bytes_per_launch": bpt * units}
 
     tokens = B * T
@@ -408,7 +427,7 @@ def main():
     fwd_flops = fwd_flops_per_token_head(K, V) * units
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     out = {
-        "metric": METRIC,
+        "metric": METRIC_SCALAR if sg else METRIC,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -420,8 +439,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, gla_fwd + gla_bwd per step" % (
-            w.name, B, H, T, K, V, w.dtype), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
+        "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, %s per step" % (
+            w.name, B, H, T, K, V, w.dtype, "scalar gate [B,T,H], gla_fwd_scalar + gla_bwd_scalar" if sg else
+            "gla_fwd + gla_bwd"), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
             "chunk": 64, "segments": P},
         "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
         "bwd_tokens_per_s": tokens / (ms_bwd * 1e-3),
@@ -431,13 +451,13 @@ def main():
         "fwd_mfma_frac": fwd_flops / (ms_fwd * 1e-3) / (peak_tf * 1e12),
         "fwdbwd_mfma_frac": (fwd_flops + bwd_flops_per_token_head(K, V) * units) / (ms_step * 1e-3) /
                             (peak_tf * 1e12),
-        "fwd_hbm_frac": e * (3 * K + 2 * V) * units / (ms_fwd * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "fwd_hbm_frac": e * (2 * K + (1 if sg else K) + 2 * V) * units / (ms_fwd * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "kernels": kern,
         "roofline": roofline,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cpu_inputs, w, args.cpu_heads)
+        out["cpu_baseline"] = cpu_baseline(cpu_inputs, w, args.cpu_heads, scalar_gate=sg)
     print(json.dumps(out), flush=True)
 
 

@@ -9,6 +9,7 @@ exception is raised.
 Functions mirror the ABI:
   gla_fwd(q, k, v, g, s0=None, ...)         -> (o, s_final)
   gla_bwd(q, k, v, g, d_o, s0=None, dht=None) -> (dq, dk, dv, dg, ds0)
+  gla_fwd_scalar / gla_bwd_scalar            (the same with a scalar gate g [B,T,H] per token and head)
   gla_decode(q, k, v, g, state)              -> o   (recurrent form; state updated in place)
   gla_out_gate(o, z, ln_w, ln_b, eps)        -> y   (per-head LayerNorm, Swish output gate)
   gla_out_gate_bwd(o, z, ln_w, ln_b, eps, dy) -> (d_o, dz, dln_w, dln_b)
@@ -43,8 +44,9 @@ class GlaError(RuntimeError):
         self.status = status
 
 
-EXPORTS = ["gla_fwd", "gla_bwd", "gla_decode", "gla_out_gate", "gla_out_gate_bwd",
-           "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_out_gate_bwd_workspace_size",
+EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode", "gla_out_gate",
+           "gla_out_gate_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_bwd_scalar_workspace_size",
+           "gla_out_gate_bwd_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
            "gla_kernel_timing", "gla_kernel_timing_read"]
 
@@ -66,6 +68,12 @@ def lib():
     L.gla_fwd.restype = ctypes.c_int
     L.gla_bwd.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gla_bwd.restype = ctypes.c_int
+    L.gla_fwd_scalar.argtypes = L.gla_fwd.argtypes
+    L.gla_fwd_scalar.restype = ctypes.c_int
+    L.gla_bwd_scalar.argtypes = L.gla_bwd.argtypes
+    L.gla_bwd_scalar.restype = ctypes.c_int
+    L.gla_bwd_scalar_workspace_size.argtypes = [sh]
+    L.gla_bwd_scalar_workspace_size.restype = ctypes.c_size_t
     L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
     L.gla_decode.restype = ctypes.c_int
     fl = ctypes.c_float
@@ -146,22 +154,28 @@ def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def gla_fwd_into(q, k, v, g, s0, o, s_final, ws, stream=None):
-    """Call the ABI with caller-owned outputs and workspace (nothing allocated)."""
+def gla_fwd_into(q, k, v, g, s0, o, s_final, ws, stream=None, scalar_gate=False):
+    """Call the ABI with caller-owned outputs and workspace (nothing allocated).
+    scalar_gate: g is [B,T,H] and gla_fwd_scalar is called."""
     B, T, H, K, V = _dims(q, v)
     shape = make_shape(B, T, H, K, V, q.dtype)
     nbytes = 0 if ws is None else ws.numel()
-    _check(lib().gla_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o),
-                         _ptr(s_final), _ptr(ws), nbytes, _stream(stream)))
+    fn = lib().gla_fwd_scalar if scalar_gate else lib().gla_fwd
+    _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(ws),
+              nbytes, _stream(stream)))
 
 
-def gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream=None):
+def gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream=None, scalar_gate=False):
     B, T, H, K, V = _dims(q, v)
     shape = make_shape(B, T, H, K, V, q.dtype)
     nbytes = 0 if ws is None else ws.numel()
-    _check(lib().gla_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(d_o),
-                         _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ds0), _ptr(ws), nbytes,
-                         _stream(stream)))
+    fn = lib().gla_bwd_scalar if scalar_gate else lib().gla_bwd
+    _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(d_o), _ptr(dht), _ptr(dq),
+              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ds0), _ptr(ws), nbytes, _stream(stream)))
+
+
+def gla_bwd_scalar_workspace_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_bwd_scalar_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
 
 
 def gla_fwd(q, k, v, g, s0=None, output_final_state=True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -192,6 +206,36 @@ def gla_bwd(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
     ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
     ws = workspace(gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
     gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream)
+    return dq, dk, dv, dg, ds0
+
+
+def gla_fwd_scalar(q, k, v, g, s0=None, output_final_state=True, stream=None):
+    """gla_fwd with a scalar gate g [B,T,H] per token and head (bf16)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H)), ("v", v, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    ws = workspace(gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+    gla_fwd_into(q, k, v, g, s0, o, sf, ws, stream, scalar_gate=True)
+    return o, sf
+
+
+def gla_bwd_scalar(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
+    """gla_bwd with a scalar gate g [B,T,H]; dg is [B,T,H] (bf16)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),
+                         ("v", v, (B, T, H, V)), ("d_o", d_o, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    _need(dht, "dht", (B, H, K, V), torch.float32, dev)
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dg = torch.empty_like(g); dv = torch.empty_like(v)
+    ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
+    ws = workspace(gla_bwd_scalar_workspace_size(B, T, H, K, V, dt), dev)
+    gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream, scalar_gate=True)
     return dq, dk, dv, dg, ds0
 
 

@@ -73,7 +73,7 @@ gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out, bool backward) {
     return GLA_OK;
 }
 
-size_t bwd_workspace_bytes(const gla::Shape& s);
+size_t bwd_workspace_bytes(const gla::Shape& s, bool sg);
 
 // The recurrent decode step: any T >= 0, the chunk field unused.
 gla_status_t check_decode_shape(const gla_shape_t* s, gla::Shape* out) {
@@ -126,46 +126,14 @@ gla_status_t check_gate_shape(const gla_shape_t* s, gla::Shape* out) {
 
 bool eps_ok(float eps) { return eps >= 0.f && eps <= 3.0e38f; }  // false for NaN and infinities
 
-}  // namespace
-
-extern "C" {
-
-int gla_abi_version(void) { return GLA_ABI_VERSION; }
-
-const char* gla_status_string(gla_status_t st) {
-    switch (st) {
-        case GLA_OK: return "GLA_OK: success";
-        case GLA_ERR_NULL: return "GLA_ERR_NULL: a required pointer is NULL";
-        case GLA_ERR_SHAPE: return "GLA_ERR_SHAPE: invalid problem size";
-        case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED: head dims, chunk or dtype not supported";
-        case GLA_ERR_ALIGN: return "GLA_ERR_ALIGN: pointer not 16-byte aligned";
-        case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace missing or too small";
-        case GLA_ERR_HIP: return "GLA_ERR_HIP: HIP runtime error";
-    }
-    return "unknown gla_status_t";
-}
-
-const char* gla_last_error_detail(void) { return g_detail.c_str(); }
-
-size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
-    gla::Shape s;
-    if (check_shape(shape, &s, false) != GLA_OK) return 0;
-    return gla::fwd_workspace_bytes(s);
-}
-
-size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
-    gla::Shape s;
-    if (check_shape(shape, &s, true) != GLA_OK) return 0;
-    return bwd_workspace_bytes(s);
-}
-
-gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
-                     const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                      const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                      void* stream, bool sg) {
     g_detail.clear();
     gla::Shape s;
     gla_status_t st = check_shape(shape, &s, false);
     if (st != GLA_OK) return st;
+    if (sg && !s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !o)) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
     const void* ptrs[] = {q, k, v, g, s0, o, s_final, workspace};
@@ -185,6 +153,7 @@ gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, con
         gla::Plan p = gla::make_fwd_plan(s);
         gla::FwdLaunch a{};
         a.bf16 = s.bf16;
+        a.sg = sg;
         a.K = (int)s.K;
         a.V = (int)s.V;
         a.BV = p.BV;
@@ -209,13 +178,14 @@ gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, con
     return GLA_OK;
 }
 
-gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
-                     const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
-                     float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
+gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                      const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                      float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg) {
     g_detail.clear();
     gla::Shape s;
     gla_status_t st = check_shape(shape, &s, true);
     if (st != GLA_OK) return st;
+    if (sg && !s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg))
         return fail(GLA_ERR_NULL, "q, k, v, g, d_o, dq, dk, dv and dg are required");
@@ -223,7 +193,7 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
     const char* names[] = {"q", "k", "v", "g", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "ds0", "workspace"};
     for (int i = 0; i < 13; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const size_t need = empty ? 0 : bwd_workspace_bytes(s);
+    const size_t need = empty ? 0 : bwd_workspace_bytes(s, sg);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -236,6 +206,7 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
         gla::BwdLaunch a{};
         gla::Plan p = gla::make_bwd_plan(s);
         a.bf16 = s.bf16;
+        a.sg = sg;
         a.K = (int)s.K;
         a.V = (int)s.V;
         a.BV = p.BV;
@@ -267,11 +238,76 @@ gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, con
             a.ws_dmid = mid;
             a.ws_gmid = reinterpret_cast<float*>(mid + sb);
         }
+        // scalar gate: each key block's per-token sum of dg, after everything else
+        if (sg) a.ws_dgp = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, false));
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_abi_version(void) { return GLA_ABI_VERSION; }
+
+const char* gla_status_string(gla_status_t st) {
+    switch (st) {
+        case GLA_OK: return "GLA_OK: success";
+        case GLA_ERR_NULL: return "GLA_ERR_NULL: a required pointer is NULL";
+        case GLA_ERR_SHAPE: return "GLA_ERR_SHAPE: invalid problem size";
+        case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED: head dims, chunk or dtype not supported";
+        case GLA_ERR_ALIGN: return "GLA_ERR_ALIGN: pointer not 16-byte aligned";
+        case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace missing or too small";
+        case GLA_ERR_HIP: return "GLA_ERR_HIP: HIP runtime error";
+    }
+    return "unknown gla_status_t";
+}
+
+const char* gla_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, false) != GLA_OK) return 0;
+    return gla::fwd_workspace_bytes(s);
+}
+
+size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, true) != GLA_OK) return 0;
+    return bwd_workspace_bytes(s, false);
+}
+
+size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, true) != GLA_OK || !s.bf16) return 0;
+    return bwd_workspace_bytes(s, true);
+}
+
+gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                     const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, false);
+}
+
+gla_status_t gla_fwd_scalar(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                            const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, true);
+}
+
+gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                     const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                     float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(shape, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes, stream, false);
+}
+
+gla_status_t gla_bwd_scalar(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                            const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                            void* dg, float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(shape, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes, stream, true);
 }
 
 gla_status_t gla_decode(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
@@ -386,15 +422,17 @@ gla_status_t gla_out_gate_bwd(const gla_shape_t* shape, const void* o, const voi
 }  // extern "C"
 
 namespace {
-size_t bwd_workspace_bytes(const gla::Shape& s) {
+size_t bwd_workspace_bytes(const gla::Shape& s, bool sg) {
     gla::Plan p = gla::make_bwd_plan(s);
     if (p.BH == 0) return 0;
+    // scalar gate: each key block's fp32 per-token sum of dg, after the rest
+    const size_t dgp = sg ? gla::round256((size_t)(s.K / p.BK) * p.BH * p.N * 64 * sizeof(float)) : 0;
     const size_t kk = (size_t)p.BH * p.P * s.K;
     // 16-bit inputs: the dq walk's dP tiles for the dk walk, and (split dv
     // walk) the segments' midpoint states and half gate totals
     const size_t dp = s.bf16 ? gla::round256((size_t)p.BH * p.N * 64 * 64 * 2) : 0;
     const size_t mid = gla::dv_split(s, p) == 2 ? gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) : 0;
     return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + gla::round256(gla::hs_bytes(s, p)) + dp +
-           mid;
+           mid + dgp;
 }
 }  // namespace

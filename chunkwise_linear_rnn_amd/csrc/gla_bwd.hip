@@ -390,6 +390,7 @@ struct RowPipeSmem {
     alignas(16) f32x4 red[RR::VS > 1 ? RR::NKQ * RR::VS * RR::NB * 64 : 1];  // [key block][reader slice][slot][lane]
     float carry[RR::VS * BK];
     alignas(16) float tot[4 * BK];  // dk walk: per token block, the column totals of dA
+    float sgt[RR::NKQ * kChunk];    // dk walk, scalar gate: each 16-column block's sum of dg per token
 };
 
 // One wave prepares key columns kc0 .. kc0+NC-1 of a chunk (lane = token row)
@@ -398,13 +399,37 @@ struct RowPipeSmem {
 // the chunk-start basis, k * exp2(-B_s), or k * exp2(B_63 - B_s) beyond
 // kBasisLimit) and the state-update factors.  QL operands never exceed 1 in
 // magnitude factor, so (pre, post) = (gamma, 1) for them.  The chunk is flagged
-// for the exact path if a column's decay exceeds kBasisLimit.
-template <typename T, int NC, bool QL, typename Buf>
-__device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<T, NC>& rx, const RowSlab<T, NC>& rg,
-                                         int kc0) {
+// for the exact path if a column's decay exceeds kBasisLimit.  A scalar gate
+// (GS::scalar) has one cumulative gate per token, shared by every column.
+template <typename T, int NC, bool QL, typename Buf, typename GS>
+__device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<T, NC>& rx, const GS& rg, int kc0) {
     constexpr int VEC = 16 / (int)sizeof(T);
     static_assert(NC <= 64, "one lane per prepared column");
     const int l = lane_id();
+    if constexpr (GS::scalar) {
+        const float bt = wave_incl_scan(rg.get(0) * kLog2e);
+        const float bl = lane_bcast(bt, 63);
+        const bool in = -bl <= kBasisLimit;
+        const float f = QL ? exp2_fast(bt) : exp2_fast((in ? 0.f : bl) - bt);
+#pragma unroll
+        for (int j0 = 0; j0 < NC; j0 += VEC) {
+            float xv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) xv[e] = rx.get(j0 + e) * f;
+            store_vec_lds<T>(bf.K + l * pK + kc0 + j0, xv);
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+                *reinterpret_cast<f32x4*>(bf.B + l * pB + kc0 + j0 + e) = f32x4{bt, bt, bt, bt};
+        }
+        if (l < NC) {
+            const float gm = exp2_fast(bl);
+            const bool pin = QL || in;
+            bf.pre[kc0 + l] = pin && !QL ? 1.f : gm;
+            bf.post[kc0 + l] = pin && !QL ? gm : 1.f;
+        }
+        if (!in && l == 0) bf.flag[0] = 1;
+        return;
+    }
     float last_l = 0.f;
     bool wide = false;
 #pragma unroll
@@ -448,7 +473,7 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
 // the dk walk (first key block only); then each wave, for its two token blocks
 // (RowRoles::block), dP Kt, the slice reduction, the factor exp2(B_t) and the
 // store of dq; the next chunk's V and d_o tiles.
-template <typename T, int BK, int V, int NW>
+template <typename T, int BK, int V, int NW, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
                 const T* __restrict__ ws_init, const float* __restrict__ s0, T* __restrict__ dq,
@@ -485,13 +510,16 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     else if (s0) S.load(s0 + (long)bh * K * V + (long)k0 * V, V, i0, j0);
     else S.zero();
 
-    RowSlab<T, CPK> rk, rg;
+    RowSlab<T, CPK> rk;
+    GateSlab<T, CPK, SG> rg;
     using TRV = TileRegs<T, V, NT>;
     TRV rv, rdo;
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    auto gbase = [&](int c) { return SG ? g + ((long)b * T_ + (long)c * kChunk) * H + h : kbase(g, c); };
+    const int rsG = SG ? H : rsK;
     auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
     rk.load(kbase(k, c_begin), rsK, kc0);
-    rg.load(kbase(g, c_begin), rsK, kc0);
+    rg.load(gbase(c_begin), rsG, kc0);
     rv.load(vbase(v, c_begin), rsV, tid);
     rdo.load(vbase(d_o, c_begin), rsV, tid);
     __syncthreads();
@@ -500,7 +528,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     rdo.store_lds(sm.dO, Sm::pV, tid);
     if (c_begin + 1 < c_end) {
         rk.load(kbase(k, c_begin + 1), rsK, kc0);
-        rg.load(kbase(g, c_begin + 1), rsK, kc0);
+        rg.load(gbase(c_begin + 1), rsG, kc0);
         rv.load(vbase(v, c_begin + 1), rsV, tid);
         rdo.load(vbase(d_o, c_begin + 1), rsV, tid);
     }
@@ -564,7 +592,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
             row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
             if (c + 2 < c_end) {
                 rk.load(kbase(k, c + 2), rsK, kc0);
-                rg.load(kbase(g, c + 2), rsK, kc0);
+                rg.load(gbase(c + 2), rsG, kc0);
             }
         }
         __syncthreads();
@@ -667,12 +695,13 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 // blocks, which the other slice's wave may own, so it is stored after the
 // step's closing barrier, at the start of the next step (after the loop for
 // the last chunk).
-template <typename T, int BK, int V, int NW>
+template <typename T, int BK, int V, int NW, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
                 const T* __restrict__ d_o, const T* __restrict__ dq, const T* __restrict__ ws_dinit,
                 const float* __restrict__ dht, const T* __restrict__ hs, const T* __restrict__ dp_in,
-                T* __restrict__ dk, T* __restrict__ dg, int T_, int H, int K, int N, int P, int seg_len, int BH) {
+                T* __restrict__ dk, T* __restrict__ dg, float* __restrict__ dg_part, int T_, int H, int K, int N,
+                int P, int seg_len, int BH) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
@@ -703,15 +732,18 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     else if (dht) S.load(dht + (long)bh * K * V + (long)k0 * V, V, i0, j0);
     else S.zero();
 
-    RowSlab<T, CPK> rq, rg;
+    RowSlab<T, CPK> rq;
+    GateSlab<T, CPK, SG> rg;
     using TRV = TileRegs<T, V, NT>;
     TRV rv, rdo;
     TileRegs<T, kChunk, NT> rp;  // the chunk's dP [t][s] from the dq walk
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    auto gbase = [&](int c) { return SG ? g + ((long)b * T_ + (long)c * kChunk) * H + h : kbase(g, c); };
+    const int rsG = SG ? H : rsK;
     auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
     if (nchunks > 0) {
         rq.load(kbase(q, chunk_of(0)), rsK, kc0);
-        rg.load(kbase(g, chunk_of(0)), rsK, kc0);
+        rg.load(gbase(chunk_of(0)), rsG, kc0);
         rv.load(vbase(v, chunk_of(0)), rsV, tid);
         rdo.load(vbase(d_o, chunk_of(0)), rsV, tid);
     }
@@ -722,7 +754,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         rdo.store_lds(sm.dO, Sm::pV, tid);
         if (nchunks > 1) {
             rq.load(kbase(q, chunk_of(1)), rsK, kc0);
-            rg.load(kbase(g, chunk_of(1)), rsK, kc0);
+            rg.load(gbase(chunk_of(1)), rsG, kc0);
             rv.load(vbase(v, chunk_of(1)), rsV, tid);
             rdo.load(vbase(d_o, chunk_of(1)), rsV, tid);
         }
@@ -746,9 +778,30 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 #pragma unroll
         for (int m = 0; m < RR::NB; ++m) {
             const int s = 16 * RR::block(m, vs) + (l & 15);
-            *reinterpret_cast<vec4_t<T>*>(dg_rows + s * rsK + ic) = to_vec4<T>(da[m] + RR::pick(run, m, vs));
+            const f32x4 out = da[m] + RR::pick(run, m, vs);
+            if constexpr (SG) {
+                // a scalar gate's gradient is the sum over the key columns: this
+                // lane's four, then the wave's sixteen (lanes 16 apart), then (in
+                // flush_sg) the key blocks of the workgroup
+                float x = (out[0] + out[1]) + (out[2] + out[3]);
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                if (l < 16) sm.sgt[kq * kChunk + s] = x;
+            } else {
+                *reinterpret_cast<vec4_t<T>*>(dg_rows + s * rsK + ic) = to_vec4<T>(out);
+            }
         }
         run_carry = run[0] + tot[0];
+    };
+    // scalar gate: this workgroup's sum over its BK key columns of chunk c's dg,
+    // one fp32 partial per key block (summed over the blocks by gla_dg_sum)
+    auto flush_sg = [&](int c) {
+        if (tid < kChunk) {
+            float x = 0.f;
+#pragma unroll
+            for (int j = 0; j < RR::NKQ; ++j) x += sm.sgt[j * kChunk + tid];
+            dg_part[(long)kb * BH * T_ + ((long)b * T_ + (long)c * kChunk + tid) * H + h] = x;
+        }
     };
     for (int it = 0; it < nchunks; ++it) {
         const int c = chunk_of(it);
@@ -836,11 +889,12 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             row_prep<T, CPK, true>(nxt, Sm::pK, Sm::pB, rq, rg, kc0);
             if (it + 2 < nchunks) {
                 rq.load(kbase(q, chunk_of(it + 2)), rsK, kc0);
-                rg.load(kbase(g, chunk_of(it + 2)), rsK, kc0);
+                rg.load(gbase(chunk_of(it + 2)), rsG, kc0);
             }
         }
         __syncthreads();
         // ---- phase 2
+        if (SG && it > 0) flush_sg(chunk_of(it - 1));
         if (exact) {
             // intra part element by element, sum_{t>=s} dP^T[s][t] q_t exp2(B_t - B_s),
             // into an fp32 [s][i] tile over the (now unused) value tiles
@@ -924,7 +978,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             } else {
                 cin = run_carry;
             }
-            dg_rows = const_cast<T*>(kbase(dg, c));
+            dg_rows = SG ? nullptr : const_cast<T*>(kbase(dg, c));
         }
         if (exact) __syncthreads();
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
@@ -938,7 +992,13 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
         __syncthreads();
     }
-    if (nchunks > 0) store_dg();
+    if (nchunks > 0) {
+        store_dg();
+        if (SG) {
+            __syncthreads();
+            flush_sg(chunk_of(nchunks - 1));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1358,7 +1418,7 @@ gla_bwd_dv(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 // Phase 1: A^T(c), the inter-chunk part of dv, preparation of chunk c-1 (first
 // column groups).  Phase 2: the intra-chunk part of dv, the dS update, the rest
 // of the preparation.  Segment 0 ends with dS_0.
-template <typename T, int KD, int BV, int NW>
+template <typename T, int KD, int BV, int NW, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
                 const T* __restrict__ d_o, const T* __restrict__ ws_dinit, const float* __restrict__ dht,
@@ -1420,20 +1480,23 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
     }
 
-    RowSlab<T, CPK> rq, rk, rg;
+    RowSlab<T, CPK> rq, rk;
+    GateSlab<T, CPK, SG> rg;
     TileRegs<T, CW, 64> rdo;
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto gbase = [&](int c) { return SG ? g + ((long)b * T_ + (long)c * kChunk) * H + h : kbase(g, c); };
+    const int rsG = SG ? H : rsK;
     auto vrow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
     auto load_slabs = [&](int c) {
         rq.load(kbase(q, c), rsK, kc0);
         rk.load(kbase(k, c), rsK, kc0);
-        rg.load(kbase(g, c), rsK, kc0);
+        rg.load(gbase(c), rsG, kc0);
     };
     constexpr int NG = CPK / VEC, MG = (NG + 1) / 2;
     auto load_groups = [&](int c, int m0, int m1) {
         rq.load_part(kbase(q, c), rsK, kc0, m0, m1);
         rk.load_part(kbase(k, c), rsK, kc0, m0, m1);
-        rg.load_part(kbase(g, c), rsK, kc0, m0, m1);
+        rg.load_part(gbase(c), rsG, kc0, m0, m1);
     };
     if (nchunks > 0) {
         load_slabs(chunk_of(0));
@@ -1484,14 +1547,21 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             for (int e = tid; e < kChunk * Sm::pF; e += NT) Af[e] = 0.f;
             __syncthreads();
             for (int j0 = 0; j0 < CPK; j0 += VEC) {
-                RowSlab<T, VEC> xq, xk, xg;
+                RowSlab<T, VEC> xq, xk;
                 xq.load(kbase(q, c), rsK, kc0 + j0);
                 xk.load(kbase(k, c), rsK, kc0 + j0);
-                xg.load(kbase(g, c), rsK, kc0 + j0);
                 float bt[VEC];
+                if constexpr (SG) {
+                    const float b0 = wave_incl_scan(Elem<T>::to_f(gbase(c)[l * rsG]) * kLog2e);
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
-                wave_incl_scan_n<VEC>(bt);
+                    for (int j = 0; j < VEC; ++j) bt[j] = b0;
+                } else {
+                    RowSlab<T, VEC> xg;
+                    xg.load(kbase(g, c), rsK, kc0 + j0);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
+                    wave_incl_scan_n<VEC>(bt);
+                }
                 for (int s = 0; s < kChunk; ++s) {
                     float part = 0.f;
 #pragma unroll
@@ -1618,8 +1688,20 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 // Segment states of both directions and their combine.  The workgroups span
 // the forward's value width (BV = a.BVS), so the key-side preparation and its
 // loads are not repeated across value blocks.
-template <typename T, int KD, int BV>
-static hipError_t launch_seg_states(const BwdLaunch& a) {
+// Scalar gate: dg[i] = sum over the nkb key blocks of their partial sums
+// part[kb][i] (fp32, in key-block order), rounded once to the I/O dtype.
+template <typename T>
+__global__ void __launch_bounds__(256)
+gla_dg_sum(const float* __restrict__ part, int nkb, long n, T* __restrict__ dg) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float x = 0.f;
+    for (int j = 0; j < nkb; ++j) x += part[(long)j * n + i];
+    dg[i] = Elem<T>::from_f(x);
+}
+
+template <typename T, int KD, int BV, bool SG>
+static hipError_t launch_seg_states_g(const BwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
@@ -1631,7 +1713,7 @@ static hipError_t launch_seg_states(const BwdLaunch& a) {
         const long nfwd = xcd_grid(nseg * a.BH, nvb);
         const long nrev = xcd_grid((nseg + (mid ? 1 : 0)) * a.BH, nvb);
         dim3 grid2((unsigned)(nfwd + nrev));
-        GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW>), grid2, dim3(NT), a.stream, (const T*)a.k,
+        GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW, SG>), grid2, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, (T*)a.ws_state,
                            (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd,
                            mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2);
@@ -1643,7 +1725,17 @@ static hipError_t launch_seg_states(const BwdLaunch& a) {
 }
 
 template <typename T, int KD, int BV>
-static hipError_t launch_dv(const BwdLaunch& a) {
+static hipError_t launch_seg_states(const BwdLaunch& a) {
+    if constexpr (sizeof(T) == 2) {
+        if (a.sg) return launch_seg_states_g<T, KD, BV, true>(a);
+    } else {
+        if (a.sg) return hipErrorInvalidValue;
+    }
+    return launch_seg_states_g<T, KD, BV, false>(a);
+}
+
+template <typename T, int KD, int BV, bool SG>
+static hipError_t launch_dv_g(const BwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     const int nvb = a.V / BV;
@@ -1653,11 +1745,12 @@ static hipError_t launch_dv(const BwdLaunch& a) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, true>) <= 160 * 1024, "LDS budget");
         const int nhalf = a.dv_split == 2 && a.P > 1 ? 2 : 1;
         dim3 gridh((unsigned)xcd_grid(a.P * a.BH * nhalf, nvb));
-        GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW>), gridh, dim3(NT), a.stream, (const T*)a.q,
+        GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW, SG>), gridh, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_dstate, a.dht,
                            (const T*)a.ws_dmid, a.ws_gmid, (a.seg_len + 1) / 2, nhalf, (T*)a.dv, a.ds0, a.T, a.H, a.V,
                            a.N, a.P, a.seg_len, (int)a.BH);
     } else {
+        static_assert(!SG, "scalar gates take the 16-bit path");
         const float* dinit = a.P > 1 ? (const float*)a.ws_dstate : a.dht;
         const long seg_stride = a.P > 1 ? KV : 0;
         const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
@@ -1668,8 +1761,18 @@ static hipError_t launch_dv(const BwdLaunch& a) {
     return hipGetLastError();
 }
 
-template <typename T, int BK, int V>
-static hipError_t launch_rows(const BwdLaunch& a) {
+template <typename T, int KD, int BV>
+static hipError_t launch_dv(const BwdLaunch& a) {
+    if constexpr (sizeof(T) == 2) {
+        if (a.sg) return launch_dv_g<T, KD, BV, true>(a);
+    } else {
+        if (a.sg) return hipErrorInvalidValue;
+    }
+    return launch_dv_g<T, KD, BV, false>(a);
+}
+
+template <typename T, int BK, int V, bool SG>
+static hipError_t launch_rows_g(const BwdLaunch& a) {
     constexpr int NW = 8;
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
@@ -1687,7 +1790,7 @@ static hipError_t launch_rows(const BwdLaunch& a) {
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
-        GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
+        GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, SG>), grid, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0, (T*)a.dq,
                            (T*)a.ws_hs, (T*)a.ws_dp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
@@ -1696,17 +1799,33 @@ static hipError_t launch_rows(const BwdLaunch& a) {
                            (T*)a.ws_hs, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     }
     if constexpr (sizeof(T) == 2) {
-        GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk_pipe<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
+        GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk_pipe<T, BK, V, NW, SG>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq,
                            (const T*)a.ws_dstate, a.dht, (const T*)a.ws_hs, (const T*)a.ws_dp, (T*)a.dk, (T*)a.dg,
-                           a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+                           a.ws_dgp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+        if (SG) {
+            const long n = a.BH * (long)a.T;
+            GLA_LAUNCH("bwd_dg_sum", (gla_dg_sum<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), a.stream,
+                       (const float*)a.ws_dgp, nkb, n, (T*)a.dg);
+        }
     } else {
+        static_assert(!SG, "scalar gates take the 16-bit path");
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq, dinit,
                            seg_stride, bh_stride, (const T*)a.ws_hs, (T*)a.dk, (T*)a.dg, a.T, a.H, a.K, a.N, a.P,
                            a.seg_len, (int)a.BH);
     }
     return hipGetLastError();
+}
+
+template <typename T, int BK, int V>
+static hipError_t launch_rows(const BwdLaunch& a) {
+    if constexpr (sizeof(T) == 2) {
+        if (a.sg) return launch_rows_g<T, BK, V, true>(a);
+    } else {
+        if (a.sg) return hipErrorInvalidValue;
+    }
+    return launch_rows_g<T, BK, V, false>(a);
 }
 
 #define GLA_COL_DISPATCH(FN, T, KD_, BV_)                              \

@@ -159,44 +159,73 @@ struct PipeSmem {
 // kc0 .. kc0+NC-1 (lane = token row) from its register slabs of q, k and the
 // raw log gate.  Lane j collects B_63 of column kc0 + j and the factors are
 // formed once per lane at the end, so the column loop has no branches and the
-// scans of a group's VEC columns interleave.
-template <typename T, int NC, typename Buf>
+// scans of a group's VEC columns interleave.  A scalar gate (GS::scalar) has
+// one cumulative gate per token: one scan and two exp2 per lane serve every
+// column, and the chunk needs the exact path only if that one decay leaves the
+// basis range.
+template <typename T, int NC, typename Buf, typename GS>
 __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSlab<T, NC>& rq,
-                                          const RowSlab<T, NC>& rk, const RowSlab<T, NC>& rg, int kc0, int m0,
-                                          int m1) {
+                                          const RowSlab<T, NC>& rk, const GS& rg, int kc0, int m0, int m1) {
     constexpr int VEC = 16 / (int)sizeof(T);
     static_assert(NC <= 64, "one lane per prepared column");
     const int l = lane_id();
-    float last_l = 0.f;
-    bool wide = false;
+    if constexpr (GS::scalar) {
+        if (m0 >= m1) return;  // no group: the slab may already hold a later chunk's gate
+        const float bt = wave_incl_scan(rg.get(0) * kLog2e);
+        const float bl = lane_bcast(bt, 63);
+        const bool in = -bl <= kBasisLimit;
+        const float fq = exp2_fast(bt), fk = exp2_fast((in ? 0.f : bl) - bt);
 #pragma unroll
-    for (int m = 0; m < NC / VEC; ++m) {
-        if (m < m0 || m >= m1) continue;
-        const int j0 = m * VEC;
-        float bt[VEC];
+        for (int m = 0; m < NC / VEC; ++m) {
+            if (m < m0 || m >= m1) continue;
+            const int j0 = m * VEC;
+            float ql[VEC], kt[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
-        wave_incl_scan_n<VEC>(bt);
-        float ql[VEC], kt[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float bl = lane_bcast(bt[e], 63);
-            const bool in = -bl <= kBasisLimit;
-            wide |= !in;
-            last_l = (l == j0 + e) ? bl : last_l;
-            ql[e] = rq.get(j0 + e) * exp2_fast(bt[e]);
-            kt[e] = rk.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
+            for (int e = 0; e < VEC; ++e) {
+                ql[e] = rq.get(j0 + e) * fq;
+                kt[e] = rk.get(j0 + e) * fk;
+            }
+            store_vec_lds<T>(bf.Ql + l * pQl + kc0 + j0, ql);
+            store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
         }
-        store_vec_lds<T>(bf.Ql + l * pQl + kc0 + j0, ql);
-        store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
+        if (l >= m0 * VEC && l < m1 * VEC) {
+            const float gm = exp2_fast(bl);
+            bf.pre[kc0 + l] = in ? 1.f : gm;
+            bf.post[kc0 + l] = in ? gm : 1.f;
+        }
+        if (!in && l == 0) bf.flag[0] = 1;
+    } else {
+        float last_l = 0.f;
+        bool wide = false;
+#pragma unroll
+        for (int m = 0; m < NC / VEC; ++m) {
+            if (m < m0 || m >= m1) continue;
+            const int j0 = m * VEC;
+            float bt[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) bt[e] = rg.get(j0 + e) * kLog2e;
+            wave_incl_scan_n<VEC>(bt);
+            float ql[VEC], kt[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float bl = lane_bcast(bt[e], 63);
+                const bool in = -bl <= kBasisLimit;
+                wide |= !in;
+                last_l = (l == j0 + e) ? bl : last_l;
+                ql[e] = rq.get(j0 + e) * exp2_fast(bt[e]);
+                kt[e] = rk.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
+            }
+            store_vec_lds<T>(bf.Ql + l * pQl + kc0 + j0, ql);
+            store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
+        }
+        if (l >= m0 * VEC && l < m1 * VEC) {
+            const float gm = exp2_fast(last_l);
+            const bool in = -last_l <= kBasisLimit;
+            bf.pre[kc0 + l] = in ? 1.f : gm;
+            bf.post[kc0 + l] = in ? gm : 1.f;
+        }
+        if (wide && l == 0) bf.flag[0] = 1;
     }
-    if (l >= m0 * VEC && l < m1 * VEC) {
-        const float gm = exp2_fast(last_l);
-        const bool in = -last_l <= kBasisLimit;
-        bf.pre[kc0 + l] = in ? 1.f : gm;
-        bf.post[kc0 + l] = in ? gm : 1.f;
-    }
-    if (wide && l == 0) bf.flag[0] = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -282,8 +311,9 @@ struct SegSmem {
     alignas(16) T Yw[2 * NW * kChunk * pW];
 };
 
-// One workgroup's segment; `bid` is its block index within its own grid.
-template <typename T, int KD, int BV, int NW, bool REV>
+// One workgroup's segment; `bid` is its block index within its own grid.  SG:
+// g is a scalar per token and head ([B, T, H]), shared by every key column.
+template <typename T, int KD, int BV, int NW, bool REV, bool SG = false>
 __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int bid, const T* __restrict__ x,
                                                const T* __restrict__ g, const T* __restrict__ y,
                                                T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_,
@@ -314,13 +344,33 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
     S.zero();
     float gtot = 0.f;  // lane j: sum of B_63 over the segment for key column kc0 + j
 
-    RowSlab<T, CPK> rx, rg;
+    RowSlab<T, CPK> rx;
+    GateSlab<T, CPK, SG> rg;
     TileRegs<T, CW, 64> ry;
     auto chunk_of = [&](int it) { return REV ? c_end - 1 - it : c_begin + it; };
     auto krow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    auto grow = [&](int c) { return SG ? g + ((long)b * T_ + (long)c * kChunk) * H + h : krow(g, c); };
+    const int rsG = SG ? H : rsK;
     auto vrow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
     auto yslice = [&](int it) { return sm.Yw + ((it & 1) * NW + w) * kChunk * Sm::pW; };
     auto prep = [&](typename Sm::Buf& bf) {
+        if constexpr (SG) {
+            const float bt = wave_incl_scan(rg.get(0) * kLog2e);
+            const float bl = lane_bcast(bt, 63);
+            const float f = exp2_fast(REV ? bt : bl - bt);
+#pragma unroll
+            for (int j0 = 0; j0 < CPK; j0 += VEC) {
+                float xv[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) xv[e] = rx.get(j0 + e) * f;
+                store_vec_lds<T>(bf.X + l * Sm::pX + kc0 + j0, xv);
+            }
+            if (l < CPK) {
+                bf.gam[kc0 + l] = exp2_fast(bl);
+                gtot += bl;
+            }
+            return;
+        }
         float last_l = 0.f;
 #pragma unroll
         for (int j0 = 0; j0 < CPK; j0 += VEC) {
@@ -378,14 +428,14 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
     if (m2 == 0) store_mid();
     if (nchunks > 0) {
         rx.load(krow(x, chunk_of(0)), rsK, kc0);
-        rg.load(krow(g, chunk_of(0)), rsK, kc0);
+        rg.load(grow(chunk_of(0)), rsG, kc0);
         ry.load(vrow(y, chunk_of(0)), rsV, l);
         prep(sm.buf[0]);
         if (m2 == 1) gmid = gtot;
         ry.store_lds(yslice(0), Sm::pW, l);
         if (nchunks > 1) {
             rx.load(krow(x, chunk_of(1)), rsK, kc0);
-            rg.load(krow(g, chunk_of(1)), rsK, kc0);
+            rg.load(grow(chunk_of(1)), rsG, kc0);
             ry.load(vrow(y, chunk_of(1)), rsV, l);
         }
     }
@@ -408,7 +458,7 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
             ry.store_lds(yslice(it + 1), Sm::pW, l);
             if (it + 2 < nchunks) {
                 rx.load(krow(x, chunk_of(it + 2)), rsK, kc0);
-                rg.load(krow(g, chunk_of(it + 2)), rsK, kc0);
+                rg.load(grow(chunk_of(it + 2)), rsG, kc0);
                 ry.load(vrow(y, chunk_of(it + 2)), rsV, l);
             }
         }
@@ -427,14 +477,14 @@ __device__ __forceinline__ void seg_state_body(SegSmem<T, KD, BV, NW>& sm, int b
     if (vb == 0 && seg >= gate_first && l < CPK) ws_gate[((long)bh * P + seg) * KD + kc0 + l] = gtot;
 }
 
-template <typename T, int KD, int BV, int NW, bool REV>
+template <typename T, int KD, int BV, int NW, bool REV, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restrict__ y,
               T* __restrict__ ws_state, float* __restrict__ ws_gate,
               int T_, int H, int V, int N, int P, int seg_len, int seg_first, int nseg, int BH) {
     __shared__ SegSmem<T, KD, BV, NW> sm;
-    seg_state_body<T, KD, BV, NW, REV>(sm, blockIdx.x, x, g, y, ws_state, ws_gate, T_, H, V, N, P, seg_len,
-                                       seg_first, nseg, BH, 0);
+    seg_state_body<T, KD, BV, NW, REV, SG>(sm, blockIdx.x, x, g, y, ws_state, ws_gate, T_, H, V, N, P, seg_len,
+                                           seg_first, nseg, BH, 0);
 }
 
 // Both directions of the backward's segment states in one grid (they are
@@ -443,7 +493,7 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
 // segment together with its midpoint state (the local dS* of the chunks from
 // c_begin + split on) and that half's gate total, from which the dv walk
 // starts a segment's first half.
-template <typename T, int KD, int BV, int NW>
+template <typename T, int KD, int BV, int NW, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ q,
                    const T* __restrict__ d_o, const T* __restrict__ g, T* __restrict__ ws_state,
@@ -453,14 +503,14 @@ gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __
     __shared__ SegSmem<T, KD, BV, NW> sm;
     const int bid = blockIdx.x;
     if (bid < nfwd)
-        seg_state_body<T, KD, BV, NW, false>(sm, bid, k, g, v, ws_state, ws_gate, T_, H, V, N, P, seg_len, 0, nseg,
-                                             BH, 0);
+        seg_state_body<T, KD, BV, NW, false, SG>(sm, bid, k, g, v, ws_state, ws_gate, T_, H, V, N, P, seg_len, 0,
+                                                 nseg, BH, 0);
     else if (!ws_dmid)  // only segment P-1 is not covered by the forward direction
-        seg_state_body<T, KD, BV, NW, true>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P, seg_len,
-                                            1, nseg, BH, P - 1);
+        seg_state_body<T, KD, BV, NW, true, SG>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P,
+                                                seg_len, 1, nseg, BH, P - 1);
     else  // every segment, for its midpoint state (segment 0's total is not needed)
-        seg_state_body<T, KD, BV, NW, true>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P, seg_len,
-                                            0, nseg + 1, BH, P - 1, ws_dmid, ws_gmid, split);
+        seg_state_body<T, KD, BV, NW, true, SG>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P,
+                                                seg_len, 0, nseg + 1, BH, P - 1, ws_dmid, ws_gmid, split);
 }
 
 }  // namespace gla

@@ -185,6 +185,7 @@ struct TileRegs {
 // row l, columns c0 .. c0+NC-1 (NC a whole number of 16-byte vectors).
 template <typename T, int NC>
 struct RowSlab {
+    static constexpr bool scalar = false;  // see GateSlab
     static constexpr int VEC = 16 / (int)sizeof(T);
     static constexpr int NV = NC / VEC;
     static_assert(NC % VEC == 0, "slab width must be a whole number of 16-byte vectors");
@@ -206,6 +207,27 @@ struct RowSlab {
         const T* v = reinterpret_cast<const T*>(&r[c / VEC]);
         return Elem<T>::to_f(v[c % VEC]);
     }
+};
+
+// The log gate of one wave's slab.  SG = false: one value per key column,
+// the RowSlab of the wave's NC columns.  SG = true (scalar gate per token and
+// head, the gates of Mamba-2 / RetNet style layers): lane l holds g of token l,
+// shared by every column; `base` then points at the chunk's first token in a
+// [B, T, H] tensor and rows are `rs` = H apart.  load_part loads the scalar
+// with the last column group, so a slab whose preparation is split over two
+// phases keeps one chunk's gate until both parts have used it.
+template <typename T, int NC, bool SG>
+struct GateSlab : RowSlab<T, NC> {};
+template <typename T, int NC>
+struct GateSlab<T, NC, true> {
+    static constexpr bool scalar = true;
+    static constexpr int NV = NC / (16 / (int)sizeof(T));
+    T r;
+    __device__ __forceinline__ void load(const T* __restrict__ base, int rs, int) { r = base[lane_id() * rs]; }
+    __device__ __forceinline__ void load_part(const T* __restrict__ base, int rs, int c0, int, int m1) {
+        if (m1 == NV) load(base, rs, c0);
+    }
+    __device__ __forceinline__ float get(int) const { return Elem<T>::to_f(r); }
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane = token): four

@@ -327,7 +327,7 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 // so the vector-ALU preparation of the next chunk overlaps the matrix work of
 // this one.  Each wave owns BV/NW value columns: its slice of V never needs a
 // workgroup barrier.
-template <typename T, int KD, int BV, int NW>
+template <typename T, int KD, int BV, int NW, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const T* __restrict__ ws_init, const float* __restrict__ s0,
@@ -366,21 +366,25 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     else if (s0) S.load(s0 + (long)bh * KD * V, V, col0);
     else S.zero();
 
-    RowSlab<T, CPK> rq, rk, rg;
+    RowSlab<T, CPK> rq, rk;
+    GateSlab<T, CPK, SG> rg;
     TileRegs<T, CW, 64> rv;
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * KD; };
+    // g: per key column [B,T,H,K], or (SG) one value per token and head [B,T,H]
+    auto gbase = [&](int c) { return SG ? g + ((long)b * T_ + (long)c * kChunk) * H + h : kbase(g, c); };
+    const int rsG = SG ? H : rsK;
     auto vrow = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
     auto load_slabs = [&](int c) {
         rq.load(kbase(q, c), rsK, kc0);
         rk.load(kbase(k, c), rsK, kc0);
-        rg.load(kbase(g, c), rsK, kc0);
+        rg.load(gbase(c), rsG, kc0);
     };
     // column groups of the preparation done in phase 1 (m < MG) and phase 2
     constexpr int NG = CPK / (16 / (int)sizeof(T)), MG = (NG + 1) / 2;
     auto load_groups = [&](int c, int m0, int m1) {
         rq.load_part(kbase(q, c), rsK, kc0, m0, m1);
         rk.load_part(kbase(k, c), rsK, kc0, m0, m1);
-        rg.load_part(kbase(g, c), rsK, kc0, m0, m1);
+        rg.load_part(gbase(c), rsG, kc0, m0, m1);
     };
     load_slabs(c_begin);
     rv.load(vrow(v, c_begin), rsV, l);
@@ -428,14 +432,21 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
             __syncthreads();
             constexpr int VEC = 16 / (int)sizeof(T);
             for (int j0 = 0; j0 < CPK; j0 += VEC) {
-                RowSlab<T, VEC> xq, xk, xg;
+                RowSlab<T, VEC> xq, xk;
                 xq.load(kbase(q, c), rsK, kc0 + j0);
                 xk.load(kbase(k, c), rsK, kc0 + j0);
-                xg.load(kbase(g, c), rsK, kc0 + j0);
                 float bt[VEC];
+                if constexpr (SG) {
+                    const float b0 = wave_incl_scan(Elem<T>::to_f(gbase(c)[l * rsG]) * kLog2e);
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
-                wave_incl_scan_n<VEC>(bt);
+                    for (int j = 0; j < VEC; ++j) bt[j] = b0;
+                } else {
+                    RowSlab<T, VEC> xg;
+                    xg.load(kbase(g, c), rsK, kc0 + j0);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
+                    wave_incl_scan_n<VEC>(bt);
+                }
                 for (int s = 0; s < kChunk; ++s) {
                     float part = 0.f;
 #pragma unroll
@@ -568,8 +579,8 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
 // ---------------------------------------------------------------------------
 // Host launchers.
-template <typename T, int KD, int BV>
-static hipError_t launch_fwd_t(const FwdLaunch& a) {
+template <typename T, int KD, int BV, bool SG>
+static hipError_t launch_fwd_sg(const FwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
@@ -579,7 +590,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
         // segments 0..P-2 feed the combine; the last segment's S* is never needed
         const int nseg = a.P - 1;
         dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
-        GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false>), grid, dim3(NT), a.stream,
+        GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false, SG>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.g, (const T*)a.v, (T*)a.ws_state, a.ws_gate,
                            a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg, (int)a.BH);
         dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
@@ -589,10 +600,11 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
-        GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW>), grid, dim3(NT), a.stream,
+        GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG>), grid, dim3(NT), a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
                            (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
+        static_assert(!SG, "scalar gates take the 16-bit path");
         // fp32: the workspace states are fp32 and hold S_init(0) = S_0 after the combine
         const float* sinit = a.P > 1 ? (const float*)a.ws_state : a.s0;
         const long seg_stride = a.P > 1 ? KV : 0;
@@ -603,6 +615,17 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
                            (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
     }
     return hipGetLastError();
+}
+
+// per-column gates, or (16-bit inputs) a scalar gate per token and head
+template <typename T, int KD, int BV>
+static hipError_t launch_fwd_t(const FwdLaunch& a) {
+    if constexpr (sizeof(T) == 2) {
+        if (a.sg) return launch_fwd_sg<T, KD, BV, true>(a);
+    } else {
+        if (a.sg) return hipErrorInvalidValue;
+    }
+    return launch_fwd_sg<T, KD, BV, false>(a);
 }
 
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream) {

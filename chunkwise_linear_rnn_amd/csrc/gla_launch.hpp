@@ -9,6 +9,7 @@ namespace gla {
 
 struct FwdLaunch {
     bool bf16;
+    bool sg;  // g is one value per token and head, [B,T,H] (16-bit inputs only)
     int K, V, BV;
     int T, H, N, P, seg_len;
     long BH;
@@ -23,6 +24,7 @@ struct FwdLaunch {
 
 struct BwdLaunch {
     bool bf16;
+    bool sg;  // g and dg are one value per token and head, [B,T,H] (16-bit inputs only)
     int K, V, BV, BK;
     int BVS;  // value columns per workgroup of the segment-state pass (the forward's)
     int BVD;  // value columns per workgroup of the dv walk
@@ -40,6 +42,7 @@ struct BwdLaunch {
     void* ws_dp;       // [BH][N][64][64] dtype (16-bit inputs): each chunk's dP = dO V^T, [t][s]
     void* ws_dmid;     // [BH][P][K][V] dtype (dv_split == 2): local dS* of each segment's second half
     float* ws_gmid;    // [BH][P][K] fp32: that half's gate total (log2)
+    float* ws_dgp;     // scalar gate: [K/BK][BH*T] fp32, each key block's sum of dg over its columns
     hipStream_t stream;
 };
 

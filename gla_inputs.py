@@ -15,6 +15,8 @@ Gate recipes (all give log gates g <= 0, i.e. alpha = exp(g) in (0, 1]):
                 W ~ N(0,1)/4 in R^{16 x (H K)}: the rank-16 gate projection with
                 temperature 16 of the GLA layer, so log gates sit near 0 with a
                 heavy negative tail.
+  * ``scalar``  one log gate per token and head, g = logsigmoid(N(0,1)) / 16, of
+                shape [B, T, H] (the scalar-gate entry points)
 """
 from __future__ import annotations
 
@@ -70,8 +72,8 @@ def custom(B, H, T, K, V, dtype="bf16", gate="iid", v_scale="rsqrt_k", s0="none"
 def make_inputs(w: Workload, device: Optional[str] = None, dht: bool = False) -> Dict[str, torch.Tensor]:
     """Draw the inputs of workload ``w`` (CPU, then moved to ``device`` if given).
 
-    Returns q, k, g [B,T,H,K] and v (+ do) [B,T,H,V] in the workload dtype, and
-    s0 / dht [B,H,K,V] in float32 (or None).
+    Returns q, k, g [B,T,H,K] (g [B,T,H] for the ``scalar`` gate) and v (+ do)
+    [B,T,H,V] in the workload dtype, and s0 / dht [B,H,K,V] in float32 (or None).
     """
     gen = torch.Generator(device="cpu").manual_seed(w.seed)
     B, H, T, K, V = w.B, w.H, w.T, w.K, w.V
@@ -89,6 +91,8 @@ def make_inputs(w: Workload, device: Optional[str] = None, dht: bool = False) ->
         x = torch.randn(B, T, 16, generator=gen)
         W = torch.randn(16, H * K, generator=gen) / 4.0
         g = (F.logsigmoid(x @ W) / 16.0).reshape(B, T, H, K)
+    elif w.gate == "scalar":
+        g = F.logsigmoid(torch.randn(B, T, H, generator=gen)) / 16.0
     else:
         raise ValueError(w.gate)
     if w.s0 == "none":

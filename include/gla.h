@@ -123,6 +123,33 @@ gla_status_t gla_bwd(const gla_shape_t* shape,
 size_t gla_bwd_workspace_size(const gla_shape_t* shape);
 
 /*
+ * gla_fwd_scalar / gla_bwd_scalar -- the same operator with a scalar forget
+ * gate per token and head, alpha_t = exp(g_t) * 1 (every key column decays
+ * alike: the data-dependent decay of Mamba-2 and the gated retention form,
+ * the scalar-decay special case of Eq. 3 discussed with Eq. 1 and Section 4.1).
+ * Intra-chunk attention is then a masked product with a rank-one decay mask,
+ * and each chunk needs one cumulative gate per token instead of one per key
+ * column, which the kernels exploit (one scan and two exponentials per token).
+ *   g  : [B,T,H] dtype (instead of [B,T,H,K]), g <= 0
+ *   dg : [B,T,H] dtype output of gla_bwd_scalar, the gradient with respect to
+ *        the scalar log gate (the sum over key columns of the per-column one)
+ * Every other argument, layout and convention is that of gla_fwd / gla_bwd.
+ * bf16 only (fp32 inputs return GLA_ERR_UNSUPPORTED).  gla_fwd_scalar takes
+ * gla_fwd_workspace_size(shape) bytes of workspace; gla_bwd_scalar takes
+ * gla_bwd_scalar_workspace_size(shape) (which is 0 for fp32 or invalid shapes).
+ */
+gla_status_t gla_fwd_scalar(const gla_shape_t* shape,
+                            const void* q, const void* k, const void* v, const void* g,
+                            const float* s0, void* o, float* s_final,
+                            void* workspace, size_t workspace_bytes, void* stream);
+gla_status_t gla_bwd_scalar(const gla_shape_t* shape,
+                            const void* q, const void* k, const void* v, const void* g,
+                            const float* s0, const void* d_o, const float* dht,
+                            void* dq, void* dk, void* dv, void* dg, float* ds0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
+
+/*
  * gla_decode -- the recurrent form of Eq. 3 (Section 3.1), for token-by-token
  * inference with the state carried between calls: for t = 1..T,
  *     S <- Diag(exp g_t) S + k_t^T v_t ,   o_t = q_t S ,

@@ -174,3 +174,31 @@ def out_gate_bwd(o, z, w, b, eps, dy):
     if rc != 0:
         raise RuntimeError("oracle_out_gate_bwd failed with code %d" % rc)
     return dx, dz, dw, db
+
+
+def gla_fwd_scalar(q, k, v, g, s0=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward recurrence with a scalar gate per token and head, g [B,T,H].
+
+    The scalar-decay case of Eq. 3 (alpha_t = exp(g_t) times the all-ones row):
+    every key column of the state decays by the same factor, so this is
+    gla_fwd with g broadcast over the K columns.  Pinned by: the quadratic
+    decay-mask form O = ((Q K^T) * D * M) V + (Q * b_t) S_0 with
+    D_ts = exp(g_{s+1} + ... + g_t), computed independently in the tests.
+    """
+    g = _as_f64(g)
+    K = _as_f64(q).shape[-1]
+    return gla_fwd(q, k, v, np.repeat(g[..., None], K, axis=-1), s0)
+
+
+def gla_bwd_scalar(q, k, v, g, d_o, s0=None, dht=None):
+    """Gradients for gla_fwd_scalar: (dq, dk, dv, dg [B,T,H], ds0).
+
+    The chain rule through the broadcast: the scalar gate's gradient is the sum
+    over key columns of the per-column gate gradient.  Pinned by: central finite
+    differences in the scalar gate and torch float64 autograd of the decay-mask
+    form.
+    """
+    g = _as_f64(g)
+    K = _as_f64(q).shape[-1]
+    dq, dk, dv, dg, ds0 = gla_bwd(q, k, v, np.repeat(g[..., None], K, axis=-1), d_o, s0, dht)
+    return dq, dk, dv, dg.sum(axis=-1), ds0

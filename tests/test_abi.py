@@ -154,3 +154,17 @@ def test_out_gate_validation_codes(L):
     assert _gate_bwd(L, _shape(T=5), wsb=16) == ERR_WORKSPACE
     assert _gate_bwd(L, _shape(T=5), dw=ctypes.c_void_p(0x10004)) == ERR_ALIGN
     assert _gate_bwd(L, _shape(T=5, V=1024)) == ERR_UNSUPPORTED
+
+
+def test_scalar_gate_entry_points_validate(L):
+    s32 = _shape(T=128, dtype=gla.GLA_DTYPE_FP32)
+    assert L.gla_bwd_scalar_workspace_size(ctypes.byref(s32)) == 0
+    s16 = _shape(T=128, K=128, V=256)
+    assert L.gla_bwd_scalar_workspace_size(ctypes.byref(s16)) >= L.gla_bwd_workspace_size(ctypes.byref(s16))
+    fwd = lambda shape, **kw: L.gla_fwd_scalar(ctypes.byref(shape), P, P, P, kw.get("g", P), None, P, None,
+                                               kw.get("ws", P), 1 << 30, None)
+    assert fwd(s32) == ERR_UNSUPPORTED
+    assert fwd(_shape(T=100)) == ERR_SHAPE
+    assert fwd(_shape(T=128), g=None) == ERR_NULL
+    assert fwd(_shape(T=128), g=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert fwd(_shape(T=0)) == OK
