@@ -430,32 +430,7 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
             float* Af = reinterpret_cast<float*>(nxt.Ql);
             for (int e = tid; e < kChunk * Sm::pF; e += NT) Af[e] = 0.f;
             __syncthreads();
-            constexpr int VEC = 16 / (int)sizeof(T);
-            for (int j0 = 0; j0 < CPK; j0 += VEC) {
-                RowSlab<T, VEC> xq, xk;
-                xq.load(kbase(q, c), rsK, kc0 + j0);
-                xk.load(kbase(k, c), rsK, kc0 + j0);
-                float bt[VEC];
-                if constexpr (SG) {
-                    const float b0 = wave_incl_scan(Elem<T>::to_f(gbase(c)[l * rsG]) * kLog2e);
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) bt[j] = b0;
-                } else {
-                    RowSlab<T, VEC> xg;
-                    xg.load(kbase(g, c), rsK, kc0 + j0);
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
-                    wave_incl_scan_n<VEC>(bt);
-                }
-                for (int s = 0; s < kChunk; ++s) {
-                    float part = 0.f;
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j)
-                        part += xq.get(j) * lane_bcast(xk.get(j), s) * exp2_fast(bt[j] - lane_bcast(bt[j], s));
-                    if (l >= s) atomicAdd(Af + l * Sm::pF + s, part);
-                }
-            }
-            __syncthreads();
+            exact_intra_tile<T, CPK, NW, SG>(Af, Sm::pF, kbase(q, c), kbase(k, c), gbase(c), rsK, rsG, kc0, w);
             for (int e = tid; e < kChunk * kChunk; e += NT) {
                 const int t = e / kChunk, s = e % kChunk;
                 if ((s >> 4) == (t >> 4) || s < t)
