@@ -312,8 +312,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; the multi-GPU sharding of the path is "
-              "described in DESIGN.md and not run (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+        print("bench.py measures one GPU only: the path is sharded across GPUs by heads and by sequence "
+              "segments, which this benchmark does not run (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 
