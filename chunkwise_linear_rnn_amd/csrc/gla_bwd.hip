@@ -180,6 +180,28 @@ gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht,
         combine_row<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr);
 }
 
+// The same with each element group's segments split between two threads
+// (P <= 2 * kSplitMax; threads t and t + 128 share 4 elements; the grid covers
+// K*V exactly, no thread may leave before the exchange barrier).
+template <typename ST>
+__global__ void __launch_bounds__(256)
+gla_seg_combine_bwd_split(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
+                          ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
+    __shared__ f32x4 carry[128];
+    const long KV = (long)K * V;
+    const int slot = threadIdx.x & 127, part = threadIdx.x >> 7;
+    const long e = ((long)blockIdx.x * 128 + slot) * kCombineVec;
+    const long bh = blockIdx.y;
+    const int i = (int)(e / V);
+    const float* gt = ws_gate + bh * P * (long)K + i;
+    if (blockIdx.z == 0)
+        combine_row_split<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr, part,
+                                 &carry[slot]);
+    else
+        combine_row_split<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr, part,
+                                &carry[slot]);
+}
+
 // ---------------------------------------------------------------------------
 // dq walk: forwards over one segment for key rows k0 .. k0+BK-1, full V.
 // State S^T in VGPRs.  dq_t = exp2(B_t - B_63) * [dO (gamma*S)^T + dP (K*Gamma)]_t
@@ -1693,9 +1715,15 @@ static hipError_t launch_seg_states_g(const BwdLaunch& a) {
                            (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, (T*)a.ws_state,
                            (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd,
                            mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2);
-        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>, dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, 2u),
-                           dim3(256), a.stream, a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V,
-                           a.P);
+        if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
+            GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd_split<T>,
+                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, 2u), dim3(256), a.stream, a.s0,
+                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P);
+        } else {
+            GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>,
+                       dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, 2u), dim3(256), a.stream,
+                       a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P);
+        }
     }
     return hipGetLastError();
 }

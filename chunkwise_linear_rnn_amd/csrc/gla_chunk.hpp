@@ -337,6 +337,63 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
     }
 }
 
+// The same recurrence split between two threads, for P <= 2 * kSplitMax: part
+// 0 walks the first ceil(P/2) segments (in walking order) from `init`, part 1
+// the rest from zero, keeping its outputs and the running product of its gates
+// in registers.  Part 0's value after its last segment (the input of part 1's
+// first) goes through `carry` (LDS, one slot per element group), and part 1
+// adds it, decayed by its gate product, to each of its outputs.  Both parts of
+// a slot must be in the same workgroup; every thread must call this (barrier).
+constexpr int kSplitMax = 16;
+template <bool REV, typename ST>
+__device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long KV, long K, int P, const float* init,
+                                                  int part, f32x4* carry) {
+    constexpr int CE = kCombineVec;
+    using VT = combine_vec_t<ST>;
+    const int h = (P + 1) / 2;
+    const int j0 = part ? h : 0, n = part ? P - h : h;  // 1 <= n <= kSplitMax
+    VT a[kSplitMax];
+    float gm[kSplitMax];
+#pragma unroll
+    for (int u = 0; u < kSplitMax; ++u) {
+        const int j = j0 + (u < n ? u : n - 1);
+        const int p = REV ? P - 1 - j : j;
+        a[u] = *reinterpret_cast<const VT*>(st + p * KV);
+        gm[u] = gt[p * K];
+    }
+    f32x4 cur = (part == 0 && init) ? *reinterpret_cast<const f32x4*>(init) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 loc[kSplitMax], fin = cur;
+    float mul[kSplitMax];
+    float m = 1.f;
+#pragma unroll
+    for (int u = 0; u < kSplitMax; ++u) {
+        const int j = j0 + u;
+        const int p = REV ? P - 1 - j : j;
+        const bool feeds = u < n && (REV ? p >= 1 : p + 1 < P);
+        const float gu = feeds ? exp2_fast(gm[u]) : 0.f;
+        loc[u] = cur;
+        mul[u] = m;
+#pragma unroll
+        for (int c = 0; c < CE; ++c) cur[c] = gu * cur[c] + (feeds ? Elem<ST>::to_f(a[u][c]) : 0.f);
+        m *= gu;
+        fin = (u == n - 1) ? cur : fin;
+    }
+    if (part == 0) *carry = fin;
+    __syncthreads();
+    const f32x4 cin = part ? *carry : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kSplitMax; ++u) {
+        if (u < n) {
+            const int j = j0 + u;
+            const int p = REV ? P - 1 - j : j;
+            VT o;
+#pragma unroll
+            for (int c = 0; c < CE; ++c) o[c] = Elem<ST>::from_f(loc[u][c] + mul[u] * cin[c]);
+            *reinterpret_cast<VT*>(st + p * KV) = o;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Step 1: segment-local states.  REV = false: S*_p from the keys and values of
 // the segment walked forwards, S <- Diag(gamma) S + (K*Gamma)^T V with

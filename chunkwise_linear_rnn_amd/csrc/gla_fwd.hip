@@ -40,6 +40,24 @@ gla_seg_combine_fwd(const float* __restrict__ s0, ST* __restrict__ ws_state, con
                        s0 ? s0 + bh * KV + e : nullptr);
 }
 
+// The same with each element group's segments split between two threads
+// (P <= 2 * kSplitMax): threads t and t + 128 of a workgroup share 4 elements.
+// The grid covers K*V exactly (K*V / (128 * kCombineVec) workgroups per head):
+// no thread may leave before the exchange barrier.
+template <typename ST>
+__global__ void __launch_bounds__(256)
+gla_seg_combine_fwd_split(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
+                          int K, int V, int P) {
+    __shared__ f32x4 carry[128];
+    const long KV = (long)K * V;
+    const int slot = threadIdx.x & 127, part = threadIdx.x >> 7;
+    const long e = ((long)blockIdx.x * 128 + slot) * kCombineVec;
+    const long bh = blockIdx.y;
+    const int i = (int)(e / V);
+    combine_row_split<false>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                             s0 ? s0 + bh * KV + e : nullptr, part, &carry[slot]);
+}
+
 // Copy (or zero) a [BH][K][V] fp32 state: final state of an empty sequence.
 __global__ void __launch_bounds__(256) gla_state_copy(const float* __restrict__ src, float* __restrict__ dst, long n) {
     long e = (long)blockIdx.x * 256 + threadIdx.x;
@@ -568,9 +586,15 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
         GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false, SG>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.g, (const T*)a.v, (T*)a.ws_state, a.ws_gate,
                            a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg, (int)a.BH);
-        dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
-        GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
-                           a.ws_gate, KD, a.V, a.P);
+        if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
+            dim3 g2((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH);
+            GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd_split<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
+                       a.ws_gate, KD, a.V, a.P);
+        } else {
+            dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
+            GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
+                       a.ws_gate, KD, a.V, a.P);
+        }
     }
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
