@@ -491,7 +491,8 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
 // (exact-path chunks: the intra part element by element from raw k and B).
 // Phase 1: dP, the value-slice partial of dO S^T, the state update
 // S^T <- post * (pre * S^T + V^T Kt), the store of S_out to `hs` (anchor chunks
-// only), the next chunk's key-side preparation.  Phase 2: dP to `dp_out` for
+// only), the next chunk's key-side preparation (first, in the value-slice-1
+// waves).  Phase 2: dP to `dp_out` for
 // the dk walk (first key block only); then each wave, for its two token blocks
 // (RowRoles::block), dP Kt, the slice reduction, the factor exp2(B_t) and the
 // store of dq; the next chunk's V and d_o tiles.
@@ -561,6 +562,10 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         const bool more = c + 1 < c_end;
         const bool exact = cur.flag[0] != 0;
         // ---- phase 1
+        // the value-slice-1 waves prepare the next chunk first, so that on each
+        // SIMD one wave's vector work overlaps its partner's dP tiles
+        const bool early = RR::VS > 1 && vs == 1;
+        if (early && more) row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
         dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
         // dq^T[i][t] partial = sum_{j in slice} S^T[j][i] dO[t][j], for this
         // wave's token blocks (own, slot m = block RR::block(m, vs)) and for
@@ -611,7 +616,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
                     to_vec4<T>(S.s[jb]);
         }
         if (more) {
-            row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
+            if (!early) row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
             if (c + 2 < c_end) {
                 rk.load(kbase(k, c + 2), rsK, kc0);
                 rg.load(gbase(c + 2), rsG, kc0);
