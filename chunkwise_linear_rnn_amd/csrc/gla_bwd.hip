@@ -1569,11 +1569,13 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             }
         } else {
             // Eq. 4 element by element into an fp32 tile (the spare buffer, refilled
-            // below once A^T is final); each wave adds its key columns' share
+            // below once A^T is final); each wave sums every key column for its own
+            // key tokens s
             float* Af = reinterpret_cast<float*>(nxt.Ql);
             for (int e = tid; e < kChunk * Sm::pF; e += NT) Af[e] = 0.f;
             __syncthreads();
-            exact_intra_tile<T, CPK, NW, SG>(Af, Sm::pF, kbase(q, c), kbase(k, c), gbase(c), rsK, rsG, kc0, w);
+            exact_intra_tile<T, KD, NW, SG>(Af, Sm::pF, kbase(q, c), kbase(k, c), gbase(c), rsK, rsG, w);
+            __syncthreads();
             for (int e = tid; e < kChunk * kChunk; e += NT) {
                 const int s = e / kChunk, t = e % kChunk;
                 if ((t >> 4) >= (s >> 4)) sm.A[s * Sm::pA + t] = Elem<T>::from_f(t >= s ? Af[t * Sm::pF + s] : 0.f);

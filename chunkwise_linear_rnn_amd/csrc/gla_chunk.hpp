@@ -229,57 +229,54 @@ __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSl
 }
 
 // Exact path of a chunk whose decay leaves the basis range (Eq. 4 element by
-// element): Af[t][s] (fp32, pitch pF, zeroed by the caller) = sum over key
-// columns i of q_ti k_si exp2(B_ti - B_si) for s <= t, each wave taking its
-// CPK columns kc0.. (q, k rows at qrow/krow with row stride rs; the log gate at
-// grow, per column with stride rs, or SG one value per token with stride
-// rsG).  A wave sums its columns for 16 key tokens s in registers, then the
-// waves add their shares to Af in wave order with a barrier between turns, so
-// the sum does not depend on timing.  Every wave of the workgroup must call it.
-template <typename T, int CPK, int NW, bool SG>
-__device__ __forceinline__ void exact_intra_tile(float* Af, int pF, const T* __restrict__ qrow,
+// element): Af[t][s] (fp32, pitch pF) = sum over all KD key columns i of
+// q_ti k_si exp2(B_ti - B_si) for s <= t (entries s > t are left as they are).
+// Wave w owns the key tokens s = w, w + NW, ... and sums every column for them
+// in a fixed order, so each entry is written once by one lane and the result
+// does not depend on timing.  q, k rows at qrow/krow (row stride rs, column 0 of
+// the head), the log gate at grow: per column with stride rs, or SG one value
+// per token with stride rsG.  Token s's values reach the lanes by shuffle.
+// Not inlined: this rarely taken branch would otherwise change the register
+// allocation and schedule of the walk's main loop (2-3 us per launch).
+template <typename T, int KD, int NW, bool SG>
+__device__ __attribute__((noinline)) void exact_intra_tile(float* Af, int pF, const T* __restrict__ qrow,
                                                  const T* __restrict__ krow, const T* __restrict__ grow, int rs,
-                                                 int rsG, int kc0, int w) {
+                                                 int rsG, int w) {
     constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int NS = kChunk / NW;  // key tokens per wave
     const int l = lane_id();
-    for (int s0 = 0; s0 < kChunk; s0 += 16) {
-        float part[16];
+    float part[NS];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) part[u] = 0.f;
-        for (int j0 = 0; j0 < CPK; j0 += VEC) {
-            RowSlab<T, VEC> xq, xk;
-            xq.load(qrow, rs, kc0 + j0);
-            xk.load(krow, rs, kc0 + j0);
-            float bt[VEC];
-            if constexpr (SG) {
-                const float b0 = wave_incl_scan(Elem<T>::to_f(grow[l * rsG]) * kLog2e);
+    for (int u = 0; u < NS; ++u) part[u] = 0.f;
+    float b0 = 0.f;
+    if constexpr (SG) b0 = wave_incl_scan(Elem<T>::to_f(grow[l * rsG]) * kLog2e);
+    for (int j0 = 0; j0 < KD; j0 += VEC) {
+        RowSlab<T, VEC> xq, xk;
+        xq.load(qrow, rs, j0);
+        xk.load(krow, rs, j0);
+        float bt[VEC];
+        if constexpr (SG) {
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) bt[j] = b0;
-            } else {
-                RowSlab<T, VEC> xg;
-                xg.load(grow, rs, kc0 + j0);
+            for (int j = 0; j < VEC; ++j) bt[j] = b0;
+        } else {
+            RowSlab<T, VEC> xg;
+            xg.load(grow, rs, j0);
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
-                wave_incl_scan_n<VEC>(bt);
-            }
-            // token s's k and B come by lane shuffle (VGPRs): scalar broadcasts of
-            // 16 x VEC pairs would crowd the scalar registers of the whole kernel
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int s = s0 + u;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j)
-                    part[u] += xq.get(j) * __shfl(xk.get(j), s) * exp2_fast(bt[j] - __shfl(bt[j], s));
-            }
+            for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
+            wave_incl_scan_n<VEC>(bt);
         }
-        for (int ww = 0; ww < NW; ++ww) {
-            if (w == ww) {
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (l >= s0 + u) Af[l * pF + s0 + u] += part[u];
-            }
-            __syncthreads();
+        for (int u = 0; u < NS; ++u) {
+            const int s = w + NW * u;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                part[u] += xq.get(j) * __shfl(xk.get(j), s) * exp2_fast(bt[j] - __shfl(bt[j], s));
         }
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int s = w + NW * u;
+        if (l >= s) Af[l * pF + s] = part[u];
     }
 }
 

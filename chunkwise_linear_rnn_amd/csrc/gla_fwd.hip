@@ -442,13 +442,14 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                     to_vec4<T>(acc);
             }
         } else {
-            // Eq. 4 element by element: each wave adds its key columns' share of
-            // A[t][s] = sum_i q_ti k_si exp2(B_ti - B_si) into an fp32 tile
-            // (the spare buffer, refilled below once A is final).
+            // Eq. 4 element by element: A[t][s] = sum_i q_ti k_si exp2(B_ti - B_si)
+            // into an fp32 tile (the spare buffer, refilled below once A is final),
+            // each wave summing every key column for its own key tokens s.
             float* Af = reinterpret_cast<float*>(nxt.Ql);
             for (int e = tid; e < kChunk * Sm::pF; e += NT) Af[e] = 0.f;
             __syncthreads();
-            exact_intra_tile<T, CPK, NW, SG>(Af, Sm::pF, kbase(q, c), kbase(k, c), gbase(c), rsK, rsG, kc0, w);
+            exact_intra_tile<T, KD, NW, SG>(Af, Sm::pF, kbase(q, c), kbase(k, c), gbase(c), rsK, rsG, w);
+            __syncthreads();
             for (int e = tid; e < kChunk * kChunk; e += NT) {
                 const int t = e / kChunk, s = e % kChunk;
                 if ((s >> 4) == (t >> 4) || s < t)
