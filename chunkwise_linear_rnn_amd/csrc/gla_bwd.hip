@@ -484,6 +484,41 @@ __device__ __forceinline__ void row_prep(Buf& bf, int pK, int pB, const RowSlab<
     if (wide && l == 0) bf.flag[0] = 1;
 }
 
+// Exact-path intra sums of the pipelined row-split walks, element by element
+// from the raw operand x (k for dq, q for dk; rows at xrow, stride rs), the
+// cumulative log gate B and dP ([t][s], both in LDS), for this wave's key
+// columns kc0 .. kc0+CPK-1:
+//   DK = false: X[t][i] = sum_{s<=t} dP[t][s] x_si exp2(B_ti - B_si)   (lane = t)
+//   DK = true:  X[s][i] = sum_{t>=s} dP[t][s] x_ti exp2(B_ti - B_si)   (lane = s)
+// Terms outside the causal range are selected away (their exp2 may overflow).
+// Not inlined: the rarely taken branch would otherwise reshape the register
+// allocation of the walk's main loop.
+template <typename T, int CPK, bool DK>
+__device__ __attribute__((noinline)) void row_exact_intra(const T* __restrict__ xrow, int rs, int kc0, const float* B,
+                                                          int pB, const T* P, int pP, float* X, int BK) {
+    const int l = lane_id();
+    RowSlab<T, CPK> xr;
+    xr.load(xrow, rs, kc0);
+    float b[CPK], sum[CPK];
+#pragma unroll
+    for (int j = 0; j < CPK; ++j) {
+        b[j] = B[l * pB + kc0 + j];
+        sum[j] = 0.f;
+    }
+    for (int u = 0; u < kChunk; ++u) {
+        const float dp = Elem<T>::to_f(DK ? P[u * pP + l] : P[l * pP + u]);
+        const bool in = DK ? u >= l : u <= l;
+#pragma unroll
+        for (int j = 0; j < CPK; ++j) {
+            const float bu = lane_bcast(b[j], u);
+            const float term = dp * lane_bcast(xr.get(j), u) * exp2_fast(DK ? bu - b[j] : b[j] - bu);
+            sum[j] += in ? term : 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < CPK; ++j) X[l * BK + kc0 + j] = sum[j];
+}
+
 // ---------------------------------------------------------------------------
 // dq walk, software-pipelined (16-bit operands): forwards over one segment for
 // key rows k0 .. k0+BK-1, full V, in the chunk-start basis:
@@ -650,26 +685,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         } else {
             // intra part element by element, sum_{s<=t} dP[t][s] k_s exp2(B_t - B_s),
             // into an fp32 [t][i] tile over the (now unused) value tiles
-            float* Xf = sm.X;
-            RowSlab<T, CPK> xk;
-            xk.load(kbase(k, c), rsK, kc0);
-            float bt[CPK], sum[CPK];
-#pragma unroll
-            for (int j = 0; j < CPK; ++j) {
-                bt[j] = cur.B[l * Sm::pB + kc0 + j];
-                sum[j] = 0.f;
-            }
-            for (int s = 0; s < kChunk; ++s) {
-                const float dp = Elem<T>::to_f(sm.P[l * Sm::pP + s]);
-#pragma unroll
-                for (int j = 0; j < CPK; ++j) {
-                    // s > t: dP is zero there and exp2 may overflow, so the term is selected away
-                    const float term = dp * lane_bcast(xk.get(j), s) * exp2_fast(bt[j] - lane_bcast(bt[j], s));
-                    sum[j] += s <= l ? term : 0.f;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < CPK; ++j) Xf[l * BK + kc0 + j] = sum[j];
+            row_exact_intra<T, CPK, false>(kbase(k, c), rsK, kc0, cur.B, Sm::pB, sm.P, Sm::pP, sm.X, BK);
             __syncthreads();
         }
         {
@@ -925,25 +941,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         if (exact) {
             // intra part element by element, sum_{t>=s} dP^T[s][t] q_t exp2(B_t - B_s),
             // into an fp32 [s][i] tile over the (now unused) value tiles
-            RowSlab<T, CPK> xq;
-            xq.load(kbase(q, c), rsK, kc0);
-            float bs[CPK], sum[CPK];
-#pragma unroll
-            for (int j = 0; j < CPK; ++j) {
-                bs[j] = cur.B[l * Sm::pB + kc0 + j];
-                sum[j] = 0.f;
-            }
-            for (int t = 0; t < kChunk; ++t) {
-                const float dp = Elem<T>::to_f(sm.P[t * Sm::pP + l]);
-#pragma unroll
-                for (int j = 0; j < CPK; ++j) {
-                    // t < s: dP^T is zero there and exp2 may overflow, so the term is selected away
-                    const float term = dp * lane_bcast(xq.get(j), t) * exp2_fast(lane_bcast(bs[j], t) - bs[j]);
-                    sum[j] += t >= l ? term : 0.f;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < CPK; ++j) sm.X[l * BK + kc0 + j] = sum[j];
+            row_exact_intra<T, CPK, true>(kbase(q, c), rsK, kc0, cur.B, Sm::pB, sm.P, Sm::pP, sm.X, BK);
             __syncthreads();
         }
         {
