@@ -837,7 +837,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         run_carry = run[0] + tot[0];
     };
     // scalar gate: this workgroup's sum over its BK key columns of chunk c's dg,
-    // one fp32 partial per key block (summed over the blocks by gla_dg_sum)
+    // one fp32 partial per key block (summed over the blocks by the dv walk)
     auto flush_sg = [&](int c) {
         if (tid < kChunk) {
             float x = 0.f;
@@ -1448,7 +1448,8 @@ __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
                 const T* __restrict__ d_o, const T* __restrict__ ws_dinit, const float* __restrict__ dht,
                 const T* __restrict__ ws_dmid, const float* __restrict__ ws_gmid, int split, int nhalf,
-                T* __restrict__ dv, float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH) {
+                T* __restrict__ dv, float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH,
+                const float* __restrict__ dg_part, int nkb, T* __restrict__ dg) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, true>;  // sm.A holds A^T [s][t]; sm.Vw the d_o slices
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
@@ -1684,6 +1685,19 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         __syncthreads();
     }
     if (ds0 && seg == 0 && half == 0) S.store(ds0 + (long)bh * KD * V, V, col0);
+    if constexpr (SG) {
+        // the scalar gate's gradient of this workgroup's tokens: the dk walk's
+        // per-key-block sums (fp32, [nkb][B*T*H]) added in key-block order
+        if (vb == 0) {
+            const long n = (long)BH * T_;
+            for (int e = tid; e < nchunks * kChunk; e += NT) {
+                const long i = ((long)b * T_ + (long)c_begin * kChunk + e) * H + h;
+                float x = 0.f;
+                for (int j = 0; j < nkb; ++j) x += dg_part[(long)j * n + i];
+                dg[i] = Elem<T>::from_f(x);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1691,18 +1705,6 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 // Segment states of both directions and their combine.  The workgroups span
 // the forward's value width (BV = a.BVS), so the key-side preparation and its
 // loads are not repeated across value blocks.
-// Scalar gate: dg[i] = sum over the nkb key blocks of their partial sums
-// part[kb][i] (fp32, in key-block order), rounded once to the I/O dtype.
-template <typename T>
-__global__ void __launch_bounds__(256)
-gla_dg_sum(const float* __restrict__ part, int nkb, long n, T* __restrict__ dg) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    float x = 0.f;
-    for (int j = 0; j < nkb; ++j) x += part[(long)j * n + i];
-    dg[i] = Elem<T>::from_f(x);
-}
-
 template <typename T, int KD, int BV, bool SG>
 static hipError_t launch_seg_states_g(const BwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
@@ -1757,7 +1759,7 @@ static hipError_t launch_dv_g(const BwdLaunch& a) {
         GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW, SG>), gridh, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_dstate, a.dht,
                            (const T*)a.ws_dmid, a.ws_gmid, (a.seg_len + 1) / 2, nhalf, (T*)a.dv, a.ds0, a.T, a.H, a.V,
-                           a.N, a.P, a.seg_len, (int)a.BH);
+                           a.N, a.P, a.seg_len, (int)a.BH, (const float*)a.ws_dgp, a.K / a.BK, (T*)a.dg);
     } else {
         static_assert(!SG, "scalar gates take the 16-bit path");
         const float* dinit = a.P > 1 ? (const float*)a.ws_dstate : a.dht;
@@ -1812,11 +1814,6 @@ static hipError_t launch_rows_g(const BwdLaunch& a) {
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq,
                            (const T*)a.ws_dstate, a.dht, (const T*)a.ws_hs, (const T*)a.ws_dp, (T*)a.dk, (T*)a.dg,
                            a.ws_dgp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
-        if (SG) {
-            const long n = a.BH * (long)a.T;
-            GLA_LAUNCH("bwd_dg_sum", (gla_dg_sum<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), a.stream,
-                       (const float*)a.ws_dgp, nkb, n, (T*)a.dg);
-        }
     } else {
         static_assert(!SG, "scalar gates take the 16-bit path");
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
