@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kGateThreads = 256;      // forward workgroup
 constexpr int kGateBwdThreads = 1024;  // backward workgroup (one per CU, kGateMaxBlocks of them)
-constexpr int kGateRowsPerGroup = 4;   // rows a lane group has in flight
+constexpr int kGateRowsPerGroup = 2;   // rows a lane group has in flight (2 measured best of 1, 2, 4, 8)
 constexpr int kGateFwdBlocks = 2048;   // forward workgroups (each loops over row passes)
 constexpr int kColsumWaves = 16;       // waves per column group in the column-sum kernel
 
