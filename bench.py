@@ -292,6 +292,52 @@ def out_gate_bench(args, torch, gla, gi):
     print(json.dumps(line), flush=True)
 
 
+def fwd_only_bench(args, torch, gla, gi):
+    """gla_fwd alone on any named workload (including those without backward
+    inputs), reported as tokens/s, % of bf16 MFMA peak (algorithmic flops at
+    C = 64) and % of HBM peak (compulsory bytes e(3K+2V) per token-head)."""
+    w = gi.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
+    dt = w.torch_dtype
+    e = 2 if w.dtype == "bf16" else 4
+    cpu = gi.make_inputs(w)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in cpu.items()}
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    ws = gla.workspace(gla.gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+    fwd = lambda: gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, ws)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    n = max(args.steps, 1) * 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    gla.gla_kernel_timing(True)
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    kt = gla.gla_kernel_timing_read()
+    gla.gla_kernel_timing(False)
+    units = B * T * H
+    peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    flops = fwd_flops_per_token_head(K, V) * units
+    line = {"metric": "GLA forward tokens/sec and %% of MFMA peak (%s)" % w.name, "value": B * T / (ms * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": n, "ms_per_step": ms, "higher_is_better": True,
+            "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, gla_fwd per step" % (
+                w.name, B, H, T, K, V, w.dtype)},
+            "mfma_frac": flops / (ms * 1e-3) / (peak_tf * 1e12),
+            "hbm_frac": e * (3 * K + 2 * V) * units / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "kernels": {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +348,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--decode", action="store_true",
                     help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time gla_fwd alone on --workload (also those without backward inputs)")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="the workload with one log gate per token and head (gla_fwd_scalar / gla_bwd_scalar)")
     ap.add_argument("--out-gate", action="store_true",
@@ -337,6 +385,9 @@ def main():
         return
     if args.out_gate:
         out_gate_bench(args, torch, gla, gi)
+        return
+    if args.fwd_only:
+        fwd_only_bench(args, torch, gla, gi)
         return
 
     w = gi.WORKLOADS[args.workload]
