@@ -171,6 +171,7 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
             a.ws_state = workspace;
             a.ws_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + gla::state_bytes(s, p));
         }
+        if (gla::fwd_wide(s)) a.ws_rec = static_cast<char*>(workspace) + gla::fwd_seg_bytes(s, p);
         a.stream = strm;
         err = gla::launch_fwd(a);
     }

@@ -1,0 +1,329 @@
+// Forward kernels for 16-bit heads with 256 key columns.
+//
+// Method: "Gated Linear Attention Transformers with Hardware-Efficient
+// Training", Section 4.2 (chunkwise form) and Section 4.3 (intra-chunk
+// attention in log-gate space).  The mathematics is that of the column-split
+// walk in gla_fwd.hip: per chunk, with B_t the cumulative log2 gate from the
+// chunk start,
+//   Ql = q * exp2(B_t),  Kt = k * exp2(-B_s)   (k * exp2(B_63 - B_s) for a key
+//   column whose chunk decay leaves the basis range),  A = causal(Ql Kt^T)
+//   (element by element when some column leaves the range),
+//   O = Ql S + A V,      S <- post * (pre * S + Kt^T V).
+//
+// At dk = 256 the state of one value column block is 256 rows deep, so a
+// workgroup holds few value columns and each head's value width is split over
+// several workgroups.  Forming Ql, Kt, the gate factors and A inside every one
+// of them repeats the vector work (cumulative sums, two exponentials per key
+// element) and the 64 x 64 x 256 product once per value block and pass.  Here
+// they are formed once per chunk and head by gla_fwd_wide_prep and stored as a
+// record in the workspace; the state pass and the output walk then stream the
+// records, and their inner loops are matrix products only.
+#pragma once
+
+#include "gla_chunk.hpp"
+
+namespace gla {
+
+// Byte layout of one chunk's record (KD key columns, 16-bit operands).
+template <int KD>
+struct WideRec {
+    static constexpr long oQl = 0;                          // [64][KD]  Ql
+    static constexpr long oKt = oQl + 2L * kChunk * KD;     // [64][KD]  Kt
+    static constexpr long oA = oKt + 2L * kChunk * KD;      // [64][64]  A, zero for s > t
+    static constexpr long oPP = oA + 2L * kChunk * kChunk;  // fp32 [3][KD]: pre, post, B_63
+    static constexpr long oFlag = oPP + 12L * KD;           // int: some column left the basis range
+    static constexpr long bytes = oFlag + 256;
+    static_assert(bytes % 256 == 0, "records stay 256-byte aligned");
+};
+
+template <typename T, int KD>
+struct WidePrepSmem {
+    static constexpr int pQl = tile_pitch<T, KD, false>();
+    static constexpr int pKt = tile_pitch<T, KD, false>();
+    static constexpr int pF = kChunk + 4;  // fp32 A of an exact-path chunk, laid over Ql
+    struct alignas(16) Buf {
+        T Ql[kChunk * pQl];
+        T Kt[kChunk * pKt];
+        float pre[KD];
+        float post[KD];
+        int flag[4];
+    };
+    static_assert(sizeof(T) * kChunk * pQl >= sizeof(float) * kChunk * pF, "exact-path scratch");
+    Buf buf;
+};
+
+// One workgroup (four waves, 64 key columns each) per chunk and head.
+template <typename T, int KD, bool SG>
+__global__ void __launch_bounds__(256)
+gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
+                  unsigned char* __restrict__ rec, int T_, int H, int N) {
+    constexpr int NW = 4, NT = NW * 64, CPK = KD / NW, VEC = 16 / (int)sizeof(T), VPR = KD / VEC;
+    static_assert(CPK <= 64 && (kChunk * VPR) % NT == 0, "prep tiling");
+    using Sm = WidePrepSmem<T, KD>;
+    using R = WideRec<KD>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const long unit = blockIdx.x;  // bh * N + chunk; the grid has exactly BH * N blocks
+    const int bh = (int)(unit / N), c = (int)(unit % N);
+    const int b = bh / H, h = bh % H;
+    const int rsK = H * KD, rsG = SG ? H : rsK;
+    const long row0 = (long)b * T_ + (long)c * kChunk;
+    const T* qb = q + row0 * rsK + (long)h * KD;
+    const T* kb = k + row0 * rsK + (long)h * KD;
+    // g: per key column [B,T,H,K], or (SG) one value per token and head [B,T,H]
+    const T* gb = SG ? g + row0 * H + h : g + row0 * rsK + (long)h * KD;
+    const int kc0 = w * CPK;
+
+    RowSlab<T, CPK> rq, rk;
+    GateSlab<T, CPK, SG> rg;
+    rq.load(qb, rsK, kc0);
+    rk.load(kb, rsK, kc0);
+    rg.load(gb, rsG, kc0);
+    if (tid == 0) sm.buf.flag[0] = 0;
+    __syncthreads();
+    pipe_prep<T, CPK>(sm.buf, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, CPK / VEC);
+    __syncthreads();
+
+    unsigned char* r = rec + unit * R::bytes;
+    T* oQl = reinterpret_cast<T*>(r + R::oQl);
+    T* oKt = reinterpret_cast<T*>(r + R::oKt);
+    T* oA = reinterpret_cast<T*>(r + R::oA);
+    float* opp = reinterpret_cast<float*>(r + R::oPP);
+#pragma unroll
+    for (int i = 0; i < kChunk * VPR / NT; ++i) {
+        const int p = tid + i * NT, row = p / VPR, col = (p % VPR) * VEC;
+        *reinterpret_cast<u32x4*>(oQl + row * KD + col) =
+            *reinterpret_cast<const u32x4*>(sm.buf.Ql + row * Sm::pQl + col);
+        *reinterpret_cast<u32x4*>(oKt + row * KD + col) =
+            *reinterpret_cast<const u32x4*>(sm.buf.Kt + row * Sm::pKt + col);
+    }
+    for (int i = tid; i < KD; i += NT) {
+        const float pre = sm.buf.pre[i], post = sm.buf.post[i];
+        opp[i] = pre;
+        opp[KD + i] = post;
+        opp[2 * KD + i] = log2f(pre * post);  // one factor is 1: the chunk's log2 decay B_63
+    }
+    const bool exact = sm.buf.flag[0] != 0;
+    if (tid == 0) *reinterpret_cast<int*>(r + R::oFlag) = exact ? 1 : 0;
+    if (!exact) {
+        // the ten lower-triangular 16 x 16 tiles
+        for (int tile = w; tile < 10; tile += NW) {
+            int is, js;
+            decode_tile(tile, is, js);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks)
+                acc = mma32(acc, frag_rm<T>(sm.buf.Kt, Sm::pKt, 16 * js, 32 * ks),
+                            frag_rm<T>(sm.buf.Kt, Sm::pKt, 16 * js, 32 * ks + 16),
+                            frag_rm<T>(sm.buf.Ql, Sm::pQl, 16 * is, 32 * ks),
+                            frag_rm<T>(sm.buf.Ql, Sm::pQl, 16 * is, 32 * ks + 16));
+            // acc holds A^T[s][t] for s = 16js + 4(l/16) + r, t = 16is + l%16
+            if (is == js) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * (l >> 4) + e > (l & 15)) acc[e] = 0.f;
+            }
+            *reinterpret_cast<vec4_t<T>*>(oA + (16 * is + (l & 15)) * kChunk + 16 * js + 4 * (l >> 4)) =
+                to_vec4<T>(acc);
+        }
+        // the six tiles above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        for (int z = w; z < 6; z += NW) {
+            const int is = (z >= 3) + (z >= 5);
+            const int js = z + 1 - (is == 1 ? 2 : (is == 2 ? 3 : 0));
+            *reinterpret_cast<vec4_t<T>*>(oA + (16 * is + (l & 15)) * kChunk + 16 * js + 4 * (l >> 4)) =
+                to_vec4<T>(zero4());
+        }
+    } else {
+        // Eq. 4 element by element into an fp32 tile laid over Ql, whose copy
+        // to the record every thread has finished at this barrier
+        __syncthreads();
+        float* Af = reinterpret_cast<float*>(sm.buf.Ql);
+        exact_intra_tile<T, KD, NW, SG>(Af, Sm::pF, qb, kb, gb, rsK, rsG, w);
+        __syncthreads();
+        for (int e = tid; e < kChunk * kChunk; e += NT) {
+            const int t = e / kChunk, s = e % kChunk;
+            oA[e] = Elem<T>::from_f(s <= t ? Af[t * Sm::pF + s] : 0.f);
+        }
+    }
+}
+
+template <typename T, int KD, int BV, bool OUT>
+struct WideSmem {
+    static constexpr int NW = 4;
+    static constexpr int CW = BV / NW;  // value columns per wave
+    static constexpr int pQl = tile_pitch<T, KD, false>();
+    static constexpr int pKt = tile_pitch<T, KD, false>();
+    static constexpr int pA = kChunk + Elem<T>::pad;
+    // wave-private V slices read with ds_read_b64_tr_b16: a pitch of 16 or 32
+    // two-byte columns keeps the four rows of a 16-lane group on disjoint banks
+    static constexpr int pW = CW;
+    static_assert(CW == 16 || CW == 32, "value slice width");
+    alignas(16) T Kt[kChunk * pKt];
+    alignas(16) T Vw[NW * kChunk * pW];
+    alignas(16) float pp[2 * KD];  // pre, post
+    alignas(16) T Ql[OUT ? kChunk * pQl : 8];
+    alignas(16) T A[OUT ? kChunk * pA : 8];
+    int flag;
+};
+
+// The state pass (OUT = false: segments 0 .. nseg-1 from a zero state, the
+// local state S*_p in the input dtype and the segment's log2 decay for the
+// combine) and the output walk (OUT = true: every segment from S_init(p),
+// writing O and, for the last segment, the final state).  Four waves; wave w
+// owns value columns col0 .. col0 + BV/4 - 1 and the whole 256-row depth of
+// the state in VGPRs.  Per chunk: one barrier, the record's tiles from
+// registers into LDS, the next chunk's record into registers, a barrier, then
+// the products; the loads have the whole chunk's matrix work to land.
+template <typename T, int KD, int BV, bool OUT>
+__global__ void __launch_bounds__(256)
+gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
+                  const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
+                  T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
+                  int seg_len, int nseg, int BH) {
+    constexpr int NW = 4, NT = NW * 64;
+    using Sm = WideSmem<T, KD, BV, OUT>;
+    using R = WideRec<KD>;
+    constexpr int CW = Sm::CW, CB = CW / 16;
+    static_assert(2 * KD / 4 <= NT && KD <= NT, "gate factors: one vector or value per thread");
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int nvb = V / BV;
+    int unit, vb;
+    xcd_decode(nvb, unit, vb);
+    if (unit >= BH * nseg) return;
+    const int seg = unit % nseg;
+    const int bh = unit / nseg;
+    const int b = bh / H, h = bh % H;
+    const int c_begin = seg * seg_len;
+    const int c_end = min(N, c_begin + seg_len);
+    const int rsV = H * V;
+    const int col0 = vb * BV + w * CW;  // first value column of this wave
+
+    StateRegs<KD, CB> S;
+    if (OUT && seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
+    else if (OUT && s0) S.load(s0 + (long)bh * KD * V, V, col0);
+    else S.zero();
+    float gtot = 0.f;  // state pass: thread tid sums B_63 of key column tid
+
+    TileRegs<T, KD, NT> rQl, rKt;
+    TileRegs<T, kChunk, NT> rA;
+    TileRegs<T, CW, 64> rv;
+    f32x4 rpp = zero4();
+    float rbl = 0.f;
+    int rflag = 0;
+    auto recp = [&](int c) { return rec + ((long)bh * N + c) * R::bytes; };
+    auto vrow = [&](int c) { return v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
+    auto fetch = [&](int c) {
+        const unsigned char* r = recp(c);
+        rKt.load(reinterpret_cast<const T*>(r + R::oKt), KD, tid);
+        if constexpr (OUT) {
+            rQl.load(reinterpret_cast<const T*>(r + R::oQl), KD, tid);
+            rA.load(reinterpret_cast<const T*>(r + R::oA), kChunk, tid);
+        }
+        if (tid < KD / 2) rpp = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(r + R::oPP) + 4 * tid);
+        if (!OUT && tid < KD) rbl = reinterpret_cast<const float*>(r + R::oPP)[2 * KD + tid];
+        if (tid == 0) rflag = *reinterpret_cast<const int*>(r + R::oFlag);
+        rv.load(vrow(c), rsV, l);
+    };
+    auto stash = [&]() {
+        rKt.store_lds(sm.Kt, Sm::pKt, tid);
+        if constexpr (OUT) {
+            rQl.store_lds(sm.Ql, Sm::pQl, tid);
+            rA.store_lds(sm.A, Sm::pA, tid);
+        }
+        if (tid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp + 4 * tid) = rpp;
+        if (!OUT && tid < KD) gtot += rbl;
+        if (tid == 0) sm.flag = rflag;
+        rv.store_lds(sm.Vw + w * kChunk * Sm::pW, Sm::pW, l);
+    };
+
+    if (c_begin < c_end) fetch(c_begin);
+    for (int c = c_begin; c < c_end; ++c) {
+        __syncthreads();  // every read of the previous chunk's tiles is done
+        stash();
+        if (c + 1 < c_end) fetch(c + 1);
+        __syncthreads();
+        const T* Vw = sm.Vw + w * kChunk * Sm::pW;
+        vec4_t<T> vf[4][CB];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
+        if constexpr (OUT) {
+            // O^T[j][t] = sum_i S[i][j] Ql[t][i] + sum_s V[s][j] A[t][s]
+            f32x4 acc[4][CB];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                vec4_t<T> sf[CB][2];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
+                    sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const vec4_t<T> blo = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks);
+                    const vec4_t<T> bhi = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], blo, bhi);
+                }
+            }
+            T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+                for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
+                    const vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
+                    const vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[rb][cb] = mma32(acc[rb][cb], vf[2 * ks2][cb], vf[2 * ks2 + 1][cb], blo, bhi);
+                }
+                // slot e: column j = col0 + 16cb + 4(l/16) + e, token t = 16rb + l%16
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    *reinterpret_cast<vec4_t<T>*>(obase + (16 * rb + (l & 15)) * rsV + 16 * cb + 4 * (l >> 4)) =
+                        to_vec4<T>(acc[rb][cb]);
+            }
+        }
+        // S <- post * (pre * S + Kt^T V); pre is 1 in every column unless some
+        // column of the chunk left the basis range (the flag)
+        if (sm.flag) {
+#pragma unroll
+            for (int a = 0; a < KD / 16; ++a) {
+                const f32x4 pre = *reinterpret_cast<const f32x4*>(sm.pp + 16 * a + 4 * (l >> 4));
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= pre;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int a = 0; a < KD / 16; ++a) {
+                const vec4_t<T> xlo = frag_cm<T>(sm.Kt, Sm::pKt, 32 * ks, 16 * a);
+                const vec4_t<T> xhi = frag_cm<T>(sm.Kt, Sm::pKt, 32 * ks + 16, 16 * a);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    S.s[a][cb] = mma32(S.s[a][cb], xlo, xhi, vf[2 * ks][cb], vf[2 * ks + 1][cb]);
+            }
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a) {
+            const f32x4 post = *reinterpret_cast<const f32x4*>(sm.pp + KD + 16 * a + 4 * (l >> 4));
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= post;
+        }
+    }
+    if constexpr (OUT) {
+        if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V, V, col0);
+    } else {
+        S.store(ws_state + ((long)bh * P + seg) * (long)KD * V, V, col0);
+        // each segment's gate total is written by one workgroup only
+        if (vb == 0 && tid < KD) ws_gate[((long)bh * P + seg) * KD + tid] = gtot;
+    }
+}
+
+}  // namespace gla

@@ -19,6 +19,7 @@ struct FwdLaunch {
     float* s_final;
     void* ws_state;   // [BH][P][K][V] in the input dtype
     float* ws_gate;   // [BH][P][K]    fp32 (log2 of the segment decay)
+    void* ws_rec;     // [BH][N] chunk records of the wide-head forward
     hipStream_t stream;
 };
 

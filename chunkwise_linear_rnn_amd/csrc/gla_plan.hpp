@@ -64,7 +64,20 @@ inline Plan make_plan(const Shape& s, int col_blocks_hint) {
     return p;
 }
 
+// 16-bit heads with 256 key columns: the forward forms each chunk's operands
+// once per chunk and head (a record in the workspace), and its state and output
+// passes take 128 value columns per four-wave workgroup.
+inline bool fwd_wide(const Shape& s) { return s.bf16 && s.K == 256; }
+constexpr size_t wide_record_bytes(int64_t K) { return (size_t)(4 * 64 * K + 2 * 64 * 64 + 12 * K + 256); }
+
 inline Plan make_fwd_plan(const Shape& s) {
+    if (fwd_wide(s)) {
+        const int bv = (int)(s.V < 128 ? s.V : 128);
+        Plan p = make_plan(s, (int)(s.V / bv));
+        p.BV = bv;
+        p.NW = 4;
+        return p;
+    }
     int bv = plan_bv(s);
     return make_plan(s, (int)(s.V / bv));
 }
@@ -103,11 +116,19 @@ inline size_t hs_bytes(const Shape& s, const Plan& p) {
     return (size_t)p.BH * p.N * (size_t)s.K * (size_t)s.V * (s.bf16 ? 2 : 4);
 }
 
-inline size_t fwd_workspace_bytes(const Shape& s) {
-    Plan p = make_fwd_plan(s);
+// segment states and gate totals (P > 1), then the chunk records (wide heads)
+inline size_t fwd_seg_bytes(const Shape& s, const Plan& p) {
     if (p.P <= 1 || p.BH == 0) return 0;
     size_t gt = (size_t)p.BH * p.P * (size_t)s.K * sizeof(float);
     return state_bytes(s, p) + round256(gt);
+}
+
+inline size_t fwd_workspace_bytes(const Shape& s) {
+    Plan p = make_fwd_plan(s);
+    if (p.BH == 0) return 0;
+    size_t n = fwd_seg_bytes(s, p);
+    if (fwd_wide(s)) n += (size_t)p.BH * p.N * wide_record_bytes(s.K);
+    return n;
 }
 
 }  // namespace gla
