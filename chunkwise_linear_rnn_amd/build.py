@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgla.so")
 
-SOURCES = ["gla_api.cpp", "gla_timing.cpp", "gla_fwd.hip", "gla_bwd.hip", "gla_decode.hip", "gla_gate.hip"]
+SOURCES = ["gla_api.cpp", "gla_timing.cpp", "gla_fwd.hip", "gla_fwd_wide.hip", "gla_bwd.hip", "gla_decode.hip",
+           "gla_gate.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.  The
@@ -34,9 +35,14 @@ def _hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+# Per-file additions.  The wide-head forward keeps its MFMA accumulators (the
+# state) in VGPRs: it decays the state with vector multiplies every chunk.
+EXTRA = {"gla_fwd_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))

@@ -18,9 +18,7 @@
 //        final state for the last segment.
 // With P = 1 only step 3 runs (the non-materialised form of Section 3.3).
 #include "gla_chunk.hpp"
-#include "gla_fwd_wide.hpp"
 #include "gla_launch.hpp"
-#include "gla_plan.hpp"
 #include "gla_timing.hpp"
 
 namespace gla {
@@ -576,7 +574,7 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 // ---------------------------------------------------------------------------
 // Host launchers.
 template <typename T>
-static void launch_combine_fwd(const FwdLaunch& a, int KD) {
+void launch_combine_fwd(const FwdLaunch& a, int KD) {
     const long KV = (long)KD * a.V;
     if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
         dim3 g2((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH);
@@ -636,36 +634,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     return launch_fwd_sg<T, KD, BV, false>(a);
 }
 
-// Wide heads (16-bit, dk = 256): chunk records, then the state pass over
-// segments 0..P-2, the combine, and the output walk over every segment.
-template <int KD, int BV, bool SG>
-static hipError_t launch_fwd_wide(const FwdLaunch& a) {
-    using T = bf16;
-    static_assert(sizeof(WidePrepSmem<T, KD>) <= 80 * 1024, "two prep workgroups per CU");
-    static_assert(sizeof(WideSmem<T, KD, BV, true>) <= 160 * 1024, "LDS budget");
-    static_assert(WideRec<KD>::bytes == (long)wide_record_bytes(KD), "record size as the workspace plans it");
-    const int nvb = a.V / BV;
-    unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);
-    GLA_LAUNCH("fwd_prep", (gla_fwd_wide_prep<T, KD, SG>), dim3((unsigned)(a.BH * a.N)), dim3(256), a.stream,
-               (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N);
-    if (a.P > 1) {
-        const int nseg = a.P - 1;
-        GLA_LAUNCH("fwd_seg_state", (gla_fwd_wide_walk<T, KD, BV, false>), dim3((unsigned)xcd_grid(nseg * a.BH, nvb)),
-                   dim3(256), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)nullptr,
-                   (const float*)nullptr, (T*)nullptr, (float*)nullptr, (T*)a.ws_state, a.ws_gate, a.T, a.H, a.V,
-                   a.N, a.P, a.seg_len, nseg, (int)a.BH);
-        launch_combine_fwd<T>(a, KD);
-    }
-    GLA_LAUNCH("fwd_walk", (gla_fwd_wide_walk<T, KD, BV, true>), dim3((unsigned)xcd_grid(a.P * a.BH, nvb)),
-               dim3(256), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,
-               a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH);
-    return hipGetLastError();
-}
-
-template <int KD, int BV>
-static hipError_t launch_fwd_wide_t(const FwdLaunch& a) {
-    return a.sg ? launch_fwd_wide<KD, BV, true>(a) : launch_fwd_wide<KD, BV, false>(a);
-}
+template void launch_combine_fwd<bf16>(const FwdLaunch& a, int KD);
 
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
@@ -684,8 +653,7 @@ hipError_t launch_fwd(const FwdLaunch& a) {
             if (a.BV == 128) return launch_fwd_t<bf16, 128, 128>(a);
             if (a.BV == 256) return launch_fwd_t<bf16, 128, 256>(a);
         } else if (a.K == 256) {
-            if (a.BV == 64) return launch_fwd_wide_t<256, 64>(a);
-            if (a.BV == 128) return launch_fwd_wide_t<256, 128>(a);
+            return launch_fwd_wide(a);
         }
     } else {
         if (a.K == 64) {

@@ -175,7 +175,7 @@ struct WideSmem {
 // registers into LDS, the next chunk's record into registers, a barrier, then
 // the products; the loads have the whole chunk's matrix work to land.
 template <typename T, int KD, int BV, bool OUT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
                   T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
@@ -256,21 +256,42 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = zero4();
+            // the Ql fragments of step ks + 1 are read while the MFMAs of step ks run
+            {
+                vec4_t<T> qf[2][4][2];
+                auto rd = [&](int ks, vec4_t<T> (&x)[4][2]) {
 #pragma unroll
-            for (int ks = 0; ks < KD / 32; ++ks) {
-                vec4_t<T> sf[CB][2];
+                    for (int rb = 0; rb < 4; ++rb) {
+                        x[rb][0] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks);
+                        x[rb][1] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
+                    }
+                };
+                __builtin_amdgcn_sched_barrier(0);
+                rd(0, qf[0]);
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
-                    sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                for (int ks = 0; ks < KD / 32; ++ks) {
+                    if (ks + 1 < KD / 32) rd(ks + 1, qf[(ks + 1) & 1]);
+                    vec4_t<T> sf[CB][2];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
+                        sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], qf[ks & 1][rb][0], qf[ks & 1][rb][1]);
                 }
+                // eight reads ahead, then one read per MFMA (CB = 2) or two (CB = 1)
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const vec4_t<T> blo = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks);
-                    const vec4_t<T> bhi = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], blo, bhi);
+                for (int i = 0; i < (KD / 32 - 1) * 4 * CB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 / CB, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * CB, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
 #pragma unroll
@@ -300,16 +321,34 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                 for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= pre;
             }
         }
+        // 2 x KD/16 steps (ks, a); the Kt fragments run LA steps ahead of the MFMAs
+        {
+            constexpr int NA = KD / 16, NS = 2 * NA, LA = 4;
+            vec4_t<T> xf[LA][2];
+            auto rd = [&](int n, vec4_t<T> (&x)[2]) {
+                x[0] = frag_cm<T>(sm.Kt, Sm::pKt, 32 * (n / NA), 16 * (n % NA));
+                x[1] = frag_cm<T>(sm.Kt, Sm::pKt, 32 * (n / NA) + 16, 16 * (n % NA));
+            };
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int n = 0; n < LA; ++n) rd(n, xf[n]);
 #pragma unroll
-            for (int a = 0; a < KD / 16; ++a) {
-                const vec4_t<T> xlo = frag_cm<T>(sm.Kt, Sm::pKt, 32 * ks, 16 * a);
-                const vec4_t<T> xhi = frag_cm<T>(sm.Kt, Sm::pKt, 32 * ks + 16, 16 * a);
+            for (int n = 0; n < NS; ++n) {
+                const int ks = n / NA, a = n % NA;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-                    S.s[a][cb] = mma32(S.s[a][cb], xlo, xhi, vf[2 * ks][cb], vf[2 * ks + 1][cb]);
+                    S.s[a][cb] = mma32(S.s[a][cb], xf[n % LA][0], xf[n % LA][1], vf[2 * ks][cb], vf[2 * ks + 1][cb]);
+                if (n + LA < NS) rd(n + LA, xf[n % LA]);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+            for (int n = 0; n < NS - LA; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, CB * LA, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int a = 0; a < KD / 16; ++a) {
             const f32x4 post = *reinterpret_cast<const f32x4*>(sm.pp + KD + 16 * a + 4 * (l >> 4));

@@ -58,6 +58,7 @@ struct DecodeLaunch {
 };
 
 hipError_t launch_fwd(const FwdLaunch& a);
+hipError_t launch_fwd_wide(const FwdLaunch& a);  // 16-bit, K = 256
 hipError_t launch_decode(const DecodeLaunch& a);
 hipError_t launch_bwd(const BwdLaunch& a);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream);
