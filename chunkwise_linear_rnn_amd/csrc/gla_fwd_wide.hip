@@ -31,13 +31,13 @@ static hipError_t launch_fwd_wide_bv(const FwdLaunch& a) {
     if (a.P > 1) {
         const int nseg = a.P - 1;
         GLA_LAUNCH("fwd_seg_state", (gla_fwd_wide_walk<T, KD, BV, false>), dim3((unsigned)xcd_grid(nseg * a.BH, nvb)),
-                   dim3(256), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)nullptr,
+                   dim3(512), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)nullptr,
                    (const float*)nullptr, (T*)nullptr, (float*)nullptr, (T*)a.ws_state, a.ws_gate, a.T, a.H, a.V,
                    a.N, a.P, a.seg_len, nseg, (int)a.BH);
         launch_combine_fwd<T>(a, KD);
     }
     GLA_LAUNCH("fwd_walk", (gla_fwd_wide_walk<T, KD, BV, true>), dim3((unsigned)xcd_grid(a.P * a.BH, nvb)),
-               dim3(256), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,
+               dim3(512), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,
                a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH);
     return hipGetLastError();
 }

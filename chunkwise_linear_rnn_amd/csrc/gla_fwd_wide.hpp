@@ -149,44 +149,56 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
 template <typename T, int KD, int BV, bool OUT>
 struct WideSmem {
-    static constexpr int NW = 4;
-    static constexpr int CW = BV / NW;  // value columns per wave
+    static constexpr int NC = 4;        // consumer (matrix) waves
+    static constexpr int CW = BV / NC;  // value columns per consumer wave
     static constexpr int pQl = tile_pitch<T, KD, false>();
-    static constexpr int pKt = tile_pitch<T, KD, false>();
+    // Kt is read by column fragments in the state update: a row pitch of 8 (mod 64)
+    // dwords puts the 8-dword windows of eight consecutive rows on disjoint banks
+    static constexpr int pKt = KD + 16;
     static constexpr int pA = kChunk + Elem<T>::pad;
     // wave-private V slices read with ds_read_b64_tr_b16: a pitch of 16 or 32
     // two-byte columns keeps the four rows of a 16-lane group on disjoint banks
     static constexpr int pW = CW;
     static_assert(CW == 16 || CW == 32, "value slice width");
-    alignas(16) T Kt[kChunk * pKt];
-    alignas(16) T Vw[NW * kChunk * pW];
-    alignas(16) float pp[2 * KD];  // pre, post
+    // two buffers of everything but Ql, which the output walk refills between
+    // the inter-chunk product and the rest of the chunk
+    alignas(16) T Kt[2][kChunk * pKt];
+    alignas(16) T Vw[2][NC * kChunk * pW];
+    alignas(16) float pp[2][2 * KD];  // pre, post
+    alignas(16) T A[OUT ? 2 : 1][OUT ? kChunk * pA : 8];
     alignas(16) T Ql[OUT ? kChunk * pQl : 8];
-    alignas(16) T A[OUT ? kChunk * pA : 8];
-    int flag;
+    int flag[2];
 };
 
 // The state pass (OUT = false: segments 0 .. nseg-1 from a zero state, the
 // local state S*_p in the input dtype and the segment's log2 decay for the
 // combine) and the output walk (OUT = true: every segment from S_init(p),
-// writing O and, for the last segment, the final state).  Four waves; wave w
-// owns value columns col0 .. col0 + BV/4 - 1 and the whole 256-row depth of
-// the state in VGPRs.  Per chunk: one barrier, the record's tiles from
-// registers into LDS, the next chunk's record into registers, a barrier, then
-// the products; the loads have the whole chunk's matrix work to land.
+// writing O and, for the last segment, the final state).
+//
+// Eight waves: waves 0-3 hold the state (wave w: value columns col0 .. col0 +
+// BV/4 - 1, all 256 rows, in VGPRs) and run the matrix products; waves 4-7 move
+// the records from memory into LDS.  A SIMD runs one wave of each kind, so the
+// loads and LDS writes overlap the MFMAs.  Per chunk c (buffer c&1):
+//   consumers: O_inter = Ql S  | barrier X | O += A V, store O; S update | barrier E
+//   producers: Kt, A, V, gate factors of c+1 into buffer (c+1)&1 | barrier X |
+//              Ql of c+1 into the single Ql buffer | barrier E
+// Each producer wave keeps the records of two chunks in registers: at chunk c
+// it fetches chunk c+2 into the set that chunk c came in.
 template <typename T, int KD, int BV, bool OUT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
                   T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
                   int seg_len, int nseg, int BH) {
-    constexpr int NW = 4, NT = NW * 64;
+    constexpr int NC = 4, NP = 64 * NC;  // consumer waves; producer threads
     using Sm = WideSmem<T, KD, BV, OUT>;
     using R = WideRec<KD>;
     constexpr int CW = Sm::CW, CB = CW / 16;
-    static_assert(2 * KD / 4 <= NT && KD <= NT, "gate factors: one vector or value per thread");
+    static_assert(2 * KD / 4 <= NP && KD <= NP, "gate factors: one vector or value per producer thread");
     __shared__ Sm sm;
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int tid = threadIdx.x, l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const bool producer = w >= NC;
     const int nvb = V / BV;
     int unit, vb;
     xcd_decode(nvb, unit, vb);
@@ -197,109 +209,138 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     const int c_begin = seg * seg_len;
     const int c_end = min(N, c_begin + seg_len);
     const int rsV = H * V;
-    const int col0 = vb * BV + w * CW;  // first value column of this wave
+    const int cw = producer ? w - NC : w;  // the consumer wave a value slice belongs to
+    const int col0 = vb * BV + cw * CW;
 
+    if (producer) {
+        // ---------------- producers: records -> LDS
+        const int ptid = tid - NP;
+        float gtot = 0.f;  // state pass: thread ptid sums B_63 of key column ptid
+        struct Regs {
+            TileRegs<T, KD, NP> Ql, Kt;
+            TileRegs<T, kChunk, NP> A;
+            TileRegs<T, CW, 64> v;
+            f32x4 pp;
+            float bl;
+            int flag;
+        };
+        Regs ra, rb;
+        auto fetch = [&](Regs& x, int c) {
+            const unsigned char* r = rec + ((long)bh * N + c) * R::bytes;
+            x.Kt.load(reinterpret_cast<const T*>(r + R::oKt), KD, ptid);
+            if constexpr (OUT) {
+                x.Ql.load(reinterpret_cast<const T*>(r + R::oQl), KD, ptid);
+                x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
+            }
+            const float* pp = reinterpret_cast<const float*>(r + R::oPP);
+            if (ptid < KD / 2) x.pp = *reinterpret_cast<const f32x4*>(pp + 4 * ptid);
+            if (!OUT && ptid < KD) x.bl = pp[2 * KD + ptid];
+            if (ptid == 0) x.flag = *reinterpret_cast<const int*>(r + R::oFlag);
+            x.v.load(v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0, rsV, l);
+        };
+        // everything but Ql into buffer bf
+        auto stash = [&](const Regs& x, int bf) {
+            x.Kt.store_lds(sm.Kt[bf], Sm::pKt, ptid);
+            if constexpr (OUT) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
+            if (ptid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp[bf] + 4 * ptid) = x.pp;
+            if (!OUT && ptid < KD) gtot += x.bl;
+            if (ptid == 0) sm.flag[bf] = x.flag;
+            x.v.store_lds(sm.Vw[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
+        };
+        // chunk c+1 (in x) into LDS during chunk c, then chunk c+3 into x
+        auto step = [&](Regs& x, int c) {
+            const bool more = c + 1 < c_end;
+            if (more) stash(x, (c + 1) & 1);
+            if constexpr (OUT) {
+                __syncthreads();  // X: the consumers are done with Ql(c)
+                if (more) x.Ql.store_lds(sm.Ql, Sm::pQl, ptid);
+            }
+            if (c + 3 < c_end) fetch(x, c + 3);
+            __syncthreads();  // E
+        };
+        if (c_begin < c_end) {
+            fetch(ra, c_begin);
+            stash(ra, c_begin & 1);  // chunk c is read from buffer c & 1
+            if constexpr (OUT) ra.Ql.store_lds(sm.Ql, Sm::pQl, ptid);
+            if (c_begin + 1 < c_end) fetch(rb, c_begin + 1);
+            if (c_begin + 2 < c_end) fetch(ra, c_begin + 2);
+        }
+        __syncthreads();  // E of the prologue
+        for (int c = c_begin; c < c_end; c += 2) {
+            step(rb, c);
+            if (c + 1 < c_end) step(ra, c + 1);
+        }
+        if (!OUT && vb == 0 && ptid < KD) ws_gate[((long)bh * P + seg) * KD + ptid] = gtot;
+        return;
+    }
+
+    // ---------------- consumers: the state and the matrix products
     StateRegs<KD, CB> S;
     if (OUT && seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
     else if (OUT && s0) S.load(s0 + (long)bh * KD * V, V, col0);
     else S.zero();
-    float gtot = 0.f;  // state pass: thread tid sums B_63 of key column tid
-
-    TileRegs<T, KD, NT> rQl, rKt;
-    TileRegs<T, kChunk, NT> rA;
-    TileRegs<T, CW, 64> rv;
-    f32x4 rpp = zero4();
-    float rbl = 0.f;
-    int rflag = 0;
-    auto recp = [&](int c) { return rec + ((long)bh * N + c) * R::bytes; };
-    auto vrow = [&](int c) { return v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0; };
-    auto fetch = [&](int c) {
-        const unsigned char* r = recp(c);
-        rKt.load(reinterpret_cast<const T*>(r + R::oKt), KD, tid);
-        if constexpr (OUT) {
-            rQl.load(reinterpret_cast<const T*>(r + R::oQl), KD, tid);
-            rA.load(reinterpret_cast<const T*>(r + R::oA), kChunk, tid);
-        }
-        if (tid < KD / 2) rpp = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(r + R::oPP) + 4 * tid);
-        if (!OUT && tid < KD) rbl = reinterpret_cast<const float*>(r + R::oPP)[2 * KD + tid];
-        if (tid == 0) rflag = *reinterpret_cast<const int*>(r + R::oFlag);
-        rv.load(vrow(c), rsV, l);
-    };
-    auto stash = [&]() {
-        rKt.store_lds(sm.Kt, Sm::pKt, tid);
-        if constexpr (OUT) {
-            rQl.store_lds(sm.Ql, Sm::pQl, tid);
-            rA.store_lds(sm.A, Sm::pA, tid);
-        }
-        if (tid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp + 4 * tid) = rpp;
-        if (!OUT && tid < KD) gtot += rbl;
-        if (tid == 0) sm.flag = rflag;
-        rv.store_lds(sm.Vw + w * kChunk * Sm::pW, Sm::pW, l);
-    };
-
-    if (c_begin < c_end) fetch(c_begin);
+    __syncthreads();  // E of the prologue
     for (int c = c_begin; c < c_end; ++c) {
-        __syncthreads();  // every read of the previous chunk's tiles is done
-        stash();
-        if (c + 1 < c_end) fetch(c + 1);
-        __syncthreads();
-        const T* Vw = sm.Vw + w * kChunk * Sm::pW;
+        const int bf = c & 1;
+        const T* Vw = sm.Vw[bf] + w * kChunk * Sm::pW;
         vec4_t<T> vf[4][CB];
+        f32x4 acc[4][CB];
+        if constexpr (OUT) {
+            // O^T[j][t] = sum_i S[i][j] Ql[t][i]; the Ql fragments of step ks + 1
+            // are read while the MFMAs of step ks run
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = zero4();
+            vec4_t<T> qf[2][4][2];
+            auto rd = [&](int ks, vec4_t<T> (&x)[4][2]) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    x[rb][0] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks);
+                    x[rb][1] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
+                }
+            };
+            __builtin_amdgcn_sched_barrier(0);
+            rd(0, qf[0]);
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                if (ks + 1 < KD / 32) rd(ks + 1, qf[(ks + 1) & 1]);
+                vec4_t<T> sf[CB][2];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
+                    sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], qf[ks & 1][rb][0], qf[ks & 1][rb][1]);
+            }
+            // eight reads ahead, then one read per MFMA (CB = 2) or two (CB = 1)
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < (KD / 32 - 1) * 4 * CB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 / CB, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * CB, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();  // X: Ql may be refilled
+        }
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
         if constexpr (OUT) {
-            // O^T[j][t] = sum_i S[i][j] Ql[t][i] + sum_s V[s][j] A[t][s]
-            f32x4 acc[4][CB];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = zero4();
-            // the Ql fragments of step ks + 1 are read while the MFMAs of step ks run
-            {
-                vec4_t<T> qf[2][4][2];
-                auto rd = [&](int ks, vec4_t<T> (&x)[4][2]) {
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) {
-                        x[rb][0] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks);
-                        x[rb][1] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
-                    }
-                };
-                __builtin_amdgcn_sched_barrier(0);
-                rd(0, qf[0]);
-#pragma unroll
-                for (int ks = 0; ks < KD / 32; ++ks) {
-                    if (ks + 1 < KD / 32) rd(ks + 1, qf[(ks + 1) & 1]);
-                    vec4_t<T> sf[CB][2];
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        sf[cb][0] = to_vec4<T>(S.s[2 * ks][cb]);
-                        sf[cb][1] = to_vec4<T>(S.s[2 * ks + 1][cb]);
-                    }
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-                            acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], qf[ks & 1][rb][0], qf[ks & 1][rb][1]);
-                }
-                // eight reads ahead, then one read per MFMA (CB = 2) or two (CB = 1)
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-                for (int i = 0; i < (KD / 32 - 1) * 4 * CB; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2 / CB, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 4 * CB, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            // O^T[j][t] += sum_s V[s][j] A[t][s]
             T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
                 for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
-                    const vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
-                    const vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
+                    const vec4_t<T> blo = frag_rm<T>(sm.A[bf], Sm::pA, 16 * rb, 32 * ks2);
+                    const vec4_t<T> bhi = frag_rm<T>(sm.A[bf], Sm::pA, 16 * rb, 32 * ks2 + 16);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
                         acc[rb][cb] = mma32(acc[rb][cb], vf[2 * ks2][cb], vf[2 * ks2 + 1][cb], blo, bhi);
@@ -313,21 +354,24 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         }
         // S <- post * (pre * S + Kt^T V); pre is 1 in every column unless some
         // column of the chunk left the basis range (the flag)
-        if (sm.flag) {
+        const float* pre = sm.pp[bf];
+        const float* post = sm.pp[bf] + KD;
+        if (sm.flag[bf]) {
 #pragma unroll
             for (int a = 0; a < KD / 16; ++a) {
-                const f32x4 pre = *reinterpret_cast<const f32x4*>(sm.pp + 16 * a + 4 * (l >> 4));
+                const f32x4 f = *reinterpret_cast<const f32x4*>(pre + 16 * a + 4 * (l >> 4));
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= pre;
+                for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= f;
             }
         }
         // 2 x KD/16 steps (ks, a); the Kt fragments run LA steps ahead of the MFMAs
         {
             constexpr int NA = KD / 16, NS = 2 * NA, LA = 4;
+            const T* Kt = sm.Kt[bf];
             vec4_t<T> xf[LA][2];
             auto rd = [&](int n, vec4_t<T> (&x)[2]) {
-                x[0] = frag_cm<T>(sm.Kt, Sm::pKt, 32 * (n / NA), 16 * (n % NA));
-                x[1] = frag_cm<T>(sm.Kt, Sm::pKt, 32 * (n / NA) + 16, 16 * (n % NA));
+                x[0] = frag_cm<T>(Kt, Sm::pKt, 32 * (n / NA), 16 * (n % NA));
+                x[1] = frag_cm<T>(Kt, Sm::pKt, 32 * (n / NA) + 16, 16 * (n % NA));
             };
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -351,17 +395,16 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         }
 #pragma unroll
         for (int a = 0; a < KD / 16; ++a) {
-            const f32x4 post = *reinterpret_cast<const f32x4*>(sm.pp + KD + 16 * a + 4 * (l >> 4));
+            const f32x4 f = *reinterpret_cast<const f32x4*>(post + 16 * a + 4 * (l >> 4));
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= post;
+            for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= f;
         }
+        __syncthreads();  // E: buffer bf may be refilled
     }
     if constexpr (OUT) {
         if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V, V, col0);
     } else {
         S.store(ws_state + ((long)bh * P + seg) * (long)KD * V, V, col0);
-        // each segment's gate total is written by one workgroup only
-        if (vb == 0 && tid < KD) ws_gate[((long)bh * P + seg) * KD + tid] = gtot;
     }
 }
 
