@@ -80,3 +80,16 @@ def test_fwd_wide_scalar_gate(B, H, T, V):
     w = gi.custom(B, H, T, 256, V, dtype="bf16", gate="scalar", s0="normal0.1", backward=False, seed=940 + T)
     heads = [(b, h) for b in range(B) for h in range(H)] if B * H <= 2 else [(0, 0), (B - 1, H - 1)]
     _check(w, gi.make_inputs(w), heads, scalar=True)
+
+
+def test_fwd_wide_scalar_gate_exact_path():
+    # a scalar decay past the basis range sends its chunk down the element-wise
+    # path of the record kernel (two segments of four chunks, second chunk of each)
+    w = gi.custom(4, 16, 64 * 8, 256, 256, dtype="bf16", gate="scalar", s0="normal0.1", backward=False, seed=951)
+    inp = gi.make_inputs(w)
+    g = inp["g"].float()
+    g[0, 70, 0] = -80.0
+    g[0, 330, 1] = -70.0
+    g[3, 300:310, 15] = -12.0
+    inp["g"] = g.to(torch.bfloat16)
+    _check(w, inp, [(0, 0), (0, 1), (3, 15)], scalar=True)
