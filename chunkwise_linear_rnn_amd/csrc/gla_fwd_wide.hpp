@@ -24,12 +24,32 @@
 
 namespace gla {
 
-// Byte layout of one chunk's record (KD key columns, 16-bit operands).
+// Byte layout of one chunk's record (KD key columns, 16-bit operands).  The
+// contraction index of a 16x16x32 MFMA step is laid out as the two halves its
+// operand fragments use: lane group g (lanes 16g .. 16g+15) holds indices
+// 4g .. 4g+3 and 16+4g .. 16+4g+3 of the step.  Ql's key columns and Kt^T's
+// tokens are stored in that order within each block of 32 (position 8g + e
+// holds index 4g + e for e < 4 and 12 + 4g + e otherwise), so each lane reads a
+// whole 32-deep fragment as one 16-byte LDS row read.
+
+// A whole 32-deep row fragment of a tile stored in that order: lane l reads row
+// r0 + l%16, positions c0 + 8(l/16) .. +7, in one 16-byte LDS read; elements
+// 0-3 are the fragment's first half, 4-7 its second.
+template <typename T>
+__device__ __forceinline__ void frag_rm32(const T* base, int pitch, int r0, int c0, vec4_t<T> (&x)[2]) {
+    static_assert(sizeof(T) == 2, "16-bit tiles");
+    typedef unsigned int __attribute__((ext_vector_type(2))) u32x2;
+    const int l = lane_id();
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (r0 + (l & 15)) * pitch + c0 + 8 * (l >> 4));
+    x[0] = __builtin_bit_cast(vec4_t<T>, u32x2{v[0], v[1]});
+    x[1] = __builtin_bit_cast(vec4_t<T>, u32x2{v[2], v[3]});
+}
+
 template <int KD>
 struct WideRec {
-    static constexpr long oQl = 0;                          // [64][KD]  Ql
-    static constexpr long oKt = oQl + 2L * kChunk * KD;     // [64][KD]  Kt
-    static constexpr long oA = oKt + 2L * kChunk * KD;      // [64][64]  A, zero for s > t
+    static constexpr long oQl = 0;                          // [64][KD]  Ql, key columns in MFMA order
+    static constexpr long oKtT = oQl + 2L * kChunk * KD;    // [KD][64]  Kt transposed, tokens in MFMA order
+    static constexpr long oA = oKtT + 2L * kChunk * KD;     // [64][64]  A, zero for s > t
     static constexpr long oPP = oA + 2L * kChunk * kChunk;  // fp32 [3][KD]: pre, post, B_63
     static constexpr long oFlag = oPP + 12L * KD;           // int: some column left the basis range
     static constexpr long bytes = oFlag + 256;
@@ -86,16 +106,30 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
     unsigned char* r = rec + unit * R::bytes;
     T* oQl = reinterpret_cast<T*>(r + R::oQl);
-    T* oKt = reinterpret_cast<T*>(r + R::oKt);
+    T* oKtT = reinterpret_cast<T*>(r + R::oKtT);
     T* oA = reinterpret_cast<T*>(r + R::oA);
     float* opp = reinterpret_cast<float*>(r + R::oPP);
+    // Ql rows: the 16-byte vector at positions 8g .. 8g+7 of a 32-column block
+    // takes columns 4g .. 4g+3 and 16+4g .. 16+4g+3
+    typedef unsigned int __attribute__((ext_vector_type(2))) u32x2;
 #pragma unroll
     for (int i = 0; i < kChunk * VPR / NT; ++i) {
         const int p = tid + i * NT, row = p / VPR, col = (p % VPR) * VEC;
-        *reinterpret_cast<u32x4*>(oQl + row * KD + col) =
-            *reinterpret_cast<const u32x4*>(sm.buf.Ql + row * Sm::pQl + col);
-        *reinterpret_cast<u32x4*>(oKt + row * KD + col) =
-            *reinterpret_cast<const u32x4*>(sm.buf.Kt + row * Sm::pKt + col);
+        const int src = (col & ~31) + 4 * ((col & 31) >> 3);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(sm.buf.Ql + row * Sm::pQl + src);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(sm.buf.Ql + row * Sm::pQl + src + 16);
+        *reinterpret_cast<u32x4*>(oQl + row * KD + col) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    // Kt^T rows (one per key column): two LDS transpose reads give lane l key
+    // column c0 + l%16 at tokens 32ks + 4(l/16) + e and 32ks + 16 + 4(l/16) + e,
+    // the eight positions 8(l/16) .. +7 of that row's token block ks
+#pragma unroll
+    for (int u = w; u < (KD / 16) * (kChunk / 32); u += NW) {
+        const int c0 = 16 * (u % (KD / 16)), ks = u / (KD / 16);
+        const vec4_t<T> lo = frag_cm<T>(sm.buf.Kt, Sm::pKt, 32 * ks, c0);
+        const vec4_t<T> hi = frag_cm<T>(sm.buf.Kt, Sm::pKt, 32 * ks + 16, c0);
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), bq = __builtin_bit_cast(u32x2, hi);
+        *reinterpret_cast<u32x4*>(oKtT + (c0 + (l & 15)) * kChunk + 32 * ks + 8 * (l >> 4)) = u32x4{a[0], a[1], bq[0], bq[1]};
     }
     for (int i = tid; i < KD; i += NT) {
         const float pre = sm.buf.pre[i], post = sm.buf.post[i];
@@ -152,9 +186,9 @@ struct WideSmem {
     static constexpr int NC = 4;        // consumer (matrix) waves
     static constexpr int CW = BV / NC;  // value columns per consumer wave
     static constexpr int pQl = tile_pitch<T, KD, false>();
-    // Kt is read by column fragments in the state update: a row pitch of 8 (mod 64)
-    // dwords puts the 8-dword windows of eight consecutive rows on disjoint banks
-    static constexpr int pKt = KD + 16;
+    // Kt^T rows (one per key column, tokens in MFMA order) read as 16-byte row
+    // fragments: a pitch of 36 (mod 64) dwords keeps sixteen rows on disjoint banks
+    static constexpr int pKtT = kChunk + 8;
     static constexpr int pA = kChunk + Elem<T>::pad;
     // wave-private V slices read with ds_read_b64_tr_b16: a pitch of 16 or 32
     // two-byte columns keeps the four rows of a 16-lane group on disjoint banks
@@ -162,7 +196,7 @@ struct WideSmem {
     static_assert(CW == 16 || CW == 32, "value slice width");
     // two buffers of everything but Ql, which the output walk refills between
     // the inter-chunk product and the rest of the chunk
-    alignas(16) T Kt[2][kChunk * pKt];
+    alignas(16) T KtT[2][KD * pKtT];
     alignas(16) T Vw[2][NC * kChunk * pW];
     alignas(16) float pp[2][2 * KD];  // pre, post
     alignas(16) T A[OUT ? 2 : 1][OUT ? kChunk * pA : 8];
@@ -217,7 +251,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         const int ptid = tid - NP;
         float gtot = 0.f;  // state pass: thread ptid sums B_63 of key column ptid
         struct Regs {
-            TileRegs<T, KD, NP> Ql, Kt;
+            TileRegs<T, KD, NP> Ql, Kt;  // Kt: the [KD][64] Kt^T block as 64 rows of KD (linear)
             TileRegs<T, kChunk, NP> A;
             TileRegs<T, CW, 64> v;
             f32x4 pp;
@@ -227,7 +261,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         Regs ra, rb;
         auto fetch = [&](Regs& x, int c) {
             const unsigned char* r = rec + ((long)bh * N + c) * R::bytes;
-            x.Kt.load(reinterpret_cast<const T*>(r + R::oKt), KD, ptid);
+            x.Kt.load(reinterpret_cast<const T*>(r + R::oKtT), KD, ptid);
             if constexpr (OUT) {
                 x.Ql.load(reinterpret_cast<const T*>(r + R::oQl), KD, ptid);
                 x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
@@ -240,7 +274,12 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         };
         // everything but Ql into buffer bf
         auto stash = [&](const Regs& x, int bf) {
-            x.Kt.store_lds(sm.Kt[bf], Sm::pKt, ptid);
+            // linear vector q of the record is row q / 8, tokens 8 (q % 8) .. of Kt^T
+#pragma unroll
+            for (int i = 0; i < TileRegs<T, KD, NP>::PER; ++i) {
+                const int q = ptid + i * NP;
+                *reinterpret_cast<u32x4*>(sm.KtT[bf] + (q / (kChunk / 8)) * Sm::pKtT + (q % (kChunk / 8)) * 8) = x.Kt.r[i];
+            }
             if constexpr (OUT) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
             if (ptid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp[bf] + 4 * ptid) = x.pp;
             if (!OUT && ptid < KD) gtot += x.bl;
@@ -295,10 +334,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             vec4_t<T> qf[2][4][2];
             auto rd = [&](int ks, vec4_t<T> (&x)[4][2]) {
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    x[rb][0] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks);
-                    x[rb][1] = frag_rm<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks + 16);
-                }
+                for (int rb = 0; rb < 4; ++rb) frag_rm32<T>(sm.Ql, Sm::pQl, 16 * rb, 32 * ks, x[rb]);
             };
             __builtin_amdgcn_sched_barrier(0);
             rd(0, qf[0]);
@@ -317,12 +353,12 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                     for (int cb = 0; cb < CB; ++cb)
                         acc[rb][cb] = mma32(acc[rb][cb], sf[cb][0], sf[cb][1], qf[ks & 1][rb][0], qf[ks & 1][rb][1]);
             }
-            // eight reads ahead, then one read per MFMA (CB = 2) or two (CB = 1)
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            // four reads ahead, then one read per MFMA (CB = 1) or per two (CB = 2)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int i = 0; i < (KD / 32 - 1) * 4 * CB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 / CB, 0);
+                if (CB == 1 || (i & 1)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4 * CB, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -367,12 +403,9 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         // 2 x KD/16 steps (ks, a); the Kt fragments run LA steps ahead of the MFMAs
         {
             constexpr int NA = KD / 16, NS = 2 * NA, LA = 4;
-            const T* Kt = sm.Kt[bf];
+            const T* KtT = sm.KtT[bf];
             vec4_t<T> xf[LA][2];
-            auto rd = [&](int n, vec4_t<T> (&x)[2]) {
-                x[0] = frag_cm<T>(Kt, Sm::pKt, 32 * (n / NA), 16 * (n % NA));
-                x[1] = frag_cm<T>(Kt, Sm::pKt, 32 * (n / NA) + 16, 16 * (n % NA));
-            };
+            auto rd = [&](int n, vec4_t<T> (&x)[2]) { frag_rm32<T>(KtT, Sm::pKtT, 16 * (n % NA), 32 * (n / NA), x); };
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = 0; n < LA; ++n) rd(n, xf[n]);
@@ -384,11 +417,11 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                     S.s[a][cb] = mma32(S.s[a][cb], xf[n % LA][0], xf[n % LA][1], vf[2 * ks][cb], vf[2 * ks + 1][cb]);
                 if (n + LA < NS) rd(n + LA, xf[n % LA]);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
             for (int n = 0; n < NS - LA; ++n) {
                 __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, CB * LA, 0);
             __builtin_amdgcn_sched_barrier(0);
