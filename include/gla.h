@@ -94,7 +94,11 @@ gla_status_t gla_fwd(const gla_shape_t* shape,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gla_fwd needs for `shape` (0 for an invalid shape).
- * A pure function of the shape: it makes no HIP call. */
+ * A pure function of the shape: it makes no HIP call.  It holds the sequence
+ * segments' states and log-decays (B*H*P*K*V elements in the input dtype plus
+ * B*H*P*K floats, P <= T/64), and for 16-bit inputs with K = 256 also one
+ * 77056-byte record of prepared chunk operands per chunk and head
+ * (B*H*T/64 records: about 1.2 KB per token and head). */
 size_t gla_fwd_workspace_size(const gla_shape_t* shape);
 
 /*

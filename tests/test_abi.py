@@ -99,6 +99,13 @@ def test_workspace_sizes(L):
     assert a == 0 or a >= 2 * 4 * 128 * 256 * 4
     bw = L.gla_bwd_workspace_size(ctypes.byref(s))
     assert bw >= 2 * 2 * 4 * 128 * 256 * 4
+    # 16-bit heads with dk = 256 also hold one prepared-operand record per chunk
+    # and head (Ql, Kt^T, A: 2*64*256 + 64*64 two-byte values, gate factors)
+    wide = _shape(B=2, H=4, T=8192, K=256, V=512)
+    records = 2 * 4 * (8192 // 64) * (2 * 2 * 64 * 256 + 2 * 64 * 64)
+    assert L.gla_fwd_workspace_size(ctypes.byref(wide)) >= records
+    one = _shape(B=1, H=1, T=64, K=256, V=64)  # a single segment still needs its record
+    assert L.gla_fwd_workspace_size(ctypes.byref(one)) >= 2 * 2 * 64 * 256 + 2 * 64 * 64
 
 
 def _dec(L, shape, q=P, k=P, v=P, g=P, state=P, o=P):
