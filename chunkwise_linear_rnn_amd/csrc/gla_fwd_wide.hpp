@@ -216,8 +216,8 @@ struct WideSmem {
 //   consumers: O_inter = Ql S  | barrier X | O += A V, store O; S update | barrier E
 //   producers: Kt, A, V, gate factors of c+1 into buffer (c+1)&1 | barrier X |
 //              Ql of c+1 into the single Ql buffer | barrier E
-// Each producer wave keeps the records of two chunks in registers: at chunk c
-// it fetches chunk c+2 into the set that chunk c came in.
+// The producers load straight into LDS (global_load_lds_dwordx4), one chunk
+// ahead, and wait for their loads before barrier E.
 template <typename T, int KD, int BV, bool OUT>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
@@ -247,67 +247,74 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     const int col0 = vb * BV + cw * CW;
 
     if (producer) {
-        // ---------------- producers: records -> LDS
-        const int ptid = tid - NP;
+        // ---------------- producers: records -> LDS, straight from memory
+        // global_load_lds_dwordx4 writes lane l's 16 bytes at LDS base + 16 l, so
+        // one wave instruction fills 1 KiB of a tile as laid out in LDS; each lane
+        // fetches the bytes of its LDS slot (the padding slot that ends a row
+        // re-reads the row's first vector).  No registers hold the records.
+        const int ptid = tid - NP, pw = w - NC;
         float gtot = 0.f;  // state pass: thread ptid sums B_63 of key column ptid
-        struct Regs {
-            TileRegs<T, KD, NP> Ql, Kt;  // Kt: the [KD][64] Kt^T block as 64 rows of KD (linear)
-            TileRegs<T, kChunk, NP> A;
-            TileRegs<T, CW, 64> v;
-            f32x4 pp;
-            float bl;
-            int flag;
-        };
-        Regs ra, rb;
-        auto fetch = [&](Regs& x, int c) {
-            const unsigned char* r = rec + ((long)bh * N + c) * R::bytes;
-            x.Kt.load(reinterpret_cast<const T*>(r + R::oKtT), KD, ptid);
-            if constexpr (OUT) {
-                x.Ql.load(reinterpret_cast<const T*>(r + R::oQl), KD, ptid);
-                x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
+        // a dense tile of `rows` rows of `vpr` 16-byte vectors, at an LDS pitch of
+        // vpr + pad vectors: this wave issues instructions pw, pw + 4, ...
+        auto dma_tile = [&](const T* src, T* dst, int rows, int vpr, int pad) {
+            const int slots = rows * (vpr + pad);
+            for (int m = pw; m * 64 < slots; m += NC) {
+                const int k = m * 64 + l, row = k / (vpr + pad), q = k % (vpr + pad);
+                __builtin_amdgcn_global_load_lds(src + ((long)row * vpr + (q < vpr ? q : 0)) * 8, dst + m * 512, 16, 0, 0);
             }
-            const float* pp = reinterpret_cast<const float*>(r + R::oPP);
-            if (ptid < KD / 2) x.pp = *reinterpret_cast<const f32x4*>(pp + 4 * ptid);
-            if (!OUT && ptid < KD) x.bl = pp[2 * KD + ptid];
-            if (ptid == 0) x.flag = *reinterpret_cast<const int*>(r + R::oFlag);
-            x.v.load(v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0, rsV, l);
         };
-        // everything but Ql into buffer bf
-        auto stash = [&](const Regs& x, int bf) {
-            // linear vector q of the record is row q / 8, tokens 8 (q % 8) .. of Kt^T
+        static_assert(sizeof(T) == 2, "16-byte vectors of 8 elements");
+        static_assert(Sm::pKtT == kChunk + 8 && Sm::pA == kChunk + 8 && Sm::pQl == KD + 8, "one padding vector per row");
+        static_assert((KD * (kChunk / 8 + 1)) % 64 == 0 && (kChunk * (kChunk / 8 + 1)) % 64 == 0 &&
+                      (kChunk * (KD / 8 + 1)) % 64 == 0 && (2 * KD * 4 / 16) % 64 == 0, "whole KiB tiles");
+        constexpr int VPRV = Sm::CW / 8;  // 16-byte vectors per row of a value slice
+        static_assert((kChunk * VPRV) % 64 == 0 && Sm::pW == Sm::CW, "value slices are dense");
+        int fl = 0;
+        float bl = 0.f;
+        auto recp = [&](int c) { return rec + ((long)bh * N + c) * R::bytes; };
+        // every part of chunk c's record but Ql, and the value slice of this
+        // wave's consumer, into buffer bf
+        auto fetch = [&](int c, int bf) {
+            const unsigned char* r = recp(c);
+            dma_tile(reinterpret_cast<const T*>(r + R::oKtT), sm.KtT[bf], KD, kChunk / 8, 1);
+            if constexpr (OUT) dma_tile(reinterpret_cast<const T*>(r + R::oA), sm.A[bf], kChunk, kChunk / 8, 1);
+            dma_tile(reinterpret_cast<const T*>(r + R::oPP), reinterpret_cast<T*>(sm.pp[bf]), 1, 2 * KD * 4 / 16, 0);
+            const T* vs = v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+            T* vd = sm.Vw[bf] + cw * kChunk * Sm::pW;
 #pragma unroll
-            for (int i = 0; i < TileRegs<T, KD, NP>::PER; ++i) {
-                const int q = ptid + i * NP;
-                *reinterpret_cast<u32x4*>(sm.KtT[bf] + (q / (kChunk / 8)) * Sm::pKtT + (q % (kChunk / 8)) * 8) = x.Kt.r[i];
+            for (int m = 0; m < kChunk * VPRV / 64; ++m) {
+                const int k = m * 64 + l;
+                __builtin_amdgcn_global_load_lds(vs + (long)(k / VPRV) * rsV + (k % VPRV) * 8, vd + m * 512, 16, 0, 0);
             }
-            if constexpr (OUT) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
-            if (ptid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp[bf] + 4 * ptid) = x.pp;
-            if (!OUT && ptid < KD) gtot += x.bl;
-            if (ptid == 0) sm.flag[bf] = x.flag;
-            x.v.store_lds(sm.Vw[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
+            if (ptid == 0) fl = *reinterpret_cast<const int*>(r + R::oFlag);
+            if (!OUT && ptid < KD) bl = reinterpret_cast<const float*>(r + R::oPP)[2 * KD + ptid];
         };
-        // chunk c+1 (in x) into LDS during chunk c, then chunk c+3 into x
-        auto step = [&](Regs& x, int c) {
-            const bool more = c + 1 < c_end;
-            if (more) stash(x, (c + 1) & 1);
-            if constexpr (OUT) {
-                __syncthreads();  // X: the consumers are done with Ql(c)
-                if (more) x.Ql.store_lds(sm.Ql, Sm::pQl, ptid);
-            }
-            if (c + 3 < c_end) fetch(x, c + 3);
-            __syncthreads();  // E
+        auto fetch_ql = [&](int c) {
+            dma_tile(reinterpret_cast<const T*>(recp(c) + R::oQl), sm.Ql, kChunk, KD / 8, 1);
+        };
+        // the loads have landed in LDS and registers; publish the small values
+        auto settle = [&](int c) {
+            __builtin_amdgcn_s_waitcnt(0);
+            if (ptid == 0) sm.flag[c & 1] = fl;
+            if (!OUT && ptid < KD) gtot += bl;
         };
         if (c_begin < c_end) {
-            fetch(ra, c_begin);
-            stash(ra, c_begin & 1);  // chunk c is read from buffer c & 1
-            if constexpr (OUT) ra.Ql.store_lds(sm.Ql, Sm::pQl, ptid);
-            if (c_begin + 1 < c_end) fetch(rb, c_begin + 1);
-            if (c_begin + 2 < c_end) fetch(ra, c_begin + 2);
+            fetch(c_begin, c_begin & 1);  // chunk c is read from buffer c & 1
+            if constexpr (OUT) fetch_ql(c_begin);
+            settle(c_begin);
         }
         __syncthreads();  // E of the prologue
-        for (int c = c_begin; c < c_end; c += 2) {
-            step(rb, c);
-            if (c + 1 < c_end) step(ra, c + 1);
+        // during chunk c: chunk c+1 into buffer (c+1) & 1, its Ql once the
+        // consumers are past the inter-chunk product
+        for (int c = c_begin; c < c_end; ++c) {
+            const bool more = c + 1 < c_end;
+            if (more) fetch(c + 1, (c + 1) & 1);
+            if constexpr (OUT) {
+                __syncthreads();  // X: the consumers are done with Ql(c)
+                if (more) fetch_ql(c + 1);
+            }
+            if (more) settle(c + 1);
+            __syncthreads();  // E
         }
         if (!OUT && vb == 0 && ptid < KD) ws_gate[((long)bh * P + seg) * KD + ptid] = gtot;
         return;
