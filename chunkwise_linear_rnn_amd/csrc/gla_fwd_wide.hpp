@@ -217,7 +217,9 @@ struct WideSmem {
 //   producers: Kt, A, V, gate factors of c+1 into buffer (c+1)&1 | barrier X |
 //              Ql of c+1 into the single Ql buffer | barrier E
 // The producers load straight into LDS (global_load_lds_dwordx4), one chunk
-// ahead, and wait for their loads before barrier E.
+// ahead, and wait for their loads before barrier E.  The consumers leave each
+// chunk's output tile in their value slices; producer wave 4+w stores wave w's
+// tile as whole rows during the next chunk, before refilling that slice.
 template <typename T, int KD, int BV, bool OUT>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
@@ -289,6 +291,23 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             if (ptid == 0) fl = *reinterpret_cast<const int*>(r + R::oFlag);
             if (!OUT && ptid < KD) bl = reinterpret_cast<const float*>(r + R::oPP)[2 * KD + ptid];
         };
+        // the output tile of chunk c that consumer wave cw left in its value slice
+        // (buffer c & 1): 64 rows of CW columns, stored as whole 16-byte vectors
+        auto store_o = [&](int c) {
+            const T* os = sm.Vw[c & 1] + cw * kChunk * Sm::pW;
+            T* od = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+            u32x4 x[kChunk * VPRV / 64];
+#pragma unroll
+            for (int m = 0; m < kChunk * VPRV / 64; ++m) {
+                const int k = m * 64 + l;
+                x[m] = *reinterpret_cast<const u32x4*>(os + (k / VPRV) * Sm::pW + (k % VPRV) * 8);
+            }
+#pragma unroll
+            for (int m = 0; m < kChunk * VPRV / 64; ++m) {
+                const int k = m * 64 + l;
+                *reinterpret_cast<u32x4*>(od + (long)(k / VPRV) * rsV + (k % VPRV) * 8) = x[m];
+            }
+        };
         auto fetch_ql = [&](int c) {
             dma_tile(reinterpret_cast<const T*>(recp(c) + R::oQl), sm.Ql, kChunk, KD / 8, 1);
         };
@@ -308,6 +327,9 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         // consumers are past the inter-chunk product
         for (int c = c_begin; c < c_end; ++c) {
             const bool more = c + 1 < c_end;
+            // buffer (c+1) & 1 still holds the output of chunk c-1 in the value
+            // slices; this wave reads its slice before its own loads refill it
+            if (OUT && c > c_begin) store_o(c - 1);
             if (more) fetch(c + 1, (c + 1) & 1);
             if constexpr (OUT) {
                 __syncthreads();  // X: the consumers are done with Ql(c)
@@ -316,6 +338,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             if (more) settle(c + 1);
             __syncthreads();  // E
         }
+        if (OUT && c_begin < c_end) store_o(c_end - 1);  // after the last barrier E
         if (!OUT && vb == 0 && ptid < KD) ws_gate[((long)bh * P + seg) * KD + ptid] = gtot;
         return;
     }
@@ -376,8 +399,10 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
         if constexpr (OUT) {
-            // O^T[j][t] += sum_s V[s][j] A[t][s]
-            T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+            // O^T[j][t] += sum_s V[s][j] A[t][s]; the finished tile goes into this
+            // wave's value slice (its V is in registers by now), from where the
+            // producers store it as whole rows
+            T* oslice = sm.Vw[bf] + w * kChunk * Sm::pW;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
@@ -391,7 +416,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                 // slot e: column j = col0 + 16cb + 4(l/16) + e, token t = 16rb + l%16
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-                    *reinterpret_cast<vec4_t<T>*>(obase + (16 * rb + (l & 15)) * rsV + 16 * cb + 4 * (l >> 4)) =
+                    *reinterpret_cast<vec4_t<T>*>(oslice + (16 * rb + (l & 15)) * Sm::pW + 16 * cb + 4 * (l >> 4)) =
                         to_vec4<T>(acc[rb][cb]);
             }
         }
