@@ -216,10 +216,8 @@ struct WideSmem {
 //   consumers: O_inter = Ql S  | barrier X | O += A V, store O; S update | barrier E
 //   producers: Kt, A, V, gate factors of c+1 into buffer (c+1)&1 | barrier X |
 //              Ql of c+1 into the single Ql buffer | barrier E
-// The producers load straight into LDS (global_load_lds_dwordx4), one chunk
-// ahead, and wait for their loads before barrier E.  The consumers leave each
-// chunk's output tile in their value slices; producer wave 4+w stores wave w's
-// tile as whole rows during the next chunk, before refilling that slice.
+// Each producer wave keeps the records of two chunks in registers: at chunk c
+// it fetches chunk c+2 into the set that chunk c came in.
 template <typename T, int KD, int BV, bool OUT>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
@@ -249,96 +247,68 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     const int col0 = vb * BV + cw * CW;
 
     if (producer) {
-        // ---------------- producers: records -> LDS, straight from memory
-        // global_load_lds_dwordx4 writes lane l's 16 bytes at LDS base + 16 l, so
-        // one wave instruction fills 1 KiB of a tile as laid out in LDS; each lane
-        // fetches the bytes of its LDS slot (the padding slot that ends a row
-        // re-reads the row's first vector).  No registers hold the records.
-        const int ptid = tid - NP, pw = w - NC;
+        // ---------------- producers: records -> LDS
+        const int ptid = tid - NP;
         float gtot = 0.f;  // state pass: thread ptid sums B_63 of key column ptid
-        // a dense tile of `rows` rows of `vpr` 16-byte vectors, at an LDS pitch of
-        // vpr + pad vectors: this wave issues instructions pw, pw + 4, ...
-        auto dma_tile = [&](const T* src, T* dst, int rows, int vpr, int pad) {
-            const int slots = rows * (vpr + pad);
-            for (int m = pw; m * 64 < slots; m += NC) {
-                const int k = m * 64 + l, row = k / (vpr + pad), q = k % (vpr + pad);
-                __builtin_amdgcn_global_load_lds(src + ((long)row * vpr + (q < vpr ? q : 0)) * 8, dst + m * 512, 16, 0, 0);
-            }
+        struct Regs {
+            TileRegs<T, KD, NP> Ql, Kt;  // Kt: the [KD][64] Kt^T block as 64 rows of KD (linear)
+            TileRegs<T, kChunk, NP> A;
+            TileRegs<T, CW, 64> v;
+            f32x4 pp;
+            float bl;
+            int flag;
         };
-        static_assert(sizeof(T) == 2, "16-byte vectors of 8 elements");
-        static_assert(Sm::pKtT == kChunk + 8 && Sm::pA == kChunk + 8 && Sm::pQl == KD + 8, "one padding vector per row");
-        static_assert((KD * (kChunk / 8 + 1)) % 64 == 0 && (kChunk * (kChunk / 8 + 1)) % 64 == 0 &&
-                      (kChunk * (KD / 8 + 1)) % 64 == 0 && (2 * KD * 4 / 16) % 64 == 0, "whole KiB tiles");
-        constexpr int VPRV = Sm::CW / 8;  // 16-byte vectors per row of a value slice
-        static_assert((kChunk * VPRV) % 64 == 0 && Sm::pW == Sm::CW, "value slices are dense");
-        int fl = 0;
-        float bl = 0.f;
-        auto recp = [&](int c) { return rec + ((long)bh * N + c) * R::bytes; };
-        // every part of chunk c's record but Ql, and the value slice of this
-        // wave's consumer, into buffer bf
-        auto fetch = [&](int c, int bf) {
-            const unsigned char* r = recp(c);
-            dma_tile(reinterpret_cast<const T*>(r + R::oKtT), sm.KtT[bf], KD, kChunk / 8, 1);
-            if constexpr (OUT) dma_tile(reinterpret_cast<const T*>(r + R::oA), sm.A[bf], kChunk, kChunk / 8, 1);
-            dma_tile(reinterpret_cast<const T*>(r + R::oPP), reinterpret_cast<T*>(sm.pp[bf]), 1, 2 * KD * 4 / 16, 0);
-            const T* vs = v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
-            T* vd = sm.Vw[bf] + cw * kChunk * Sm::pW;
+        Regs ra, rb;
+        auto fetch = [&](Regs& x, int c) {
+            const unsigned char* r = rec + ((long)bh * N + c) * R::bytes;
+            x.Kt.load(reinterpret_cast<const T*>(r + R::oKtT), KD, ptid);
+            if constexpr (OUT) {
+                x.Ql.load(reinterpret_cast<const T*>(r + R::oQl), KD, ptid);
+                x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
+            }
+            const float* pp = reinterpret_cast<const float*>(r + R::oPP);
+            if (ptid < KD / 2) x.pp = *reinterpret_cast<const f32x4*>(pp + 4 * ptid);
+            if (!OUT && ptid < KD) x.bl = pp[2 * KD + ptid];
+            if (ptid == 0) x.flag = *reinterpret_cast<const int*>(r + R::oFlag);
+            x.v.load(v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0, rsV, l);
+        };
+        // everything but Ql into buffer bf
+        auto stash = [&](const Regs& x, int bf) {
+            // linear vector q of the record is row q / 8, tokens 8 (q % 8) .. of Kt^T
 #pragma unroll
-            for (int m = 0; m < kChunk * VPRV / 64; ++m) {
-                const int k = m * 64 + l;
-                __builtin_amdgcn_global_load_lds(vs + (long)(k / VPRV) * rsV + (k % VPRV) * 8, vd + m * 512, 16, 0, 0);
+            for (int i = 0; i < TileRegs<T, KD, NP>::PER; ++i) {
+                const int q = ptid + i * NP;
+                *reinterpret_cast<u32x4*>(sm.KtT[bf] + (q / (kChunk / 8)) * Sm::pKtT + (q % (kChunk / 8)) * 8) = x.Kt.r[i];
             }
-            if (ptid == 0) fl = *reinterpret_cast<const int*>(r + R::oFlag);
-            if (!OUT && ptid < KD) bl = reinterpret_cast<const float*>(r + R::oPP)[2 * KD + ptid];
+            if constexpr (OUT) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
+            if (ptid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp[bf] + 4 * ptid) = x.pp;
+            if (!OUT && ptid < KD) gtot += x.bl;
+            if (ptid == 0) sm.flag[bf] = x.flag;
+            x.v.store_lds(sm.Vw[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
         };
-        // the output tile of chunk c that consumer wave cw left in its value slice
-        // (buffer c & 1): 64 rows of CW columns, stored as whole 16-byte vectors
-        auto store_o = [&](int c) {
-            const T* os = sm.Vw[c & 1] + cw * kChunk * Sm::pW;
-            T* od = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
-            u32x4 x[kChunk * VPRV / 64];
-#pragma unroll
-            for (int m = 0; m < kChunk * VPRV / 64; ++m) {
-                const int k = m * 64 + l;
-                x[m] = *reinterpret_cast<const u32x4*>(os + (k / VPRV) * Sm::pW + (k % VPRV) * 8);
-            }
-#pragma unroll
-            for (int m = 0; m < kChunk * VPRV / 64; ++m) {
-                const int k = m * 64 + l;
-                *reinterpret_cast<u32x4*>(od + (long)(k / VPRV) * rsV + (k % VPRV) * 8) = x[m];
-            }
-        };
-        auto fetch_ql = [&](int c) {
-            dma_tile(reinterpret_cast<const T*>(recp(c) + R::oQl), sm.Ql, kChunk, KD / 8, 1);
-        };
-        // the loads have landed in LDS and registers; publish the small values
-        auto settle = [&](int c) {
-            __builtin_amdgcn_s_waitcnt(0);
-            if (ptid == 0) sm.flag[c & 1] = fl;
-            if (!OUT && ptid < KD) gtot += bl;
-        };
-        if (c_begin < c_end) {
-            fetch(c_begin, c_begin & 1);  // chunk c is read from buffer c & 1
-            if constexpr (OUT) fetch_ql(c_begin);
-            settle(c_begin);
-        }
-        __syncthreads();  // E of the prologue
-        // during chunk c: chunk c+1 into buffer (c+1) & 1, its Ql once the
-        // consumers are past the inter-chunk product
-        for (int c = c_begin; c < c_end; ++c) {
+        // chunk c+1 (in x) into LDS during chunk c, then chunk c+3 into x
+        auto step = [&](Regs& x, int c) {
             const bool more = c + 1 < c_end;
-            // buffer (c+1) & 1 still holds the output of chunk c-1 in the value
-            // slices; this wave reads its slice before its own loads refill it
-            if (OUT && c > c_begin) store_o(c - 1);
-            if (more) fetch(c + 1, (c + 1) & 1);
+            if (more) stash(x, (c + 1) & 1);
             if constexpr (OUT) {
                 __syncthreads();  // X: the consumers are done with Ql(c)
-                if (more) fetch_ql(c + 1);
+                if (more) x.Ql.store_lds(sm.Ql, Sm::pQl, ptid);
             }
-            if (more) settle(c + 1);
+            if (c + 3 < c_end) fetch(x, c + 3);
             __syncthreads();  // E
+        };
+        if (c_begin < c_end) {
+            fetch(ra, c_begin);
+            stash(ra, c_begin & 1);  // chunk c is read from buffer c & 1
+            if constexpr (OUT) ra.Ql.store_lds(sm.Ql, Sm::pQl, ptid);
+            if (c_begin + 1 < c_end) fetch(rb, c_begin + 1);
+            if (c_begin + 2 < c_end) fetch(ra, c_begin + 2);
         }
-        if (OUT && c_begin < c_end) store_o(c_end - 1);  // after the last barrier E
+        __syncthreads();  // E of the prologue
+        for (int c = c_begin; c < c_end; c += 2) {
+            step(rb, c);
+            if (c + 1 < c_end) step(ra, c + 1);
+        }
         if (!OUT && vb == 0 && ptid < KD) ws_gate[((long)bh * P + seg) * KD + ptid] = gtot;
         return;
     }
@@ -399,10 +369,8 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
         if constexpr (OUT) {
-            // O^T[j][t] += sum_s V[s][j] A[t][s]; the finished tile goes into this
-            // wave's value slice (its V is in registers by now), from where the
-            // producers store it as whole rows
-            T* oslice = sm.Vw[bf] + w * kChunk * Sm::pW;
+            // O^T[j][t] += sum_s V[s][j] A[t][s]
+            T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
@@ -416,7 +384,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                 // slot e: column j = col0 + 16cb + 4(l/16) + e, token t = 16rb + l%16
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-                    *reinterpret_cast<vec4_t<T>*>(oslice + (16 * rb + (l & 15)) * Sm::pW + 16 * cb + 4 * (l >> 4)) =
+                    *reinterpret_cast<vec4_t<T>*>(obase + (16 * rb + (l & 15)) * rsV + 16 * cb + 4 * (l >> 4)) =
                         to_vec4<T>(acc[rb][cb]);
             }
         }
