@@ -53,6 +53,8 @@ def _load():
     lib.oracle_gla_fwd.restype = ctypes.c_int
     lib.oracle_gla_bwd.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_gla_bwd.restype = ctypes.c_int
+    lib.oracle_gla_fwd_general.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.oracle_gla_fwd_general.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     D = ctypes.c_double
     lib.oracle_out_gate_fwd.argtypes = [L, L, dp, dp, dp, dp, D, dp]
@@ -106,6 +108,35 @@ def gla_fwd(q, k, v, g, s0=None) -> Tuple[np.ndarray, np.ndarray]:
     rc = _load().oracle_gla_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o), _ptr(sf))
     if rc != 0:
         raise RuntimeError("oracle_gla_fwd failed with code %d" % rc)
+    return o, sf
+
+
+def gla_fwd_general(q, k, v, g, h, s0=None) -> Tuple[np.ndarray, np.ndarray]:
+    """General gated linear attention forward in fp64: (o [B,T,H,V], s_final).
+
+    Follows "Gated Linear Attention Transformers with Hardware-Efficient
+    Training", the chapter summary's Knowl 12 and Appendix C: the forget gate is
+    the outer product alpha_t^T beta_t of a key-side gate alpha_t = exp(g_t)
+    [B,T,H,K] and a value-side gate beta_t = exp(h_t) [B,T,H,V],
+    S_t = (alpha_t^T beta_t) * S_{t-1} + k_t^T v_t, o_t = q_t S_t.
+    Pinned by: the brute-force double-product form, the pages' parallel form
+    O = (((Q*B)(K/B)^T) * M)(V/D) * D, its h = 0 reduction to gla_fwd, and the
+    closed-form final state.
+    """
+    q, k, v, g, h = (_as_f64(x) for x in (q, k, v, g, h))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, T, H, K) and g.shape == (B, T, H, K)
+    assert v.shape == (B, T, H, V) and h.shape == (B, T, H, V)
+    s0 = _as_f64(s0)
+    if s0 is not None:
+        assert s0.shape == (B, H, K, V)
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    sf = np.zeros((B, H, K, V), dtype=np.float64)
+    rc = _load().oracle_gla_fwd_general(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h), _ptr(s0),
+                                        _ptr(o), _ptr(sf))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_fwd_general failed with code %d" % rc)
     return o, sf
 
 

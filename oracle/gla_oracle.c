@@ -116,6 +116,56 @@ int oracle_gla_fwd(long B, long T, long H, long K, long V,
     return err;
 }
 
+/* General gated linear attention ("Gated Linear Attention Transformers with
+ * Hardware-Efficient Training", the chapter summary's Knowl 12 and Appendix C):
+ * the forget gate is the outer product of a key-side gate alpha_t = exp(g_t)
+ * (1 x K) and a value-side gate beta_t = exp(h_t) (1 x V),
+ *   S_t = (alpha_t^T beta_t) .* S_{t-1} + k_t^T v_t ,   o_t = q_t S_t ,
+ * token by token, with S_0 = s0 or zero.  h is laid out like v: [B, T, H, V]. */
+int oracle_gla_fwd_general(long B, long T, long H, long K, long V,
+                           const double *q, const double *k, const double *v, const double *g,
+                           const double *h, const double *s0, double *o, double *s_final) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return 1;
+    long nbh = B * H;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        long b = bh / H, hh = bh % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)K * (size_t)V);
+        double *av = (double *)malloc(sizeof(double) * (size_t)K);
+        double *bv = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!S || !av || !bv) {
+#pragma omp atomic write
+            err = 2;
+            free(S); free(av); free(bv);
+            continue;
+        }
+        for (long i = 0; i < K; ++i)
+            for (long j = 0; j < V; ++j)
+                S[i * V + j] = s0 ? s0[IDX_ST(b, hh, i, j, H, K, V)] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            for (long i = 0; i < K; ++i) av[i] = exp(g[IDX_TOK(b, t, hh, i, T, H, K)]);
+            for (long j = 0; j < V; ++j) bv[j] = exp(h[IDX_TOK(b, t, hh, j, T, H, V)]);
+            for (long i = 0; i < K; ++i) {
+                const double ki = k[IDX_TOK(b, t, hh, i, T, H, K)];
+                double *row = S + i * V;
+                for (long j = 0; j < V; ++j)
+                    row[j] = (av[i] * bv[j]) * row[j] + ki * v[IDX_TOK(b, t, hh, j, T, H, V)];
+            }
+            for (long j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < K; ++i) acc += q[IDX_TOK(b, t, hh, i, T, H, K)] * S[i * V + j];
+                o[IDX_TOK(b, t, hh, j, T, H, V)] = acc;
+            }
+        }
+        if (s_final)
+            for (long i = 0; i < K; ++i)
+                for (long j = 0; j < V; ++j) s_final[IDX_ST(b, hh, i, j, H, K, V)] = S[i * V + j];
+        free(S); free(av); free(bv);
+    }
+    return err;
+}
+
 /* Backward of the same loop.  With S_t the post-update state and dS the
  * running gradient with respect to it, for t = T..1:
  *   dS      += q_t^T do_t                       (o_t = q_t S_t)
