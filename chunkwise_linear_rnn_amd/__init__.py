@@ -46,7 +46,7 @@ class GlaError(RuntimeError):
 
 EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode", "gla_out_gate",
            "gla_out_gate_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_bwd_scalar_workspace_size",
-           "gla_out_gate_bwd_workspace_size",
+           "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
            "gla_kernel_timing", "gla_kernel_timing_read"]
 
@@ -73,6 +73,10 @@ def lib():
     L.gla_bwd_scalar.argtypes = L.gla_bwd.argtypes
     L.gla_bwd_scalar.restype = ctypes.c_int
     L.gla_bwd_scalar_workspace_size.argtypes = [sh]
+    L.gla_fwd_general.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gla_fwd_general.restype = ctypes.c_int
+    L.gla_fwd_general_workspace_size.argtypes = [sh]
+    L.gla_fwd_general_workspace_size.restype = ctypes.c_size_t
     L.gla_bwd_scalar_workspace_size.restype = ctypes.c_size_t
     L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
     L.gla_decode.restype = ctypes.c_int
@@ -237,6 +241,36 @@ def gla_bwd_scalar(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=N
     ws = workspace(gla_bwd_scalar_workspace_size(B, T, H, K, V, dt), dev)
     gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream, scalar_gate=True)
     return dq, dk, dv, dg, ds0
+
+
+def gla_fwd_general_workspace_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_fwd_general_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
+
+
+def gla_fwd_general_into(q, k, v, g, h, s0, o, s_final, ws, stream=None):
+    """gla_fwd_general with caller-owned outputs and workspace (nothing allocated)."""
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib().gla_fwd_general(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h), _ptr(s0), _ptr(o),
+                                 _ptr(s_final), _ptr(ws), nbytes, _stream(stream)))
+
+
+def gla_fwd_general(q, k, v, g, h, s0=None, output_final_state=True, stream=None):
+    """o, S_T of general gated linear attention, forget gate exp(g_t)^T exp(h_t).
+
+    q, k, g: [B,T,H,K]; v, h: [B,T,H,V] (bf16); s0: [B,H,K,V] fp32 or None."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
+                         ("h", h, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    ws = workspace(gla_fwd_general_workspace_size(B, T, H, K, V, dt), dev)
+    gla_fwd_general_into(q, k, v, g, h, s0, o, sf, ws, stream)
+    return o, sf
 
 
 def gla_decode_into(q, k, v, g, state, o, stream=None):

@@ -179,6 +179,62 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     return GLA_OK;
 }
 
+gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                              const void* g, const void* h, const float* s0, void* o, float* s_final,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, false);
+    if (st != GLA_OK) return st;
+    if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
+    if (s.K != 128 && s.K != 256)
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 128 or 256 (got %lld)", (long long)s.K);
+    const bool empty = s.B * s.H == 0 || s.T == 0;
+    if (!empty && (!q || !k || !v || !g || !h || !o)) return fail(GLA_ERR_NULL, "q, k, v, g, h and o are required");
+    const void* ptrs[] = {q, k, v, g, h, s0, o, s_final, workspace};
+    const char* names[] = {"q", "k", "v", "g", "h", "s0", "o", "s_final", "workspace"};
+    for (int i = 0; i < 9; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t need = empty ? 0 : gla::fwd_general_workspace_bytes(s);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (empty) {
+        err = s_final ? gla::launch_state_copy(s0, s_final, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else {
+        gla::Plan p = gla::make_fwd_general_plan(s);
+        gla::FwdLaunch a{};
+        a.bf16 = true;
+        a.K = (int)s.K;
+        a.V = (int)s.V;
+        a.BV = p.BV;
+        a.T = (int)s.T;
+        a.H = (int)s.H;
+        a.N = (int)p.N;
+        a.P = p.P;
+        a.seg_len = p.seg_len;
+        a.BH = p.BH;
+        a.q = q; a.k = k; a.v = v; a.g = g; a.h = h;
+        a.s0 = s0;
+        a.o = o;
+        a.s_final = s_final;
+        char* ws = static_cast<char*>(workspace);
+        if (p.P > 1) {
+            const size_t sb = gla::state_bytes(s, p);
+            a.ws_state = ws;
+            a.ws_gate = reinterpret_cast<float*>(ws + sb);
+            a.ws_gateb = reinterpret_cast<float*>(ws + sb + gla::round256((size_t)p.BH * p.P * s.K * sizeof(float)));
+        }
+        a.ws_rec = ws + gla::fwd_general_seg_bytes(s, p);
+        a.stream = strm;
+        err = gla::launch_fwd_general(a);
+    }
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
 gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
                       float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg) {
@@ -297,6 +353,18 @@ gla_status_t gla_fwd_scalar(const gla_shape_t* shape, const void* q, const void*
                             const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
                             void* stream) {
     return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, true);
+}
+
+size_t gla_fwd_general_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, false) != GLA_OK || !s.bf16 || (s.K != 128 && s.K != 256)) return 0;
+    return gla::fwd_general_workspace_bytes(s);
+}
+
+gla_status_t gla_fwd_general(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                             const void* h, const float* s0, void* o, float* s_final, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return fwd_general_impl(shape, q, k, v, g, h, s0, o, s_final, workspace, workspace_bytes, stream);
 }
 
 gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

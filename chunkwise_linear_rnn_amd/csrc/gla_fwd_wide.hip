@@ -47,6 +47,90 @@ static hipError_t launch_fwd_wide_t(const FwdLaunch& a) {
     return a.sg ? launch_fwd_wide_bv<KD, BV, true>(a) : launch_fwd_wide_bv<KD, BV, false>(a);
 }
 
+// Segment combine under general gates: out[0] = S_0, out[p+1] = exp2(GA_p[i] +
+// GB_p[j]) out[p] + in[p], with GA/GB the segment's log2 decays of key row i
+// and value column j.  One thread per 4 adjacent elements of a state row.
+__global__ void __launch_bounds__(256)
+gla_seg_combine_fwd_general(const float* __restrict__ s0, bf16* __restrict__ ws_state,
+                            const float* __restrict__ ws_gate, const float* __restrict__ ws_gateb, int K, int V,
+                            int P) {
+    using VT = bf16 __attribute__((ext_vector_type(4)));
+    const long KV = (long)K * V;
+    const long e = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+    const long bh = blockIdx.y;
+    if (e >= KV) return;
+    const int i = (int)(e / V), j = (int)(e % V);
+    bf16* st = ws_state + bh * P * KV + e;
+    const float* ga = ws_gate + bh * P * (long)K + i;
+    const float* gbv = ws_gateb + bh * P * (long)V + j;
+    f32x4 cur = s0 ? *reinterpret_cast<const f32x4*>(s0 + bh * KV + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < P; ++p) {
+        // segment P-1 has no state of its own: only its initial state is written
+        const bool feeds = p + 1 < P;
+        VT in{};
+        float gr = 0.f;
+        f32x4 gcol{0.f, 0.f, 0.f, 0.f};
+        if (feeds) {
+            in = *reinterpret_cast<const VT*>(st + p * KV);
+            gr = ga[(long)p * K];
+            gcol = *reinterpret_cast<const f32x4*>(gbv + (long)p * V);
+        }
+        VT o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = Elem<bf16>::from_f(cur[c]);
+        *reinterpret_cast<VT*>(st + p * KV) = o;
+        if (feeds) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cur[c] = exp2f(gr + gcol[c]) * cur[c] + Elem<bf16>::to_f(in[c]);
+        }
+    }
+}
+
+// General gates (16-bit): records, the state pass over segments 0..P-2, the
+// combine, and the output walk, all at 64 value columns per workgroup.
+template <int KD, int VP>
+static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
+    using T = bf16;
+    constexpr int BV = 64;
+    static_assert(sizeof(GenPrepSmem<T, KD, VP>) <= 160 * 1024, "LDS budget");
+    static_assert(sizeof(WideSmem<T, KD, BV, true, true>) <= 160 * 1024, "LDS budget");
+    static_assert(GenRec<KD>::bytes(512) == (long)gen_record_bytes(KD, 512), "record size as the workspace plans it");
+    if ((long)GenRec<KD>::bytes(a.V) != (long)gen_record_bytes(KD, a.V)) return hipErrorInvalidValue;
+    const int nvb = a.V / BV;
+    unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);
+    GLA_LAUNCH("fwd_general_prep", (gla_fwd_general_prep<T, KD, VP>), dim3((unsigned)(a.BH * a.N)), dim3(256),
+               a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.h, rec, a.T, a.H,
+               a.V, a.N);
+    if (a.P > 1) {
+        const int nseg = a.P - 1;
+        GLA_LAUNCH("fwd_general_seg_state", (gla_fwd_wide_walk<T, KD, BV, false, true>),
+                   dim3((unsigned)xcd_grid(nseg * a.BH, nvb)), dim3(512), a.stream, (const unsigned char*)rec,
+                   (const T*)a.v, (const T*)nullptr, (const float*)nullptr, (T*)nullptr, (float*)nullptr,
+                   (T*)a.ws_state, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, a.ws_gateb);
+        const long KV = (long)KD * a.V;
+        GLA_LAUNCH("combine_fwd_general", gla_seg_combine_fwd_general, dim3((unsigned)((KV / 4 + 255) / 256), (unsigned)a.BH),
+                   dim3(256), a.stream, a.s0, (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD,
+                   a.V, a.P);
+    }
+    GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true>),
+               dim3((unsigned)xcd_grid(a.P * a.BH, nvb)), dim3(512), a.stream, (const unsigned char*)rec,
+               (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H,
+               a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr);
+    return hipGetLastError();
+}
+
+template <int KD>
+static hipError_t launch_fwd_general_k(const FwdLaunch& a) {
+    return a.V % 128 == 0 ? launch_fwd_general_kv<KD, 128>(a) : launch_fwd_general_kv<KD, 64>(a);
+}
+
+hipError_t launch_fwd_general(const FwdLaunch& a) {
+    if (!a.bf16 || a.V % 64 != 0) return hipErrorInvalidValue;
+    if (a.K == 128) return launch_fwd_general_k<128>(a);
+    if (a.K == 256) return launch_fwd_general_k<256>(a);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_fwd_wide(const FwdLaunch& a) {
     if (a.K != 256) return hipErrorInvalidValue;
     if (a.BV == 64) return launch_fwd_wide_t<256, 64>(a);

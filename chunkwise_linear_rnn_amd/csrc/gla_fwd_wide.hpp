@@ -56,6 +56,25 @@ struct WideRec {
     static_assert(bytes % 256 == 0, "records stay 256-byte aligned");
 };
 
+// The record of one chunk and head under general gates G_t = alpha_t^T beta_t
+// ("Gated Linear Attention Transformers with Hardware-Efficient Training", the
+// chapter summary's Knowl 12 and Appendix C): the key side
+// as above (no A: the intra-chunk output comes whole), then the value side,
+// with C_t the intra-chunk cumulative log2 of beta in each value column.
+template <int KD>
+struct GenRec {
+    static constexpr long oQl = 0;                        // [64][KD]  Ql, key columns in MFMA order
+    static constexpr long oKtT = oQl + 2L * kChunk * KD;  // [KD][64]  Kt transposed, tokens in MFMA order
+    static constexpr long oPP = oKtT + 2L * kChunk * KD;  // fp32 [3][KD]: pre, post, B_63
+    static constexpr long oFlag = oPP + 12L * KD;         // int: some key column left the basis range
+    static constexpr long oVp = oFlag + 256;              // [64][V]  v * exp2(C_63 - C_t)
+    static constexpr long oCs(int V) { return oVp + 2L * kChunk * V; }  // [64][V]  exp2(C_t)
+    static constexpr long oOi(int V) { return oCs(V) + 2L * kChunk * V; }  // [64][V]  intra-chunk output
+    static constexpr long oPB(int V) { return oOi(V) + 2L * kChunk * V; }  // fp32 [2][V]: exp2(C_63), C_63
+    static constexpr long bytes(int V) { return oPB(V) + 8L * V; }
+    static_assert(oVp % 256 == 0, "value-side tiles stay 256-byte aligned");
+};
+
 template <typename T, int KD>
 struct WidePrepSmem {
     static constexpr int pQl = tile_pitch<T, KD, false>();
@@ -181,7 +200,217 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     }
 }
 
-template <typename T, int KD, int BV, bool OUT>
+template <typename T, int KD, int VP>
+struct GenPrepSmem {
+    static constexpr int pA = kChunk + 8;  // A, read as row fragments
+    static constexpr int pV = VP + 8;      // scaled (or raw) values, read as column fragments
+    static constexpr int pC = VP + 4;      // C_t, fp32
+    typename WidePrepSmem<T, KD>::Buf buf;
+    alignas(16) T A[kChunk * pA];
+    alignas(16) T Vt[kChunk * pV];
+    alignas(16) float Cl[kChunk * pC];
+    float tot[4][VP];
+    int flagb;
+};
+
+// One workgroup (four waves) per chunk and head under general gates.  The key
+// side is the forward's record (Ql, Kt, pre/post, flag) with A kept in LDS;
+// the value side then takes VP columns per pass:
+//   C_t = cumulative sum of h * log2(e) within the chunk (exp(h) = beta)
+//   Vp = v * exp2(C_63 - C_t), Cs = exp2(C_t), and the intra-chunk output
+//   Oi[t][j] = sum_{s <= t} A[t][s] v[s][j] exp2(C_t[j] - C_s[j])
+// formed as exp2(C_t) * (A (v * exp2(-C))) on the matrix cores, or element by
+// element when some column's C_63 leaves the basis range (exp2(-C) would not
+// stay a well-scaled fp32/bf16 value).
+template <typename T, int KD, int VP>
+__global__ void __launch_bounds__(256)
+gla_fwd_general_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                     const T* __restrict__ g, const T* __restrict__ hg, unsigned char* __restrict__ rec, int T_, int H,
+                     int V, int N) {
+    constexpr int NW = 4, NT = NW * 64, CPK = KD / NW, VEC = 16 / (int)sizeof(T), VPR = KD / VEC;
+    constexpr int NPART = NT / VP, TPP = kChunk / NPART;  // token parts per column, tokens per part
+    constexpr int CB2 = VP / NW / 16;                     // 16-column blocks per wave in the output product
+    static_assert(CPK <= 64 && (kChunk * VPR) % NT == 0, "prep tiling");
+    static_assert((VP == 64 || VP == 128) && CB2 >= 1, "value pass width");
+    using Sm = GenPrepSmem<T, KD, VP>;
+    using WS = WidePrepSmem<T, KD>;
+    using G = GenRec<KD>;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const long unit = blockIdx.x;  // bh * N + chunk; the grid has exactly BH * N blocks
+    const int bh = (int)(unit / N), c = (int)(unit % N);
+    const int b = bh / H, h = bh % H;
+    const int rsK = H * KD, rsV = H * V;
+    const long row0 = (long)b * T_ + (long)c * kChunk;
+    const T* qb = q + row0 * rsK + (long)h * KD;
+    const T* kb = k + row0 * rsK + (long)h * KD;
+    const T* gb = g + row0 * rsK + (long)h * KD;
+    const int kc0 = w * CPK;
+
+    // ---- key side
+    RowSlab<T, CPK> rq, rk;
+    GateSlab<T, CPK, false> rg;
+    rq.load(qb, rsK, kc0);
+    rk.load(kb, rsK, kc0);
+    rg.load(gb, rsK, kc0);
+    if (tid == 0) sm.buf.flag[0] = 0;
+    __syncthreads();
+    pipe_prep<T, CPK>(sm.buf, WS::pQl, WS::pKt, rq, rk, rg, kc0, 0, CPK / VEC);
+    __syncthreads();
+
+    unsigned char* r = rec + unit * G::bytes(V);
+    T* oQl = reinterpret_cast<T*>(r + G::oQl);
+    T* oKtT = reinterpret_cast<T*>(r + G::oKtT);
+    float* opp = reinterpret_cast<float*>(r + G::oPP);
+    typedef unsigned int __attribute__((ext_vector_type(2))) u32x2;
+#pragma unroll
+    for (int i = 0; i < kChunk * VPR / NT; ++i) {
+        const int p = tid + i * NT, row = p / VPR, col = (p % VPR) * VEC;
+        const int src = (col & ~31) + 4 * ((col & 31) >> 3);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(sm.buf.Ql + row * WS::pQl + src);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(sm.buf.Ql + row * WS::pQl + src + 16);
+        *reinterpret_cast<u32x4*>(oQl + row * KD + col) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+#pragma unroll
+    for (int u = w; u < (KD / 16) * (kChunk / 32); u += NW) {
+        const int c0 = 16 * (u % (KD / 16)), ks = u / (KD / 16);
+        const vec4_t<T> lo = frag_cm<T>(sm.buf.Kt, WS::pKt, 32 * ks, c0);
+        const vec4_t<T> hi = frag_cm<T>(sm.buf.Kt, WS::pKt, 32 * ks + 16, c0);
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), bq = __builtin_bit_cast(u32x2, hi);
+        *reinterpret_cast<u32x4*>(oKtT + (c0 + (l & 15)) * kChunk + 32 * ks + 8 * (l >> 4)) = u32x4{a[0], a[1], bq[0], bq[1]};
+    }
+    for (int i = tid; i < KD; i += NT) {
+        const float pre = sm.buf.pre[i], post = sm.buf.post[i];
+        opp[i] = pre;
+        opp[KD + i] = post;
+        opp[2 * KD + i] = log2f(pre * post);
+    }
+    const bool exact = sm.buf.flag[0] != 0;
+    if (tid == 0) *reinterpret_cast<int*>(r + G::oFlag) = exact ? 1 : 0;
+    if (!exact) {
+        for (int tile = w; tile < 10; tile += NW) {
+            int is, js;
+            decode_tile(tile, is, js);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KD / 32; ++ks)
+                acc = mma32(acc, frag_rm<T>(sm.buf.Kt, WS::pKt, 16 * js, 32 * ks),
+                            frag_rm<T>(sm.buf.Kt, WS::pKt, 16 * js, 32 * ks + 16),
+                            frag_rm<T>(sm.buf.Ql, WS::pQl, 16 * is, 32 * ks),
+                            frag_rm<T>(sm.buf.Ql, WS::pQl, 16 * is, 32 * ks + 16));
+            // acc holds A^T[s][t] for s = 16js + 4(l/16) + e, t = 16is + l%16
+            if (is == js) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * (l >> 4) + e > (l & 15)) acc[e] = 0.f;
+            }
+            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
+                to_vec4<T>(acc);
+        }
+        for (int z = w; z < 6; z += NW) {
+            const int is = (z >= 3) + (z >= 5);
+            const int js = z + 1 - (is == 1 ? 2 : (is == 2 ? 3 : 0));
+            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
+                to_vec4<T>(zero4());
+        }
+    } else {
+        __syncthreads();  // every thread has copied Ql out
+        float* Af = reinterpret_cast<float*>(sm.buf.Ql);
+        exact_intra_tile<T, KD, NW, false>(Af, WS::pF, qb, kb, gb, rsK, rsK, w);
+        __syncthreads();
+        for (int e = tid; e < kChunk * kChunk; e += NT) {
+            const int t = e / kChunk, s2 = e % kChunk;
+            sm.A[t * Sm::pA + s2] = Elem<T>::from_f(s2 <= t ? Af[t * WS::pF + s2] : 0.f);
+        }
+    }
+
+    // ---- value side, VP columns per pass
+    T* oVp = reinterpret_cast<T*>(r + G::oVp);
+    T* oCs = reinterpret_cast<T*>(r + G::oCs(V));
+    T* oOi = reinterpret_cast<T*>(r + G::oOi(V));
+    float* opb = reinterpret_cast<float*>(r + G::oPB(V));
+    const int jj = tid % VP, part = tid / VP, t0 = part * TPP;
+    for (int j0 = 0; j0 < V; j0 += VP) {
+        const long gofs = row0 * rsV + (long)h * V + j0 + jj;
+        float cl[TPP], vr[TPP];
+#pragma unroll
+        for (int i = 0; i < TPP; ++i) {
+            cl[i] = Elem<T>::to_f(hg[gofs + (long)(t0 + i) * rsV]) * kLog2e;
+            vr[i] = Elem<T>::to_f(v[gofs + (long)(t0 + i) * rsV]);
+        }
+#pragma unroll
+        for (int i = 1; i < TPP; ++i) cl[i] += cl[i - 1];
+        if (tid == 0) sm.flagb = 0;
+        sm.tot[part][jj] = cl[TPP - 1];
+        __syncthreads();  // B1: part totals (and A) visible, flag cleared
+        float off = 0.f, c63 = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < NPART; ++pp) {
+            const float x = sm.tot[pp][jj];
+            if (pp < part) off += x;
+            c63 += x;
+        }
+        if (-c63 > kBasisLimit) sm.flagb = 1;
+        if (part == 0) {
+            opb[j0 + jj] = exp2f(c63);
+            opb[V + j0 + jj] = c63;
+        }
+        __syncthreads();  // B2: the pass's flag
+        const bool fl = sm.flagb != 0;
+#pragma unroll
+        for (int i = 0; i < TPP; ++i) {
+            const int t = t0 + i;
+            const float ct = off + cl[i];
+            oVp[t * V + j0 + jj] = Elem<T>::from_f(vr[i] * exp2f(c63 - ct));
+            oCs[t * V + j0 + jj] = Elem<T>::from_f(exp2f(ct));
+            sm.Vt[t * Sm::pV + jj] = Elem<T>::from_f(fl ? vr[i] : vr[i] * exp2f(-ct));
+            sm.Cl[t * Sm::pC + jj] = ct;
+        }
+        __syncthreads();  // B3: Vt and Cl complete
+        if (!fl) {
+            const int c0 = w * (VP / NW);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4 acc[CB2];
+#pragma unroll
+                for (int cb = 0; cb < CB2; ++cb) acc[cb] = zero4();
+#pragma unroll
+                for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
+                    const vec4_t<T> blo = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2);
+                    const vec4_t<T> bhi = frag_rm<T>(sm.A, Sm::pA, 16 * rb, 32 * ks2 + 16);
+#pragma unroll
+                    for (int cb = 0; cb < CB2; ++cb)
+                        acc[cb] = mma32(acc[cb], frag_cm<T>(sm.Vt, Sm::pV, 32 * ks2, c0 + 16 * cb),
+                                        frag_cm<T>(sm.Vt, Sm::pV, 32 * ks2 + 16, c0 + 16 * cb), blo, bhi);
+                }
+                // slot e: column c0 + 16cb + 4(l/16) + e of the pass, token 16rb + l%16
+                const int t = 16 * rb + (l & 15);
+#pragma unroll
+                for (int cb = 0; cb < CB2; ++cb) {
+                    const int jc = c0 + 16 * cb + 4 * (l >> 4);
+                    const f32x4 ct = *reinterpret_cast<const f32x4*>(sm.Cl + t * Sm::pC + jc);
+                    f32x4 o4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o4[e] = acc[cb][e] * exp2f(ct[e]);
+                    *reinterpret_cast<vec4_t<T>*>(oOi + t * V + j0 + jc) = to_vec4<T>(o4);
+                }
+            }
+        } else {
+            // element by element: column jj, tokens part, part + NPART, ...
+            for (int t = part; t < kChunk; t += NPART) {
+                const float ct = sm.Cl[t * Sm::pC + jj];
+                float acc = 0.f;
+                for (int s2 = 0; s2 <= t; ++s2)
+                    acc += Elem<T>::to_f(sm.A[t * Sm::pA + s2]) * Elem<T>::to_f(sm.Vt[s2 * Sm::pV + jj]) *
+                           exp2f(ct - sm.Cl[s2 * Sm::pC + jj]);
+                oOi[t * V + j0 + jj] = Elem<T>::from_f(acc);
+            }
+        }
+        __syncthreads();  // B4: the pass's LDS may be refilled
+    }
+}
+
+template <typename T, int KD, int BV, bool OUT, bool GEN = false>
 struct WideSmem {
     static constexpr int NC = 4;        // consumer (matrix) waves
     static constexpr int CW = BV / NC;  // value columns per consumer wave
@@ -199,8 +428,13 @@ struct WideSmem {
     alignas(16) T KtT[2][KD * pKtT];
     alignas(16) T Vw[2][NC * kChunk * pW];
     alignas(16) float pp[2][2 * KD];  // pre, post
-    alignas(16) T A[OUT ? 2 : 1][OUT ? kChunk * pA : 8];
+    alignas(16) T A[OUT && !GEN ? 2 : 1][OUT && !GEN ? kChunk * pA : 8];
     alignas(16) T Ql[OUT ? kChunk * pQl : 8];
+    // general gates: each consumer's slices of exp2(C_t) and of the intra-chunk
+    // output (laid out like its value slice), and exp2(C_63) of the block's columns
+    alignas(16) T Cs[GEN && OUT ? 2 : 1][GEN && OUT ? NC * kChunk * pW : 8];
+    alignas(16) T Oi[GEN && OUT ? 2 : 1][GEN && OUT ? NC * kChunk * pW : 8];
+    alignas(16) float pb[GEN ? 2 : 1][GEN ? BV : 4];
     int flag[2];
 };
 
@@ -218,17 +452,27 @@ struct WideSmem {
 //              Ql of c+1 into the single Ql buffer | barrier E
 // Each producer wave keeps the records of two chunks in registers: at chunk c
 // it fetches chunk c+2 into the set that chunk c came in.
-template <typename T, int KD, int BV, bool OUT>
+//
+// GEN: general gates (value-side gate beta = exp(h) as well, records of
+// GenRec): the value slices come from the records (v * exp2(C_63 - C_t)), the
+// output is (Ql S) * exp2(C_t) plus the record's intra-chunk output, and the
+// state's columns decay by exp2(C_63) as its rows do by the key-side gate; the
+// state pass also writes the segment's column log2 decays to ws_gateb.
+template <typename T, int KD, int BV, bool OUT, bool GEN = false>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
                   T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
-                  int seg_len, int nseg, int BH) {
+                  int seg_len, int nseg, int BH, float* __restrict__ ws_gateb = nullptr) {
     constexpr int NC = 4, NP = 64 * NC;  // consumer waves; producer threads
-    using Sm = WideSmem<T, KD, BV, OUT>;
+    using Sm = WideSmem<T, KD, BV, OUT, GEN>;
     using R = WideRec<KD>;
+    using G = GenRec<KD>;
+    const long rbytes = GEN ? G::bytes(V) : R::bytes;
+    const long oQl = GEN ? G::oQl : R::oQl, oKtT = GEN ? G::oKtT : R::oKtT;
+    const long oPP = GEN ? G::oPP : R::oPP, oFlag = GEN ? G::oFlag : R::oFlag;
     constexpr int CW = Sm::CW, CB = CW / 16;
-    static_assert(2 * KD / 4 <= NP && KD <= NP, "gate factors: one vector or value per producer thread");
+    static_assert(2 * KD / 4 <= NP && KD <= NP && BV <= NP, "gate factors: one vector or value per producer thread");
     __shared__ Sm sm;
     const int tid = threadIdx.x, l = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
@@ -249,28 +493,42 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     if (producer) {
         // ---------------- producers: records -> LDS
         const int ptid = tid - NP;
-        float gtot = 0.f;  // state pass: thread ptid sums B_63 of key column ptid
+        float gtot = 0.f;   // state pass: thread ptid sums B_63 of key column ptid
+        float gtotb = 0.f;  // GEN state pass: thread ptid sums C_63 of value column vb*BV + ptid
         struct Regs {
             TileRegs<T, KD, NP> Ql, Kt;  // Kt: the [KD][64] Kt^T block as 64 rows of KD (linear)
             TileRegs<T, kChunk, NP> A;
-            TileRegs<T, CW, 64> v;
+            TileRegs<T, CW, 64> v, cs, oi;
             f32x4 pp;
-            float bl;
+            float bl, gb, cb;
             int flag;
         };
         Regs ra, rb;
         auto fetch = [&](Regs& x, int c) {
-            const unsigned char* r = rec + ((long)bh * N + c) * R::bytes;
-            x.Kt.load(reinterpret_cast<const T*>(r + R::oKtT), KD, ptid);
+            const unsigned char* r = rec + ((long)bh * N + c) * rbytes;
+            x.Kt.load(reinterpret_cast<const T*>(r + oKtT), KD, ptid);
             if constexpr (OUT) {
-                x.Ql.load(reinterpret_cast<const T*>(r + R::oQl), KD, ptid);
-                x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
+                x.Ql.load(reinterpret_cast<const T*>(r + oQl), KD, ptid);
+                if constexpr (!GEN) x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
             }
-            const float* pp = reinterpret_cast<const float*>(r + R::oPP);
+            const float* pp = reinterpret_cast<const float*>(r + oPP);
             if (ptid < KD / 2) x.pp = *reinterpret_cast<const f32x4*>(pp + 4 * ptid);
             if (!OUT && ptid < KD) x.bl = pp[2 * KD + ptid];
-            if (ptid == 0) x.flag = *reinterpret_cast<const int*>(r + R::oFlag);
-            x.v.load(v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0, rsV, l);
+            if (ptid == 0) x.flag = *reinterpret_cast<const int*>(r + oFlag);
+            if constexpr (GEN) {
+                x.v.load(reinterpret_cast<const T*>(r + G::oVp) + col0, V, l);
+                if constexpr (OUT) {
+                    x.cs.load(reinterpret_cast<const T*>(r + G::oCs(V)) + col0, V, l);
+                    x.oi.load(reinterpret_cast<const T*>(r + G::oOi(V)) + col0, V, l);
+                }
+                const float* pbg = reinterpret_cast<const float*>(r + G::oPB(V));
+                if (ptid < BV) {
+                    x.gb = pbg[vb * BV + ptid];
+                    if (!OUT) x.cb = pbg[V + vb * BV + ptid];
+                }
+            } else {
+                x.v.load(v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0, rsV, l);
+            }
         };
         // everything but Ql into buffer bf
         auto stash = [&](const Regs& x, int bf) {
@@ -280,11 +538,21 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                 const int q = ptid + i * NP;
                 *reinterpret_cast<u32x4*>(sm.KtT[bf] + (q / (kChunk / 8)) * Sm::pKtT + (q % (kChunk / 8)) * 8) = x.Kt.r[i];
             }
-            if constexpr (OUT) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
+            if constexpr (OUT && !GEN) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
             if (ptid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp[bf] + 4 * ptid) = x.pp;
             if (!OUT && ptid < KD) gtot += x.bl;
             if (ptid == 0) sm.flag[bf] = x.flag;
             x.v.store_lds(sm.Vw[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
+            if constexpr (GEN) {
+                if constexpr (OUT) {
+                    x.cs.store_lds(sm.Cs[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
+                    x.oi.store_lds(sm.Oi[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
+                }
+                if (ptid < BV) {
+                    sm.pb[bf][ptid] = x.gb;
+                    if (!OUT) gtotb += x.cb;
+                }
+            }
         };
         // chunk c+1 (in x) into LDS during chunk c, then chunk c+3 into x
         auto step = [&](Regs& x, int c) {
@@ -310,6 +578,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             if (c + 1 < c_end) step(ra, c + 1);
         }
         if (!OUT && vb == 0 && ptid < KD) ws_gate[((long)bh * P + seg) * KD + ptid] = gtot;
+        if (GEN && !OUT && ptid < BV) ws_gateb[((long)bh * P + seg) * V + vb * BV + ptid] = gtotb;
         return;
     }
 
@@ -368,7 +637,26 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
-        if constexpr (OUT) {
+        if constexpr (OUT && GEN) {
+            // O = (Ql S) * exp2(C_t) + the record's intra-chunk output; slot e:
+            // column 16cb + 4(l/16) + e of the slice, token 16rb + l%16
+            T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+            const T* csw = sm.Cs[bf] + w * kChunk * Sm::pW;
+            const T* oiw = sm.Oi[bf] + w * kChunk * Sm::pW;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int t = 16 * rb + (l & 15), jc = 16 * cb + 4 * (l >> 4);
+                    const vec4_t<T> cs = *reinterpret_cast<const vec4_t<T>*>(csw + t * Sm::pW + jc);
+                    const vec4_t<T> oi = *reinterpret_cast<const vec4_t<T>*>(oiw + t * Sm::pW + jc);
+                    f32x4 o4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o4[e] = acc[rb][cb][e] * Elem<T>::to_f(cs[e]) + Elem<T>::to_f(oi[e]);
+                    *reinterpret_cast<vec4_t<T>*>(obase + t * rsV + jc) = to_vec4<T>(o4);
+                }
+        } else if constexpr (OUT) {
             // O^T[j][t] += sum_s V[s][j] A[t][s]
             T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
 #pragma unroll
@@ -392,7 +680,21 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         // column of the chunk left the basis range (the flag)
         const float* pre = sm.pp[bf];
         const float* post = sm.pp[bf] + KD;
-        if (sm.flag[bf]) {
+        if constexpr (GEN) {
+            // rows by pre (when flagged), columns by exp2(C_63): slot e of S.s[a][cb]
+            // is key row 16a + 4(l/16) + e, column 16cb + l%16 of the slice
+            float gc[CB];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) gc[cb] = sm.pb[bf][w * CW + 16 * cb + (l & 15)];
+            const bool fl = sm.flag[bf] != 0;
+#pragma unroll
+            for (int a = 0; a < KD / 16; ++a) {
+                const f32x4 f = fl ? *reinterpret_cast<const f32x4*>(pre + 16 * a + 4 * (l >> 4))
+                                   : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= f * gc[cb];
+            }
+        } else if (sm.flag[bf]) {
 #pragma unroll
             for (int a = 0; a < KD / 16; ++a) {
                 const f32x4 f = *reinterpret_cast<const f32x4*>(pre + 16 * a + 4 * (l >> 4));

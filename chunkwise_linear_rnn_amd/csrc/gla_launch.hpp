@@ -20,6 +20,8 @@ struct FwdLaunch {
     void* ws_state;   // [BH][P][K][V] in the input dtype
     float* ws_gate;   // [BH][P][K]    fp32 (log2 of the segment decay)
     void* ws_rec;     // [BH][N] chunk records of the wide-head forward
+    const void* h;    // general gates: log beta, [B,T,H,V] (null otherwise)
+    float* ws_gateb;  // general gates: [BH][P][V] fp32 (log2 of the segment's column decay)
     hipStream_t stream;
 };
 
@@ -58,7 +60,8 @@ struct DecodeLaunch {
 };
 
 hipError_t launch_fwd(const FwdLaunch& a);
-hipError_t launch_fwd_wide(const FwdLaunch& a);  // 16-bit, K = 256
+hipError_t launch_fwd_wide(const FwdLaunch& a);
+hipError_t launch_fwd_general(const FwdLaunch& a);  // 16-bit, K = 256
 hipError_t launch_decode(const DecodeLaunch& a);
 hipError_t launch_bwd(const BwdLaunch& a);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream);

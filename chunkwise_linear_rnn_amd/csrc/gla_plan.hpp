@@ -123,6 +123,29 @@ inline size_t fwd_seg_bytes(const Shape& s, const Plan& p) {
     return state_bytes(s, p) + round256(gt);
 }
 
+// General gates (16-bit, K in {128, 256}): 64 value columns per
+// workgroup; records carry the key side and the value side of each chunk.
+inline Plan make_fwd_general_plan(const Shape& s) {
+    Plan p = make_plan(s, (int)(s.V / 64));
+    p.BV = 64;
+    p.NW = 4;
+    return p;
+}
+constexpr size_t gen_record_bytes(int64_t K, int64_t V) {
+    return (size_t)(4 * 64 * K + 12 * K + 256 + 6 * 64 * V + 8 * V);
+}
+// segment states, key-row and value-column gate totals (P > 1), then records
+inline size_t fwd_general_seg_bytes(const Shape& s, const Plan& p) {
+    if (p.P <= 1 || p.BH == 0) return 0;
+    return state_bytes(s, p) + round256((size_t)p.BH * p.P * (size_t)s.K * sizeof(float)) +
+           round256((size_t)p.BH * p.P * (size_t)s.V * sizeof(float));
+}
+inline size_t fwd_general_workspace_bytes(const Shape& s) {
+    Plan p = make_fwd_general_plan(s);
+    if (p.BH == 0) return 0;
+    return fwd_general_seg_bytes(s, p) + (size_t)p.BH * p.N * gen_record_bytes(s.K, s.V);
+}
+
 inline size_t fwd_workspace_bytes(const Shape& s) {
     Plan p = make_fwd_plan(s);
     if (p.BH == 0) return 0;

@@ -115,6 +115,26 @@ def make_inputs(w: Workload, device: Optional[str] = None, dht: bool = False) ->
     return out
 
 
+def make_value_gate(B: int, T: int, H: int, V: int, dtype: str = "bf16", seed: int = 0,
+                    kind: str = "lowrank") -> torch.Tensor:
+    """The value-side log gate h = log beta [B,T,H,V] of general gated linear
+    attention, drawn like the key-side gate: ``lowrank`` logsigmoid(x W) / 16
+    with x ~ N(0,1) in R^{B x T x 16} and W ~ N(0,1)/4 in R^{16 x H*V}; ``iid``
+    logsigmoid(N(0,1)) / 16; ``zero`` all zeros (beta = 1)."""
+    gen = torch.Generator().manual_seed(seed)
+    if kind == "lowrank":
+        x = torch.randn(B, T, 16, generator=gen)
+        W = torch.randn(16, H * V, generator=gen) / 4.0
+        h = (F.logsigmoid(x @ W) / 16.0).reshape(B, T, H, V)
+    elif kind == "iid":
+        h = F.logsigmoid(torch.randn(B, T, H, V, generator=gen)) / 16.0
+    elif kind == "zero":
+        h = torch.zeros(B, T, H, V)
+    else:
+        raise ValueError(kind)
+    return h.to(torch.float32 if dtype == "fp32" else torch.bfloat16)
+
+
 def make_gate_inputs(B: int, T: int, H: int, V: int, dtype: str = "bf16", seed: int = 0, bias: bool = True,
                      device: Optional[str] = None) -> Dict[str, Optional[torch.Tensor]]:
     """Inputs of the GLA layer's output epilogue (per-head LayerNorm, Swish gate).

@@ -154,6 +154,36 @@ gla_status_t gla_bwd_scalar(const gla_shape_t* shape,
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
 
 /*
+ * gla_fwd_general -- forward pass of general gated linear attention, whose
+ * forget gate is an outer product G_t = alpha_t^T beta_t of a key-side gate
+ * alpha_t = exp(g_t) and a value-side gate beta_t = exp(h_t) ("Gated Linear
+ * Attention Transformers with Hardware-Efficient Training", the chapter
+ * summary's Knowl 12 and Appendix C):
+ *     S_t = (alpha_t^T beta_t) .* S_{t-1} + k_t^T v_t ,   o_t = q_t S_t .
+ * h = 0 gives gla_fwd.  Chunkwise: per chunk, with B_t / C_t the cumulative
+ * log2 gates of the key / value columns, the output is
+ * (q_t exp2(B_t)) S exp2(C_t) plus the intra-chunk term, and the state's rows
+ * and columns decay by exp2(B_63) and exp2(C_63).
+ *   q, k, g : [B,T,H,K] bf16   (g <= 0)
+ *   v, h    : [B,T,H,V] bf16   (h = log beta <= 0)
+ *   s0, o, s_final, stream : as for gla_fwd
+ *   workspace : at least gla_fwd_general_workspace_size(shape) bytes
+ * bf16 with K in {128, 256} and V in {64, 128, 256, 512}; other shapes and
+ * fp32 return GLA_ERR_UNSUPPORTED.  Results are deterministic.  Forward only.
+ */
+gla_status_t gla_fwd_general(const gla_shape_t* shape,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const void* h, const float* s0, void* o, float* s_final,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gla_fwd_general needs (0 for fp32, K = 64 or an invalid
+ * shape; no HIP call).  Segment states and the segments' key-row and
+ * value-column log-decays, and one record per chunk and head of
+ * 268 K + 392 V + 256 bytes (prepared key-side operands, v * exp2(C_63 - C_t),
+ * exp2(C_t), the intra-chunk output and the column decays). */
+size_t gla_fwd_general_workspace_size(const gla_shape_t* shape);
+
+/*
  * gla_decode -- the recurrent form of Eq. 3 (Section 3.1), for token-by-token
  * inference with the state carried between calls: for t = 1..T,
  *     S <- Diag(exp g_t) S + k_t^T v_t ,   o_t = q_t S ,

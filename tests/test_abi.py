@@ -175,3 +175,24 @@ def test_scalar_gate_entry_points_validate(L):
     assert fwd(_shape(T=128), g=None) == ERR_NULL
     assert fwd(_shape(T=128), g=ctypes.c_void_p(0x10002)) == ERR_ALIGN
     assert fwd(_shape(T=0)) == OK
+
+
+def test_general_gate_entry_point_validates(L):
+    # bf16 with K in {128, 256} only; one record per chunk and head holding the
+    # key side (Ql, Kt^T and gate factors) and the value side (three [64, V]
+    # tiles and the column decays)
+    ws = lambda shape: L.gla_fwd_general_workspace_size(ctypes.byref(shape))
+    assert ws(_shape(T=128, dtype=gla.GLA_DTYPE_FP32)) == 0
+    assert ws(_shape(T=128, K=64, V=64)) == 0
+    assert ws(_shape(T=100, K=128)) == 0
+    s = _shape(B=2, H=4, T=8192, K=256, V=512)
+    assert ws(s) == ws(s) and ws(s) >= 2 * 4 * 128 * (2 * 2 * 64 * 256 + 3 * 2 * 64 * 512)
+    fwd = lambda shape, **kw: L.gla_fwd_general(ctypes.byref(shape), P, P, P, P, kw.get("h", P), None, P, None,
+                                                kw.get("ws", P), 1 << 40, None)
+    assert fwd(_shape(T=128, K=128, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert fwd(_shape(T=128, K=64, V=64)) == ERR_UNSUPPORTED
+    assert fwd(_shape(T=100, K=128)) == ERR_SHAPE
+    assert fwd(_shape(T=128, K=128), h=None) == ERR_NULL
+    assert fwd(_shape(T=128, K=128), h=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert fwd(_shape(T=128, K=128), ws=None) == ERR_WORKSPACE
+    assert fwd(_shape(T=0, K=128)) == OK
