@@ -305,8 +305,15 @@ def fwd_only_bench(args, torch, gla, gi):
     d = {k: (v.to(dev) if v is not None else None) for k, v in cpu.items()}
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
     sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
-    ws = gla.workspace(gla.gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
-    fwd = lambda: gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, ws)
+    general = args.general_gate
+    if general:
+        # general gates: a value-side log gate h [B,T,H,V] as well (gla_fwd_general)
+        hv = gi.make_value_gate(B, T, H, V, dtype=w.dtype, seed=w.seed + 1).to(dev)
+        ws = gla.workspace(gla.gla_fwd_general_workspace_size(B, T, H, K, V, dt), dev)
+        fwd = lambda: gla.gla_fwd_general_into(d["q"], d["k"], d["v"], d["g"], hv, d["s0"], o, sf, ws)
+    else:
+        ws = gla.workspace(gla.gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+        fwd = lambda: gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, ws)
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
@@ -327,13 +334,15 @@ def fwd_only_bench(args, torch, gla, gi):
     units = B * T * H
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     flops = fwd_flops_per_token_head(K, V) * units
-    line = {"metric": "GLA forward tokens/sec and %% of MFMA peak (%s)" % w.name, "value": B * T / (ms * 1e-3),
+    op = "gla_fwd_general" if general else "gla_fwd"
+    line = {"metric": "%s forward tokens/sec and %% of MFMA peak (%s)" % ("General GLA" if general else "GLA", w.name),
+            "value": B * T / (ms * 1e-3),
             "unit": "tokens/s", "n_gpus": 1, "steps": n, "ms_per_step": ms, "higher_is_better": True,
             "dtype": w.dtype, "data": "synthetic",
-            "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, gla_fwd per step" % (
-                w.name, B, H, T, K, V, w.dtype)},
+            "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, %s per step" % (
+                w.name, B, H, T, K, V, w.dtype, op)},
             "mfma_frac": flops / (ms * 1e-3) / (peak_tf * 1e12),
-            "hbm_frac": e * (3 * K + 2 * V) * units / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "hbm_frac": e * (3 * K + (3 if general else 2) * V) * units / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "kernels": {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}}
     print(json.dumps(line), flush=True)
 
@@ -350,6 +359,8 @@ def main():
                     help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time gla_fwd alone on --workload (also those without backward inputs)")
+    ap.add_argument("--general-gate", action="store_true",
+                    help="with --fwd-only: time gla_fwd_general (alpha^T beta gates, h drawn like g)")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="the workload with one log gate per token and head (gla_fwd_scalar / gla_bwd_scalar)")
     ap.add_argument("--out-gate", action="store_true",

@@ -27,7 +27,7 @@ static hipError_t launch_fwd_wide_bv(const FwdLaunch& a) {
     const int nvb = a.V / BV;
     unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);
     GLA_LAUNCH("fwd_prep", (gla_fwd_wide_prep<T, KD, SG>), dim3((unsigned)(a.BH * a.N)), dim3(256), a.stream,
-               (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N);
+               (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N, (long)WideRec<KD>::bytes);
     if (a.P > 1) {
         const int nseg = a.P - 1;
         GLA_LAUNCH("fwd_seg_state", (gla_fwd_wide_walk<T, KD, BV, false>), dim3((unsigned)xcd_grid(nseg * a.BH, nvb)),
@@ -87,20 +87,21 @@ gla_seg_combine_fwd_general(const float* __restrict__ s0, bf16* __restrict__ ws_
 }
 
 // General gates (16-bit): records, the state pass over segments 0..P-2, the
-// combine, and the output walk, all at 64 value columns per workgroup.
-template <int KD, int VP>
+// combine, and the output walk, at BV value columns per workgroup.
+template <int KD, int VP, int BV>
 static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
     using T = bf16;
-    constexpr int BV = 64;
-    static_assert(sizeof(GenPrepSmem<T, KD, VP>) <= 160 * 1024, "LDS budget");
+    static_assert(sizeof(GenPrepSmem<T, VP>) <= 80 * 1024, "two value-side workgroups per CU");
     static_assert(sizeof(WideSmem<T, KD, BV, true, true>) <= 160 * 1024, "LDS budget");
     static_assert(GenRec<KD>::bytes(512) == (long)gen_record_bytes(KD, 512), "record size as the workspace plans it");
     if ((long)GenRec<KD>::bytes(a.V) != (long)gen_record_bytes(KD, a.V)) return hipErrorInvalidValue;
     const int nvb = a.V / BV;
     unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);
-    GLA_LAUNCH("fwd_general_prep", (gla_fwd_general_prep<T, KD, VP>), dim3((unsigned)(a.BH * a.N)), dim3(256),
-               a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.h, rec, a.T, a.H,
-               a.V, a.N);
+    GLA_LAUNCH("fwd_prep", (gla_fwd_wide_prep<T, KD, false>), dim3((unsigned)(a.BH * a.N)), dim3(256), a.stream,
+               (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N, (long)GenRec<KD>::bytes(a.V));
+    GLA_LAUNCH("fwd_general_vprep", (gla_fwd_general_vprep<T, KD, VP>),
+               dim3((unsigned)(a.BH * a.N), (unsigned)(a.V / VP)), dim3(256), a.stream, (const T*)a.v,
+               (const T*)a.h, rec, a.T, a.H, a.V, a.N);
     if (a.P > 1) {
         const int nseg = a.P - 1;
         GLA_LAUNCH("fwd_general_seg_state", (gla_fwd_wide_walk<T, KD, BV, false, true>),
@@ -121,7 +122,9 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
 
 template <int KD>
 static hipError_t launch_fwd_general_k(const FwdLaunch& a) {
-    return a.V % 128 == 0 ? launch_fwd_general_kv<KD, 128>(a) : launch_fwd_general_kv<KD, 64>(a);
+    if (a.BV == 128 && a.V % 128 == 0) return launch_fwd_general_kv<KD, 128, 128>(a);
+    if (a.BV == 64 && a.V == 64) return launch_fwd_general_kv<KD, 64, 64>(a);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_general(const FwdLaunch& a) {

@@ -58,21 +58,17 @@ struct WideRec {
 
 // The record of one chunk and head under general gates G_t = alpha_t^T beta_t
 // ("Gated Linear Attention Transformers with Hardware-Efficient Training", the
-// chapter summary's Knowl 12 and Appendix C): the key side
-// as above (no A: the intra-chunk output comes whole), then the value side,
-// with C_t the intra-chunk cumulative log2 of beta in each value column.
+// chapter summary's Knowl 12 and Appendix C): the key-side record above, then
+// the value side, with C_t the intra-chunk cumulative log2 of beta per column.
 template <int KD>
 struct GenRec {
-    static constexpr long oQl = 0;                        // [64][KD]  Ql, key columns in MFMA order
-    static constexpr long oKtT = oQl + 2L * kChunk * KD;  // [KD][64]  Kt transposed, tokens in MFMA order
-    static constexpr long oPP = oKtT + 2L * kChunk * KD;  // fp32 [3][KD]: pre, post, B_63
-    static constexpr long oFlag = oPP + 12L * KD;         // int: some key column left the basis range
-    static constexpr long oVp = oFlag + 256;              // [64][V]  v * exp2(C_63 - C_t)
-    static constexpr long oCs(int V) { return oVp + 2L * kChunk * V; }  // [64][V]  exp2(C_t)
-    static constexpr long oOi(int V) { return oCs(V) + 2L * kChunk * V; }  // [64][V]  intra-chunk output
-    static constexpr long oPB(int V) { return oOi(V) + 2L * kChunk * V; }  // fp32 [2][V]: exp2(C_63), C_63
+    static constexpr long oQl = WideRec<KD>::oQl, oKtT = WideRec<KD>::oKtT, oA = WideRec<KD>::oA;
+    static constexpr long oPP = WideRec<KD>::oPP, oFlag = WideRec<KD>::oFlag;
+    static constexpr long oVp = WideRec<KD>::bytes;                           // [64][V]  v * exp2(C_63 - C_t)
+    static constexpr long oCs(int V) { return oVp + 2L * kChunk * V; }      // [64][V]  exp2(C_t)
+    static constexpr long oOi(int V) { return oCs(V) + 2L * kChunk * V; }   // [64][V]  intra-chunk output
+    static constexpr long oPB(int V) { return oOi(V) + 2L * kChunk * V; }   // fp32 [2][V]: exp2(C_63), C_63
     static constexpr long bytes(int V) { return oPB(V) + 8L * V; }
-    static_assert(oVp % 256 == 0, "value-side tiles stay 256-byte aligned");
 };
 
 template <typename T, int KD>
@@ -95,7 +91,7 @@ struct WidePrepSmem {
 template <typename T, int KD, bool SG>
 __global__ void __launch_bounds__(256)
 gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
-                  unsigned char* __restrict__ rec, int T_, int H, int N) {
+                  unsigned char* __restrict__ rec, int T_, int H, int N, long rstride) {
     constexpr int NW = 4, NT = NW * 64, CPK = KD / NW, VEC = 16 / (int)sizeof(T), VPR = KD / VEC;
     static_assert(CPK <= 64 && (kChunk * VPR) % NT == 0, "prep tiling");
     using Sm = WidePrepSmem<T, KD>;
@@ -123,7 +119,7 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     pipe_prep<T, CPK>(sm.buf, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, CPK / VEC);
     __syncthreads();
 
-    unsigned char* r = rec + unit * R::bytes;
+    unsigned char* r = rec + unit * rstride;  // records of WideRec or GenRec layout
     T* oQl = reinterpret_cast<T*>(r + R::oQl);
     T* oKtT = reinterpret_cast<T*>(r + R::oKtT);
     T* oA = reinterpret_cast<T*>(r + R::oA);
@@ -200,22 +196,22 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     }
 }
 
-template <typename T, int KD, int VP>
+template <typename T, int VP>
 struct GenPrepSmem {
+    static constexpr int NT = 256;
     static constexpr int pA = kChunk + 8;  // A, read as row fragments
     static constexpr int pV = VP + 8;      // scaled (or raw) values, read as column fragments
     static constexpr int pC = VP + 4;      // C_t, fp32
-    typename WidePrepSmem<T, KD>::Buf buf;
     alignas(16) T A[kChunk * pA];
     alignas(16) T Vt[kChunk * pV];
     alignas(16) float Cl[kChunk * pC];
-    float tot[4][VP];
+    alignas(16) float tot[NT / (VP / 8)][VP];
     int flagb;
 };
 
-// One workgroup (four waves) per chunk and head under general gates.  The key
-// side is the forward's record (Ql, Kt, pre/post, flag) with A kept in LDS;
-// the value side then takes VP columns per pass:
+// The value side of a general-gate record: one workgroup (four waves) per
+// chunk, head and VP value columns, after the key side (gla_fwd_wide_prep,
+// which leaves A in the record):
 //   C_t = cumulative sum of h * log2(e) within the chunk (exp(h) = beta)
 //   Vp = v * exp2(C_63 - C_t), Cs = exp2(C_t), and the intra-chunk output
 //   Oi[t][j] = sum_{s <= t} A[t][s] v[s][j] exp2(C_t[j] - C_s[j])
@@ -224,147 +220,105 @@ struct GenPrepSmem {
 // stay a well-scaled fp32/bf16 value).
 template <typename T, int KD, int VP>
 __global__ void __launch_bounds__(256)
-gla_fwd_general_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                     const T* __restrict__ g, const T* __restrict__ hg, unsigned char* __restrict__ rec, int T_, int H,
-                     int V, int N) {
-    constexpr int NW = 4, NT = NW * 64, CPK = KD / NW, VEC = 16 / (int)sizeof(T), VPR = KD / VEC;
-    constexpr int NPART = NT / VP, TPP = kChunk / NPART;  // token parts per column, tokens per part
-    constexpr int CB2 = VP / NW / 16;                     // 16-column blocks per wave in the output product
-    static_assert(CPK <= 64 && (kChunk * VPR) % NT == 0, "prep tiling");
-    static_assert((VP == 64 || VP == 128) && CB2 >= 1, "value pass width");
-    using Sm = GenPrepSmem<T, KD, VP>;
-    using WS = WidePrepSmem<T, KD>;
+gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigned char* __restrict__ rec, int T_,
+                      int H, int V, int N) {
+    constexpr int NW = 4, NT = NW * 64;
+    constexpr int CV = VP / 8, NPART = NT / CV, TPP = kChunk / NPART;  // column vectors, token parts, tokens per part
+    constexpr int CB2 = VP / NW / 16;                                  // 16-column blocks per wave in the output product
+    static_assert((VP == 64 || VP == 128) && CB2 >= 1 && NPART * TPP == kChunk, "value pass width");
+    using Sm = GenPrepSmem<T, VP>;
     using G = GenRec<KD>;
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-    const long unit = blockIdx.x;  // bh * N + chunk; the grid has exactly BH * N blocks
+    const long unit = blockIdx.x;  // bh * N + chunk; the grid has exactly BH * N x V / VP blocks
+    const int j0 = blockIdx.y * VP;
     const int bh = (int)(unit / N), c = (int)(unit % N);
     const int b = bh / H, h = bh % H;
-    const int rsK = H * KD, rsV = H * V;
+    const int rsV = H * V;
     const long row0 = (long)b * T_ + (long)c * kChunk;
-    const T* qb = q + row0 * rsK + (long)h * KD;
-    const T* kb = k + row0 * rsK + (long)h * KD;
-    const T* gb = g + row0 * rsK + (long)h * KD;
-    const int kc0 = w * CPK;
-
-    // ---- key side
-    RowSlab<T, CPK> rq, rk;
-    GateSlab<T, CPK, false> rg;
-    rq.load(qb, rsK, kc0);
-    rk.load(kb, rsK, kc0);
-    rg.load(gb, rsK, kc0);
-    if (tid == 0) sm.buf.flag[0] = 0;
-    __syncthreads();
-    pipe_prep<T, CPK>(sm.buf, WS::pQl, WS::pKt, rq, rk, rg, kc0, 0, CPK / VEC);
-    __syncthreads();
-
     unsigned char* r = rec + unit * G::bytes(V);
-    T* oQl = reinterpret_cast<T*>(r + G::oQl);
-    T* oKtT = reinterpret_cast<T*>(r + G::oKtT);
-    float* opp = reinterpret_cast<float*>(r + G::oPP);
-    typedef unsigned int __attribute__((ext_vector_type(2))) u32x2;
+    {
+        const T* a = reinterpret_cast<const T*>(r + G::oA);
 #pragma unroll
-    for (int i = 0; i < kChunk * VPR / NT; ++i) {
-        const int p = tid + i * NT, row = p / VPR, col = (p % VPR) * VEC;
-        const int src = (col & ~31) + 4 * ((col & 31) >> 3);
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(sm.buf.Ql + row * WS::pQl + src);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(sm.buf.Ql + row * WS::pQl + src + 16);
-        *reinterpret_cast<u32x4*>(oQl + row * KD + col) = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-#pragma unroll
-    for (int u = w; u < (KD / 16) * (kChunk / 32); u += NW) {
-        const int c0 = 16 * (u % (KD / 16)), ks = u / (KD / 16);
-        const vec4_t<T> lo = frag_cm<T>(sm.buf.Kt, WS::pKt, 32 * ks, c0);
-        const vec4_t<T> hi = frag_cm<T>(sm.buf.Kt, WS::pKt, 32 * ks + 16, c0);
-        const u32x2 a = __builtin_bit_cast(u32x2, lo), bq = __builtin_bit_cast(u32x2, hi);
-        *reinterpret_cast<u32x4*>(oKtT + (c0 + (l & 15)) * kChunk + 32 * ks + 8 * (l >> 4)) = u32x4{a[0], a[1], bq[0], bq[1]};
-    }
-    for (int i = tid; i < KD; i += NT) {
-        const float pre = sm.buf.pre[i], post = sm.buf.post[i];
-        opp[i] = pre;
-        opp[KD + i] = post;
-        opp[2 * KD + i] = log2f(pre * post);
-    }
-    const bool exact = sm.buf.flag[0] != 0;
-    if (tid == 0) *reinterpret_cast<int*>(r + G::oFlag) = exact ? 1 : 0;
-    if (!exact) {
-        for (int tile = w; tile < 10; tile += NW) {
-            int is, js;
-            decode_tile(tile, is, js);
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KD / 32; ++ks)
-                acc = mma32(acc, frag_rm<T>(sm.buf.Kt, WS::pKt, 16 * js, 32 * ks),
-                            frag_rm<T>(sm.buf.Kt, WS::pKt, 16 * js, 32 * ks + 16),
-                            frag_rm<T>(sm.buf.Ql, WS::pQl, 16 * is, 32 * ks),
-                            frag_rm<T>(sm.buf.Ql, WS::pQl, 16 * is, 32 * ks + 16));
-            // acc holds A^T[s][t] for s = 16js + 4(l/16) + e, t = 16is + l%16
-            if (is == js) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * (l >> 4) + e > (l & 15)) acc[e] = 0.f;
-            }
-            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
-                to_vec4<T>(acc);
-        }
-        for (int z = w; z < 6; z += NW) {
-            const int is = (z >= 3) + (z >= 5);
-            const int js = z + 1 - (is == 1 ? 2 : (is == 2 ? 3 : 0));
-            *reinterpret_cast<vec4_t<T>*>(sm.A + (16 * is + (l & 15)) * Sm::pA + 16 * js + 4 * (l >> 4)) =
-                to_vec4<T>(zero4());
-        }
-    } else {
-        __syncthreads();  // every thread has copied Ql out
-        float* Af = reinterpret_cast<float*>(sm.buf.Ql);
-        exact_intra_tile<T, KD, NW, false>(Af, WS::pF, qb, kb, gb, rsK, rsK, w);
-        __syncthreads();
-        for (int e = tid; e < kChunk * kChunk; e += NT) {
-            const int t = e / kChunk, s2 = e % kChunk;
-            sm.A[t * Sm::pA + s2] = Elem<T>::from_f(s2 <= t ? Af[t * WS::pF + s2] : 0.f);
+        for (int i = 0; i < kChunk * kChunk / 8 / NT; ++i) {
+            const int p = tid + i * NT, row = p / (kChunk / 8), col = (p % (kChunk / 8)) * 8;
+            *reinterpret_cast<u32x4*>(sm.A + row * Sm::pA + col) = *reinterpret_cast<const u32x4*>(a + row * kChunk + col);
         }
     }
-
-    // ---- value side, VP columns per pass
+    // ---- value side, VP columns per pass; thread (part, cv) scans columns
+    // 8cv .. 8cv+7 over tokens part*TPP .. +TPP-1 with 16-byte loads and stores
     T* oVp = reinterpret_cast<T*>(r + G::oVp);
     T* oCs = reinterpret_cast<T*>(r + G::oCs(V));
     T* oOi = reinterpret_cast<T*>(r + G::oOi(V));
     float* opb = reinterpret_cast<float*>(r + G::oPB(V));
-    const int jj = tid % VP, part = tid / VP, t0 = part * TPP;
-    for (int j0 = 0; j0 < V; j0 += VP) {
-        const long gofs = row0 * rsV + (long)h * V + j0 + jj;
-        float cl[TPP], vr[TPP];
+    const int cv = tid % CV, part = tid / CV, t0 = part * TPP, jv = 8 * cv;
+    const int jj = tid % VP, epart = tid / VP;  // element-wise path: column jj, tokens epart + k * (NT / VP)
+    {
+        const long gofs = row0 * rsV + (long)h * V + j0 + jv;
+        u32x4 hraw[TPP], vraw[TPP];
 #pragma unroll
         for (int i = 0; i < TPP; ++i) {
-            cl[i] = Elem<T>::to_f(hg[gofs + (long)(t0 + i) * rsV]) * kLog2e;
-            vr[i] = Elem<T>::to_f(v[gofs + (long)(t0 + i) * rsV]);
+            hraw[i] = *reinterpret_cast<const u32x4*>(hg + gofs + (long)(t0 + i) * rsV);
+            vraw[i] = *reinterpret_cast<const u32x4*>(v + gofs + (long)(t0 + i) * rsV);
         }
+        float cl[TPP][8];
 #pragma unroll
-        for (int i = 1; i < TPP; ++i) cl[i] += cl[i - 1];
+        for (int i = 0; i < TPP; ++i) {
+            const T* hx = reinterpret_cast<const T*>(&hraw[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cl[i][e] = Elem<T>::to_f(hx[e]) * kLog2e + (i > 0 ? cl[i - 1][e] : 0.f);
+        }
         if (tid == 0) sm.flagb = 0;
-        sm.tot[part][jj] = cl[TPP - 1];
-        __syncthreads();  // B1: part totals (and A) visible, flag cleared
-        float off = 0.f, c63 = 0.f;
+        *reinterpret_cast<f32x4*>(&sm.tot[part][jv]) = f32x4{cl[TPP - 1][0], cl[TPP - 1][1], cl[TPP - 1][2], cl[TPP - 1][3]};
+        *reinterpret_cast<f32x4*>(&sm.tot[part][jv + 4]) = f32x4{cl[TPP - 1][4], cl[TPP - 1][5], cl[TPP - 1][6], cl[TPP - 1][7]};
+        __syncthreads();  // B1: part totals and A visible, flag cleared
+        float off[8], c63[8];
 #pragma unroll
+        for (int e = 0; e < 8; ++e) off[e] = c63[e] = 0.f;
         for (int pp = 0; pp < NPART; ++pp) {
-            const float x = sm.tot[pp][jj];
-            if (pp < part) off += x;
-            c63 += x;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sm.tot[pp][jv]);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(&sm.tot[pp][jv + 4]);
+            const float m = pp < part ? 1.f : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                off[e] += m * x0[e];
+                off[4 + e] += m * x1[e];
+                c63[e] += x0[e];
+                c63[4 + e] += x1[e];
+            }
         }
-        if (-c63 > kBasisLimit) sm.flagb = 1;
+        bool out_of_range = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out_of_range |= -c63[e] > kBasisLimit;
+        if (out_of_range) sm.flagb = 1;
         if (part == 0) {
-            opb[j0 + jj] = exp2f(c63);
-            opb[V + j0 + jj] = c63;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                opb[j0 + jv + e] = exp2f(c63[e]);
+                opb[V + j0 + jv + e] = c63[e];
+            }
         }
         __syncthreads();  // B2: the pass's flag
         const bool fl = sm.flagb != 0;
 #pragma unroll
         for (int i = 0; i < TPP; ++i) {
             const int t = t0 + i;
-            const float ct = off + cl[i];
-            oVp[t * V + j0 + jj] = Elem<T>::from_f(vr[i] * exp2f(c63 - ct));
-            oCs[t * V + j0 + jj] = Elem<T>::from_f(exp2f(ct));
-            sm.Vt[t * Sm::pV + jj] = Elem<T>::from_f(fl ? vr[i] : vr[i] * exp2f(-ct));
-            sm.Cl[t * Sm::pC + jj] = ct;
+            const T* vx = reinterpret_cast<const T*>(&vraw[i]);
+            alignas(16) T vp8[8], cs8[8], vt8[8];
+            alignas(16) float ct8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ct = off[e] + cl[i][e], vv = Elem<T>::to_f(vx[e]);
+                ct8[e] = ct;
+                vp8[e] = Elem<T>::from_f(vv * exp2f(c63[e] - ct));
+                cs8[e] = Elem<T>::from_f(exp2f(ct));
+                vt8[e] = Elem<T>::from_f(fl ? vv : vv * exp2f(-ct));
+            }
+            *reinterpret_cast<u32x4*>(oVp + t * V + j0 + jv) = *reinterpret_cast<const u32x4*>(vp8);
+            *reinterpret_cast<u32x4*>(oCs + t * V + j0 + jv) = *reinterpret_cast<const u32x4*>(cs8);
+            *reinterpret_cast<u32x4*>(sm.Vt + t * Sm::pV + jv) = *reinterpret_cast<const u32x4*>(vt8);
+            *reinterpret_cast<f32x4*>(sm.Cl + t * Sm::pC + jv) = *reinterpret_cast<const f32x4*>(ct8);
+            *reinterpret_cast<f32x4*>(sm.Cl + t * Sm::pC + jv + 4) = *reinterpret_cast<const f32x4*>(ct8 + 4);
         }
         __syncthreads();  // B3: Vt and Cl complete
         if (!fl) {
@@ -396,8 +350,7 @@ gla_fwd_general_prep(const T* __restrict__ q, const T* __restrict__ k, const T* 
                 }
             }
         } else {
-            // element by element: column jj, tokens part, part + NPART, ...
-            for (int t = part; t < kChunk; t += NPART) {
+            for (int t = epart; t < kChunk; t += NT / VP) {
                 const float ct = sm.Cl[t * Sm::pC + jj];
                 float acc = 0.f;
                 for (int s2 = 0; s2 <= t; ++s2)
@@ -406,7 +359,6 @@ gla_fwd_general_prep(const T* __restrict__ q, const T* __restrict__ k, const T* 
                 oOi[t * V + j0 + jj] = Elem<T>::from_f(acc);
             }
         }
-        __syncthreads();  // B4: the pass's LDS may be refilled
     }
 }
 
@@ -430,10 +382,7 @@ struct WideSmem {
     alignas(16) float pp[2][2 * KD];  // pre, post
     alignas(16) T A[OUT && !GEN ? 2 : 1][OUT && !GEN ? kChunk * pA : 8];
     alignas(16) T Ql[OUT ? kChunk * pQl : 8];
-    // general gates: each consumer's slices of exp2(C_t) and of the intra-chunk
-    // output (laid out like its value slice), and exp2(C_63) of the block's columns
-    alignas(16) T Cs[GEN && OUT ? 2 : 1][GEN && OUT ? NC * kChunk * pW : 8];
-    alignas(16) T Oi[GEN && OUT ? 2 : 1][GEN && OUT ? NC * kChunk * pW : 8];
+    // general gates: exp2(C_63) of the block's value columns
     alignas(16) float pb[GEN ? 2 : 1][GEN ? BV : 4];
     int flag[2];
 };
@@ -498,7 +447,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         struct Regs {
             TileRegs<T, KD, NP> Ql, Kt;  // Kt: the [KD][64] Kt^T block as 64 rows of KD (linear)
             TileRegs<T, kChunk, NP> A;
-            TileRegs<T, CW, 64> v, cs, oi;
+            TileRegs<T, CW, 64> v;
             f32x4 pp;
             float bl, gb, cb;
             int flag;
@@ -517,10 +466,6 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             if (ptid == 0) x.flag = *reinterpret_cast<const int*>(r + oFlag);
             if constexpr (GEN) {
                 x.v.load(reinterpret_cast<const T*>(r + G::oVp) + col0, V, l);
-                if constexpr (OUT) {
-                    x.cs.load(reinterpret_cast<const T*>(r + G::oCs(V)) + col0, V, l);
-                    x.oi.load(reinterpret_cast<const T*>(r + G::oOi(V)) + col0, V, l);
-                }
                 const float* pbg = reinterpret_cast<const float*>(r + G::oPB(V));
                 if (ptid < BV) {
                     x.gb = pbg[vb * BV + ptid];
@@ -544,10 +489,6 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             if (ptid == 0) sm.flag[bf] = x.flag;
             x.v.store_lds(sm.Vw[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
             if constexpr (GEN) {
-                if constexpr (OUT) {
-                    x.cs.store_lds(sm.Cs[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
-                    x.oi.store_lds(sm.Oi[bf] + cw * kChunk * Sm::pW, Sm::pW, l);
-                }
                 if (ptid < BV) {
                     sm.pb[bf][ptid] = x.gb;
                     if (!OUT) gtotb += x.cb;
@@ -593,6 +534,22 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         const T* Vw = sm.Vw[bf] + w * kChunk * Sm::pW;
         vec4_t<T> vf[4][CB];
         f32x4 acc[4][CB];
+        // general gates: this lane's exp2(C_t) and intra-chunk output values,
+        // loaded from the record now and used after the matrix products
+        vec4_t<T> csr[GEN && OUT ? 4 : 1][CB], oir[GEN && OUT ? 4 : 1][CB];
+        if constexpr (GEN && OUT) {
+            const unsigned char* r = rec + ((long)bh * N + c) * rbytes;
+            const T* csg = reinterpret_cast<const T*>(r + G::oCs(V)) + col0;
+            const T* oig = reinterpret_cast<const T*>(r + G::oOi(V)) + col0;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int off = (16 * rb + (l & 15)) * V + 16 * cb + 4 * (l >> 4);
+                    csr[rb][cb] = *reinterpret_cast<const vec4_t<T>*>(csg + off);
+                    oir[rb][cb] = *reinterpret_cast<const vec4_t<T>*>(oig + off);
+                }
+        }
         if constexpr (OUT) {
             // O^T[j][t] = sum_i S[i][j] Ql[t][i]; the Ql fragments of step ks + 1
             // are read while the MFMAs of step ks run
@@ -641,19 +598,15 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             // O = (Ql S) * exp2(C_t) + the record's intra-chunk output; slot e:
             // column 16cb + 4(l/16) + e of the slice, token 16rb + l%16
             T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
-            const T* csw = sm.Cs[bf] + w * kChunk * Sm::pW;
-            const T* oiw = sm.Oi[bf] + w * kChunk * Sm::pW;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     const int t = 16 * rb + (l & 15), jc = 16 * cb + 4 * (l >> 4);
-                    const vec4_t<T> cs = *reinterpret_cast<const vec4_t<T>*>(csw + t * Sm::pW + jc);
-                    const vec4_t<T> oi = *reinterpret_cast<const vec4_t<T>*>(oiw + t * Sm::pW + jc);
                     f32x4 o4;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        o4[e] = acc[rb][cb][e] * Elem<T>::to_f(cs[e]) + Elem<T>::to_f(oi[e]);
+                        o4[e] = acc[rb][cb][e] * Elem<T>::to_f(csr[rb][cb][e]) + Elem<T>::to_f(oir[rb][cb][e]);
                     *reinterpret_cast<vec4_t<T>*>(obase + t * rsV + jc) = to_vec4<T>(o4);
                 }
         } else if constexpr (OUT) {

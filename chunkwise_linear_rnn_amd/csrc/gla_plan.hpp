@@ -123,16 +123,17 @@ inline size_t fwd_seg_bytes(const Shape& s, const Plan& p) {
     return state_bytes(s, p) + round256(gt);
 }
 
-// General gates (16-bit, K in {128, 256}): 64 value columns per
+// General gates (16-bit, K in {128, 256}): up to 128 value columns per
 // workgroup; records carry the key side and the value side of each chunk.
 inline Plan make_fwd_general_plan(const Shape& s) {
-    Plan p = make_plan(s, (int)(s.V / 64));
-    p.BV = 64;
+    const int bv = (int)(s.V < 128 ? s.V : 128);
+    Plan p = make_plan(s, (int)(s.V / bv));
+    p.BV = bv;
     p.NW = 4;
     return p;
 }
 constexpr size_t gen_record_bytes(int64_t K, int64_t V) {
-    return (size_t)(4 * 64 * K + 12 * K + 256 + 6 * 64 * V + 8 * V);
+    return wide_record_bytes(K) + (size_t)(6 * 64 * V + 8 * V);
 }
 // segment states, key-row and value-column gate totals (P > 1), then records
 inline size_t fwd_general_seg_bytes(const Shape& s, const Plan& p) {
