@@ -96,3 +96,14 @@ def test_fwd_general_deterministic():
     b = gla.gla_fwd_general(d["q"], d["k"], d["v"], d["g"], h, d["s0"])
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["gla_1p3b_long", "metric_8k"])
+def test_fwd_general_full_size_sampled_heads(name):
+    # the benchmark's shapes and launch configuration (bench.py --fwd-only
+    # --general-gate), h drawn as the bench draws it; two heads against the oracle
+    w = gi.WORKLOADS[name]
+    inp = gi.make_inputs(w)
+    inp.pop("do", None)
+    h = gi.make_value_gate(w.B, w.T, w.H, w.V, dtype=w.dtype, seed=w.seed + 1)
+    _check(w, inp, h, [(0, 0), (w.B - 1, w.H - 1)])
