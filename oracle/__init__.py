@@ -55,6 +55,8 @@ def _load():
     lib.oracle_gla_bwd.restype = ctypes.c_int
     lib.oracle_gla_fwd_general.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_gla_fwd_general.restype = ctypes.c_int
+    lib.oracle_gla_bwd_general.argtypes = [L, L, L, L, L] + [dp] * 14
+    lib.oracle_gla_bwd_general.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     D = ctypes.c_double
     lib.oracle_out_gate_fwd.argtypes = [L, L, dp, dp, dp, dp, D, dp]
@@ -233,3 +235,31 @@ def gla_bwd_scalar(q, k, v, g, d_o, s0=None, dht=None):
     K = _as_f64(q).shape[-1]
     dq, dk, dv, dg, ds0 = gla_bwd(q, k, v, np.repeat(g[..., None], K, axis=-1), d_o, s0, dht)
     return dq, dk, dv, dg.sum(axis=-1), ds0
+
+
+def gla_bwd_general(q, k, v, g, h, d_o, s0=None, dht=None):
+    """Reverse-mode gradient of gla_fwd_general (fp64) for the loss
+    <o, d_o> + <S_T, dht>: returns (dq, dk, dv, dg, dh, ds0), dg and dh with
+    respect to the log gates g (key side) and h (value side).  The chain rule
+    through S_t = (exp(g_t)^T exp(h_t)) * S_{t-1} + k_t^T v_t, token by token
+    ("Gated Linear Attention Transformers with Hardware-Efficient Training", the
+    chapter summary's Knowl 12 and Appendix C), with states replayed from
+    checkpoints.  Pinned by central finite differences, torch fp64 autograd of the
+    pages' parallel form, the h = 0 reduction to gla_bwd and the pages' closed forms
+    of the two gate gradients.
+    """
+    q, k, v, g, h, d_o = (_as_f64(x) for x in (q, k, v, g, h, d_o))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, T, H, K) and g.shape == (B, T, H, K)
+    assert v.shape == (B, T, H, V) and h.shape == (B, T, H, V) and d_o.shape == (B, T, H, V)
+    s0, dht = _as_f64(s0), _as_f64(dht)
+    dq = np.zeros_like(q); dk = np.zeros_like(k); dg = np.zeros_like(g)
+    dv = np.zeros_like(v); dh = np.zeros_like(h)
+    ds0 = np.zeros((B, H, K, V), dtype=np.float64)
+    rc = _load().oracle_gla_bwd_general(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h), _ptr(s0),
+                                        _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh),
+                                        _ptr(ds0))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_bwd_general failed with code %d" % rc)
+    return dq, dk, dv, dg, dh, ds0

@@ -166,6 +166,123 @@ int oracle_gla_fwd_general(long B, long T, long H, long K, long V,
     return err;
 }
 
+/* One token of the general recurrence in place: S <- (alpha^T beta) .* S + k^T v,
+ * with alpha = exp(g_t), beta = exp(h_t) already exponentiated in av, bv. */
+static void step_general(double *S, const double *kt, const double *av, const double *vt, const double *bv,
+                         long K, long V) {
+    for (long i = 0; i < K; ++i) {
+        double *row = S + i * V;
+        for (long j = 0; j < V; ++j) row[j] = (av[i] * bv[j]) * row[j] + kt[i] * vt[j];
+    }
+}
+
+/* Reverse-mode gradient of oracle_gla_fwd_general for the loss
+ * L = <o, d_o> + <S_T, dht> (same pages and notation).  With dS the running
+ * gradient with respect to the post-update state S_t and G_t = alpha_t^T beta_t,
+ * for t = T-1 .. 0:
+ *   dS += q_t^T do_t ;  dq_t = do_t S_t^T ;  dk_t = v_t dS^T ;  dv_t = k_t dS ;
+ *   dg_t[i] = sum_j dS[i,j] G_t[i,j] S_{t-1}[i,j] ,  dh_t[j] = sum_i (the same) ;
+ *   dS <- G_t .* dS            (now the gradient with respect to S_{t-1}),
+ * and ds0 is the last dS.  g and h are log gates, so d/dg of alpha = alpha.
+ * States come from checkpoints every ORACLE_CKPT tokens and a forward replay. */
+int oracle_gla_bwd_general(long B, long T, long H, long K, long V,
+                           const double *q, const double *k, const double *v, const double *g,
+                           const double *h, const double *s0, const double *d_o, const double *dht,
+                           double *dq, double *dk, double *dv, double *dg, double *dh, double *ds0) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return 1;
+    const long KV = K * V;
+    const long nseg = (T + ORACLE_CKPT - 1) / ORACLE_CKPT;
+    long nbh = B * H;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        long b = bh / H, hh = bh % H;
+        double *ckpt = (double *)malloc(sizeof(double) * (size_t)KV * (size_t)(nseg > 0 ? nseg : 1));
+        double *seg = (double *)malloc(sizeof(double) * (size_t)KV * (ORACLE_CKPT + 1));
+        double *dS = (double *)malloc(sizeof(double) * (size_t)KV);
+        double *kt = (double *)malloc(sizeof(double) * (size_t)K);
+        double *av = (double *)malloc(sizeof(double) * (size_t)K);
+        double *vt = (double *)malloc(sizeof(double) * (size_t)V);
+        double *bv = (double *)malloc(sizeof(double) * (size_t)V);
+        double *dhacc = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!ckpt || !seg || !dS || !kt || !av || !vt || !bv || !dhacc) {
+#pragma omp atomic write
+            err = 2;
+            free(ckpt); free(seg); free(dS); free(kt); free(av); free(vt); free(bv); free(dhacc);
+            continue;
+        }
+#define LOAD_TOKEN(t)                                                        \
+        do {                                                                 \
+            for (long i = 0; i < K; ++i) {                                   \
+                kt[i] = k[IDX_TOK(b, (t), hh, i, T, H, K)];                  \
+                av[i] = exp(g[IDX_TOK(b, (t), hh, i, T, H, K)]);             \
+            }                                                                \
+            for (long j = 0; j < V; ++j) {                                   \
+                vt[j] = v[IDX_TOK(b, (t), hh, j, T, H, V)];                  \
+                bv[j] = exp(h[IDX_TOK(b, (t), hh, j, T, H, V)]);             \
+            }                                                                \
+        } while (0)
+        double *S = seg;
+        for (long i = 0; i < K; ++i)
+            for (long j = 0; j < V; ++j) S[i * V + j] = s0 ? s0[IDX_ST(b, hh, i, j, H, K, V)] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            if (t % ORACLE_CKPT == 0) memcpy(ckpt + (t / ORACLE_CKPT) * KV, S, sizeof(double) * KV);
+            LOAD_TOKEN(t);
+            step_general(S, kt, av, vt, bv, K, V);
+        }
+        for (long i = 0; i < K; ++i)
+            for (long j = 0; j < V; ++j) dS[i * V + j] = dht ? dht[IDX_ST(b, hh, i, j, H, K, V)] : 0.0;
+        for (long m = nseg - 1; m >= 0; --m) {
+            long t0 = m * ORACLE_CKPT;
+            long t1 = t0 + ORACLE_CKPT < T ? t0 + ORACLE_CKPT : T;
+            memcpy(seg, ckpt + m * KV, sizeof(double) * KV);
+            for (long t = t0; t < t1; ++t) {
+                double *dst = seg + (t - t0 + 1) * KV;
+                memcpy(dst, seg + (t - t0) * KV, sizeof(double) * KV);
+                LOAD_TOKEN(t);
+                step_general(dst, kt, av, vt, bv, K, V);
+            }
+            for (long t = t1 - 1; t >= t0; --t) {
+                const double *St = seg + (t - t0 + 1) * KV;
+                const double *Sp = seg + (t - t0) * KV;
+                LOAD_TOKEN(t);
+                for (long i = 0; i < K; ++i) {
+                    const double qi = q[IDX_TOK(b, t, hh, i, T, H, K)];
+                    for (long j = 0; j < V; ++j) dS[i * V + j] += qi * d_o[IDX_TOK(b, t, hh, j, T, H, V)];
+                }
+                for (long j = 0; j < V; ++j) dhacc[j] = 0.0;
+                for (long i = 0; i < K; ++i) {
+                    double aq = 0.0, ak = 0.0, ag = 0.0;
+                    for (long j = 0; j < V; ++j) {
+                        const double decayed = (av[i] * bv[j]) * Sp[i * V + j];  /* G_t .* S_{t-1} */
+                        aq += d_o[IDX_TOK(b, t, hh, j, T, H, V)] * St[i * V + j];
+                        ak += dS[i * V + j] * vt[j];
+                        ag += dS[i * V + j] * decayed;
+                        dhacc[j] += dS[i * V + j] * decayed;
+                    }
+                    dq[IDX_TOK(b, t, hh, i, T, H, K)] = aq;
+                    dk[IDX_TOK(b, t, hh, i, T, H, K)] = ak;
+                    dg[IDX_TOK(b, t, hh, i, T, H, K)] = ag;
+                }
+                for (long j = 0; j < V; ++j) {
+                    double acc = 0.0;
+                    for (long i = 0; i < K; ++i) acc += kt[i] * dS[i * V + j];
+                    dv[IDX_TOK(b, t, hh, j, T, H, V)] = acc;
+                    dh[IDX_TOK(b, t, hh, j, T, H, V)] = dhacc[j];
+                }
+                for (long i = 0; i < K; ++i)
+                    for (long j = 0; j < V; ++j) dS[i * V + j] *= av[i] * bv[j];
+            }
+        }
+#undef LOAD_TOKEN
+        if (ds0)
+            for (long i = 0; i < K; ++i)
+                for (long j = 0; j < V; ++j) ds0[IDX_ST(b, hh, i, j, H, K, V)] = dS[i * V + j];
+        free(ckpt); free(seg); free(dS); free(kt); free(av); free(vt); free(bv); free(dhacc);
+    }
+    return err;
+}
+
 /* Backward of the same loop.  With S_t the post-update state and dS the
  * running gradient with respect to it, for t = T..1:
  *   dS      += q_t^T do_t                       (o_t = q_t S_t)
