@@ -47,6 +47,7 @@ class GlaError(RuntimeError):
 EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode", "gla_out_gate",
            "gla_out_gate_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_bwd_scalar_workspace_size",
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
+           "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
            "gla_kernel_timing", "gla_kernel_timing_read"]
 
@@ -76,6 +77,10 @@ def lib():
     L.gla_fwd_general.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gla_fwd_general.restype = ctypes.c_int
     L.gla_fwd_general_workspace_size.argtypes = [sh]
+    L.gla_bwd_general.argtypes = [sh] + [vp] * 15 + [ctypes.c_size_t, vp]
+    L.gla_bwd_general.restype = ctypes.c_int
+    L.gla_bwd_general_workspace_size.argtypes = [sh]
+    L.gla_bwd_general_workspace_size.restype = ctypes.c_size_t
     L.gla_fwd_general_workspace_size.restype = ctypes.c_size_t
     L.gla_bwd_scalar_workspace_size.restype = ctypes.c_size_t
     L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
@@ -271,6 +276,36 @@ def gla_fwd_general(q, k, v, g, h, s0=None, output_final_state=True, stream=None
     ws = workspace(gla_fwd_general_workspace_size(B, T, H, K, V, dt), dev)
     gla_fwd_general_into(q, k, v, g, h, s0, o, sf, ws, stream)
     return o, sf
+
+
+def gla_bwd_general_workspace_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_bwd_general_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
+
+
+def gla_bwd_general_into(q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, ws, stream=None):
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib().gla_bwd_general(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h), _ptr(s0),
+                                 _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh), _ptr(ds0),
+                                 _ptr(ws), nbytes, _stream(stream)))
+
+
+def gla_bwd_general(q, k, v, g, h, d_o, s0=None, dht=None, output_ds0=True, stream=None):
+    """dq, dk, dv, dg, dh, dS0 of <o, d_o> + <S_T, dht> for gla_fwd_general (bf16)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
+                         ("h", h, (B, T, H, V)), ("d_o", d_o, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    _need(dht, "dht", (B, H, K, V), torch.float32, dev)
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dg = torch.empty_like(g)
+    dv = torch.empty_like(v); dh = torch.empty_like(h)
+    ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
+    ws = workspace(gla_bwd_general_workspace_size(B, T, H, K, V, dt), dev)
+    gla_bwd_general_into(q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, ws, stream)
+    return dq, dk, dv, dg, dh, ds0
 
 
 def gla_decode_into(q, k, v, g, state, o, stream=None):

@@ -235,6 +235,48 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     return GLA_OK;
 }
 
+gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                              const void* g, const void* h, const float* s0, const void* d_o, const float* dht,
+                              void* dq, void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, true);
+    if (st != GLA_OK) return st;
+    if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
+    if ((s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256))
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {128, 256} (got K=%lld V=%lld)",
+                    (long long)s.K, (long long)s.V);
+    const bool empty = s.B * s.H == 0 || s.T == 0;
+    if (!empty && (!q || !k || !v || !g || !h || !d_o || !dq || !dk || !dv || !dg || !dh))
+        return fail(GLA_ERR_NULL, "q, k, v, g, h, d_o, dq, dk, dv, dg and dh are required");
+    const void* ptrs[] = {q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace};
+    const char* names[] = {"q", "k", "v", "g", "h", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "dh", "ds0",
+                           "workspace"};
+    for (int i = 0; i < 15; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t need = empty ? 0 : gla::bwd_general_layout(s).total;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (empty) {
+        err = ds0 ? gla::launch_state_copy(dht, ds0, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else {
+        gla::BwdGeneralLaunch a{};
+        a.B = (int)s.B; a.T = (int)s.T; a.H = (int)s.H; a.K = (int)s.K; a.V = (int)s.V;
+        a.q = q; a.k = k; a.v = v; a.g = g; a.h = h; a.d_o = d_o;
+        a.s0 = s0; a.dht = dht;
+        a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dh = dh; a.ds0 = ds0;
+        a.workspace = workspace;
+        a.stream = strm;
+        err = gla::launch_bwd_general(a);
+    }
+    if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GLA_OK;
+}
+
 gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
                       float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg) {
@@ -365,6 +407,21 @@ gla_status_t gla_fwd_general(const gla_shape_t* shape, const void* q, const void
                              const void* h, const float* s0, void* o, float* s_final, void* workspace,
                              size_t workspace_bytes, void* stream) {
     return fwd_general_impl(shape, q, k, v, g, h, s0, o, s_final, workspace, workspace_bytes, stream);
+}
+
+size_t gla_bwd_general_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, true) != GLA_OK || !s.bf16 || (s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256))
+        return 0;
+    return gla::bwd_general_layout(s).total;
+}
+
+gla_status_t gla_bwd_general(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                             const void* h, const float* s0, const void* d_o, const float* dht, void* dq, void* dk,
+                             void* dv, void* dg, void* dh, float* ds0, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return bwd_general_impl(shape, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, workspace_bytes,
+                            stream);
 }
 
 gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

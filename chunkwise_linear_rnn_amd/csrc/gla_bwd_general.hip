@@ -1,0 +1,230 @@
+// Backward of general gated linear attention (forget gate exp(g_t)^T exp(h_t);
+// "Gated Linear Attention Transformers with Hardware-Efficient Training", the
+// chapter summary's Knowl 12 and Appendix C), built from the general forward's
+// kernels on three related recurrences:
+//   dq_t = do_t S_t^T: the forward of the transposed state S^T, whose recurrence
+//        is the general one with (do, v, k) as (q, k, v) and the gates swapped;
+//   dS, the gradient with respect to S_t, runs backwards in time:
+//        dS_t = q_t^T do_t + (alpha_{t+1}^T beta_{t+1}) * dS_{t+1},  dS_{T-1} also + dht,
+//        a general recurrence over the reversed sequence with keys q, values do
+//        and the gates shifted by one token; dv_t = k_t dS_t is its output for
+//        queries k, and its final state gives dS_0 = (alpha_0^T beta_0) * dS_0';
+//   dk_t = v_t dS_t^T: the same reversed recurrence for dS^T, queries v.
+// The gate gradients take the closed forms (GLA paper Section 4.3 and the
+// appendix general form), reverse cumulative sums of q*dq - k*dk and
+// o*do - v*dv, within each chunk only: every chunk starts from an exact anchor
+// at its end boundary (below), so rounding does not build up over the sequence.
+// Everything runs in the kernels below and those of gla_fwd_wide.hip, on the
+// caller's stream, with every intermediate in the caller's workspace.
+#include "gla_device.hpp"
+#include "gla_launch.hpp"
+#include "gla_plan.hpp"
+#include "gla_timing.hpp"
+
+namespace gla {
+
+// out[b][t] = in[b][T-1-t] (shift = 0) or in[b][T-t] with a zero row at t = 0
+// (shift = 1), rows of W elements (W a multiple of 8), one 16-byte vector per thread.
+__global__ void __launch_bounds__(256)
+gla_flip_rows(const bf16* __restrict__ in, bf16* __restrict__ out, int T, int W, int shift) {
+    const long nvec = (long)W / 8;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)T * nvec) return;
+    const long b = blockIdx.y;
+    const int t = (int)(e / nvec);
+    const long vi = e % nvec;
+    const int src = shift ? T - t : T - 1 - t;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (src < T) x = *reinterpret_cast<const u32x4*>(in + (b * T + src) * (long)W + vi * 8);
+    *reinterpret_cast<u32x4*>(out + (b * T + t) * (long)W + vi * 8) = x;
+}
+
+// dst[bh][j][i] = src[bh][i][j] for [BH][K][V] fp32 states
+__global__ void __launch_bounds__(256)
+gla_transpose_state(const float* __restrict__ src, float* __restrict__ dst, int K, int V, long n) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const long KV = (long)K * V;
+    const long bh = e / KV, r = e % KV;
+    const int i = (int)(r / V), j = (int)(r % V);
+    dst[bh * KV + (long)j * K + i] = src[e];
+}
+
+// ds0[bh][i][j] *= exp(g[b,0,h,i] + h[b,0,h,j]): the gradient one gate further back
+__global__ void __launch_bounds__(256)
+gla_scale_ds0(float* __restrict__ ds0, const bf16* __restrict__ g, const bf16* __restrict__ hg, int T, int H, int K,
+              int V, long n) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const long KV = (long)K * V;
+    const long bh = e / KV, r = e % KV;
+    const int i = (int)(r / V), j = (int)(r % V);
+    const long b = bh / H, h = bh % H;
+    const float gi = Elem<bf16>::to_f(g[(b * T * H + h) * K + i]);
+    const float hj = Elem<bf16>::to_f(hg[(b * T * H + h) * V + j]);
+    ds0[e] *= __expf(gi + hj);
+}
+
+// Gate-gradient anchors at the chunk boundaries.  With dg_t the key-side gate
+// gradient, dg_t = q_t*dq_t - k_t*dk_t + dg_{t+1} and, at a boundary 64m,
+//   dg_{64m}[i] = sum_j (G_{64m} .* dS_{64m})[i,j] S_{64m-1}[i,j] ,
+// (dh the same summed over i), with G_{64m} = alpha^T beta of token 64m; at
+// m = N the term is sum_j dht S_T (no gate).  S_{64m-1} is the forward walk's
+// state before chunk m (hsf), dS_{64m} the reversed walk's state before its
+// chunk N - m (hsr).  One thread per (head, boundary, row or column).
+__global__ void __launch_bounds__(256)
+gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, const float* __restrict__ st,
+                const float* __restrict__ dht, const bf16* __restrict__ g, const bf16* __restrict__ hg,
+                float* __restrict__ ag, float* __restrict__ ah, int T, int H, int K, int V) {
+    const int N = T / 64;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long per_bh = (long)N * (K + V);
+    if (e >= (long)gridDim.y * per_bh) return;
+    const long bh = blockIdx.y;
+    if (e >= per_bh) return;
+    const int m = (int)(e / (K + V)) + 1, r = (int)(e % (K + V));
+    const bool row = r < K;
+    const int x = row ? r : r - K;
+    const long b = bh / H, h = bh % H, KV = (long)K * V;
+    float acc = 0.f;
+    if (m == N) {
+        if (dht) {
+            const float* S = st + bh * KV;
+            const float* D = dht + bh * KV;
+            if (row) { for (int j = 0; j < V; ++j) acc += D[(long)x * V + j] * S[(long)x * V + j]; }
+            else { for (int i = 0; i < K; ++i) acc += D[(long)i * V + x] * S[(long)i * V + x]; }
+        }
+    } else {
+        const bf16* S = hsf + (bh * N + m) * KV;
+        const bf16* D = hsr + (bh * N + (N - m)) * KV;
+        const long tok = (b * T + 64L * m) * H + h;
+        if (row) {
+            const float a = __expf(Elem<bf16>::to_f(g[tok * K + x]));
+            for (int j = 0; j < V; ++j)
+                acc += __expf(Elem<bf16>::to_f(hg[tok * V + j])) * Elem<bf16>::to_f(D[(long)x * V + j]) *
+                       Elem<bf16>::to_f(S[(long)x * V + j]);
+            acc *= a;
+        } else {
+            const float bt = __expf(Elem<bf16>::to_f(hg[tok * V + x]));
+            for (int i = 0; i < K; ++i)
+                acc += __expf(Elem<bf16>::to_f(g[tok * K + i])) * Elem<bf16>::to_f(D[(long)i * V + x]) *
+                       Elem<bf16>::to_f(S[(long)i * V + x]);
+            acc *= bt;
+        }
+    }
+    if (row) ag[(bh * (N + 1) + m) * K + x] = acc;
+    else ah[(bh * (N + 1) + m) * V + x] = acc;
+}
+
+// out_t = the anchor of the chunk's end boundary + the chunk's own reverse
+// cumulative sum of a*da - c*dc (tensors [B,T,H,D]); one thread per column.
+__global__ void __launch_bounds__(64)
+gla_gate_grad_out(const bf16* __restrict__ a, const bf16* __restrict__ da, const bf16* __restrict__ c,
+                  const bf16* __restrict__ dc, const float* __restrict__ anchor, bf16* __restrict__ out, int T, int H,
+                  int D) {
+    const int n = blockIdx.x, col = blockIdx.y * 64 + threadIdx.x;
+    const long bh = blockIdx.z, b = bh / H, h = bh % H, N = T / 64;
+    float acc = anchor[(bh * (N + 1) + n + 1) * D + col];
+    const long base = ((b * T + (long)n * 64) * H + h) * D + col, rs = (long)H * D;
+    for (int t = 63; t >= 0; --t) {
+        const long o = base + t * rs;
+        acc += Elem<bf16>::to_f(a[o]) * Elem<bf16>::to_f(da[o]) - Elem<bf16>::to_f(c[o]) * Elem<bf16>::to_f(dc[o]);
+        out[o] = Elem<bf16>::from_f(acc);
+    }
+}
+
+static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void* q, const void* k, const void* v,
+                                  const void* g, const void* h, const float* s0, void* o, float* s_final, char* ws,
+                                  void* hs, hipStream_t stream) {
+    Shape s{B, T, H, K, V, true};
+    Plan p = make_fwd_general_plan(s);
+    FwdLaunch a{};
+    a.bf16 = true;
+    a.K = K; a.V = V; a.BV = p.BV;
+    a.T = T; a.H = H; a.N = (int)p.N; a.P = p.P; a.seg_len = p.seg_len; a.BH = p.BH;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.h = h; a.s0 = s0; a.o = o; a.s_final = s_final;
+    if (p.P > 1) {
+        const size_t sb = state_bytes(s, p);
+        a.ws_state = ws;
+        a.ws_gate = reinterpret_cast<float*>(ws + sb);
+        a.ws_gateb = reinterpret_cast<float*>(ws + sb + round256((size_t)p.BH * p.P * K * sizeof(float)));
+    }
+    a.ws_rec = ws + fwd_general_seg_bytes(s, p);
+    a.ws_hs = hs;
+    a.stream = stream;
+    return a;
+}
+
+hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
+    const int B = L.B, T = L.T, H = L.H, K = L.K, V = L.V;
+    const long BH = (long)B * H, KV = (long)K * V;
+    const BwdGeneralLayout w = bwd_general_layout(Shape{B, T, H, K, V, true});
+    char* ws = static_cast<char*>(L.workspace);
+    bf16* o = reinterpret_cast<bf16*>(ws + w.o);
+    float* st = reinterpret_cast<float*>(ws + w.st);
+    float* s0T = L.s0 ? reinterpret_cast<float*>(ws + w.s0t) : nullptr;
+    float* dhtT = L.dht ? reinterpret_cast<float*>(ws + w.dhtt) : nullptr;
+    bf16* qr = reinterpret_cast<bf16*>(ws + w.qr);
+    bf16* kr = reinterpret_cast<bf16*>(ws + w.kr);
+    bf16* vr = reinterpret_cast<bf16*>(ws + w.vr);
+    bf16* dor = reinterpret_cast<bf16*>(ws + w.dor);
+    bf16* gs = reinterpret_cast<bf16*>(ws + w.gs);
+    bf16* hs = reinterpret_cast<bf16*>(ws + w.hs);
+    bf16* dvr = reinterpret_cast<bf16*>(ws + w.dvr);
+    bf16* dkr = reinterpret_cast<bf16*>(ws + w.dkr);
+    bf16* hsf = reinterpret_cast<bf16*>(ws + w.hsf);
+    bf16* hsr = reinterpret_cast<bf16*>(ws + w.hsr);
+    float* ag = reinterpret_cast<float*>(ws + w.ag);
+    float* ah = reinterpret_cast<float*>(ws + w.ah);
+    char* fws = ws + w.fws;
+    hipStream_t sm = L.stream;
+    hipError_t err;
+    const long nst = BH * KV;
+    const unsigned gst = (unsigned)((nst + 255) / 256);
+    // forward (o, S_T) and the transposed initial / final-state gradient
+    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, o, st, fws, hsf, sm));
+    if (err != hipSuccess) return err;
+    if (L.s0) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.s0, s0T, K, V, nst);
+    if (L.dht) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.dht, dhtT, K, V, nst);
+    // dq: the transposed state's forward
+    err = launch_fwd_general(general_fwd_args(B, T, H, V, K, L.d_o, L.v, L.k, L.h, L.g, s0T, L.dq, nullptr, fws, nullptr, sm));
+    if (err != hipSuccess) return err;
+    // reversed inputs, gates shifted by one token
+    auto flip = [&](const void* in, bf16* out, int W, int shift) {
+        const long nvec = (long)T * H * W / 8;
+        GLA_LAUNCH("bwdg_flip", gla_flip_rows, dim3((unsigned)((nvec + 255) / 256), (unsigned)B), dim3(256), sm,
+                   (const bf16*)in, out, T, H * W, shift);
+    };
+    flip(L.q, qr, K, 0);
+    flip(L.k, kr, K, 0);
+    flip(L.v, vr, V, 0);
+    flip(L.d_o, dor, V, 0);
+    flip(L.g, gs, K, 1);
+    flip(L.h, hs, V, 1);
+    // dv (reversed) and dS_0' from the reversed recurrence of dS
+    float* ds0 = L.ds0;
+    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, kr, qr, dor, gs, hs, L.dht, dvr, ds0, fws, hsr, sm));
+    if (err != hipSuccess) return err;
+    if (ds0) GLA_LAUNCH("bwdg_scale_ds0", gla_scale_ds0, dim3(gst), dim3(256), sm, ds0, (const bf16*)L.g,
+                        (const bf16*)L.h, T, H, K, V, nst);
+    // dk (reversed) from the reversed recurrence of dS^T
+    err = launch_fwd_general(general_fwd_args(B, T, H, V, K, vr, dor, qr, hs, gs, dhtT, dkr, nullptr, fws, nullptr, sm));
+    if (err != hipSuccess) return err;
+    flip(dvr, static_cast<bf16*>(L.dv), V, 0);
+    flip(dkr, static_cast<bf16*>(L.dk), K, 0);
+    // gate gradients: anchors at the chunk boundaries, then each chunk's reverse sums
+    const unsigned N = (unsigned)(T / 64);
+    const long per_bh = (long)N * (K + V);
+    GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor, dim3((unsigned)((per_bh + 255) / 256), (unsigned)BH), dim3(256),
+               sm, (const bf16*)hsf, (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h,
+               ag, ah, T, H, K, V);
+    GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out, dim3(N, (unsigned)(K / 64), (unsigned)BH), dim3(64), sm,
+               (const bf16*)L.q, (const bf16*)L.dq, (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag,
+               static_cast<bf16*>(L.dg), T, H, K);
+    GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out, dim3(N, (unsigned)(V / 64), (unsigned)BH), dim3(64), sm,
+               (const bf16*)o, (const bf16*)L.d_o, (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah,
+               static_cast<bf16*>(L.dh), T, H, V);
+    return hipGetLastError();
+}
+
+}  // namespace gla

@@ -116,7 +116,7 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
     GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true>),
                dim3((unsigned)xcd_grid(a.P * a.BH, nvb)), dim3(512), a.stream, (const unsigned char*)rec,
                (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H,
-               a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr);
+               a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr, (T*)a.ws_hs);
     return hipGetLastError();
 }
 

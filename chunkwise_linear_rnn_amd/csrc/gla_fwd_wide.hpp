@@ -406,13 +406,15 @@ struct WideSmem {
 // GenRec): the value slices come from the records (v * exp2(C_63 - C_t)), the
 // output is (Ql S) * exp2(C_t) plus the record's intra-chunk output, and the
 // state's columns decay by exp2(C_63) as its rows do by the key-side gate; the
-// state pass also writes the segment's column log2 decays to ws_gateb.
+// state pass also writes the segment's column log2 decays to ws_gateb, and the
+// output walk, given hs_out, the state before every chunk.
 template <typename T, int KD, int BV, bool OUT, bool GEN = false>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
                   T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
-                  int seg_len, int nseg, int BH, float* __restrict__ ws_gateb = nullptr) {
+                  int seg_len, int nseg, int BH, float* __restrict__ ws_gateb = nullptr,
+                  T* __restrict__ hs_out = nullptr) {
     constexpr int NC = 4, NP = 64 * NC;  // consumer waves; producer threads
     using Sm = WideSmem<T, KD, BV, OUT, GEN>;
     using R = WideRec<KD>;
@@ -532,6 +534,10 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     for (int c = c_begin; c < c_end; ++c) {
         const int bf = c & 1;
         const T* Vw = sm.Vw[bf] + w * kChunk * Sm::pW;
+        // general mode, on request: the state before each chunk, [BH][N][KD][V]
+        if constexpr (OUT && GEN) {
+            if (hs_out) S.store(hs_out + ((long)bh * N + c) * KD * V, V, col0);
+        }
         vec4_t<T> vf[4][CB];
         f32x4 acc[4][CB];
         // general gates: this lane's exp2(C_t) and intra-chunk output values,

@@ -22,6 +22,7 @@ struct FwdLaunch {
     void* ws_rec;     // [BH][N] chunk records of the wide-head forward
     const void* h;    // general gates: log beta, [B,T,H,V] (null otherwise)
     float* ws_gateb;  // general gates: [BH][P][V] fp32 (log2 of the segment's column decay)
+    void* ws_hs;      // general gates, optional: the state before every chunk, [BH][N][K][V] bf16
     hipStream_t stream;
 };
 
@@ -61,7 +62,19 @@ struct DecodeLaunch {
 
 hipError_t launch_fwd(const FwdLaunch& a);
 hipError_t launch_fwd_wide(const FwdLaunch& a);
-hipError_t launch_fwd_general(const FwdLaunch& a);  // 16-bit, K = 256
+hipError_t launch_fwd_general(const FwdLaunch& a);
+
+// general-gate backward (bf16): inputs, outputs and the caller's workspace
+struct BwdGeneralLaunch {
+    int B, T, H, K, V;
+    const void *q, *k, *v, *g, *h, *d_o;
+    const float *s0, *dht;
+    void *dq, *dk, *dv, *dg, *dh;
+    float* ds0;
+    void* workspace;
+    hipStream_t stream;
+};
+hipError_t launch_bwd_general(const BwdGeneralLaunch& a);  // 16-bit, K = 256
 hipError_t launch_decode(const DecodeLaunch& a);
 hipError_t launch_bwd(const BwdLaunch& a);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream);

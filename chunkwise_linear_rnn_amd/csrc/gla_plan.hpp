@@ -147,6 +147,45 @@ inline size_t fwd_general_workspace_bytes(const Shape& s) {
     return fwd_general_seg_bytes(s, p) + (size_t)p.BH * p.N * gen_record_bytes(s.K, s.V);
 }
 
+// Backward under general gates: the forward's o and S_T, transposed S_0 and
+// dht, reversed copies of q, k, v, do and the shifted gates, the reversed dv
+// and dk, the chunk-start states of the forward and of the reversed dS
+// recurrence with the gate-gradient anchors formed from them, and the forward workspace of the largest of
+// the four general forwards it runs (shapes K x V and V x K).
+struct BwdGeneralLayout {
+    size_t o, st, s0t, dhtt, qr, kr, vr, dor, gs, hs, dvr, dkr, hsf, hsr, ag, ah, fws, total;
+};
+inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
+    BwdGeneralLayout w{};
+    const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H), KV = (size_t)(s.K * s.V);
+    const size_t tk = round256(BTH * s.K * 2), tv = round256(BTH * s.V * 2), sf = round256(BH * KV * 4);
+    Shape st = s;
+    st.K = s.V;
+    st.V = s.K;
+    const size_t f1 = fwd_general_workspace_bytes(s), f2 = fwd_general_workspace_bytes(st);
+    size_t at = 0;
+    w.o = at; at += tv;
+    w.st = at; at += sf;
+    w.s0t = at; at += sf;
+    w.dhtt = at; at += sf;
+    w.qr = at; at += tk;
+    w.kr = at; at += tk;
+    w.vr = at; at += tv;
+    w.dor = at; at += tv;
+    w.gs = at; at += tk;
+    w.hs = at; at += tv;
+    w.dvr = at; at += tv;
+    w.dkr = at; at += tk;
+    const size_t N = (size_t)(s.T / 64);
+    w.hsf = at; at += round256(BH * N * KV * 2);
+    w.hsr = at; at += round256(BH * N * KV * 2);
+    w.ag = at; at += round256(BH * (N + 1) * (size_t)s.K * 4);
+    w.ah = at; at += round256(BH * (N + 1) * (size_t)s.V * 4);
+    w.fws = at; at += round256(f1 > f2 ? f1 : f2);
+    w.total = at;
+    return w;
+}
+
 inline size_t fwd_workspace_bytes(const Shape& s) {
     Plan p = make_fwd_plan(s);
     if (p.BH == 0) return 0;

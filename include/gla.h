@@ -184,6 +184,35 @@ gla_status_t gla_fwd_general(const gla_shape_t* shape,
 size_t gla_fwd_general_workspace_size(const gla_shape_t* shape);
 
 /*
+ * gla_bwd_general -- gradients of L = <o, d_o> + <S_T, dht> for gla_fwd_general
+ * with respect to q, k, v, both log gates g and h, and S_0.  States are
+ * recomputed.  dq is the output of the transposed state's recurrence
+ * (S_t^T = (beta_t^T alpha_t) .* S_{t-1}^T + v_t^T k_t, queried by do); dv and dk
+ * are the outputs of the gradient dS_t and of dS_t^T, which follow the general
+ * recurrence backwards in time with the gates one token later; the gate
+ * gradients take the closed forms of Section 4.3 and the appendix general form,
+ * dg_t = sum_{s>=t} (q_s*dq_s - k_s*dk_s) + sum_j S_T[i,j] dht[i,j] and
+ * dh_t = sum_{s>=t} (o_s*do_s - v_s*dv_s) + sum_i S_T[i,j] dht[i,j].
+ *   q, k, g, v, h, s0 : as for gla_fwd_general;  d_o, dht : as for gla_bwd
+ *   dq, dk, dg : [B,T,H,K] bf16;  dv, dh : [B,T,H,V] bf16;  ds0 : [B,H,K,V] fp32 or NULL
+ *   workspace : at least gla_bwd_general_workspace_size(shape) bytes
+ * bf16 with K and V in {128, 256}; other shapes and fp32 return
+ * GLA_ERR_UNSUPPORTED.  Results are deterministic.
+ */
+gla_status_t gla_bwd_general(const gla_shape_t* shape,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const void* h, const float* s0, const void* d_o, const float* dht,
+                             void* dq, void* dk, void* dv, void* dg, void* dh, float* ds0,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace gla_bwd_general needs (0 for an unsupported or
+ * invalid shape; no HIP call): the forward's o and S_T, time-reversed copies of
+ * q, k, v, do and the gates, the reversed dv and dk, per-chunk gate sums and
+ * the general forward's workspace (about 16 (K + V) bytes per token and head
+ * plus the records). */
+size_t gla_bwd_general_workspace_size(const gla_shape_t* shape);
+
+/*
  * gla_decode -- the recurrent form of Eq. 3 (Section 3.1), for token-by-token
  * inference with the state carried between calls: for t = 1..T,
  *     S <- Diag(exp g_t) S + k_t^T v_t ,   o_t = q_t S ,

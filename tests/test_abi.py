@@ -196,3 +196,23 @@ def test_general_gate_entry_point_validates(L):
     assert fwd(_shape(T=128, K=128), h=ctypes.c_void_p(0x10002)) == ERR_ALIGN
     assert fwd(_shape(T=128, K=128), ws=None) == ERR_WORKSPACE
     assert fwd(_shape(T=0, K=128)) == OK
+
+
+def test_general_gate_backward_validates(L):
+    ws = lambda shape: L.gla_bwd_general_workspace_size(ctypes.byref(shape))
+    assert ws(_shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)) == 0
+    assert ws(_shape(T=128, K=64, V=128)) == 0
+    assert ws(_shape(T=128, K=128, V=512)) == 0
+    s = _shape(B=2, H=4, T=8192, K=128, V=256)
+    # at least the reversed copies of q, k, v, do and both gates
+    assert ws(s) == ws(s) and ws(s) >= 2 * 8192 * 4 * 2 * (3 * 128 + 3 * 256)
+    bwd = lambda shape, **kw: L.gla_bwd_general(ctypes.byref(shape), P, P, P, P, kw.get("h", P), None, P, None,
+                                                P, P, P, P, kw.get("dh", P), None, kw.get("ws", P), 1 << 40, None)
+    assert bwd(_shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert bwd(_shape(T=128, K=256, V=64)) == ERR_UNSUPPORTED
+    assert bwd(_shape(T=100, K=128, V=128)) == ERR_SHAPE
+    assert bwd(_shape(T=128, K=128, V=128), h=None) == ERR_NULL
+    assert bwd(_shape(T=128, K=128, V=128), dh=None) == ERR_NULL
+    assert bwd(_shape(T=128, K=128, V=128), h=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert bwd(_shape(T=128, K=128, V=128), ws=None) == ERR_WORKSPACE
+    assert bwd(_shape(T=0, K=128, V=128)) == OK

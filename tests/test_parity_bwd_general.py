@@ -1,0 +1,80 @@
+"""GPU backward parity of general gated linear attention against the fp64
+oracle's chain rule: dq, dk, dv, both gate gradients and dS0, on one chunk,
+several segments, both key and value widths, gates past the basis range, and
+the benchmark's full size (sampled heads)."""
+import pytest
+import torch
+
+import chunkwise_linear_rnn_amd as gla
+import gla_inputs as gi
+import oracle
+from tests.parity_util import TOL, gpu_heads, head_subset, note, rel_l2, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _check(w, inp, h, heads):
+    note("general bwd parity: B=%d H=%d T=%d K=%d V=%d s0=%s" % (w.B, w.H, w.T, w.K, w.V, w.s0))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    hd = h.to(DEV)
+    dq, dk, dv, dg, dh, ds0 = gla.gla_bwd_general(d["q"], d["k"], d["v"], d["g"], hd, d["do"], d["s0"], d["dht"])
+    torch.cuda.synchronize()
+    sel = lambda a: head_subset(to_np(a), heads)
+    sst = lambda a: head_subset(to_np(a), heads, state=True) if a is not None else None
+    ref = oracle.gla_bwd_general(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["g"]), sel(h), sel(inp["do"]),
+                                 sst(inp["s0"]), sst(inp["dht"]))
+    tol = TOL[torch.bfloat16]
+    errs = {}
+    for name, got, r in zip(("dq", "dk", "dv", "dg", "dh"), (dq, dk, dv, dg, dh), ref[:5]):
+        errs[name] = rel_l2(gpu_heads(got, heads), r[:, :, 0, :])
+    errs["ds0"] = rel_l2(gpu_heads(ds0, heads, state=True), ref[5][:, 0])
+    note("  rel-L2 " + " ".join("%s=%.2e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
+    assert all(e <= tol for e in errs.values()), errs
+
+
+def _heads(B, H):
+    return [(b, hh) for b in range(B) for hh in range(H)] if B * H <= 2 else [(0, 0), (B - 1, H - 1)]
+
+
+@pytest.mark.parametrize("B,H,T,K,V,s0", [
+    (1, 1, 64, 128, 128, "normal0.1"),      # one chunk
+    (2, 2, 64 * 9, 128, 256, "normal0.1"),  # one chunk per segment
+    (2, 4, 64 * 13, 256, 128, "none"),      # K > V
+    (1, 2, 64 * 20, 256, 256, "normal0.1"),
+])
+def test_bwd_general_heads(B, H, T, K, V, s0):
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0=s0, backward=True, seed=1500 + T + K + V)
+    inp = gi.make_inputs(w, dht=True)
+    h = gi.make_value_gate(B, T, H, V, seed=1600 + T + V)
+    _check(w, inp, h, _heads(B, H))
+
+
+def test_bwd_general_exact_paths_and_no_dht():
+    B, H, T, K, V = 2, 2, 64 * 6, 128, 128
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=1701)
+    inp = gi.make_inputs(w)
+    g = inp["g"].float()
+    g[0, 70, 0, :5] = -60.0
+    inp["g"] = g.to(torch.bfloat16)
+    h = gi.make_value_gate(B, T, H, V, seed=1702).float()
+    h[1, 200, 1, :] = -70.0
+    h[0, 300:310, 1, 64:] = -9.0
+    _check(w, inp, h.to(torch.bfloat16), [(0, 0), (1, 1), (0, 1)])
+
+
+def test_bwd_general_full_size_sampled_heads():
+    w = gi.WORKLOADS["metric_8k"]
+    inp = gi.make_inputs(w, dht=True)
+    h = gi.make_value_gate(w.B, w.T, w.H, w.V, dtype=w.dtype, seed=w.seed + 1)
+    _check(w, inp, h, [(0, 0), (w.B - 1, w.H - 1)])
+
+
+def test_bwd_general_deterministic():
+    w = gi.custom(2, 4, 64 * 11, 128, 256, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=1710)
+    d = gi.make_inputs(w, device=DEV, dht=True)
+    h = gi.make_value_gate(2, 64 * 11, 4, 256, seed=1711).to(DEV)
+    a = gla.gla_bwd_general(d["q"], d["k"], d["v"], d["g"], h, d["do"], d["s0"], d["dht"])
+    b = gla.gla_bwd_general(d["q"], d["k"], d["v"], d["g"], h, d["do"], d["s0"], d["dht"])
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
