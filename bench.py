@@ -347,6 +347,56 @@ def fwd_only_bench(args, torch, gla, gi):
     print(json.dumps(line), flush=True)
 
 
+def general_step_bench(args, torch, gla, gi):
+    """gla_fwd_general + gla_bwd_general (alpha^T beta gates) per step on
+    --workload (K and V in {128, 256}), h drawn like g; tokens/s and per-kernel
+    times.  A measurement of that operator, not the headline metric."""
+    w = gi.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
+    dt = w.torch_dtype
+    cpu = gi.make_inputs(w, dht=True)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in cpu.items()}
+    hv = gi.make_value_gate(B, T, H, V, dtype=w.dtype, seed=w.seed + 1).to(dev)
+    do = d.get("do")
+    if do is None:
+        do = torch.randn(B, T, H, V, generator=torch.Generator().manual_seed(w.seed + 2)).to(dt).to(dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
+    grads = [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]), torch.empty_like(d["g"]),
+             torch.empty_like(hv), torch.empty(B, H, K, V, dtype=torch.float32, device=dev)]
+    wsf = gla.workspace(gla.gla_fwd_general_workspace_size(B, T, H, K, V, dt), dev)
+    wsb = gla.workspace(gla.gla_bwd_general_workspace_size(B, T, H, K, V, dt), dev)
+
+    def step():
+        gla.gla_fwd_general_into(d["q"], d["k"], d["v"], d["g"], hv, d["s0"], o, sf, wsf)
+        gla.gla_bwd_general_into(d["q"], d["k"], d["v"], d["g"], hv, d["s0"], do, d["dht"], *grads, wsb)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n = max(args.steps, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    gla.gla_kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = gla.gla_kernel_timing_read()
+    gla.gla_kernel_timing(False)
+    line = {"metric": "General GLA fwd+bwd tokens/sec (%s)" % w.name, "value": B * T / (ms * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": n, "ms_per_step": ms, "higher_is_better": True,
+            "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, gla_fwd_general + gla_bwd_general per step" % (
+                w.name, B, H, T, K, V, w.dtype)},
+            "kernels": {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -360,7 +410,8 @@ def main():
     ap.add_argument("--fwd-only", action="store_true",
                     help="time gla_fwd alone on --workload (also those without backward inputs)")
     ap.add_argument("--general-gate", action="store_true",
-                    help="with --fwd-only: time gla_fwd_general (alpha^T beta gates, h drawn like g)")
+                    help="time gla_fwd_general + gla_bwd_general on --workload (alpha^T beta gates, h drawn "
+                         "like g); with --fwd-only the forward alone")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="the workload with one log gate per token and head (gla_fwd_scalar / gla_bwd_scalar)")
     ap.add_argument("--out-gate", action="store_true",
@@ -396,6 +447,9 @@ def main():
         return
     if args.out_gate:
         out_gate_bench(args, torch, gla, gi)
+        return
+    if args.general_gate and not args.fwd_only:
+        general_step_bench(args, torch, gla, gi)
         return
     if args.fwd_only:
         fwd_only_bench(args, torch, gla, gi)

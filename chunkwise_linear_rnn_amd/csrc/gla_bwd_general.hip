@@ -71,49 +71,76 @@ gla_scale_ds0(float* __restrict__ ds0, const bf16* __restrict__ g, const bf16* _
 // (dh the same summed over i), with G_{64m} = alpha^T beta of token 64m; at
 // m = N the term is sum_j dht S_T (no gate).  S_{64m-1} is the forward walk's
 // state before chunk m (hsf), dS_{64m} the reversed walk's state before its
-// chunk N - m (hsr).  One thread per (head, boundary, row or column).
+// chunk N - m (hsr).
+// One workgroup per (head, boundary m = 1..N): W[i][j] = alpha_i beta_j
+// dS[i][j] S[i][j] over the K x V tile read as 16-byte vectors; thread
+// (row group rg, column vector cv) takes rows rg, rg + RG, ... of columns
+// 8cv .. 8cv+7.  Row sums reduce across the V/8 lanes of a row by shuffles,
+// column sums across the row groups through LDS.
+template <int V>
 __global__ void __launch_bounds__(256)
 gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, const float* __restrict__ st,
                 const float* __restrict__ dht, const bf16* __restrict__ g, const bf16* __restrict__ hg,
-                float* __restrict__ ag, float* __restrict__ ah, int T, int H, int K, int V) {
+                float* __restrict__ ag, float* __restrict__ ah, int T, int H, int K) {
+    constexpr int CVN = V / 8, RG = 256 / CVN;
+    static_assert(CVN <= 64 && (CVN & (CVN - 1)) == 0, "a row's lanes sit in one wave");
+    __shared__ float alpha[256];
+    __shared__ float beta[V];
+    __shared__ float colp[RG][V];
     const int N = T / 64;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    const long per_bh = (long)N * (K + V);
-    if (e >= (long)gridDim.y * per_bh) return;
-    const long bh = blockIdx.y;
-    if (e >= per_bh) return;
-    const int m = (int)(e / (K + V)) + 1, r = (int)(e % (K + V));
-    const bool row = r < K;
-    const int x = row ? r : r - K;
-    const long b = bh / H, h = bh % H, KV = (long)K * V;
-    float acc = 0.f;
-    if (m == N) {
-        if (dht) {
-            const float* S = st + bh * KV;
-            const float* D = dht + bh * KV;
-            if (row) { for (int j = 0; j < V; ++j) acc += D[(long)x * V + j] * S[(long)x * V + j]; }
-            else { for (int i = 0; i < K; ++i) acc += D[(long)i * V + x] * S[(long)i * V + x]; }
-        }
-    } else {
-        const bf16* S = hsf + (bh * N + m) * KV;
-        const bf16* D = hsr + (bh * N + (N - m)) * KV;
-        const long tok = (b * T + 64L * m) * H + h;
-        if (row) {
-            const float a = __expf(Elem<bf16>::to_f(g[tok * K + x]));
-            for (int j = 0; j < V; ++j)
-                acc += __expf(Elem<bf16>::to_f(hg[tok * V + j])) * Elem<bf16>::to_f(D[(long)x * V + j]) *
-                       Elem<bf16>::to_f(S[(long)x * V + j]);
-            acc *= a;
+    const int m = blockIdx.x + 1;
+    const long bh = blockIdx.y, b = bh / H, h = bh % H, KV = (long)K * V;
+    const int tid = threadIdx.x, cv = tid % CVN, rg = tid / CVN;
+    const bool last = m == N;  // S_T and dht, no gate
+    const long tok = last ? 0 : (b * T + 64L * m) * H + h;
+    for (int i = tid; i < K; i += 256) alpha[i] = last ? 1.f : __expf(Elem<bf16>::to_f(g[tok * K + i]));
+    for (int j = tid; j < V; j += 256) beta[j] = last ? 1.f : __expf(Elem<bf16>::to_f(hg[tok * V + j]));
+    __syncthreads();
+    float cs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+    const bf16* S16 = hsf + (bh * N + (last ? 0 : m)) * KV;
+    const bf16* D16 = hsr + (bh * N + (last ? 0 : N - m)) * KV;
+    const float* S32 = st + bh * KV;
+    const float* D32 = dht ? dht + bh * KV : nullptr;
+    for (int i = rg; i < K; i += RG) {
+        float p[8];
+        const long off = (long)i * V + 8 * cv;
+        if (!last) {
+            const u32x4 sv = *reinterpret_cast<const u32x4*>(S16 + off);
+            const u32x4 dv = *reinterpret_cast<const u32x4*>(D16 + off);
+            const bf16* sx = reinterpret_cast<const bf16*>(&sv);
+            const bf16* dx = reinterpret_cast<const bf16*>(&dv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = Elem<bf16>::to_f(sx[e]) * Elem<bf16>::to_f(dx[e]);
+        } else if (D32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = S32[off + e] * D32[off + e];
         } else {
-            const float bt = __expf(Elem<bf16>::to_f(hg[tok * V + x]));
-            for (int i = 0; i < K; ++i)
-                acc += __expf(Elem<bf16>::to_f(g[tok * K + i])) * Elem<bf16>::to_f(D[(long)i * V + x]) *
-                       Elem<bf16>::to_f(S[(long)i * V + x]);
-            acc *= bt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = 0.f;
         }
+        const float a = alpha[i];
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float wv = a * beta[8 * cv + e] * p[e];
+            rs += wv;
+            cs[e] += wv;
+        }
+#pragma unroll
+        for (int o = CVN / 2; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, CVN);
+        if (cv == 0) ag[(bh * (N + 1) + m) * K + i] = rs;
     }
-    if (row) ag[(bh * (N + 1) + m) * K + x] = acc;
-    else ah[(bh * (N + 1) + m) * V + x] = acc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) colp[rg][8 * cv + e] = cs[e];
+    __syncthreads();
+    for (int j = tid; j < V; j += 256) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) acc += colp[r][j];
+        ah[(bh * (N + 1) + m) * V + j] = acc;
+    }
 }
 
 // out_t = the anchor of the chunk's end boundary + the chunk's own reverse
@@ -214,10 +241,15 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     flip(dkr, static_cast<bf16*>(L.dk), K, 0);
     // gate gradients: anchors at the chunk boundaries, then each chunk's reverse sums
     const unsigned N = (unsigned)(T / 64);
-    const long per_bh = (long)N * (K + V);
-    GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor, dim3((unsigned)((per_bh + 255) / 256), (unsigned)BH), dim3(256),
-               sm, (const bf16*)hsf, (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h,
-               ag, ah, T, H, K, V);
+    {
+        const dim3 ga(N, (unsigned)BH);
+        if (V == 128)
+            GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor<128>, ga, dim3(256), sm, (const bf16*)hsf,
+                       (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K);
+        else
+            GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor<256>, ga, dim3(256), sm, (const bf16*)hsf,
+                       (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K);
+    }
     GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out, dim3(N, (unsigned)(K / 64), (unsigned)BH), dim3(64), sm,
                (const bf16*)L.q, (const bf16*)L.dq, (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag,
                static_cast<bf16*>(L.dg), T, H, K);
