@@ -297,6 +297,11 @@ def fwd_only_bench(args, torch, gla, gi):
     inputs), reported as tokens/s, % of bf16 MFMA peak (algorithmic flops at
     C = 64) and % of HBM peak (compulsory bytes e(3K+2V) per token-head)."""
     w = gi.WORKLOADS[args.workload]
+    if args.dims:
+        # another head shape with the workload's recipe: "B,H,T,K,V"
+        B_, H_, T_, K_, V_ = (int(x) for x in args.dims.split(","))
+        w = gi.Workload("%s@%s" % (w.name, args.dims), B_, H_, T_, K_, V_, w.dtype, w.gate, w.v_scale, w.s0,
+                        w.backward, w.seed)
     dev = "cuda:0"
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     dt = w.torch_dtype
@@ -409,6 +414,8 @@ def main():
                     help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time gla_fwd alone on --workload (also those without backward inputs)")
+    ap.add_argument("--dims", default="",
+                    help="with --fwd-only: B,H,T,K,V instead of the workload's head shape (same input recipe)")
     ap.add_argument("--general-gate", action="store_true",
                     help="time gla_fwd_general + gla_bwd_general on --workload (alpha^T beta gates, h drawn "
                          "like g); with --fwd-only the forward alone")
