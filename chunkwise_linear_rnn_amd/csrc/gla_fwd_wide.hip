@@ -113,10 +113,17 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
                    dim3(256), a.stream, a.s0, (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD,
                    a.V, a.P);
     }
-    GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true>),
-               dim3((unsigned)xcd_grid(a.P * a.BH, nvb)), dim3(512), a.stream, (const unsigned char*)rec,
-               (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H,
-               a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr, (T*)a.ws_hs);
+    const dim3 gw((unsigned)xcd_grid(a.P * a.BH, nvb));
+    if (a.ws_hs)
+        GLA_LAUNCH("fwd_general_walk_hs", (gla_fwd_wide_walk<T, KD, BV, true, true, true>), gw, dim3(512), a.stream,
+                   (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final,
+                   (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr,
+                   (T*)a.ws_hs);
+    else
+        GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true>), gw, dim3(512), a.stream,
+                   (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final,
+                   (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr,
+                   (T*)nullptr);
     return hipGetLastError();
 }
 

@@ -407,8 +407,8 @@ struct WideSmem {
 // output is (Ql S) * exp2(C_t) plus the record's intra-chunk output, and the
 // state's columns decay by exp2(C_63) as its rows do by the key-side gate; the
 // state pass also writes the segment's column log2 decays to ws_gateb, and the
-// output walk, given hs_out, the state before every chunk.
-template <typename T, int KD, int BV, bool OUT, bool GEN = false>
+// output walk with HS the state before every chunk to hs_out.
+template <typename T, int KD, int BV, bool OUT, bool GEN = false, bool HS = false>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
@@ -530,14 +530,15 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     if (OUT && seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
     else if (OUT && s0) S.load(s0 + (long)bh * KD * V, V, col0);
     else S.zero();
+    // HS (general mode): the state before every chunk to hs_out, [BH][N][KD][V];
+    // each is written after the previous chunk's update, when little else is live
+    if constexpr (OUT && GEN && HS) {
+        if (c_begin < c_end) S.store(hs_out + ((long)bh * N + c_begin) * KD * V, V, col0);
+    }
     __syncthreads();  // E of the prologue
     for (int c = c_begin; c < c_end; ++c) {
         const int bf = c & 1;
         const T* Vw = sm.Vw[bf] + w * kChunk * Sm::pW;
-        // general mode, on request: the state before each chunk, [BH][N][KD][V]
-        if constexpr (OUT && GEN) {
-            if (hs_out) S.store(hs_out + ((long)bh * N + c) * KD * V, V, col0);
-        }
         vec4_t<T> vf[4][CB];
         f32x4 acc[4][CB];
         // general gates: this lane's exp2(C_t) and intra-chunk output values,
@@ -692,6 +693,9 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             const f32x4 f = *reinterpret_cast<const f32x4*>(post + 16 * a + 4 * (l >> 4));
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= f;
+        }
+        if constexpr (OUT && GEN && HS) {
+            if (c + 1 < c_end) S.store(hs_out + ((long)bh * N + c + 1) * KD * V, V, col0);
         }
         __syncthreads();  // E: buffer bf may be refilled
     }
