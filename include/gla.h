@@ -169,7 +169,8 @@ size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
  *   s0, o, s_final, stream : as for gla_fwd
  *   workspace : at least gla_fwd_general_workspace_size(shape) bytes
  * bf16 with K in {128, 256} and V in {64, 128, 256, 512}; other shapes and
- * fp32 return GLA_ERR_UNSUPPORTED.  Results are deterministic.  Forward only.
+ * fp32 return GLA_ERR_UNSUPPORTED.  Results are deterministic.  The backward is
+ * gla_bwd_general.
  */
 gla_status_t gla_fwd_general(const gla_shape_t* shape,
                              const void* q, const void* k, const void* v, const void* g,
