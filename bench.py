@@ -8,8 +8,13 @@ cumsum, intra-chunk attention, state scan, output, state recompute, dS scan,
 chunk gradients, gate gradient) over one batch of seeded synthetic inputs that
 are resident in HBM before timing starts.  Prints one JSON line.
 
+Timing: the headline is cold, the median of the K timed steps with every step
+behind a read of a 512 MiB buffer (so the inputs do not sit in L2 or the
+Infinity Cache); p10/p90 and the warm mean of K back-to-back steps are beside
+it.  The box's attainable copy bandwidth and bf16 GEMM rate are measured too.
+
 Roofline: the dominant kernel (largest share of step time, timed with HIP
-events on the launch stream through the library's kernel-timing interface) is
+events on the launch stream through the library's launch recorder) is
 compared with the HBM peak using its algorithmic bytes (each input it needs read
 once, each output written once; workspace traffic excluded).  The CPU baseline
 is the fp64 oracle on a bounded sample of the same workload.
@@ -113,7 +118,7 @@ def plan_dv_split(B, H, T, K, V, bf16):
 
 
 # sources of the forward and backward step kernels (the recorded traffic is theirs)
-STEP_SOURCES = ["gla_bwd.hip", "gla_chunk.hpp", "gla_device.hpp", "gla_fwd.hip", "gla_launch.hpp", "gla_plan.hpp"]
+STEP_SOURCES = ["gla_bwd.hip", "gla_chunk.hpp", "gla_device.hpp", "gla_fwd.hip", "gla_plan.hpp"]
 
 
 def source_digest() -> str:
@@ -142,6 +147,210 @@ def load_traffic(workload: str, kernel: str, units: int):
     return k.get("bytes_per_launch")
 
 
+# Kernel function (as rocprofv3 names it) -> the launch name the library's
+# launch recorder reports for it (the keys of the bench line's "kernels").
+LAUNCH_LABEL = {
+    "gla_fwd_walk_pipe": "fwd_walk", "gla_fwd_walk": "fwd_walk", "gla_seg_state": "fwd_seg_state",
+    "gla_seg_combine_fwd_split": "combine_fwd", "gla_seg_combine_fwd": "combine_fwd",
+    "gla_seg_state_pair": "bwd_seg_states", "gla_seg_combine_bwd_split": "combine_bwd",
+    "gla_seg_combine_bwd": "combine_bwd", "gla_bwd_dq_pipe": "bwd_dq_walk", "gla_bwd_dq": "bwd_dq_walk",
+    "gla_bwd_dk_pipe": "bwd_dk_walk", "gla_bwd_dk": "bwd_dk_walk", "gla_bwd_dv_pipe": "bwd_dv_walk",
+    "gla_bwd_dv": "bwd_dv_walk", "gla_fwd_wide_prep": "fwd_prep", "gla_fwd_wide_walk": "fwd_walk",
+}
+
+
+def _kernel_base(mangled: str) -> str:
+    """The kernel's function name inside namespace gla, e.g. gla_bwd_dq_pipe."""
+    import re
+    m = re.search(r"3gla(\d+)", mangled)
+    if m:
+        n = int(m.group(1))
+        return mangled[m.end():m.end() + n]
+    m = re.search(r"(gla_[a-z0-9_]+)", mangled)
+    return m.group(1) if m else mangled
+
+
+def _demangle(names):
+    import subprocess
+    try:
+        # GNU c++filt does not know the bfloat16 code DF16b: spell it as a vendor type
+        fixed = [n.replace("DF16b", "u4bf16") for n in names]
+        r = subprocess.run(["c++filt"], input="\n".join(fixed), capture_output=True, text=True, timeout=30)
+        out = r.stdout.splitlines()
+        if len(out) == len(names):
+            return [x.replace("__hip_bfloat16", "bf16").replace("(anonymous namespace)::", "") for x in out]
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return list(names)
+
+
+def _short(demangled: str) -> str:
+    """'void gla::f<a, b>(args)' -> 'f<a,b>'."""
+    s = demangled
+    if s.startswith("void "):
+        s = s[5:]
+    s = s.split("(")[0].replace("gla::", "").replace(" ", "")
+    return s
+
+
+def summarize_trace(csv_path, out_md, title, command):
+    """Markdown table from a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    names = _demangle([r["Name"] for r in rows])
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["# Kernel times: %s (MI355X, rocprofv3 kernel trace)" % title, "",
+             "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "",
+             "    " + command, "", "Source: `%s` (every dispatch of the run)." % os.path.basename(csv_path), "",
+             "| kernel | launch name | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    for r, n in sorted(zip(rows, names), key=lambda x: -float(x[0]["TotalDurationNs"])):
+        base = _kernel_base(r["Name"])
+        lines.append("| %s | %s | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
+            _short(n), LAUNCH_LABEL.get(base, "-"), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def _counter_rows(csv_path):
+    """{(dispatch, kernel name): {counter: value}} from a counter_collection.csv."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        d = out.setdefault(key, {"_scratch": int(r["Scratch_Size"]), "_ns": int(r["End_Timestamp"]) -
+                                 int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _per_kernel_means(rows):
+    acc = {}
+    for (_, name), d in rows.items():
+        a = acc.setdefault(name, {"_n": 0})
+        a["_n"] += 1
+        for k, v in d.items():
+            a[k] = a.get(k, 0.0) + v
+    return {name: {k: (v / a["_n"] if k != "_n" else v) for k, v in a.items()} for name, a in acc.items()}
+
+
+def summarize_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, workload, commands, out_json, out_md,
+                      alg_mb=None):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch),
+    each scaled by what the same counter reads for a 1 GiB device copy."""
+    copy_kib = 1 << 20
+    cf = [d for (_, n), d in _counter_rows(cfetch_csv).items() if "copyBuffer" in n]
+    cw = [d for (_, n), d in _counter_rows(cwrite_csv).items() if "copyBuffer" in n]
+    fscale = copy_kib / max(d["FETCH_SIZE"] for d in cf)
+    wscale = copy_kib / max(d["WRITE_SIZE"] for d in cw)
+    fm = _per_kernel_means(_counter_rows(fetch_csv))
+    wm = _per_kernel_means(_counter_rows(write_csv))
+    kernels = {}
+    for name in fm:
+        if name not in wm:
+            continue
+        base = _kernel_base(name)
+        label = LAUNCH_LABEL.get(base, base)
+        f, w = fm[name]["FETCH_SIZE"] * fscale, wm[name]["WRITE_SIZE"] * wscale
+        kernels[label] = {"kernel": name, "bytes_per_launch": (f + w) * 1024.0, "fetch_kib": f, "write_kib": w,
+                          "dispatches": fm[name]["_n"]}
+    rec = {"workload": workload, "source_digest": source_digest(), "fetch_scale": fscale, "write_scale": wscale,
+           "kernels": kernels, "commands": commands}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    lines = ["# HBM traffic per launch: %s (MI355X, rocprofv3 FETCH_SIZE / WRITE_SIZE)" % workload, "",
+             "Each counter in its own run (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "Calibration: a 1 GiB device copy reads and writes 1048576 KiB; FETCH_SIZE is scaled x%.4f and "
+              "WRITE_SIZE x%.4f to match." % (fscale, wscale),
+              "Per-launch bytes = mean over dispatches of (FETCH_SIZE x fetch scale + WRITE_SIZE x write scale)"
+              " x 1024.", "",
+              "| kernel | fetch MB | write MB | HBM MB per launch | algorithmic MB | ratio |", "|---|---|---|---|---|---|"]
+    total = 0.0
+    for label, k in sorted(kernels.items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
+        alg = (alg_mb or {}).get(label)
+        total += k["bytes_per_launch"]
+        lines.append("| %s | %.1f | %.1f | %.1f | %s | %s |" % (
+            label, k["fetch_kib"] * 1024 / 1e6, k["write_kib"] * 1024 / 1e6, k["bytes_per_launch"] / 1e6,
+            "%.1f" % alg if alg else "-", "%.2f" % (k["bytes_per_launch"] / 1e6 / alg) if alg else "-"))
+    lines += ["", "Sum over the kernels listed: %.1f MB." % (total / 1e6),
+              "`%s` holds the same figures with the digest of the kernel sources they were taken from; bench.py "
+              "reports them only while those sources are unchanged." % os.path.basename(out_json)]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(csv_path, trace_csv, out_md, title, command):
+    """Per-kernel MFMA and LDS counters (means per dispatch) beside the
+    kernel-trace durations: MfmaUtil = busy MFMA cycles over (GPU active cycles x
+    1024 SIMDs); bf16 flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
+    import csv
+    means = _per_kernel_means(_counter_rows(csv_path))
+    dur = {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(trace_csv))}
+    names = list(means)
+    dem = dict(zip(names, _demangle(names)))
+    lines = ["# MFMA and LDS counters: %s (MI355X, rocprofv3 --pmc)" % title, "",
+             "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "", "    " + command, "",
+             "Durations from the kernel trace of the same workload (`%s`)." % os.path.basename(trace_csv),
+             "MfmaUtil is rocprofv3's derived metric (MFMA busy cycles summed over the SIMDs / (GPU active cycles x "
+             "1024 SIMDs) x 100).  MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / trace duration; "
+             "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel | launch name | MfmaUtil % | bf16 MFMA TFLOP/s | % of 2516.6 | MFMA insts | VALU insts | "
+             "LDS insts | LDS conflict | scratch B/lane |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for n in sorted(names, key=lambda x: -dur.get(x, 0.0)):
+        m = means[n]
+        ns = dur.get(n)
+        fl = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        tf = fl / (ns * 1e-9) / 1e12 if ns else float("nan")
+        conf = m.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(1.0, m.get("SQ_LDS_IDX_ACTIVE", 0.0))
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.3g | %.3g | %.3g | %.2f | %d |" % (
+            _short(dem[n]), LAUNCH_LABEL.get(_kernel_base(n), "-"), m.get("MfmaUtil", float("nan")), tf,
+            100 * tf / BF16_MFMA_PEAK_TFLOPS, m.get("SQ_INSTS_MFMA", 0.0), m.get("SQ_INSTS_VALU", 0.0),
+            m.get("SQ_INSTS_LDS", 0.0), conf, m["_scratch"]))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def attainable_peaks(torch, dev):
+    """What this GPU reaches on plain library work, for scale: a 1 GiB
+    device-to-device copy (read + write bytes per second) and an 8192^3 bf16
+    matrix product (hipBLASLt through torch.matmul), each the best of 5 runs
+    after one warm-up run, timed with HIP events."""
+    def best(fn, reps=5):
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        torch.cuda.synchronize()
+        for a, b in e:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return min(a.elapsed_time(b) for a, b in e)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms_copy = best(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    ms_mm = best(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    return {"copy_GBps": 2 * n / (ms_copy * 1e-3) / 1e9, "copy_frac_of_peak": 2 * n / (ms_copy * 1e-3) / 1e9 /
+            HBM_PEAK_GBS, "gemm_bf16_TFLOPs": 2 * m ** 3 / (ms_mm * 1e-3) / 1e12,
+            "gemm_frac_of_peak": 2 * m ** 3 / (ms_mm * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "what": "1 GiB device copy; 8192^3 bf16 torch.matmul; best of 5"}
+
+
 def cpu_baseline(inputs, w, n_heads, scalar_gate=False):
     """fp64 oracle forward + backward on n_heads full-length heads of the workload."""
     import numpy as np
@@ -167,6 +376,8 @@ def cpu_baseline(inputs, w, n_heads, scalar_gate=False):
         "value": tokens_equiv / dt,
         "unit": "tokens/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": "fp64 oracle fwd+bwd on %d of %d heads, full T=%d (%.1f s wall)" % (len(heads), w.B * w.H,
                                                                                   w.T, dt),
@@ -189,8 +400,6 @@ def decode_bench(args, torch, gla, gi):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    gla.gla_kernel_timing(True)
-    gla.gla_kernel_timing_read()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = max(args.steps, 1) * 10
     e0.record()
@@ -199,8 +408,11 @@ def decode_bench(args, torch, gla, gi):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    kt = gla.gla_kernel_timing_read()
-    gla.gla_kernel_timing(False)
+    timer = gla.KernelTimer(n)
+    with timer:
+        for _ in range(n):
+            call()
+    kt = timer.read()
     kern_ms = kt["decode"][1] / kt["decode"][0]
     alg = B * H * (8 * K * V + 2 * (3 * K + 2 * V))
     achieved = alg / (kern_ms * 1e-3) / 1e9
@@ -254,13 +466,11 @@ def out_gate_bench(args, torch, gla, gi):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    gla.gla_kernel_timing(True)
-    gla.gla_kernel_timing_read()
-    for _ in range(n):
-        step()
-    torch.cuda.synchronize()
-    kt = gla.gla_kernel_timing_read()
-    gla.gla_kernel_timing(False)
+    timer = gla.KernelTimer(3 * n)
+    with timer:
+        for _ in range(n):
+            step()
+    kt = timer.read()
     kern = {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}
     alg_f, alg_b = 2 * V * R * 3, 2 * V * R * 5
     bwd_us = kern["out_gate_bwd"]["avg_us"]
@@ -330,12 +540,11 @@ def fwd_only_bench(args, torch, gla, gi):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    gla.gla_kernel_timing(True)
-    for _ in range(args.steps):
-        fwd()
-    torch.cuda.synchronize()
-    kt = gla.gla_kernel_timing_read()
-    gla.gla_kernel_timing(False)
+    timer = gla.KernelTimer(16 * args.steps)
+    with timer:
+        for _ in range(args.steps):
+            fwd()
+    kt = timer.read()
     units = B * T * H
     peak_tf = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     flops = fwd_flops_per_token_head(K, V) * units
@@ -387,12 +596,11 @@ def general_step_bench(args, torch, gla, gi):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    gla.gla_kernel_timing(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kt = gla.gla_kernel_timing_read()
-    gla.gla_kernel_timing(False)
+    timer = gla.KernelTimer(64 * args.steps)
+    with timer:
+        for _ in range(args.steps):
+            step()
+    kt = timer.read()
     line = {"metric": "General GLA fwd+bwd tokens/sec (%s)" % w.name, "value": B * T / (ms * 1e-3),
             "unit": "tokens/s", "n_gpus": 1, "steps": n, "ms_per_step": ms, "higher_is_better": True,
             "dtype": w.dtype, "data": "synthetic",
@@ -409,6 +617,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="metric_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip measuring the box's attainable copy bandwidth and bf16 GEMM rate")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--decode", action="store_true",
                     help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
@@ -424,9 +634,41 @@ def main():
     ap.add_argument("--out-gate", action="store_true",
                     help="measure the output epilogue (LayerNorm + Swish gate, fwd + bwd) on the metric "
                          "workload's output rows instead")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_STATS_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of a rocprofv3 kernel trace (no GPU needed)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                              "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json/.md from FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("COUNTER_CSV", "KERNEL_STATS_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of MFMA / LDS counters")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", action="append", default=[],
+                    help="the command(s) that produced the input files, quoted in the summary")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (to calibrate rocprofv3 byte counters)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.title or args.workload,
+                        " && ".join(args.command))
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2],
+                      args.title or args.workload, " && ".join(args.command))
+        return
+    if args.summarize_traffic:
+        w = __import__("gla_inputs").WORKLOADS[args.workload]
+        e = 2 if w.dtype == "bf16" else 4
+        P = plan_segments(w.B, w.H, w.T, w.K, w.V, e == 2)
+        Pb = plan_segments_bwd(w.B, w.H, w.T, w.K, w.V, e == 2)
+        split = plan_dv_split(w.B, w.H, w.T, w.K, w.V, e == 2)
+        alg = {}
+        for k in ("fwd_walk", "bwd_dq_walk", "bwd_dk_walk", "bwd_dv_walk", "fwd_seg_state", "bwd_seg_states"):
+            b = alg_bytes_per_token_head(k, w.K, w.V, e, P, Pb, split)
+            if b:
+                alg[k] = b * w.B * w.T * w.H / 1e6
+        base = os.path.join(ROOT, "profiles", "traffic_%s" % args.workload)
+        summarize_traffic(*args.summarize_traffic, args.workload, args.command, base + ".json", base + ".md", alg)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the path is sharded across GPUs by heads and by sequence "
@@ -497,6 +739,7 @@ def main():
         bwd()
 
     def timed(fn, n):
+        # warm: n back-to-back calls, inputs left in the caches by the previous call
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -506,30 +749,48 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # cold: before every timed call a 512 MiB buffer is read, which evicts the
+    # inputs from L2 and from the 256 MB Infinity Cache (a read leaves no dirty
+    # lines to be written back during the timed call).  The read is enqueued
+    # ahead of the call's start event, so the call's launches are queued while
+    # it runs and the interval holds no host launch gap.
+    scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+
+    def cold_times(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            scrub.sum()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    def pct(xs, p):
+        return xs[min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))]
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed region: exactly K steps (each behind a cache scrub)
     wall0 = time.perf_counter()
-    ms_step = timed(step, args.steps)
+    cold = cold_times(step, args.steps)
     wall = time.perf_counter() - wall0
-    ms_fwd = timed(fwd, args.steps)
-    ms_bwd = timed(bwd, args.steps)
-    # cold-cache variant: overwrite a 512 MiB buffer between steps (not part of value)
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(min(args.steps, 10)):
-        scrub.fill_(1)
-        torch.cuda.synchronize()
-        cold.append(timed(step, 1))
+    ms_step = pct(cold, 50)
+    ms_warm = timed(step, args.steps)
+    cold_fwd = cold_times(fwd, args.steps)
+    cold_bwd = cold_times(bwd, args.steps)
+    ms_fwd, ms_bwd = pct(cold_fwd, 50), pct(cold_bwd, 50)
+    ms_fwd_warm, ms_bwd_warm = timed(fwd, args.steps), timed(bwd, args.steps)
     del scrub
 
-    # per-kernel HIP-event timing over another K steps
-    gla.gla_kernel_timing(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kt = gla.gla_kernel_timing_read()
-    gla.gla_kernel_timing(False)
+    # per-kernel HIP-event timing over another K steps (each kernel bracketed on
+    # its launch stream by the library's launch recorder)
+    timer = gla.KernelTimer(32 * args.steps)
+    with timer:
+        for _ in range(args.steps):
+            step()
+    kt = timer.read()
     kern = {n: {"launches": c, "avg_us": 1e3 * ms / c, "share": ms / max(1e-9, sum(x[1] for x in kt.values()))}
             for n, (c, ms) in kt.items()}
     dom = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches"])
@@ -557,6 +818,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "timing": "cold: median over the K timed steps, each behind a 512 MiB cache scrub; warm: mean of K "
+                  "back-to-back steps",
+        "ms_per_step_p10": pct(cold, 10),
+        "ms_per_step_p90": pct(cold, 90),
+        "ms_per_step_warm": ms_warm,
+        "warm_tokens_per_s": tokens / (ms_warm * 1e-3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -570,15 +837,22 @@ def main():
         "bwd_tokens_per_s": tokens / (ms_bwd * 1e-3),
         "ms_fwd": ms_fwd,
         "ms_bwd": ms_bwd,
-        "ms_per_step_cold": sorted(cold)[len(cold) // 2] if cold else None,
+        "ms_fwd_p10_p90": [pct(cold_fwd, 10), pct(cold_fwd, 90)],
+        "ms_bwd_p10_p90": [pct(cold_bwd, 10), pct(cold_bwd, 90)],
+        "ms_fwd_warm": ms_fwd_warm,
+        "ms_bwd_warm": ms_bwd_warm,
         "fwd_mfma_frac": fwd_flops / (ms_fwd * 1e-3) / (peak_tf * 1e12),
         "fwdbwd_mfma_frac": (fwd_flops + bwd_flops_per_token_head(K, V) * units) / (ms_step * 1e-3) /
                             (peak_tf * 1e12),
         "fwd_hbm_frac": e * (2 * K + (1 if sg else K) + 2 * V) * units / (ms_fwd * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "step_hbm_frac": e * (2 * K + (1 if sg else K) + 2 * V + 2 * K + (1 if sg else K) + 2 * V +
+                              2 * K + (1 if sg else K) + V) * units / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "kernels": kern,
         "roofline": roofline,
         "wall_s_timed": wall,
     }
+    if not args.no_attainable:
+        out["attainable"] = attainable_peaks(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_inputs, w, args.cpu_heads, scalar_gate=sg)
     print(json.dumps(out), flush=True)

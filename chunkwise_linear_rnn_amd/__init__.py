@@ -38,6 +38,13 @@ class GlaShape(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class LaunchRecorder(ctypes.Structure):
+    """gla_launch_recorder_t: caller-owned events the library records around its launches."""
+    _fields_ = [("capacity", ctypes.c_int32), ("count", ctypes.c_int32), ("failed", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("start", ctypes.POINTER(ctypes.c_void_p)),
+                ("stop", ctypes.POINTER(ctypes.c_void_p)), ("name", ctypes.POINTER(ctypes.c_char_p))]
+
+
 class GlaError(RuntimeError):
     def __init__(self, status: int, detail: str, message: str):
         super().__init__("%s (%s)" % (message, detail) if detail else message)
@@ -49,7 +56,7 @@ EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
-           "gla_kernel_timing", "gla_kernel_timing_read"]
+           "gla_set_launch_recorder"]
 
 _lib = None
 
@@ -101,10 +108,8 @@ def lib():
     L.gla_last_error_detail.argtypes = []
     L.gla_last_error_detail.restype = ctypes.c_char_p
     L.gla_abi_version.restype = ctypes.c_int
-    L.gla_kernel_timing.argtypes = [ctypes.c_int]
-    L.gla_kernel_timing.restype = ctypes.c_int
-    L.gla_kernel_timing_read.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
-    L.gla_kernel_timing_read.restype = ctypes.c_int
+    L.gla_set_launch_recorder.argtypes = [ctypes.POINTER(LaunchRecorder)]
+    L.gla_set_launch_recorder.restype = None
     _lib = L
     return L
 
@@ -140,6 +145,8 @@ def gla_bwd_workspace_size(B, T, H, K, V, dtype) -> int:
 
 
 def _dims(q, v):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B,T,H,D] (got %d and %d dims)" % (q.dim(), v.dim()))
     B, T, H, K = q.shape
     return B, T, H, K, v.shape[-1]
 
@@ -222,7 +229,8 @@ def gla_fwd_scalar(q, k, v, g, s0=None, output_final_state=True, stream=None):
     """gla_fwd with a scalar gate g [B,T,H] per token and head (bf16)."""
     B, T, H, K, V = _dims(q, v)
     dev, dt = q.device, q.dtype
-    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H)), ("v", v, (B, T, H, V))):
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),
+                         ("v", v, (B, T, H, V))):
         _need(t, name, shp, dt, dev)
     _need(s0, "s0", (B, H, K, V), torch.float32, dev)
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
@@ -267,8 +275,8 @@ def gla_fwd_general(q, k, v, g, h, s0=None, output_final_state=True, stream=None
     q, k, g: [B,T,H,K]; v, h: [B,T,H,V] (bf16); s0: [B,H,K,V] fp32 or None."""
     B, T, H, K, V = _dims(q, v)
     dev, dt = q.device, q.dtype
-    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
-                         ("h", h, (B, T, H, V))):
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("h", h, (B, T, H, V))):
         _need(t, name, shp, dt, dev)
     _need(s0, "s0", (B, H, K, V), torch.float32, dev)
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
@@ -295,8 +303,8 @@ def gla_bwd_general(q, k, v, g, h, d_o, s0=None, dht=None, output_ds0=True, stre
     """dq, dk, dv, dg, dh, dS0 of <o, d_o> + <S_T, dht> for gla_fwd_general (bf16)."""
     B, T, H, K, V = _dims(q, v)
     dev, dt = q.device, q.dtype
-    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
-                         ("h", h, (B, T, H, V)), ("d_o", d_o, (B, T, H, V))):
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("h", h, (B, T, H, V)), ("d_o", d_o, (B, T, H, V))):
         _need(t, name, shp, dt, dev)
     _need(s0, "s0", (B, H, K, V), torch.float32, dev)
     _need(dht, "dht", (B, H, K, V), torch.float32, dev)
@@ -387,19 +395,44 @@ def gla_out_gate_bwd(o, z, ln_w, ln_b, eps, dy, stream=None):
     return d_o, dz, dln_w, dln_b
 
 
-def gla_kernel_timing(enable: bool) -> None:
-    """Turn per-kernel HIP-event timing of library launches on or off."""
-    lib().gla_kernel_timing(1 if enable else 0)
+class KernelTimer:
+    """Per-kernel HIP-event times of the library launches this thread makes
+    inside ``with timer:`` (gla_set_launch_recorder).  The events are torch
+    events with timing enabled, owned here; ``read()`` waits for them and
+    returns {kernel: (launches, total_ms)}."""
 
+    def __init__(self, capacity: int = 4096):
+        self.capacity = capacity
+        self.ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        self.ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for e in self.ev0 + self.ev1:
+            e.record()  # creates the underlying hipEvent_t
+        torch.cuda.synchronize()
+        self._start = (ctypes.c_void_p * capacity)(*[e.cuda_event for e in self.ev0])
+        self._stop = (ctypes.c_void_p * capacity)(*[e.cuda_event for e in self.ev1])
+        self._name = (ctypes.c_char_p * capacity)()
+        self.rec = LaunchRecorder(capacity, 0, 0, 0, self._start, self._stop, self._name)
 
-def gla_kernel_timing_read() -> dict:
-    """{kernel: (launches, total_ms)} recorded since the previous read."""
-    buf = ctypes.create_string_buffer(1 << 16)
-    n = lib().gla_kernel_timing_read(buf, len(buf))
-    if n < 0:
-        raise RuntimeError("gla_kernel_timing_read: HIP event query failed")
-    out = {}
-    for line in buf.value.decode().splitlines():
-        name, cnt, ms = line.split()
-        out[name] = (int(cnt), float(ms))
-    return out
+    def __enter__(self):
+        self.rec.count = 0
+        self.rec.failed = 0
+        lib().gla_set_launch_recorder(ctypes.byref(self.rec))
+        return self
+
+    def __exit__(self, *exc):
+        lib().gla_set_launch_recorder(None)
+        return False
+
+    def read(self) -> dict:
+        torch.cuda.synchronize()
+        if self.rec.failed:
+            raise RuntimeError("gla launch recorder: hipEventRecord failed")
+        if self.rec.count > self.capacity:
+            raise RuntimeError("gla launch recorder: %d launches for %d event pairs" % (self.rec.count,
+                                                                                     self.capacity))
+        out = {}
+        for i in range(self.rec.count):
+            name = self._name[i].decode()
+            c, t = out.get(name, (0, 0.0))
+            out[name] = (c + 1, t + self.ev0[i].elapsed_time(self.ev1[i]))
+        return out

@@ -1,5 +1,6 @@
-// RAII bracket for kernel launches: when kernel timing is enabled it records a
-// HIP event on `stream` before the launch and another after it.
+// RAII bracket for kernel launches: while the calling thread has a launch
+// recorder set it records one of the caller's HIP events on `stream` before the
+// launch and another after it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,7 +17,7 @@ public:
 private:
     const char* name_;
     hipStream_t stream_;
-    hipEvent_t start_;
+    int slot_;
 };
 
 }  // namespace gla

@@ -8,8 +8,8 @@
  *     S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t ,     o_t = q_t S_t ,
  *
  * with the forget gate passed in log space, g_t = log(alpha_t) <= 0, and the
- * initial state S_0 either zero or a caller-supplied state (Section 2.2: "zero
- * or from the previous segment's hidden state").  The library computes it in
+ * initial state S_0 either zero or a caller-supplied state carried over from an
+ * earlier segment of the sequence (Section 2.2).  The library computes it in
  * the chunkwise form of Section 4.2 (chunk C = 64) with the secondary
  * sub-chunking of Section 4.3 (sub-chunk c = 16), on hand-written HIP kernels.
  *
@@ -284,21 +284,33 @@ const char* gla_last_error_detail(void);
 int gla_abi_version(void);
 
 /*
- * Kernel timing, for benchmarks and profiling (off by default).
- * gla_kernel_timing(1): every later gla_fwd / gla_bwd call, on any thread,
- *   brackets each kernel it enqueues with two HIP events recorded on the
- *   call's stream (so the measured interval is that kernel on that stream).
- *   gla_kernel_timing(0) stops recording.  Returns 0.
- * gla_kernel_timing_read(buf, len): waits for every recorded event, then
- *   writes one line "<kernel> <launches> <total_ms>" per kernel name, summed
- *   since the previous read, into buf (NUL-terminated, truncated to len
- *   bytes; buf may be NULL to just discard), and clears the record.  Returns
- *   the number of kernel names, or -1 if a HIP event query failed.
- * The events come from a library-owned pool that is kept for the life of the
- * process; recording costs two hipEventRecord calls per launch.
+ * Per-kernel timing, for benchmarks and profiling (off by default).
+ * gla_set_launch_recorder(rec): until it is called again with NULL, every
+ *   library call made by the CALLING THREAD brackets each kernel it enqueues
+ *   with two of the caller's HIP events, recorded on that call's stream (so
+ *   the interval between them is that kernel on that stream).  For the i-th
+ *   launch seen (i = rec->count before the launch; count is then incremented)
+ *   the library records start[i] and stop[i] and sets name[i] to a static,
+ *   NUL-terminated kernel name, as long as i < capacity; later launches only
+ *   increment count, so count > capacity tells the caller that entries were
+ *   dropped.  A failed hipEventRecord sets failed = 1.
+ * Ownership: the record, its arrays and the events (created by the caller
+ *   with timing enabled) stay the caller's and must outlive their use; the
+ *   library creates, destroys and synchronises no event and keeps only the
+ *   pointer, per thread.  Reading the times (hipEventElapsedTime) is the
+ *   caller's job once the stream has passed the stop events.
  */
-int gla_kernel_timing(int enable);
-int gla_kernel_timing_read(char* buf, size_t len);
+typedef struct {
+    int32_t capacity;     /* entries in start, stop and name                 */
+    int32_t count;        /* launches seen while set; the library increments */
+    int32_t failed;       /* set to 1 by the library if an event record fails */
+    int32_t reserved;
+    void* const* start;   /* hipEvent_t[capacity]                            */
+    void* const* stop;    /* hipEvent_t[capacity]                            */
+    const char** name;    /* written by the library                          */
+} gla_launch_recorder_t;
+
+void gla_set_launch_recorder(gla_launch_recorder_t* recorder);
 
 #ifdef __cplusplus
 }

@@ -14,9 +14,9 @@
  *       S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t ,   o_t = q_t S_t
  *   with alpha_t = exp(g_t) given as the log forget gate g_t (Section 4.3 and
  *   the chapter summary's Knowl 3 take the gate in log space).  S_0 is zero or
- *   the previous segment's state (Section 2.2, "initialized to zero or from the
- *   previous segment's hidden state"); the final state S_T is returned so that
- *   segments can be chained (truncated BPTT, Section 5.2).
+ *   the state an earlier segment of the sequence ended with (Section 2.2); the
+ *   final state S_T is returned so that segments can be chained (truncated
+ *   BPTT, Section 5.2).
  *
  * The backward pass is reverse-mode differentiation of that same loop (the
  * hand-computed gradient of the recurrence).  It does NOT use the paper's

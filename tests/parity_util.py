@@ -57,3 +57,34 @@ def gpu_heads(x, heads, state=False):
     if state:
         return np.stack([x[b, h] for b, h in heads])
     return np.stack([x[b, :, h, :] for b, h in heads])
+
+
+LOG2E = 1.4426950408889634
+
+
+def max_chunk_decay_log2(g, chunk=64):
+    """Largest decay of one chunk and key column, -sum_{t in chunk} g_t[i] in
+    log2 units, over a [B,T,H,K] (or scalar [B,T,H]) log-gate tensor as stored.
+    Returns the maximum over batch, chunks and key columns, per head index."""
+    a = to_np(g)
+    if a.ndim == 3:
+        a = a[..., None]
+    B, T, H, K = a.shape
+    s = -a.reshape(B, T // chunk, chunk, H, K).sum(axis=2) * LOG2E   # [B, N, H, K]
+    return s.max(axis=(0, 1, 3))                                      # [H]
+
+
+def chunk_rel_l2(x, ref, chunk=64):
+    """Largest rel-L2 over (head, 64-token chunk) blocks of [n, T, D] arrays.
+    Blocks whose reference norm is zero are compared by their absolute norm."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    n, T, D = ref.shape
+    xs = x.reshape(n, T // chunk, chunk * D)
+    rs = ref.reshape(n, T // chunk, chunk * D)
+    num = np.linalg.norm(xs - rs, axis=2)
+    den = np.linalg.norm(rs, axis=2)
+    r = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    return float(r.max())

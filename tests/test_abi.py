@@ -216,3 +216,35 @@ def test_general_gate_backward_validates(L):
     assert bwd(_shape(T=128, K=128, V=128), h=ctypes.c_void_p(0x10002)) == ERR_ALIGN
     assert bwd(_shape(T=128, K=128, V=128), ws=None) == ERR_WORKSPACE
     assert bwd(_shape(T=0, K=128, V=128)) == OK
+
+
+def test_binding_rejects_non_contiguous_q():
+    # a q sliced out of a fused projection (or expanded with stride 0) must be
+    # refused by every wrapper before the library is called: the kernels read
+    # dense [B,T,H,K] rows
+    import torch
+
+    B, T, H, K, V = 1, 64, 2, 64, 64
+    fused = torch.zeros(B, T, H, 3 * K, dtype=torch.bfloat16)
+    q_slice = fused[..., :K]
+    q_bcast = torch.zeros(1, 1, 1, K, dtype=torch.bfloat16).expand(B, T, H, K)
+    k = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    g = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    gs = torch.zeros(B, T, H, dtype=torch.bfloat16)
+    v = torch.zeros(B, T, H, V, dtype=torch.bfloat16)
+    hv = torch.zeros(B, T, H, V, dtype=torch.bfloat16)
+    state = torch.zeros(B, H, K, V)
+    for q in (q_slice, q_bcast):
+        assert not q.is_contiguous()
+        calls = [
+            lambda: gla.gla_fwd(q, k, v, g),
+            lambda: gla.gla_bwd(q, k, v, g, v),
+            lambda: gla.gla_fwd_scalar(q, k, v, gs),
+            lambda: gla.gla_bwd_scalar(q, k, v, gs, v),
+            lambda: gla.gla_fwd_general(q, k, v, g, hv),
+            lambda: gla.gla_bwd_general(q, k, v, g, hv, v),
+            lambda: gla.gla_decode(q, k, v, g, state),
+        ]
+        for call in calls:
+            with pytest.raises(ValueError, match="q must be contiguous"):
+                call()

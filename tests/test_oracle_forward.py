@@ -114,7 +114,7 @@ def test_chunk_size_invariance(C, c):
 
 
 def test_segment_invariance_state_passing():
-    # S_0 "from the previous segment's hidden state" (Section 2.2): running T1 then T-T1 equals running T.
+    # S_0 carried over from an earlier segment (Section 2.2): running T1 then T-T1 equals running T.
     rng = np.random.default_rng(14)
     B, T, H, K, V = 2, 100, 2, 4, 3
     q, k, v, g, S0 = _rand_case(rng, B, T, H, K, V)

@@ -11,7 +11,8 @@ import torch
 import chunkwise_linear_rnn_amd as gla
 import gla_inputs as gi
 import oracle
-from tests.parity_util import TOL, gpu_heads, head_subset, note, rel_l2, to_np
+from tests.parity_util import TOL, chunk_rel_l2, gpu_heads, head_subset, max_chunk_decay_log2, note, rel_l2, to_np
+from tests.test_parity_fwd import exact_path_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -33,14 +34,22 @@ def _check_bwd(w, heads=None, with_dht=False, inputs=None, tol=None):
     names = ("dq", "dk", "dv", "dg", "ds0")
     got = (dq, dk, dv, dg, ds0)
     tol = tol if tol is not None else TOL[w.torch_dtype]
-    errs = {}
+    errs, worst = {}, {}
     for name, x, r in zip(names, got, ref):
         if name == "ds0":
-            errs[name] = rel_l2(gpu_heads(x, heads, state=True), r[:, 0])
+            xs, rs = gpu_heads(x, heads, state=True), r[:, 0]
+            errs[name] = rel_l2(xs, rs)
+            worst[name] = max(rel_l2(xs[i], rs[i]) for i in range(len(heads)))
         else:
-            errs[name] = rel_l2(gpu_heads(x, heads), r[:, :, 0, :])
+            xs, rs = gpu_heads(x, heads), r[:, :, 0, :]
+            errs[name] = rel_l2(xs, rs)
+            worst[name] = chunk_rel_l2(xs, rs)
     note("  rel-L2 " + " ".join("%s=%.3e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
+    note("  worst 64-token chunk (ds0: worst head) " + " ".join("%s=%.3e" % kv for kv in worst.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+    # the bound holds on every chunk of every compared head as well
+    bad = {k: v for k, v in worst.items() if not v <= tol}
     assert not bad, bad
     return errs
 
@@ -54,8 +63,6 @@ def _check_bwd(w, heads=None, with_dht=False, inputs=None, tol=None):
     (1, 1, 192, 128, 128, "normal0.1", True),
 ])
 def test_bwd_small(dtype, B, H, T, K, V, s0, dht):
-    if dtype == "fp32" and K * V > 128 * 64 and V > 64:
-        pytest.skip("fp32 backward holds K-blocks x V; covered by the smaller fp32 cases")
     w = gi.custom(B, H, T, K, V, dtype=dtype, gate="iid", s0=s0, backward=True, seed=200 + T + K + V)
     _check_bwd(w, with_dht=dht)
 
@@ -73,14 +80,27 @@ def test_bwd_ungated(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_bwd_extreme_gates_exact_path(dtype):
+def test_bwd_near_basis_limit(dtype):
+    # resets of -60 and -45 nat: about 92 log2 units of chunk decay, inside the
+    # 16-bit factorised range (96); fp32 takes its element-wise path
     w = gi.custom(1, 2, 256, 64, 64, dtype=dtype, gate="iid", s0="normal0.1", backward=True, seed=13)
     inp = gi.make_inputs(w, dht=True)
     g = inp["g"].float()
     g[0, 70, :, :5] = -60.0
     g[0, 200, 1, :] = -45.0
     inp["g"] = g.to(w.torch_dtype)
+    decay = max_chunk_decay_log2(inp["g"])
+    assert 80.0 < decay.max() < 96.0, decay
     _check_bwd(w, inputs=inp)
+
+
+@pytest.mark.parametrize("dtype,K,V", [("fp32", 64, 64), ("fp32", 64, 128), ("fp32", 128, 128)] + [
+    ("bf16", K, V) for K, V in ((64, 64), (64, 128), (128, 128), (128, 256), (256, 64), (256, 256))])
+def test_bwd_exact_path(dtype, K, V):
+    # chunks past the factorised range (an asserted decay above 100 log2 units
+    # in both heads): the intra-chunk parts of dq, dk and dv element by element
+    w = gi.custom(1, 2, 256, K, V, dtype=dtype, gate="iid", s0="normal0.1", backward=True, seed=13 + K + V)
+    _check_bwd(w, inputs=exact_path_inputs(w))
 
 
 def test_bwd_empty_sequence():
@@ -103,8 +123,8 @@ def test_bwd_deterministic():
 
 
 @pytest.mark.parametrize("name,heads", [
-    ("metric_8k", [(0, 0), (1, 3)]),
-    ("fwdbwd_16k", [(0, 5), (3, 15)]),
+    ("metric_8k", None),
+    ("fwdbwd_16k", [(b, h) for b in range(4) for h in (0, 5, 10, 15)]),
 ])
 def test_bwd_named_workloads(name, heads):
     w = gi.WORKLOADS[name]
@@ -131,6 +151,7 @@ def test_exact_path_deterministic():
     g[0, 70, :, :40] = -60.0
     g[0, 150:160, 1, 64:] = -9.0
     inp["g"] = g.to(torch.bfloat16)
+    assert max_chunk_decay_log2(inp["g"])[1] > 96.0
     d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
     outs = []
     for _ in range(2):

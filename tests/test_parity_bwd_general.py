@@ -55,7 +55,7 @@ def test_bwd_general_exact_paths_and_no_dht():
     w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=1701)
     inp = gi.make_inputs(w)
     g = inp["g"].float()
-    g[0, 70, 0, :5] = -60.0
+    g[0, 70, 0, :5] = -70.0
     inp["g"] = g.to(torch.bfloat16)
     h = gi.make_value_gate(B, T, H, V, seed=1702).float()
     h[1, 200, 1, :] = -70.0

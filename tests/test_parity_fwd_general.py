@@ -64,7 +64,7 @@ def test_fwd_general_exact_paths():
     w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=False, seed=1401)
     inp = gi.make_inputs(w)
     g = inp["g"].float()
-    g[0, 70, 0, :7] = -60.0
+    g[0, 70, 0, :7] = -70.0
     inp["g"] = g.to(torch.bfloat16)
     h = gi.make_value_gate(B, T, H, V, seed=1402).float()
     h[0, 140, 0, :] = -70.0

@@ -12,7 +12,7 @@ import torch
 
 import chunkwise_linear_rnn_amd as gla
 import gla_inputs as gi
-from tests.parity_util import TOL, gpu_heads, note, oracle_fwd_heads, rel_l2
+from tests.parity_util import TOL, gpu_heads, max_chunk_decay_log2, note, oracle_fwd_heads, rel_l2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -54,15 +54,17 @@ def test_fwd_wide_heads(B, H, T, V, s0):
 
 def test_fwd_wide_exact_path_inside_segments():
     # B*H = 64 heads and two value blocks give two segments of four chunks: a
-    # chunk past the basis range at token 70 (second chunk of segment 0, in the
-    # state pass) and at token 330 (second chunk of segment 1, in the output walk)
+    # chunk past the basis range (96 log2 units) at token 70 (second chunk of
+    # segment 0, in the state pass), at token 330 (second chunk of segment 1, in
+    # the output walk), and over tokens 300..309 in half the key columns
     w = gi.custom(4, 16, 64 * 8, 256, 256, dtype="bf16", gate="iid", s0="normal0.1", backward=False, seed=931)
     inp = gi.make_inputs(w)
     g = inp["g"].float()
-    g[0, 70, 0, :5] = -60.0
-    g[0, 330, 1, :] = -45.0
+    g[0, 70, 0, :5] = -70.0
+    g[0, 330, 1, :] = -70.0
     g[3, 300:310, 15, 128:] = -9.0
     inp["g"] = g.to(torch.bfloat16)
+    assert (max_chunk_decay_log2(inp["g"])[[0, 1, 15]] > 100.0).all()
     _check(w, inp, [(0, 0), (0, 1), (3, 15)])
 
 
