@@ -196,12 +196,13 @@ def _short(demangled: str) -> str:
 def summarize_trace(csv_path, out_md, title, command):
     """Markdown table from a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
     import csv
-    rows = list(csv.DictReader(open(csv_path)))
+    rows = [r for r in csv.DictReader(open(csv_path)) if "3gla" in r["Name"]]  # the library's kernels
     names = _demangle([r["Name"] for r in rows])
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     lines = ["# Kernel times: %s (MI355X, rocprofv3 kernel trace)" % title, "",
              "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "",
-             "    " + command, "", "Source: `%s` (every dispatch of the run)." % os.path.basename(csv_path), "",
+             "    " + command, "", "Source: `%s` (every dispatch of the library's kernels in the run; torch's cache "
+             "scrub and fills are left out of the table and of the shares)." % os.path.basename(csv_path), "",
              "| kernel | launch name | calls | avg us | min us | max us | share of GPU time |",
              "|---|---|---|---|---|---|---|"]
     for r, n in sorted(zip(rows, names), key=lambda x: -float(x[0]["TotalDurationNs"])):
@@ -247,7 +248,7 @@ def summarize_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, workload, co
     wm = _per_kernel_means(_counter_rows(write_csv))
     kernels = {}
     for name in fm:
-        if name not in wm:
+        if name not in wm or "3gla" not in name:  # the library's kernels only (not torch's scrub or fills)
             continue
         base = _kernel_base(name)
         label = LAUNCH_LABEL.get(base, base)
@@ -283,7 +284,7 @@ def summarize_pmc(csv_path, trace_csv, out_md, title, command):
     kernel-trace durations: MfmaUtil = busy MFMA cycles over (GPU active cycles x
     1024 SIMDs); bf16 flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
     import csv
-    means = _per_kernel_means(_counter_rows(csv_path))
+    means = {n: m for n, m in _per_kernel_means(_counter_rows(csv_path)).items() if "3gla" in n}
     dur = {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(trace_csv))}
     names = list(means)
     dem = dict(zip(names, _demangle(names)))
