@@ -56,7 +56,7 @@ EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
-           "gla_set_launch_recorder"]
+           "gla_set_launch_recorder", "gla_fwd_noalloc"]
 
 _lib = None
 
@@ -76,6 +76,8 @@ def lib():
     L.gla_fwd.restype = ctypes.c_int
     L.gla_bwd.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gla_bwd.restype = ctypes.c_int
+    L.gla_fwd_noalloc.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.gla_fwd_noalloc.restype = ctypes.c_int
     L.gla_fwd_scalar.argtypes = L.gla_fwd.argtypes
     L.gla_fwd_scalar.restype = ctypes.c_int
     L.gla_bwd_scalar.argtypes = L.gla_bwd.argtypes
@@ -179,6 +181,15 @@ def gla_fwd_into(q, k, v, g, s0, o, s_final, ws, stream=None, scalar_gate=False)
     fn = lib().gla_fwd_scalar if scalar_gate else lib().gla_fwd
     _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(ws),
               nbytes, _stream(stream)))
+
+
+def gla_fwd_noalloc_into(q, k, v, g, s0, o, s_final, stream=None):
+    """gla_fwd_noalloc: the forward with the library's fixed device scratch
+    instead of a workspace (outputs caller-owned; nothing allocated)."""
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    _check(lib().gla_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o),
+                                 _ptr(s_final), _stream(stream)))
 
 
 def gla_bwd_into(q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, ws, stream=None, scalar_gate=False):

@@ -126,20 +126,30 @@ gla_status_t check_gate_shape(const gla_shape_t* s, gla::Shape* out) {
 
 bool eps_ok(float eps) { return eps >= 0.f && eps <= 3.0e38f; }  // false for NaN and infinities
 
+// Validation of the forward's arguments other than the workspace; fills `s`.
+gla_status_t fwd_check(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                       const float* s0, void* o, float* s_final, bool sg, gla::Shape* s) {
+    gla_status_t st = check_shape(shape, s, false);
+    if (st != GLA_OK) return st;
+    if (sg && !s->bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
+    const bool empty = s->B * s->H == 0 || s->T == 0;
+    if (!empty && (!q || !k || !v || !g || !o)) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
+    const void* ptrs[] = {q, k, v, g, s0, o, s_final};
+    const char* names[] = {"q", "k", "v", "g", "s0", "o", "s_final"};
+    for (int i = 0; i < 7; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    return GLA_OK;
+}
+
 gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
                       void* stream, bool sg) {
     g_detail.clear();
     gla::Shape s;
-    gla_status_t st = check_shape(shape, &s, false);
+    gla_status_t st = fwd_check(shape, q, k, v, g, s0, o, s_final, sg, &s);
     if (st != GLA_OK) return st;
-    if (sg && !s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
+    if (!aligned16(workspace)) return fail(GLA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const bool empty = s.B * s.H == 0 || s.T == 0;
-    if (!empty && (!q || !k || !v || !g || !o)) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
-    const void* ptrs[] = {q, k, v, g, s0, o, s_final, workspace};
-    const char* names[] = {"q", "k", "v", "g", "s0", "o", "s_final", "workspace"};
-    for (int i = 0; i < 8; ++i)
-        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     const size_t need = empty ? 0 : gla::fwd_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
@@ -389,6 +399,28 @@ gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, con
                      const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
                      void* stream) {
     return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, false);
+}
+
+gla_status_t gla_fwd_noalloc(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                             const void* g, const float* s0, void* o, float* s_final, void* stream) {
+    static_assert(GLA_NOALLOC_SCRATCH_BYTES == gla::kNoAllocScratchBytes, "one scratch size");
+    g_detail.clear();
+    gla::Shape s;
+    // every argument is checked before the first HIP call (the scratch lookup)
+    gla_status_t st = fwd_check(shape, q, k, v, g, s0, o, s_final, false, &s);
+    if (st != GLA_OK) return st;
+    const bool empty = s.B * s.H == 0 || s.T == 0;
+    const size_t need = empty ? 0 : gla::fwd_workspace_bytes(s);
+    if (need > gla::kNoAllocScratchBytes)
+        return fail(GLA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the fixed scratch of gla_fwd_noalloc "
+                    "holds %zu (call gla_fwd with a workspace)", need, gla::kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t err = gla::noalloc_scratch(&ws);
+        if (err != hipSuccess)
+            return fail(GLA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(err));
+    }
+    return fwd_impl(shape, q, k, v, g, s0, o, s_final, ws, need > 0 ? gla::kNoAllocScratchBytes : 0, stream, false);
 }
 
 gla_status_t gla_fwd_scalar(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

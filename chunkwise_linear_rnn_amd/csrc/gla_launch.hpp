@@ -7,6 +7,10 @@
 
 namespace gla {
 
+// Size of the fixed device scratch behind gla_fwd_noalloc (gla_noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 struct FwdLaunch {
     bool bf16;
     bool sg;  // g is one value per token and head, [B,T,H] (16-bit inputs only)

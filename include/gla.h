@@ -102,6 +102,31 @@ gla_status_t gla_fwd(const gla_shape_t* shape,
 size_t gla_fwd_workspace_size(const gla_shape_t* shape);
 
 /*
+ * gla_fwd_noalloc -- gla_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The arguments, results, validation and errors are gla_fwd's,
+ * without the workspace: the forward's scratch (segment states and segment
+ * gate totals) lives in a fixed device array inside the library,
+ * GLA_NOALLOC_SCRATCH_BYTES per GPU, which that GPU holds until the process
+ * ends.  The call allocates nothing (no hipMalloc, no library allocation).
+ *  - Shapes whose gla_fwd_workspace_size() exceeds GLA_NOALLOC_SCRATCH_BYTES
+ *    return GLA_ERR_WORKSPACE before anything is enqueued (16-bit heads with
+ *    K = 256, whose forward keeps per-chunk records, always need gla_fwd).
+ *  - Every call on one GPU uses that GPU's single array, and its contents
+ *    are whatever the last call left (nothing in it needs to start at zero).
+ *    Calls that overlap on one GPU -- on different streams, or from several
+ *    threads without ordering them on one stream -- race on the array and
+ *    give wrong results; order them.
+ *  - The first call on each device looks up the array's address on that
+ *    device (hipGetSymbolAddress, the device current at the call); a failure
+ *    there is GLA_ERR_HIP.
+ */
+#define GLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+gla_status_t gla_fwd_noalloc(const gla_shape_t* shape,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const float* s0, void* o, float* s_final, void* stream);
+
+/*
  * gla_bwd -- gradients of the loss L = <o, d_o> + <S_T, dht> with respect to
  * q, k, v, g and S_0, for the same forward as gla_fwd.  States are recomputed
  * (Section 3.3: hidden states are discarded after the forward pass and

@@ -248,3 +248,21 @@ def test_binding_rejects_non_contiguous_q():
         for call in calls:
             with pytest.raises(ValueError, match="q must be contiguous"):
                 call()
+
+
+def test_fwd_noalloc_validates_before_any_hip_call(L):
+    # gla_fwd_noalloc checks every argument, and that the shape's scratch fits
+    # the library's fixed array, before it looks up that array on the device
+    na = lambda shape, **kw: L.gla_fwd_noalloc(ctypes.byref(shape) if shape is not None else None, kw.get("q", P),
+                                               P, P, P, kw.get("s0", None), kw.get("o", P), None, None)
+    assert na(None) == ERR_NULL
+    assert na(_shape(), q=None) == ERR_NULL
+    assert na(_shape(), o=None) == ERR_NULL
+    assert na(_shape(T=100)) == ERR_SHAPE
+    assert na(_shape(K=96)) == ERR_UNSUPPORTED
+    assert na(_shape(), s0=ctypes.c_void_p(0x10004)) == ERR_ALIGN
+    assert na(_shape(T=0)) == OK            # nothing to compute, no scratch needed
+    wide = _shape(B=2, H=4, T=8192, K=256, V=512)
+    assert L.gla_fwd_workspace_size(ctypes.byref(wide)) > 32 << 20
+    assert na(wide) == ERR_WORKSPACE
+    assert b"fixed scratch" in L.gla_last_error_detail()
