@@ -40,14 +40,15 @@ METRIC_SCALAR = "GLA scalar-gate fwd+bwd tokens/sec at T=8K, dk=128, dv=256"
 
 
 def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int, dv_split: bool = False,
-                             G: int = None):
+                             G: int = None, ckpt: bool = False):
     """Algorithmic HBM bytes per (token, head) of one launch of `kernel`.
 
     G is the number of log-gate values per token and head (K for per-column
     gates, 1 for a scalar gate; g and dg have G elements).  The backward's
     segment-state pass reads q, g, d_o of every segment instead of all but the
     first when the dv walk takes segments in halves (it then also needs each
-    segment's midpoint state)."""
+    segment's midpoint state); with a checkpoint (ckpt) it runs only that
+    backward direction."""
     G = K if G is None else G
     seg_frac = (P - 1) / P if P > 1 else 0.0
     seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
@@ -58,7 +59,7 @@ def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd:
         "bwd_dv_walk": e * (2 * K + G + 2 * V),         # q, k, g, d_o read; dv written
         "fwd_seg_state": e * (K + G + V) * seg_frac,    # k, g, v of all but the last segment
         # k, g, v of all but the last segment and q, g, d_o of all but the first (or all)
-        "bwd_seg_states": e * (K + G + V) * (seg_frac_bwd + (1.0 if dv_split else seg_frac_bwd)),
+        "bwd_seg_states": e * (K + G + V) * ((0.0 if ckpt else seg_frac_bwd) + (1.0 if dv_split else seg_frac_bwd)),
     }
     return table.get(kernel)
 
@@ -618,6 +619,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="metric_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="time gla_fwd + gla_bwd as the step (no checkpoint handed from forward to backward)")
     ap.add_argument("--no-attainable", action="store_true",
                     help="skip measuring the box's attainable copy bandwidth and bf16 GEMM rate")
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -664,7 +667,7 @@ def main():
         split = plan_dv_split(w.B, w.H, w.T, w.K, w.V, e == 2)
         alg = {}
         for k in ("fwd_walk", "bwd_dq_walk", "bwd_dk_walk", "bwd_dv_walk", "fwd_seg_state", "bwd_seg_states"):
-            b = alg_bytes_per_token_head(k, w.K, w.V, e, P, Pb, split)
+            b = alg_bytes_per_token_head(k, w.K, w.V, e, P, Pb, split, ckpt=not args.recompute and w.dtype == "bf16" and w.K <= 128)
             if b:
                 alg[k] = b * w.B * w.T * w.H / 1e6
         base = os.path.join(ROOT, "profiles", "traffic_%s" % args.workload)
@@ -728,16 +731,39 @@ def main():
     wsb = gla.workspace((gla.gla_bwd_scalar_workspace_size if sg else gla.gla_bwd_workspace_size)(
         B, T, H, K, V, dt), dev)
 
-    def fwd():
+    # The step is the checkpointed training pair when the shape has one (the
+    # forward keeps each backward segment's starting state, the backward
+    # starts from it); the recompute pair gla_fwd + gla_bwd is timed beside it.
+    ck_bytes = 0 if (sg or args.recompute) else gla.gla_ckpt_size(B, T, H, K, V, dt)
+    ck = gla.workspace(ck_bytes, dev)
+
+    def fwd_rc():
         gla.gla_fwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, wsf, scalar_gate=sg)
 
-    def bwd():
+    def bwd_rc():
         gla.gla_bwd_into(d["q"], d["k"], d["v"], d["g"], d["s0"], d["do"], None, dq, dk, dv, dg, ds0, wsb,
                          scalar_gate=sg)
+
+    def fwd():
+        if ck_bytes:
+            gla.gla_fwd_ckpt_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, ck, wsf)
+        else:
+            fwd_rc()
+
+    def bwd():
+        if ck_bytes:
+            gla.gla_bwd_ckpt_into(d["q"], d["k"], d["v"], d["g"], d["s0"], ck, d["do"], None, dq, dk, dv, dg, ds0,
+                                  wsb)
+        else:
+            bwd_rc()
 
     def step():
         fwd()
         bwd()
+
+    def step_rc():
+        fwd_rc()
+        bwd_rc()
 
     def timed(fn, n):
         # warm: n back-to-back calls, inputs left in the caches by the previous call
@@ -783,6 +809,7 @@ def main():
     cold_bwd = cold_times(bwd, args.steps)
     ms_fwd, ms_bwd = pct(cold_fwd, 50), pct(cold_bwd, 50)
     ms_fwd_warm, ms_bwd_warm = timed(fwd, args.steps), timed(bwd, args.steps)
+    cold_rc = cold_times(step_rc, args.steps) if ck_bytes else cold
     del scrub
 
     # per-kernel HIP-event timing over another K steps (each kernel bracketed on
@@ -799,7 +826,7 @@ def main():
     P_bwd = plan_segments_bwd(B, H, T, K, V, w.dtype == "bf16")
     units = B * T * H
     bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd, plan_dv_split(B, H, T, K, V, w.dtype == "bf16"),
-                                   G=1 if sg else K)
+                                   G=1 if sg else K, ckpt=bool(ck_bytes))
     roofline = None
     if bpt is not None:
         ach = bpt * units / (kern[dom]["avg_us"] * 1e-6) / 1e9
@@ -832,8 +859,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, %s per step" % (
             w.name, B, H, T, K, V, w.dtype, "scalar gate [B,T,H], gla_fwd_scalar + gla_bwd_scalar" if sg else
-            "gla_fwd + gla_bwd"), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
+            ("gla_fwd_ckpt + gla_bwd_ckpt (the backward starts its segments from the forward's states)" if ck_bytes
+             else "gla_fwd + gla_bwd")), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
             "chunk": 64, "segments": P},
+        "ms_per_step_recompute": pct(cold_rc, 50),
+        "recompute_step": "gla_fwd + gla_bwd (every state recomputed in the backward), cold median",
         "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
         "bwd_tokens_per_s": tokens / (ms_bwd * 1e-3),
         "ms_fwd": ms_fwd,

@@ -141,9 +141,18 @@ gla_status_t fwd_check(const gla_shape_t* shape, const void* q, const void* k, c
     return GLA_OK;
 }
 
+// Shapes whose backward can start from a checkpointing forward's segment
+// states: 16-bit inputs on the pipelined walks (K <= 128) with more than one
+// backward segment.  Returns the checkpoint's size in bytes, or 0.
+size_t ckpt_bytes(const gla::Shape& s) {
+    if (!s.bf16 || s.K > 128 || s.B * s.H == 0 || s.T == 0) return 0;
+    const gla::Plan pb = gla::make_bwd_plan(s);
+    return pb.P > 1 ? gla::state_bytes(s, pb) : 0;
+}
+
 gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
-                      void* stream, bool sg) {
+                      void* stream, bool sg, void* ckpt = nullptr) {
     g_detail.clear();
     gla::Shape s;
     gla_status_t st = fwd_check(shape, q, k, v, g, s0, o, s_final, sg, &s);
@@ -182,6 +191,12 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
             a.ws_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + gla::state_bytes(s, p));
         }
         if (gla::fwd_wide(s)) a.ws_rec = static_cast<char*>(workspace) + gla::fwd_seg_bytes(s, p);
+        if (ckpt && ckpt_bytes(s) > 0) {
+            const gla::Plan pb = gla::make_bwd_plan(s);
+            a.ckpt = ckpt;
+            a.ck_len = pb.seg_len;
+            a.ck_P = pb.P;
+        }
         a.stream = strm;
         err = gla::launch_fwd(a);
     }
@@ -289,7 +304,8 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
 
 gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
-                      float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg) {
+                      float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg,
+                      const void* ckpt = nullptr) {
     g_detail.clear();
     gla::Shape s;
     gla_status_t st = check_shape(shape, &s, true);
@@ -337,7 +353,10 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
         const size_t sb = gla::state_bytes(s, p);
         const size_t kk = (size_t)p.BH * p.P * s.K;
         char* ws = static_cast<char*>(workspace);
-        a.ws_state = ws;
+        // a checkpoint holds S_init(p) in the layout of the workspace's state area
+        const bool use_ck = ckpt && ckpt_bytes(s) > 0;
+        a.ckpt = use_ck;
+        a.ws_state = use_ck ? const_cast<void*>(ckpt) : ws;
         a.ws_dstate = ws + sb;
         a.ws_gate = reinterpret_cast<float*>(ws + 2 * sb);
         a.ws_hs = ws + 2 * sb + gla::round256(kk * sizeof(float));
@@ -421,6 +440,40 @@ gla_status_t gla_fwd_noalloc(const gla_shape_t* shape, const void* q, const void
             return fail(GLA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(err));
     }
     return fwd_impl(shape, q, k, v, g, s0, o, s_final, ws, need > 0 ? gla::kNoAllocScratchBytes : 0, stream, false);
+}
+
+size_t gla_ckpt_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, true) != GLA_OK) return 0;
+    return ckpt_bytes(s);
+}
+
+gla_status_t gla_fwd_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                          const float* s0, void* o, float* s_final, void* ckpt, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, true);
+    if (st != GLA_OK) return st;
+    const size_t need = ckpt_bytes(s);
+    if (need > 0 && !ckpt) return fail(GLA_ERR_NULL, "ckpt is required (gla_ckpt_size = %zu bytes)", need);
+    if (!aligned16(ckpt)) return fail(GLA_ERR_ALIGN, "ckpt is not 16-byte aligned");
+    return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, false,
+                    need > 0 ? ckpt : nullptr);
+}
+
+gla_status_t gla_bwd_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                          const float* s0, const void* ckpt, const void* d_o, const float* dht, void* dq, void* dk,
+                          void* dv, void* dg, float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, true);
+    if (st != GLA_OK) return st;
+    const size_t need = ckpt_bytes(s);
+    if (need > 0 && !ckpt) return fail(GLA_ERR_NULL, "ckpt is required (gla_ckpt_size = %zu bytes)", need);
+    if (!aligned16(ckpt)) return fail(GLA_ERR_ALIGN, "ckpt is not 16-byte aligned");
+    return bwd_impl(shape, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes, stream, false,
+                    need > 0 ? ckpt : nullptr);
 }
 
 gla_status_t gla_fwd_scalar(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

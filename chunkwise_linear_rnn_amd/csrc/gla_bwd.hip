@@ -160,21 +160,23 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
 
 // ---------------------------------------------------------------------------
 // Backward combine, one thread per kCombineVec adjacent elements of a state
-// row; blockIdx.z = 0 combines the states, 1 the state gradients:
+// row; blockIdx.z + z0 = 0 combines the states, 1 the state gradients (z0 = 1
+// with a one-deep grid: the gradients only, the states being a checkpointing
+// forward's):
 //   S_init(0) = S_0;  S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p
 //   dS_end(P-1) = dht; dS_end(p-1) = Diag(exp2 G_p) dS_end(p) + dS*_p
 // ws_state / ws_dstate hold S*_p / dS*_p on entry and S_init / dS_end on exit.
 template <typename ST>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
-                    ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
+                    ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P, int z0) {
     const long KV = (long)K * V;
     const long e = ((long)blockIdx.x * 256 + threadIdx.x) * kCombineVec;
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
     const float* gt = ws_gate + bh * P * (long)K + i;
-    if (blockIdx.z == 0)
+    if (blockIdx.z + z0 == 0)
         combine_row<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr);
     else
         combine_row<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr);
@@ -186,7 +188,8 @@ gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht,
 template <typename ST>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_bwd_split(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
-                          ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P) {
+                          ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P,
+                          int z0) {
     __shared__ f32x4 carry[128];
     const long KV = (long)K * V;
     const int slot = threadIdx.x & 127, part = threadIdx.x >> 7;
@@ -194,7 +197,7 @@ gla_seg_combine_bwd_split(const float* __restrict__ s0, const float* __restrict_
     const long bh = blockIdx.y;
     const int i = (int)(e / V);
     const float* gt = ws_gate + bh * P * (long)K + i;
-    if (blockIdx.z == 0)
+    if (blockIdx.z + z0 == 0)
         combine_row_split<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr, part,
                                  &carry[slot]);
     else
@@ -1713,23 +1716,27 @@ static hipError_t launch_seg_states_g(const BwdLaunch& a) {
     const int nvb = a.V / BV;
     const long KV = (long)KD * a.V;
     if (a.P > 1) {
+        // with a checkpoint the states S_init(p) are given: only dS*_p (and the
+        // gate totals, from the backward direction) are formed, and only dS combined
         const int nseg = a.P - 1;
         const bool mid = a.dv_split == 2;
-        const long nfwd = xcd_grid(nseg * a.BH, nvb);
+        const long nfwd = a.ckpt ? 0 : xcd_grid(nseg * a.BH, nvb);
         const long nrev = xcd_grid((nseg + (mid ? 1 : 0)) * a.BH, nvb);
         dim3 grid2((unsigned)(nfwd + nrev));
         GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW, SG>), grid2, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, (T*)a.ws_state,
                            (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd,
-                           mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2);
+                           mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2, a.ckpt ? 0 : a.P - 1);
+        const unsigned nz = a.ckpt ? 1u : 2u;
+        const int z0 = a.ckpt ? 1 : 0;
         if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
             GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd_split<T>,
-                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, 2u), dim3(256), a.stream, a.s0,
-                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P);
+                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
+                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P, z0);
         } else {
             GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>,
-                       dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, 2u), dim3(256), a.stream,
-                       a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P);
+                       dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, nz), dim3(256), a.stream,
+                       a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P, z0);
         }
     }
     return hipGetLastError();

@@ -601,14 +601,17 @@ gla_seg_state(const T* __restrict__ x, const T* __restrict__ g, const T* __restr
 // rest take dS*_p of segments 1 .. P-1 from q, d_o, or, with ws_dmid, of every
 // segment together with its midpoint state (the local dS* of the chunks from
 // c_begin + split on) and that half's gate total, from which the dv walk
-// starts a segment's first half.
+// starts a segment's first half.  Each segment's gate total G_p is written by
+// the forward direction, except from rev_gate_first on, where the backward
+// direction writes it (P - 1 when both directions run; 0 when nfwd = 0 because
+// the states come from a checkpointing forward).
 template <typename T, int KD, int BV, int NW, bool SG = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ q,
                    const T* __restrict__ d_o, const T* __restrict__ g, T* __restrict__ ws_state,
                    T* __restrict__ ws_dstate, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
                    int seg_len, int nseg, int BH, int nfwd, T* __restrict__ ws_dmid, float* __restrict__ ws_gmid,
-                   int split) {
+                   int split, int rev_gate_first) {
     __shared__ SegSmem<T, KD, BV, NW> sm;
     const int bid = blockIdx.x;
     if (bid < nfwd)
@@ -616,10 +619,10 @@ gla_seg_state_pair(const T* __restrict__ k, const T* __restrict__ v, const T* __
                                                  nseg, BH, 0);
     else if (!ws_dmid)  // only segment P-1 is not covered by the forward direction
         seg_state_body<T, KD, BV, NW, true, SG>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P,
-                                                seg_len, 1, nseg, BH, P - 1);
+                                                seg_len, 1, nseg, BH, rev_gate_first);
     else  // every segment, for its midpoint state (segment 0's total is not needed)
         seg_state_body<T, KD, BV, NW, true, SG>(sm, bid - nfwd, q, g, d_o, ws_dstate, ws_gate, T_, H, V, N, P,
-                                                seg_len, 0, nseg + 1, BH, P - 1, ws_dmid, ws_gmid, split);
+                                                seg_len, 0, nseg + 1, BH, rev_gate_first, ws_dmid, ws_gmid, split);
 }
 
 }  // namespace gla

@@ -345,12 +345,17 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 // so the vector-ALU preparation of the next chunk overlaps the matrix work of
 // this one.  Each wave owns BV/NW value columns: its slice of V never needs a
 // workgroup barrier.
-template <typename T, int KD, int BV, int NW, bool SG = false>
+//
+// CK (checkpointing forward): after the update of every chunk c with c + 1 a
+// multiple of ck_len (and c + 1 < N), the state before chunk c + 1 is also
+// written to ck[bh][(c + 1) / ck_len] ([BH][ck_P][K][V], input dtype): the
+// segment-start states of a backward whose segments are ck_len chunks long.
+template <typename T, int KD, int BV, int NW, bool SG = false, bool CK = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const T* __restrict__ ws_init, const float* __restrict__ s0,
                   T* __restrict__ o, float* __restrict__ s_final, int T_, int H, int V, int N, int P, int seg_len,
-                  int BH) {
+                  int BH, T* __restrict__ ck = nullptr, int ck_len = 1, int ck_P = 1) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, false>;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
@@ -560,6 +565,10 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                 update();
             }
             if (c + 2 < c_end) load_groups(c + 2, MG, NG);
+            if constexpr (CK) {
+                if ((c + 1) % ck_len == 0 && c + 1 < N)
+                    S.store(ck + ((long)bh * ck_P + (c + 1) / ck_len) * KD * V, V, col0);
+            }
         }
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
         if (Sm::VB == 1 && more) {
@@ -606,9 +615,19 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
-        GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG>), grid, dim3(NT), a.stream,
+        if (a.ckpt) {
+            if constexpr (!SG)
+                GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, true>), grid, dim3(NT), a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
-                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
+                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
+                           a.ck_len, a.ck_P);
+            else
+                return hipErrorInvalidValue;
+        } else {
+            GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG>), grid, dim3(NT), a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
+                       (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
+        }
     } else {
         static_assert(!SG, "scalar gates take the 16-bit path");
         // fp32: the workspace states are fp32 and hold S_init(0) = S_0 after the combine

@@ -27,6 +27,8 @@ struct FwdLaunch {
     const void* h;    // general gates: log beta, [B,T,H,V] (null otherwise)
     float* ws_gateb;  // general gates: [BH][P][V] fp32 (log2 of the segment's column decay)
     void* ws_hs;      // general gates, optional: the state before every chunk, [BH][N][K][V] bf16
+    void* ckpt;       // optional: the state before every ck_len-th chunk, [BH][ck_P][K][V] input dtype
+    int ck_len, ck_P;
     hipStream_t stream;
 };
 
@@ -51,6 +53,7 @@ struct BwdLaunch {
     void* ws_dmid;     // [BH][P][K][V] dtype (dv_split == 2): local dS* of each segment's second half
     float* ws_gmid;    // [BH][P][K] fp32: that half's gate total (log2)
     float* ws_dgp;     // scalar gate: [K/BK][BH*T] fp32, each key block's sum of dg over its columns
+    bool ckpt;         // ws_state already holds S_init(p) (a checkpointing forward's): only dS is combined
     hipStream_t stream;
 };
 

@@ -152,6 +152,41 @@ gla_status_t gla_bwd(const gla_shape_t* shape,
 size_t gla_bwd_workspace_size(const gla_shape_t* shape);
 
 /*
+ * Checkpointed training pair: gla_fwd_ckpt + gla_bwd_ckpt.
+ * Section 3.3 weighs materialising the hidden states in the forward pass
+ * against recomputing them in the backward pass.  This pair keeps a small
+ * part: the state at the start of each sequence segment the backward splits a
+ * head into (one K x V state per segment), written by the forward walk when it
+ * passes that chunk boundary.  The backward then recomputes every chunk state
+ * inside its segments from those starting states (instead of first running
+ * its own pass over k, v and g to find them); everything else is gla_bwd.
+ *   gla_ckpt_size(shape) : bytes of the checkpoint, [B,H,P,K,V] in the
+ *     token dtype (P = the backward's segment count; entry 0 of each head is
+ *     not written: segment 0 starts from s0).  0 when the shape has no
+ *     checkpoint: fp32 inputs, K = 256, a single segment, or an invalid or
+ *     empty shape; both calls then behave exactly like gla_fwd / gla_bwd and
+ *     ckpt may be NULL.  The shape must also be a valid backward shape.
+ *   gla_fwd_ckpt : gla_fwd (same arguments, results and workspace), plus
+ *     writes ckpt (device, caller-owned, 16-byte aligned).
+ *   gla_bwd_ckpt : gla_bwd (same arguments, results and workspace), plus
+ *     reads ckpt, which must hold what gla_fwd_ckpt wrote for the same shape,
+ *     q, k, v, g and s0, unmodified since.  A checkpoint from other inputs
+ *     gives wrong gradients (it is not checked).
+ * Errors: as gla_fwd / gla_bwd; GLA_ERR_NULL for a NULL ckpt when
+ * gla_ckpt_size(shape) > 0, GLA_ERR_ALIGN for a misaligned one.
+ */
+size_t gla_ckpt_size(const gla_shape_t* shape);
+gla_status_t gla_fwd_ckpt(const gla_shape_t* shape,
+                          const void* q, const void* k, const void* v, const void* g,
+                          const float* s0, void* o, float* s_final, void* ckpt,
+                          void* workspace, size_t workspace_bytes, void* stream);
+gla_status_t gla_bwd_ckpt(const gla_shape_t* shape,
+                          const void* q, const void* k, const void* v, const void* g,
+                          const float* s0, const void* ckpt, const void* d_o, const float* dht,
+                          void* dq, void* dk, void* dv, void* dg, float* ds0,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gla_fwd_scalar / gla_bwd_scalar -- the same operator with a scalar forget
  * gate per token and head, alpha_t = exp(g_t) * 1 (every key column decays
  * alike: the data-dependent decay of Mamba-2 and the gated retention form,

@@ -266,3 +266,23 @@ def test_fwd_noalloc_validates_before_any_hip_call(L):
     assert L.gla_fwd_workspace_size(ctypes.byref(wide)) > 32 << 20
     assert na(wide) == ERR_WORKSPACE
     assert b"fixed scratch" in L.gla_last_error_detail()
+
+
+def test_ckpt_entry_points_validate(L):
+    size = lambda shape: L.gla_ckpt_size(ctypes.byref(shape))
+    s = _shape(B=2, H=4, T=8192, K=128, V=256)
+    assert size(s) == size(s) > 0
+    assert size(s) % (128 * 256 * 2) == 0              # whole bf16 states
+    assert size(_shape(dtype=gla.GLA_DTYPE_FP32)) == 0  # fp32: no checkpoint
+    assert size(_shape(K=256, V=256, T=8192)) == 0      # wide heads: no checkpoint
+    assert size(_shape(B=1, H=1, T=64)) == 0            # one segment
+    assert size(_shape(V=512, T=8192)) == 0             # not a backward shape
+    fwd = lambda shape, ck=P: L.gla_fwd_ckpt(ctypes.byref(shape), P, P, P, P, None, P, None, ck, P, 1 << 40, None)
+    bwd = lambda shape, ck=P: L.gla_bwd_ckpt(ctypes.byref(shape), P, P, P, P, None, ck, P, None, P, P, P, P, None,
+                                             P, 1 << 40, None)
+    assert fwd(s, ck=None) == ERR_NULL
+    assert bwd(s, ck=None) == ERR_NULL
+    assert fwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert bwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert fwd(_shape(T=100)) == ERR_SHAPE
+    assert bwd(_shape(V=512)) == ERR_UNSUPPORTED
