@@ -340,6 +340,16 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
         // segment as two halves (same workgroup count, no repeated key-side work)
         a.dv_split = gla::dv_split(s, p);
         a.BVD = a.dv_split == 2 ? a.BVS : a.BV;
+        a.BVSEG = a.BVS;
+        const bool ck_used = ckpt && ckpt_bytes(s) > 0;
+        const int dsub = ck_used && a.dv_split == 2 && p.seg_len % 2 == 0 ? 2 : 1;
+        if (ck_used) {
+            // only the dS direction runs (over half segments when dsub = 2): half
+            // the value width when the full width would leave CUs idle
+            const long nsub = dsub == 2 ? (p.N + p.seg_len / 2 - 1) / (p.seg_len / 2) : p.P;
+            const long nrev = (nsub - 1 + (a.dv_split == 2 && dsub == 1 ? 1 : 0)) * p.BH * (s.V / a.BVS);
+            if (2 * nrev <= gla::kTargetWorkgroups && a.BVS >= 128) a.BVSEG = a.BVS / 2;
+        }
         a.BK = p.BK;
         a.T = (int)s.T;
         a.H = (int)s.H;
@@ -358,6 +368,11 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
         a.ckpt = use_ck;
         a.ws_state = use_ck ? const_cast<void*>(ckpt) : ws;
         a.ws_dstate = ws + sb;
+        // checkpoint with the dv walk in halves: the gradients are combined at
+        // every half-segment end, in the workspace's two state areas (the first
+        // one is free: the states come from the checkpoint)
+        a.dsub = dsub;
+        if (a.dsub == 2) a.ws_dstate = ws;
         a.ws_gate = reinterpret_cast<float*>(ws + 2 * sb);
         a.ws_hs = ws + 2 * sb + gla::round256(kk * sizeof(float));
         a.ws_dp = s.bf16 ? static_cast<char*>(a.ws_hs) + gla::round256(gla::hs_bytes(s, p)) : nullptr;
@@ -368,6 +383,9 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
         }
         // scalar gate: each key block's per-token sum of dg, after everything else
         if (sg) a.ws_dgp = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, false));
+        // the half-segment gate totals (dsub = 2) sit in the last area
+        if (a.dsub == 2) a.ws_gate = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, sg) -
+                                                             gla::round256(2 * kk * sizeof(float)));
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
@@ -643,7 +661,9 @@ size_t bwd_workspace_bytes(const gla::Shape& s, bool sg) {
     // walk) the segments' midpoint states and half gate totals
     const size_t dp = s.bf16 ? gla::round256((size_t)p.BH * p.N * 64 * 64 * 2) : 0;
     const size_t mid = gla::dv_split(s, p) == 2 ? gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) : 0;
+    // last: [BH][2P][K] fp32 half-segment gate totals of the checkpointed backward
+    const size_t gsub = gla::round256(2 * kk * sizeof(float));
     return 2 * gla::state_bytes(s, p) + gla::round256(kk * sizeof(float)) + gla::round256(gla::hs_bytes(s, p)) + dp +
-           mid + dgp;
+           mid + dgp + gsub;
 }
 }  // namespace

@@ -162,24 +162,25 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
 // Backward combine, one thread per kCombineVec adjacent elements of a state
 // row; blockIdx.z + z0 = 0 combines the states, 1 the state gradients (z0 = 1
 // with a one-deep grid: the gradients only, the states being a checkpointing
-// forward's):
+// forward's).  P segments are combined, laid out PH >= P apart per head:
 //   S_init(0) = S_0;  S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p
 //   dS_end(P-1) = dht; dS_end(p-1) = Diag(exp2 G_p) dS_end(p) + dS*_p
 // ws_state / ws_dstate hold S*_p / dS*_p on entry and S_init / dS_end on exit.
 template <typename ST>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
-                    ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P, int z0) {
+                    ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P, int z0,
+                    int PH) {
     const long KV = (long)K * V;
     const long e = ((long)blockIdx.x * 256 + threadIdx.x) * kCombineVec;
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
-    const float* gt = ws_gate + bh * P * (long)K + i;
+    const float* gt = ws_gate + bh * PH * (long)K + i;
     if (blockIdx.z + z0 == 0)
-        combine_row<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr);
+        combine_row<false>(ws_state + bh * PH * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr);
     else
-        combine_row<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr);
+        combine_row<true>(ws_dstate + bh * PH * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr);
 }
 
 // The same with each element group's segments split between two threads
@@ -189,19 +190,19 @@ template <typename ST>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_bwd_split(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
                           ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P,
-                          int z0) {
+                          int z0, int PH) {
     __shared__ f32x4 carry[128];
     const long KV = (long)K * V;
     const int slot = threadIdx.x & 127, part = threadIdx.x >> 7;
     const long e = ((long)blockIdx.x * 128 + slot) * kCombineVec;
     const long bh = blockIdx.y;
     const int i = (int)(e / V);
-    const float* gt = ws_gate + bh * P * (long)K + i;
+    const float* gt = ws_gate + bh * PH * (long)K + i;
     if (blockIdx.z + z0 == 0)
-        combine_row_split<false>(ws_state + bh * P * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr, part,
+        combine_row_split<false>(ws_state + bh * PH * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr, part,
                                  &carry[slot]);
     else
-        combine_row_split<true>(ws_dstate + bh * P * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr, part,
+        combine_row_split<true>(ws_dstate + bh * PH * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr, part,
                                 &carry[slot]);
 }
 
@@ -747,7 +748,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 const T* __restrict__ d_o, const T* __restrict__ dq, const T* __restrict__ ws_dinit,
                 const float* __restrict__ dht, const T* __restrict__ hs, const T* __restrict__ dp_in,
                 T* __restrict__ dk, T* __restrict__ dg, float* __restrict__ dg_part, int T_, int H, int K, int N,
-                int P, int seg_len, int BH) {
+                int P, int seg_len, int BH, int dsub) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
@@ -772,9 +773,12 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     auto chunk_of = [&](int it) { return c_end - 1 - it; };
 
     if (tid < 2) sm.buf[tid].flag[0] = 0;
-    // the last segment starts from the caller's fp32 dht, earlier ones from the combined gradients
+    // the last segment starts from the caller's fp32 dht, earlier ones from the
+    // combined gradients ([BH][dsub*P][K][V]: with dsub = 2 one per half segment,
+    // and this segment's end is that of its second half)
     TStateRegs<VW> S;  // dS^T
-    if (seg < P - 1) S.load(ws_dinit + ((long)bh * P + seg) * (long)K * V + (long)k0 * V, V, i0, j0);
+    if (seg < P - 1)
+        S.load(ws_dinit + ((long)bh * dsub * P + dsub * seg + dsub - 1) * (long)K * V + (long)k0 * V, V, i0, j0);
     else if (dht) S.load(dht + (long)bh * K * V + (long)k0 * V, V, i0, j0);
     else S.zero();
 
@@ -1452,7 +1456,7 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 const T* __restrict__ d_o, const T* __restrict__ ws_dinit, const float* __restrict__ dht,
                 const T* __restrict__ ws_dmid, const float* __restrict__ ws_gmid, int split, int nhalf,
                 T* __restrict__ dv, float* __restrict__ ds0, int T_, int H, int V, int N, int P, int seg_len, int BH,
-                const float* __restrict__ dg_part, int nkb, T* __restrict__ dg) {
+                const float* __restrict__ dg_part, int nkb, T* __restrict__ dg, int dsub) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, true>;  // sm.A holds A^T [s][t]; sm.Vw the d_o slices
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
@@ -1490,10 +1494,22 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     // the last segment starts from the caller's fp32 dht, earlier ones from the
     // combined segment gradients ([BH][P][K][V], input dtype)
     StateRegs<KD, CB> S;  // dS
-    if (seg < P - 1) S.load(ws_dinit + ((long)bh * P + seg) * KD * V, V, col0);
-    else if (dht) S.load(dht + (long)bh * KD * V, V, col0);
-    else S.zero();
-    if (nhalf == 2 && half == 0) {
+    if (dsub == 2) {
+        // one combined gradient per half segment ([BH][2P][K][V]); the last
+        // half that holds chunks starts from dht
+        const int sub = 2 * seg + half;
+        const int nsub = (N + split - 1) / split;
+        if (sub < nsub - 1) S.load(ws_dinit + ((long)bh * 2 * P + sub) * KD * V, V, col0);
+        else if (dht) S.load(dht + (long)bh * KD * V, V, col0);
+        else S.zero();
+    } else if (seg < P - 1) {
+        S.load(ws_dinit + ((long)bh * P + seg) * KD * V, V, col0);
+    } else if (dht) {
+        S.load(dht + (long)bh * KD * V, V, col0);
+    } else {
+        S.zero();
+    }
+    if (nhalf == 2 && half == 0 && dsub == 1) {
         // dS at the midpoint = Diag(exp2 G_half) dS_end + the second half's local dS*;
         // slot r of tile (a, cb) is key row 16a + 4(l/16) + r
         StateRegs<KD, CB> D;
@@ -1706,8 +1722,10 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 // ---------------------------------------------------------------------------
 // Host launchers.
 // Segment states of both directions and their combine.  The workgroups span
-// the forward's value width (BV = a.BVS), so the key-side preparation and its
-// loads are not repeated across value blocks.
+// the forward's value width (BV = a.BVSEG = a.BVS), so the key-side preparation
+// and its loads are not repeated across value blocks; with a checkpoint only
+// the backward direction runs, on half that width when the full width would
+// leave CUs idle.
 template <typename T, int KD, int BV, bool SG>
 static hipError_t launch_seg_states_g(const BwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
@@ -1717,26 +1735,32 @@ static hipError_t launch_seg_states_g(const BwdLaunch& a) {
     const long KV = (long)KD * a.V;
     if (a.P > 1) {
         // with a checkpoint the states S_init(p) are given: only dS*_p (and the
-        // gate totals, from the backward direction) are formed, and only dS combined
-        const int nseg = a.P - 1;
-        const bool mid = a.dv_split == 2;
+        // gate totals, from the backward direction) are formed, and only dS
+        // combined; with dsub = 2 over half segments (PS = the number of half
+        // segments that hold chunks), so that each walk covers half as many chunks
+        const int PS = a.dsub == 2 ? (a.N + a.seg_len / 2 - 1) / (a.seg_len / 2) : a.P;
+        const int lenS = a.dsub == 2 ? a.seg_len / 2 : a.seg_len;
+        const int nseg = PS - 1;
+        const bool mid = a.dv_split == 2 && a.dsub == 1;
         const long nfwd = a.ckpt ? 0 : xcd_grid(nseg * a.BH, nvb);
         const long nrev = xcd_grid((nseg + (mid ? 1 : 0)) * a.BH, nvb);
         dim3 grid2((unsigned)(nfwd + nrev));
         GLA_LAUNCH("bwd_seg_states", (gla_seg_state_pair<T, KD, BV, NW, SG>), grid2, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.q, (const T*)a.d_o, (const T*)a.g, (T*)a.ws_state,
-                           (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, (int)nfwd,
-                           mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2, a.ckpt ? 0 : a.P - 1);
+                           (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.dsub * a.P, lenS, nseg, (int)a.BH,
+                           (int)nfwd, mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2,
+                           a.ckpt ? 0 : a.P - 1);
         const unsigned nz = a.ckpt ? 1u : 2u;
         const int z0 = a.ckpt ? 1 : 0;
-        if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
+        // the combine walks the PS entries that hold chunks, at a stride of dsub*P per head
+        if (PS <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
             GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd_split<T>,
                        dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
-                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P, z0);
+                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, PS, z0, a.dsub * a.P);
         } else {
             GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>,
                        dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, nz), dim3(256), a.stream,
-                       a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, a.P, z0);
+                       a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, PS, z0, a.dsub * a.P);
         }
     }
     return hipGetLastError();
@@ -1766,7 +1790,7 @@ static hipError_t launch_dv_g(const BwdLaunch& a) {
         GLA_LAUNCH("bwd_dv_walk", (gla_bwd_dv_pipe<T, KD, BV, NW, SG>), gridh, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_dstate, a.dht,
                            (const T*)a.ws_dmid, a.ws_gmid, (a.seg_len + 1) / 2, nhalf, (T*)a.dv, a.ds0, a.T, a.H, a.V,
-                           a.N, a.P, a.seg_len, (int)a.BH, (const float*)a.ws_dgp, a.K / a.BK, (T*)a.dg);
+                           a.N, a.P, a.seg_len, (int)a.BH, (const float*)a.ws_dgp, a.K / a.BK, (T*)a.dg, a.dsub);
     } else {
         static_assert(!SG, "scalar gates take the 16-bit path");
         const float* dinit = a.P > 1 ? (const float*)a.ws_dstate : a.dht;
@@ -1820,7 +1844,7 @@ static hipError_t launch_rows_g(const BwdLaunch& a) {
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk_pipe<T, BK, V, NW, SG>), grid, dim3(NT), a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.dq,
                            (const T*)a.ws_dstate, a.dht, (const T*)a.ws_hs, (const T*)a.ws_dp, (T*)a.dk, (T*)a.dg,
-                           a.ws_dgp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+                           a.ws_dgp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH, a.dsub);
     } else {
         static_assert(!SG, "scalar gates take the 16-bit path");
         GLA_LAUNCH("bwd_dk_walk", (gla_bwd_dk<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.q,
@@ -1842,7 +1866,7 @@ static hipError_t launch_rows(const BwdLaunch& a) {
 }
 
 #define GLA_COL_DISPATCH(FN, T, KD_, BV_)                              \
-    if (a.K == KD_ && (dv_stage ? a.BVD : a.BVS) == BV_) {             \
+    if (a.K == KD_ && (dv_stage ? a.BVD : a.BVSEG) == BV_) {           \
         hipError_t e = FN<T, KD_, BV_>(a);                             \
         return e;                                                      \
     }

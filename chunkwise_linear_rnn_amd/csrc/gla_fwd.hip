@@ -566,8 +566,22 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
             }
             if (c + 2 < c_end) load_groups(c + 2, MG, NG);
             if constexpr (CK) {
-                if ((c + 1) % ck_len == 0 && c + 1 < N)
-                    S.store(ck + ((long)bh * ck_P + (c + 1) / ck_len) * KD * V, V, col0);
+                if ((c + 1) % ck_len == 0 && c + 1 < N) {
+                    // the lane's offset is formed here, behind an empty asm: hoisted
+                    // out of the chunk loop, the store's 64 addresses would stay
+                    // live across every chunk and spill
+                    int lo = 4 * (l >> 4) * V + col0 + (l & 15);
+                    int vs = V;
+                    asm volatile("" : "+v"(lo), "+s"(vs));
+                    T* dst = ck + ((long)bh * ck_P + (c + 1) / ck_len) * KD * V + lo;
+#pragma unroll
+                    for (int a = 0; a < KD / 16; ++a)
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                dst[(16 * a + r) * vs + 16 * cb] = Elem<T>::from_f(S.s[a][cb][r]);
+                }
             }
         }
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier

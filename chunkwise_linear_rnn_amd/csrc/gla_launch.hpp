@@ -36,7 +36,8 @@ struct BwdLaunch {
     bool bf16;
     bool sg;  // g and dg are one value per token and head, [B,T,H] (16-bit inputs only)
     int K, V, BV, BK;
-    int BVS;  // value columns per workgroup of the segment-state pass (the forward's)
+    int BVS;  // value columns per workgroup of the forward's segment-state pass
+    int BVSEG;  // value columns per workgroup of the backward's segment-state pass
     int BVD;  // value columns per workgroup of the dv walk
     int dv_split;  // 2: the dv walk takes each segment in two halves (from the midpoint states)
     int T, H, N, P, seg_len;
@@ -54,6 +55,8 @@ struct BwdLaunch {
     float* ws_gmid;    // [BH][P][K] fp32: that half's gate total (log2)
     float* ws_dgp;     // scalar gate: [K/BK][BH*T] fp32, each key block's sum of dg over its columns
     bool ckpt;         // ws_state already holds S_init(p) (a checkpointing forward's): only dS is combined
+    int dsub;          // 2 (checkpoint, dv walk in halves, even seg_len): ws_dstate holds [BH][2P][K][V],
+                       // the combined gradient at every half-segment end, and ws_gate [BH][2P][K]
     hipStream_t stream;
 };
 
