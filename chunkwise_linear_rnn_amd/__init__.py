@@ -25,7 +25,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgla.so")
+# GLA_LIBRARY selects another build of the same ABI (the host-sanitizer build
+# of the validation layer, whose launchers are stubs); default: libgla.so here.
+LIB_PATH = os.environ.get("GLA_LIBRARY") or os.path.join(_HERE, "libgla.so")
 
 GLA_DTYPE_FP32 = 0
 GLA_DTYPE_BF16 = 1

@@ -65,6 +65,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "libgla_hostsan.so")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The ABI layer (validation, launch plans, workspace sizes, launch recorder)
+    built by the host compiler with AddressSanitizer and UndefinedBehaviorSanitizer,
+    its kernel launchers replaced by host stubs that report hipErrorNoDevice
+    (``csrc/gla_host_stubs.cpp``).  No GPU code is compiled.  Load it in place
+    of libgla.so by setting GLA_LIBRARY to the returned path, in a process that
+    preloads the sanitizer runtime."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [os.path.join(CSRC, f) for f in ("gla_api.cpp", "gla_timing.cpp", "gla_host_stubs.cpp")]
+    tmp = SAN_LIB + ".tmp%d" % os.getpid()
+    cmd = (["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+            "-I", os.path.join(ROOT, "include")] + SANITIZE + srcs +
+           ["-L", "/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64", "-o", tmp])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitizer build failed:\n%s" % r.stderr)
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -28,25 +28,37 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile ``gla_oracle.c`` into ``liboracle.so`` with gcc (fp64, no fast-math)."""
-    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
-        return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+SAN_LIB_PATH = os.path.join(_HERE, "liboracle_hostsan.so")
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile ``gla_oracle.c`` into ``liboracle.so`` with gcc (fp64, no fast-math).
+    sanitize: ``liboracle_hostsan.so`` instead, with AddressSanitizer and
+    UndefinedBehaviorSanitizer (load it with GLA_ORACLE_LIBRARY in a process
+    that preloads the sanitizer runtime)."""
+    out = SAN_LIB_PATH if sanitize else _LIB_PATH
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(_SRC):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
            "-std=c99", "-o", tmp, _SRC, "-lm"]
+    if sanitize:
+        cmd[1:1] = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    path = os.environ.get("GLA_ORACLE_LIBRARY")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     L = ctypes.c_long
     lib.oracle_gla_fwd.argtypes = [L, L, L, L, L, dp, dp, dp, dp, dp, dp, dp]
