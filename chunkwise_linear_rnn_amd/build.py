@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgla.so")
 
 SOURCES = ["gla_api.cpp", "gla_timing.cpp", "gla_fwd.hip", "gla_fwd_wide.hip", "gla_bwd.hip", "gla_decode.hip",
-           "gla_gate.hip", "gla_bwd_general.hip", "gla_noalloc.hip"]
+           "gla_gate.hip", "gla_bwd_general.hip", "gla_noalloc.hip", "gla_split.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.  The

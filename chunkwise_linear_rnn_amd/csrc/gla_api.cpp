@@ -33,11 +33,12 @@ bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr
 
 // Head dims with kernel instantiations.  The limits come from the 160 KiB of
 // LDS per CU: fp32 tiles are twice the size of bf16 ones, and the backward
-// holds both the value and d_o tiles at full V.
+// holds both the value and d_o tiles at full V (its bf16 V = 512 runs as two
+// V = 256 column halves, bwd_split_launch).
 bool supported_kv(int64_t K, int64_t V, bool bf16, bool backward) {
     if (bf16) {
         const bool k_ok = K == 64 || K == 128 || K == 256;
-        const bool v_ok = V == 64 || V == 128 || V == 256 || (!backward && V == 512);
+        const bool v_ok = V == 64 || V == 128 || V == 256 || V == 512;
         return k_ok && v_ok;
     }
     return (K == 64 || K == 128) && (V == 64 || V == 128);
@@ -145,7 +146,7 @@ gla_status_t fwd_check(const gla_shape_t* shape, const void* q, const void* k, c
 // states: 16-bit inputs on the pipelined walks (K <= 128) with more than one
 // backward segment.  Returns the checkpoint's size in bytes, or 0.
 size_t ckpt_bytes(const gla::Shape& s) {
-    if (!s.bf16 || s.K > 128 || s.B * s.H == 0 || s.T == 0) return 0;
+    if (!s.bf16 || s.K > 128 || s.V > 256 || s.B * s.H == 0 || s.T == 0) return 0;
     const gla::Plan pb = gla::make_bwd_plan(s);
     return pb.P > 1 ? gla::state_bytes(s, pb) : 0;
 }
@@ -302,32 +303,12 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     return GLA_OK;
 }
 
-gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
-                      const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
-                      float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg,
-                      const void* ckpt = nullptr) {
-    g_detail.clear();
-    gla::Shape s;
-    gla_status_t st = check_shape(shape, &s, true);
-    if (st != GLA_OK) return st;
-    if (sg && !s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
-    const bool empty = s.B * s.H == 0 || s.T == 0;
-    if (!empty && (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg))
-        return fail(GLA_ERR_NULL, "q, k, v, g, d_o, dq, dk, dv and dg are required");
-    const void* ptrs[] = {q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace};
-    const char* names[] = {"q", "k", "v", "g", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "ds0", "workspace"};
-    for (int i = 0; i < 13; ++i)
-        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const size_t need = empty ? 0 : bwd_workspace_bytes(s, sg);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
-                    workspace ? "" : " (NULL)");
-    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+// The backward's launches for a validated, non-empty shape with V <= 256.
+hipError_t bwd_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g, const float* s0,
+                      const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg, float* ds0,
+                      void* workspace, bool sg, const void* ckpt, hipStream_t strm) {
     hipError_t err;
-    if (empty) {
-        // no tokens: dS_0 = dht (the state passes through unchanged)
-        err = ds0 ? gla::launch_state_copy(dht, ds0, s.B * s.H * s.K * s.V, strm) : hipSuccess;
-    } else {
+    {
         gla::BwdLaunch a{};
         gla::Plan p = gla::make_bwd_plan(s);
         a.bf16 = s.bf16;
@@ -389,6 +370,108 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
+    return err;
+}
+
+// V = 512 (16-bit): the recurrence acts on each value column independently,
+// so the backward is two V = 256 backwards over the column halves of v, d_o,
+// S_0, dht (gathered into the workspace), sharing q, k, g.  dv and dS_0 are
+// the halves side by side; dq, dk and dg are the sums of the halves' values
+// (half 0 writes the caller's buffers, half 1 the workspace, then one add).
+struct SplitLayout {
+    size_t vh, doh, dq1, dk1, dg1, dvh, s0h, dhth, ds0h, inner, total;
+};
+SplitLayout split_layout(const gla::Shape& s, bool sg) {
+    SplitLayout w{};
+    gla::Shape h = s;
+    h.V = s.V / 2;
+    const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.vh = take(BTH * h.V * 2);
+    w.doh = take(BTH * h.V * 2);
+    w.dq1 = take(BTH * s.K * 2);
+    w.dk1 = take(BTH * s.K * 2);
+    w.dg1 = take(BTH * (sg ? 1 : s.K) * 2);
+    w.dvh = take(BTH * h.V * 2);
+    w.s0h = take(BH * s.K * h.V * 4);
+    w.dhth = take(BH * s.K * h.V * 4);
+    w.ds0h = take(BH * s.K * h.V * 4);
+    w.inner = take(bwd_workspace_bytes(h, sg));
+    w.total = at;
+    return w;
+}
+
+hipError_t bwd_split_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                            const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                            float* ds0, void* workspace, bool sg, hipStream_t strm) {
+    const SplitLayout L = split_layout(s, sg);
+    gla::Shape h = s;
+    h.V = s.V / 2;
+    char* ws = static_cast<char*>(workspace);
+    const long W = h.V, VT = s.V;
+    const long rows_t = s.B * s.T * s.H, rows_s = s.B * s.H * s.K;
+    const long n_k = rows_t * s.K, n_g = rows_t * (sg ? 1 : s.K);
+    hipError_t err = hipSuccess;
+    for (int half = 0; half < 2 && err == hipSuccess; ++half) {
+        const long off = half * W;
+        err = gla::launch_copy_cols(true, v, VT, off, ws + L.vh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, d_o, VT, off, ws + L.doh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && s0) err = gla::launch_copy_cols(false, s0, VT, off, ws + L.s0h, W, 0, W, rows_s, strm);
+        if (err == hipSuccess && dht)
+            err = gla::launch_copy_cols(false, dht, VT, off, ws + L.dhth, W, 0, W, rows_s, strm);
+        if (err != hipSuccess) break;
+        err = bwd_launch(h, q, k, ws + L.vh, g, s0 ? (const float*)(ws + L.s0h) : nullptr, ws + L.doh,
+                         dht ? (const float*)(ws + L.dhth) : nullptr, half ? ws + L.dq1 : dq, half ? ws + L.dk1 : dk,
+                         ws + L.dvh, half ? ws + L.dg1 : dg, ds0 ? (float*)(ws + L.ds0h) : nullptr, ws + L.inner, sg,
+                         nullptr, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dvh, W, 0, dv, VT, off, W, rows_t, strm);
+        if (err == hipSuccess && ds0)
+            err = gla::launch_copy_cols(false, ws + L.ds0h, W, 0, ds0, VT, off, W, rows_s, strm);
+    }
+    if (err == hipSuccess) err = gla::launch_add_into(dq, ws + L.dq1, n_k, strm);
+    if (err == hipSuccess) err = gla::launch_add_into(dk, ws + L.dk1, n_k, strm);
+    if (err == hipSuccess) err = gla::launch_add_into(dg, ws + L.dg1, n_g, strm);
+    return err;
+}
+
+bool split_bwd(const gla::Shape& s) { return s.bf16 && s.V == 512; }
+
+size_t bwd_total_bytes(const gla::Shape& s, bool sg) {
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    return split_bwd(s) ? split_layout(s, sg).total : bwd_workspace_bytes(s, sg);
+}
+
+gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                      const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                      float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg,
+                      const void* ckpt = nullptr) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, true);
+    if (st != GLA_OK) return st;
+    if (sg && !s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
+    const bool empty = s.B * s.H == 0 || s.T == 0;
+    if (!empty && (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg))
+        return fail(GLA_ERR_NULL, "q, k, v, g, d_o, dq, dk, dv and dg are required");
+    const void* ptrs[] = {q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace};
+    const char* names[] = {"q", "k", "v", "g", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "ds0", "workspace"};
+    for (int i = 0; i < 13; ++i)
+        if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t need = bwd_total_bytes(s, sg);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (empty) {
+        // no tokens: dS_0 = dht (the state passes through unchanged)
+        err = ds0 ? gla::launch_state_copy(dht, ds0, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else if (split_bwd(s)) {
+        err = bwd_split_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, strm);
+    } else {
+        err = bwd_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, ckpt, strm);
+    }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
 }
@@ -423,13 +506,13 @@ size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
 size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
     if (check_shape(shape, &s, true) != GLA_OK) return 0;
-    return bwd_workspace_bytes(s, false);
+    return bwd_total_bytes(s, false);
 }
 
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
     if (check_shape(shape, &s, true) != GLA_OK || !s.bf16) return 0;
-    return bwd_workspace_bytes(s, true);
+    return bwd_total_bytes(s, true);
 }
 
 gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

@@ -1,0 +1,74 @@
+// Column-half plumbing of the backward at value width 512 (16-bit inputs).
+//
+// The recurrence of Section 4.1, Eq. 3 acts on each value column of the state
+// independently: column j of S_t depends only on column j of v and of S_0.  A
+// head with V = 512 is therefore two heads with V = 256 that share q, k and g;
+// their gradients dv and dS_0 are the two halves side by side, and dq, dk and
+// dg (whose closed form of Section 4.3 is linear in the per-half terms) are the
+// sums of the two halves' values.  These kernels move the halves in and out of
+// contiguous buffers and add them.
+#include <hip/hip_runtime.h>
+
+#include "gla_device.hpp"
+#include "gla_launch.hpp"
+#include "gla_timing.hpp"
+
+namespace gla {
+
+// dst[r][off_d + c] = src[r][off_s + c] for c < W, r < rows; W, offsets and row
+// strides in elements, all multiples of 16 bytes.
+template <typename T>
+__global__ void __launch_bounds__(256)
+gla_copy_cols(const T* __restrict__ src, long ld_s, long off_s, T* __restrict__ dst, long ld_d, long off_d, long W,
+              long rows) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const long per_row = W / VEC;
+    const long n = rows * per_row;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        const long r = i / per_row, c = (i % per_row) * VEC;
+        *reinterpret_cast<u32x4*>(dst + r * ld_d + off_d + c) = *reinterpret_cast<const u32x4*>(src + r * ld_s + off_s + c);
+    }
+}
+
+// a[i] = a[i] + b[i] in fp32, rounded once to T; n a multiple of 8.
+template <typename T>
+__global__ void __launch_bounds__(256)
+gla_add_into(T* __restrict__ a, const T* __restrict__ b, long n) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * VEC; i < n; i += (long)gridDim.x * 256 * VEC) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(a + i);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(b + i);
+        T* xv = reinterpret_cast<T*>(&x);
+        const T* yv = reinterpret_cast<const T*>(&y);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xv[e] = Elem<T>::from_f(Elem<T>::to_f(xv[e]) + Elem<T>::to_f(yv[e]));
+        *reinterpret_cast<u32x4*>(a + i) = x;
+    }
+}
+
+static unsigned grid_for(long work) {
+    const long g = (work + 255) / 256;
+    return (unsigned)(g < 2048 ? (g > 0 ? g : 1) : 2048);
+}
+
+hipError_t launch_copy_cols(bool bf16, const void* src, long ld_s, long off_s, void* dst, long ld_d, long off_d, long W,
+                            long rows, hipStream_t stream) {
+    if (rows <= 0 || W <= 0) return hipSuccess;
+    const int vec = bf16 ? 8 : 4;
+    const unsigned g = grid_for(rows * (W / vec));
+    if (bf16)
+        GLA_LAUNCH("copy_cols", gla_copy_cols<__bf16>, dim3(g), dim3(256), stream, (const __bf16*)src, ld_s, off_s,
+                   (__bf16*)dst, ld_d, off_d, W, rows);
+    else
+        GLA_LAUNCH("copy_cols", gla_copy_cols<float>, dim3(g), dim3(256), stream, (const float*)src, ld_s, off_s,
+                   (float*)dst, ld_d, off_d, W, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_into(void* a, const void* b, long n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    GLA_LAUNCH("add_halves", gla_add_into<__bf16>, dim3(grid_for(n / 8)), dim3(256), stream, (__bf16*)a, (const __bf16*)b, n);
+    return hipGetLastError();
+}
+
+}  // namespace gla

@@ -40,7 +40,8 @@
  *      Eq. 1).  Violations give unspecified values, never an out-of-bounds
  *      access.
  *  Supported sizes: chunk == 64; T a multiple of 64; bf16: K in
- *      {64, 128, 256} and V in {64, 128, 256, 512} (backward: V <= 256);
+ *      {64, 128, 256} and V in {64, 128, 256, 512} (the backward runs V = 512
+ *      as two V = 256 column halves: the recurrence never mixes value columns);
  *      fp32: K and V in {64, 128}.  B, H >= 0 and T >= 0; B*H == 0 or T == 0
  *      is a valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
  */
@@ -163,9 +164,9 @@ size_t gla_bwd_workspace_size(const gla_shape_t* shape);
  *   gla_ckpt_size(shape) : bytes of the checkpoint, [B,H,P,K,V] in the
  *     token dtype (P = the backward's segment count; entry 0 of each head is
  *     not written: segment 0 starts from s0).  0 when the shape has no
- *     checkpoint: fp32 inputs, K = 256, a single segment, or an invalid or
- *     empty shape; both calls then behave exactly like gla_fwd / gla_bwd and
- *     ckpt may be NULL.  The shape must also be a valid backward shape.
+ *     checkpoint: fp32 inputs, K = 256, V = 512, a single segment, or an
+ *     invalid or empty shape; both calls then behave exactly like gla_fwd /
+ *     gla_bwd and ckpt may be NULL.  The shape must be a valid backward shape.
  *   gla_fwd_ckpt : gla_fwd (same arguments, results and workspace), plus
  *     writes ckpt (device, caller-owned, 16-byte aligned).
  *   gla_bwd_ckpt : gla_bwd (same arguments, results and workspace), plus

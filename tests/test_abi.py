@@ -276,7 +276,8 @@ def test_ckpt_entry_points_validate(L):
     assert size(_shape(dtype=gla.GLA_DTYPE_FP32)) == 0  # fp32: no checkpoint
     assert size(_shape(K=256, V=256, T=8192)) == 0      # wide heads: no checkpoint
     assert size(_shape(B=1, H=1, T=64)) == 0            # one segment
-    assert size(_shape(V=512, T=8192)) == 0             # not a backward shape
+    assert size(_shape(V=512, T=8192)) == 0             # V = 512: the column-half backward, no checkpoint
+    assert size(_shape(V=1024, T=8192)) == 0            # not a backward shape
     fwd = lambda shape, ck=P: L.gla_fwd_ckpt(ctypes.byref(shape), P, P, P, P, None, P, None, ck, P, 1 << 40, None)
     bwd = lambda shape, ck=P: L.gla_bwd_ckpt(ctypes.byref(shape), P, P, P, P, None, ck, P, None, P, P, P, P, None,
                                              P, 1 << 40, None)
@@ -285,4 +286,5 @@ def test_ckpt_entry_points_validate(L):
     assert fwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
     assert bwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
     assert fwd(_shape(T=100)) == ERR_SHAPE
-    assert bwd(_shape(V=512)) == ERR_UNSUPPORTED
+    assert bwd(_shape(V=1024)) == ERR_UNSUPPORTED
+    assert bwd(_shape(K=256, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED

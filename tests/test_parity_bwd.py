@@ -162,3 +162,25 @@ def test_exact_path_deterministic():
     for a, b in zip(*outs):
         assert torch.equal(a, b)
     _check_bwd(w, inputs=inp)
+
+
+@pytest.mark.parametrize("K,T,s0,dht", [(64, 192, "normal0.1", True), (128, 256, "none", True),
+                                       (256, 320, "normal0.1", False)])
+def test_bwd_value_width_512(K, T, s0, dht):
+    # V = 512 runs as two V = 256 backwards over the value-column halves
+    # (the recurrence never mixes value columns); dq, dk, dg add the halves
+    w = gi.custom(1, 2, T, K, 512, dtype="bf16", gate="lowrank", s0=s0, backward=True, seed=600 + K + T)
+    _check_bwd(w, with_dht=dht)
+
+
+def test_bwd_value_width_512_exact_path():
+    from tests.test_parity_fwd import exact_path_inputs
+    w = gi.custom(1, 2, 256, 128, 512, dtype="bf16", gate="iid", s0="normal0.1", backward=True, seed=611)
+    _check_bwd(w, inputs=exact_path_inputs(w))
+
+
+def test_bwd_1p3b_head_shape_sampled_heads():
+    # the 1.3B-model head shape at length 8K (the gla_1p3b_long recipe and seed,
+    # with an upstream gradient drawn as well), two heads against the oracle
+    w = gi.custom(2, 4, 8192, 256, 512, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=4)
+    _check_bwd(w, heads=[(0, 1), (1, 3)])
