@@ -310,6 +310,40 @@ def summarize_pmc(csv_path, trace_csv, out_md, title, command):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def summarize_stalls(csv_path, out_md, title, command):
+    """Where the waves of each kernel spend their time, from one rocprofv3 pass
+    of SQ counters (all per-SE sums; the ratios divide like units): the share
+    of wave cycles spent waiting (SQ_WAIT_ANY) and waiting on LDS issue
+    (SQ_WAIT_INST_LDS), LDS-active cycles per CU-busy cycle, and the bank
+    conflict share of LDS-active cycles."""
+    acc = {}
+    for (_, name), d in _counter_rows(csv_path).items():
+        if "3gla" not in name:
+            continue
+        a = acc.setdefault(name, {})
+        for k, v in d.items():
+            a[k] = a.get(k, 0.0) + v
+    names = list(acc)
+    dem = dict(zip(names, _demangle(names)))
+    lines = ["# Wave stalls and LDS use: %s (MI355X, rocprofv3 --pmc)" % title, "",
+             "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "", "    " + command, "",
+             "wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles); wait on LDS = SQ_WAIT_INST_LDS / "
+             "SQ_WAVE_CYCLES; LDS busy = SQ_LDS_IDX_ACTIVE / (4 x SQ_BUSY_CU_CYCLES); conflicts = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; VALU = SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES (quad-cycles "
+             "both).", "",
+             "| kernel | launch name | wait | wait on LDS | LDS busy | LDS conflicts | VALU |", "|---|---|---|---|---|---|---|"]
+    for n in names:
+        d = acc[n]
+        wave = max(1.0, d.get("SQ_WAVE_CYCLES", 0.0))
+        busy = max(1.0, 4 * d.get("SQ_BUSY_CU_CYCLES", 0.0))
+        lds = d.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        lines.append("| %s | %s | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+            _short(dem[n]), LAUNCH_LABEL.get(_kernel_base(n), "-"), d.get("SQ_WAIT_ANY", 0.0) / wave,
+            d.get("SQ_WAIT_INST_LDS", 0.0) / wave, lds / busy, d.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(1.0, lds),
+            d.get("SQ_ACTIVE_INST_VALU", 0.0) / wave))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -645,6 +679,8 @@ def main():
                     help="write profiles/traffic_<workload>.json/.md from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("COUNTER_CSV", "KERNEL_STATS_CSV", "OUT_MD"),
                     help="write a profiles/ summary of MFMA / LDS counters")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
+                    help="write a profiles/ summary of wave-stall and LDS counters")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the input files, quoted in the summary")
@@ -654,6 +690,10 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.title or args.workload,
                         " && ".join(args.command))
+        return
+    if args.summarize_stalls:
+        summarize_stalls(args.summarize_stalls[0], args.summarize_stalls[1], args.title or args.workload,
+                         " && ".join(args.command))
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summarize_pmc[2],
