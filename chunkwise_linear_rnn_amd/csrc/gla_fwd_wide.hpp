@@ -695,7 +695,21 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= f;
         }
         if constexpr (OUT && GEN && HS) {
-            if (c + 1 < c_end) S.store(hs_out + ((long)bh * N + c + 1) * KD * V, V, col0);
+            if (c + 1 < c_end) {
+                // the lane's offset is formed here, behind an empty asm: hoisted out
+                // of the chunk loop, the store's addresses would stay live (and spill)
+                int lo = 4 * (l >> 4) * V + col0 + (l & 15);
+                int vs = V;
+                asm volatile("" : "+v"(lo), "+s"(vs));
+                T* dst = hs_out + ((long)bh * N + c + 1) * KD * V + lo;
+#pragma unroll
+                for (int a = 0; a < KD / 16; ++a)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            dst[(16 * a + r) * vs + 16 * cb] = Elem<T>::from_f(S.s[a][cb][r]);
+            }
         }
         __syncthreads();  // E: buffer bf may be refilled
     }
