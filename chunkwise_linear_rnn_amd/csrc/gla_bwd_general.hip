@@ -7,8 +7,10 @@
 //   dS, the gradient with respect to S_t, runs backwards in time:
 //        dS_t = q_t^T do_t + (alpha_{t+1}^T beta_{t+1}) * dS_{t+1},  dS_{T-1} also + dht,
 //        a general recurrence over the reversed sequence with keys q, values do
-//        and the gates shifted by one token; dv_t = k_t dS_t is its output for
-//        queries k, and its final state gives dS_0 = (alpha_0^T beta_0) * dS_0';
+//        and the gates shifted by one token (run in place: the general
+//        forward's kernels read token T-1-t and write row T-1-t); dv_t = k_t dS_t
+//        is its output for queries k, and its final state gives
+//        dS_0 = (alpha_0^T beta_0) * dS_0';
 //   dk_t = v_t dS_t^T: the same reversed recurrence for dS^T, queries v.
 // The gate gradients take the closed forms (GLA paper Section 4.3 and the
 // appendix general form), reverse cumulative sums of q*dq - k*dk and
@@ -22,22 +24,6 @@
 #include "gla_timing.hpp"
 
 namespace gla {
-
-// out[b][t] = in[b][T-1-t] (shift = 0) or in[b][T-t] with a zero row at t = 0
-// (shift = 1), rows of W elements (W a multiple of 8), one 16-byte vector per thread.
-__global__ void __launch_bounds__(256)
-gla_flip_rows(const bf16* __restrict__ in, bf16* __restrict__ out, int T, int W, int shift) {
-    const long nvec = (long)W / 8;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (long)T * nvec) return;
-    const long b = blockIdx.y;
-    const int t = (int)(e / nvec);
-    const long vi = e % nvec;
-    const int src = shift ? T - t : T - 1 - t;
-    u32x4 x = u32x4{0u, 0u, 0u, 0u};
-    if (src < T) x = *reinterpret_cast<const u32x4*>(in + (b * T + src) * (long)W + vi * 8);
-    *reinterpret_cast<u32x4*>(out + (b * T + t) * (long)W + vi * 8) = x;
-}
 
 // dst[bh][j][i] = src[bh][i][j] for [BH][K][V] fp32 states
 __global__ void __launch_bounds__(256)
@@ -162,7 +148,7 @@ gla_gate_grad_out(const bf16* __restrict__ a, const bf16* __restrict__ da, const
 
 static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void* q, const void* k, const void* v,
                                   const void* g, const void* h, const float* s0, void* o, float* s_final, char* ws,
-                                  void* hs, hipStream_t stream) {
+                                  void* hs, int rev, hipStream_t stream) {
     Shape s{B, T, H, K, V, true};
     Plan p = make_fwd_general_plan(s);
     FwdLaunch a{};
@@ -178,6 +164,7 @@ static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void*
     }
     a.ws_rec = ws + fwd_general_seg_bytes(s, p);
     a.ws_hs = hs;
+    a.rev = rev;
     a.stream = stream;
     return a;
 }
@@ -191,14 +178,6 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     float* st = reinterpret_cast<float*>(ws + w.st);
     float* s0T = L.s0 ? reinterpret_cast<float*>(ws + w.s0t) : nullptr;
     float* dhtT = L.dht ? reinterpret_cast<float*>(ws + w.dhtt) : nullptr;
-    bf16* qr = reinterpret_cast<bf16*>(ws + w.qr);
-    bf16* kr = reinterpret_cast<bf16*>(ws + w.kr);
-    bf16* vr = reinterpret_cast<bf16*>(ws + w.vr);
-    bf16* dor = reinterpret_cast<bf16*>(ws + w.dor);
-    bf16* gs = reinterpret_cast<bf16*>(ws + w.gs);
-    bf16* hs = reinterpret_cast<bf16*>(ws + w.hs);
-    bf16* dvr = reinterpret_cast<bf16*>(ws + w.dvr);
-    bf16* dkr = reinterpret_cast<bf16*>(ws + w.dkr);
     bf16* hsf = reinterpret_cast<bf16*>(ws + w.hsf);
     bf16* hsr = reinterpret_cast<bf16*>(ws + w.hsr);
     float* ag = reinterpret_cast<float*>(ws + w.ag);
@@ -209,36 +188,25 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     const long nst = BH * KV;
     const unsigned gst = (unsigned)((nst + 255) / 256);
     // forward (o, S_T) and the transposed initial / final-state gradient
-    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, o, st, fws, hsf, sm));
+    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, o, st, fws, hsf, 0, sm));
     if (err != hipSuccess) return err;
     if (L.s0) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.s0, s0T, K, V, nst);
     if (L.dht) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.dht, dhtT, K, V, nst);
     // dq: the transposed state's forward
-    err = launch_fwd_general(general_fwd_args(B, T, H, V, K, L.d_o, L.v, L.k, L.h, L.g, s0T, L.dq, nullptr, fws, nullptr, sm));
+    err = launch_fwd_general(
+        general_fwd_args(B, T, H, V, K, L.d_o, L.v, L.k, L.h, L.g, s0T, L.dq, nullptr, fws, nullptr, 0, sm));
     if (err != hipSuccess) return err;
-    // reversed inputs, gates shifted by one token
-    auto flip = [&](const void* in, bf16* out, int W, int shift) {
-        const long nvec = (long)T * H * W / 8;
-        GLA_LAUNCH("bwdg_flip", gla_flip_rows, dim3((unsigned)((nvec + 255) / 256), (unsigned)B), dim3(256), sm,
-                   (const bf16*)in, out, T, H * W, shift);
-    };
-    flip(L.q, qr, K, 0);
-    flip(L.k, kr, K, 0);
-    flip(L.v, vr, V, 0);
-    flip(L.d_o, dor, V, 0);
-    flip(L.g, gs, K, 1);
-    flip(L.h, hs, V, 1);
-    // dv (reversed) and dS_0' from the reversed recurrence of dS
+    // dv and dS_0' from the time-reversed recurrence of dS (its gates one token
+    // later), read and written in place in the input's token order
     float* ds0 = L.ds0;
-    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, kr, qr, dor, gs, hs, L.dht, dvr, ds0, fws, hsr, sm));
+    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.k, L.q, L.d_o, L.g, L.h, L.dht, L.dv, ds0, fws, hsr, 1, sm));
     if (err != hipSuccess) return err;
     if (ds0) GLA_LAUNCH("bwdg_scale_ds0", gla_scale_ds0, dim3(gst), dim3(256), sm, ds0, (const bf16*)L.g,
                         (const bf16*)L.h, T, H, K, V, nst);
-    // dk (reversed) from the reversed recurrence of dS^T
-    err = launch_fwd_general(general_fwd_args(B, T, H, V, K, vr, dor, qr, hs, gs, dhtT, dkr, nullptr, fws, nullptr, sm));
+    // dk from the time-reversed recurrence of dS^T
+    err = launch_fwd_general(
+        general_fwd_args(B, T, H, V, K, L.v, L.d_o, L.q, L.h, L.g, dhtT, L.dk, nullptr, fws, nullptr, 1, sm));
     if (err != hipSuccess) return err;
-    flip(dvr, static_cast<bf16*>(L.dv), V, 0);
-    flip(dkr, static_cast<bf16*>(L.dk), K, 0);
     // gate gradients: anchors at the chunk boundaries, then each chunk's reverse sums
     const unsigned N = (unsigned)(T / 64);
     {

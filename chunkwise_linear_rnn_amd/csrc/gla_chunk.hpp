@@ -235,13 +235,16 @@ __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSl
 // in a fixed order, so each entry is written once by one lane and the result
 // does not depend on timing.  q, k rows at qrow/krow (row stride rs, column 0 of
 // the head), the log gate at grow: per column with stride rs, or SG one value
-// per token with stride rsG.  Token s's values reach the lanes by shuffle.
+// per token with stride rsG (strides may be negative: rows taken in reverse
+// time order).  zero_g0: token 0's gate is zero and not read (a time-reversed
+// sequence whose first step has no decay).  Token s's values reach the lanes
+// by shuffle.
 // Not inlined: this rarely taken branch would otherwise change the register
 // allocation and schedule of the walk's main loop (2-3 us per launch).
 template <typename T, int KD, int NW, bool SG>
 __device__ __attribute__((noinline)) void exact_intra_tile(float* Af, int pF, const T* __restrict__ qrow,
                                                  const T* __restrict__ krow, const T* __restrict__ grow, int rs,
-                                                 int rsG, int w) {
+                                                 int rsG, int w, bool zero_g0 = false) {
     constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int NS = kChunk / NW;  // key tokens per wave
     const int l = lane_id();
@@ -249,7 +252,8 @@ __device__ __attribute__((noinline)) void exact_intra_tile(float* Af, int pF, co
 #pragma unroll
     for (int u = 0; u < NS; ++u) part[u] = 0.f;
     float b0 = 0.f;
-    if constexpr (SG) b0 = wave_incl_scan(Elem<T>::to_f(grow[l * rsG]) * kLog2e);
+    const bool z0 = zero_g0 && l == 0;  // token 0's gate is zero and lies outside the tensor
+    if constexpr (SG) b0 = wave_incl_scan(z0 ? 0.f : Elem<T>::to_f(grow[l * rsG]) * kLog2e);
     for (int j0 = 0; j0 < KD; j0 += VEC) {
         RowSlab<T, VEC> xq, xk;
         xq.load(qrow, rs, j0);
@@ -260,7 +264,7 @@ __device__ __attribute__((noinline)) void exact_intra_tile(float* Af, int pF, co
             for (int j = 0; j < VEC; ++j) bt[j] = b0;
         } else {
             RowSlab<T, VEC> xg;
-            xg.load(grow, rs, j0);
+            xg.load_unless(grow, rs, j0, z0);
 #pragma unroll
             for (int j = 0; j < VEC; ++j) bt[j] = xg.get(j) * kLog2e;
             wave_incl_scan_n<VEC>(bt);

@@ -196,6 +196,16 @@ struct RowSlab {
 #pragma unroll
         for (int m = 0; m < NV; ++m) r[m] = *reinterpret_cast<const u32x4*>(p + m * VEC);
     }
+    // load, except that the lanes with `skip` set read nothing and hold zeros
+    // (a row that lies outside the tensor and stands for a zero row)
+    __device__ __forceinline__ void load_unless(const T* __restrict__ base, int rs, int c0, bool skip) {
+        if (skip) {
+#pragma unroll
+            for (int m = 0; m < NV; ++m) r[m] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            load(base, rs, c0);
+        }
+    }
     // only the 16-byte vectors m0 .. m1-1 (columns c0 + m*VEC ..)
     __device__ __forceinline__ void load_part(const T* __restrict__ base, int rs, int c0, int m0, int m1) {
         const T* p = base + (lane_id() * rs + c0);

@@ -98,10 +98,10 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
     const int nvb = a.V / BV;
     unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);
     GLA_LAUNCH("fwd_prep", (gla_fwd_wide_prep<T, KD, false>), dim3((unsigned)(a.BH * a.N)), dim3(256), a.stream,
-               (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N, (long)GenRec<KD>::bytes(a.V));
+               (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N, (long)GenRec<KD>::bytes(a.V), a.rev);
     GLA_LAUNCH("fwd_general_vprep", (gla_fwd_general_vprep<T, KD, VP>),
                dim3((unsigned)(a.BH * a.N), (unsigned)(a.V / VP)), dim3(256), a.stream, (const T*)a.v,
-               (const T*)a.h, rec, a.T, a.H, a.V, a.N);
+               (const T*)a.h, rec, a.T, a.H, a.V, a.N, a.rev);
     if (a.P > 1) {
         const int nseg = a.P - 1;
         GLA_LAUNCH("fwd_general_seg_state", (gla_fwd_wide_walk<T, KD, BV, false, true>),
@@ -114,11 +114,21 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
                    a.V, a.P);
     }
     const dim3 gw((unsigned)xcd_grid(a.P * a.BH, nvb));
-    if (a.ws_hs)
+    if (a.ws_hs && a.rev)
+        GLA_LAUNCH("fwd_general_walk_hs", (gla_fwd_wide_walk<T, KD, BV, true, true, true, true>), gw, dim3(512),
+                   a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,
+                   a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH,
+                   (float*)nullptr, (T*)a.ws_hs);
+    else if (a.ws_hs)
         GLA_LAUNCH("fwd_general_walk_hs", (gla_fwd_wide_walk<T, KD, BV, true, true, true>), gw, dim3(512), a.stream,
                    (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final,
                    (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr,
                    (T*)a.ws_hs);
+    else if (a.rev)
+        GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true, false, true>), gw, dim3(512),
+                   a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,
+                   a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH,
+                   (float*)nullptr, (T*)nullptr);
     else
         GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true>), gw, dim3(512), a.stream,
                    (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final,

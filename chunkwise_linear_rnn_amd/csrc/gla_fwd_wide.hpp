@@ -88,10 +88,14 @@ struct WidePrepSmem {
 };
 
 // One workgroup (four waves, 64 key columns each) per chunk and head.
+// rev (general gates, per-column g): the records of the time-reversed
+// sequence, whose token t is the input's token T-1-t and whose gate at t is the
+// input's gate of token T-t (none at t = 0): chunk c reads the input's rows
+// T-1-64c down to T-64-64c, its gates one token later, in place.
 template <typename T, int KD, bool SG>
 __global__ void __launch_bounds__(256)
 gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
-                  unsigned char* __restrict__ rec, int T_, int H, int N, long rstride) {
+                  unsigned char* __restrict__ rec, int T_, int H, int N, long rstride, int rev = 0) {
     constexpr int NW = 4, NT = NW * 64, CPK = KD / NW, VEC = 16 / (int)sizeof(T), VPR = KD / VEC;
     static_assert(CPK <= 64 && (kChunk * VPR) % NT == 0, "prep tiling");
     using Sm = WidePrepSmem<T, KD>;
@@ -101,19 +105,26 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     const long unit = blockIdx.x;  // bh * N + chunk; the grid has exactly BH * N blocks
     const int bh = (int)(unit / N), c = (int)(unit % N);
     const int b = bh / H, h = bh % H;
-    const int rsK = H * KD, rsG = SG ? H : rsK;
-    const long row0 = (long)b * T_ + (long)c * kChunk;
-    const T* qb = q + row0 * rsK + (long)h * KD;
-    const T* kb = k + row0 * rsK + (long)h * KD;
+    const bool rv = !SG && rev;
+    const int rsK = rv ? -H * KD : H * KD, rsG = SG ? H : rsK;
+    // input rows of the chunk's token 0 (q, k) and of its gate
+    const long row0 = rv ? (long)b * T_ + T_ - 1 - (long)c * kChunk : (long)b * T_ + (long)c * kChunk;
+    const long rowg = rv ? row0 + 1 : row0;
+    const bool zg0 = rv && c == 0;  // the reversed sequence's token 0 has no gate
+    const T* qb = q + row0 * (H * KD) + (long)h * KD;
+    const T* kb = k + row0 * (H * KD) + (long)h * KD;
     // g: per key column [B,T,H,K], or (SG) one value per token and head [B,T,H]
-    const T* gb = SG ? g + row0 * H + h : g + row0 * rsK + (long)h * KD;
+    const T* gb = SG ? g + rowg * H + h : g + rowg * (H * KD) + (long)h * KD;
     const int kc0 = w * CPK;
 
     RowSlab<T, CPK> rq, rk;
     GateSlab<T, CPK, SG> rg;
     rq.load(qb, rsK, kc0);
     rk.load(kb, rsK, kc0);
-    rg.load(gb, rsG, kc0);
+    if constexpr (SG)
+        rg.load(gb, rsG, kc0);
+    else
+        rg.load_unless(gb, rsG, kc0, zg0 && l == 0);
     if (tid == 0) sm.buf.flag[0] = 0;
     __syncthreads();
     pipe_prep<T, CPK>(sm.buf, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, CPK / VEC);
@@ -187,7 +198,7 @@ gla_fwd_wide_prep(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         // to the record every thread has finished at this barrier
         __syncthreads();
         float* Af = reinterpret_cast<float*>(sm.buf.Ql);
-        exact_intra_tile<T, KD, NW, SG>(Af, Sm::pF, qb, kb, gb, rsK, rsG, w);
+        exact_intra_tile<T, KD, NW, SG>(Af, Sm::pF, qb, kb, gb, rsK, rsG, w, zg0);
         __syncthreads();
         for (int e = tid; e < kChunk * kChunk; e += NT) {
             const int t = e / kChunk, s = e % kChunk;
@@ -217,11 +228,12 @@ struct GenPrepSmem {
 //   Oi[t][j] = sum_{s <= t} A[t][s] v[s][j] exp2(C_t[j] - C_s[j])
 // formed as exp2(C_t) * (A (v * exp2(-C))) on the matrix cores, or element by
 // element when some column's C_63 leaves the basis range (exp2(-C) would not
-// stay a well-scaled fp32/bf16 value).
+// stay a well-scaled fp32/bf16 value).  rev: the time-reversed sequence, read in
+// place as gla_fwd_wide_prep reads it (values at token T-1-t, gates at T-t).
 template <typename T, int KD, int VP>
 __global__ void __launch_bounds__(256)
 gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigned char* __restrict__ rec, int T_,
-                      int H, int V, int N) {
+                      int H, int V, int N, int rev = 0) {
     constexpr int NW = 4, NT = NW * 64;
     constexpr int CV = VP / 8, NPART = NT / CV, TPP = kChunk / NPART;  // column vectors, token parts, tokens per part
     constexpr int CB2 = VP / NW / 16;                                  // 16-column blocks per wave in the output product
@@ -235,7 +247,10 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
     const int bh = (int)(unit / N), c = (int)(unit % N);
     const int b = bh / H, h = bh % H;
     const int rsV = H * V;
-    const long row0 = (long)b * T_ + (long)c * kChunk;
+    // input rows of the chunk's token 0 (v) and of its gate, and the row step
+    const long row0 = rev ? (long)b * T_ + T_ - 1 - (long)c * kChunk : (long)b * T_ + (long)c * kChunk;
+    const long rowh = rev ? row0 + 1 : row0;
+    const long rstep = rev ? -(long)rsV : (long)rsV;
     unsigned char* r = rec + unit * G::bytes(V);
     {
         const T* a = reinterpret_cast<const T*>(r + G::oA);
@@ -254,12 +269,15 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
     const int cv = tid % CV, part = tid / CV, t0 = part * TPP, jv = 8 * cv;
     const int jj = tid % VP, epart = tid / VP;  // element-wise path: column jj, tokens epart + k * (NT / VP)
     {
-        const long gofs = row0 * rsV + (long)h * V + j0 + jv;
+        const long cofs = (long)h * V + j0 + jv;
         u32x4 hraw[TPP], vraw[TPP];
 #pragma unroll
         for (int i = 0; i < TPP; ++i) {
-            hraw[i] = *reinterpret_cast<const u32x4*>(hg + gofs + (long)(t0 + i) * rsV);
-            vraw[i] = *reinterpret_cast<const u32x4*>(v + gofs + (long)(t0 + i) * rsV);
+            // the reversed sequence's token 0 has no gate (its row lies past the input)
+            const bool nog = rev && c == 0 && t0 + i == 0;
+            hraw[i] = nog ? u32x4{0u, 0u, 0u, 0u}
+                          : *reinterpret_cast<const u32x4*>(hg + rowh * rsV + cofs + (long)(t0 + i) * rstep);
+            vraw[i] = *reinterpret_cast<const u32x4*>(v + row0 * rsV + cofs + (long)(t0 + i) * rstep);
         }
         float cl[TPP][8];
 #pragma unroll
@@ -407,8 +425,10 @@ struct WideSmem {
 // output is (Ql S) * exp2(C_t) plus the record's intra-chunk output, and the
 // state's columns decay by exp2(C_63) as its rows do by the key-side gate; the
 // state pass also writes the segment's column log2 decays to ws_gateb, and the
-// output walk with HS the state before every chunk to hs_out.
-template <typename T, int KD, int BV, bool OUT, bool GEN = false, bool HS = false>
+// output walk with HS the state before every chunk to hs_out.  REV (GEN output
+// walk): the records are those of the time-reversed sequence, and the output
+// of its token t goes to row T-1-t.
+template <typename T, int KD, int BV, bool OUT, bool GEN = false, bool HS = false, bool REV = false>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
@@ -603,8 +623,11 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
         if constexpr (OUT && GEN) {
             // O = (Ql S) * exp2(C_t) + the record's intra-chunk output; slot e:
-            // column 16cb + 4(l/16) + e of the slice, token 16rb + l%16
-            T* obase = o + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0;
+            // column 16cb + 4(l/16) + e of the slice, token 16rb + l%16 (REV:
+            // the time-reversed sequence's token, written to row T-1-t)
+            const long orow = REV ? (long)b * T_ + T_ - 1 - (long)c * kChunk : (long)b * T_ + (long)c * kChunk;
+            const int ostep = REV ? -rsV : rsV;
+            T* obase = o + orow * rsV + (long)h * V + col0;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -614,7 +637,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         o4[e] = acc[rb][cb][e] * Elem<T>::to_f(csr[rb][cb][e]) + Elem<T>::to_f(oir[rb][cb][e]);
-                    *reinterpret_cast<vec4_t<T>*>(obase + t * rsV + jc) = to_vec4<T>(o4);
+                    *reinterpret_cast<vec4_t<T>*>(obase + t * ostep + jc) = to_vec4<T>(o4);
                 }
         } else if constexpr (OUT) {
             // O^T[j][t] += sum_s V[s][j] A[t][s]

@@ -27,6 +27,8 @@ struct FwdLaunch {
     const void* h;    // general gates: log beta, [B,T,H,V] (null otherwise)
     float* ws_gateb;  // general gates: [BH][P][V] fp32 (log2 of the segment's column decay)
     void* ws_hs;      // general gates, optional: the state before every chunk, [BH][N][K][V] bf16
+    int rev;          // general gates: run the time-reversed sequence in place (token t = input token T-1-t,
+                      // its gate the input's gate of token T-t, none at t = 0; o written at row T-1-t)
     void* ckpt;       // optional: the state before every ck_len-th chunk, [BH][ck_P][K][V] input dtype
     int ck_len, ck_P;
     hipStream_t stream;

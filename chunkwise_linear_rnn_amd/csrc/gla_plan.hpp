@@ -148,17 +148,17 @@ inline size_t fwd_general_workspace_bytes(const Shape& s) {
 }
 
 // Backward under general gates: the forward's o and S_T, transposed S_0 and
-// dht, reversed copies of q, k, v, do and the shifted gates, the reversed dv
-// and dk, the chunk-start states of the forward and of the reversed dS
-// recurrence with the gate-gradient anchors formed from them, and the forward workspace of the largest of
-// the four general forwards it runs (shapes K x V and V x K).
+// dht, the chunk-start states of the forward and of the time-reversed dS
+// recurrence with the gate-gradient anchors formed from them, and the forward
+// workspace of the largest of the four general forwards it runs (shapes K x V
+// and V x K).  The reversed recurrences read their inputs in place.
 struct BwdGeneralLayout {
-    size_t o, st, s0t, dhtt, qr, kr, vr, dor, gs, hs, dvr, dkr, hsf, hsr, ag, ah, fws, total;
+    size_t o, st, s0t, dhtt, hsf, hsr, ag, ah, fws, total;
 };
 inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
     BwdGeneralLayout w{};
     const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H), KV = (size_t)(s.K * s.V);
-    const size_t tk = round256(BTH * s.K * 2), tv = round256(BTH * s.V * 2), sf = round256(BH * KV * 4);
+    const size_t tv = round256(BTH * s.V * 2), sf = round256(BH * KV * 4);
     Shape st = s;
     st.K = s.V;
     st.V = s.K;
@@ -168,14 +168,6 @@ inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
     w.st = at; at += sf;
     w.s0t = at; at += sf;
     w.dhtt = at; at += sf;
-    w.qr = at; at += tk;
-    w.kr = at; at += tk;
-    w.vr = at; at += tv;
-    w.dor = at; at += tv;
-    w.gs = at; at += tk;
-    w.hs = at; at += tv;
-    w.dvr = at; at += tv;
-    w.dkr = at; at += tk;
     const size_t N = (size_t)(s.T / 64);
     w.hsf = at; at += round256(BH * N * KV * 2);
     w.hsr = at; at += round256(BH * N * KV * 2);
