@@ -58,7 +58,8 @@ EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
-           "gla_set_launch_recorder", "gla_fwd_noalloc", "gla_ckpt_size", "gla_fwd_ckpt", "gla_bwd_ckpt"]
+           "gla_set_launch_recorder", "gla_fwd_noalloc", "gla_ckpt_size", "gla_fwd_ckpt", "gla_bwd_ckpt",
+           "gla_general_ckpt_size", "gla_fwd_general_ckpt", "gla_bwd_general_ckpt"]
 
 _lib = None
 
@@ -99,6 +100,12 @@ def lib():
     L.gla_bwd_general_workspace_size.argtypes = [sh]
     L.gla_bwd_general_workspace_size.restype = ctypes.c_size_t
     L.gla_fwd_general_workspace_size.restype = ctypes.c_size_t
+    L.gla_general_ckpt_size.argtypes = [sh]
+    L.gla_general_ckpt_size.restype = ctypes.c_size_t
+    L.gla_fwd_general_ckpt.argtypes = [sh] + [vp] * 10 + [ctypes.c_size_t, vp]
+    L.gla_fwd_general_ckpt.restype = ctypes.c_int
+    L.gla_bwd_general_ckpt.argtypes = [sh] + [vp] * 17 + [ctypes.c_size_t, vp]
+    L.gla_bwd_general_ckpt.restype = ctypes.c_int
     L.gla_bwd_scalar_workspace_size.restype = ctypes.c_size_t
     L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
     L.gla_decode.restype = ctypes.c_int
@@ -391,6 +398,68 @@ def gla_bwd_general(q, k, v, g, h, d_o, s0=None, dht=None, output_ds0=True, stre
     ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
     ws = workspace(gla_bwd_general_workspace_size(B, T, H, K, V, dt), dev)
     gla_bwd_general_into(q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, ws, stream)
+    return dq, dk, dv, dg, dh, ds0
+
+
+def gla_general_ckpt_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_general_ckpt_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
+
+
+def gla_fwd_general_ckpt_into(q, k, v, g, h, s0, o, s_final, ckpt, ws, stream=None):
+    """gla_fwd_general_ckpt with caller-owned outputs, checkpoint and workspace."""
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib().gla_fwd_general_ckpt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h), _ptr(s0),
+                                      _ptr(o), _ptr(s_final), _ptr(ckpt), _ptr(ws), nbytes, _stream(stream)))
+
+
+def gla_bwd_general_ckpt_into(q, k, v, g, h, s0, o, ckpt, d_o, dht, dq, dk, dv, dg, dh, ds0, ws, stream=None):
+    B, T, H, K, V = _dims(q, v)
+    shape = make_shape(B, T, H, K, V, q.dtype)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib().gla_bwd_general_ckpt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h), _ptr(s0),
+                                      _ptr(o), _ptr(ckpt), _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(dg), _ptr(dh), _ptr(ds0), _ptr(ws), nbytes, _stream(stream)))
+
+
+def gla_fwd_general_ckpt(q, k, v, g, h, s0=None, output_final_state=True, stream=None):
+    """(o, S_T, ckpt): gla_fwd_general that also keeps its state before every
+    chunk and S_T for gla_bwd_general_ckpt (shapes of gla_bwd_general)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("h", h, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    ck = workspace(gla_general_ckpt_size(B, T, H, K, V, dt), dev)
+    ws = workspace(gla_fwd_general_workspace_size(B, T, H, K, V, dt), dev)
+    gla_fwd_general_ckpt_into(q, k, v, g, h, s0, o, sf, ck, ws, stream)
+    return o, sf, ck
+
+
+def gla_bwd_general_ckpt(q, k, v, g, h, d_o, o, ckpt, s0=None, dht=None, output_ds0=True, stream=None):
+    """gla_bwd_general from the forward's o and the checkpoint gla_fwd_general_ckpt
+    kept for the same inputs (no forward is rerun)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("h", h, (B, T, H, V)), ("d_o", d_o, (B, T, H, V)),
+                         ("o", o, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    _need(dht, "dht", (B, H, K, V), torch.float32, dev)
+    need = gla_general_ckpt_size(B, T, H, K, V, dt)
+    if need > 0 and (ckpt is None or ckpt.numel() * ckpt.element_size() < need or ckpt.device != dev
+                     or not ckpt.is_contiguous()):
+        raise ValueError("ckpt must be the contiguous %d-byte checkpoint of gla_fwd_general_ckpt on %s" % (need, dev))
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dg = torch.empty_like(g)
+    dv = torch.empty_like(v); dh = torch.empty_like(h)
+    ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
+    ws = workspace(gla_bwd_general_workspace_size(B, T, H, K, V, dt), dev)
+    gla_bwd_general_ckpt_into(q, k, v, g, h, s0, o, ckpt, d_o, dht, dq, dk, dv, dg, dh, ds0, ws, stream)
     return dq, dk, dv, dg, dh, ds0
 
 

@@ -205,21 +205,40 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     return GLA_OK;
 }
 
+// Bytes of the general-gate checkpoint: the state before every chunk [BH][N][K][V]
+// bf16, then S_T [BH][K][V] fp32; 0 for shapes the general backward does not take.
+size_t general_ckpt_bytes(const gla::Shape& s) {
+    if (!s.bf16 || (s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256)) return 0;
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    const size_t BH = (size_t)(s.B * s.H), KV = (size_t)(s.K * s.V);
+    return gla::round256(BH * (size_t)(s.T / 64) * KV * 2) + gla::round256(BH * KV * 4);
+}
+size_t general_ckpt_st_offset(const gla::Shape& s) {
+    return gla::round256((size_t)(s.B * s.H) * (size_t)(s.T / 64) * (size_t)(s.K * s.V) * 2);
+}
+
+// ckpt (optional, general_ckpt_bytes(s) bytes): the forward also writes the
+// state before every chunk and S_T there, for gla_bwd_general_ckpt.
 gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
                               const void* g, const void* h, const float* s0, void* o, float* s_final,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream, void* ckpt = nullptr,
+                              bool want_ckpt = false) {
     g_detail.clear();
     gla::Shape s;
-    gla_status_t st = check_shape(shape, &s, false);
+    gla_status_t st = check_shape(shape, &s, want_ckpt);
     if (st != GLA_OK) return st;
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
     if (s.K != 128 && s.K != 256)
         return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 128 or 256 (got %lld)", (long long)s.K);
+    if (want_ckpt && s.V != 128 && s.V != 256)
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate checkpoint takes V = 128 or 256 (got %lld)", (long long)s.V);
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !o)) return fail(GLA_ERR_NULL, "q, k, v, g, h and o are required");
-    const void* ptrs[] = {q, k, v, g, h, s0, o, s_final, workspace};
-    const char* names[] = {"q", "k", "v", "g", "h", "s0", "o", "s_final", "workspace"};
-    for (int i = 0; i < 9; ++i)
+    if (want_ckpt && !empty && !ckpt)
+        return fail(GLA_ERR_NULL, "ckpt is required (gla_general_ckpt_size = %zu bytes)", general_ckpt_bytes(s));
+    const void* ptrs[] = {q, k, v, g, h, s0, o, s_final, workspace, ckpt};
+    const char* names[] = {"q", "k", "v", "g", "h", "s0", "o", "s_final", "workspace", "ckpt"};
+    for (int i = 0; i < 10; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     const size_t need = empty ? 0 : gla::fwd_general_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -246,6 +265,12 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
         a.s0 = s0;
         a.o = o;
         a.s_final = s_final;
+        float* ck_st = nullptr;
+        if (ckpt) {
+            ck_st = reinterpret_cast<float*>(static_cast<char*>(ckpt) + general_ckpt_st_offset(s));
+            a.ws_hs = ckpt;
+            a.s_final = ck_st;
+        }
         char* ws = static_cast<char*>(workspace);
         if (p.P > 1) {
             const size_t sb = gla::state_bytes(s, p);
@@ -256,15 +281,20 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
         a.ws_rec = ws + gla::fwd_general_seg_bytes(s, p);
         a.stream = strm;
         err = gla::launch_fwd_general(a);
+        if (err == hipSuccess && ckpt && s_final)
+            err = gla::launch_state_copy(ck_st, s_final, s.B * s.H * s.K * s.V, strm);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
 }
 
+// o, ckpt (both or neither): the forward's output and what gla_fwd_general_ckpt
+// wrote; the backward then runs no forward of its own.
 gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
                               const void* g, const void* h, const float* s0, const void* d_o, const float* dht,
                               void* dq, void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              size_t workspace_bytes, void* stream, const void* o = nullptr,
+                              const void* ckpt = nullptr, bool want_ckpt = false) {
     g_detail.clear();
     gla::Shape s;
     gla_status_t st = check_shape(shape, &s, true);
@@ -276,10 +306,12 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !d_o || !dq || !dk || !dv || !dg || !dh))
         return fail(GLA_ERR_NULL, "q, k, v, g, h, d_o, dq, dk, dv, dg and dh are required");
-    const void* ptrs[] = {q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace};
+    if (want_ckpt && !empty && (!o || !ckpt))
+        return fail(GLA_ERR_NULL, "o and ckpt are required (gla_general_ckpt_size = %zu bytes)", general_ckpt_bytes(s));
+    const void* ptrs[] = {q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, o, ckpt};
     const char* names[] = {"q", "k", "v", "g", "h", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "dh", "ds0",
-                           "workspace"};
-    for (int i = 0; i < 15; ++i)
+                           "workspace", "o", "ckpt"};
+    for (int i = 0; i < 17; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     const size_t need = empty ? 0 : gla::bwd_general_layout(s).total;
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -295,6 +327,11 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
         a.q = q; a.k = k; a.v = v; a.g = g; a.h = h; a.d_o = d_o;
         a.s0 = s0; a.dht = dht;
         a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dh = dh; a.ds0 = ds0;
+        if (want_ckpt) {
+            a.o_in = o;
+            a.hs_in = ckpt;
+            a.st_in = reinterpret_cast<const float*>(static_cast<const char*>(ckpt) + general_ckpt_st_offset(s));
+        }
         a.workspace = workspace;
         a.stream = strm;
         err = gla::launch_bwd_general(a);
@@ -608,6 +645,26 @@ gla_status_t gla_bwd_general(const gla_shape_t* shape, const void* q, const void
                              void* stream) {
     return bwd_general_impl(shape, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, workspace_bytes,
                             stream);
+}
+
+size_t gla_general_ckpt_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, true) != GLA_OK) return 0;
+    return general_ckpt_bytes(s);
+}
+
+gla_status_t gla_fwd_general_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                                  const void* g, const void* h, const float* s0, void* o, float* s_final, void* ckpt,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_general_impl(shape, q, k, v, g, h, s0, o, s_final, workspace, workspace_bytes, stream, ckpt, true);
+}
+
+gla_status_t gla_bwd_general_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                                  const void* g, const void* h, const float* s0, const void* o, const void* ckpt,
+                                  const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg, void* dh,
+                                  float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_general_impl(shape, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, workspace_bytes,
+                            stream, o, ckpt, true);
 }
 
 gla_status_t gla_bwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

@@ -174,11 +174,12 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     const long BH = (long)B * H, KV = (long)K * V;
     const BwdGeneralLayout w = bwd_general_layout(Shape{B, T, H, K, V, true});
     char* ws = static_cast<char*>(L.workspace);
-    bf16* o = reinterpret_cast<bf16*>(ws + w.o);
-    float* st = reinterpret_cast<float*>(ws + w.st);
+    const bool ck = L.hs_in != nullptr;  // the forward's results come in
+    const bf16* o = ck ? static_cast<const bf16*>(L.o_in) : reinterpret_cast<bf16*>(ws + w.o);
+    const float* st = ck ? L.st_in : reinterpret_cast<float*>(ws + w.st);
     float* s0T = L.s0 ? reinterpret_cast<float*>(ws + w.s0t) : nullptr;
     float* dhtT = L.dht ? reinterpret_cast<float*>(ws + w.dhtt) : nullptr;
-    bf16* hsf = reinterpret_cast<bf16*>(ws + w.hsf);
+    const bf16* hsf = ck ? static_cast<const bf16*>(L.hs_in) : reinterpret_cast<bf16*>(ws + w.hsf);
     bf16* hsr = reinterpret_cast<bf16*>(ws + w.hsr);
     float* ag = reinterpret_cast<float*>(ws + w.ag);
     float* ah = reinterpret_cast<float*>(ws + w.ah);
@@ -187,9 +188,13 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     hipError_t err;
     const long nst = BH * KV;
     const unsigned gst = (unsigned)((nst + 255) / 256);
-    // forward (o, S_T) and the transposed initial / final-state gradient
-    err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, o, st, fws, hsf, 0, sm));
-    if (err != hipSuccess) return err;
+    // forward (o, S_T and the state before every chunk), unless given, and the
+    // transposed initial / final-state gradient
+    if (!ck) {
+        err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, ws + w.o,
+                                                  reinterpret_cast<float*>(ws + w.st), fws, ws + w.hsf, 0, sm));
+        if (err != hipSuccess) return err;
+    }
     if (L.s0) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.s0, s0T, K, V, nst);
     if (L.dht) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.dht, dhtT, K, V, nst);
     // dq: the transposed state's forward

@@ -83,6 +83,11 @@ struct BwdGeneralLaunch {
     const float *s0, *dht;
     void *dq, *dk, *dv, *dg, *dh;
     float* ds0;
+    // optional, all three or none: the forward's output o, its state before every
+    // chunk [BH][N][K][V] bf16 and S_T [BH][K][V]; the backward then runs no forward
+    const void* o_in;
+    const void* hs_in;
+    const float* st_in;
     void* workspace;
     hipStream_t stream;
 };

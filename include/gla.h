@@ -268,11 +268,46 @@ gla_status_t gla_bwd_general(const gla_shape_t* shape,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gla_bwd_general needs (0 for an unsupported or
- * invalid shape; no HIP call): the forward's o and S_T, time-reversed copies of
- * q, k, v, do and the gates, the reversed dv and dk, per-chunk gate sums and
- * the general forward's workspace (about 16 (K + V) bytes per token and head
- * plus the records). */
+ * invalid shape; no HIP call): the forward's o and S_T, the states before every
+ * chunk of the forward and of the time-reversed dS recurrence, the gate-gradient
+ * anchors and the general forward's workspace.  The time-reversed recurrences
+ * read q, k, v, d_o and the gates in place. */
 size_t gla_bwd_general_workspace_size(const gla_shape_t* shape);
+
+/*
+ * General-gate training pair: gla_fwd_general_ckpt + gla_bwd_general_ckpt.
+ * gla_bwd_general recomputes the forward for the output o (in the closed form
+ * of dh) and for the state before every chunk (the gate-gradient anchors at the
+ * chunk boundaries).  This pair keeps them instead (Section 3.3's
+ * materialisation side): the forward also writes its state before every chunk
+ * and S_T into a caller-owned checkpoint, and the backward takes that and the
+ * forward's o and runs no forward.
+ *   gla_general_ckpt_size(shape) : bytes of the checkpoint, the states
+ *     [B,H,T/64,K,V] bf16 (entry 0 of each head is not used), then S_T
+ *     [B,H,K,V] fp32 at a 256-byte aligned offset; 0 for an empty, invalid or
+ *     unsupported shape (the shapes of gla_bwd_general).
+ *   gla_fwd_general_ckpt : gla_fwd_general (same arguments, results and
+ *     workspace) for the shapes of gla_bwd_general, plus writes ckpt (device,
+ *     16-byte aligned, required unless the shape is empty).
+ *   gla_bwd_general_ckpt : gla_bwd_general (same arguments, results and
+ *     workspace), plus reads o and ckpt, which must hold what
+ *     gla_fwd_general_ckpt returned for the same shape, q, k, v, g, h and s0,
+ *     unmodified since (not checked: other contents give wrong gradients).
+ * Errors: as gla_fwd_general / gla_bwd_general; GLA_ERR_UNSUPPORTED for a shape
+ * gla_bwd_general does not take, GLA_ERR_NULL for a NULL o or ckpt on a
+ * non-empty shape, GLA_ERR_ALIGN for a misaligned one.
+ */
+size_t gla_general_ckpt_size(const gla_shape_t* shape);
+gla_status_t gla_fwd_general_ckpt(const gla_shape_t* shape,
+                                  const void* q, const void* k, const void* v, const void* g,
+                                  const void* h, const float* s0, void* o, float* s_final, void* ckpt,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+gla_status_t gla_bwd_general_ckpt(const gla_shape_t* shape,
+                                  const void* q, const void* k, const void* v, const void* g,
+                                  const void* h, const float* s0, const void* o, const void* ckpt,
+                                  const void* d_o, const float* dht,
+                                  void* dq, void* dk, void* dv, void* dg, void* dh, float* ds0,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gla_decode -- the recurrent form of Eq. 3 (Section 3.1), for token-by-token

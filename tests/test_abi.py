@@ -288,3 +288,32 @@ def test_ckpt_entry_points_validate(L):
     assert fwd(_shape(T=100)) == ERR_SHAPE
     assert bwd(_shape(V=1024)) == ERR_UNSUPPORTED
     assert bwd(_shape(K=256, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+
+
+def test_general_ckpt_entry_points_validate(L):
+    size = lambda shape: L.gla_general_ckpt_size(ctypes.byref(shape))
+    s = _shape(B=2, H=4, T=8192, K=128, V=256)
+    # the states before every chunk (bf16), then S_T (fp32) at a 256-byte offset
+    assert size(s) == 8 * 128 * 128 * 256 * 2 + 8 * 128 * 256 * 4
+    assert size(_shape(K=256, V=128, T=640)) > 0
+    assert size(_shape(dtype=gla.GLA_DTYPE_FP32)) == 0   # the general path takes bf16
+    assert size(_shape(K=64)) == 0                       # K not in {128, 256}
+    assert size(_shape(K=128, V=512, T=8192)) == 0       # V = 512: no general backward
+    assert size(_shape(T=0)) == 0
+    fwd = lambda shape, ck=P, o=P: L.gla_fwd_general_ckpt(ctypes.byref(shape), P, P, P, P, P, None, o, None, ck, P,
+                                                          1 << 40, None)
+    bwd = lambda shape, ck=P, o=P: L.gla_bwd_general_ckpt(ctypes.byref(shape), P, P, P, P, P, None, o, ck, P, None,
+                                                          P, P, P, P, P, None, P, 1 << 40, None)
+    assert fwd(s, ck=None) == ERR_NULL
+    assert bwd(s, ck=None) == ERR_NULL
+    assert bwd(s, o=None) == ERR_NULL
+    assert fwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert bwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert bwd(s, o=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert fwd(_shape(T=100)) == ERR_SHAPE
+    assert fwd(_shape(K=128, V=512, T=8192)) == ERR_UNSUPPORTED   # gla_fwd_general takes it; the pair does not
+    assert bwd(_shape(K=128, V=512, T=8192)) == ERR_UNSUPPORTED
+    assert fwd(_shape(dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    empty = _shape(T=0, K=128, V=128)
+    assert fwd(empty, ck=None, o=None) == OK              # nothing to compute: no checkpoint needed
+    assert bwd(empty, ck=None, o=None) == OK

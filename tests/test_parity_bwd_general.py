@@ -78,3 +78,32 @@ def test_bwd_general_deterministic():
     b = gla.gla_bwd_general(d["q"], d["k"], d["v"], d["g"], h, d["do"], d["s0"], d["dht"])
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("B,H,T,K,V,s0,dht", [
+    (1, 1, 64, 128, 128, "normal0.1", True),      # one chunk: only the S_T anchor
+    (2, 2, 64 * 9, 128, 256, "normal0.1", True),  # one chunk per segment
+    (2, 4, 64 * 13, 256, 128, "none", False),     # K > V, no dht
+    (2, 4, 8192, 128, 256, "normal0.1", True),    # the benchmark's shape
+])
+def test_bwd_general_ckpt_pair(B, H, T, K, V, s0, dht):
+    # the pair runs the same kernels as gla_fwd_general + gla_bwd_general, with
+    # the forward's o, chunk-start states and S_T kept instead of recomputed:
+    # every result must be bit-identical; the first case also meets the oracle
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0=s0, backward=True, seed=1800 + T + K + V)
+    inp = gi.make_inputs(w, dht=dht)
+    h = gi.make_value_gate(B, T, H, V, seed=1900 + T + V)
+    note("general ckpt pair: B=%d H=%d T=%d K=%d V=%d s0=%s dht=%s" % (B, H, T, K, V, s0, dht))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    hd = h.to(DEV)
+    assert gla.gla_general_ckpt_size(B, T, H, K, V, torch.bfloat16) > 0
+    o, sf, ck = gla.gla_fwd_general_ckpt(d["q"], d["k"], d["v"], d["g"], hd, d["s0"])
+    o_ref, sf_ref = gla.gla_fwd_general(d["q"], d["k"], d["v"], d["g"], hd, d["s0"])
+    got = gla.gla_bwd_general_ckpt(d["q"], d["k"], d["v"], d["g"], hd, d["do"], o, ck, d["s0"], d["dht"])
+    ref = gla.gla_bwd_general(d["q"], d["k"], d["v"], d["g"], hd, d["do"], d["s0"], d["dht"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(sf, sf_ref)
+    for name, a, b in zip(("dq", "dk", "dv", "dg", "dh", "ds0"), got, ref):
+        assert torch.equal(a, b), name
+    if T == 64:
+        _check(w, inp, h, _heads(B, H))
