@@ -89,34 +89,49 @@ gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, cons
     const bf16* D16 = hsr + (bh * N + (last ? 0 : N - m)) * KV;
     const float* S32 = st + bh * KV;
     const float* D32 = dht ? dht + bh * KV : nullptr;
-    for (int i = rg; i < K; i += RG) {
-        float p[8];
-        const long off = (long)i * V + 8 * cv;
-        if (!last) {
-            const u32x4 sv = *reinterpret_cast<const u32x4*>(S16 + off);
-            const u32x4 dv = *reinterpret_cast<const u32x4*>(D16 + off);
-            const bf16* sx = reinterpret_cast<const bf16*>(&sv);
-            const bf16* dx = reinterpret_cast<const bf16*>(&dv);
+    // rows in groups of four: the group's loads are independent, then its four
+    // row reductions (also independent) follow
+    constexpr int GR = 4;
+#pragma unroll 1
+    for (int i0 = rg; i0 < K; i0 += GR * RG) {
+        float rsum[GR];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = Elem<bf16>::to_f(sx[e]) * Elem<bf16>::to_f(dx[e]);
-        } else if (D32) {
+        for (int r = 0; r < GR; ++r) {
+            const int i = i0 + r * RG;
+            rsum[r] = 0.f;
+            if (i >= K) continue;
+            float p[8];
+            const long off = (long)i * V + 8 * cv;
+            if (!last) {
+                const u32x4 sv = *reinterpret_cast<const u32x4*>(S16 + off);
+                const u32x4 dv = *reinterpret_cast<const u32x4*>(D16 + off);
+                const bf16* sx = reinterpret_cast<const bf16*>(&sv);
+                const bf16* dx = reinterpret_cast<const bf16*>(&dv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = S32[off + e] * D32[off + e];
-        } else {
+                for (int e = 0; e < 8; ++e) p[e] = Elem<bf16>::to_f(sx[e]) * Elem<bf16>::to_f(dx[e]);
+            } else if (D32) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = 0.f;
+                for (int e = 0; e < 8; ++e) p[e] = S32[off + e] * D32[off + e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = 0.f;
+            }
+            const float a = alpha[i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float wv = a * beta[8 * cv + e] * p[e];
+                rsum[r] += wv;
+                cs[e] += wv;
+            }
         }
-        const float a = alpha[i];
-        float rs = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float wv = a * beta[8 * cv + e] * p[e];
-            rs += wv;
-            cs[e] += wv;
+        for (int r = 0; r < GR; ++r) {
+            const int i = i0 + r * RG;
+            float rs = rsum[r];
+#pragma unroll
+            for (int o = CVN / 2; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, CVN);
+            if (cv == 0 && i < K) ag[(bh * (N + 1) + m) * K + i] = rs;
         }
-#pragma unroll
-        for (int o = CVN / 2; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, CVN);
-        if (cv == 0) ag[(bh * (N + 1) + m) * K + i] = rs;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) colp[rg][8 * cv + e] = cs[e];
@@ -130,19 +145,56 @@ gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, cons
 }
 
 // out_t = the anchor of the chunk's end boundary + the chunk's own reverse
-// cumulative sum of a*da - c*dc (tensors [B,T,H,D]); one thread per column.
-__global__ void __launch_bounds__(64)
+// cumulative sum of a*da - c*dc (tensors [B,T,H,D]).  One workgroup per chunk
+// and head: thread (part, cv) takes columns 8cv .. 8cv+7 over the tokens
+// part*TPP .. +TPP-1 with 16-byte loads, sums them in reverse, and adds the
+// totals of the later parts (through LDS) and the anchor.
+template <int D>
+__global__ void __launch_bounds__(256)
 gla_gate_grad_out(const bf16* __restrict__ a, const bf16* __restrict__ da, const bf16* __restrict__ c,
-                  const bf16* __restrict__ dc, const float* __restrict__ anchor, bf16* __restrict__ out, int T, int H,
-                  int D) {
-    const int n = blockIdx.x, col = blockIdx.y * 64 + threadIdx.x;
-    const long bh = blockIdx.z, b = bh / H, h = bh % H, N = T / 64;
-    float acc = anchor[(bh * (N + 1) + n + 1) * D + col];
-    const long base = ((b * T + (long)n * 64) * H + h) * D + col, rs = (long)H * D;
-    for (int t = 63; t >= 0; --t) {
-        const long o = base + t * rs;
-        acc += Elem<bf16>::to_f(a[o]) * Elem<bf16>::to_f(da[o]) - Elem<bf16>::to_f(c[o]) * Elem<bf16>::to_f(dc[o]);
-        out[o] = Elem<bf16>::from_f(acc);
+                  const bf16* __restrict__ dc, const float* __restrict__ anchor, bf16* __restrict__ out, int T,
+                  int H) {
+    constexpr int CV = D / 8, NPART = 256 / CV, TPP = kChunk / NPART;
+    static_assert(NPART * CV == 256 && NPART * TPP == kChunk, "gate-gradient tiling");
+    __shared__ float tot[NPART][D];
+    const int n = blockIdx.x, N = T / kChunk;
+    const long bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, cv = tid % CV, part = tid / CV, jv = 8 * cv;
+    const long rs = (long)H * D;
+    const long base = ((b * T + (long)n * kChunk + part * TPP) * H + h) * D + jv;
+    float x[TPP][8];
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+        const long o = base + i * rs;
+        const u32x4 ra = *reinterpret_cast<const u32x4*>(a + o), rda = *reinterpret_cast<const u32x4*>(da + o);
+        const u32x4 rc = *reinterpret_cast<const u32x4*>(c + o), rdc = *reinterpret_cast<const u32x4*>(dc + o);
+        const bf16 *pa = reinterpret_cast<const bf16*>(&ra), *pda = reinterpret_cast<const bf16*>(&rda);
+        const bf16 *pc = reinterpret_cast<const bf16*>(&rc), *pdc = reinterpret_cast<const bf16*>(&rdc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            x[i][e] = Elem<bf16>::to_f(pa[e]) * Elem<bf16>::to_f(pda[e]) -
+                      Elem<bf16>::to_f(pc[e]) * Elem<bf16>::to_f(pdc[e]);
+    }
+#pragma unroll
+    for (int i = TPP - 2; i >= 0; --i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] += x[i + 1][e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tot[part][jv + e] = x[0][e];
+    __syncthreads();
+    float off[8];
+    const float* an = anchor + (bh * (N + 1) + n + 1) * D + jv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) off[e] = an[e];
+    for (int p = part + 1; p < NPART; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) off[e] += tot[p][jv + e];
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+        alignas(16) bf16 y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = Elem<bf16>::from_f(x[i][e] + off[e]);
+        *reinterpret_cast<u32x4*>(out + base + i * rs) = *reinterpret_cast<const u32x4*>(y);
     }
 }
 
@@ -223,12 +275,19 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
             GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor<256>, ga, dim3(256), sm, (const bf16*)hsf,
                        (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K);
     }
-    GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out, dim3(N, (unsigned)(K / 64), (unsigned)BH), dim3(64), sm,
-               (const bf16*)L.q, (const bf16*)L.dq, (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag,
-               static_cast<bf16*>(L.dg), T, H, K);
-    GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out, dim3(N, (unsigned)(V / 64), (unsigned)BH), dim3(64), sm,
-               (const bf16*)o, (const bf16*)L.d_o, (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah,
-               static_cast<bf16*>(L.dh), T, H, V);
+    const dim3 gg(N, (unsigned)BH);
+    if (K == 128)
+        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<128>, gg, dim3(256), sm, (const bf16*)L.q, (const bf16*)L.dq,
+                   (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag, static_cast<bf16*>(L.dg), T, H);
+    else
+        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<256>, gg, dim3(256), sm, (const bf16*)L.q, (const bf16*)L.dq,
+                   (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag, static_cast<bf16*>(L.dg), T, H);
+    if (V == 128)
+        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<128>, gg, dim3(256), sm, o, (const bf16*)L.d_o,
+                   (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah, static_cast<bf16*>(L.dh), T, H);
+    else
+        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<256>, gg, dim3(256), sm, o, (const bf16*)L.d_o,
+                   (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah, static_cast<bf16*>(L.dh), T, H);
     return hipGetLastError();
 }
 
