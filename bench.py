@@ -710,6 +710,8 @@ def main():
                     help="write a profiles/ summary of MFMA / LDS counters")
     ap.add_argument("--summarize-stalls", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"),
                     help="write a profiles/ summary of wave-stall and LDS counters")
+    ap.add_argument("--step-only", action="store_true",
+                    help="run no recompute pair beside the step (so that counter runs see the step's kernels only)")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the input files, quoted in the summary")
@@ -878,7 +880,7 @@ def main():
     cold_bwd = cold_times(bwd, args.steps)
     ms_fwd, ms_bwd = pct(cold_fwd, 50), pct(cold_bwd, 50)
     ms_fwd_warm, ms_bwd_warm = timed(fwd, args.steps), timed(bwd, args.steps)
-    cold_rc = cold_times(step_rc, args.steps) if ck_bytes else cold
+    cold_rc = cold_times(step_rc, args.steps) if (ck_bytes and not args.step_only) else cold
     del scrub
 
     # per-kernel HIP-event timing over another K steps (each kernel bracketed on
@@ -931,7 +933,7 @@ def main():
             ("gla_fwd_ckpt + gla_bwd_ckpt (the backward starts its segments from the forward's states)" if ck_bytes
              else "gla_fwd + gla_bwd")), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
             "chunk": 64, "segments": P},
-        "ms_per_step_recompute": pct(cold_rc, 50),
+        "ms_per_step_recompute": pct(cold_rc, 50) if (ck_bytes and not args.step_only) else None,
         "recompute_step": "gla_fwd + gla_bwd (every state recomputed in the backward), cold median",
         "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
         "bwd_tokens_per_s": tokens / (ms_bwd * 1e-3),
