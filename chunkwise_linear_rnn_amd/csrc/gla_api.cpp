@@ -404,6 +404,9 @@ hipError_t bwd_launch(const gla::Shape& s, const void* q, const void* k, const v
         // the half-segment gate totals (dsub = 2) sit in the last area
         if (a.dsub == 2) a.ws_gate = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, sg) -
                                                              gla::round256(2 * kk * sizeof(float)));
+        // checkpointed, half segments, per-column 16-bit gates: the dq walk
+        // forms the half segments' dS* (no segment pass of its own)
+        a.ds_fused = a.dsub == 2 && s.bf16 && !sg && p.BK == 64;
         a.stream = strm;
         err = gla::launch_bwd(a);
     }

@@ -388,7 +388,7 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
 // double-buffered key-side slice of BK columns per chunk (the decayed operand
 // read with column fragments, the fp32 cumulative log gate, the per-column
 // state-update factors).
-template <typename T, int BK, int V, int NW>
+template <typename T, int BK, int V, int NW, bool WQ = false>
 struct RowPipeSmem {
     using RR = RowRoles<BK, V, NW>;
     static constexpr int PT = Elem<T>::pad;
@@ -414,9 +414,14 @@ struct RowPipeSmem {
     };
     alignas(16) T P[kChunk * pP];
     alignas(16) f32x4 red[RR::VS > 1 ? RR::NKQ * RR::VS * RR::NB * 64 : 1];  // [key block][reader slice][slot][lane]
-    float carry[RR::VS * BK];
-    alignas(16) float tot[4 * BK];  // dk walk: per token block, the column totals of dA
-    float sgt[RR::NKQ * kChunk];    // dk walk, scalar gate: each 16-column block's sum of dg per token
+    union {
+        struct {
+            float carry[RR::VS * BK];
+            alignas(16) float tot[4 * BK];  // dk walk: per token block, the column totals of dA
+            float sgt[RR::NKQ * kChunk];    // dk walk, scalar gate: each 16-column block's sum of dg per token
+        };
+        alignas(16) T Q[WQ ? kChunk * pK : 1];  // WQ (dq walk with DS): q * exp2(offset + B_t)
+    };
 };
 
 // One wave prepares key columns kc0 .. kc0+NC-1 of a chunk (lane = token row)
@@ -535,16 +540,25 @@ __device__ __attribute__((noinline)) void row_exact_intra(const T* __restrict__ 
 // the dk walk (first key block only); then each wave, for its two token blocks
 // (RowRoles::block), dP Kt, the slice reduction, the factor exp2(B_t) and the
 // store of dq; the next chunk's V and d_o tiles.
-template <typename T, int BK, int V, int NW, bool SG = false>
+// DS (checkpointed backward over half segments): the walk also forms each half
+// segment's local dS*, the sum over its tokens of (q_t exp2(B_t - B_start))^T
+// dO_t, whose factors never exceed 1: phase 2 scales the next chunk's q into
+// LDS, phase 1 adds its product with the chunk's d_o tile to a second register
+// tile laid out like S^T, stored with the half segment's log2 decay at its last
+// chunk.  The backward's separate pass over q, g and d_o is then not run.
+template <typename T, int BK, int V, int NW, bool SG = false, bool DS = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ d_o,
                 const T* __restrict__ ws_init, const float* __restrict__ s0, T* __restrict__ dq,
-                T* __restrict__ hs, T* __restrict__ dp_out, int T_, int H, int K, int N, int P, int seg_len, int BH) {
+                T* __restrict__ hs, T* __restrict__ dp_out, int T_, int H, int K, int N, int P, int seg_len, int BH,
+                const T* __restrict__ q = nullptr, T* __restrict__ ds_out = nullptr,
+                float* __restrict__ dg_out = nullptr, int half_len = 0) {
     constexpr int NT = NW * 64;
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
     static_assert(CPK % VEC == 0, "wave tiling");
-    using Sm = RowPipeSmem<T, BK, V, NW>;
+    static_assert(!DS || (BK == 64 && !SG), "dS* in the dq walk: 64-row key blocks, per-column gates");
+    using Sm = RowPipeSmem<T, BK, V, NW, DS>;
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
@@ -577,6 +591,30 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     using TRV = TileRegs<T, V, NT>;
     TRV rv, rdo;
     auto kbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsK + (long)h * K + k0; };
+    // DS: the local dS* of each half segment (half_len chunks from the
+    // segment's start, then the rest), forward-accumulated as the sum over its
+    // tokens of (q_t * exp2(B_t - B_start))^T dO_t, in S's layout, with the
+    // half segment's log2 decay per key column (lanes < CPK, column kc0 + l)
+    TStateRegs<VW> D;
+    RowSlab<T, CPK> rq;
+    float dsoff = 0.f, dsg = 0.f;
+    // Q of chunk c into sm.Q from its cumulative gate (this wave's own columns
+    // of bf.B, written by this lane) and the offset of the chunks before it
+    auto q_prep = [&](const typename Sm::Buf& bf, int c) {
+        const int pos = c - c_begin;
+        if (pos == 0 || pos == half_len) dsoff = 0.f;
+        float xv[CPK];
+#pragma unroll
+        for (int j = 0; j < CPK; ++j) xv[j] = rq.get(j) * exp2_fast(lane_bcast(dsoff, j) + bf.B[l * Sm::pB + kc0 + j]);
+#pragma unroll
+        for (int j0q = 0; j0q < CPK; j0q += VEC) store_vec_lds<T>(sm.Q + l * Sm::pK + kc0 + j0q, xv + j0q);
+        if (l < CPK) dsoff += bf.B[(kChunk - 1) * Sm::pB + kc0 + l];
+        if (c + 1 < c_end) rq.load(kbase(q, c + 1), rsK, kc0);
+    };
+    if constexpr (DS) {
+        D.zero();
+        rq.load(kbase(q, c_begin), rsK, kc0);
+    }
     auto gbase = [&](int c) { return SG ? g + ((long)b * T_ + (long)c * kChunk) * H + h : kbase(g, c); };
     const int rsG = SG ? H : rsK;
     auto vbase = [&](const T* p, int c) { return p + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V; };
@@ -586,6 +624,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     rdo.load(vbase(d_o, c_begin), rsV, tid);
     __syncthreads();
     row_prep<T, CPK, false>(sm.buf[c_begin & 1], Sm::pK, Sm::pB, rk, rg, kc0);
+    if constexpr (DS) q_prep(sm.buf[c_begin & 1], c_begin);
     rv.store_lds(sm.Vt, Sm::pV, tid);
     rdo.store_lds(sm.dO, Sm::pV, tid);
     if (c_begin + 1 < c_end) {
@@ -654,6 +693,29 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
                 *reinterpret_cast<vec4_t<T>*>(dst + ((kq * (V / 16) + j0 / 16 + jb) * 64 + l) * 4) =
                     to_vec4<T>(S.s[jb]);
         }
+        if constexpr (DS) {
+            // D += (q exp2(offset + B))^T dO over the chunk, as the state update
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const vec4_t<T> x0 = frag_cm<T>(sm.Q, Sm::pK, 32 * ks, i0);
+                const vec4_t<T> x1 = frag_cm<T>(sm.Q, Sm::pK, 32 * ks + 16, i0);
+#pragma unroll
+                for (int jb = 0; jb < VW / 16; ++jb)
+                    D.s[jb] = mma32(D.s[jb], frag_cm<T>(sm.dO, Sm::pV, 32 * ks, j0 + 16 * jb),
+                                    frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
+            }
+            if (l < CPK) dsg += cur.B[(kChunk - 1) * Sm::pB + kc0 + l];
+            const int pos = c - c_begin;
+            if (pos + 1 == half_len || c + 1 == c_end) {
+                const long sub = (long)bh * 2 * P + 2 * seg + (pos >= half_len ? 1 : 0);
+                T* dd = ds_out + sub * (long)K * V + (long)k0 * V + (long)(i0 + (l & 15)) * V + j0 + 4 * (l >> 4);
+#pragma unroll
+                for (int jb = 0; jb < VW / 16; ++jb) *reinterpret_cast<vec4_t<T>*>(dd + 16 * jb) = to_vec4<T>(D.s[jb]);
+                if (l < CPK) dg_out[sub * K + k0 + kc0 + l] = dsg;
+                D.zero();
+                dsg = 0.f;
+            }
+        }
         if (more) {
             if (!early) row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
             if (c + 2 < c_end) {
@@ -711,6 +773,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         if (exact) __syncthreads();
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
         if (more) {
+            if constexpr (DS) q_prep(nxt, c + 1);
             rv.store_lds(sm.Vt, Sm::pV, tid);
             rdo.store_lds(sm.dO, Sm::pV, tid);
             if (c + 2 < c_end) {
@@ -1725,14 +1788,32 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 // the forward's value width (BV = a.BVSEG = a.BVS), so the key-side preparation
 // and its loads are not repeated across value blocks; with a checkpoint only
 // the backward direction runs, on half that width when the full width would
-// leave CUs idle.
+// leave CUs idle, and not at all when the dq walk forms it (ds_fused: the
+// combine then follows the dq walk).
+template <typename T>
+static void launch_combine_bwd(const BwdLaunch& a, int PS) {
+    const long KV = (long)a.K * a.V;
+    const unsigned nz = a.ckpt ? 1u : 2u;
+    const int z0 = a.ckpt ? 1 : 0;
+    // the combine walks the PS entries that hold chunks, at a stride of dsub*P per head
+    if (PS <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
+        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd_split<T>,
+                   dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
+                   a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, a.K, a.V, PS, z0, a.dsub * a.P);
+    } else {
+        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>,
+                   dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, nz), dim3(256), a.stream,
+                   a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, a.K, a.V, PS, z0, a.dsub * a.P);
+    }
+}
+
 template <typename T, int KD, int BV, bool SG>
 static hipError_t launch_seg_states_g(const BwdLaunch& a) {
     constexpr int NW = (BV / 16 < 8) ? BV / 16 : 8;
     constexpr int NT = NW * 64;
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
     const int nvb = a.V / BV;
-    const long KV = (long)KD * a.V;
+    if (a.ds_fused) return hipSuccess;  // the dq walk forms dS*, the combine follows it
     if (a.P > 1) {
         // with a checkpoint the states S_init(p) are given: only dS*_p (and the
         // gate totals, from the backward direction) are formed, and only dS
@@ -1750,18 +1831,7 @@ static hipError_t launch_seg_states_g(const BwdLaunch& a) {
                            (T*)a.ws_dstate, a.ws_gate, a.T, a.H, a.V, a.N, a.dsub * a.P, lenS, nseg, (int)a.BH,
                            (int)nfwd, mid ? (T*)a.ws_dmid : nullptr, a.ws_gmid, (a.seg_len + 1) / 2,
                            a.ckpt ? 0 : a.P - 1);
-        const unsigned nz = a.ckpt ? 1u : 2u;
-        const int z0 = a.ckpt ? 1 : 0;
-        // the combine walks the PS entries that hold chunks, at a stride of dsub*P per head
-        if (PS <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
-            GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd_split<T>,
-                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
-                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, PS, z0, a.dsub * a.P);
-        } else {
-            GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>,
-                       dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, nz), dim3(256), a.stream,
-                       a.s0, a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, KD, a.V, PS, z0, a.dsub * a.P);
-        }
+        launch_combine_bwd<T>(a, PS);
     }
     return hipGetLastError();
 }
@@ -1832,9 +1902,22 @@ static hipError_t launch_rows_g(const BwdLaunch& a) {
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
-        GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, SG>), grid, dim3(NT), a.stream, (const T*)a.k,
-                           (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0, (T*)a.dq,
-                           (T*)a.ws_hs, (T*)a.ws_dp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
+        if constexpr (!SG && BK == 64) {
+            static_assert(sizeof(RowPipeSmem<T, BK, V, NW, true>) <= 160 * 1024, "LDS budget");
+            if (a.ds_fused) {
+                // dS* of every half segment formed by the dq walk, then their combine
+                GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, false, true>), grid, dim3(NT), a.stream,
+                           (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0,
+                           (T*)a.dq, (T*)a.ws_hs, (T*)a.ws_dp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH,
+                           (const T*)a.q, (T*)a.ws_dstate, a.ws_gate, a.seg_len / 2);
+                const int half = a.seg_len / 2;
+                launch_combine_bwd<T>(a, (a.N + half - 1) / half);
+            }
+        }
+        if (!a.ds_fused)
+            GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, SG>), grid, dim3(NT), a.stream, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0, (T*)a.dq,
+                       (T*)a.ws_hs, (T*)a.ws_dp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH);
     } else {
         GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq<T, BK, V, NW>), grid, dim3(NT), a.stream, (const T*)a.k,
                            (const T*)a.v, (const T*)a.g, (const T*)a.d_o, sinit, seg_stride, bh_stride, (T*)a.dq,

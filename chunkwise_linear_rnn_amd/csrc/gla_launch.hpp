@@ -42,6 +42,7 @@ struct BwdLaunch {
     int BVSEG;  // value columns per workgroup of the backward's segment-state pass
     int BVD;  // value columns per workgroup of the dv walk
     int dv_split;  // 2: the dv walk takes each segment in two halves (from the midpoint states)
+    bool ds_fused;  // the dq walk forms the half segments' dS* (checkpointed, dsub = 2, 16-bit, per-column gates)
     int T, H, N, P, seg_len;
     long BH;
     const void *q, *k, *v, *g, *d_o;
