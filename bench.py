@@ -40,7 +40,7 @@ METRIC_SCALAR = "GLA scalar-gate fwd+bwd tokens/sec at T=8K, dk=128, dv=256"
 
 
 def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int, dv_split: bool = False,
-                             G: int = None, ckpt: bool = False):
+                             G: int = None, ckpt: bool = False, T: int = 0):
     """Algorithmic HBM bytes per (token, head) of one launch of `kernel`.
 
     G is the number of log-gate values per token and head (K for per-column
@@ -48,18 +48,23 @@ def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd:
     segment-state pass reads q, g, d_o of every segment instead of all but the
     first when the dv walk takes segments in halves (it then also needs each
     segment's midpoint state); with a checkpoint (ckpt) it runs only that
-    backward direction."""
+    backward direction, and with a checkpoint, 16-bit per-column gates and the
+    dv walk in halves (`fused`) the dq walk forms it: it then also reads q and
+    writes the 2 P_bwd half-segment states of K x V per head (T tokens)."""
     G = K if G is None else G
     seg_frac = (P - 1) / P if P > 1 else 0.0
     seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
+    fused = ckpt and dv_split and e == 2 and G == K and T > 0
     table = {
         "fwd_walk": e * (2 * K + G + 2 * V),            # q, k, g, v read; o written
-        "bwd_dq_walk": e * (2 * K + G + 2 * V),         # k, g, v, d_o read; dq written
+        # k, g, v, d_o read; dq written (fused: q read, the half segments' dS* written)
+        "bwd_dq_walk": e * (2 * K + G + 2 * V) + (e * K + 2 * P_bwd * K * V * e / T if fused else 0),
         "bwd_dk_walk": e * (4 * K + 2 * G + 2 * V),     # q, k, g, dq, v, d_o read; dk, dg written
         "bwd_dv_walk": e * (2 * K + G + 2 * V),         # q, k, g, d_o read; dv written
         "fwd_seg_state": e * (K + G + V) * seg_frac,    # k, g, v of all but the last segment
         # k, g, v of all but the last segment and q, g, d_o of all but the first (or all)
-        "bwd_seg_states": e * (K + G + V) * ((0.0 if ckpt else seg_frac_bwd) + (1.0 if dv_split else seg_frac_bwd)),
+        "bwd_seg_states": None if fused else
+        e * (K + G + V) * ((0.0 if ckpt else seg_frac_bwd) + (1.0 if dv_split else seg_frac_bwd)),
     }
     return table.get(kernel)
 
@@ -738,7 +743,8 @@ def main():
         split = plan_dv_split(w.B, w.H, w.T, w.K, w.V, e == 2)
         alg = {}
         for k in ("fwd_walk", "bwd_dq_walk", "bwd_dk_walk", "bwd_dv_walk", "fwd_seg_state", "bwd_seg_states"):
-            b = alg_bytes_per_token_head(k, w.K, w.V, e, P, Pb, split, ckpt=not args.recompute and w.dtype == "bf16" and w.K <= 128)
+            b = alg_bytes_per_token_head(k, w.K, w.V, e, P, Pb, split, T=w.T,
+                                         ckpt=not args.recompute and w.dtype == "bf16" and w.K <= 128)
             if b:
                 alg[k] = b * w.B * w.T * w.H / 1e6
         base = os.path.join(ROOT, "profiles", "traffic_%s" % args.workload)
@@ -897,7 +903,7 @@ def main():
     P_bwd = plan_segments_bwd(B, H, T, K, V, w.dtype == "bf16")
     units = B * T * H
     bpt = alg_bytes_per_token_head(dom, K, V, e, P, P_bwd, plan_dv_split(B, H, T, K, V, w.dtype == "bf16"),
-                                   G=1 if sg else K, ckpt=bool(ck_bytes))
+                                   G=1 if sg else K, ckpt=bool(ck_bytes), T=T)
     roofline = None
     if bpt is not None:
         ach = bpt * units / (kern[dom]["avg_us"] * 1e-6) / 1e9
