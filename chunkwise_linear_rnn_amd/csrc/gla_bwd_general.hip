@@ -25,17 +25,6 @@
 
 namespace gla {
 
-// dst[bh][j][i] = src[bh][i][j] for [BH][K][V] fp32 states
-__global__ void __launch_bounds__(256)
-gla_transpose_state(const float* __restrict__ src, float* __restrict__ dst, int K, int V, long n) {
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= n) return;
-    const long KV = (long)K * V;
-    const long bh = e / KV, r = e % KV;
-    const int i = (int)(r / V), j = (int)(r % V);
-    dst[bh * KV + (long)j * K + i] = src[e];
-}
-
 // ds0[bh][i][j] *= exp(g[b,0,h,i] + h[b,0,h,j]): the gradient one gate further back
 __global__ void __launch_bounds__(256)
 gla_scale_ds0(float* __restrict__ ds0, const bf16* __restrict__ g, const bf16* __restrict__ hg, int T, int H, int K,
@@ -200,7 +189,7 @@ gla_gate_grad_out(const bf16* __restrict__ a, const bf16* __restrict__ da, const
 
 static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void* q, const void* k, const void* v,
                                   const void* g, const void* h, const float* s0, void* o, float* s_final, char* ws,
-                                  void* hs, int rev, hipStream_t stream) {
+                                  void* hs, int rev, hipStream_t stream, const void* init_t = nullptr) {
     Shape s{B, T, H, K, V, true};
     Plan p = make_fwd_general_plan(s);
     FwdLaunch a{};
@@ -217,6 +206,7 @@ static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void*
     a.ws_rec = ws + fwd_general_seg_bytes(s, p);
     a.ws_hs = hs;
     a.rev = rev;
+    a.init_t = init_t;
     a.stream = stream;
     return a;
 }
@@ -229,8 +219,6 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     const bool ck = L.hs_in != nullptr;  // the forward's results come in
     const bf16* o = ck ? static_cast<const bf16*>(L.o_in) : reinterpret_cast<bf16*>(ws + w.o);
     const float* st = ck ? L.st_in : reinterpret_cast<float*>(ws + w.st);
-    float* s0T = L.s0 ? reinterpret_cast<float*>(ws + w.s0t) : nullptr;
-    float* dhtT = L.dht ? reinterpret_cast<float*>(ws + w.dhtt) : nullptr;
     const bf16* hsf = ck ? static_cast<const bf16*>(L.hs_in) : reinterpret_cast<bf16*>(ws + w.hsf);
     bf16* hsr = reinterpret_cast<bf16*>(ws + w.hsr);
     float* ag = reinterpret_cast<float*>(ws + w.ag);
@@ -240,18 +228,17 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     hipError_t err;
     const long nst = BH * KV;
     const unsigned gst = (unsigned)((nst + 255) / 256);
-    // forward (o, S_T and the state before every chunk), unless given, and the
-    // transposed initial / final-state gradient
+    // forward (o, S_T and the state before every chunk), unless given
     if (!ck) {
         err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, ws + w.o,
                                                   reinterpret_cast<float*>(ws + w.st), fws, ws + w.hsf, 0, sm));
         if (err != hipSuccess) return err;
     }
-    if (L.s0) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.s0, s0T, K, V, nst);
-    if (L.dht) GLA_LAUNCH("bwdg_transpose", gla_transpose_state, dim3(gst), dim3(256), sm, L.dht, dhtT, K, V, nst);
-    // dq: the transposed state's forward
-    err = launch_fwd_general(
-        general_fwd_args(B, T, H, V, K, L.d_o, L.v, L.k, L.h, L.g, s0T, L.dq, nullptr, fws, nullptr, 0, sm));
+    // dq: the transposed state's forward; its states at every chunk boundary are
+    // the transposes of the forward's, so each segment starts from one of those
+    // (segment 0 from S_0^T) and no state pass runs
+    err = launch_fwd_general(general_fwd_args(B, T, H, V, K, L.d_o, L.v, L.k, L.h, L.g, L.s0, L.dq, nullptr, fws,
+                                              nullptr, 0, sm, hsf));
     if (err != hipSuccess) return err;
     // dv and dS_0' from the time-reversed recurrence of dS (its gates one token
     // later), read and written in place in the input's token order
@@ -260,9 +247,10 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     if (err != hipSuccess) return err;
     if (ds0) GLA_LAUNCH("bwdg_scale_ds0", gla_scale_ds0, dim3(gst), dim3(256), sm, ds0, (const bf16*)L.g,
                         (const bf16*)L.h, T, H, K, V, nst);
-    // dk from the time-reversed recurrence of dS^T
-    err = launch_fwd_general(
-        general_fwd_args(B, T, H, V, K, L.v, L.d_o, L.q, L.h, L.g, dhtT, L.dk, nullptr, fws, nullptr, 1, sm));
+    // dk from the time-reversed recurrence of dS^T, whose segments start from
+    // the transposes of the dv pass's states (segment 0 from dht^T)
+    err = launch_fwd_general(general_fwd_args(B, T, H, V, K, L.v, L.d_o, L.q, L.h, L.g, L.dht, L.dk, nullptr, fws,
+                                              nullptr, 1, sm, hsr));
     if (err != hipSuccess) return err;
     // gate gradients: anchors at the chunk boundaries, then each chunk's reverse sums
     const unsigned N = (unsigned)(T / 64);

@@ -52,6 +52,18 @@ struct StateRegs {
                 for (int r = 0; r < 4; ++r)
                     s[a][c][r] = Elem<U>::to_f(src[(long)(16 * a + 4 * (l >> 4) + r) * ld + col0 + 16 * c + (l & 15)]);
     }
+    // the transpose of a [cols][ld] array: element (i, j) from src[j * ld + i]
+    template <typename U>
+    __device__ __forceinline__ void load_t(const U* __restrict__ src, long ld, int col0) {
+        const int l = lane_id();
+#pragma unroll
+        for (int a = 0; a < KD / 16; ++a)
+#pragma unroll
+            for (int c = 0; c < CB; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s[a][c][r] = Elem<U>::to_f(src[(long)(col0 + 16 * c + (l & 15)) * ld + 16 * a + 4 * (l >> 4) + r]);
+    }
     template <typename U>
     __device__ __forceinline__ void store(U* __restrict__ dst, long ld, int col0) const {
         const int l = lane_id();

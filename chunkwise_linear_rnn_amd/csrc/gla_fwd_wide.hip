@@ -102,6 +102,22 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
     GLA_LAUNCH("fwd_general_vprep", (gla_fwd_general_vprep<T, KD, VP>),
                dim3((unsigned)(a.BH * a.N), (unsigned)(a.V / VP)), dim3(256), a.stream, (const T*)a.v,
                (const T*)a.h, rec, a.T, a.H, a.V, a.N, a.rev);
+    const dim3 gw((unsigned)xcd_grid(a.P * a.BH, nvb));
+    if (a.init_t) {
+        // every segment starts from the transpose of a known state: no state pass, no combine
+        if (a.ws_hs) return hipErrorInvalidValue;
+        if (a.rev)
+            GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true, false, true, true>), gw,
+                       dim3(512), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.init_t, a.s0,
+                       (T*)a.o, a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P,
+                       (int)a.BH, (float*)nullptr, (T*)nullptr);
+        else
+            GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true, false, false, true>), gw,
+                       dim3(512), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.init_t, a.s0,
+                       (T*)a.o, a.s_final, (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P,
+                       (int)a.BH, (float*)nullptr, (T*)nullptr);
+        return hipGetLastError();
+    }
     if (a.P > 1) {
         const int nseg = a.P - 1;
         GLA_LAUNCH("fwd_general_seg_state", (gla_fwd_wide_walk<T, KD, BV, false, true>),
@@ -113,7 +129,6 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
                    dim3(256), a.stream, a.s0, (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD,
                    a.V, a.P);
     }
-    const dim3 gw((unsigned)xcd_grid(a.P * a.BH, nvb));
     if (a.ws_hs && a.rev)
         GLA_LAUNCH("fwd_general_walk_hs", (gla_fwd_wide_walk<T, KD, BV, true, true, true, true>), gw, dim3(512),
                    a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,

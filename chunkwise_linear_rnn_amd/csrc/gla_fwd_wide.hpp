@@ -427,8 +427,12 @@ struct WideSmem {
 // state pass also writes the segment's column log2 decays to ws_gateb, and the
 // output walk with HS the state before every chunk to hs_out.  REV (GEN output
 // walk): the records are those of the time-reversed sequence, and the output
-// of its token t goes to row T-1-t.
-template <typename T, int KD, int BV, bool OUT, bool GEN = false, bool HS = false, bool REV = false>
+// of its token t goes to row T-1-t.  TI (GEN output walk): each segment's
+// initial state is the transpose of a known state of the transposed recurrence,
+// ws_init[bh][chunk][V][KD] at the segment's first chunk (segment 0: s0 given as
+// [V][KD]), so no state pass or combine precedes the walk.
+template <typename T, int KD, int BV, bool OUT, bool GEN = false, bool HS = false, bool REV = false,
+          bool TI = false>
 __global__ void __launch_bounds__(512)
 gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v, const T* __restrict__ ws_init,
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
@@ -547,9 +551,15 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
 
     // ---------------- consumers: the state and the matrix products
     StateRegs<KD, CB> S;
-    if (OUT && seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
-    else if (OUT && s0) S.load(s0 + (long)bh * KD * V, V, col0);
-    else S.zero();
+    if constexpr (TI) {
+        if (seg > 0) S.load_t(ws_init + ((long)bh * N + (long)seg * seg_len) * KD * V, KD, col0);
+        else if (s0) S.load_t(s0 + (long)bh * KD * V, KD, col0);
+        else S.zero();
+    } else {
+        if (OUT && seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
+        else if (OUT && s0) S.load(s0 + (long)bh * KD * V, V, col0);
+        else S.zero();
+    }
     // HS (general mode): the state before every chunk to hs_out, [BH][N][KD][V];
     // each is written after the previous chunk's update, when little else is live
     if constexpr (OUT && GEN && HS) {

@@ -29,6 +29,9 @@ struct FwdLaunch {
     void* ws_hs;      // general gates, optional: the state before every chunk, [BH][N][K][V] bf16
     int rev;          // general gates: run the time-reversed sequence in place (token t = input token T-1-t,
                       // its gate the input's gate of token T-t, none at t = 0; o written at row T-1-t)
+    const void* init_t;  // general gates, optional: the state before every chunk of the transposed recurrence,
+                         // [BH][N][V][K] bf16; segments start from its transposes (s0 then also given as
+                         // [V][K]) and no state pass or combine runs
     void* ckpt;       // optional: the state before every ck_len-th chunk, [BH][ck_P][K][V] input dtype
     int ck_len, ck_P;
     hipStream_t stream;

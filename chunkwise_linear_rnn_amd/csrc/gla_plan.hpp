@@ -147,13 +147,14 @@ inline size_t fwd_general_workspace_bytes(const Shape& s) {
     return fwd_general_seg_bytes(s, p) + (size_t)p.BH * p.N * gen_record_bytes(s.K, s.V);
 }
 
-// Backward under general gates: the forward's o and S_T, transposed S_0 and
-// dht, the chunk-start states of the forward and of the time-reversed dS
-// recurrence with the gate-gradient anchors formed from them, and the forward
-// workspace of the largest of the four general forwards it runs (shapes K x V
-// and V x K).  The reversed recurrences read their inputs in place.
+// Backward under general gates: the forward's o and S_T, the chunk-start
+// states of the forward and of the time-reversed dS recurrence (the anchors of
+// the gate gradients, and the starting states of the transposed passes) with
+// the anchors formed from them, and the forward workspace of the largest of the
+// four general forwards it runs (shapes K x V and V x K).  The reversed
+// recurrences read their inputs in place.
 struct BwdGeneralLayout {
-    size_t o, st, s0t, dhtt, hsf, hsr, ag, ah, fws, total;
+    size_t o, st, hsf, hsr, ag, ah, fws, total;
 };
 inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
     BwdGeneralLayout w{};
@@ -166,8 +167,6 @@ inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
     size_t at = 0;
     w.o = at; at += tv;
     w.st = at; at += sf;
-    w.s0t = at; at += sf;
-    w.dhtt = at; at += sf;
     const size_t N = (size_t)(s.T / 64);
     w.hsf = at; at += round256(BH * N * KV * 2);
     w.hsr = at; at += round256(BH * N * KV * 2);
