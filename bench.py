@@ -162,7 +162,15 @@ LAUNCH_LABEL = {
     "gla_seg_combine_bwd": "combine_bwd", "gla_bwd_dq_pipe": "bwd_dq_walk", "gla_bwd_dq": "bwd_dq_walk",
     "gla_bwd_dk_pipe": "bwd_dk_walk", "gla_bwd_dk": "bwd_dk_walk", "gla_bwd_dv_pipe": "bwd_dv_walk",
     "gla_bwd_dv": "bwd_dv_walk", "gla_fwd_wide_prep": "fwd_prep", "gla_fwd_wide_walk": "fwd_walk",
+    "gla_fwd_general_vprep": "fwd_general_vprep", "gla_seg_combine_fwd_general": "combine_fwd_general",
+    "gla_gate_anchor": "bwdg_gate_anchor", "gla_gate_grad_out": "bwdg_gate_out", "gla_scale_ds0": "bwdg_scale_ds0",
+    "gla_state_copy": "state_copy", "gla_decode_kernel": "decode",
 }
+
+
+def _is_lib(name: str) -> bool:
+    """A kernel of this library (rocprofv3 prints some names mangled, some demangled)."""
+    return "3gla" in name or "gla::" in name
 
 
 def _kernel_base(mangled: str) -> str:
@@ -202,7 +210,7 @@ def _short(demangled: str) -> str:
 def summarize_trace(csv_path, out_md, title, command):
     """Markdown table from a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
     import csv
-    rows = [r for r in csv.DictReader(open(csv_path)) if "3gla" in r["Name"]]  # the library's kernels
+    rows = [r for r in csv.DictReader(open(csv_path)) if _is_lib(r["Name"])]  # the library's kernels
     names = _demangle([r["Name"] for r in rows])
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     lines = ["# Kernel times: %s (MI355X, rocprofv3 kernel trace)" % title, "",
@@ -254,7 +262,7 @@ def summarize_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, workload, co
     wm = _per_kernel_means(_counter_rows(write_csv))
     kernels = {}
     for name in fm:
-        if name not in wm or "3gla" not in name:  # the library's kernels only (not torch's scrub or fills)
+        if name not in wm or not _is_lib(name):  # the library's kernels only (not torch's scrub or fills)
             continue
         base = _kernel_base(name)
         label = LAUNCH_LABEL.get(base, base)
@@ -290,7 +298,7 @@ def summarize_pmc(csv_path, trace_csv, out_md, title, command):
     kernel-trace durations: MfmaUtil = busy MFMA cycles over (GPU active cycles x
     1024 SIMDs); bf16 flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
     import csv
-    means = {n: m for n, m in _per_kernel_means(_counter_rows(csv_path)).items() if "3gla" in n}
+    means = {n: m for n, m in _per_kernel_means(_counter_rows(csv_path)).items() if _is_lib(n)}
     dur = {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(trace_csv))}
     names = list(means)
     dem = dict(zip(names, _demangle(names)))
@@ -323,7 +331,7 @@ def summarize_stalls(csv_path, out_md, title, command):
     conflict share of LDS-active cycles."""
     acc = {}
     for (_, name), d in _counter_rows(csv_path).items():
-        if "3gla" not in name:
+        if not _is_lib(name):
             continue
         a = acc.setdefault(name, {})
         for k, v in d.items():
