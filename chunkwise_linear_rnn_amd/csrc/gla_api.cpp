@@ -267,9 +267,11 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
         a.s_final = s_final;
         float* ck_st = nullptr;
         if (ckpt) {
+            // S_T goes to the checkpoint, and to s_final too when the caller asks for it
             ck_st = reinterpret_cast<float*>(static_cast<char*>(ckpt) + general_ckpt_st_offset(s));
             a.ws_hs = ckpt;
             a.s_final = ck_st;
+            a.s_final2 = s_final;
         }
         char* ws = static_cast<char*>(workspace);
         if (p.P > 1) {
@@ -281,8 +283,6 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
         a.ws_rec = ws + gla::fwd_general_seg_bytes(s, p);
         a.stream = strm;
         err = gla::launch_fwd_general(a);
-        if (err == hipSuccess && ckpt && s_final)
-            err = gla::launch_state_copy(ck_st, s_final, s.B * s.H * s.K * s.V, strm);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;

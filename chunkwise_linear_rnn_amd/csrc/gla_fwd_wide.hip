@@ -138,7 +138,7 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
         GLA_LAUNCH("fwd_general_walk_hs", (gla_fwd_wide_walk<T, KD, BV, true, true, true>), gw, dim3(512), a.stream,
                    (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final,
                    (T*)nullptr, (float*)nullptr, a.T, a.H, a.V, a.N, a.P, a.seg_len, a.P, (int)a.BH, (float*)nullptr,
-                   (T*)a.ws_hs);
+                   (T*)a.ws_hs, a.s_final2);
     else if (a.rev)
         GLA_LAUNCH("fwd_general_walk", (gla_fwd_wide_walk<T, KD, BV, true, true, false, true>), gw, dim3(512),
                    a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,

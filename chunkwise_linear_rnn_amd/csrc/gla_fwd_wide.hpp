@@ -425,7 +425,8 @@ struct WideSmem {
 // output is (Ql S) * exp2(C_t) plus the record's intra-chunk output, and the
 // state's columns decay by exp2(C_63) as its rows do by the key-side gate; the
 // state pass also writes the segment's column log2 decays to ws_gateb, and the
-// output walk with HS the state before every chunk to hs_out.  REV (GEN output
+// output walk with HS the state before every chunk to hs_out (and S_T to
+// s_final2 as well as s_final, when given).  REV (GEN output
 // walk): the records are those of the time-reversed sequence, and the output
 // of its token t goes to row T-1-t.  TI (GEN output walk): each segment's
 // initial state is the transpose of a known state of the transposed recurrence,
@@ -438,7 +439,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                   const float* __restrict__ s0, T* __restrict__ o, float* __restrict__ s_final,
                   T* __restrict__ ws_state, float* __restrict__ ws_gate, int T_, int H, int V, int N, int P,
                   int seg_len, int nseg, int BH, float* __restrict__ ws_gateb = nullptr,
-                  T* __restrict__ hs_out = nullptr) {
+                  T* __restrict__ hs_out = nullptr, float* __restrict__ s_final2 = nullptr) {
     constexpr int NC = 4, NP = 64 * NC;  // consumer waves; producer threads
     using Sm = WideSmem<T, KD, BV, OUT, GEN>;
     using R = WideRec<KD>;
@@ -748,6 +749,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
     }
     if constexpr (OUT) {
         if (s_final && seg == P - 1) S.store(s_final + (long)bh * KD * V, V, col0);
+        if (s_final2 && seg == P - 1) S.store(s_final2 + (long)bh * KD * V, V, col0);
     } else {
         S.store(ws_state + ((long)bh * P + seg) * (long)KD * V, V, col0);
     }

@@ -29,6 +29,7 @@ struct FwdLaunch {
     void* ws_hs;      // general gates, optional: the state before every chunk, [BH][N][K][V] bf16
     int rev;          // general gates: run the time-reversed sequence in place (token t = input token T-1-t,
                       // its gate the input's gate of token T-t, none at t = 0; o written at row T-1-t)
+    float* s_final2;     // general gates, optional: S_T also here (the forward's checkpoint)
     const void* init_t;  // general gates, optional: the state before every chunk of the transposed recurrence,
                          // [BH][N][V][K] bf16; segments start from its transposes (s0 then also given as
                          // [V][K]) and no state pass or combine runs
