@@ -99,7 +99,7 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
     unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);
     GLA_LAUNCH("fwd_prep", (gla_fwd_wide_prep<T, KD, false>), dim3((unsigned)(a.BH * a.N)), dim3(256), a.stream,
                (const T*)a.q, (const T*)a.k, (const T*)a.g, rec, a.T, a.H, a.N, (long)GenRec<KD>::bytes(a.V), a.rev);
-    GLA_LAUNCH("fwd_general_vprep", (gla_fwd_general_vprep<T, KD, VP>),
+    GLA_LAUNCH("fwd_general_vprep", (gla_fwd_general_vprep<T, KD, VP, WideSmem<T, KD, BV, true, true>::WI>),
                dim3((unsigned)(a.BH * a.N), (unsigned)(a.V / VP)), dim3(256), a.stream, (const T*)a.v,
                (const T*)a.h, rec, a.T, a.H, a.V, a.N, a.rev);
     const dim3 gw((unsigned)xcd_grid(a.P * a.BH, nvb));

@@ -68,7 +68,8 @@ struct GenRec {
     static constexpr long oCs(int V) { return oVp + 2L * kChunk * V; }      // [64][V]  exp2(C_t)
     static constexpr long oOi(int V) { return oCs(V) + 2L * kChunk * V; }   // [64][V]  intra-chunk output
     static constexpr long oPB(int V) { return oOi(V) + 2L * kChunk * V; }   // fp32 [2][V]: exp2(C_63), C_63
-    static constexpr long bytes(int V) { return oPB(V) + 8L * V; }
+    static constexpr long oVF(int V) { return oPB(V) + 8L * V; }            // int [16]: value pass out of range
+    static constexpr long bytes(int V) { return oVF(V) + 64; }
 };
 
 template <typename T, int KD>
@@ -230,7 +231,9 @@ struct GenPrepSmem {
 // element when some column's C_63 leaves the basis range (exp2(-C) would not
 // stay a well-scaled fp32/bf16 value).  rev: the time-reversed sequence, read in
 // place as gla_fwd_wide_prep reads it (values at token T-1-t, gates at T-t).
-template <typename T, int KD, int VP>
+// The pass's range flag goes to the record; WI (the walk forms the intra-chunk
+// output itself from A and Vp): the output is stored for flagged passes only.
+template <typename T, int KD, int VP, bool WI>
 __global__ void __launch_bounds__(256)
 gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigned char* __restrict__ rec, int T_,
                       int H, int V, int N, int rev = 0) {
@@ -252,14 +255,16 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
     const long rowh = rev ? row0 + 1 : row0;
     const long rstep = rev ? -(long)rsV : (long)rsV;
     unsigned char* r = rec + unit * G::bytes(V);
-    {
+    // A of the chunk (from the key side), for the intra-chunk output
+    auto load_a = [&]() {
         const T* a = reinterpret_cast<const T*>(r + G::oA);
 #pragma unroll
         for (int i = 0; i < kChunk * kChunk / 8 / NT; ++i) {
             const int p = tid + i * NT, row = p / (kChunk / 8), col = (p % (kChunk / 8)) * 8;
             *reinterpret_cast<u32x4*>(sm.A + row * Sm::pA + col) = *reinterpret_cast<const u32x4*>(a + row * kChunk + col);
         }
-    }
+    };
+    if constexpr (!WI) load_a();
     // ---- value side, VP columns per pass; thread (part, cv) scans columns
     // 8cv .. 8cv+7 over tokens part*TPP .. +TPP-1 with 16-byte loads and stores
     T* oVp = reinterpret_cast<T*>(r + G::oVp);
@@ -289,7 +294,7 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
         if (tid == 0) sm.flagb = 0;
         *reinterpret_cast<f32x4*>(&sm.tot[part][jv]) = f32x4{cl[TPP - 1][0], cl[TPP - 1][1], cl[TPP - 1][2], cl[TPP - 1][3]};
         *reinterpret_cast<f32x4*>(&sm.tot[part][jv + 4]) = f32x4{cl[TPP - 1][4], cl[TPP - 1][5], cl[TPP - 1][6], cl[TPP - 1][7]};
-        __syncthreads();  // B1: part totals and A visible, flag cleared
+        __syncthreads();  // B1: part totals (and A) visible, flag cleared
         float off[8], c63[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) off[e] = c63[e] = 0.f;
@@ -318,6 +323,8 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
         }
         __syncthreads();  // B2: the pass's flag
         const bool fl = sm.flagb != 0;
+        if (tid == 0) reinterpret_cast<int*>(r + G::oVF(V))[blockIdx.y] = fl ? 1 : 0;
+        if (WI && fl) load_a();  // visible after B3
 #pragma unroll
         for (int i = 0; i < TPP; ++i) {
             const int t = t0 + i;
@@ -339,7 +346,7 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
             *reinterpret_cast<f32x4*>(sm.Cl + t * Sm::pC + jv + 4) = *reinterpret_cast<const f32x4*>(ct8 + 4);
         }
         __syncthreads();  // B3: Vt and Cl complete
-        if (!fl) {
+        if (!fl && !WI) {
             const int c0 = w * (VP / NW);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
@@ -367,7 +374,7 @@ gla_fwd_general_vprep(const T* __restrict__ v, const T* __restrict__ hg, unsigne
                     *reinterpret_cast<vec4_t<T>*>(oOi + t * V + j0 + jc) = to_vec4<T>(o4);
                 }
             }
-        } else {
+        } else if (fl) {
             for (int t = epart; t < kChunk; t += NT / VP) {
                 const float ct = sm.Cl[t * Sm::pC + jj];
                 float acc = 0.f;
@@ -393,16 +400,21 @@ struct WideSmem {
     // two-byte columns keeps the four rows of a 16-lane group on disjoint banks
     static constexpr int pW = CW;
     static_assert(CW == 16 || CW == 32, "value slice width");
+    // general output walk at KD <= 128: the intra-chunk output is formed here
+    // from A and the record's v * exp2(C_63 - C_t), unless the value pass is
+    // out of range (then the record holds it)
+    static constexpr bool WI = GEN && OUT && KD <= 128;
     // two buffers of everything but Ql, which the output walk refills between
     // the inter-chunk product and the rest of the chunk
     alignas(16) T KtT[2][KD * pKtT];
     alignas(16) T Vw[2][NC * kChunk * pW];
     alignas(16) float pp[2][2 * KD];  // pre, post
-    alignas(16) T A[OUT && !GEN ? 2 : 1][OUT && !GEN ? kChunk * pA : 8];
+    alignas(16) T A[OUT && (!GEN || WI) ? 2 : 1][OUT && (!GEN || WI) ? kChunk * pA : 8];
     alignas(16) T Ql[OUT ? kChunk * pQl : 8];
     // general gates: exp2(C_63) of the block's value columns
     alignas(16) float pb[GEN ? 2 : 1][GEN ? BV : 4];
     int flag[2];
+    int vflag[2];  // WI: the value pass of the chunk is out of range
 };
 
 // The state pass (OUT = false: segments 0 .. nseg-1 from a zero state, the
@@ -477,7 +489,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             TileRegs<T, CW, 64> v;
             f32x4 pp;
             float bl, gb, cb;
-            int flag;
+            int flag, vflag;
         };
         Regs ra, rb;
         auto fetch = [&](Regs& x, int c) {
@@ -485,7 +497,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
             x.Kt.load(reinterpret_cast<const T*>(r + oKtT), KD, ptid);
             if constexpr (OUT) {
                 x.Ql.load(reinterpret_cast<const T*>(r + oQl), KD, ptid);
-                if constexpr (!GEN) x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
+                if constexpr (!GEN || Sm::WI) x.A.load(reinterpret_cast<const T*>(r + R::oA), kChunk, ptid);
             }
             const float* pp = reinterpret_cast<const float*>(r + oPP);
             if (ptid < KD / 2) x.pp = *reinterpret_cast<const f32x4*>(pp + 4 * ptid);
@@ -498,6 +510,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                     x.gb = pbg[vb * BV + ptid];
                     if (!OUT) x.cb = pbg[V + vb * BV + ptid];
                 }
+                if (Sm::WI && ptid == 0) x.vflag = reinterpret_cast<const int*>(r + G::oVF(V))[vb];
             } else {
                 x.v.load(v + ((long)b * T_ + (long)c * kChunk) * rsV + (long)h * V + col0, rsV, l);
             }
@@ -510,7 +523,8 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                 const int q = ptid + i * NP;
                 *reinterpret_cast<u32x4*>(sm.KtT[bf] + (q / (kChunk / 8)) * Sm::pKtT + (q % (kChunk / 8)) * 8) = x.Kt.r[i];
             }
-            if constexpr (OUT && !GEN) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
+            if constexpr (OUT && (!GEN || Sm::WI)) x.A.store_lds(sm.A[bf], Sm::pA, ptid);
+            if (Sm::WI && ptid == 0) sm.vflag[bf] = x.vflag;
             if (ptid < KD / 2) *reinterpret_cast<f32x4*>(sm.pp[bf] + 4 * ptid) = x.pp;
             if (!OUT && ptid < KD) gtot += x.bl;
             if (ptid == 0) sm.flag[bf] = x.flag;
@@ -575,6 +589,8 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         // general gates: this lane's exp2(C_t) and intra-chunk output values,
         // loaded from the record now and used after the matrix products
         vec4_t<T> csr[GEN && OUT ? 4 : 1][CB], oir[GEN && OUT ? 4 : 1][CB];
+        // WI: the record's intra-chunk output is read only for a value pass out of range
+        const bool vfl = Sm::WI ? sm.vflag[bf] != 0 : true;
         if constexpr (GEN && OUT) {
             const unsigned char* r = rec + ((long)bh * N + c) * rbytes;
             const T* csg = reinterpret_cast<const T*>(r + G::oCs(V)) + col0;
@@ -585,7 +601,7 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
                 for (int cb = 0; cb < CB; ++cb) {
                     const int off = (16 * rb + (l & 15)) * V + 16 * cb + 4 * (l >> 4);
                     csr[rb][cb] = *reinterpret_cast<const vec4_t<T>*>(csg + off);
-                    oir[rb][cb] = *reinterpret_cast<const vec4_t<T>*>(oig + off);
+                    oir[rb][cb] = vfl ? *reinterpret_cast<const vec4_t<T>*>(oig + off) : vec4_t<T>{};
                 }
         }
         if constexpr (OUT) {
@@ -632,8 +648,37 @@ gla_fwd_wide_walk(const unsigned char* __restrict__ rec, const T* __restrict__ v
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) vf[sb][cb] = frag_cm<T>(Vw, Sm::pW, 16 * sb, 16 * cb);
+        if constexpr (Sm::WI) {
+            // in range: O^T += (A Vp) / exp2(C_63), i.e. A (v * exp2(-C_t)), per column
+            if (!vfl) {
+                float ig[CB][4];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ig[cb][e] = __builtin_amdgcn_rcpf(sm.pb[bf][w * CW + 16 * cb + 4 * (l >> 4) + e]);
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    f32x4 t4[CB];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) t4[cb] = zero4();
+#pragma unroll
+                    for (int ks2 = 0; ks2 <= rb / 2; ++ks2) {
+                        const vec4_t<T> blo = frag_rm<T>(sm.A[bf], Sm::pA, 16 * rb, 32 * ks2);
+                        const vec4_t<T> bhi = frag_rm<T>(sm.A[bf], Sm::pA, 16 * rb, 32 * ks2 + 16);
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            t4[cb] = mma32(t4[cb], vf[2 * ks2][cb], vf[2 * ks2 + 1][cb], blo, bhi);
+                    }
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[rb][cb][e] += t4[cb][e] * ig[cb][e];
+                }
+            }
+        }
         if constexpr (OUT && GEN) {
-            // O = (Ql S) * exp2(C_t) + the record's intra-chunk output; slot e:
+            // O = (Ql S + intra) * exp2(C_t) + the record's intra-chunk output; slot e:
             // column 16cb + 4(l/16) + e of the slice, token 16rb + l%16 (REV:
             // the time-reversed sequence's token, written to row T-1-t)
             const long orow = REV ? (long)b * T_ + T_ - 1 - (long)c * kChunk : (long)b * T_ + (long)c * kChunk;
