@@ -139,10 +139,10 @@ gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, cons
 // part*TPP .. +TPP-1 with 16-byte loads, sums them in reverse, and adds the
 // totals of the later parts (through LDS) and the anchor.
 template <int D>
-__global__ void __launch_bounds__(256)
-gla_gate_grad_out(const bf16* __restrict__ a, const bf16* __restrict__ da, const bf16* __restrict__ c,
-                  const bf16* __restrict__ dc, const float* __restrict__ anchor, bf16* __restrict__ out, int T,
-                  int H) {
+__device__ __forceinline__ void gate_grad_chunk(const bf16* __restrict__ a, const bf16* __restrict__ da,
+                                                const bf16* __restrict__ c, const bf16* __restrict__ dc,
+                                                const float* __restrict__ anchor, bf16* __restrict__ out, int T,
+                                                int H) {
     constexpr int CV = D / 8, NPART = 256 / CV, TPP = kChunk / NPART;
     static_assert(NPART * CV == 256 && NPART * TPP == kChunk, "gate-gradient tiling");
     __shared__ float tot[NPART][D];
@@ -187,6 +187,20 @@ gla_gate_grad_out(const bf16* __restrict__ a, const bf16* __restrict__ da, const
     }
 }
 
+// Both gate gradients in one launch: blockIdx.z = 0 the key side (dg from q,
+// dq, k, dk), 1 the value side (dh from o, d_o, v, dv).
+template <int DK, int DV>
+__global__ void __launch_bounds__(256)
+gla_gate_grad_out(const bf16* __restrict__ q, const bf16* __restrict__ dq, const bf16* __restrict__ k,
+                  const bf16* __restrict__ dk, const float* __restrict__ ag, bf16* __restrict__ dg,
+                  const bf16* __restrict__ o, const bf16* __restrict__ d_o, const bf16* __restrict__ v,
+                  const bf16* __restrict__ dv, const float* __restrict__ ah, bf16* __restrict__ dh, int T, int H) {
+    if (blockIdx.z == 0)
+        gate_grad_chunk<DK>(q, dq, k, dk, ag, dg, T, H);
+    else
+        gate_grad_chunk<DV>(o, d_o, v, dv, ah, dh, T, H);
+}
+
 static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void* q, const void* k, const void* v,
                                   const void* g, const void* h, const float* s0, void* o, float* s_final, char* ws,
                                   void* hs, int rev, hipStream_t stream, const void* init_t = nullptr) {
@@ -226,8 +240,6 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     char* fws = ws + w.fws;
     hipStream_t sm = L.stream;
     hipError_t err;
-    const long nst = BH * KV;
-    const unsigned gst = (unsigned)((nst + 255) / 256);
     // forward (o, S_T and the state before every chunk), unless given
     if (!ck) {
         err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.q, L.k, L.v, L.g, L.h, L.s0, ws + w.o,
@@ -245,8 +257,11 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     float* ds0 = L.ds0;
     err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.k, L.q, L.d_o, L.g, L.h, L.dht, L.dv, ds0, fws, hsr, 1, sm));
     if (err != hipSuccess) return err;
-    if (ds0) GLA_LAUNCH("bwdg_scale_ds0", gla_scale_ds0, dim3(gst), dim3(256), sm, ds0, (const bf16*)L.g,
-                        (const bf16*)L.h, T, H, K, V, nst);
+    if (ds0) {
+        const long nst = BH * KV;
+        GLA_LAUNCH("bwdg_scale_ds0", gla_scale_ds0, dim3((unsigned)((nst + 255) / 256)), dim3(256), sm, ds0,
+                   (const bf16*)L.g, (const bf16*)L.h, T, H, K, V, nst);
+    }
     // dk from the time-reversed recurrence of dS^T, whose segments start from
     // the transposes of the dv pass's states (segment 0 from dht^T)
     err = launch_fwd_general(general_fwd_args(B, T, H, V, K, L.v, L.d_o, L.q, L.h, L.g, L.dht, L.dk, nullptr, fws,
@@ -263,19 +278,17 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
             GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor<256>, ga, dim3(256), sm, (const bf16*)hsf,
                        (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K);
     }
-    const dim3 gg(N, (unsigned)BH);
-    if (K == 128)
-        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<128>, gg, dim3(256), sm, (const bf16*)L.q, (const bf16*)L.dq,
-                   (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag, static_cast<bf16*>(L.dg), T, H);
-    else
-        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<256>, gg, dim3(256), sm, (const bf16*)L.q, (const bf16*)L.dq,
-                   (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag, static_cast<bf16*>(L.dg), T, H);
-    if (V == 128)
-        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<128>, gg, dim3(256), sm, o, (const bf16*)L.d_o,
-                   (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah, static_cast<bf16*>(L.dh), T, H);
-    else
-        GLA_LAUNCH("bwdg_gate_out", gla_gate_grad_out<256>, gg, dim3(256), sm, o, (const bf16*)L.d_o,
-                   (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah, static_cast<bf16*>(L.dh), T, H);
+    const dim3 gg(N, (unsigned)BH, 2);
+#define GLA_GATE_OUT(DK_, DV_)                                                                                  \
+    GLA_LAUNCH("bwdg_gate_out", (gla_gate_grad_out<DK_, DV_>), gg, dim3(256), sm, (const bf16*)L.q,           \
+               (const bf16*)L.dq, (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag, static_cast<bf16*>(L.dg), \
+               o, (const bf16*)L.d_o, (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah,                      \
+               static_cast<bf16*>(L.dh), T, H)
+    if (K == 128 && V == 128) GLA_GATE_OUT(128, 128);
+    else if (K == 128) GLA_GATE_OUT(128, 256);
+    else if (V == 128) GLA_GATE_OUT(256, 128);
+    else GLA_GATE_OUT(256, 256);
+#undef GLA_GATE_OUT
     return hipGetLastError();
 }
 
