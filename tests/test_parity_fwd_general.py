@@ -73,6 +73,25 @@ def test_fwd_general_exact_paths():
     _check(w, inp, h.to(torch.bfloat16), [(0, 0), (3, 3), (1, 2)])
 
 
+@pytest.mark.parametrize("V", [128, 64])
+def test_fwd_general_exact_paths_k128(V):
+    # at K = 128 the output walk forms the intra-chunk output itself for value
+    # passes in range and takes the record's for passes out of range: a
+    # key-side reset at token 70, value-side resets at token 140 (all columns)
+    # and 330 (one column), and -9 per token over 300..309 in half the columns
+    B, H, T, K = 2, 4, 64 * 9, 128
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=False, seed=1430 + V)
+    inp = gi.make_inputs(w)
+    g = inp["g"].float()
+    g[0, 70, 0, :7] = -70.0
+    inp["g"] = g.to(torch.bfloat16)
+    h = gi.make_value_gate(B, T, H, V, seed=1440 + V).float()
+    h[0, 140, 0, :] = -70.0
+    h[1, 300:310, 2, V // 2:] = -9.0
+    h[1, 330, 3, 5] = -80.0
+    _check(w, inp, h.to(torch.bfloat16), [(0, 0), (1, 2), (1, 3), (0, 1)])
+
+
 def test_fwd_general_zero_value_gate_matches_gla_fwd():
     # beta = 1 is the key-side-only operator: the same oracle values as gla_fwd
     B, H, T, K, V = 2, 4, 64 * 7, 128, 256
