@@ -94,6 +94,7 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
     static_assert(sizeof(GenPrepSmem<T, VP>) <= 80 * 1024, "two value-side workgroups per CU");
     static_assert(sizeof(WideSmem<T, KD, BV, true, true>) <= 160 * 1024, "LDS budget");
     static_assert(GenRec<KD>::bytes(512) == (long)gen_record_bytes(KD, 512), "record size as the workspace plans it");
+    static_assert(GenRec<KD>::bytes(64) % 256 == 0 && GenRec<KD>::bytes(128) % 256 == 0, "records stay 256-byte aligned");
     if ((long)GenRec<KD>::bytes(a.V) != (long)gen_record_bytes(KD, a.V)) return hipErrorInvalidValue;
     const int nvb = a.V / BV;
     unsigned char* rec = static_cast<unsigned char*>(a.ws_rec);

@@ -69,7 +69,9 @@ struct GenRec {
     static constexpr long oOi(int V) { return oCs(V) + 2L * kChunk * V; }   // [64][V]  intra-chunk output
     static constexpr long oPB(int V) { return oOi(V) + 2L * kChunk * V; }   // fp32 [2][V]: exp2(C_63), C_63
     static constexpr long oVF(int V) { return oPB(V) + 8L * V; }            // int [16]: value pass out of range
-    static constexpr long bytes(int V) { return oVF(V) + 64; }
+    // 256 bytes for the flags keep every record 256-byte aligned (as the record
+    // without them is): an unaligned record splits each row across one more line
+    static constexpr long bytes(int V) { return oVF(V) + 256; }
 };
 
 template <typename T, int KD>

@@ -133,7 +133,7 @@ inline Plan make_fwd_general_plan(const Shape& s) {
     return p;
 }
 constexpr size_t gen_record_bytes(int64_t K, int64_t V) {
-    return wide_record_bytes(K) + (size_t)(6 * 64 * V + 8 * V + 64);
+    return wide_record_bytes(K) + (size_t)(6 * 64 * V + 8 * V + 256);
 }
 // segment states, key-row and value-column gate totals (P > 1), then records
 inline size_t fwd_general_seg_bytes(const Shape& s, const Plan& p) {

@@ -241,7 +241,7 @@ gla_status_t gla_fwd_general(const gla_shape_t* shape,
 /* Bytes of device workspace gla_fwd_general needs (0 for fp32, K = 64 or an invalid
  * shape; no HIP call).  Segment states and the segments' key-row and
  * value-column log-decays, and one record per chunk and head of
- * 268 K + 392 V + 8512 bytes (prepared key-side operands and A, v * exp2(C_63 - C_t),
+ * 268 K + 392 V + 8704 bytes (prepared key-side operands and A, v * exp2(C_63 - C_t),
  * exp2(C_t), the intra-chunk output (kept only where the walk cannot form it) and the
  * column decays). */
 size_t gla_fwd_general_workspace_size(const gla_shape_t* shape);
