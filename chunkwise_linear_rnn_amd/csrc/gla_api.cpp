@@ -33,15 +33,14 @@ bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr
 
 // Head dims with kernel instantiations.  The limits come from the 160 KiB of
 // LDS per CU: fp32 tiles are twice the size of bf16 ones, and the backward
-// holds both the value and d_o tiles at full V (its bf16 V = 512 runs as two
-// V = 256 column halves, bwd_split_launch).
+// holds both the value and d_o tiles at full V.  Wider values run as column
+// slices (bwd_split_launch: 16-bit V = 512 in two slices of 256; fp32 V = 256
+// or 512 in slices of 128, forward by fwd_split_launch too).
 bool supported_kv(int64_t K, int64_t V, bool bf16, bool backward) {
-    if (bf16) {
-        const bool k_ok = K == 64 || K == 128 || K == 256;
-        const bool v_ok = V == 64 || V == 128 || V == 256 || V == 512;
-        return k_ok && v_ok;
-    }
-    return (K == 64 || K == 128) && (V == 64 || V == 128);
+    (void)backward;
+    const bool v_ok = V == 64 || V == 128 || V == 256 || V == 512;
+    if (bf16) return (K == 64 || K == 128 || K == 256) && v_ok;
+    return (K == 64 || K == 128) && v_ok;
 }
 
 // Shape checks shared by forward and backward.  On success fills `out`.
@@ -151,6 +150,96 @@ size_t ckpt_bytes(const gla::Shape& s) {
     return pb.P > 1 ? gla::state_bytes(s, pb) : 0;
 }
 
+// The forward's launches for a validated, non-empty shape on one set of kernels
+// (fp32 at V <= 128, 16-bit at any supported V).
+hipError_t fwd_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                      const float* s0, void* o, float* s_final, void* workspace, bool sg, void* ckpt,
+                      hipStream_t strm) {
+    gla::Plan p = gla::make_fwd_plan(s);
+    gla::FwdLaunch a{};
+    a.bf16 = s.bf16;
+    a.sg = sg;
+    a.K = (int)s.K;
+    a.V = (int)s.V;
+    a.BV = p.BV;
+    a.T = (int)s.T;
+    a.H = (int)s.H;
+    a.N = (int)p.N;
+    a.P = p.P;
+    a.seg_len = p.seg_len;
+    a.BH = p.BH;
+    a.q = q; a.k = k; a.v = v; a.g = g;
+    a.s0 = s0;
+    a.o = o;
+    a.s_final = s_final;
+    if (p.P > 1) {
+        a.ws_state = workspace;
+        a.ws_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + gla::state_bytes(s, p));
+    }
+    if (gla::fwd_wide(s)) a.ws_rec = static_cast<char*>(workspace) + gla::fwd_seg_bytes(s, p);
+    if (ckpt && ckpt_bytes(s) > 0) {
+        const gla::Plan pb = gla::make_bwd_plan(s);
+        a.ckpt = ckpt;
+        a.ck_len = pb.seg_len;
+        a.ck_P = pb.P;
+    }
+    a.stream = strm;
+    return gla::launch_fwd(a);
+}
+
+// fp32 at V = 256 or 512: the recurrence acts on each value column independently
+// (Section 4.1, Eq. 3), so the forward is V / 128 forwards over column slices of
+// v and S_0 (gathered into the workspace) that share q, k and g; o and S_T are
+// the slices side by side.  The same holds for the backward (split_layout).
+constexpr long kFp32SliceV = 128;
+bool split_fwd(const gla::Shape& s) { return !s.bf16 && s.V > kFp32SliceV; }
+
+struct FwdSplitLayout {
+    size_t vh, oh, s0h, sfh, inner, total;
+};
+FwdSplitLayout fwd_split_layout(const gla::Shape& s) {
+    FwdSplitLayout w{};
+    gla::Shape h = s;
+    h.V = kFp32SliceV;
+    const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.vh = take(BTH * h.V * 4);
+    w.oh = take(BTH * h.V * 4);
+    w.s0h = take(BH * s.K * h.V * 4);
+    w.sfh = take(BH * s.K * h.V * 4);
+    w.inner = take(gla::fwd_workspace_bytes(h));
+    w.total = at;
+    return w;
+}
+
+hipError_t fwd_split_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                            const float* s0, void* o, float* s_final, void* workspace, hipStream_t strm) {
+    const FwdSplitLayout L = fwd_split_layout(s);
+    gla::Shape h = s;
+    h.V = kFp32SliceV;
+    char* ws = static_cast<char*>(workspace);
+    const long W = h.V, VT = s.V;
+    const long rows_t = s.B * s.T * s.H, rows_s = s.B * s.H * s.K;
+    hipError_t err = hipSuccess;
+    for (long off = 0; off < VT && err == hipSuccess; off += W) {
+        err = gla::launch_copy_cols(false, v, VT, off, ws + L.vh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && s0) err = gla::launch_copy_cols(false, s0, VT, off, ws + L.s0h, W, 0, W, rows_s, strm);
+        if (err != hipSuccess) break;
+        err = fwd_launch(h, q, k, ws + L.vh, g, s0 ? (const float*)(ws + L.s0h) : nullptr, ws + L.oh,
+                         s_final ? (float*)(ws + L.sfh) : nullptr, ws + L.inner, false, nullptr, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(false, ws + L.oh, W, 0, o, VT, off, W, rows_t, strm);
+        if (err == hipSuccess && s_final)
+            err = gla::launch_copy_cols(false, ws + L.sfh, W, 0, s_final, VT, off, W, rows_s, strm);
+    }
+    return err;
+}
+
+size_t fwd_total_bytes(const gla::Shape& s) {
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    return split_fwd(s) ? fwd_split_layout(s).total : gla::fwd_workspace_bytes(s);
+}
+
 gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
                       void* stream, bool sg, void* ckpt = nullptr) {
@@ -160,7 +249,7 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     if (st != GLA_OK) return st;
     if (!aligned16(workspace)) return fail(GLA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const bool empty = s.B * s.H == 0 || s.T == 0;
-    const size_t need = empty ? 0 : gla::fwd_workspace_bytes(s);
+    const size_t need = fwd_total_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -169,37 +258,10 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     if (empty) {
         // no tokens: the final state is the initial state (Section 2.2)
         err = s_final ? gla::launch_state_copy(s0, s_final, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else if (split_fwd(s)) {
+        err = fwd_split_launch(s, q, k, v, g, s0, o, s_final, workspace, strm);
     } else {
-        gla::Plan p = gla::make_fwd_plan(s);
-        gla::FwdLaunch a{};
-        a.bf16 = s.bf16;
-        a.sg = sg;
-        a.K = (int)s.K;
-        a.V = (int)s.V;
-        a.BV = p.BV;
-        a.T = (int)s.T;
-        a.H = (int)s.H;
-        a.N = (int)p.N;
-        a.P = p.P;
-        a.seg_len = p.seg_len;
-        a.BH = p.BH;
-        a.q = q; a.k = k; a.v = v; a.g = g;
-        a.s0 = s0;
-        a.o = o;
-        a.s_final = s_final;
-        if (p.P > 1) {
-            a.ws_state = workspace;
-            a.ws_gate = reinterpret_cast<float*>(static_cast<char*>(workspace) + gla::state_bytes(s, p));
-        }
-        if (gla::fwd_wide(s)) a.ws_rec = static_cast<char*>(workspace) + gla::fwd_seg_bytes(s, p);
-        if (ckpt && ckpt_bytes(s) > 0) {
-            const gla::Plan pb = gla::make_bwd_plan(s);
-            a.ckpt = ckpt;
-            a.ck_len = pb.seg_len;
-            a.ck_P = pb.P;
-        }
-        a.stream = strm;
-        err = gla::launch_fwd(a);
+        err = fwd_launch(s, q, k, v, g, s0, o, s_final, workspace, sg, ckpt, strm);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
@@ -413,27 +475,32 @@ hipError_t bwd_launch(const gla::Shape& s, const void* q, const void* k, const v
     return err;
 }
 
-// V = 512 (16-bit): the recurrence acts on each value column independently,
-// so the backward is two V = 256 backwards over the column halves of v, d_o,
-// S_0, dht (gathered into the workspace), sharing q, k, g.  dv and dS_0 are
-// the halves side by side; dq, dk and dg are the sums of the halves' values
-// (half 0 writes the caller's buffers, half 1 the workspace, then one add).
+// 16-bit V = 512 and fp32 V = 256 or 512: the recurrence acts on each value
+// column independently, so the backward is V / W backwards over column slices
+// of width W (256 for 16-bit inputs, 128 for fp32) of v, d_o, S_0 and dht
+// (gathered into the workspace), sharing q, k and g.  dv and dS_0 are the
+// slices side by side; dq, dk and dg are the sums of the slices' values (slice
+// 0 writes the caller's buffers, every later slice the workspace, then an add).
+bool split_bwd(const gla::Shape& s) { return s.bf16 ? s.V == 512 : s.V > kFp32SliceV; }
+long split_width(const gla::Shape& s) { return s.bf16 ? 256 : kFp32SliceV; }
+
 struct SplitLayout {
     size_t vh, doh, dq1, dk1, dg1, dvh, s0h, dhth, ds0h, inner, total;
 };
 SplitLayout split_layout(const gla::Shape& s, bool sg) {
     SplitLayout w{};
     gla::Shape h = s;
-    h.V = s.V / 2;
+    h.V = split_width(s);
     const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    const size_t e = s.bf16 ? 2 : 4;
     size_t at = 0;
     auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
-    w.vh = take(BTH * h.V * 2);
-    w.doh = take(BTH * h.V * 2);
-    w.dq1 = take(BTH * s.K * 2);
-    w.dk1 = take(BTH * s.K * 2);
-    w.dg1 = take(BTH * (sg ? 1 : s.K) * 2);
-    w.dvh = take(BTH * h.V * 2);
+    w.vh = take(BTH * h.V * e);
+    w.doh = take(BTH * h.V * e);
+    w.dq1 = take(BTH * s.K * e);
+    w.dk1 = take(BTH * s.K * e);
+    w.dg1 = take(BTH * (sg ? 1 : s.K) * e);
+    w.dvh = take(BTH * h.V * e);
     w.s0h = take(BH * s.K * h.V * 4);
     w.dhth = take(BH * s.K * h.V * 4);
     w.ds0h = take(BH * s.K * h.V * 4);
@@ -447,35 +514,36 @@ hipError_t bwd_split_launch(const gla::Shape& s, const void* q, const void* k, c
                             float* ds0, void* workspace, bool sg, hipStream_t strm) {
     const SplitLayout L = split_layout(s, sg);
     gla::Shape h = s;
-    h.V = s.V / 2;
+    h.V = split_width(s);
     char* ws = static_cast<char*>(workspace);
     const long W = h.V, VT = s.V;
     const long rows_t = s.B * s.T * s.H, rows_s = s.B * s.H * s.K;
     const long n_k = rows_t * s.K, n_g = rows_t * (sg ? 1 : s.K);
+    const bool b = s.bf16;
     hipError_t err = hipSuccess;
-    for (int half = 0; half < 2 && err == hipSuccess; ++half) {
-        const long off = half * W;
-        err = gla::launch_copy_cols(true, v, VT, off, ws + L.vh, W, 0, W, rows_t, strm);
-        if (err == hipSuccess) err = gla::launch_copy_cols(true, d_o, VT, off, ws + L.doh, W, 0, W, rows_t, strm);
+    for (long off = 0; off < VT && err == hipSuccess; off += W) {
+        const bool first = off == 0;
+        err = gla::launch_copy_cols(b, v, VT, off, ws + L.vh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(b, d_o, VT, off, ws + L.doh, W, 0, W, rows_t, strm);
         if (err == hipSuccess && s0) err = gla::launch_copy_cols(false, s0, VT, off, ws + L.s0h, W, 0, W, rows_s, strm);
         if (err == hipSuccess && dht)
             err = gla::launch_copy_cols(false, dht, VT, off, ws + L.dhth, W, 0, W, rows_s, strm);
         if (err != hipSuccess) break;
         err = bwd_launch(h, q, k, ws + L.vh, g, s0 ? (const float*)(ws + L.s0h) : nullptr, ws + L.doh,
-                         dht ? (const float*)(ws + L.dhth) : nullptr, half ? ws + L.dq1 : dq, half ? ws + L.dk1 : dk,
-                         ws + L.dvh, half ? ws + L.dg1 : dg, ds0 ? (float*)(ws + L.ds0h) : nullptr, ws + L.inner, sg,
-                         nullptr, strm);
-        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dvh, W, 0, dv, VT, off, W, rows_t, strm);
+                         dht ? (const float*)(ws + L.dhth) : nullptr, first ? dq : ws + L.dq1,
+                         first ? dk : ws + L.dk1, ws + L.dvh, first ? dg : ws + L.dg1,
+                         ds0 ? (float*)(ws + L.ds0h) : nullptr, ws + L.inner, sg, nullptr, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(b, ws + L.dvh, W, 0, dv, VT, off, W, rows_t, strm);
         if (err == hipSuccess && ds0)
             err = gla::launch_copy_cols(false, ws + L.ds0h, W, 0, ds0, VT, off, W, rows_s, strm);
+        if (!first) {
+            if (err == hipSuccess) err = gla::launch_add_into(b, dq, ws + L.dq1, n_k, strm);
+            if (err == hipSuccess) err = gla::launch_add_into(b, dk, ws + L.dk1, n_k, strm);
+            if (err == hipSuccess) err = gla::launch_add_into(b, dg, ws + L.dg1, n_g, strm);
+        }
     }
-    if (err == hipSuccess) err = gla::launch_add_into(dq, ws + L.dq1, n_k, strm);
-    if (err == hipSuccess) err = gla::launch_add_into(dk, ws + L.dk1, n_k, strm);
-    if (err == hipSuccess) err = gla::launch_add_into(dg, ws + L.dg1, n_g, strm);
     return err;
 }
-
-bool split_bwd(const gla::Shape& s) { return s.bf16 && s.V == 512; }
 
 size_t bwd_total_bytes(const gla::Shape& s, bool sg) {
     if (s.B * s.H == 0 || s.T == 0) return 0;
@@ -540,7 +608,7 @@ const char* gla_last_error_detail(void) { return g_detail.c_str(); }
 size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
     if (check_shape(shape, &s, false) != GLA_OK) return 0;
-    return gla::fwd_workspace_bytes(s);
+    return fwd_total_bytes(s);
 }
 
 size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
@@ -569,8 +637,7 @@ gla_status_t gla_fwd_noalloc(const gla_shape_t* shape, const void* q, const void
     // every argument is checked before the first HIP call (the scratch lookup)
     gla_status_t st = fwd_check(shape, q, k, v, g, s0, o, s_final, false, &s);
     if (st != GLA_OK) return st;
-    const bool empty = s.B * s.H == 0 || s.T == 0;
-    const size_t need = empty ? 0 : gla::fwd_workspace_bytes(s);
+    const size_t need = fwd_total_bytes(s);
     if (need > gla::kNoAllocScratchBytes)
         return fail(GLA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the fixed scratch of gla_fwd_noalloc "
                     "holds %zu (call gla_fwd with a workspace)", need, gla::kNoAllocScratchBytes);

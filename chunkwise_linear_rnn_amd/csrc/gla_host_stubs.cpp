@@ -28,6 +28,6 @@ hipError_t launch_state_copy(const float*, float*, long n, hipStream_t) {
 hipError_t launch_copy_cols(bool, const void*, long, long, void*, long, long, long W, long rows, hipStream_t) {
     return rows <= 0 || W <= 0 ? hipSuccess : hipErrorNoDevice;
 }
-hipError_t launch_add_into(void*, const void*, long n, hipStream_t) { return n <= 0 ? hipSuccess : hipErrorNoDevice; }
+hipError_t launch_add_into(bool, void*, const void*, long n, hipStream_t) { return n <= 0 ? hipSuccess : hipErrorNoDevice; }
 
 }  // namespace gla

@@ -103,6 +103,6 @@ hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s
 // dst[r][off_d + c] = src[r][off_s + c], c < W, r < rows (bf16 or fp32; 16-byte multiples)
 hipError_t launch_copy_cols(bool bf16, const void* src, long ld_s, long off_s, void* dst, long ld_d, long off_d, long W,
                             long rows, hipStream_t stream);
-hipError_t launch_add_into(void* a, const void* b, long n, hipStream_t stream);  // bf16 a += b
+hipError_t launch_add_into(bool bf16, void* a, const void* b, long n, hipStream_t stream);  // a += b (bf16 or fp32)
 
 }  // namespace gla

@@ -1,4 +1,6 @@
-// Column-half plumbing of the backward at value width 512 (16-bit inputs).
+// Column-slice plumbing of the wide-value paths: the backward at value width 512
+// (16-bit inputs, two slices of 256) and fp32 at value width 256 or 512 (slices
+// of 128, forward and backward).
 //
 // The recurrence of Section 4.1, Eq. 3 acts on each value column of the state
 // independently: column j of S_t depends only on column j of v and of S_0.  A
@@ -30,7 +32,7 @@ gla_copy_cols(const T* __restrict__ src, long ld_s, long off_s, T* __restrict__ 
     }
 }
 
-// a[i] = a[i] + b[i] in fp32, rounded once to T; n a multiple of 8.
+// a[i] = a[i] + b[i] in fp32, rounded once to T; n a multiple of 16 bytes' worth of T.
 template <typename T>
 __global__ void __launch_bounds__(256)
 gla_add_into(T* __restrict__ a, const T* __restrict__ b, long n) {
@@ -65,9 +67,14 @@ hipError_t launch_copy_cols(bool bf16, const void* src, long ld_s, long off_s, v
     return hipGetLastError();
 }
 
-hipError_t launch_add_into(void* a, const void* b, long n, hipStream_t stream) {
+hipError_t launch_add_into(bool bf16, void* a, const void* b, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    GLA_LAUNCH("add_halves", gla_add_into<__bf16>, dim3(grid_for(n / 8)), dim3(256), stream, (__bf16*)a, (const __bf16*)b, n);
+    if (bf16)
+        GLA_LAUNCH("add_halves", gla_add_into<__bf16>, dim3(grid_for(n / 8)), dim3(256), stream, (__bf16*)a,
+                   (const __bf16*)b, n);
+    else
+        GLA_LAUNCH("add_halves", gla_add_into<float>, dim3(grid_for(n / 4)), dim3(256), stream, (float*)a,
+                   (const float*)b, n);
     return hipGetLastError();
 }
 

@@ -42,7 +42,9 @@
  *  Supported sizes: chunk == 64; T a multiple of 64; bf16: K in
  *      {64, 128, 256} and V in {64, 128, 256, 512} (the backward runs V = 512
  *      as two V = 256 column halves: the recurrence never mixes value columns);
- *      fp32: K and V in {64, 128}.  B, H >= 0 and T >= 0; B*H == 0 or T == 0
+ *      fp32: K in {64, 128} and V in {64, 128, 256, 512} (V = 256 and 512 run,
+ *      forward and backward, as slices of 128 value columns whose staging
+ *      copies sit in the workspace).  B, H >= 0 and T >= 0; B*H == 0 or T == 0
  *      is a valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
  */
 #ifndef GLA_H_

@@ -163,6 +163,26 @@ def test_out_gate_validation_codes(L):
     assert _gate_bwd(L, _shape(T=5, V=1024)) == ERR_UNSUPPORTED
 
 
+def test_fp32_wide_values_run_as_slices(L):
+    # fp32 takes V = 256 and 512 as slices of 128 value columns: the workspace
+    # holds one slice's v, o (forward) or v, d_o, dv and the key-side partial
+    # sums (backward) plus that slice's own workspace, whatever the slice count
+    f32 = gla.GLA_DTYPE_FP32
+    fw = lambda V: L.gla_fwd_workspace_size(ctypes.byref(_shape(B=2, H=4, T=1024, K=128, V=V, dtype=f32)))
+    bw = lambda V: L.gla_bwd_workspace_size(ctypes.byref(_shape(B=2, H=4, T=1024, K=128, V=V, dtype=f32)))
+    rows = 2 * 4 * 1024
+    assert fw(256) == fw(512) and fw(256) >= 2 * rows * 128 * 4
+    assert bw(256) == bw(512) and bw(256) >= 3 * rows * 128 * 4 + 3 * rows * 128 * 4
+    for V in (256, 512):
+        s = _shape(T=128, K=64, V=V, dtype=f32)
+        need_f = L.gla_fwd_workspace_size(ctypes.byref(s))
+        assert need_f > 0 and _fwd(L, s, wsb=need_f - 1) == ERR_WORKSPACE
+        need_b = L.gla_bwd_workspace_size(ctypes.byref(s))
+        assert need_b > 0 and _bwd(L, s, wsb=need_b - 1) == ERR_WORKSPACE
+    assert _fwd(L, _shape(K=256, V=256, dtype=f32)) == ERR_UNSUPPORTED
+    assert L.gla_ckpt_size(ctypes.byref(_shape(T=1024, K=128, V=256, dtype=f32))) == 0
+
+
 def test_scalar_gate_entry_points_validate(L):
     s32 = _shape(T=128, dtype=gla.GLA_DTYPE_FP32)
     assert L.gla_bwd_scalar_workspace_size(ctypes.byref(s32)) == 0
@@ -204,8 +224,8 @@ def test_general_gate_backward_validates(L):
     assert ws(_shape(T=128, K=64, V=128)) == 0
     assert ws(_shape(T=128, K=128, V=512)) == 0
     s = _shape(B=2, H=4, T=8192, K=128, V=256)
-    # at least the reversed copies of q, k, v, do and both gates
-    assert ws(s) == ws(s) and ws(s) >= 2 * 8192 * 4 * 2 * (3 * 128 + 3 * 256)
+    # at least the chunk-start states of the forward and of the reversed dS pass
+    assert ws(s) == ws(s) and ws(s) >= 2 * (2 * 4 * 128 * 128 * 256 * 2)
     bwd = lambda shape, **kw: L.gla_bwd_general(ctypes.byref(shape), P, P, P, P, kw.get("h", P), None, P, None,
                                                 P, P, P, P, kw.get("dh", P), None, kw.get("ws", P), 1 << 40, None)
     assert bwd(_shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED

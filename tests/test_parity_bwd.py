@@ -179,6 +179,21 @@ def test_bwd_value_width_512_exact_path():
     _check_bwd(w, inputs=exact_path_inputs(w))
 
 
+@pytest.mark.parametrize("K,V,T,s0,dht", [(64, 256, 320, "normal0.1", True), (128, 256, 192, "none", True),
+                                         (64, 512, 256, "normal0.1", False), (128, 512, 448, "normal0.1", True)])
+def test_bwd_fp32_wide_values(K, V, T, s0, dht):
+    # fp32 with V = 256 or 512 runs as V / 128 backwards over value-column
+    # slices; dv and dS0 are the slices side by side, dq, dk, dg their sums
+    w = gi.custom(1, 2, T, K, V, dtype="fp32", gate="lowrank", s0=s0, backward=True, seed=640 + K + V + T)
+    _check_bwd(w, with_dht=dht)
+
+
+def test_bwd_fp32_wide_values_exact_path():
+    from tests.test_parity_fwd import exact_path_inputs
+    w = gi.custom(1, 2, 256, 64, 512, dtype="fp32", gate="iid", s0="normal0.1", backward=True, seed=651)
+    _check_bwd(w, inputs=exact_path_inputs(w))
+
+
 def test_bwd_1p3b_head_shape_sampled_heads():
     # the 1.3B-model head shape at length 8K (the gla_1p3b_long recipe and seed,
     # with an upstream gradient drawn as well), two heads against the oracle

@@ -61,6 +61,19 @@ def test_fwd_small_wide_bf16(K, V):
     _run_and_check(w)
 
 
+@pytest.mark.parametrize("K,V,T", [(64, 256, 320), (128, 256, 192), (64, 512, 256), (128, 512, 448)])
+def test_fwd_fp32_wide_values(K, V, T):
+    # fp32 with V = 256 or 512 runs as value-column slices of 128 (the
+    # recurrence never mixes value columns); o and S_T are the slices side by side
+    w = gi.custom(1, 2, T, K, V, dtype="fp32", gate="lowrank", s0="normal0.1", backward=False, seed=620 + K + V + T)
+    _run_and_check(w)
+
+
+def test_fwd_fp32_wide_values_exact_path():
+    w = gi.custom(1, 2, 256, 128, 256, dtype="fp32", gate="iid", s0="normal0.1", backward=False, seed=631)
+    _run_and_check(w, inputs=exact_path_inputs(w))
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_fwd_ungated(dtype):
     w = gi.custom(2, 2, 256, 64, 128, dtype=dtype, gate="zero", v_scale="unit", backward=False, seed=8)
