@@ -31,16 +31,18 @@ gla_status_t fail(gla_status_t st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Head dims with kernel instantiations.  The limits come from the 160 KiB of
-// LDS per CU: fp32 tiles are twice the size of bf16 ones, and the backward
-// holds both the value and d_o tiles at full V.  Wider values run as column
-// slices (bwd_split_launch: 16-bit V = 512 in two slices of 256; fp32 V = 256
-// or 512 in slices of 128, forward by fwd_split_launch too).
+// Head dims of the plain and scalar-gate paths: K and V in {64, 128, 256,
+// 512}.  The kernels take K <= 256 (16-bit) or 128 (fp32) and V <= 256 in the
+// backward, 128 for fp32 (160 KiB of LDS per CU: fp32 tiles are twice the
+// size of bf16 ones, and the backward holds both the value and d_o tiles at
+// full V).  Wider heads run as slices: key slices (fwd_any_launch,
+// bwd_any_launch), value slices (fwd_split_launch, bwd_split_launch).
 bool supported_kv(int64_t K, int64_t V, bool bf16, bool backward) {
+    (void)bf16;
     (void)backward;
+    const bool k_ok = K == 64 || K == 128 || K == 256 || K == 512;
     const bool v_ok = V == 64 || V == 128 || V == 256 || V == 512;
-    if (bf16) return (K == 64 || K == 128 || K == 256) && v_ok;
-    return (K == 64 || K == 128) && v_ok;
+    return k_ok && v_ok;
 }
 
 // Shape checks shared by forward and backward.  On success fills `out`.
@@ -84,7 +86,7 @@ gla_status_t check_decode_shape(const gla_shape_t* s, gla::Shape* out) {
                     (long long)s->H);
     if (s->dtype != GLA_DTYPE_BF16 && s->dtype != GLA_DTYPE_FP32)
         return fail(GLA_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
-    const bool k_ok = s->K == 64 || s->K == 128 || s->K == 256;
+    const bool k_ok = s->K == 64 || s->K == 128 || s->K == 256 || s->K == 512;
     const bool v_ok = s->V == 64 || s->V == 128 || s->V == 256 || s->V == 512;
     if (!k_ok || !v_ok)
         return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for decode", (long long)s->K,
@@ -240,6 +242,102 @@ size_t fwd_total_bytes(const gla::Shape& s) {
     return split_fwd(s) ? fwd_split_layout(s).total : gla::fwd_workspace_bytes(s);
 }
 
+hipError_t fwd_v_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                        const float* s0, void* o, float* s_final, void* workspace, bool sg, void* ckpt,
+                        hipStream_t strm) {
+    return split_fwd(s) ? fwd_split_launch(s, q, k, v, g, s0, o, s_final, workspace, strm)
+                        : fwd_launch(s, q, k, v, g, s0, o, s_final, workspace, sg, ckpt, strm);
+}
+
+// Key dims past a kernel set's widest (16-bit: 256, fp32: 128) run as slices
+// of key columns.  Diag(alpha_t) scales each row of the state on its own and
+// k_t^T v_t builds row i from k_t[i] alone (Section 4.1, Eq. 3), so row i of
+// S_t depends only on column i of k and g, while o_t = q_t S_t sums over the
+// rows: a head with K key columns is K / W heads of width W that share v (and
+// a per-token scalar gate, or a value-side gate) and whose outputs add.  Each
+// slice's state is a block of W rows of the head's state.
+long kslice_width(const gla::Shape& s) { return s.bf16 ? 256 : 128; }
+bool split_k(const gla::Shape& s) { return s.K > kslice_width(s); }
+
+// [BH][K][V] rows k0 .. k0 + W - 1  ->  [BH][W][V], and back
+hipError_t state_rows_out(const float* src, const gla::Shape& s, long k0, long W, void* dst, hipStream_t strm) {
+    return gla::launch_copy_cols(false, src, s.K * s.V, k0 * s.V, dst, W * s.V, 0, W * s.V, s.B * s.H, strm);
+}
+hipError_t state_rows_in(const void* src, const gla::Shape& s, long k0, long W, float* dst, hipStream_t strm) {
+    return gla::launch_copy_cols(false, src, W * s.V, 0, dst, s.K * s.V, k0 * s.V, W * s.V, s.B * s.H, strm);
+}
+
+// Workspace of a key-sliced call: per-slice copies of the token tensors with K
+// columns (q, k and the gate, unless it is one value per token), the partial
+// output, the state row blocks, then the slice's own workspace.
+struct KFwdLayout {
+    size_t qh, kh, gh, oh, s0h, sfh, inner, total;
+};
+KFwdLayout kfwd_layout(const gla::Shape& s, bool sg, size_t inner_bytes) {
+    KFwdLayout w{};
+    const size_t W = (size_t)kslice_width(s);
+    const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H), e = s.bf16 ? 2 : 4;
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.qh = take(BTH * W * e);
+    w.kh = take(BTH * W * e);
+    w.gh = sg ? 0 : take(BTH * W * e);
+    w.oh = take(BTH * s.V * e);
+    w.s0h = take(BH * W * s.V * 4);
+    w.sfh = take(BH * W * s.V * 4);
+    w.inner = take(inner_bytes);
+    w.total = at;
+    return w;
+}
+gla::Shape kslice_shape(const gla::Shape& s) {
+    gla::Shape h = s;
+    h.K = kslice_width(s);
+    return h;
+}
+
+// One forward per key slice: gather its q, k, g columns and S_0 rows, run, add
+// its output into o (the first slice writes o) and place its S_T rows.  `run`
+// launches the slice's forward on (q, k, g, s0, o, s_final, workspace).
+template <class Run>
+hipError_t fwd_ksplit(const gla::Shape& s, const void* q, const void* k, const void* g, const float* s0, void* o,
+                      float* s_final, void* workspace, bool sg, const KFwdLayout& L, hipStream_t strm, Run run) {
+    const long W = kslice_width(s), KT = s.K, rows_t = s.B * s.T * s.H;
+    const bool b = s.bf16;
+    char* ws = static_cast<char*>(workspace);
+    hipError_t err = hipSuccess;
+    for (long k0 = 0; k0 < KT && err == hipSuccess; k0 += W) {
+        const bool first = k0 == 0;
+        err = gla::launch_copy_cols(b, q, KT, k0, ws + L.qh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(b, k, KT, k0, ws + L.kh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && !sg) err = gla::launch_copy_cols(b, g, KT, k0, ws + L.gh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && s0) err = state_rows_out(s0, s, k0, W, ws + L.s0h, strm);
+        if (err != hipSuccess) break;
+        err = run(ws + L.qh, ws + L.kh, sg ? g : ws + L.gh, s0 ? (const float*)(ws + L.s0h) : nullptr,
+                  first ? o : ws + L.oh, s_final ? (float*)(ws + L.sfh) : nullptr, ws + L.inner);
+        if (err == hipSuccess && !first) err = gla::launch_add_into(b, o, ws + L.oh, rows_t * s.V, strm);
+        if (err == hipSuccess && s_final) err = state_rows_in(ws + L.sfh, s, k0, W, s_final, strm);
+    }
+    return err;
+}
+
+size_t fwd_any_bytes(const gla::Shape& s, bool sg) {
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (!split_k(s)) return fwd_total_bytes(s);
+    return kfwd_layout(s, sg, fwd_total_bytes(kslice_shape(s))).total;
+}
+
+// The plain and scalar-gate forward for a validated, non-empty shape.
+hipError_t fwd_any_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                          const float* s0, void* o, float* s_final, void* workspace, bool sg, void* ckpt,
+                          hipStream_t strm) {
+    if (!split_k(s)) return fwd_v_launch(s, q, k, v, g, s0, o, s_final, workspace, sg, ckpt, strm);
+    const gla::Shape h = kslice_shape(s);
+    const KFwdLayout L = kfwd_layout(s, sg, fwd_total_bytes(h));
+    return fwd_ksplit(s, q, k, g, s0, o, s_final, workspace, sg, L, strm,
+                      [&](const void* qh, const void* kh, const void* gh, const float* s0h, void* oh, float* sfh,
+                          void* inner) { return fwd_v_launch(h, qh, kh, v, gh, s0h, oh, sfh, inner, sg, nullptr, strm); });
+}
+
 gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, void* o, float* s_final, void* workspace, size_t workspace_bytes,
                       void* stream, bool sg, void* ckpt = nullptr) {
@@ -249,7 +347,7 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     if (st != GLA_OK) return st;
     if (!aligned16(workspace)) return fail(GLA_ERR_ALIGN, "workspace is not 16-byte aligned");
     const bool empty = s.B * s.H == 0 || s.T == 0;
-    const size_t need = fwd_total_bytes(s);
+    const size_t need = fwd_any_bytes(s, sg);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -258,10 +356,8 @@ gla_status_t fwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     if (empty) {
         // no tokens: the final state is the initial state (Section 2.2)
         err = s_final ? gla::launch_state_copy(s0, s_final, s.B * s.H * s.K * s.V, strm) : hipSuccess;
-    } else if (split_fwd(s)) {
-        err = fwd_split_launch(s, q, k, v, g, s0, o, s_final, workspace, strm);
     } else {
-        err = fwd_launch(s, q, k, v, g, s0, o, s_final, workspace, sg, ckpt, strm);
+        err = fwd_any_launch(s, q, k, v, g, s0, o, s_final, workspace, sg, ckpt, strm);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
@@ -279,8 +375,56 @@ size_t general_ckpt_st_offset(const gla::Shape& s) {
     return gla::round256((size_t)(s.B * s.H) * (size_t)(s.T / 64) * (size_t)(s.K * s.V) * 2);
 }
 
-// ckpt (optional, general_ckpt_bytes(s) bytes): the forward also writes the
-// state before every chunk and S_T there, for gla_bwd_general_ckpt.
+// The general-gate forward for a validated, non-empty shape with K in {128,
+// 256}.  ckpt (optional, general_ckpt_bytes(s) bytes): the forward also writes
+// the state before every chunk and S_T there, for gla_bwd_general_ckpt.
+hipError_t fwd_general_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                              const void* h, const float* s0, void* o, float* s_final, void* workspace, void* ckpt,
+                              hipStream_t strm) {
+    gla::Plan p = gla::make_fwd_general_plan(s);
+    gla::FwdLaunch a{};
+    a.bf16 = true;
+    a.K = (int)s.K;
+    a.V = (int)s.V;
+    a.BV = p.BV;
+    a.T = (int)s.T;
+    a.H = (int)s.H;
+    a.N = (int)p.N;
+    a.P = p.P;
+    a.seg_len = p.seg_len;
+    a.BH = p.BH;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.h = h;
+    a.s0 = s0;
+    a.o = o;
+    a.s_final = s_final;
+    if (ckpt) {
+        // S_T goes to the checkpoint, and to s_final too when the caller asks for it
+        a.ws_hs = ckpt;
+        a.s_final = reinterpret_cast<float*>(static_cast<char*>(ckpt) + general_ckpt_st_offset(s));
+        a.s_final2 = s_final;
+    }
+    char* ws = static_cast<char*>(workspace);
+    if (p.P > 1) {
+        const size_t sb = gla::state_bytes(s, p);
+        a.ws_state = ws;
+        a.ws_gate = reinterpret_cast<float*>(ws + sb);
+        a.ws_gateb = reinterpret_cast<float*>(ws + sb + gla::round256((size_t)p.BH * p.P * s.K * sizeof(float)));
+    }
+    a.ws_rec = ws + gla::fwd_general_seg_bytes(s, p);
+    a.stream = strm;
+    return gla::launch_fwd_general(a);
+}
+
+// General gates take K in {128, 256, 512} (512 as two key slices: the gate
+// alpha^T beta still scales each state row on its own, so the slices share v
+// and the value-side gate h) and V in {64 .. 512} in the forward.
+bool general_k_ok(int64_t K) { return K == 128 || K == 256 || K == 512; }
+size_t fwd_general_any_bytes(const gla::Shape& s) {
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (!split_k(s)) return gla::fwd_general_workspace_bytes(s);
+    return kfwd_layout(s, false, gla::fwd_general_workspace_bytes(kslice_shape(s))).total;
+}
+
 gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
                               const void* g, const void* h, const float* s0, void* o, float* s_final,
                               void* workspace, size_t workspace_bytes, void* stream, void* ckpt = nullptr,
@@ -290,10 +434,11 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     gla_status_t st = check_shape(shape, &s, want_ckpt);
     if (st != GLA_OK) return st;
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
-    if (s.K != 128 && s.K != 256)
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 128 or 256 (got %lld)", (long long)s.K);
-    if (want_ckpt && s.V != 128 && s.V != 256)
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate checkpoint takes V = 128 or 256 (got %lld)", (long long)s.V);
+    if (!general_k_ok(s.K))
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 128, 256 or 512 (got %lld)", (long long)s.K);
+    if (want_ckpt && (s.K > 256 || (s.V != 128 && s.V != 256)))
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate checkpoint takes K and V in {128, 256} (got K=%lld V=%lld)",
+                    (long long)s.K, (long long)s.V);
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !o)) return fail(GLA_ERR_NULL, "q, k, v, g, h and o are required");
     if (want_ckpt && !empty && !ckpt)
@@ -302,7 +447,7 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     const char* names[] = {"q", "k", "v", "g", "h", "s0", "o", "s_final", "workspace", "ckpt"};
     for (int i = 0; i < 10; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const size_t need = empty ? 0 : gla::fwd_general_workspace_bytes(s);
+    const size_t need = fwd_general_any_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -310,48 +455,184 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     hipError_t err;
     if (empty) {
         err = s_final ? gla::launch_state_copy(s0, s_final, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else if (!split_k(s)) {
+        err = fwd_general_launch(s, q, k, v, g, h, s0, o, s_final, workspace, want_ckpt ? ckpt : nullptr, strm);
     } else {
-        gla::Plan p = gla::make_fwd_general_plan(s);
-        gla::FwdLaunch a{};
-        a.bf16 = true;
-        a.K = (int)s.K;
-        a.V = (int)s.V;
-        a.BV = p.BV;
-        a.T = (int)s.T;
-        a.H = (int)s.H;
-        a.N = (int)p.N;
-        a.P = p.P;
-        a.seg_len = p.seg_len;
-        a.BH = p.BH;
-        a.q = q; a.k = k; a.v = v; a.g = g; a.h = h;
-        a.s0 = s0;
-        a.o = o;
-        a.s_final = s_final;
-        float* ck_st = nullptr;
-        if (ckpt) {
-            // S_T goes to the checkpoint, and to s_final too when the caller asks for it
-            ck_st = reinterpret_cast<float*>(static_cast<char*>(ckpt) + general_ckpt_st_offset(s));
-            a.ws_hs = ckpt;
-            a.s_final = ck_st;
-            a.s_final2 = s_final;
-        }
-        char* ws = static_cast<char*>(workspace);
-        if (p.P > 1) {
-            const size_t sb = gla::state_bytes(s, p);
-            a.ws_state = ws;
-            a.ws_gate = reinterpret_cast<float*>(ws + sb);
-            a.ws_gateb = reinterpret_cast<float*>(ws + sb + gla::round256((size_t)p.BH * p.P * s.K * sizeof(float)));
-        }
-        a.ws_rec = ws + gla::fwd_general_seg_bytes(s, p);
-        a.stream = strm;
-        err = gla::launch_fwd_general(a);
+        const gla::Shape hs = kslice_shape(s);
+        const KFwdLayout L = kfwd_layout(s, false, gla::fwd_general_workspace_bytes(hs));
+        err = fwd_ksplit(s, q, k, g, s0, o, s_final, workspace, false, L, strm,
+                         [&](const void* qh, const void* kh, const void* gh, const float* s0h, void* oh, float* sfh,
+                             void* inner) {
+                             return fwd_general_launch(hs, qh, kh, v, gh, h, s0h, oh, sfh, inner, nullptr, strm);
+                         });
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
 }
 
-// o, ckpt (both or neither): the forward's output and what gla_fwd_general_ckpt
-// wrote; the backward then runs no forward of its own.
+// The general-gate backward for a validated, non-empty shape with K and V in
+// {128, 256}.  o, ckpt (both or neither): the forward's output and what
+// gla_fwd_general_ckpt wrote; the backward then runs no forward of its own.
+hipError_t bwd_general_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                              const void* h, const float* s0, const void* d_o, const float* dht, void* dq, void* dk,
+                              void* dv, void* dg, void* dh, float* ds0, void* workspace, const void* o,
+                              const void* ckpt, hipStream_t strm) {
+    gla::BwdGeneralLaunch a{};
+    a.B = (int)s.B; a.T = (int)s.T; a.H = (int)s.H; a.K = (int)s.K; a.V = (int)s.V;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.h = h; a.d_o = d_o;
+    a.s0 = s0; a.dht = dht;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dh = dh; a.ds0 = ds0;
+    if (ckpt) {
+        a.o_in = o;
+        a.hs_in = ckpt;
+        a.st_in = reinterpret_cast<const float*>(static_cast<const char*>(ckpt) + general_ckpt_st_offset(s));
+    }
+    a.workspace = workspace;
+    a.stream = strm;
+    return gla::launch_bwd_general(a);
+}
+
+// V = 512 as two value slices of 256 (each value column of the state, with its
+// gate beta_j, evolves on its own): v, h, d_o and the S_0 / dht columns are
+// gathered per slice; dv, dh and dS_0 are the slices side by side, dq, dk and
+// dg the sums of the slices' values.
+constexpr long kGeneralSliceV = 256;
+struct GVLayout {
+    size_t vh, hh, doh, dq1, dk1, dg1, dvh, dhh, s0h, dhth, ds0h, inner, total;
+};
+GVLayout general_v_layout(const gla::Shape& s) {
+    GVLayout w{};
+    gla::Shape sub = s;
+    sub.V = kGeneralSliceV;
+    const size_t W = kGeneralSliceV, BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.vh = take(BTH * W * 2);
+    w.hh = take(BTH * W * 2);
+    w.doh = take(BTH * W * 2);
+    w.dq1 = take(BTH * s.K * 2);
+    w.dk1 = take(BTH * s.K * 2);
+    w.dg1 = take(BTH * s.K * 2);
+    w.dvh = take(BTH * W * 2);
+    w.dhh = take(BTH * W * 2);
+    w.s0h = take(BH * s.K * W * 4);
+    w.dhth = take(BH * s.K * W * 4);
+    w.ds0h = take(BH * s.K * W * 4);
+    w.inner = take(gla::bwd_general_layout(sub).total);
+    w.total = at;
+    return w;
+}
+size_t bwd_general_v_bytes(const gla::Shape& s) {
+    return s.V > kGeneralSliceV ? general_v_layout(s).total : gla::bwd_general_layout(s).total;
+}
+
+hipError_t bwd_general_v_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                                const void* h, const float* s0, const void* d_o, const float* dht, void* dq,
+                                void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
+                                hipStream_t strm) {
+    if (s.V <= kGeneralSliceV)
+        return bwd_general_launch(s, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, nullptr,
+                                  nullptr, strm);
+    const GVLayout L = general_v_layout(s);
+    gla::Shape sub = s;
+    sub.V = kGeneralSliceV;
+    char* ws = static_cast<char*>(workspace);
+    const long W = kGeneralSliceV, VT = s.V, rows_t = s.B * s.T * s.H, rows_s = s.B * s.H * s.K;
+    const long n_k = rows_t * s.K;
+    hipError_t err = hipSuccess;
+    for (long off = 0; off < VT && err == hipSuccess; off += W) {
+        const bool first = off == 0;
+        err = gla::launch_copy_cols(true, v, VT, off, ws + L.vh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, h, VT, off, ws + L.hh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, d_o, VT, off, ws + L.doh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && s0) err = gla::launch_copy_cols(false, s0, VT, off, ws + L.s0h, W, 0, W, rows_s, strm);
+        if (err == hipSuccess && dht)
+            err = gla::launch_copy_cols(false, dht, VT, off, ws + L.dhth, W, 0, W, rows_s, strm);
+        if (err != hipSuccess) break;
+        err = bwd_general_launch(sub, q, k, ws + L.vh, g, ws + L.hh, s0 ? (const float*)(ws + L.s0h) : nullptr,
+                                 ws + L.doh, dht ? (const float*)(ws + L.dhth) : nullptr, first ? dq : ws + L.dq1,
+                                 first ? dk : ws + L.dk1, ws + L.dvh, first ? dg : ws + L.dg1, ws + L.dhh,
+                                 ds0 ? (float*)(ws + L.ds0h) : nullptr, ws + L.inner, nullptr, nullptr, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dvh, W, 0, dv, VT, off, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dhh, W, 0, dh, VT, off, W, rows_t, strm);
+        if (err == hipSuccess && ds0)
+            err = gla::launch_copy_cols(false, ws + L.ds0h, W, 0, ds0, VT, off, W, rows_s, strm);
+        if (!first) {
+            if (err == hipSuccess) err = gla::launch_add_into(true, dq, ws + L.dq1, n_k, strm);
+            if (err == hipSuccess) err = gla::launch_add_into(true, dk, ws + L.dk1, n_k, strm);
+            if (err == hipSuccess) err = gla::launch_add_into(true, dg, ws + L.dg1, n_k, strm);
+        }
+    }
+    return err;
+}
+
+// K = 512 as two key slices of 256 (kbwd_layout's pattern): dq, dk and dg are
+// the slices' columns, dv and dh the sums of the slices' values (h is the
+// gate of the value columns, which every row shares), dS_0 the row blocks.
+struct GKLayout {
+    size_t qh, kh, gh, dqh, dkh, dgh, dvh, dhh, s0h, dhth, ds0h, inner, total;
+};
+GKLayout general_k_layout(const gla::Shape& s) {
+    GKLayout w{};
+    const size_t W = (size_t)kslice_width(s);
+    const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.qh = take(BTH * W * 2);
+    w.kh = take(BTH * W * 2);
+    w.gh = take(BTH * W * 2);
+    w.dqh = take(BTH * W * 2);
+    w.dkh = take(BTH * W * 2);
+    w.dgh = take(BTH * W * 2);
+    w.dvh = take(BTH * s.V * 2);
+    w.dhh = take(BTH * s.V * 2);
+    w.s0h = take(BH * W * s.V * 4);
+    w.dhth = take(BH * W * s.V * 4);
+    w.ds0h = take(BH * W * s.V * 4);
+    w.inner = take(bwd_general_v_bytes(kslice_shape(s)));
+    w.total = at;
+    return w;
+}
+bool general_bwd_kv_ok(int64_t K, int64_t V) { return general_k_ok(K) && (V == 128 || V == 256 || V == 512); }
+size_t bwd_general_any_bytes(const gla::Shape& s) {
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    return split_k(s) ? general_k_layout(s).total : bwd_general_v_bytes(s);
+}
+
+hipError_t bwd_general_any_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                                  const void* h, const float* s0, const void* d_o, const float* dht, void* dq,
+                                  void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
+                                  hipStream_t strm) {
+    if (!split_k(s))
+        return bwd_general_v_launch(s, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, strm);
+    const GKLayout L = general_k_layout(s);
+    const gla::Shape sub = kslice_shape(s);
+    char* ws = static_cast<char*>(workspace);
+    const long W = sub.K, KT = s.K, rows_t = s.B * s.T * s.H;
+    hipError_t err = hipSuccess;
+    for (long k0 = 0; k0 < KT && err == hipSuccess; k0 += W) {
+        const bool first = k0 == 0;
+        err = gla::launch_copy_cols(true, q, KT, k0, ws + L.qh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, k, KT, k0, ws + L.kh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, g, KT, k0, ws + L.gh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && s0) err = state_rows_out(s0, s, k0, W, ws + L.s0h, strm);
+        if (err == hipSuccess && dht) err = state_rows_out(dht, s, k0, W, ws + L.dhth, strm);
+        if (err != hipSuccess) break;
+        err = bwd_general_v_launch(sub, ws + L.qh, ws + L.kh, v, ws + L.gh, h,
+                                   s0 ? (const float*)(ws + L.s0h) : nullptr, d_o,
+                                   dht ? (const float*)(ws + L.dhth) : nullptr, ws + L.dqh, ws + L.dkh,
+                                   first ? dv : ws + L.dvh, ws + L.dgh, first ? dh : ws + L.dhh,
+                                   ds0 ? (float*)(ws + L.ds0h) : nullptr, ws + L.inner, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dqh, W, 0, dq, KT, k0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dkh, W, 0, dk, KT, k0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dgh, W, 0, dg, KT, k0, W, rows_t, strm);
+        if (err == hipSuccess && !first) err = gla::launch_add_into(true, dv, ws + L.dvh, rows_t * s.V, strm);
+        if (err == hipSuccess && !first) err = gla::launch_add_into(true, dh, ws + L.dhh, rows_t * s.V, strm);
+        if (err == hipSuccess && ds0) err = state_rows_in(ws + L.ds0h, s, k0, W, ds0, strm);
+    }
+    return err;
+}
+
 gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
                               const void* g, const void* h, const float* s0, const void* d_o, const float* dht,
                               void* dq, void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
@@ -362,9 +643,9 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     gla_status_t st = check_shape(shape, &s, true);
     if (st != GLA_OK) return st;
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
-    if ((s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256))
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {128, 256} (got K=%lld V=%lld)",
-                    (long long)s.K, (long long)s.V);
+    if (want_ckpt ? (s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256) : !general_bwd_kv_ok(s.K, s.V))
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {128, 256%s} (got K=%lld V=%lld)",
+                    want_ckpt ? "" : ", 512", (long long)s.K, (long long)s.V);
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !d_o || !dq || !dk || !dv || !dg || !dh))
         return fail(GLA_ERR_NULL, "q, k, v, g, h, d_o, dq, dk, dv, dg and dh are required");
@@ -375,7 +656,7 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
                            "workspace", "o", "ckpt"};
     for (int i = 0; i < 17; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const size_t need = empty ? 0 : gla::bwd_general_layout(s).total;
+    const size_t need = empty ? 0 : want_ckpt ? gla::bwd_general_layout(s).total : bwd_general_any_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -383,20 +664,10 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     hipError_t err;
     if (empty) {
         err = ds0 ? gla::launch_state_copy(dht, ds0, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else if (want_ckpt) {
+        err = bwd_general_launch(s, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, o, ckpt, strm);
     } else {
-        gla::BwdGeneralLaunch a{};
-        a.B = (int)s.B; a.T = (int)s.T; a.H = (int)s.H; a.K = (int)s.K; a.V = (int)s.V;
-        a.q = q; a.k = k; a.v = v; a.g = g; a.h = h; a.d_o = d_o;
-        a.s0 = s0; a.dht = dht;
-        a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dh = dh; a.ds0 = ds0;
-        if (want_ckpt) {
-            a.o_in = o;
-            a.hs_in = ckpt;
-            a.st_in = reinterpret_cast<const float*>(static_cast<const char*>(ckpt) + general_ckpt_st_offset(s));
-        }
-        a.workspace = workspace;
-        a.stream = strm;
-        err = gla::launch_bwd_general(a);
+        err = bwd_general_any_launch(s, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, strm);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
@@ -550,6 +821,80 @@ size_t bwd_total_bytes(const gla::Shape& s, bool sg) {
     return split_bwd(s) ? split_layout(s, sg).total : bwd_workspace_bytes(s, sg);
 }
 
+hipError_t bwd_v_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                        const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                        float* ds0, void* workspace, bool sg, const void* ckpt, hipStream_t strm) {
+    return split_bwd(s) ? bwd_split_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, strm)
+                        : bwd_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, ckpt, strm);
+}
+
+// Backward over key slices (the forward's kfwd_layout): a slice's dq, dk and
+// dg are its columns of the head's; dv is the sum of the slices' (and so is
+// dg for a scalar gate, which every row shares); dS_0 is the slices' row
+// blocks.
+struct KBwdLayout {
+    size_t qh, kh, gh, dqh, dkh, dgh, dvh, s0h, dhth, ds0h, inner, total;
+};
+KBwdLayout kbwd_layout(const gla::Shape& s, bool sg, size_t inner_bytes) {
+    KBwdLayout w{};
+    const size_t W = (size_t)kslice_width(s);
+    const size_t BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H), e = s.bf16 ? 2 : 4;
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.qh = take(BTH * W * e);
+    w.kh = take(BTH * W * e);
+    w.gh = sg ? 0 : take(BTH * W * e);
+    w.dqh = take(BTH * W * e);
+    w.dkh = take(BTH * W * e);
+    w.dgh = take(BTH * (sg ? 1 : W) * e);
+    w.dvh = take(BTH * s.V * e);
+    w.s0h = take(BH * W * s.V * 4);
+    w.dhth = take(BH * W * s.V * 4);
+    w.ds0h = take(BH * W * s.V * 4);
+    w.inner = take(inner_bytes);
+    w.total = at;
+    return w;
+}
+
+size_t bwd_any_bytes(const gla::Shape& s, bool sg) {
+    if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (!split_k(s)) return bwd_total_bytes(s, sg);
+    return kbwd_layout(s, sg, bwd_total_bytes(kslice_shape(s), sg)).total;
+}
+
+// The plain and scalar-gate backward for a validated, non-empty shape.
+hipError_t bwd_any_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                          const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
+                          float* ds0, void* workspace, bool sg, const void* ckpt, hipStream_t strm) {
+    if (!split_k(s)) return bwd_v_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, ckpt, strm);
+    const gla::Shape h = kslice_shape(s);
+    const KBwdLayout L = kbwd_layout(s, sg, bwd_total_bytes(h, sg));
+    const long W = h.K, KT = s.K, rows_t = s.B * s.T * s.H;
+    const bool b = s.bf16;
+    char* ws = static_cast<char*>(workspace);
+    hipError_t err = hipSuccess;
+    for (long k0 = 0; k0 < KT && err == hipSuccess; k0 += W) {
+        const bool first = k0 == 0;
+        err = gla::launch_copy_cols(b, q, KT, k0, ws + L.qh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(b, k, KT, k0, ws + L.kh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && !sg) err = gla::launch_copy_cols(b, g, KT, k0, ws + L.gh, W, 0, W, rows_t, strm);
+        if (err == hipSuccess && s0) err = state_rows_out(s0, s, k0, W, ws + L.s0h, strm);
+        if (err == hipSuccess && dht) err = state_rows_out(dht, s, k0, W, ws + L.dhth, strm);
+        if (err != hipSuccess) break;
+        err = bwd_v_launch(h, ws + L.qh, ws + L.kh, v, sg ? g : ws + L.gh, s0 ? (const float*)(ws + L.s0h) : nullptr,
+                           d_o, dht ? (const float*)(ws + L.dhth) : nullptr, ws + L.dqh, ws + L.dkh,
+                           first ? dv : ws + L.dvh, sg && first ? dg : ws + L.dgh,
+                           ds0 ? (float*)(ws + L.ds0h) : nullptr, ws + L.inner, sg, nullptr, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(b, ws + L.dqh, W, 0, dq, KT, k0, W, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(b, ws + L.dkh, W, 0, dk, KT, k0, W, rows_t, strm);
+        if (err == hipSuccess && !sg) err = gla::launch_copy_cols(b, ws + L.dgh, W, 0, dg, KT, k0, W, rows_t, strm);
+        if (err == hipSuccess && !first) err = gla::launch_add_into(b, dv, ws + L.dvh, rows_t * s.V, strm);
+        if (err == hipSuccess && !first && sg) err = gla::launch_add_into(b, dg, ws + L.dgh, rows_t, strm);
+        if (err == hipSuccess && ds0) err = state_rows_in(ws + L.ds0h, s, k0, W, ds0, strm);
+    }
+    return err;
+}
+
 gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                       const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
                       float* ds0, void* workspace, size_t workspace_bytes, void* stream, bool sg,
@@ -566,7 +911,7 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     const char* names[] = {"q", "k", "v", "g", "s0", "d_o", "dht", "dq", "dk", "dv", "dg", "ds0", "workspace"};
     for (int i = 0; i < 13; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const size_t need = bwd_total_bytes(s, sg);
+    const size_t need = bwd_any_bytes(s, sg);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -575,10 +920,8 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     if (empty) {
         // no tokens: dS_0 = dht (the state passes through unchanged)
         err = ds0 ? gla::launch_state_copy(dht, ds0, s.B * s.H * s.K * s.V, strm) : hipSuccess;
-    } else if (split_bwd(s)) {
-        err = bwd_split_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, strm);
     } else {
-        err = bwd_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, ckpt, strm);
+        err = bwd_any_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, ckpt, strm);
     }
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
@@ -608,19 +951,19 @@ const char* gla_last_error_detail(void) { return g_detail.c_str(); }
 size_t gla_fwd_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
     if (check_shape(shape, &s, false) != GLA_OK) return 0;
-    return fwd_total_bytes(s);
+    return fwd_any_bytes(s, false);
 }
 
 size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
     if (check_shape(shape, &s, true) != GLA_OK) return 0;
-    return bwd_total_bytes(s, false);
+    return bwd_any_bytes(s, false);
 }
 
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
     if (check_shape(shape, &s, true) != GLA_OK || !s.bf16) return 0;
-    return bwd_total_bytes(s, true);
+    return bwd_any_bytes(s, true);
 }
 
 gla_status_t gla_fwd(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
@@ -637,7 +980,7 @@ gla_status_t gla_fwd_noalloc(const gla_shape_t* shape, const void* q, const void
     // every argument is checked before the first HIP call (the scratch lookup)
     gla_status_t st = fwd_check(shape, q, k, v, g, s0, o, s_final, false, &s);
     if (st != GLA_OK) return st;
-    const size_t need = fwd_total_bytes(s);
+    const size_t need = fwd_any_bytes(s, false);
     if (need > gla::kNoAllocScratchBytes)
         return fail(GLA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the fixed scratch of gla_fwd_noalloc "
                     "holds %zu (call gla_fwd with a workspace)", need, gla::kNoAllocScratchBytes);
@@ -692,8 +1035,8 @@ gla_status_t gla_fwd_scalar(const gla_shape_t* shape, const void* q, const void*
 
 size_t gla_fwd_general_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
-    if (check_shape(shape, &s, false) != GLA_OK || !s.bf16 || (s.K != 128 && s.K != 256)) return 0;
-    return gla::fwd_general_workspace_bytes(s);
+    if (check_shape(shape, &s, false) != GLA_OK || !s.bf16 || !general_k_ok(s.K)) return 0;
+    return fwd_general_any_bytes(s);
 }
 
 gla_status_t gla_fwd_general(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
@@ -704,9 +1047,8 @@ gla_status_t gla_fwd_general(const gla_shape_t* shape, const void* q, const void
 
 size_t gla_bwd_general_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
-    if (check_shape(shape, &s, true) != GLA_OK || !s.bf16 || (s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256))
-        return 0;
-    return gla::bwd_general_layout(s).total;
+    if (check_shape(shape, &s, true) != GLA_OK || !s.bf16 || !general_bwd_kv_ok(s.K, s.V)) return 0;
+    return bwd_general_any_bytes(s);
 }
 
 gla_status_t gla_bwd_general(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

@@ -104,6 +104,7 @@ hipError_t launch_decode_t(const DecodeLaunch& a) {
         case 64: return launch_decode_k<T, 64>(a);
         case 128: return launch_decode_k<T, 128>(a);
         case 256: return launch_decode_k<T, 256>(a);
+        case 512: return launch_decode_k<T, 512>(a);
     }
     return hipErrorInvalidValue;
 }

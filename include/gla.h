@@ -39,12 +39,14 @@
  *      definition in Section 4.1 requires; g = 0 is ungated linear attention,
  *      Eq. 1).  Violations give unspecified values, never an out-of-bounds
  *      access.
- *  Supported sizes: chunk == 64; T a multiple of 64; bf16: K in
- *      {64, 128, 256} and V in {64, 128, 256, 512} (the backward runs V = 512
- *      as two V = 256 column halves: the recurrence never mixes value columns);
- *      fp32: K in {64, 128} and V in {64, 128, 256, 512} (V = 256 and 512 run,
- *      forward and backward, as slices of 128 value columns whose staging
- *      copies sit in the workspace).  B, H >= 0 and T >= 0; B*H == 0 or T == 0
+ *  Supported sizes: chunk == 64; T a multiple of 64; K and V in {64, 128,
+ *      256, 512}, bf16 or fp32.  Heads wider than the kernels run as slices
+ *      whose staging copies sit in the workspace: value slices (the
+ *      recurrence never mixes value columns: the 16-bit backward at V = 512
+ *      in two slices of 256, fp32 at V = 256 and 512 in slices of 128) and key
+ *      slices (Diag(alpha_t) never mixes state rows and o_t sums over them:
+ *      16-bit K = 512 in two slices of 256, fp32 K = 256 and 512 in slices of
+ *      128; the slices' outputs and dv add).  B, H >= 0 and T >= 0; B*H == 0 or T == 0
  *      is a valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
  */
 #ifndef GLA_H_
@@ -231,7 +233,8 @@ size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
  *   v, h    : [B,T,H,V] bf16   (h = log beta <= 0)
  *   s0, o, s_final, stream : as for gla_fwd
  *   workspace : at least gla_fwd_general_workspace_size(shape) bytes
- * bf16 with K in {128, 256} and V in {64, 128, 256, 512}; other shapes and
+ * bf16 with K in {128, 256, 512} (512 as two key slices of 256 that share v
+ * and h, their outputs added) and V in {64, 128, 256, 512}; other shapes and
  * fp32 return GLA_ERR_UNSUPPORTED.  Results are deterministic.  The backward is
  * gla_bwd_general.
  */
@@ -241,7 +244,8 @@ gla_status_t gla_fwd_general(const gla_shape_t* shape,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gla_fwd_general needs (0 for fp32, K = 64 or an invalid
- * shape; no HIP call).  Segment states and the segments' key-row and
+ * shape; no HIP call).  At K = 512 the key slice's q, k, g, partial output and
+ * state rows, then the K = 256 workspace.  Segment states and the segments' key-row and
  * value-column log-decays, and one record per chunk and head of
  * 268 K + 392 V + 8704 bytes (prepared key-side operands and A, v * exp2(C_63 - C_t),
  * exp2(C_t), the intra-chunk output (kept only where the walk cannot form it) and the
@@ -261,8 +265,10 @@ size_t gla_fwd_general_workspace_size(const gla_shape_t* shape);
  *   q, k, g, v, h, s0 : as for gla_fwd_general;  d_o, dht : as for gla_bwd
  *   dq, dk, dg : [B,T,H,K] bf16;  dv, dh : [B,T,H,V] bf16;  ds0 : [B,H,K,V] fp32 or NULL
  *   workspace : at least gla_bwd_general_workspace_size(shape) bytes
- * bf16 with K and V in {128, 256}; other shapes and fp32 return
- * GLA_ERR_UNSUPPORTED.  Results are deterministic.
+ * bf16 with K and V in {128, 256, 512}; 512 runs as two slices of 256: key
+ * slices share v and h (dq, dk, dg side by side, dv and dh added), value
+ * slices share q, k and g (dv, dh side by side, dq, dk, dg added).  Other
+ * shapes and fp32 return GLA_ERR_UNSUPPORTED.  Results are deterministic.
  */
 gla_status_t gla_bwd_general(const gla_shape_t* shape,
                              const void* q, const void* k, const void* v, const void* g,
@@ -274,7 +280,8 @@ gla_status_t gla_bwd_general(const gla_shape_t* shape,
  * invalid shape; no HIP call): the forward's o and S_T, the states before every
  * chunk of the forward and of the time-reversed dS recurrence, the gate-gradient
  * anchors and the general forward's workspace.  The time-reversed recurrences
- * read q, k, v, d_o and the gates in place. */
+ * read q, k, v, d_o and the gates in place.  At K or V = 512, the slices'
+ * gathered inputs and partial gradients come first. */
 size_t gla_bwd_general_workspace_size(const gla_shape_t* shape);
 
 /*
@@ -288,16 +295,16 @@ size_t gla_bwd_general_workspace_size(const gla_shape_t* shape);
  *   gla_general_ckpt_size(shape) : bytes of the checkpoint, the states
  *     [B,H,T/64,K,V] bf16 (entry 0 of each head is not used), then S_T
  *     [B,H,K,V] fp32 at a 256-byte aligned offset; 0 for an empty, invalid or
- *     unsupported shape (the shapes of gla_bwd_general).
+ *     unsupported shape (bf16 with K and V in {128, 256}).
  *   gla_fwd_general_ckpt : gla_fwd_general (same arguments, results and
- *     workspace) for the shapes of gla_bwd_general, plus writes ckpt (device,
+ *     workspace) for bf16 with K and V in {128, 256}, plus writes ckpt (device,
  *     16-byte aligned, required unless the shape is empty).
  *   gla_bwd_general_ckpt : gla_bwd_general (same arguments, results and
  *     workspace), plus reads o and ckpt, which must hold what
  *     gla_fwd_general_ckpt returned for the same shape, q, k, v, g, h and s0,
  *     unmodified since (not checked: other contents give wrong gradients).
- * Errors: as gla_fwd_general / gla_bwd_general; GLA_ERR_UNSUPPORTED for a shape
- * gla_bwd_general does not take, GLA_ERR_NULL for a NULL o or ckpt on a
+ * Errors: as gla_fwd_general / gla_bwd_general; GLA_ERR_UNSUPPORTED for K or V
+ * outside {128, 256}, GLA_ERR_NULL for a NULL o or ckpt on a
  * non-empty shape, GLA_ERR_ALIGN for a misaligned one.
  */
 size_t gla_general_ckpt_size(const gla_shape_t* shape);
@@ -323,7 +330,7 @@ gla_status_t gla_bwd_general_ckpt(const gla_shape_t* shape,
  *   state   : [B,H,K,V] float32, read and overwritten in place (required)
  *   o       : [B,T,H,V] dtype output
  *   stream  : as for gla_fwd.  No workspace.
- * Supported: K in {64, 128, 256}, V in {64, 128, 256, 512}, bf16 or fp32.
+ * Supported: K and V in {64, 128, 256, 512}, bf16 or fp32.
  * T == 0 or B*H == 0 is a no-op.  Returns GLA_OK or an error code.
  */
 gla_status_t gla_decode(const gla_shape_t* shape,

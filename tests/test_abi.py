@@ -71,7 +71,8 @@ def test_validation_codes(L):
     assert _fwd(L, _shape(K=96)) == ERR_UNSUPPORTED
     assert _fwd(L, _shape(V=1024)) == ERR_UNSUPPORTED
     assert _fwd(L, _shape(dtype=7)) == ERR_UNSUPPORTED
-    assert _fwd(L, _shape(K=256, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(K=1024, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert _fwd(L, _shape(K=1024)) == ERR_UNSUPPORTED
     assert _fwd(L, _shape(reserved=1)) == ERR_UNSUPPORTED
     assert _fwd(L, _shape(), k=ctypes.c_void_p(0x10008)) == ERR_ALIGN
     assert _fwd(L, _shape(), s0=ctypes.c_void_p(0x10004)) == ERR_ALIGN
@@ -121,6 +122,7 @@ def test_decode_validation_codes(L):
     assert _dec(L, _shape(T=5), o=None) == ERR_NULL
     assert _dec(L, _shape(T=-1)) == ERR_SHAPE
     assert _dec(L, _shape(T=5, K=96)) == ERR_UNSUPPORTED
+    assert _dec(L, _shape(T=5, K=1024)) == ERR_UNSUPPORTED
     assert _dec(L, _shape(T=5, V=1024)) == ERR_UNSUPPORTED
     assert _dec(L, _shape(T=5, dtype=7)) == ERR_UNSUPPORTED
     assert _dec(L, _shape(T=5, reserved=1)) == ERR_UNSUPPORTED
@@ -179,8 +181,29 @@ def test_fp32_wide_values_run_as_slices(L):
         assert need_f > 0 and _fwd(L, s, wsb=need_f - 1) == ERR_WORKSPACE
         need_b = L.gla_bwd_workspace_size(ctypes.byref(s))
         assert need_b > 0 and _bwd(L, s, wsb=need_b - 1) == ERR_WORKSPACE
-    assert _fwd(L, _shape(K=256, V=256, dtype=f32)) == ERR_UNSUPPORTED
     assert L.gla_ckpt_size(ctypes.byref(_shape(T=1024, K=128, V=256, dtype=f32))) == 0
+
+
+def test_wide_keys_run_as_slices(L):
+    # K past the kernels' widest (16-bit: 256, fp32: 128) runs as key slices:
+    # the workspace holds one slice's q, k, g columns (per-column gates), the
+    # partial output (forward) or dq, dk, dg and the partial dv (backward), its
+    # state rows and that slice's own workspace
+    rows = 2 * 4 * 1024
+    for dtype, W, e in ((gla.GLA_DTYPE_BF16, 256, 2), (gla.GLA_DTYPE_FP32, 128, 4)):
+        for K in (2 * W, 512):
+            s = _shape(B=2, H=4, T=1024, K=K, V=128, dtype=dtype)
+            sub = _shape(B=2, H=4, T=1024, K=W, V=128, dtype=dtype)
+            f, fs = L.gla_fwd_workspace_size(ctypes.byref(s)), L.gla_fwd_workspace_size(ctypes.byref(sub))
+            b, bs = L.gla_bwd_workspace_size(ctypes.byref(s)), L.gla_bwd_workspace_size(ctypes.byref(sub))
+            assert f >= fs + 3 * rows * W * e + rows * 128 * e
+            assert b >= bs + 6 * rows * W * e + rows * 128 * e
+            assert _fwd(L, s, wsb=f - 1) == ERR_WORKSPACE
+            assert _bwd(L, s, wsb=b - 1) == ERR_WORKSPACE
+    # the scalar gate is shared by the slices: no per-slice gate copy, one dg partial
+    s = _shape(B=2, H=4, T=1024, K=512, V=128)
+    assert L.gla_bwd_scalar_workspace_size(ctypes.byref(s)) > 0
+    assert L.gla_ckpt_size(ctypes.byref(_shape(T=8192, K=512, V=128))) == 0
 
 
 def test_scalar_gate_entry_points_validate(L):
@@ -222,7 +245,11 @@ def test_general_gate_backward_validates(L):
     ws = lambda shape: L.gla_bwd_general_workspace_size(ctypes.byref(shape))
     assert ws(_shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)) == 0
     assert ws(_shape(T=128, K=64, V=128)) == 0
-    assert ws(_shape(T=128, K=128, V=512)) == 0
+    assert ws(_shape(T=128, K=128, V=64)) == 0
+    # V = 512 as two value slices, K = 512 as two key slices, around the K, V <= 256 backward
+    sub = ws(_shape(T=128, K=128, V=256))
+    assert ws(_shape(T=128, K=128, V=512)) > sub > 0
+    assert ws(_shape(T=128, K=512, V=512)) > ws(_shape(T=128, K=256, V=512)) > 0
     s = _shape(B=2, H=4, T=8192, K=128, V=256)
     # at least the chunk-start states of the forward and of the reversed dS pass
     assert ws(s) == ws(s) and ws(s) >= 2 * (2 * 4 * 128 * 128 * 256 * 2)
@@ -307,7 +334,7 @@ def test_ckpt_entry_points_validate(L):
     assert bwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
     assert fwd(_shape(T=100)) == ERR_SHAPE
     assert bwd(_shape(V=1024)) == ERR_UNSUPPORTED
-    assert bwd(_shape(K=256, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert bwd(_shape(K=1024, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
 
 
 def test_general_ckpt_entry_points_validate(L):
@@ -318,7 +345,8 @@ def test_general_ckpt_entry_points_validate(L):
     assert size(_shape(K=256, V=128, T=640)) > 0
     assert size(_shape(dtype=gla.GLA_DTYPE_FP32)) == 0   # the general path takes bf16
     assert size(_shape(K=64)) == 0                       # K not in {128, 256}
-    assert size(_shape(K=128, V=512, T=8192)) == 0       # V = 512: no general backward
+    assert size(_shape(K=128, V=512, T=8192)) == 0       # V = 512: the value-sliced backward, no checkpoint
+    assert size(_shape(K=512, V=128, T=8192)) == 0       # K = 512: the key-sliced backward, no checkpoint
     assert size(_shape(T=0)) == 0
     fwd = lambda shape, ck=P, o=P: L.gla_fwd_general_ckpt(ctypes.byref(shape), P, P, P, P, P, None, o, None, ck, P,
                                                           1 << 40, None)

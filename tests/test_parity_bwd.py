@@ -194,6 +194,23 @@ def test_bwd_fp32_wide_values_exact_path():
     _check_bwd(w, inputs=exact_path_inputs(w))
 
 
+@pytest.mark.parametrize("dtype,K,V,T,dht", [("bf16", 512, 64, 320, True), ("bf16", 512, 512, 192, True),
+                                             ("fp32", 256, 128, 256, True), ("fp32", 512, 256, 192, False),
+                                             ("fp32", 256, 64, 448, True)])
+def test_bwd_wide_keys(dtype, K, V, T, dht):
+    # key slices: dq, dk, dg are the slices' columns, dv their sum, dS0 their
+    # row blocks (fp32 K = 512, V = 256 is sliced both ways)
+    w = gi.custom(1, 2, T, K, V, dtype=dtype, gate="lowrank", s0="normal0.1", backward=True, seed=680 + K + V + T)
+    _check_bwd(w, with_dht=dht)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_wide_keys_exact_path(dtype):
+    from tests.test_parity_fwd import exact_path_inputs
+    w = gi.custom(1, 2, 256, 512, 128, dtype=dtype, gate="iid", s0="normal0.1", backward=True, seed=691)
+    _check_bwd(w, inputs=exact_path_inputs(w))
+
+
 def test_bwd_1p3b_head_shape_sampled_heads():
     # the 1.3B-model head shape at length 8K (the gla_1p3b_long recipe and seed,
     # with an upstream gradient drawn as well), two heads against the oracle

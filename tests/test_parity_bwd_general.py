@@ -50,6 +50,18 @@ def test_bwd_general_heads(B, H, T, K, V, s0):
     _check(w, inp, h, _heads(B, H))
 
 
+@pytest.mark.parametrize("B,H,T,K,V,s0", [
+    (1, 2, 64 * 5, 512, 128, "normal0.1"),   # two key slices: dv, dh added
+    (1, 2, 64 * 6, 128, 512, "normal0.1"),   # two value slices: dq, dk, dg added
+    (1, 2, 64 * 3, 512, 512, "none"),        # both
+])
+def test_bwd_general_wide_heads(B, H, T, K, V, s0):
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0=s0, backward=True, seed=1520 + T + K + V)
+    inp = gi.make_inputs(w, dht=True)
+    h = gi.make_value_gate(B, T, H, V, seed=1620 + T + V)
+    _check(w, inp, h, _heads(B, H))
+
+
 def test_bwd_general_exact_paths_and_no_dht():
     B, H, T, K, V = 2, 2, 64 * 6, 128, 128
     w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=1701)

@@ -30,6 +30,8 @@ def _inputs(B, H, T, K, V, dtype, gate, seed):
     (2, 3, 5, 64, 128, "fp32", "iid"),
     (1, 2, 7, 128, 256, "bf16", "lowrank"),
     (2, 1, 3, 256, 512, "bf16", "lowrank"),
+    (1, 2, 4, 512, 128, "bf16", "lowrank"),  # 32 state rows per thread
+    (1, 1, 3, 512, 64, "fp32", "iid"),
     (3, 2, 4, 128, 64, "bf16", "zero"),      # ungated: plain causal linear attention
     (1, 2, 70, 64, 64, "bf16", "iid"),       # longer than a chunk, not a multiple of it
 ])

@@ -69,6 +69,23 @@ def test_fwd_fp32_wide_values(K, V, T):
     _run_and_check(w)
 
 
+@pytest.mark.parametrize("dtype,K,V,T", [("bf16", 512, 64, 320), ("bf16", 512, 512, 192), ("fp32", 256, 128, 256),
+                                         ("fp32", 512, 256, 192), ("fp32", 256, 64, 448)])
+def test_fwd_wide_keys(dtype, K, V, T):
+    # K past the kernels' widest (16-bit: 256, fp32: 128) runs as key slices:
+    # each state row evolves on its own, o adds the slices' outputs and S_T
+    # stacks their row blocks (fp32 K = 512, V = 256 is sliced both ways)
+    w = gi.custom(1, 2, T, K, V, dtype=dtype, gate="lowrank", s0="normal0.1", backward=False, seed=660 + K + V + T)
+    _run_and_check(w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fwd_wide_keys_exact_path(dtype):
+    # the -70 nat reset lands in the first key slice, the -9 nat run in the second
+    w = gi.custom(1, 2, 256, 512, 128, dtype=dtype, gate="iid", s0="normal0.1", backward=False, seed=671)
+    _run_and_check(w, inputs=exact_path_inputs(w))
+
+
 def test_fwd_fp32_wide_values_exact_path():
     w = gi.custom(1, 2, 256, 128, 256, dtype="fp32", gate="iid", s0="normal0.1", backward=False, seed=631)
     _run_and_check(w, inputs=exact_path_inputs(w))

@@ -84,10 +84,18 @@ def test_scalar_gate_matches_oracle(B, H, T, K, V, s0):
     _check(w, inp)
 
 
-def test_scalar_gate_forward_wide_values():
-    # dv = 512 has a forward kernel (the backward holds V <= 256)
+def test_scalar_gate_wide_values():
+    # dv = 512: a forward kernel; the backward runs two value slices of 256
     w, inp = _inputs(1, 2, 256, 128, 512, "normal0.1", seed=771)
-    _check(w, inp, backward=False)
+    _check(w, inp)
+
+
+@pytest.mark.parametrize("K,V,T", [(512, 128, 320), (512, 512, 192)])
+def test_scalar_gate_wide_keys(K, V, T):
+    # dk = 512: two key slices of 256 that share the per-token gate; dg is the
+    # sum of the slices' gate gradients
+    w, inp = _inputs(1, 2, T, K, V, "normal0.1", seed=780 + K + V + T)
+    _check(w, inp)
 
 
 def test_scalar_gate_ungated():
