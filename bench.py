@@ -812,7 +812,8 @@ def main():
     dg = torch.empty(*d["g"].shape, dtype=dt, device=dev)
     dv = torch.empty(B, T, H, V, dtype=dt, device=dev)
     ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev)
-    wsf = gla.workspace(gla.gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+    wsf = gla.workspace((gla.gla_fwd_scalar_workspace_size if sg else gla.gla_fwd_workspace_size)(
+        B, T, H, K, V, dt), dev)
     wsb = gla.workspace((gla.gla_bwd_scalar_workspace_size if sg else gla.gla_bwd_workspace_size)(
         B, T, H, K, V, dt), dev)
 

@@ -55,6 +55,7 @@ class GlaError(RuntimeError):
 
 EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode", "gla_out_gate",
            "gla_out_gate_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_bwd_scalar_workspace_size",
+           "gla_fwd_scalar_workspace_size",
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
@@ -92,6 +93,8 @@ def lib():
     L.gla_bwd_scalar.argtypes = L.gla_bwd.argtypes
     L.gla_bwd_scalar.restype = ctypes.c_int
     L.gla_bwd_scalar_workspace_size.argtypes = [sh]
+    L.gla_fwd_scalar_workspace_size.argtypes = [sh]
+    L.gla_fwd_scalar_workspace_size.restype = ctypes.c_size_t
     L.gla_fwd_general.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gla_fwd_general.restype = ctypes.c_int
     L.gla_fwd_general_workspace_size.argtypes = [sh]
@@ -275,6 +278,10 @@ def gla_bwd_ckpt(q, k, v, g, d_o, ckpt, s0=None, dht=None, output_ds0=True, stre
     return dq, dk, dv, dg, ds0
 
 
+def gla_fwd_scalar_workspace_size(B, T, H, K, V, dtype) -> int:
+    return int(lib().gla_fwd_scalar_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
+
+
 def gla_bwd_scalar_workspace_size(B, T, H, K, V, dtype) -> int:
     return int(lib().gla_bwd_scalar_workspace_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
 
@@ -311,7 +318,7 @@ def gla_bwd(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
 
 
 def gla_fwd_scalar(q, k, v, g, s0=None, output_final_state=True, stream=None):
-    """gla_fwd with a scalar gate g [B,T,H] per token and head (bf16)."""
+    """gla_fwd with a scalar gate g [B,T,H] per token and head."""
     B, T, H, K, V = _dims(q, v)
     dev, dt = q.device, q.dtype
     for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),
@@ -320,13 +327,13 @@ def gla_fwd_scalar(q, k, v, g, s0=None, output_final_state=True, stream=None):
     _need(s0, "s0", (B, H, K, V), torch.float32, dev)
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
     sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
-    ws = workspace(gla_fwd_workspace_size(B, T, H, K, V, dt), dev)
+    ws = workspace(gla_fwd_scalar_workspace_size(B, T, H, K, V, dt), dev)
     gla_fwd_into(q, k, v, g, s0, o, sf, ws, stream, scalar_gate=True)
     return o, sf
 
 
 def gla_bwd_scalar(q, k, v, g, d_o, s0=None, dht=None, output_ds0=True, stream=None):
-    """gla_bwd with a scalar gate g [B,T,H]; dg is [B,T,H] (bf16)."""
+    """gla_bwd with a scalar gate g [B,T,H]; dg is [B,T,H]."""
     B, T, H, K, V = _dims(q, v)
     dev, dt = q.device, q.dtype
     for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),

@@ -133,7 +133,6 @@ gla_status_t fwd_check(const gla_shape_t* shape, const void* q, const void* k, c
                        const float* s0, void* o, float* s_final, bool sg, gla::Shape* s) {
     gla_status_t st = check_shape(shape, s, false);
     if (st != GLA_OK) return st;
-    if (sg && !s->bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
     const bool empty = s->B * s->H == 0 || s->T == 0;
     if (!empty && (!q || !k || !v || !g || !o)) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
     const void* ptrs[] = {q, k, v, g, s0, o, s_final};
@@ -320,8 +319,17 @@ hipError_t fwd_ksplit(const gla::Shape& s, const void* q, const void* k, const v
     return err;
 }
 
+// fp32 inputs with one gate per token run the per-column path on the gate
+// repeated over the key columns (alpha_t = exp(g_t) times the all-ones row is
+// exactly the per-column gate with equal columns); the gate's gradient is then
+// the sum over the columns of the per-column one.  The repeated gate (and, in
+// the backward, the per-column gradient) sit at the start of the workspace.
+bool sg_bcast(const gla::Shape& s, bool sg) { return sg && !s.bf16; }
+size_t bcast_gate_bytes(const gla::Shape& s) { return gla::round256((size_t)(s.B * s.T * s.H) * (size_t)s.K * 4); }
+
 size_t fwd_any_bytes(const gla::Shape& s, bool sg) {
     if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (sg_bcast(s, sg)) return bcast_gate_bytes(s) + fwd_any_bytes(s, false);
     if (!split_k(s)) return fwd_total_bytes(s);
     return kfwd_layout(s, sg, fwd_total_bytes(kslice_shape(s))).total;
 }
@@ -330,6 +338,13 @@ size_t fwd_any_bytes(const gla::Shape& s, bool sg) {
 hipError_t fwd_any_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
                           const float* s0, void* o, float* s_final, void* workspace, bool sg, void* ckpt,
                           hipStream_t strm) {
+    if (sg_bcast(s, sg)) {
+        float* gk = static_cast<float*>(workspace);
+        const hipError_t err = gla::launch_bcast_cols(static_cast<const float*>(g), gk, s.K, s.B * s.T * s.H, strm);
+        if (err != hipSuccess) return err;
+        return fwd_any_launch(s, q, k, v, gk, s0, o, s_final, static_cast<char*>(workspace) + bcast_gate_bytes(s),
+                              false, nullptr, strm);
+    }
     if (!split_k(s)) return fwd_v_launch(s, q, k, v, g, s0, o, s_final, workspace, sg, ckpt, strm);
     const gla::Shape h = kslice_shape(s);
     const KFwdLayout L = kfwd_layout(s, sg, fwd_total_bytes(h));
@@ -418,11 +433,59 @@ hipError_t fwd_general_launch(const gla::Shape& s, const void* q, const void* k,
 // General gates take K in {128, 256, 512} (512 as two key slices: the gate
 // alpha^T beta still scales each state row on its own, so the slices share v
 // and the value-side gate h) and V in {64 .. 512} in the forward.
-bool general_k_ok(int64_t K) { return K == 128 || K == 256 || K == 512; }
+// K = 64 is padded to 128 with zero columns of q, k and g (and zero rows of
+// S_0): a zero gate keeps alpha = 1 there, so the padded state rows start and
+// stay zero and add nothing to o = q S; the results are exactly the K = 64
+// ones.  (The value side pads the same way in the backward: zero columns of
+// v, h and d_o.)
+bool general_k_ok(int64_t K) { return K == 64 || K == 128 || K == 256 || K == 512; }
+constexpr long kGeneralMinDim = 128;
+gla::Shape general_kpad_shape(const gla::Shape& s) {
+    gla::Shape p = s;
+    p.K = kGeneralMinDim;
+    return p;
+}
+struct GKPadFwd {
+    size_t qp, kp, gp, s0p, sfp, inner, total;
+};
+GKPadFwd general_kpad_fwd_layout(const gla::Shape& s) {
+    GKPadFwd w{};
+    const size_t P = kGeneralMinDim, BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.qp = take(BTH * P * 2);
+    w.kp = take(BTH * P * 2);
+    w.gp = take(BTH * P * 2);
+    w.s0p = take(BH * P * s.V * 4);
+    w.sfp = take(BH * P * s.V * 4);
+    w.inner = take(gla::fwd_general_workspace_bytes(general_kpad_shape(s)));
+    w.total = at;
+    return w;
+}
 size_t fwd_general_any_bytes(const gla::Shape& s) {
     if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (s.K < kGeneralMinDim) return general_kpad_fwd_layout(s).total;
     if (!split_k(s)) return gla::fwd_general_workspace_bytes(s);
     return kfwd_layout(s, false, gla::fwd_general_workspace_bytes(kslice_shape(s))).total;
+}
+
+hipError_t fwd_general_kpad_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
+                                   const void* h, const float* s0, void* o, float* s_final, void* workspace,
+                                   hipStream_t strm) {
+    const GKPadFwd L = general_kpad_fwd_layout(s);
+    const gla::Shape p = general_kpad_shape(s);
+    char* ws = static_cast<char*>(workspace);
+    const long K = s.K, P = p.K, rows_t = s.B * s.T * s.H, BH = s.B * s.H;
+    hipError_t err = gla::launch_pad_cols(true, q, K, K, ws + L.qp, P, P, rows_t, strm);
+    if (err == hipSuccess) err = gla::launch_pad_cols(true, k, K, K, ws + L.kp, P, P, rows_t, strm);
+    if (err == hipSuccess) err = gla::launch_pad_cols(true, g, K, K, ws + L.gp, P, P, rows_t, strm);
+    if (err == hipSuccess && s0) err = gla::launch_pad_cols(false, s0, K * s.V, K * s.V, ws + L.s0p, P * s.V, P * s.V, BH, strm);
+    if (err != hipSuccess) return err;
+    err = fwd_general_launch(p, ws + L.qp, ws + L.kp, v, ws + L.gp, h, s0 ? (const float*)(ws + L.s0p) : nullptr, o,
+                             s_final ? (float*)(ws + L.sfp) : nullptr, ws + L.inner, nullptr, strm);
+    if (err == hipSuccess && s_final)
+        err = gla::launch_copy_cols(false, ws + L.sfp, P * s.V, 0, s_final, K * s.V, 0, K * s.V, BH, strm);
+    return err;
 }
 
 gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v,
@@ -435,8 +498,8 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     if (st != GLA_OK) return st;
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
     if (!general_k_ok(s.K))
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 128, 256 or 512 (got %lld)", (long long)s.K);
-    if (want_ckpt && (s.K > 256 || (s.V != 128 && s.V != 256)))
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 64, 128, 256 or 512 (got %lld)", (long long)s.K);
+    if (want_ckpt && ((s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256)))
         return fail(GLA_ERR_UNSUPPORTED, "the general-gate checkpoint takes K and V in {128, 256} (got K=%lld V=%lld)",
                     (long long)s.K, (long long)s.V);
     const bool empty = s.B * s.H == 0 || s.T == 0;
@@ -455,6 +518,8 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     hipError_t err;
     if (empty) {
         err = s_final ? gla::launch_state_copy(s0, s_final, s.B * s.H * s.K * s.V, strm) : hipSuccess;
+    } else if (s.K < kGeneralMinDim) {
+        err = fwd_general_kpad_launch(s, q, k, v, g, h, s0, o, s_final, workspace, strm);
     } else if (!split_k(s)) {
         err = fwd_general_launch(s, q, k, v, g, h, s0, o, s_final, workspace, want_ckpt ? ckpt : nullptr, strm);
     } else {
@@ -522,7 +587,33 @@ GVLayout general_v_layout(const gla::Shape& s) {
     w.total = at;
     return w;
 }
+// V = 64: v, h and d_o padded with zero columns (S_0, dht with zero columns):
+// the padded state columns start and stay zero, so dq, dk and dg are exact and
+// dv, dh, dS_0 are the first 64 columns of the padded problem's.
+struct GVPad {
+    size_t vp, hp, dop, dvp, dhp, s0p, dhtp, ds0p, inner, total;
+};
+GVPad general_vpad_layout(const gla::Shape& s) {
+    GVPad w{};
+    gla::Shape p = s;
+    p.V = kGeneralMinDim;
+    const size_t P = kGeneralMinDim, BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.vp = take(BTH * P * 2);
+    w.hp = take(BTH * P * 2);
+    w.dop = take(BTH * P * 2);
+    w.dvp = take(BTH * P * 2);
+    w.dhp = take(BTH * P * 2);
+    w.s0p = take(BH * s.K * P * 4);
+    w.dhtp = take(BH * s.K * P * 4);
+    w.ds0p = take(BH * s.K * P * 4);
+    w.inner = take(gla::bwd_general_layout(p).total);
+    w.total = at;
+    return w;
+}
 size_t bwd_general_v_bytes(const gla::Shape& s) {
+    if (s.V < kGeneralMinDim) return general_vpad_layout(s).total;
     return s.V > kGeneralSliceV ? general_v_layout(s).total : gla::bwd_general_layout(s).total;
 }
 
@@ -530,6 +621,28 @@ hipError_t bwd_general_v_launch(const gla::Shape& s, const void* q, const void* 
                                 const void* h, const float* s0, const void* d_o, const float* dht, void* dq,
                                 void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
                                 hipStream_t strm) {
+    if (s.V < kGeneralMinDim) {
+        const GVPad L = general_vpad_layout(s);
+        gla::Shape p = s;
+        p.V = kGeneralMinDim;
+        char* ws = static_cast<char*>(workspace);
+        const long V = s.V, P = p.V, rows_t = s.B * s.T * s.H, rows_s = s.B * s.H * s.K;
+        hipError_t err = gla::launch_pad_cols(true, v, V, V, ws + L.vp, P, P, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_pad_cols(true, h, V, V, ws + L.hp, P, P, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_pad_cols(true, d_o, V, V, ws + L.dop, P, P, rows_t, strm);
+        if (err == hipSuccess && s0) err = gla::launch_pad_cols(false, s0, V, V, ws + L.s0p, P, P, rows_s, strm);
+        if (err == hipSuccess && dht) err = gla::launch_pad_cols(false, dht, V, V, ws + L.dhtp, P, P, rows_s, strm);
+        if (err != hipSuccess) return err;
+        err = bwd_general_launch(p, q, k, ws + L.vp, g, ws + L.hp, s0 ? (const float*)(ws + L.s0p) : nullptr,
+                                 ws + L.dop, dht ? (const float*)(ws + L.dhtp) : nullptr, dq, dk, ws + L.dvp, dg,
+                                 ws + L.dhp, ds0 ? (float*)(ws + L.ds0p) : nullptr, ws + L.inner, nullptr, nullptr,
+                                 strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dvp, P, 0, dv, V, 0, V, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dhp, P, 0, dh, V, 0, V, rows_t, strm);
+        if (err == hipSuccess && ds0)
+            err = gla::launch_copy_cols(false, ws + L.ds0p, P, 0, ds0, V, 0, V, rows_s, strm);
+        return err;
+    }
     if (s.V <= kGeneralSliceV)
         return bwd_general_launch(s, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, nullptr,
                                   nullptr, strm);
@@ -593,9 +706,36 @@ GKLayout general_k_layout(const gla::Shape& s) {
     w.total = at;
     return w;
 }
-bool general_bwd_kv_ok(int64_t K, int64_t V) { return general_k_ok(K) && (V == 128 || V == 256 || V == 512); }
+bool general_bwd_kv_ok(int64_t K, int64_t V) { return general_k_ok(K) && (V == 64 || V == 128 || V == 256 || V == 512); }
+
+// K = 64 (the forward's padding): q, k, g with zero columns, S_0 and dht with
+// zero rows; dq, dk, dg and dS_0 are the first 64 columns / rows, dv and dh
+// are exact as they are.
+struct GKPadBwd {
+    size_t qp, kp, gp, dqp, dkp, dgp, s0p, dhtp, ds0p, inner, total;
+};
+GKPadBwd general_kpad_bwd_layout(const gla::Shape& s) {
+    GKPadBwd w{};
+    const size_t P = kGeneralMinDim, BTH = (size_t)(s.B * s.T * s.H), BH = (size_t)(s.B * s.H);
+    size_t at = 0;
+    auto take = [&](size_t n) { const size_t o = at; at += gla::round256(n); return o; };
+    w.qp = take(BTH * P * 2);
+    w.kp = take(BTH * P * 2);
+    w.gp = take(BTH * P * 2);
+    w.dqp = take(BTH * P * 2);
+    w.dkp = take(BTH * P * 2);
+    w.dgp = take(BTH * P * 2);
+    w.s0p = take(BH * P * s.V * 4);
+    w.dhtp = take(BH * P * s.V * 4);
+    w.ds0p = take(BH * P * s.V * 4);
+    w.inner = take(bwd_general_v_bytes(general_kpad_shape(s)));
+    w.total = at;
+    return w;
+}
+
 size_t bwd_general_any_bytes(const gla::Shape& s) {
     if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (s.K < kGeneralMinDim) return general_kpad_bwd_layout(s).total;
     return split_k(s) ? general_k_layout(s).total : bwd_general_v_bytes(s);
 }
 
@@ -603,6 +743,26 @@ hipError_t bwd_general_any_launch(const gla::Shape& s, const void* q, const void
                                   const void* h, const float* s0, const void* d_o, const float* dht, void* dq,
                                   void* dk, void* dv, void* dg, void* dh, float* ds0, void* workspace,
                                   hipStream_t strm) {
+    if (s.K < kGeneralMinDim) {
+        const GKPadBwd L = general_kpad_bwd_layout(s);
+        const gla::Shape p = general_kpad_shape(s);
+        char* ws = static_cast<char*>(workspace);
+        const long K = s.K, P = p.K, rows_t = s.B * s.T * s.H, BH = s.B * s.H, KV = s.K * s.V, PV = p.K * s.V;
+        hipError_t err = gla::launch_pad_cols(true, q, K, K, ws + L.qp, P, P, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_pad_cols(true, k, K, K, ws + L.kp, P, P, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_pad_cols(true, g, K, K, ws + L.gp, P, P, rows_t, strm);
+        if (err == hipSuccess && s0) err = gla::launch_pad_cols(false, s0, KV, KV, ws + L.s0p, PV, PV, BH, strm);
+        if (err == hipSuccess && dht) err = gla::launch_pad_cols(false, dht, KV, KV, ws + L.dhtp, PV, PV, BH, strm);
+        if (err != hipSuccess) return err;
+        err = bwd_general_v_launch(p, ws + L.qp, ws + L.kp, v, ws + L.gp, h, s0 ? (const float*)(ws + L.s0p) : nullptr,
+                                   d_o, dht ? (const float*)(ws + L.dhtp) : nullptr, ws + L.dqp, ws + L.dkp, dv,
+                                   ws + L.dgp, dh, ds0 ? (float*)(ws + L.ds0p) : nullptr, ws + L.inner, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dqp, P, 0, dq, K, 0, K, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dkp, P, 0, dk, K, 0, K, rows_t, strm);
+        if (err == hipSuccess) err = gla::launch_copy_cols(true, ws + L.dgp, P, 0, dg, K, 0, K, rows_t, strm);
+        if (err == hipSuccess && ds0) err = gla::launch_copy_cols(false, ws + L.ds0p, PV, 0, ds0, KV, 0, KV, BH, strm);
+        return err;
+    }
     if (!split_k(s))
         return bwd_general_v_launch(s, q, k, v, g, h, s0, d_o, dht, dq, dk, dv, dg, dh, ds0, workspace, strm);
     const GKLayout L = general_k_layout(s);
@@ -644,8 +804,8 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     if (st != GLA_OK) return st;
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
     if (want_ckpt ? (s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256) : !general_bwd_kv_ok(s.K, s.V))
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {128, 256%s} (got K=%lld V=%lld)",
-                    want_ckpt ? "" : ", 512", (long long)s.K, (long long)s.V);
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {%s} (got K=%lld V=%lld)",
+                    want_ckpt ? "128, 256" : "64, 128, 256, 512", (long long)s.K, (long long)s.V);
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !d_o || !dq || !dk || !dv || !dg || !dh))
         return fail(GLA_ERR_NULL, "q, k, v, g, h, d_o, dq, dk, dv, dg and dh are required");
@@ -858,6 +1018,7 @@ KBwdLayout kbwd_layout(const gla::Shape& s, bool sg, size_t inner_bytes) {
 
 size_t bwd_any_bytes(const gla::Shape& s, bool sg) {
     if (s.B * s.H == 0 || s.T == 0) return 0;
+    if (sg_bcast(s, sg)) return 2 * bcast_gate_bytes(s) + bwd_any_bytes(s, false);
     if (!split_k(s)) return bwd_total_bytes(s, sg);
     return kbwd_layout(s, sg, bwd_total_bytes(kslice_shape(s), sg)).total;
 }
@@ -866,6 +1027,18 @@ size_t bwd_any_bytes(const gla::Shape& s, bool sg) {
 hipError_t bwd_any_launch(const gla::Shape& s, const void* q, const void* k, const void* v, const void* g,
                           const float* s0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, void* dg,
                           float* ds0, void* workspace, bool sg, const void* ckpt, hipStream_t strm) {
+    if (sg_bcast(s, sg)) {
+        const size_t gb = bcast_gate_bytes(s);
+        const long rows_t = s.B * s.T * s.H;
+        char* ws = static_cast<char*>(workspace);
+        float* gk = reinterpret_cast<float*>(ws);
+        float* dgk = reinterpret_cast<float*>(ws + gb);
+        hipError_t err = gla::launch_bcast_cols(static_cast<const float*>(g), gk, s.K, rows_t, strm);
+        if (err == hipSuccess)
+            err = bwd_any_launch(s, q, k, v, gk, s0, d_o, dht, dq, dk, dv, dgk, ds0, ws + 2 * gb, false, nullptr, strm);
+        if (err == hipSuccess) err = gla::launch_row_sums(dgk, s.K, static_cast<float*>(dg), rows_t, strm);
+        return err;
+    }
     if (!split_k(s)) return bwd_v_launch(s, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, sg, ckpt, strm);
     const gla::Shape h = kslice_shape(s);
     const KBwdLayout L = kbwd_layout(s, sg, bwd_total_bytes(h, sg));
@@ -903,7 +1076,6 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     gla::Shape s;
     gla_status_t st = check_shape(shape, &s, true);
     if (st != GLA_OK) return st;
-    if (sg && !s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the scalar-gate path takes bf16 inputs");
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !d_o || !dq || !dk || !dv || !dg))
         return fail(GLA_ERR_NULL, "q, k, v, g, d_o, dq, dk, dv and dg are required");
@@ -960,9 +1132,15 @@ size_t gla_bwd_workspace_size(const gla_shape_t* shape) {
     return bwd_any_bytes(s, false);
 }
 
+size_t gla_fwd_scalar_workspace_size(const gla_shape_t* shape) {
+    gla::Shape s;
+    if (check_shape(shape, &s, false) != GLA_OK) return 0;
+    return fwd_any_bytes(s, true);
+}
+
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape) {
     gla::Shape s;
-    if (check_shape(shape, &s, true) != GLA_OK || !s.bf16) return 0;
+    if (check_shape(shape, &s, true) != GLA_OK) return 0;
     return bwd_any_bytes(s, true);
 }
 

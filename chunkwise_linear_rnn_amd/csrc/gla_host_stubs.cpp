@@ -29,5 +29,14 @@ hipError_t launch_copy_cols(bool, const void*, long, long, void*, long, long, lo
     return rows <= 0 || W <= 0 ? hipSuccess : hipErrorNoDevice;
 }
 hipError_t launch_add_into(bool, void*, const void*, long n, hipStream_t) { return n <= 0 ? hipSuccess : hipErrorNoDevice; }
+hipError_t launch_pad_cols(bool, const void*, long, long, void*, long, long W_dst, long rows, hipStream_t) {
+    return rows <= 0 || W_dst <= 0 ? hipSuccess : hipErrorNoDevice;
+}
+hipError_t launch_bcast_cols(const float*, float*, long W, long rows, hipStream_t) {
+    return rows <= 0 || W <= 0 ? hipSuccess : hipErrorNoDevice;
+}
+hipError_t launch_row_sums(const float*, long, float*, long rows, hipStream_t) {
+    return rows <= 0 ? hipSuccess : hipErrorNoDevice;
+}
 
 }  // namespace gla

@@ -104,5 +104,10 @@ hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s
 hipError_t launch_copy_cols(bool bf16, const void* src, long ld_s, long off_s, void* dst, long ld_d, long off_d, long W,
                             long rows, hipStream_t stream);
 hipError_t launch_add_into(bool bf16, void* a, const void* b, long n, hipStream_t stream);  // a += b (bf16 or fp32)
+// dst[r][c] = c < W_src ? src[r][c] : 0, c < W_dst (bf16 or fp32; 16-byte multiples)
+hipError_t launch_pad_cols(bool bf16, const void* src, long ld_s, long W_src, void* dst, long ld_d, long W_dst,
+                           long rows, hipStream_t stream);
+hipError_t launch_bcast_cols(const float* src, float* dst, long W, long rows, hipStream_t stream);  // dst[r][:] = src[r]
+hipError_t launch_row_sums(const float* src, long W, float* dst, long rows, hipStream_t stream);    // dst[r] = sum src[r][:]
 
 }  // namespace gla

@@ -203,9 +203,13 @@ gla_status_t gla_bwd_ckpt(const gla_shape_t* shape,
  *   dg : [B,T,H] dtype output of gla_bwd_scalar, the gradient with respect to
  *        the scalar log gate (the sum over key columns of the per-column one)
  * Every other argument, layout and convention is that of gla_fwd / gla_bwd.
- * bf16 only (fp32 inputs return GLA_ERR_UNSUPPORTED).  gla_fwd_scalar takes
- * gla_fwd_workspace_size(shape) bytes of workspace; gla_bwd_scalar takes
- * gla_bwd_scalar_workspace_size(shape) (which is 0 for fp32 or invalid shapes).
+ * bf16 or fp32.  fp32 runs the per-column path on the gate repeated over the
+ * key columns (exactly the same gate) and sums its per-column dg, so its
+ * workspace also holds the repeated gate and that dg ([B,T,H,K] fp32 each).
+ * gla_fwd_scalar takes gla_fwd_scalar_workspace_size(shape) bytes of workspace
+ * (equal to gla_fwd_workspace_size for bf16); gla_bwd_scalar takes
+ * gla_bwd_scalar_workspace_size(shape).  Both sizes are 0 for an invalid or
+ * empty shape.
  */
 gla_status_t gla_fwd_scalar(const gla_shape_t* shape,
                             const void* q, const void* k, const void* v, const void* g,
@@ -216,6 +220,7 @@ gla_status_t gla_bwd_scalar(const gla_shape_t* shape,
                             const float* s0, const void* d_o, const float* dht,
                             void* dq, void* dk, void* dv, void* dg, float* ds0,
                             void* workspace, size_t workspace_bytes, void* stream);
+size_t gla_fwd_scalar_workspace_size(const gla_shape_t* shape);
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
 
 /*

@@ -207,13 +207,22 @@ def test_wide_keys_run_as_slices(L):
 
 
 def test_scalar_gate_entry_points_validate(L):
-    s32 = _shape(T=128, dtype=gla.GLA_DTYPE_FP32)
-    assert L.gla_bwd_scalar_workspace_size(ctypes.byref(s32)) == 0
+    # fp32: the per-column path on the gate repeated over the key columns, plus
+    # the repeated gate and the per-column dg ([B,T,H,K] fp32 each)
+    s32 = _shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)
+    rows = 2 * 128 * 3
+    assert (L.gla_bwd_scalar_workspace_size(ctypes.byref(s32)) >=
+            L.gla_bwd_workspace_size(ctypes.byref(s32)) + 2 * rows * 128 * 4)
+    assert (L.gla_fwd_scalar_workspace_size(ctypes.byref(s32)) >=
+            L.gla_fwd_workspace_size(ctypes.byref(s32)) + rows * 128 * 4)
+    b16 = _shape(T=128, K=128, V=128)
+    assert L.gla_fwd_scalar_workspace_size(ctypes.byref(b16)) == L.gla_fwd_workspace_size(ctypes.byref(b16))
+    assert L.gla_fwd_scalar_workspace_size(ctypes.byref(_shape(T=100))) == 0
     s16 = _shape(T=128, K=128, V=256)
     assert L.gla_bwd_scalar_workspace_size(ctypes.byref(s16)) >= L.gla_bwd_workspace_size(ctypes.byref(s16))
     fwd = lambda shape, **kw: L.gla_fwd_scalar(ctypes.byref(shape), P, P, P, kw.get("g", P), None, P, None,
                                                kw.get("ws", P), 1 << 30, None)
-    assert fwd(s32) == ERR_UNSUPPORTED
+    assert fwd(s32, ws=None) == ERR_WORKSPACE
     assert fwd(_shape(T=100)) == ERR_SHAPE
     assert fwd(_shape(T=128), g=None) == ERR_NULL
     assert fwd(_shape(T=128), g=ctypes.c_void_p(0x10002)) == ERR_ALIGN
@@ -221,19 +230,22 @@ def test_scalar_gate_entry_points_validate(L):
 
 
 def test_general_gate_entry_point_validates(L):
-    # bf16 with K in {128, 256} only; one record per chunk and head holding the
-    # key side (Ql, Kt^T and gate factors) and the value side (three [64, V]
-    # tiles and the column decays)
+    # bf16; the kernels take K in {128, 256} (K = 64 padded to 128, K = 512 as
+    # two key slices); one record per chunk and head holding the key side (Ql,
+    # Kt^T and gate factors) and the value side (three [64, V] tiles and the
+    # column decays)
     ws = lambda shape: L.gla_fwd_general_workspace_size(ctypes.byref(shape))
     assert ws(_shape(T=128, dtype=gla.GLA_DTYPE_FP32)) == 0
-    assert ws(_shape(T=128, K=64, V=64)) == 0
+    assert ws(_shape(T=128, K=64, V=64)) > ws(_shape(T=128, K=128, V=64)) > 0
+    assert ws(_shape(T=128, K=96, V=64)) == 0
     assert ws(_shape(T=100, K=128)) == 0
     s = _shape(B=2, H=4, T=8192, K=256, V=512)
     assert ws(s) == ws(s) and ws(s) >= 2 * 4 * 128 * (2 * 2 * 64 * 256 + 3 * 2 * 64 * 512)
     fwd = lambda shape, **kw: L.gla_fwd_general(ctypes.byref(shape), P, P, P, P, kw.get("h", P), None, P, None,
                                                 kw.get("ws", P), 1 << 40, None)
     assert fwd(_shape(T=128, K=128, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
-    assert fwd(_shape(T=128, K=64, V=64)) == ERR_UNSUPPORTED
+    assert fwd(_shape(T=128, K=1024, V=64)) == ERR_UNSUPPORTED
+    assert fwd(_shape(T=128, K=64, V=64), ws=None) == ERR_WORKSPACE
     assert fwd(_shape(T=100, K=128)) == ERR_SHAPE
     assert fwd(_shape(T=128, K=128), h=None) == ERR_NULL
     assert fwd(_shape(T=128, K=128), h=ctypes.c_void_p(0x10002)) == ERR_ALIGN
@@ -244,8 +256,10 @@ def test_general_gate_entry_point_validates(L):
 def test_general_gate_backward_validates(L):
     ws = lambda shape: L.gla_bwd_general_workspace_size(ctypes.byref(shape))
     assert ws(_shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)) == 0
-    assert ws(_shape(T=128, K=64, V=128)) == 0
-    assert ws(_shape(T=128, K=128, V=64)) == 0
+    # K or V = 64: padded to 128 with zero columns
+    assert ws(_shape(T=128, K=64, V=128)) > ws(_shape(T=128, K=128, V=128)) > 0
+    assert ws(_shape(T=128, K=128, V=64)) > ws(_shape(T=128, K=128, V=128))
+    assert ws(_shape(T=128, K=64, V=64)) > 0
     # V = 512 as two value slices, K = 512 as two key slices, around the K, V <= 256 backward
     sub = ws(_shape(T=128, K=128, V=256))
     assert ws(_shape(T=128, K=128, V=512)) > sub > 0
@@ -256,7 +270,8 @@ def test_general_gate_backward_validates(L):
     bwd = lambda shape, **kw: L.gla_bwd_general(ctypes.byref(shape), P, P, P, P, kw.get("h", P), None, P, None,
                                                 P, P, P, P, kw.get("dh", P), None, kw.get("ws", P), 1 << 40, None)
     assert bwd(_shape(T=128, K=128, V=128, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
-    assert bwd(_shape(T=128, K=256, V=64)) == ERR_UNSUPPORTED
+    assert bwd(_shape(T=128, K=256, V=1024)) == ERR_UNSUPPORTED
+    assert bwd(_shape(T=128, K=64, V=64), ws=None) == ERR_WORKSPACE
     assert bwd(_shape(T=100, K=128, V=128)) == ERR_SHAPE
     assert bwd(_shape(T=128, K=128, V=128), h=None) == ERR_NULL
     assert bwd(_shape(T=128, K=128, V=128), dh=None) == ERR_NULL

@@ -54,6 +54,10 @@ def test_bwd_general_heads(B, H, T, K, V, s0):
     (1, 2, 64 * 5, 512, 128, "normal0.1"),   # two key slices: dv, dh added
     (1, 2, 64 * 6, 128, 512, "normal0.1"),   # two value slices: dq, dk, dg added
     (1, 2, 64 * 3, 512, 512, "none"),        # both
+    (1, 2, 64 * 7, 64, 128, "normal0.1"),    # K = 64 padded with zero key columns
+    (2, 1, 64 * 5, 256, 64, "normal0.1"),    # V = 64 padded with zero value columns
+    (1, 2, 64 * 4, 64, 64, "none"),          # both padded
+    (1, 2, 64 * 3, 64, 512, "normal0.1"),    # padded keys, sliced values
 ])
 def test_bwd_general_wide_heads(B, H, T, K, V, s0):
     w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0=s0, backward=True, seed=1520 + T + K + V)

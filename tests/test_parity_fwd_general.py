@@ -56,10 +56,12 @@ def test_fwd_general_heads(B, H, T, K, V, s0):
     _check(w, gi.make_inputs(w), h, _heads(B, H))
 
 
-@pytest.mark.parametrize("B,H,T,K,V", [(1, 2, 64 * 5, 512, 128), (2, 2, 64 * 3, 512, 512)])
+@pytest.mark.parametrize("B,H,T,K,V", [(1, 2, 64 * 5, 512, 128), (2, 2, 64 * 3, 512, 512), (1, 2, 64 * 7, 64, 64),
+                                       (2, 2, 64 * 4, 64, 256)])
 def test_fwd_general_wide_keys(B, H, T, K, V):
     # dk = 512: two key slices of 256 sharing v and the value-side gate; o adds
-    # the slices' outputs, S_T stacks their row blocks
+    # the slices' outputs, S_T stacks their row blocks.  dk = 64: padded to 128
+    # with zero columns of q, k and g (the padded state rows stay zero)
     w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=False, seed=1250 + T + V)
     h = gi.make_value_gate(B, T, H, V, seed=1350 + T + V)
     _check(w, gi.make_inputs(w), h, _heads(B, H))

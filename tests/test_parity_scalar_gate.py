@@ -33,8 +33,8 @@ def _gpu(x, heads, state=False):
     return np.stack([x[b, :, h, :] for b, h in heads])
 
 
-def _inputs(B, H, T, K, V, s0, seed, gate_fn=None):
-    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="scalar", s0=s0, backward=True, seed=seed)
+def _inputs(B, H, T, K, V, s0, seed, gate_fn=None, dtype="bf16"):
+    w = gi.custom(B, H, T, K, V, dtype=dtype, gate="scalar", s0=s0, backward=True, seed=seed)
     inp = gi.make_inputs(w, dht=True)
     if gate_fn is not None:
         inp["g"] = gate_fn(inp["g"])
@@ -64,7 +64,7 @@ def _check(w, inp, heads=None, backward=True, with_dht=True):
             errs[name] = rel_l2(_gpu(x, heads), r[:, :, 0, :])
         errs["dg"] = rel_l2(_gpu(dg, heads), ref[3][:, :, 0])
         errs["dS0"] = rel_l2(_gpu(ds0, heads, True), ref[4][:, 0])
-    tol = TOL[torch.bfloat16]
+    tol = TOL[w.torch_dtype]
     note("  rel-L2 " + " ".join("%s=%.3e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
@@ -121,8 +121,9 @@ def test_scalar_gate_metric_size():
     _check(w, inp, heads=[(0, 1), (1, 3)], with_dht=False)
 
 
-def test_scalar_gate_rejects_fp32():
-    q = torch.zeros(1, 64, 1, 64, device=DEV)
-    g = torch.zeros(1, 64, 1, device=DEV)
-    with pytest.raises(gla.GlaError):
-        gla.gla_fwd_scalar(q, q, q, g)
+@pytest.mark.parametrize("B,H,T,K,V", [(1, 2, 320, 64, 64), (2, 1, 192, 128, 128), (1, 2, 256, 256, 256)])
+def test_scalar_gate_fp32(B, H, T, K, V):
+    # fp32: the per-column path on the gate repeated over the key columns, dg
+    # summed over them (K = 256 and V = 256 as slices of 128)
+    w, inp = _inputs(B, H, T, K, V, "normal0.1", seed=790 + T + K + V, dtype="fp32")
+    _check(w, inp)
