@@ -310,8 +310,14 @@ __device__ __attribute__((noinline)) void exact_intra_tile(float* Af, int pF, co
 constexpr int kCombineVec = 4;  // elements per thread
 template <typename ST> using combine_vec_t = ST __attribute__((ext_vector_type(kCombineVec)));
 
-template <bool REV, typename ST>
-__device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, long K, int P, const float* init) {
+//
+// CKO (forward only): every output S_init(p) with p > 0 and p % ck_r == 0 is
+// stored to ck[(p / ck_r) * KV] instead of st[p * KV] (a checkpoint of the
+// states at every ck_r-th segment start, read from there by the walk).
+template <bool REV, typename ST, bool CKO = false>
+__device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, long K, int P, const float* init,
+                                            ST* ck = nullptr, int ck_r = 1) {
+    static_assert(!(CKO && REV), "the checkpoint is written by the forward combine");
     constexpr int CE = kCombineVec;
     constexpr int CU = 32;
     using VT = combine_vec_t<ST>;
@@ -335,6 +341,8 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
             gm[u] = feeds ? exp2_fast(gm[u]) : 0.f;
             if (!feeds) a[u] = VT{};
         }
+        // CKO: segment b0 + u is checkpoint entry m when rem == 0 (one division per block)
+        int m = CKO ? b0 / ck_r : 0, rem = CKO ? b0 % ck_r : 0;
 #pragma unroll
         for (int u = 0; u < CU; ++u) {
             const int p = REV ? P - 1 - (b0 + u) : b0 + u;
@@ -342,7 +350,12 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
                 VT o;
 #pragma unroll
                 for (int c = 0; c < CE; ++c) o[c] = Elem<ST>::from_f(cur[c]);
-                *reinterpret_cast<VT*>(st + p * KV) = o;
+                ST* dst = st + p * KV;
+                if constexpr (CKO) {
+                    if (p > 0 && rem == 0) dst = ck + (long)m * KV;
+                    if (++rem == ck_r) rem = 0, ++m;
+                }
+                *reinterpret_cast<VT*>(dst) = o;
 #pragma unroll
                 for (int c = 0; c < CE; ++c) cur[c] = gm[u] * cur[c] + Elem<ST>::to_f(a[u][c]);
             }
@@ -358,9 +371,10 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
 // adds it, decayed by its gate product, to each of its outputs.  Both parts of
 // a slot must be in the same workgroup; every thread must call this (barrier).
 constexpr int kSplitMax = 16;
-template <bool REV, typename ST>
+template <bool REV, typename ST, bool CKO = false>
 __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long KV, long K, int P, const float* init,
-                                                  int part, f32x4* carry) {
+                                                  int part, f32x4* carry, ST* ck = nullptr, int ck_r = 1) {
+    static_assert(!(CKO && REV), "the checkpoint is written by the forward combine");
     constexpr int CE = kCombineVec;
     using VT = combine_vec_t<ST>;
     const int h = (P + 1) / 2;
@@ -394,6 +408,7 @@ __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long 
     if (part == 0) *carry = fin;
     __syncthreads();
     const f32x4 cin = part ? *carry : f32x4{0.f, 0.f, 0.f, 0.f};
+    int ckm = CKO ? j0 / ck_r : 0, rem = CKO ? j0 % ck_r : 0;  // as in combine_row (CKO: REV is false)
 #pragma unroll
     for (int u = 0; u < kSplitMax; ++u) {
         if (u < n) {
@@ -402,7 +417,12 @@ __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long 
             VT o;
 #pragma unroll
             for (int c = 0; c < CE; ++c) o[c] = Elem<ST>::from_f(loc[u][c] + mul[u] * cin[c]);
-            *reinterpret_cast<VT*>(st + p * KV) = o;
+            ST* dst = st + p * KV;
+            if constexpr (CKO) {
+                if (p > 0 && rem == 0) dst = ck + (long)ckm * KV;
+                if (++rem == ck_r) rem = 0, ++ckm;
+            }
+            *reinterpret_cast<VT*>(dst) = o;
         }
     }
 }

@@ -27,35 +27,39 @@ namespace gla {
 // Step 2 (forward): S_init(0) = S_0 (or 0); S_init(p+1) = Diag(exp2 G_p) S_init(p) + S*_p.
 // ws_state[p] holds S*_p on entry and S_init(p) on exit.  One thread per
 // kCombineVec adjacent elements of a state row (V is a multiple of 64).
-template <typename ST>
+// CKO: S_init(p) for p = m * ck_r (m >= 1) goes to ck[bh][m] ([BH][ck_P][K][V])
+// instead of ws_state[p]: the starting states of a backward whose segments are
+// ck_r forward segments long, which the walk then reads from there.
+template <typename ST, bool CKO = false>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_fwd(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
-                    int K, int V, int P) {
+                    int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1) {
     const long KV = (long)K * V;
     const long e = ((long)blockIdx.x * 256 + threadIdx.x) * kCombineVec;
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
-    combine_row<false>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
-                       s0 ? s0 + bh * KV + e : nullptr);
+    combine_row<false, ST, CKO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                                s0 ? s0 + bh * KV + e : nullptr, CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r);
 }
 
 // The same with each element group's segments split between two threads
 // (P <= 2 * kSplitMax): threads t and t + 128 of a workgroup share 4 elements.
 // The grid covers K*V exactly (K*V / (128 * kCombineVec) workgroups per head):
 // no thread may leave before the exchange barrier.
-template <typename ST>
+template <typename ST, bool CKO = false>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_fwd_split(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
-                          int K, int V, int P) {
+                          int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1) {
     __shared__ f32x4 carry[128];
     const long KV = (long)K * V;
     const int slot = threadIdx.x & 127, part = threadIdx.x >> 7;
     const long e = ((long)blockIdx.x * 128 + slot) * kCombineVec;
     const long bh = blockIdx.y;
     const int i = (int)(e / V);
-    combine_row_split<false>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
-                             s0 ? s0 + bh * KV + e : nullptr, part, &carry[slot]);
+    combine_row_split<false, ST, CKO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                                      s0 ? s0 + bh * KV + e : nullptr, part, &carry[slot],
+                                      CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r);
 }
 
 // Copy (or zero) a [BH][K][V] fp32 state: final state of an empty sequence.
@@ -350,7 +354,9 @@ gla_fwd_walk(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 // multiple of ck_len (and c + 1 < N), the state before chunk c + 1 is also
 // written to ck[bh][(c + 1) / ck_len] ([BH][ck_P][K][V], input dtype): the
 // segment-start states of a backward whose segments are ck_len chunks long.
-template <typename T, int KD, int BV, int NW, bool SG = false, bool CK = false>
+// CKI (the combine wrote that checkpoint): segments seg with seg % ck_len == 0
+// (ck_len counted in segments here) start from ck[bh][seg / ck_len].
+template <typename T, int KD, int BV, int NW, bool SG = false, bool CK = false, bool CKI = false>
 __global__ void __launch_bounds__(NW * 64)
 gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const T* __restrict__ ws_init, const float* __restrict__ s0,
@@ -385,9 +391,17 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     // segment 0 starts from the caller's fp32 S_0, later ones from the combined
     // segment states ([BH][P][K][V], input dtype)
     StateRegs<KD, CB> S;
-    if (seg > 0) S.load(ws_init + ((long)bh * P + seg) * KD * V, V, col0);
-    else if (s0) S.load(s0 + (long)bh * KD * V, V, col0);
-    else S.zero();
+    if (seg > 0) {
+        const T* st = ws_init + ((long)bh * P + seg) * KD * V;
+        if constexpr (CKI) {
+            if (seg % ck_len == 0) st = ck + ((long)bh * ck_P + seg / ck_len) * KD * V;
+        }
+        S.load(st, V, col0);
+    } else if (s0) {
+        S.load(s0 + (long)bh * KD * V, V, col0);
+    } else {
+        S.zero();
+    }
 
     RowSlab<T, CPK> rq, rk;
     GateSlab<T, CPK, SG> rg;
@@ -596,17 +610,29 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
 // ---------------------------------------------------------------------------
 // Host launchers.
+// ck_out: the combine writes every a.ck_len / a.seg_len-th segment start into
+// the checkpoint a.ckpt instead of the workspace (the caller checks that this
+// ratio is whole), so the walk stores none and reads those from there.
 template <typename T>
-void launch_combine_fwd(const FwdLaunch& a, int KD) {
+void launch_combine_fwd(const FwdLaunch& a, int KD, bool ck_out) {
     const long KV = (long)KD * a.V;
+    const int r = ck_out ? a.ck_len / a.seg_len : 1;
     if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
         dim3 g2((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH);
-        GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd_split<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
-                   a.ws_gate, KD, a.V, a.P);
+        if (ck_out)
+            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<T, true>), g2, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P);
+        else
+            GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd_split<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
+                       a.ws_gate, KD, a.V, a.P);
     } else {
         dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
-        GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
-                   a.ws_gate, KD, a.V, a.P);
+        if (ck_out)
+            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd<T, true>), g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
+                       a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P);
+        else
+            GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
+                       a.ws_gate, KD, a.V, a.P);
     }
 }
 
@@ -617,6 +643,8 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
     const int nvb = a.V / BV;
     const long KV = (long)KD * a.V;
+    // a checkpoint whose states are all segment starts comes from the combine
+    const bool ck_comb = sizeof(T) == 2 && a.ckpt && a.P > 1 && a.ck_len % a.seg_len == 0;
     if (a.P > 1) {
         // segments 0..P-2 feed the combine; the last segment's S* is never needed
         const int nseg = a.P - 1;
@@ -624,19 +652,26 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
         GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false, SG>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.g, (const T*)a.v, (T*)a.ws_state, a.ws_gate,
                            a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg, (int)a.BH);
-        launch_combine_fwd<T>(a, KD);
+        launch_combine_fwd<T>(a, KD, ck_comb);
     }
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
         if (a.ckpt) {
-            if constexpr (!SG)
-                GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, true>), grid, dim3(NT), a.stream,
-                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
-                           (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
-                           a.ck_len, a.ck_P);
-            else
+            if constexpr (!SG) {
+                if (ck_comb)
+                    GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, false, true>), grid, dim3(NT),
+                               a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                               (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len,
+                               (int)a.BH, (T*)a.ckpt, a.ck_len / a.seg_len, a.ck_P);
+                else
+                    GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, true>), grid, dim3(NT), a.stream,
+                               (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
+                               (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
+                               a.ck_len, a.ck_P);
+            } else {
                 return hipErrorInvalidValue;
+            }
         } else {
             GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG>), grid, dim3(NT), a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
@@ -667,7 +702,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     return launch_fwd_sg<T, KD, BV, false>(a);
 }
 
-template void launch_combine_fwd<bf16>(const FwdLaunch& a, int KD);
+template void launch_combine_fwd<bf16>(const FwdLaunch& a, int KD, bool ck_out);
 
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
