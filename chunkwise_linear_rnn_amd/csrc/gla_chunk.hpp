@@ -314,10 +314,12 @@ template <typename ST> using combine_vec_t = ST __attribute__((ext_vector_type(k
 // CKO (forward only): every output S_init(p) with p > 0 and p % ck_r == 0 is
 // stored to ck[(p / ck_r) * KV] instead of st[p * KV] (a checkpoint of the
 // states at every ck_r-th segment start, read from there by the walk).
-template <bool REV, typename ST, bool CKO = false>
+// STO (forward only): the last segment's S* is present too, and the state
+// after it, S_T = Diag(exp2 G_{P-1}) S_init(P-1) + S*_{P-1}, goes to sT (fp32).
+template <bool REV, typename ST, bool CKO = false, bool STO = false>
 __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, long K, int P, const float* init,
-                                            ST* ck = nullptr, int ck_r = 1) {
-    static_assert(!(CKO && REV), "the checkpoint is written by the forward combine");
+                                            ST* ck = nullptr, int ck_r = 1, float* sT = nullptr) {
+    static_assert(!((CKO || STO) && REV), "the checkpoint and S_T are written by the forward combine");
     constexpr int CE = kCombineVec;
     constexpr int CU = 32;
     using VT = combine_vec_t<ST>;
@@ -337,7 +339,7 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
 #pragma unroll
         for (int u = 0; u < CU; ++u) {
             const int p = REV ? P - 1 - (b0 + u) : b0 + u;
-            const bool feeds = b0 + u < P && (REV ? p >= 1 : p + 1 < P);
+            const bool feeds = b0 + u < P && (REV ? p >= 1 : (STO || p + 1 < P));
             gm[u] = feeds ? exp2_fast(gm[u]) : 0.f;
             if (!feeds) a[u] = VT{};
         }
@@ -361,6 +363,7 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
             }
         }
     }
+    if constexpr (STO) *reinterpret_cast<f32x4*>(sT) = cur;
 }
 
 // The same recurrence split between two threads, for P <= 2 * kSplitMax: part
@@ -371,10 +374,11 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
 // adds it, decayed by its gate product, to each of its outputs.  Both parts of
 // a slot must be in the same workgroup; every thread must call this (barrier).
 constexpr int kSplitMax = 16;
-template <bool REV, typename ST, bool CKO = false>
+template <bool REV, typename ST, bool CKO = false, bool STO = false>
 __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long KV, long K, int P, const float* init,
-                                                  int part, f32x4* carry, ST* ck = nullptr, int ck_r = 1) {
-    static_assert(!(CKO && REV), "the checkpoint is written by the forward combine");
+                                                  int part, f32x4* carry, ST* ck = nullptr, int ck_r = 1,
+                                                  float* sT = nullptr) {
+    static_assert(!((CKO || STO) && REV), "the checkpoint and S_T are written by the forward combine");
     constexpr int CE = kCombineVec;
     using VT = combine_vec_t<ST>;
     const int h = (P + 1) / 2;
@@ -391,12 +395,12 @@ __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long 
     f32x4 cur = (part == 0 && init) ? *reinterpret_cast<const f32x4*>(init) : f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 loc[kSplitMax], fin = cur;
     float mul[kSplitMax];
-    float m = 1.f;
+    float m = 1.f, mfin = 1.f;
 #pragma unroll
     for (int u = 0; u < kSplitMax; ++u) {
         const int j = j0 + u;
         const int p = REV ? P - 1 - j : j;
-        const bool feeds = u < n && (REV ? p >= 1 : p + 1 < P);
+        const bool feeds = u < n && (REV ? p >= 1 : (STO || p + 1 < P));
         const float gu = feeds ? exp2_fast(gm[u]) : 0.f;
         loc[u] = cur;
         mul[u] = m;
@@ -404,6 +408,7 @@ __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long 
         for (int c = 0; c < CE; ++c) cur[c] = gu * cur[c] + (feeds ? Elem<ST>::to_f(a[u][c]) : 0.f);
         m *= gu;
         fin = (u == n - 1) ? cur : fin;
+        if constexpr (STO) mfin = (u == n - 1) ? m : mfin;
     }
     if (part == 0) *carry = fin;
     __syncthreads();
@@ -423,6 +428,15 @@ __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long 
                 if (++rem == ck_r) rem = 0, ++ckm;
             }
             *reinterpret_cast<VT*>(dst) = o;
+        }
+    }
+    // S_T: part 1 holds the last segment (P >= 2); its chain from zero plus part 0's carry
+    if constexpr (STO) {
+        if (part == 1) {
+            f32x4 t;
+#pragma unroll
+            for (int c = 0; c < CE; ++c) t[c] = fin[c] + mfin * cin[c];
+            *reinterpret_cast<f32x4*>(sT) = t;
         }
     }
 }

@@ -30,36 +30,42 @@ namespace gla {
 // CKO: S_init(p) for p = m * ck_r (m >= 1) goes to ck[bh][m] ([BH][ck_P][K][V])
 // instead of ws_state[p]: the starting states of a backward whose segments are
 // ck_r forward segments long, which the walk then reads from there.
-template <typename ST, bool CKO = false>
+// STO: ws_state also holds the last segment's S*, and the final state S_T goes
+// to s_final ([BH][K][V] fp32), so the walk need not store it.
+template <typename ST, bool CKO = false, bool STO = false>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_fwd(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
-                    int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1) {
+                    int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1,
+                    float* __restrict__ s_final = nullptr) {
     const long KV = (long)K * V;
     const long e = ((long)blockIdx.x * 256 + threadIdx.x) * kCombineVec;
     const long bh = blockIdx.y;
     if (e >= KV) return;
     const int i = (int)(e / V);
-    combine_row<false, ST, CKO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
-                                s0 ? s0 + bh * KV + e : nullptr, CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r);
+    combine_row<false, ST, CKO, STO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                                     s0 ? s0 + bh * KV + e : nullptr, CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r,
+                                     STO ? s_final + bh * KV + e : nullptr);
 }
 
 // The same with each element group's segments split between two threads
 // (P <= 2 * kSplitMax): threads t and t + 128 of a workgroup share 4 elements.
 // The grid covers K*V exactly (K*V / (128 * kCombineVec) workgroups per head):
 // no thread may leave before the exchange barrier.
-template <typename ST, bool CKO = false>
+template <typename ST, bool CKO = false, bool STO = false>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_fwd_split(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
-                          int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1) {
+                          int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1,
+                          float* __restrict__ s_final = nullptr) {
     __shared__ f32x4 carry[128];
     const long KV = (long)K * V;
     const int slot = threadIdx.x & 127, part = threadIdx.x >> 7;
     const long e = ((long)blockIdx.x * 128 + slot) * kCombineVec;
     const long bh = blockIdx.y;
     const int i = (int)(e / V);
-    combine_row_split<false, ST, CKO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
-                                      s0 ? s0 + bh * KV + e : nullptr, part, &carry[slot],
-                                      CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r);
+    combine_row_split<false, ST, CKO, STO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+                                           s0 ? s0 + bh * KV + e : nullptr, part, &carry[slot],
+                                           CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r,
+                                           STO ? s_final + bh * KV + e : nullptr);
 }
 
 // Copy (or zero) a [BH][K][V] fp32 state: final state of an empty sequence.
@@ -613,27 +619,28 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 // ck_out: the combine writes every a.ck_len / a.seg_len-th segment start into
 // the checkpoint a.ckpt instead of the workspace (the caller checks that this
 // ratio is whole), so the walk stores none and reads those from there.
-template <typename T>
-void launch_combine_fwd(const FwdLaunch& a, int KD, bool ck_out) {
+// st_out: the segment pass has formed every segment's S*, and the combine
+// writes S_T to a.s_final (the walk's last segments then store nothing).
+template <typename T, bool CKO, bool STO>
+static void launch_combine_fwd_v(const FwdLaunch& a, int KD) {
     const long KV = (long)KD * a.V;
-    const int r = ck_out ? a.ck_len / a.seg_len : 1;
+    const int r = CKO ? a.ck_len / a.seg_len : 1;
     if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
         dim3 g2((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH);
-        if (ck_out)
-            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<T, true>), g2, dim3(256), a.stream, a.s0,
-                       (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P);
-        else
-            GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd_split<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
-                       a.ws_gate, KD, a.V, a.P);
+        GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
+                   (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P, a.s_final);
     } else {
         dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
-        if (ck_out)
-            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd<T, true>), g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
-                       a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P);
-        else
-            GLA_LAUNCH("combine_fwd", gla_seg_combine_fwd<T>, g2, dim3(256), a.stream, a.s0, (T*)a.ws_state,
-                       a.ws_gate, KD, a.V, a.P);
+        GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd<T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
+                   (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P, a.s_final);
     }
+}
+template <typename T>
+void launch_combine_fwd(const FwdLaunch& a, int KD, bool ck_out, bool st_out) {
+    if (ck_out && st_out) launch_combine_fwd_v<T, true, true>(a, KD);
+    else if (ck_out) launch_combine_fwd_v<T, true, false>(a, KD);
+    else if (st_out) launch_combine_fwd_v<T, false, true>(a, KD);
+    else launch_combine_fwd_v<T, false, false>(a, KD);
 }
 
 template <typename T, int KD, int BV, bool SG>
@@ -643,17 +650,22 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
     static_assert(sizeof(ChunkSmem<T, KD, BV, NT>) <= 160 * 1024, "LDS budget");
     const int nvb = a.V / BV;
     const long KV = (long)KD * a.V;
-    // a checkpoint whose states are all segment starts comes from the combine
+    // a checkpoint whose states are all segment starts comes from the combine;
+    // so does S_T (16-bit inputs): the segment pass then also forms the last
+    // segment's S* (its workgroups fill CUs that would otherwise stay idle),
+    // and the walk's last segments need not store S_T at their end
     const bool ck_comb = sizeof(T) == 2 && a.ckpt && a.P > 1 && a.ck_len % a.seg_len == 0;
+    const bool st_comb = sizeof(T) == 2 && a.s_final && a.P > 1;
     if (a.P > 1) {
-        // segments 0..P-2 feed the combine; the last segment's S* is never needed
-        const int nseg = a.P - 1;
+        // segments 0..P-2 feed the combine, and the last one too for S_T
+        const int nseg = st_comb ? a.P : a.P - 1;
         dim3 grid((unsigned)xcd_grid(nseg * a.BH, nvb));
         GLA_LAUNCH("fwd_seg_state", (gla_seg_state<T, KD, BV, NW, false, SG>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.g, (const T*)a.v, (T*)a.ws_state, a.ws_gate,
                            a.T, a.H, a.V, a.N, a.P, a.seg_len, 0, nseg, (int)a.BH);
-        launch_combine_fwd<T>(a, KD, ck_comb);
+        launch_combine_fwd<T>(a, KD, ck_comb, st_comb);
     }
+    float* walk_sfinal = st_comb ? nullptr : a.s_final;
     dim3 grid((unsigned)xcd_grid(a.P * a.BH, nvb));
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
@@ -662,12 +674,12 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
                 if (ck_comb)
                     GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, false, true>), grid, dim3(NT),
                                a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                               (const T*)a.ws_state, a.s0, (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len,
+                               (const T*)a.ws_state, a.s0, (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len,
                                (int)a.BH, (T*)a.ckpt, a.ck_len / a.seg_len, a.ck_P);
                 else
                     GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, true>), grid, dim3(NT), a.stream,
                                (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
-                               (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
+                               (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
                                a.ck_len, a.ck_P);
             } else {
                 return hipErrorInvalidValue;
@@ -675,7 +687,7 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
         } else {
             GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG>), grid, dim3(NT), a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
-                       (T*)a.o, a.s_final, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
+                       (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH);
         }
     } else {
         static_assert(!SG, "scalar gates take the 16-bit path");
@@ -702,7 +714,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a) {
     return launch_fwd_sg<T, KD, BV, false>(a);
 }
 
-template void launch_combine_fwd<bf16>(const FwdLaunch& a, int KD, bool ck_out);
+template void launch_combine_fwd<bf16>(const FwdLaunch& a, int KD, bool ck_out, bool st_out);
 
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;

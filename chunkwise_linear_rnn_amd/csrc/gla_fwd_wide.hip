@@ -14,7 +14,7 @@
 namespace gla {
 
 template <typename T>
-void launch_combine_fwd(const FwdLaunch& a, int KD, bool ck_out);  // gla_fwd.hip
+void launch_combine_fwd(const FwdLaunch& a, int KD, bool ck_out, bool st_out);  // gla_fwd.hip
 
 // Wide heads (16-bit, dk = 256): chunk records, then the state pass over
 // segments 0..P-2, the combine, and the output walk over every segment.
@@ -34,7 +34,7 @@ static hipError_t launch_fwd_wide_bv(const FwdLaunch& a) {
                    dim3(512), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)nullptr,
                    (const float*)nullptr, (T*)nullptr, (float*)nullptr, (T*)a.ws_state, a.ws_gate, a.T, a.H, a.V,
                    a.N, a.P, a.seg_len, nseg, (int)a.BH);
-        launch_combine_fwd<T>(a, KD, false);
+        launch_combine_fwd<T>(a, KD, false, false);
     }
     GLA_LAUNCH("fwd_walk", (gla_fwd_wide_walk<T, KD, BV, true>), dim3((unsigned)xcd_grid(a.P * a.BH, nvb)),
                dim3(512), a.stream, (const unsigned char*)rec, (const T*)a.v, (const T*)a.ws_state, a.s0, (T*)a.o,
