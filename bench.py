@@ -40,7 +40,7 @@ METRIC_SCALAR = "GLA scalar-gate fwd+bwd tokens/sec at T=8K, dk=128, dv=256"
 
 
 def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd: int, dv_split: bool = False,
-                             G: int = None, ckpt: bool = False, T: int = 0):
+                             G: int = None, ckpt: bool = False, T: int = 0, final_state: bool = True):
     """Algorithmic HBM bytes per (token, head) of one launch of `kernel`.
 
     G is the number of log-gate values per token and head (K for per-column
@@ -50,9 +50,11 @@ def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd:
     segment's midpoint state); with a checkpoint (ckpt) it runs only that
     backward direction, and with a checkpoint, 16-bit per-column gates and the
     dv walk in halves (`fused`) the dq walk forms it: it then also reads q and
-    writes the 2 P_bwd half-segment states of K x V per head (T tokens)."""
+    writes the 2 P_bwd half-segment states of K x V per head (T tokens).  The
+    forward's segment pass skips the last segment unless the final state is
+    asked for (16-bit inputs: the combine then forms S_T from every segment)."""
     G = K if G is None else G
-    seg_frac = (P - 1) / P if P > 1 else 0.0
+    seg_frac = (1.0 if final_state and e == 2 else (P - 1) / P) if P > 1 else 0.0
     seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
     fused = ckpt and dv_split and e == 2 and G == K and T > 0
     table = {
@@ -61,7 +63,7 @@ def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd:
         "bwd_dq_walk": e * (2 * K + G + 2 * V) + (e * K + 2 * P_bwd * K * V * e / T if fused else 0),
         "bwd_dk_walk": e * (4 * K + 2 * G + 2 * V),     # q, k, g, dq, v, d_o read; dk, dg written
         "bwd_dv_walk": e * (2 * K + G + 2 * V),         # q, k, g, d_o read; dv written
-        "fwd_seg_state": e * (K + G + V) * seg_frac,    # k, g, v of all but the last segment
+        "fwd_seg_state": e * (K + G + V) * seg_frac,    # k, g, v of the segments (above)
         # k, g, v of all but the last segment and q, g, d_o of all but the first (or all)
         "bwd_seg_states": None if fused else
         e * (K + G + V) * ((0.0 if ckpt else seg_frac_bwd) + (1.0 if dv_split else seg_frac_bwd)),
@@ -198,6 +200,49 @@ def _demangle(names):
     return list(names)
 
 
+def _cxa_demangle(name: str):
+    """libstdc++'s own demangling of `name` (what rocprofv3 prints), or None."""
+    import ctypes
+    try:
+        lib = ctypes.CDLL("libstdc++.so.6")
+        f = lib.__cxa_demangle
+        f.restype = ctypes.c_void_p
+        f.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+        st = ctypes.c_int()
+        r = f(name.encode(), None, None, ctypes.byref(st))
+        return ctypes.cast(r, ctypes.c_char_p).value.decode() if r else None
+    except (OSError, AttributeError):
+        return None
+
+
+def _resolve_names(names, lib_path=None):
+    """{name: display name}.  rocprofv3 writes most kernel names mangled, but
+    demangles some itself, and libstdc++ misreads a bfloat16 template argument
+    followed by a literal 1 (an `_Accum` type appears).  Such a name is mapped
+    back to the library's kernel symbol whose libstdc++ demangling it is (the
+    kernels' host-side launch stubs carry the same mangled names)."""
+    import subprocess
+    dem = dict(zip(names, _demangle(names)))
+    bad = [n for n in names if "_Accum" in n]
+    if not bad:
+        return dem
+    lib_path = lib_path or os.path.join(ROOT, "chunkwise_linear_rnn_amd", "libgla.so")
+    try:
+        out = subprocess.run(["nm", lib_path], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return dem
+    syms = sorted(set(t.split()[-1] for t in out.splitlines() if "_ZN3gla" in t))
+    back = {}
+    for m in syms:
+        d = _cxa_demangle(m)
+        if d and "_Accum" in d:
+            back[d] = m
+    hits = [n for n in bad if n in back]
+    for n, d in zip(hits, _demangle([back[n] for n in hits])):
+        dem[n] = d
+    return dem
+
+
 def _short(demangled: str) -> str:
     """'void gla::f<a, b>(args)' -> 'f<a,b>'."""
     s = demangled
@@ -211,7 +256,8 @@ def summarize_trace(csv_path, out_md, title, command):
     """Markdown table from a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
     import csv
     rows = [r for r in csv.DictReader(open(csv_path)) if _is_lib(r["Name"])]  # the library's kernels
-    names = _demangle([r["Name"] for r in rows])
+    dem = _resolve_names([r["Name"] for r in rows])
+    names = [dem[r["Name"]] for r in rows]
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     lines = ["# Kernel times: %s (MI355X, rocprofv3 kernel trace)" % title, "",
              "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "",
@@ -301,7 +347,7 @@ def summarize_pmc(csv_path, trace_csv, out_md, title, command):
     means = {n: m for n, m in _per_kernel_means(_counter_rows(csv_path)).items() if _is_lib(n)}
     dur = {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(trace_csv))}
     names = list(means)
-    dem = dict(zip(names, _demangle(names)))
+    dem = _resolve_names(names)
     lines = ["# MFMA and LDS counters: %s (MI355X, rocprofv3 --pmc)" % title, "",
              "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "", "    " + command, "",
              "Durations from the kernel trace of the same workload (`%s`)." % os.path.basename(trace_csv),
@@ -337,7 +383,7 @@ def summarize_stalls(csv_path, out_md, title, command):
         for k, v in d.items():
             a[k] = a.get(k, 0.0) + v
     names = list(acc)
-    dem = dict(zip(names, _demangle(names)))
+    dem = _resolve_names(names)
     lines = ["# Wave stalls and LDS use: %s (MI355X, rocprofv3 --pmc)" % title, "",
              "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "", "    " + command, "",
              "wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles); wait on LDS = SQ_WAIT_INST_LDS / "
