@@ -44,9 +44,11 @@ gla_scale_ds0(float* __restrict__ ds0, const bf16* __restrict__ g, const bf16* _
 // gradient, dg_t = q_t*dq_t - k_t*dk_t + dg_{t+1} and, at a boundary 64m,
 //   dg_{64m}[i] = sum_j (G_{64m} .* dS_{64m})[i,j] S_{64m-1}[i,j] ,
 // (dh the same summed over i), with G_{64m} = alpha^T beta of token 64m; at
-// m = N the term is sum_j dht S_T (no gate).  S_{64m-1} is the forward walk's
-// state before chunk m (hsf), dS_{64m} the reversed walk's state before its
-// chunk N - m (hsr).
+// m = N the term is sum_j dht S_T (no gate), and at m = 0 it is sum_j dS_0'
+// S_0 with dS_0' = G_0 .* dS_0 the gradient of the initial state (blocks for
+// m = 0 run only when there is an S_0: without one, dg_0 = 0).  S_{64m-1} is
+// the forward walk's state before chunk m (hsf), dS_{64m} the reversed walk's
+// state before its chunk N - m (hsr).
 // One workgroup per (head, boundary m = 1..N): W[i][j] = alpha_i beta_j
 // dS[i][j] S[i][j] over the K x V tile read as 16-byte vectors; thread
 // (row group rg, column vector cv) takes rows rg, rg + RG, ... of columns
@@ -56,28 +58,31 @@ template <int V>
 __global__ void __launch_bounds__(256)
 gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, const float* __restrict__ st,
                 const float* __restrict__ dht, const bf16* __restrict__ g, const bf16* __restrict__ hg,
-                float* __restrict__ ag, float* __restrict__ ah, int T, int H, int K) {
+                float* __restrict__ ag, float* __restrict__ ah, int T, int H, int K,
+                const float* __restrict__ s0 = nullptr, const float* __restrict__ ds0 = nullptr) {
     constexpr int CVN = V / 8, RG = 256 / CVN;
     static_assert(CVN <= 64 && (CVN & (CVN - 1)) == 0, "a row's lanes sit in one wave");
     __shared__ float alpha[256];
     __shared__ float beta[V];
     __shared__ float colp[RG][V];
     const int N = T / 64;
-    const int m = blockIdx.x + 1;
+    const int m = blockIdx.x + (s0 ? 0 : 1);
     const long bh = blockIdx.y, b = bh / H, h = bh % H, KV = (long)K * V;
     const int tid = threadIdx.x, cv = tid % CVN, rg = tid / CVN;
-    const bool last = m == N;  // S_T and dht, no gate
-    const long tok = last ? 0 : (b * T + 64L * m) * H + h;
-    for (int i = tid; i < K; i += 256) alpha[i] = last ? 1.f : __expf(Elem<bf16>::to_f(g[tok * K + i]));
-    for (int j = tid; j < V; j += 256) beta[j] = last ? 1.f : __expf(Elem<bf16>::to_f(hg[tok * V + j]));
+    const bool last = m == N;   // S_T and dht, no gate
+    const bool first = m == 0;  // S_0 and dS_0', the gate already applied
+    const bool edge = last || first;
+    const long tok = edge ? 0 : (b * T + 64L * m) * H + h;
+    for (int i = tid; i < K; i += 256) alpha[i] = edge ? 1.f : __expf(Elem<bf16>::to_f(g[tok * K + i]));
+    for (int j = tid; j < V; j += 256) beta[j] = edge ? 1.f : __expf(Elem<bf16>::to_f(hg[tok * V + j]));
     __syncthreads();
     float cs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) cs[e] = 0.f;
-    const bf16* S16 = hsf + (bh * N + (last ? 0 : m)) * KV;
-    const bf16* D16 = hsr + (bh * N + (last ? 0 : N - m)) * KV;
-    const float* S32 = st + bh * KV;
-    const float* D32 = dht ? dht + bh * KV : nullptr;
+    const bf16* S16 = hsf + (bh * N + (edge ? 0 : m)) * KV;
+    const bf16* D16 = hsr + (bh * N + (edge ? 0 : N - m)) * KV;
+    const float* S32 = first ? s0 + bh * KV : st + bh * KV;
+    const float* D32 = first ? ds0 + bh * KV : (dht ? dht + bh * KV : nullptr);
     // rows in groups of four: the group's loads are independent, then its four
     // row reductions (also independent) follow
     constexpr int GR = 4;
@@ -91,7 +96,7 @@ gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, cons
             if (i >= K) continue;
             float p[8];
             const long off = (long)i * V + 8 * cv;
-            if (!last) {
+            if (!edge) {
                 const u32x4 sv = *reinterpret_cast<const u32x4*>(S16 + off);
                 const u32x4 dv = *reinterpret_cast<const u32x4*>(D16 + off);
                 const bf16* sx = reinterpret_cast<const bf16*>(&sv);
@@ -134,15 +139,23 @@ gla_gate_anchor(const bf16* __restrict__ hsf, const bf16* __restrict__ hsr, cons
 }
 
 // out_t = the anchor of the chunk's end boundary + the chunk's own reverse
-// cumulative sum of a*da - c*dc (tensors [B,T,H,D]).  One workgroup per chunk
-// and head: thread (part, cv) takes columns 8cv .. 8cv+7 over the tokens
-// part*TPP .. +TPP-1 with 16-byte loads, sums them in reverse, and adds the
-// totals of the later parts (through LDS) and the anchor.
+// cumulative sum of a*da - c*dc (tensors [B,T,H,D]), pinned to the anchor of
+// the chunk's start boundary as well: that anchor is the exact value at the
+// chunk's first token, and its mismatch delta with (end anchor + the chunk's
+// whole sum) is the sum's accumulated rounding, which is spread linearly over
+// the chunk (token p of 64 gets delta * (64 - p) / 64), so both ends are exact
+// and the error in between is that of a path pinned at both ends rather than
+// one free at the start.  The first chunk's start anchor is zero when the
+// initial state is (zero_start), else the anchor of boundary 0.  One
+// workgroup per chunk and head: thread (part, cv) takes
+// columns 8cv .. 8cv+7 over the tokens part*TPP .. +TPP-1 with 16-byte loads,
+// sums them in reverse, and adds the totals of the later parts (through LDS)
+// and the anchors.
 template <int D>
 __device__ __forceinline__ void gate_grad_chunk(const bf16* __restrict__ a, const bf16* __restrict__ da,
                                                 const bf16* __restrict__ c, const bf16* __restrict__ dc,
                                                 const float* __restrict__ anchor, bf16* __restrict__ out, int T,
-                                                int H) {
+                                                int H, bool zero_start) {
     constexpr int CV = D / 8, NPART = 256 / CV, TPP = kChunk / NPART;
     static_assert(NPART * CV == 256 && NPART * TPP == kChunk, "gate-gradient tiling");
     __shared__ float tot[NPART][D];
@@ -171,18 +184,26 @@ __device__ __forceinline__ void gate_grad_chunk(const bf16* __restrict__ a, cons
 #pragma unroll
     for (int e = 0; e < 8; ++e) tot[part][jv + e] = x[0][e];
     __syncthreads();
-    float off[8];
+    float off[8], all[8], del[8];
     const float* an = anchor + (bh * (N + 1) + n + 1) * D + jv;
+    const float* an0 = anchor + (bh * (N + 1) + n) * D + jv;  // n = 0: written only when there is an S_0
 #pragma unroll
-    for (int e = 0; e < 8; ++e) off[e] = an[e];
-    for (int p = part + 1; p < NPART; ++p)
+    for (int e = 0; e < 8; ++e) off[e] = all[e] = an[e];
+    for (int p = 0; p < NPART; ++p)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) off[e] += tot[p][jv + e];
+        for (int e = 0; e < 8; ++e) {
+            const float t = tot[p][jv + e];
+            all[e] += t;
+            off[e] += p > part ? t : 0.f;
+        }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) del[e] = (n > 0 || !zero_start ? an0[e] : 0.f) - all[e];
 #pragma unroll
     for (int i = 0; i < TPP; ++i) {
+        const float wt = (float)(kChunk - (part * TPP + i)) * (1.f / kChunk);
         alignas(16) bf16 y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = Elem<bf16>::from_f(x[i][e] + off[e]);
+        for (int e = 0; e < 8; ++e) y[e] = Elem<bf16>::from_f(x[i][e] + off[e] + del[e] * wt);
         *reinterpret_cast<u32x4*>(out + base + i * rs) = *reinterpret_cast<const u32x4*>(y);
     }
 }
@@ -194,11 +215,12 @@ __global__ void __launch_bounds__(256)
 gla_gate_grad_out(const bf16* __restrict__ q, const bf16* __restrict__ dq, const bf16* __restrict__ k,
                   const bf16* __restrict__ dk, const float* __restrict__ ag, bf16* __restrict__ dg,
                   const bf16* __restrict__ o, const bf16* __restrict__ d_o, const bf16* __restrict__ v,
-                  const bf16* __restrict__ dv, const float* __restrict__ ah, bf16* __restrict__ dh, int T, int H) {
+                  const bf16* __restrict__ dv, const float* __restrict__ ah, bf16* __restrict__ dh, int T, int H,
+                  int zero_start) {
     if (blockIdx.z == 0)
-        gate_grad_chunk<DK>(q, dq, k, dk, ag, dg, T, H);
+        gate_grad_chunk<DK>(q, dq, k, dk, ag, dg, T, H, zero_start != 0);
     else
-        gate_grad_chunk<DV>(o, d_o, v, dv, ah, dh, T, H);
+        gate_grad_chunk<DV>(o, d_o, v, dv, ah, dh, T, H, zero_start != 0);
 }
 
 static FwdLaunch general_fwd_args(int B, int T, int H, int K, int V, const void* q, const void* k, const void* v,
@@ -254,7 +276,9 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     if (err != hipSuccess) return err;
     // dv and dS_0' from the time-reversed recurrence of dS (its gates one token
     // later), read and written in place in the input's token order
-    float* ds0 = L.ds0;
+    // (dS_0' goes to the workspace when the caller asks for none but there is an
+    // S_0: the first chunk's gate anchor is sum dS_0' S_0)
+    float* ds0 = L.ds0 ? L.ds0 : (L.s0 ? reinterpret_cast<float*>(ws + w.ds0) : nullptr);
     err = launch_fwd_general(general_fwd_args(B, T, H, K, V, L.k, L.q, L.d_o, L.g, L.h, L.dht, L.dv, ds0, fws, hsr, 1, sm));
     if (err != hipSuccess) return err;
     if (ds0) {
@@ -270,20 +294,23 @@ hipError_t launch_bwd_general(const BwdGeneralLaunch& L) {
     // gate gradients: anchors at the chunk boundaries, then each chunk's reverse sums
     const unsigned N = (unsigned)(T / 64);
     {
-        const dim3 ga(N, (unsigned)BH);
+        // boundaries 1 .. N, and 0 when there is an S_0
+        const dim3 ga(N + (L.s0 ? 1 : 0), (unsigned)BH);
         if (V == 128)
             GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor<128>, ga, dim3(256), sm, (const bf16*)hsf,
-                       (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K);
+                       (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K,
+                       L.s0, ds0);
         else
             GLA_LAUNCH("bwdg_gate_anchor", gla_gate_anchor<256>, ga, dim3(256), sm, (const bf16*)hsf,
-                       (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K);
+                       (const bf16*)hsr, (const float*)st, L.dht, (const bf16*)L.g, (const bf16*)L.h, ag, ah, T, H, K,
+                       L.s0, ds0);
     }
     const dim3 gg(N, (unsigned)BH, 2);
 #define GLA_GATE_OUT(DK_, DV_)                                                                                  \
     GLA_LAUNCH("bwdg_gate_out", (gla_gate_grad_out<DK_, DV_>), gg, dim3(256), sm, (const bf16*)L.q,           \
                (const bf16*)L.dq, (const bf16*)L.k, (const bf16*)L.dk, (const float*)ag, static_cast<bf16*>(L.dg), \
                o, (const bf16*)L.d_o, (const bf16*)L.v, (const bf16*)L.dv, (const float*)ah,                      \
-               static_cast<bf16*>(L.dh), T, H)
+               static_cast<bf16*>(L.dh), T, H, L.s0 == nullptr ? 1 : 0)
     if (K == 128 && V == 128) GLA_GATE_OUT(128, 128);
     else if (K == 128) GLA_GATE_OUT(128, 256);
     else if (V == 128) GLA_GATE_OUT(256, 128);

@@ -154,7 +154,7 @@ inline size_t fwd_general_workspace_bytes(const Shape& s) {
 // four general forwards it runs (shapes K x V and V x K).  The reversed
 // recurrences read their inputs in place.
 struct BwdGeneralLayout {
-    size_t o, st, hsf, hsr, ag, ah, fws, total;
+    size_t o, st, hsf, hsr, ag, ah, ds0, fws, total;
 };
 inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
     BwdGeneralLayout w{};
@@ -172,6 +172,7 @@ inline BwdGeneralLayout bwd_general_layout(const Shape& s) {
     w.hsr = at; at += round256(BH * N * KV * 2);
     w.ag = at; at += round256(BH * (N + 1) * (size_t)s.K * 4);
     w.ah = at; at += round256(BH * (N + 1) * (size_t)s.V * 4);
+    w.ds0 = at; at += sf;  // dS_0 when the caller asks for none (the first chunk's gate anchor needs it)
     w.fws = at; at += round256(f1 > f2 ? f1 : f2);
     w.total = at;
     return w;
