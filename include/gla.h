@@ -103,7 +103,10 @@ gla_status_t gla_fwd(const gla_shape_t* shape,
  * segments' states and log-decays (B*H*P*K*V elements in the input dtype plus
  * B*H*P*K floats, P <= T/64), and for 16-bit inputs with K = 256 also one
  * 77056-byte record of prepared chunk operands per chunk and head
- * (B*H*T/64 records: about 1.2 KB per token and head). */
+ * (B*H*T/64 records: about 1.2 KB per token and head).  Heads run as slices
+ * (16-bit K = 512; fp32 K or V above 128) add the staging copies of one slice
+ * (its q, k, g columns or v columns, its partial output and state rows) in
+ * front of the slice's own workspace. */
 size_t gla_fwd_workspace_size(const gla_shape_t* shape);
 
 /*
@@ -153,7 +156,11 @@ gla_status_t gla_bwd(const gla_shape_t* shape,
                      void* dq, void* dk, void* dv, void* dg, float* ds0,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace gla_bwd needs for `shape` (0 for an invalid shape). */
+/* Bytes of device workspace gla_bwd needs for `shape` (0 for an invalid shape; no
+ * HIP call).  It holds the segment states and gradients, the backward's chunk
+ * anchors and the dP tiles handed from the dq walk to the dk walk; heads run as
+ * slices (16-bit V = 512 or K = 512, fp32 K or V above 128) add one slice's staging
+ * copies and partial gradients in front of the slice's own workspace. */
 size_t gla_bwd_workspace_size(const gla_shape_t* shape);
 
 /*
