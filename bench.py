@@ -48,15 +48,15 @@ def alg_bytes_per_token_head(kernel: str, K: int, V: int, e: int, P: int, P_bwd:
     segment-state pass reads q, g, d_o of every segment instead of all but the
     first when the dv walk takes segments in halves (it then also needs each
     segment's midpoint state); with a checkpoint (ckpt) it runs only that
-    backward direction, and with a checkpoint, 16-bit per-column gates and the
-    dv walk in halves (`fused`) the dq walk forms it: it then also reads q and
+    backward direction, and with a checkpoint, 16-bit inputs and the dv walk
+    in halves (`fused`) the dq walk forms it: it then also reads q and
     writes the 2 P_bwd half-segment states of K x V per head (T tokens).  The
     forward's segment pass skips the last segment unless the final state is
     asked for (16-bit inputs: the combine then forms S_T from every segment)."""
     G = K if G is None else G
     seg_frac = (1.0 if final_state and e == 2 else (P - 1) / P) if P > 1 else 0.0
     seg_frac_bwd = (P_bwd - 1) / P_bwd if P_bwd > 1 else 0.0
-    fused = ckpt and dv_split and e == 2 and G == K and T > 0
+    fused = ckpt and dv_split and e == 2 and T > 0
     table = {
         "fwd_walk": e * (2 * K + G + 2 * V),            # q, k, g, v read; o written
         # k, g, v, d_o read; dq written (fused: q read, the half segments' dS* written)
@@ -866,7 +866,7 @@ def main():
     # The step is the checkpointed training pair when the shape has one (the
     # forward keeps each backward segment's starting state, the backward
     # starts from it); the recompute pair gla_fwd + gla_bwd is timed beside it.
-    ck_bytes = 0 if (sg or args.recompute) else gla.gla_ckpt_size(B, T, H, K, V, dt)
+    ck_bytes = 0 if args.recompute else gla.gla_ckpt_size(B, T, H, K, V, dt)
     ck = gla.workspace(ck_bytes, dev)
 
     def fwd_rc():
@@ -878,14 +878,14 @@ def main():
 
     def fwd():
         if ck_bytes:
-            gla.gla_fwd_ckpt_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, ck, wsf)
+            gla.gla_fwd_ckpt_into(d["q"], d["k"], d["v"], d["g"], d["s0"], o, sf, ck, wsf, scalar_gate=sg)
         else:
             fwd_rc()
 
     def bwd():
         if ck_bytes:
             gla.gla_bwd_ckpt_into(d["q"], d["k"], d["v"], d["g"], d["s0"], ck, d["do"], None, dq, dk, dv, dg, ds0,
-                                  wsb)
+                                  wsb, scalar_gate=sg)
         else:
             bwd_rc()
 
@@ -990,12 +990,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, %s per step" % (
-            w.name, B, H, T, K, V, w.dtype, "scalar gate [B,T,H], gla_fwd_scalar + gla_bwd_scalar" if sg else
-            ("gla_fwd_ckpt + gla_bwd_ckpt (the backward starts its segments from the forward's states)" if ck_bytes
-             else "gla_fwd + gla_bwd")), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
+            w.name, B, H, T, K, V, w.dtype,
+            ("scalar gate [B,T,H], " if sg else "") +
+            (("gla_fwd_scalar_ckpt + gla_bwd_scalar_ckpt" if sg else "gla_fwd_ckpt + gla_bwd_ckpt") +
+             " (the backward starts its segments from the forward's states)" if ck_bytes else
+             ("gla_fwd_scalar + gla_bwd_scalar" if sg else "gla_fwd + gla_bwd"))), "global_batch": B, "seq_len": T, "heads": H, "dk": K, "dv": V,
             "chunk": 64, "segments": P},
         "ms_per_step_recompute": pct(cold_rc, 50) if (ck_bytes and not args.step_only) else None,
-        "recompute_step": "gla_fwd + gla_bwd (every state recomputed in the backward), cold median",
+        "recompute_step": ("gla_fwd_scalar + gla_bwd_scalar" if sg else "gla_fwd + gla_bwd") +
+                          " (every state recomputed in the backward), cold median",
         "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
         "bwd_tokens_per_s": tokens / (ms_bwd * 1e-3),
         "ms_fwd": ms_fwd,

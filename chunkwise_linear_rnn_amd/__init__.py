@@ -10,6 +10,7 @@ Functions mirror the ABI:
   gla_fwd(q, k, v, g, s0=None, ...)         -> (o, s_final)
   gla_bwd(q, k, v, g, d_o, s0=None, dht=None) -> (dq, dk, dv, dg, ds0)
   gla_fwd_scalar / gla_bwd_scalar            (the same with a scalar gate g [B,T,H] per token and head)
+  gla_fwd_ckpt / gla_bwd_ckpt, gla_fwd_scalar_ckpt / gla_bwd_scalar_ckpt  (training pairs with a checkpoint)
   gla_decode(q, k, v, g, state)              -> o   (recurrent form; state updated in place)
   gla_out_gate(o, z, ln_w, ln_b, eps)        -> y   (per-head LayerNorm, Swish output gate)
   gla_out_gate_bwd(o, z, ln_w, ln_b, eps, dy) -> (d_o, dz, dln_w, dln_b)
@@ -55,7 +56,7 @@ class GlaError(RuntimeError):
 
 EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode", "gla_out_gate",
            "gla_out_gate_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_bwd_scalar_workspace_size",
-           "gla_fwd_scalar_workspace_size",
+           "gla_fwd_scalar_workspace_size", "gla_fwd_scalar_ckpt", "gla_bwd_scalar_ckpt",
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
@@ -86,6 +87,10 @@ def lib():
     L.gla_fwd_ckpt.restype = ctypes.c_int
     L.gla_bwd_ckpt.argtypes = [sh] + [vp] * 14 + [ctypes.c_size_t, vp]
     L.gla_bwd_ckpt.restype = ctypes.c_int
+    L.gla_fwd_scalar_ckpt.argtypes = L.gla_fwd_ckpt.argtypes
+    L.gla_fwd_scalar_ckpt.restype = ctypes.c_int
+    L.gla_bwd_scalar_ckpt.argtypes = L.gla_bwd_ckpt.argtypes
+    L.gla_bwd_scalar_ckpt.restype = ctypes.c_int
     L.gla_fwd_noalloc.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gla_fwd_noalloc.restype = ctypes.c_int
     L.gla_fwd_scalar.argtypes = L.gla_fwd.argtypes
@@ -223,20 +228,23 @@ def gla_ckpt_size(B, T, H, K, V, dtype) -> int:
     return int(lib().gla_ckpt_size(ctypes.byref(make_shape(B, T, H, K, V, dtype))))
 
 
-def gla_fwd_ckpt_into(q, k, v, g, s0, o, s_final, ckpt, ws, stream=None):
-    """gla_fwd_ckpt with caller-owned outputs, checkpoint and workspace."""
+def gla_fwd_ckpt_into(q, k, v, g, s0, o, s_final, ckpt, ws, stream=None, scalar_gate=False):
+    """gla_fwd_ckpt with caller-owned outputs, checkpoint and workspace
+    (scalar_gate: g is [B,T,H] and gla_fwd_scalar_ckpt is called)."""
     B, T, H, K, V = _dims(q, v)
     shape = make_shape(B, T, H, K, V, q.dtype)
     nbytes = 0 if ws is None else ws.numel()
-    _check(lib().gla_fwd_ckpt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o),
+    fn = lib().gla_fwd_scalar_ckpt if scalar_gate else lib().gla_fwd_ckpt
+    _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(o),
                               _ptr(s_final), _ptr(ckpt), _ptr(ws), nbytes, _stream(stream)))
 
 
-def gla_bwd_ckpt_into(q, k, v, g, s0, ckpt, d_o, dht, dq, dk, dv, dg, ds0, ws, stream=None):
+def gla_bwd_ckpt_into(q, k, v, g, s0, ckpt, d_o, dht, dq, dk, dv, dg, ds0, ws, stream=None, scalar_gate=False):
     B, T, H, K, V = _dims(q, v)
     shape = make_shape(B, T, H, K, V, q.dtype)
     nbytes = 0 if ws is None else ws.numel()
-    _check(lib().gla_bwd_ckpt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(ckpt),
+    fn = lib().gla_bwd_scalar_ckpt if scalar_gate else lib().gla_bwd_ckpt
+    _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(ckpt),
                               _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ds0), _ptr(ws),
                               nbytes, _stream(stream)))
 
@@ -275,6 +283,44 @@ def gla_bwd_ckpt(q, k, v, g, d_o, ckpt, s0=None, dht=None, output_ds0=True, stre
     ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
     ws = workspace(gla_bwd_workspace_size(B, T, H, K, V, dt), dev)
     gla_bwd_ckpt_into(q, k, v, g, s0, ckpt if need > 0 else None, d_o, dht, dq, dk, dv, dg, ds0, ws, stream)
+    return dq, dk, dv, dg, ds0
+
+
+def gla_fwd_scalar_ckpt(q, k, v, g, s0=None, output_final_state=True, stream=None):
+    """(o, S_T, ckpt): gla_fwd_scalar that also keeps the backward's segment-start
+    states (None when the shape has no checkpoint)."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),
+                         ("v", v, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    sf = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    ck = workspace(gla_ckpt_size(B, T, H, K, V, dt), dev)
+    ws = workspace(gla_fwd_scalar_workspace_size(B, T, H, K, V, dt), dev)
+    gla_fwd_ckpt_into(q, k, v, g, s0, o, sf, ck, ws, stream, scalar_gate=True)
+    return o, sf, ck
+
+
+def gla_bwd_scalar_ckpt(q, k, v, g, d_o, ckpt, s0=None, dht=None, output_ds0=True, stream=None):
+    """gla_bwd_scalar starting from the segment states gla_fwd_scalar_ckpt kept."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),
+                         ("v", v, (B, T, H, V)), ("d_o", d_o, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    _need(s0, "s0", (B, H, K, V), torch.float32, dev)
+    _need(dht, "dht", (B, H, K, V), torch.float32, dev)
+    need = gla_ckpt_size(B, T, H, K, V, dt)
+    if need > 0 and (ckpt is None or ckpt.numel() * ckpt.element_size() < need or ckpt.device != dev
+                     or not ckpt.is_contiguous()):
+        raise ValueError("ckpt must be the contiguous %d-byte checkpoint of gla_fwd_scalar_ckpt on %s" % (need, dev))
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dg = torch.empty_like(g); dv = torch.empty_like(v)
+    ds0 = torch.empty(B, H, K, V, dtype=torch.float32, device=dev) if output_ds0 else None
+    ws = workspace(gla_bwd_scalar_workspace_size(B, T, H, K, V, dt), dev)
+    gla_bwd_ckpt_into(q, k, v, g, s0, ckpt if need > 0 else None, d_o, dht, dq, dk, dv, dg, ds0, ws, stream,
+                      scalar_gate=True)
     return dq, dk, dv, dg, ds0
 
 

@@ -894,12 +894,13 @@ hipError_t bwd_launch(const gla::Shape& s, const void* q, const void* k, const v
         }
         // scalar gate: each key block's per-token sum of dg, after everything else
         if (sg) a.ws_dgp = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, false));
-        // the half-segment gate totals (dsub = 2) sit in the last area
-        if (a.dsub == 2) a.ws_gate = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, sg) -
+        // the half-segment gate totals (dsub = 2) sit in the last area of the
+        // per-column layout (the scalar gate's dg partials come after it)
+        if (a.dsub == 2) a.ws_gate = reinterpret_cast<float*>(ws + bwd_workspace_bytes(s, false) -
                                                              gla::round256(2 * kk * sizeof(float)));
-        // checkpointed, half segments, per-column 16-bit gates: the dq walk
-        // forms the half segments' dS* (no segment pass of its own)
-        a.ds_fused = a.dsub == 2 && s.bf16 && !sg && p.BK == 64;
+        // checkpointed, half segments, 16-bit inputs: the dq walk forms the half
+        // segments' dS* (no segment pass of its own)
+        a.ds_fused = a.dsub == 2 && s.bf16 && p.BK == 64;
         a.stream = strm;
         err = gla::launch_bwd(a);
     }
@@ -1099,6 +1100,36 @@ gla_status_t bwd_impl(const gla_shape_t* shape, const void* q, const void* k, co
     return GLA_OK;
 }
 
+// The training pair for per-column (sg = false) or per-token (sg = true) gates.
+gla_status_t fwd_ckpt_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                           const float* s0, void* o, float* s_final, void* ckpt, void* workspace,
+                           size_t workspace_bytes, void* stream, bool sg) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, true);
+    if (st != GLA_OK) return st;
+    const size_t need = ckpt_bytes(s);
+    if (need > 0 && !ckpt) return fail(GLA_ERR_NULL, "ckpt is required (gla_ckpt_size = %zu bytes)", need);
+    if (!aligned16(ckpt)) return fail(GLA_ERR_ALIGN, "ckpt is not 16-byte aligned");
+    return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, sg,
+                    need > 0 ? ckpt : nullptr);
+}
+
+gla_status_t bwd_ckpt_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                           const float* s0, const void* ckpt, const void* d_o, const float* dht, void* dq, void* dk,
+                           void* dv, void* dg, float* ds0, void* workspace, size_t workspace_bytes, void* stream,
+                           bool sg) {
+    g_detail.clear();
+    gla::Shape s;
+    gla_status_t st = check_shape(shape, &s, true);
+    if (st != GLA_OK) return st;
+    const size_t need = ckpt_bytes(s);
+    if (need > 0 && !ckpt) return fail(GLA_ERR_NULL, "ckpt is required (gla_ckpt_size = %zu bytes)", need);
+    if (!aligned16(ckpt)) return fail(GLA_ERR_ALIGN, "ckpt is not 16-byte aligned");
+    return bwd_impl(shape, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes, stream, sg,
+                    need > 0 ? ckpt : nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1180,29 +1211,28 @@ size_t gla_ckpt_size(const gla_shape_t* shape) {
 gla_status_t gla_fwd_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                           const float* s0, void* o, float* s_final, void* ckpt, void* workspace,
                           size_t workspace_bytes, void* stream) {
-    g_detail.clear();
-    gla::Shape s;
-    gla_status_t st = check_shape(shape, &s, true);
-    if (st != GLA_OK) return st;
-    const size_t need = ckpt_bytes(s);
-    if (need > 0 && !ckpt) return fail(GLA_ERR_NULL, "ckpt is required (gla_ckpt_size = %zu bytes)", need);
-    if (!aligned16(ckpt)) return fail(GLA_ERR_ALIGN, "ckpt is not 16-byte aligned");
-    return fwd_impl(shape, q, k, v, g, s0, o, s_final, workspace, workspace_bytes, stream, false,
-                    need > 0 ? ckpt : nullptr);
+    return fwd_ckpt_impl(shape, q, k, v, g, s0, o, s_final, ckpt, workspace, workspace_bytes, stream, false);
 }
 
 gla_status_t gla_bwd_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
                           const float* s0, const void* ckpt, const void* d_o, const float* dht, void* dq, void* dk,
                           void* dv, void* dg, float* ds0, void* workspace, size_t workspace_bytes, void* stream) {
-    g_detail.clear();
-    gla::Shape s;
-    gla_status_t st = check_shape(shape, &s, true);
-    if (st != GLA_OK) return st;
-    const size_t need = ckpt_bytes(s);
-    if (need > 0 && !ckpt) return fail(GLA_ERR_NULL, "ckpt is required (gla_ckpt_size = %zu bytes)", need);
-    if (!aligned16(ckpt)) return fail(GLA_ERR_ALIGN, "ckpt is not 16-byte aligned");
-    return bwd_impl(shape, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes, stream, false,
-                    need > 0 ? ckpt : nullptr);
+    return bwd_ckpt_impl(shape, q, k, v, g, s0, ckpt, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes,
+                         stream, false);
+}
+
+gla_status_t gla_fwd_scalar_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                                 const void* g, const float* s0, void* o, float* s_final, void* ckpt,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_ckpt_impl(shape, q, k, v, g, s0, o, s_final, ckpt, workspace, workspace_bytes, stream, true);
+}
+
+gla_status_t gla_bwd_scalar_ckpt(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                                 const void* g, const float* s0, const void* ckpt, const void* d_o, const float* dht,
+                                 void* dq, void* dk, void* dv, void* dg, float* ds0, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return bwd_ckpt_impl(shape, q, k, v, g, s0, ckpt, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes,
+                         stream, true);
 }
 
 gla_status_t gla_fwd_scalar(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,

@@ -557,7 +557,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
     static_assert(CPK % VEC == 0, "wave tiling");
-    static_assert(!DS || (BK == 64 && !SG), "dS* in the dq walk: 64-row key blocks, per-column gates");
+    static_assert(!DS || BK == 64, "dS* in the dq walk: 64-row key blocks");
     using Sm = RowPipeSmem<T, BK, V, NW, DS>;
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
@@ -1902,11 +1902,11 @@ static hipError_t launch_rows_g(const BwdLaunch& a) {
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
-        if constexpr (!SG && BK == 64) {
+        if constexpr (BK == 64) {
             static_assert(sizeof(RowPipeSmem<T, BK, V, NW, true>) <= 160 * 1024, "LDS budget");
             if (a.ds_fused) {
                 // dS* of every half segment formed by the dq walk, then their combine
-                GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, false, true>), grid, dim3(NT), a.stream,
+                GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, SG, true>), grid, dim3(NT), a.stream,
                            (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.d_o, (const T*)a.ws_state, a.s0,
                            (T*)a.dq, (T*)a.ws_hs, (T*)a.ws_dp, a.T, a.H, a.K, a.N, a.P, a.seg_len, (int)a.BH,
                            (const T*)a.q, (T*)a.ws_dstate, a.ws_gate, a.seg_len / 2);

@@ -670,20 +670,16 @@ static hipError_t launch_fwd_sg(const FwdLaunch& a) {
     if constexpr (sizeof(T) == 2) {
         static_assert(sizeof(PipeSmem<T, KD, BV, NW, false>) <= 160 * 1024, "LDS budget");
         if (a.ckpt) {
-            if constexpr (!SG) {
-                if (ck_comb)
-                    GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, false, true>), grid, dim3(NT),
-                               a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                               (const T*)a.ws_state, a.s0, (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len,
-                               (int)a.BH, (T*)a.ckpt, a.ck_len / a.seg_len, a.ck_P);
-                else
-                    GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, false, true>), grid, dim3(NT), a.stream,
-                               (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
-                               (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
-                               a.ck_len, a.ck_P);
-            } else {
-                return hipErrorInvalidValue;
-            }
+            if (ck_comb)
+                GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG, false, true>), grid, dim3(NT),
+                           a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                           (const T*)a.ws_state, a.s0, (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len,
+                           (int)a.BH, (T*)a.ckpt, a.ck_len / a.seg_len, a.ck_P);
+            else
+                GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG, true>), grid, dim3(NT), a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,
+                           (T*)a.o, walk_sfinal, a.T, a.H, a.V, a.N, a.P, a.seg_len, (int)a.BH, (T*)a.ckpt,
+                           a.ck_len, a.ck_P);
         } else {
             GLA_LAUNCH("fwd_walk", (gla_fwd_walk_pipe<T, KD, BV, NW, SG>), grid, dim3(NT), a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, (const T*)a.ws_state, a.s0,

@@ -231,6 +231,27 @@ size_t gla_fwd_scalar_workspace_size(const gla_shape_t* shape);
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
 
 /*
+ * The training pair of the scalar gate: gla_fwd_ckpt / gla_bwd_ckpt (below) with
+ * g and dg [B,T,H] as for gla_fwd_scalar / gla_bwd_scalar.  The checkpoint has the
+ * layout and size of gla_ckpt_size(shape) and the same contract (written by
+ * gla_fwd_scalar_ckpt, read unmodified by gla_bwd_scalar_ckpt for the same inputs);
+ * shapes without one (gla_ckpt_size == 0: fp32, K > 128, V > 256, a single
+ * backward segment) run the plain pair.  Workspaces: gla_fwd_scalar_workspace_size
+ * and gla_bwd_scalar_workspace_size.  Errors: as gla_fwd_scalar / gla_bwd_scalar,
+ * plus GLA_ERR_NULL for a NULL ckpt the shape needs and GLA_ERR_ALIGN for a
+ * misaligned one.
+ */
+gla_status_t gla_fwd_scalar_ckpt(const gla_shape_t* shape,
+                                 const void* q, const void* k, const void* v, const void* g,
+                                 const float* s0, void* o, float* s_final, void* ckpt,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+gla_status_t gla_bwd_scalar_ckpt(const gla_shape_t* shape,
+                                 const void* q, const void* k, const void* v, const void* g,
+                                 const float* s0, const void* ckpt, const void* d_o, const float* dht,
+                                 void* dq, void* dk, void* dv, void* dg, float* ds0,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gla_fwd_general -- forward pass of general gated linear attention, whose
  * forget gate is an outer product G_t = alpha_t^T beta_t of a key-side gate
  * alpha_t = exp(g_t) and a value-side gate beta_t = exp(h_t) ("Gated Linear

@@ -352,6 +352,27 @@ def test_ckpt_entry_points_validate(L):
     assert bwd(_shape(K=1024, dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
 
 
+def test_scalar_ckpt_entry_points_validate(L):
+    # the scalar gate's pair takes gla_ckpt_size's checkpoint and the scalar workspaces
+    s = _shape(B=2, H=4, T=8192, K=128, V=256)
+    fwd = lambda shape, ck=P: L.gla_fwd_scalar_ckpt(ctypes.byref(shape), P, P, P, P, None, P, None, ck, P, 1 << 40,
+                                                    None)
+    bwd = lambda shape, ck=P: L.gla_bwd_scalar_ckpt(ctypes.byref(shape), P, P, P, P, None, ck, P, None, P, P, P, P,
+                                                    None, P, 1 << 40, None)
+    assert fwd(s, ck=None) == ERR_NULL
+    assert bwd(s, ck=None) == ERR_NULL
+    assert fwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert bwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
+    assert fwd(_shape(T=100)) == ERR_SHAPE
+    assert bwd(_shape(K=1024)) == ERR_UNSUPPORTED
+    assert fwd(_shape(T=0)) == OK
+    # the workspace is checked before anything is enqueued
+    ws_b = L.gla_bwd_scalar_workspace_size(ctypes.byref(s))
+    assert ws_b > 0
+    assert L.gla_bwd_scalar_ckpt(ctypes.byref(s), P, P, P, P, None, P, P, None, P, P, P, P, None, P, ws_b - 1,
+                                 None) == ERR_WORKSPACE
+
+
 def test_general_ckpt_entry_points_validate(L):
     size = lambda shape: L.gla_general_ckpt_size(ctypes.byref(shape))
     s = _shape(B=2, H=4, T=8192, K=128, V=256)

@@ -1,9 +1,11 @@
-"""GPU parity of the checkpointed training pair (gla_fwd_ckpt + gla_bwd_ckpt).
+"""GPU parity of the checkpointed training pairs (gla_fwd_ckpt + gla_bwd_ckpt, and
+gla_fwd_scalar_ckpt + gla_bwd_scalar_ckpt for one gate per token and head).
 
-The forward writes the state at the start of each backward segment while its
-walk passes that chunk boundary; the backward starts its segments from those
-states instead of recomputing them.  The forward's outputs must equal gla_fwd's
-bit for bit (the same walk, plus stores), and the gradients must match the fp64
+The forward keeps the state at the start of each backward segment (the segment
+combine writes it when every such start is a forward segment start, else the
+walk stores it as it passes that chunk boundary); the backward starts its
+segments from those states instead of recomputing them.  The forward's outputs
+must equal the plain forward's bit for bit, and the gradients must match the fp64
 oracle's reverse-mode gradient to the bf16 bound on every head and every
 64-token chunk, at small shapes (several segments, ragged last segment, the
 half-segment dv walk) and at the full size of the benchmark workload.
@@ -95,3 +97,55 @@ def test_ckpt_absent_for_uncovered_shapes():
     b = gla.gla_bwd(d["q"], d["k"], d["v"], d["g"], d["do"], d["s0"], d["dht"])
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def _check_scalar(w, inp, heads=None, with_dht=True):
+    from tests.test_parity_scalar_gate import _gpu, _sel
+    note("scalar ckpt parity: B=%d H=%d T=%d K=%d V=%d s0=%s" % (w.B, w.H, w.T, w.K, w.V, w.s0))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    dht = d["dht"] if with_dht else None
+    assert gla.gla_ckpt_size(w.B, w.T, w.H, w.K, w.V, w.torch_dtype) > 0
+    o, sf, ck = gla.gla_fwd_scalar_ckpt(d["q"], d["k"], d["v"], d["g"], d["s0"])
+    o_ref, sf_ref = gla.gla_fwd_scalar(d["q"], d["k"], d["v"], d["g"], d["s0"])
+    grads = gla.gla_bwd_scalar_ckpt(d["q"], d["k"], d["v"], d["g"], d["do"], ck, d["s0"], dht)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(sf, sf_ref)
+    if heads is None:
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    c = {n: to_np(inp[n]) for n in ("q", "k", "v", "g", "do")}
+    ref = oracle.gla_bwd_scalar(_sel(c["q"], heads), _sel(c["k"], heads), _sel(c["v"], heads), _sel(c["g"], heads),
+                                _sel(c["do"], heads), _sel(to_np(inp.get("s0")), heads, state=True),
+                                _sel(to_np(inp["dht"]), heads, state=True) if with_dht else None)
+    errs = {}
+    for name, x, r in zip(("dq", "dk", "dv"), grads[:3], ref[:3]):
+        errs[name] = rel_l2(_gpu(x, heads), r[:, :, 0, :])
+    errs["dg"] = rel_l2(_gpu(grads[3], heads), ref[3][:, :, 0])
+    errs["ds0"] = rel_l2(_gpu(grads[4], heads, True), ref[4][:, 0])
+    tol = TOL[torch.bfloat16]
+    note("  rel-L2 " + " ".join("%s=%.3e" % kv for kv in errs.items()) + " (tol %.0e)" % tol)
+    assert all(v <= tol for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("B,H,T,K,V,s0,dht", [
+    (1, 2, 320, 64, 64, "normal0.1", True),        # several segments per head
+    (2, 2, 448, 64, 128, "none", True),            # uneven segments
+    (4, 16, 64 * 13, 128, 256, "normal0.1", True),  # the half-segment walks, ragged last segment
+    (2, 16, 64 * 21, 128, 256, "none", False),     # a last segment with an empty second half
+    (2, 4, 8192, 128, 256, "none", False),         # the throughput shape, every head
+])
+def test_scalar_ckpt(B, H, T, K, V, s0, dht):
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="scalar", s0=s0, backward=True, seed=760 + T + K + V)
+    inp = gi.make_inputs(w, dht=True)
+    heads = None if B * H <= 8 else [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    _check_scalar(w, inp, heads=heads, with_dht=dht)
+
+
+def test_scalar_ckpt_exact_path():
+    # decays past the chunk basis range (one -80 nat reset, a run of -12 nat)
+    w = gi.custom(2, 2, 64 * 9, 64, 128, dtype="bf16", gate="scalar", s0="normal0.1", backward=True, seed=781)
+    inp = gi.make_inputs(w, dht=True)
+    g = inp["g"].float()
+    g[0, 70, :] = -80.0
+    g[1, 300:310, 1] = -12.0
+    inp["g"] = g.to(torch.bfloat16)
+    _check_scalar(w, inp)
