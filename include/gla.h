@@ -168,14 +168,16 @@ size_t gla_bwd_workspace_size(const gla_shape_t* shape);
  * Section 3.3 weighs materialising the hidden states in the forward pass
  * against recomputing them in the backward pass.  This pair keeps a small
  * part: the state at the start of each sequence segment the backward splits a
- * head into (one K x V state per segment), written by the forward walk when it
- * passes that chunk boundary.  The backward then recomputes every chunk state
+ * head into (one K x V state per segment), written by the forward's segment
+ * combine (or, when such a start is not one of the forward's own segment
+ * starts, by the forward walk as it passes that chunk boundary).  The backward
+ * then recomputes every chunk state
  * inside its segments from those starting states (instead of first running
  * its own pass over k, v and g to find them); everything else is gla_bwd.
  *   gla_ckpt_size(shape) : bytes of the checkpoint, [B,H,P,K,V] in the
  *     token dtype (P = the backward's segment count; entry 0 of each head is
  *     not written: segment 0 starts from s0).  0 when the shape has no
- *     checkpoint: fp32 inputs, K = 256, V = 512, a single segment, or an
+ *     checkpoint: fp32 inputs, K above 128, V = 512, a single segment, or an
  *     invalid or empty shape; both calls then behave exactly like gla_fwd /
  *     gla_bwd and ckpt may be NULL.  The shape must be a valid backward shape.
  *   gla_fwd_ckpt : gla_fwd (same arguments, results and workspace), plus
@@ -231,7 +233,7 @@ size_t gla_fwd_scalar_workspace_size(const gla_shape_t* shape);
 size_t gla_bwd_scalar_workspace_size(const gla_shape_t* shape);
 
 /*
- * The training pair of the scalar gate: gla_fwd_ckpt / gla_bwd_ckpt (below) with
+ * The training pair of the scalar gate: gla_fwd_ckpt / gla_bwd_ckpt (above) with
  * g and dg [B,T,H] as for gla_fwd_scalar / gla_bwd_scalar.  The checkpoint has the
  * layout and size of gla_ckpt_size(shape) and the same contract (written by
  * gla_fwd_scalar_ckpt, read unmodified by gla_bwd_scalar_ckpt for the same inputs);
