@@ -57,6 +57,7 @@ class GlaError(RuntimeError):
 EXPORTS = ["gla_fwd", "gla_bwd", "gla_fwd_scalar", "gla_bwd_scalar", "gla_decode", "gla_out_gate",
            "gla_out_gate_bwd", "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_bwd_scalar_workspace_size",
            "gla_fwd_scalar_workspace_size", "gla_fwd_scalar_ckpt", "gla_bwd_scalar_ckpt",
+           "gla_decode_scalar", "gla_decode_general",
            "gla_out_gate_bwd_workspace_size", "gla_fwd_general", "gla_fwd_general_workspace_size",
            "gla_bwd_general", "gla_bwd_general_workspace_size",
            "gla_status_string", "gla_last_error_detail", "gla_abi_version",
@@ -117,6 +118,10 @@ def lib():
     L.gla_bwd_scalar_workspace_size.restype = ctypes.c_size_t
     L.gla_decode.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp]
     L.gla_decode.restype = ctypes.c_int
+    L.gla_decode_scalar.argtypes = L.gla_decode.argtypes
+    L.gla_decode_scalar.restype = ctypes.c_int
+    L.gla_decode_general.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.gla_decode_general.restype = ctypes.c_int
     fl = ctypes.c_float
     L.gla_out_gate.argtypes = [sh, vp, vp, vp, vp, fl, vp, vp]
     L.gla_out_gate.restype = ctypes.c_int
@@ -516,11 +521,17 @@ def gla_bwd_general_ckpt(q, k, v, g, h, d_o, o, ckpt, s0=None, dht=None, output_
     return dq, dk, dv, dg, dh, ds0
 
 
-def gla_decode_into(q, k, v, g, state, o, stream=None):
+def gla_decode_into(q, k, v, g, state, o, stream=None, h=None, scalar_gate=False):
+    """The decode call on caller-owned o: gla_decode, gla_decode_scalar (g [B,T,H])
+    or, with h [B,T,H,V], gla_decode_general."""
     B, T, H, K, V = _dims(q, v)
     shape = make_shape(B, T, H, K, V, q.dtype)
-    _check(lib().gla_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(o),
-                            _stream(stream)))
+    if h is not None:
+        _check(lib().gla_decode_general(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h),
+                                        _ptr(state), _ptr(o), _stream(stream)))
+        return
+    fn = lib().gla_decode_scalar if scalar_gate else lib().gla_decode
+    _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(o), _stream(stream)))
 
 
 def gla_decode(q, k, v, g, state, stream=None) -> torch.Tensor:
@@ -537,6 +548,36 @@ def gla_decode(q, k, v, g, state, stream=None) -> torch.Tensor:
     _need(state, "state", (B, H, K, V), torch.float32, dev)
     o = torch.empty(B, T, H, V, dtype=dt, device=dev)
     gla_decode_into(q, k, v, g, state, o, stream)
+    return o
+
+
+def gla_decode_scalar(q, k, v, g, state, stream=None) -> torch.Tensor:
+    """gla_decode with one log gate per token and head, g [B,T,H]."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H)),
+                         ("v", v, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    if state is None:
+        raise ValueError("state is required (it is read and updated in place)")
+    _need(state, "state", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    gla_decode_into(q, k, v, g, state, o, stream, scalar_gate=True)
+    return o
+
+
+def gla_decode_general(q, k, v, g, h, state, stream=None) -> torch.Tensor:
+    """gla_decode with the general gate exp(g)^T exp(h); h [B,T,H,V] like v."""
+    B, T, H, K, V = _dims(q, v)
+    dev, dt = q.device, q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("h", h, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    if state is None:
+        raise ValueError("state is required (it is read and updated in place)")
+    _need(state, "state", (B, H, K, V), torch.float32, dev)
+    o = torch.empty(B, T, H, V, dtype=dt, device=dev)
+    gla_decode_into(q, k, v, g, state, o, stream, h=h)
     return o
 
 

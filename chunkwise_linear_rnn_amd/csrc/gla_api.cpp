@@ -1299,17 +1299,23 @@ gla_status_t gla_bwd_scalar(const gla_shape_t* shape, const void* q, const void*
     return bwd_impl(shape, q, k, v, g, s0, d_o, dht, dq, dk, dv, dg, ds0, workspace, workspace_bytes, stream, true);
 }
 
-gla_status_t gla_decode(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
-                        float* state, void* o, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gate: 0 per key column, 1 one per token, 2 per key column and per value column (h)
+gla_status_t decode_impl(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                         const void* h, float* state, void* o, void* stream, int gate) {
     g_detail.clear();
     gla::Shape s;
     gla_status_t st = check_decode_shape(shape, &s);
     if (st != GLA_OK) return st;
     if (s.B * s.H == 0 || s.T == 0) return GLA_OK;
     if (!q || !k || !v || !g || !state || !o) return fail(GLA_ERR_NULL, "q, k, v, g, state and o are required");
-    const void* ptrs[] = {q, k, v, g, state, o};
-    const char* names[] = {"q", "k", "v", "g", "state", "o"};
-    for (int i = 0; i < 6; ++i)
+    if (gate == 2 && !h) return fail(GLA_ERR_NULL, "h is required");
+    const void* ptrs[] = {q, k, v, g, state, o, h};
+    const char* names[] = {"q", "k", "v", "g", "state", "o", "h"};
+    for (int i = 0; i < 7; ++i)
         if (!aligned16(ptrs[i])) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     gla::DecodeLaunch a{};
     a.bf16 = s.bf16;
@@ -1318,13 +1324,33 @@ gla_status_t gla_decode(const gla_shape_t* shape, const void* q, const void* k, 
     a.T = (int)s.T;
     a.H = (int)s.H;
     a.BH = s.B * s.H;
-    a.q = q; a.k = k; a.v = v; a.g = g;
+    a.gate = gate;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.h = h;
     a.state = state;
     a.o = o;
     a.stream = reinterpret_cast<hipStream_t>(stream);
     const hipError_t err = gla::launch_decode(a);
     if (err != hipSuccess) return fail(GLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gla_status_t gla_decode(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                        float* state, void* o, void* stream) {
+    return decode_impl(shape, q, k, v, g, nullptr, state, o, stream, 0);
+}
+
+gla_status_t gla_decode_scalar(const gla_shape_t* shape, const void* q, const void* k, const void* v, const void* g,
+                               float* state, void* o, void* stream) {
+    return decode_impl(shape, q, k, v, g, nullptr, state, o, stream, 1);
+}
+
+gla_status_t gla_decode_general(const gla_shape_t* shape, const void* q, const void* k, const void* v,
+                                const void* g, const void* h, float* state, void* o, void* stream) {
+    return decode_impl(shape, q, k, v, g, h, state, o, stream, 2);
 }
 
 gla_status_t gla_out_gate(const gla_shape_t* shape, const void* o, const void* z, const float* ln_w,

@@ -71,7 +71,8 @@ struct DecodeLaunch {
     bool bf16;
     int K, V, T, H;
     long BH;
-    const void *q, *k, *v, *g;
+    int gate;  // 0: g per key column [B,T,H,K]; 1: one g per token [B,T,H]; 2: g per key column and h per value column
+    const void *q, *k, *v, *g, *h;
     float* state;  // [BH][K][V] fp32, read and written in place
     void* o;
     hipStream_t stream;

@@ -373,6 +373,23 @@ gla_status_t gla_decode(const gla_shape_t* shape,
                         float* state, void* o, void* stream);
 
 /*
+ * gla_decode_scalar / gla_decode_general -- gla_decode for the other two gate
+ * forms of the chunked paths (same arguments, sizes, state contract and errors):
+ *   gla_decode_scalar  : g is [B,T,H] dtype, one log gate per token and head
+ *                        (alpha_t = exp(g_t) times the all-ones row, as for
+ *                        gla_fwd_scalar);
+ *   gla_decode_general : g is [B,T,H,K] and h is [B,T,H,V] dtype (required,
+ *                        16-byte aligned), S <- (exp(g_t)^T exp(h_t)) .* S +
+ *                        k_t^T v_t, as for gla_fwd_general.
+ */
+gla_status_t gla_decode_scalar(const gla_shape_t* shape,
+                               const void* q, const void* k, const void* v, const void* g,
+                               float* state, void* o, void* stream);
+gla_status_t gla_decode_general(const gla_shape_t* shape,
+                                const void* q, const void* k, const void* v, const void* g, const void* h,
+                                float* state, void* o, void* stream);
+
+/*
  * gla_out_gate -- the output epilogue of the multi-head GLA layer (Section 4.4,
  * "GLA Transformer"): every head's output row is normalised by LayerNorm on its
  * own, then multiplied elementwise by the Swish output gate r = Swish(z),

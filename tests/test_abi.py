@@ -128,6 +128,18 @@ def test_decode_validation_codes(L):
     assert _dec(L, _shape(T=5, reserved=1)) == ERR_UNSUPPORTED
     assert _dec(L, _shape(T=5), state=ctypes.c_void_p(0x10004)) == ERR_ALIGN
     assert b"state" in L.gla_last_error_detail()
+    # the scalar- and general-gate forms validate the same way; h is required
+    sc = lambda shape, **kw: L.gla_decode_scalar(ctypes.byref(shape), P, P, P, kw.get("g", P), kw.get("state", P),
+                                                 P, None)
+    ge = lambda shape, **kw: L.gla_decode_general(ctypes.byref(shape), P, P, P, P, kw.get("h", P),
+                                                  kw.get("state", P), P, None)
+    assert sc(_shape(T=0)) == OK and ge(_shape(T=0)) == OK
+    assert sc(_shape(T=5), g=None) == ERR_NULL
+    assert sc(_shape(T=5, K=96)) == ERR_UNSUPPORTED
+    assert ge(_shape(T=5), h=None) == ERR_NULL
+    assert ge(_shape(T=5), h=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    assert b"h" in L.gla_last_error_detail()
+    assert ge(_shape(T=5, V=1024)) == ERR_UNSUPPORTED
 
 
 def _gate(L, shape, o=P, z=P, w=P, b=None, eps=1e-5, y=P):

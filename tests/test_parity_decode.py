@@ -85,3 +85,60 @@ def test_decode_empty_is_a_no_op():
     torch.cuda.synchronize()
     assert o.shape == (2, 0, 2, 64)
     assert torch.equal(state, before)
+
+
+@pytest.mark.parametrize("B,H,T,K,V,dtype", [
+    (2, 3, 5, 64, 128, "fp32"),
+    (1, 2, 70, 128, 256, "bf16"),      # longer than a chunk, not a multiple of it
+    (1, 2, 4, 512, 128, "bf16"),
+])
+def test_decode_scalar_gate_matches_oracle(B, H, T, K, V, dtype):
+    # one log gate per token and head, against the oracle's scalar-gate recurrence
+    w = gi.custom(B, H, T, K, V, dtype=dtype, gate="scalar", s0="normal0.1", backward=False, seed=320 + T + K)
+    inp = gi.make_inputs(w)
+    note("decode parity (scalar gate): B=%d H=%d T=%d K=%d V=%d %s" % (B, H, T, K, V, dtype))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    state = d["s0"].clone()
+    o = gla.gla_decode_scalar(d["q"], d["k"], d["v"], d["g"], state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gla_fwd_scalar(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(inp["g"]),
+                                         to_np(inp["s0"]))
+    eo, es = rel_l2(to_np(o), o_ref), rel_l2(to_np(state), s_ref)
+    tol = TOL[w.torch_dtype]
+    note("  rel-L2 o=%.3e S_T=%.3e (tol %.0e)" % (eo, es, tol))
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+@pytest.mark.parametrize("B,H,T,K,V,dtype", [
+    (2, 3, 5, 64, 128, "fp32"),
+    (1, 2, 70, 128, 256, "bf16"),
+    (1, 1, 3, 256, 512, "bf16"),
+])
+def test_decode_general_gate_matches_oracle(B, H, T, K, V, dtype):
+    # the outer-product gate exp(g)^T exp(h), against the oracle's general recurrence
+    w = gi.custom(B, H, T, K, V, dtype=dtype, gate="lowrank", s0="normal0.1", backward=False, seed=340 + T + K)
+    inp = gi.make_inputs(w)
+    h = gi.make_value_gate(B, T, H, V, dtype=dtype, seed=350 + T)
+    note("decode parity (general gate): B=%d H=%d T=%d K=%d V=%d %s" % (B, H, T, K, V, dtype))
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    state = d["s0"].clone()
+    o = gla.gla_decode_general(d["q"], d["k"], d["v"], d["g"], h.to(DEV), state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gla_fwd_general(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(inp["g"]),
+                                          to_np(h), to_np(inp["s0"]))
+    eo, es = rel_l2(to_np(o), o_ref), rel_l2(to_np(state), s_ref)
+    tol = TOL[w.torch_dtype]
+    note("  rel-L2 o=%.3e S_T=%.3e (tol %.0e)" % (eo, es, tol))
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+def test_decode_general_zero_value_gate_is_gla_decode():
+    # h = 0 (beta = 1) gives the key-side recurrence exactly (the same fp32 arithmetic)
+    w, inp = _inputs(1, 2, 9, 128, 128, "bf16", "lowrank", seed=361)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    h = torch.zeros(1, 9, 2, 128, dtype=torch.bfloat16, device=DEV)
+    s_a, s_b = d["s0"].clone(), d["s0"].clone()
+    o_a = gla.gla_decode(d["q"], d["k"], d["v"], d["g"], s_a)
+    o_b = gla.gla_decode_general(d["q"], d["k"], d["v"], d["g"], h, s_b)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(s_a, s_b)
