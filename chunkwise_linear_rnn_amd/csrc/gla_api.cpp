@@ -499,9 +499,11 @@ gla_status_t fwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
     if (!general_k_ok(s.K))
         return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes K = 64, 128, 256 or 512 (got %lld)", (long long)s.K);
-    if (want_ckpt && ((s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256)))
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate checkpoint takes K and V in {128, 256} (got K=%lld V=%lld)",
-                    (long long)s.K, (long long)s.V);
+    // shapes without a checkpoint (K or V outside {128, 256}, or empty): the plain forward
+    if (want_ckpt && general_ckpt_bytes(s) == 0) {
+        want_ckpt = false;
+        ckpt = nullptr;
+    }
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !o)) return fail(GLA_ERR_NULL, "q, k, v, g, h and o are required");
     if (want_ckpt && !empty && !ckpt)
@@ -803,9 +805,16 @@ gla_status_t bwd_general_impl(const gla_shape_t* shape, const void* q, const voi
     gla_status_t st = check_shape(shape, &s, true);
     if (st != GLA_OK) return st;
     if (!s.bf16) return fail(GLA_ERR_UNSUPPORTED, "the general-gate path takes bf16 inputs");
-    if (want_ckpt ? (s.K != 128 && s.K != 256) || (s.V != 128 && s.V != 256) : !general_bwd_kv_ok(s.K, s.V))
-        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {%s} (got K=%lld V=%lld)",
-                    want_ckpt ? "128, 256" : "64, 128, 256, 512", (long long)s.K, (long long)s.V);
+    // shapes without a checkpoint (K or V outside {128, 256}, or empty): the plain
+    // backward, which recomputes the forward (o and ckpt are not read)
+    if (want_ckpt && general_ckpt_bytes(s) == 0) {
+        want_ckpt = false;
+        o = nullptr;
+        ckpt = nullptr;
+    }
+    if (!general_bwd_kv_ok(s.K, s.V))
+        return fail(GLA_ERR_UNSUPPORTED, "the general-gate backward takes K and V in {64, 128, 256, 512} (got K=%lld "
+                    "V=%lld)", (long long)s.K, (long long)s.V);
     const bool empty = s.B * s.H == 0 || s.T == 0;
     if (!empty && (!q || !k || !v || !g || !h || !d_o || !dq || !dk || !dv || !dg || !dh))
         return fail(GLA_ERR_NULL, "q, k, v, g, h, d_o, dq, dk, dv, dg and dh are required");

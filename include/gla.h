@@ -329,18 +329,19 @@ size_t gla_bwd_general_workspace_size(const gla_shape_t* shape);
  * forward's o and runs no forward.
  *   gla_general_ckpt_size(shape) : bytes of the checkpoint, the states
  *     [B,H,T/64,K,V] bf16 (entry 0 of each head is not used), then S_T
- *     [B,H,K,V] fp32 at a 256-byte aligned offset; 0 for an empty, invalid or
- *     unsupported shape (bf16 with K and V in {128, 256}).
+ *     [B,H,K,V] fp32 at a 256-byte aligned offset; 0 for an empty or invalid
+ *     shape and for one without a checkpoint (K or V outside {128, 256}): both
+ *     calls then behave exactly like gla_fwd_general / gla_bwd_general, and
+ *     ckpt (and the backward's o) may be NULL.
  *   gla_fwd_general_ckpt : gla_fwd_general (same arguments, results and
- *     workspace) for bf16 with K and V in {128, 256}, plus writes ckpt (device,
+ *     workspace), plus, for bf16 with K and V in {128, 256}, writes ckpt (device,
  *     16-byte aligned, required unless the shape is empty).
  *   gla_bwd_general_ckpt : gla_bwd_general (same arguments, results and
  *     workspace), plus reads o and ckpt, which must hold what
  *     gla_fwd_general_ckpt returned for the same shape, q, k, v, g, h and s0,
  *     unmodified since (not checked: other contents give wrong gradients).
- * Errors: as gla_fwd_general / gla_bwd_general; GLA_ERR_UNSUPPORTED for K or V
- * outside {128, 256}, GLA_ERR_NULL for a NULL o or ckpt on a
- * non-empty shape, GLA_ERR_ALIGN for a misaligned one.
+ * Errors: as gla_fwd_general / gla_bwd_general; GLA_ERR_NULL for a NULL o or
+ * ckpt on a shape with a checkpoint, GLA_ERR_ALIGN for a misaligned one.
  */
 size_t gla_general_ckpt_size(const gla_shape_t* shape);
 gla_status_t gla_fwd_general_ckpt(const gla_shape_t* shape,

@@ -407,9 +407,15 @@ def test_general_ckpt_entry_points_validate(L):
     assert bwd(s, ck=ctypes.c_void_p(0x10008)) == ERR_ALIGN
     assert bwd(s, o=ctypes.c_void_p(0x10008)) == ERR_ALIGN
     assert fwd(_shape(T=100)) == ERR_SHAPE
-    assert fwd(_shape(K=128, V=512, T=8192)) == ERR_UNSUPPORTED   # gla_fwd_general takes it; the pair does not
-    assert bwd(_shape(K=128, V=512, T=8192)) == ERR_UNSUPPORTED
+    # a shape without a checkpoint runs the plain pair: ckpt and o may be NULL, and the
+    # plain calls' own checks apply (o is the forward's output; the backward's workspace)
+    nock = _shape(K=128, V=512, T=8192)
+    assert fwd(nock, ck=None, o=None) == ERR_NULL
+    assert b"o" in L.gla_last_error_detail()
+    assert L.gla_bwd_general_ckpt(ctypes.byref(nock), P, P, P, P, P, None, None, None, P, None, P, P, P, P, P, None,
+                                  None, 1 << 40, None) == ERR_WORKSPACE
     assert fwd(_shape(dtype=gla.GLA_DTYPE_FP32)) == ERR_UNSUPPORTED
+    assert fwd(_shape(K=1024, V=128)) == ERR_UNSUPPORTED
     empty = _shape(T=0, K=128, V=128)
     assert fwd(empty, ck=None, o=None) == OK              # nothing to compute: no checkpoint needed
     assert bwd(empty, ck=None, o=None) == OK

@@ -127,3 +127,21 @@ def test_bwd_general_ckpt_pair(B, H, T, K, V, s0, dht):
         assert torch.equal(a, b), name
     if T == 64:
         _check(w, inp, h, _heads(B, H))
+
+
+def test_general_ckpt_pair_without_checkpoint_is_the_plain_pair():
+    # V = 512 (value slices) has no checkpoint: the pair runs gla_fwd_general /
+    # gla_bwd_general, bit for bit
+    B, H, T, K, V = 1, 2, 64 * 3, 128, 512
+    assert gla.gla_general_ckpt_size(B, T, H, K, V, torch.bfloat16) == 0
+    w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=True, seed=1720)
+    d = gi.make_inputs(w, device=DEV, dht=True)
+    h = gi.make_value_gate(B, T, H, V, seed=1721).to(DEV)
+    o, sf, ck = gla.gla_fwd_general_ckpt(d["q"], d["k"], d["v"], d["g"], h, d["s0"])
+    o_ref, sf_ref = gla.gla_fwd_general(d["q"], d["k"], d["v"], d["g"], h, d["s0"])
+    a = gla.gla_bwd_general_ckpt(d["q"], d["k"], d["v"], d["g"], h, d["do"], o, ck, d["s0"], d["dht"])
+    b = gla.gla_bwd_general(d["q"], d["k"], d["v"], d["g"], h, d["do"], d["s0"], d["dht"])
+    torch.cuda.synchronize()
+    assert ck is None
+    assert torch.equal(o, o_ref) and torch.equal(sf, sf_ref)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
