@@ -29,7 +29,10 @@ def _shape(B, T, H, K, V, dtype=gla.GLA_DTYPE_BF16):
 SHAPES = [(1, 256, 1, 64, 64, gla.GLA_DTYPE_FP32), (4, 1024, 8, 64, 64, gla.GLA_DTYPE_BF16),
           (8, 2048, 4, 128, 256, gla.GLA_DTYPE_BF16), (2, 8192, 4, 128, 256, gla.GLA_DTYPE_BF16),
           (2, 8192, 4, 256, 512, gla.GLA_DTYPE_BF16), (4, 16384, 16, 128, 128, gla.GLA_DTYPE_BF16),
-          (2, 64 * 21, 16, 128, 256, gla.GLA_DTYPE_BF16), (1, 64, 1, 128, 128, gla.GLA_DTYPE_FP32)]
+          (2, 64 * 21, 16, 128, 256, gla.GLA_DTYPE_BF16), (1, 64, 1, 128, 128, gla.GLA_DTYPE_FP32),
+          # heads run as key and value slices, or (general gates) padded to 128
+          (1, 256, 2, 512, 512, gla.GLA_DTYPE_BF16), (1, 256, 2, 512, 256, gla.GLA_DTYPE_FP32),
+          (1, 128, 2, 256, 512, gla.GLA_DTYPE_FP32), (1, 320, 2, 64, 512, gla.GLA_DTYPE_BF16)]
 
 
 @pytest.mark.parametrize("B,T,H,K,V,dt", SHAPES)
@@ -38,19 +41,24 @@ def test_every_entry_point_plans_to_a_launch(B, T, H, K, V, dt):
     s = _shape(B, T, H, K, V, dt)
     big = 1 << 40
     assert L.gla_fwd(ctypes.byref(s), P, P, P, P, P, P, P, P, big, None) == ERR_HIP
-    if V <= 256 or dt == gla.GLA_DTYPE_BF16:
-        assert L.gla_bwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
-        ck = P if L.gla_ckpt_size(ctypes.byref(s)) else None
-        assert L.gla_fwd_ckpt(ctypes.byref(s), P, P, P, P, P, P, P, ck, P, big, None) == ERR_HIP
-        assert L.gla_bwd_ckpt(ctypes.byref(s), P, P, P, P, P, ck, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
+    assert L.gla_bwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
+    ck = P if L.gla_ckpt_size(ctypes.byref(s)) else None
+    for f, b in ((L.gla_fwd_ckpt, L.gla_bwd_ckpt), (L.gla_fwd_scalar_ckpt, L.gla_bwd_scalar_ckpt)):
+        assert f(ctypes.byref(s), P, P, P, P, P, P, P, ck, P, big, None) == ERR_HIP
+        assert b(ctypes.byref(s), P, P, P, P, P, ck, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
+    assert L.gla_fwd_scalar(ctypes.byref(s), P, P, P, P, P, P, P, P, big, None) == ERR_HIP
+    assert L.gla_bwd_scalar(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
     assert L.gla_decode(ctypes.byref(s), P, P, P, P, P, P, None) == ERR_HIP
+    assert L.gla_decode_scalar(ctypes.byref(s), P, P, P, P, P, P, None) == ERR_HIP
+    assert L.gla_decode_general(ctypes.byref(s), P, P, P, P, P, P, P, None) == ERR_HIP
     assert L.gla_out_gate(ctypes.byref(s), P, P, P, P, ctypes.c_float(1e-5), P, None) == ERR_HIP
     if dt == gla.GLA_DTYPE_BF16:
-        assert L.gla_fwd_scalar(ctypes.byref(s), P, P, P, P, P, P, P, P, big, None) == ERR_HIP
-        if K in (128, 256):
-            assert L.gla_fwd_general(ctypes.byref(s), P, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
-        if K in (128, 256) and V in (128, 256):
-            assert L.gla_bwd_general(ctypes.byref(s), *([P] * 15), big, None) == ERR_HIP
+        assert L.gla_fwd_general(ctypes.byref(s), P, P, P, P, P, P, P, P, P, big, None) == ERR_HIP
+        assert L.gla_bwd_general(ctypes.byref(s), *([P] * 15), big, None) == ERR_HIP
+        gck = P if L.gla_general_ckpt_size(ctypes.byref(s)) else None
+        assert L.gla_fwd_general_ckpt(ctypes.byref(s), P, P, P, P, P, P, P, P, gck, P, big, None) == ERR_HIP
+        assert L.gla_bwd_general_ckpt(ctypes.byref(s), P, P, P, P, P, P, P, gck, P, P, *([P] * 6), P, big,
+                                      None) == ERR_HIP
     if L.gla_fwd_workspace_size(ctypes.byref(s)) <= 32 << 20:
         assert L.gla_fwd_noalloc(ctypes.byref(s), P, P, P, P, P, P, P, None) == ERR_HIP
 
