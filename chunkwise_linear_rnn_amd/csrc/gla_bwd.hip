@@ -184,9 +184,9 @@ gla_seg_combine_bwd(const float* __restrict__ s0, const float* __restrict__ dht,
 }
 
 // The same with each element group's segments split between two threads
-// (P <= 2 * kSplitMax; threads t and t + 128 share 4 elements; the grid covers
+// (P <= 2 * NMAX; threads t and t + 128 share 4 elements; the grid covers
 // K*V exactly, no thread may leave before the exchange barrier).
-template <typename ST>
+template <int NMAX, typename ST>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_bwd_split(const float* __restrict__ s0, const float* __restrict__ dht, ST* __restrict__ ws_state,
                           ST* __restrict__ ws_dstate, const float* __restrict__ ws_gate, int K, int V, int P,
@@ -199,10 +199,10 @@ gla_seg_combine_bwd_split(const float* __restrict__ s0, const float* __restrict_
     const int i = (int)(e / V);
     const float* gt = ws_gate + bh * PH * (long)K + i;
     if (blockIdx.z + z0 == 0)
-        combine_row_split<false>(ws_state + bh * PH * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr, part,
+        combine_row_split<NMAX, false>(ws_state + bh * PH * KV + e, gt, KV, K, P, s0 ? s0 + bh * KV + e : nullptr, part,
                                  &carry[slot]);
     else
-        combine_row_split<true>(ws_dstate + bh * PH * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr, part,
+        combine_row_split<NMAX, true>(ws_dstate + bh * PH * KV + e, gt, KV, K, P, dht ? dht + bh * KV + e : nullptr, part,
                                 &carry[slot]);
 }
 
@@ -1797,9 +1797,19 @@ static void launch_combine_bwd(const BwdLaunch& a, int PS) {
     const int z0 = a.ckpt ? 1 : 0;
     // the combine walks the PS entries that hold chunks, at a stride of dsub*P per head
     if (PS <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
-        GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd_split<T>,
-                   dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
-                   a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, a.K, a.V, PS, z0, a.dsub * a.P);
+        const int nm = split_nmax(PS);
+        if (nm == 4)
+            GLA_LAUNCH("combine_bwd", (gla_seg_combine_bwd_split<4, T>),
+                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
+                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, a.K, a.V, PS, z0, a.dsub * a.P);
+        else if (nm == 8)
+            GLA_LAUNCH("combine_bwd", (gla_seg_combine_bwd_split<8, T>),
+                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
+                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, a.K, a.V, PS, z0, a.dsub * a.P);
+        else
+            GLA_LAUNCH("combine_bwd", (gla_seg_combine_bwd_split<16, T>),
+                       dim3((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH, nz), dim3(256), a.stream, a.s0,
+                       a.dht, (T*)a.ws_state, (T*)a.ws_dstate, a.ws_gate, a.K, a.V, PS, z0, a.dsub * a.P);
     } else {
         GLA_LAUNCH("combine_bwd", gla_seg_combine_bwd<T>,
                    dim3((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH, nz), dim3(256), a.stream,

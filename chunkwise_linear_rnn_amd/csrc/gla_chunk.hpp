@@ -366,38 +366,43 @@ __device__ __forceinline__ void combine_row(ST* st, const float* gt, long KV, lo
     if constexpr (STO) *reinterpret_cast<f32x4*>(sT) = cur;
 }
 
-// The same recurrence split between two threads, for P <= 2 * kSplitMax: part
+// The same recurrence split between two threads, for P <= 2 * NMAX: part
 // 0 walks the first ceil(P/2) segments (in walking order) from `init`, part 1
 // the rest from zero, keeping its outputs and the running product of its gates
 // in registers.  Part 0's value after its last segment (the input of part 1's
 // first) goes through `carry` (LDS, one slot per element group), and part 1
 // adds it, decayed by its gate product, to each of its outputs.  Both parts of
 // a slot must be in the same workgroup; every thread must call this (barrier).
+// NMAX (4, 8 or 16, the launcher picks the smallest that holds ceil(P/2))
+// bounds the segments per thread: each thread issues NMAX loads, the ones past
+// its n repeating its last segment's address.
 constexpr int kSplitMax = 16;
-template <bool REV, typename ST, bool CKO = false, bool STO = false>
+__host__ __device__ constexpr int split_nmax(int P) { return (P + 1) / 2 <= 4 ? 4 : ((P + 1) / 2 <= 8 ? 8 : 16); }
+template <int NMAX, bool REV, typename ST, bool CKO = false, bool STO = false>
 __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long KV, long K, int P, const float* init,
                                                   int part, f32x4* carry, ST* ck = nullptr, int ck_r = 1,
                                                   float* sT = nullptr) {
+    static_assert(NMAX <= kSplitMax, "segments per thread");
     static_assert(!((CKO || STO) && REV), "the checkpoint and S_T are written by the forward combine");
     constexpr int CE = kCombineVec;
     using VT = combine_vec_t<ST>;
     const int h = (P + 1) / 2;
-    const int j0 = part ? h : 0, n = part ? P - h : h;  // 1 <= n <= kSplitMax
-    VT a[kSplitMax];
-    float gm[kSplitMax];
+    const int j0 = part ? h : 0, n = part ? P - h : h;  // 1 <= n <= NMAX
+    VT a[NMAX];
+    float gm[NMAX];
 #pragma unroll
-    for (int u = 0; u < kSplitMax; ++u) {
+    for (int u = 0; u < NMAX; ++u) {
         const int j = j0 + (u < n ? u : n - 1);
         const int p = REV ? P - 1 - j : j;
         a[u] = *reinterpret_cast<const VT*>(st + p * KV);
         gm[u] = gt[p * K];
     }
     f32x4 cur = (part == 0 && init) ? *reinterpret_cast<const f32x4*>(init) : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 loc[kSplitMax], fin = cur;
-    float mul[kSplitMax];
+    f32x4 loc[NMAX], fin = cur;
+    float mul[NMAX];
     float m = 1.f, mfin = 1.f;
 #pragma unroll
-    for (int u = 0; u < kSplitMax; ++u) {
+    for (int u = 0; u < NMAX; ++u) {
         const int j = j0 + u;
         const int p = REV ? P - 1 - j : j;
         const bool feeds = u < n && (REV ? p >= 1 : (STO || p + 1 < P));
@@ -415,7 +420,7 @@ __device__ __forceinline__ void combine_row_split(ST* st, const float* gt, long 
     const f32x4 cin = part ? *carry : f32x4{0.f, 0.f, 0.f, 0.f};
     int ckm = CKO ? j0 / ck_r : 0, rem = CKO ? j0 % ck_r : 0;  // as in combine_row (CKO: REV is false)
 #pragma unroll
-    for (int u = 0; u < kSplitMax; ++u) {
+    for (int u = 0; u < NMAX; ++u) {
         if (u < n) {
             const int j = j0 + u;
             const int p = REV ? P - 1 - j : j;

@@ -48,10 +48,10 @@ gla_seg_combine_fwd(const float* __restrict__ s0, ST* __restrict__ ws_state, con
 }
 
 // The same with each element group's segments split between two threads
-// (P <= 2 * kSplitMax): threads t and t + 128 of a workgroup share 4 elements.
+// (P <= 2 * NMAX): threads t and t + 128 of a workgroup share 4 elements.
 // The grid covers K*V exactly (K*V / (128 * kCombineVec) workgroups per head):
 // no thread may leave before the exchange barrier.
-template <typename ST, bool CKO = false, bool STO = false>
+template <int NMAX, typename ST, bool CKO = false, bool STO = false>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_fwd_split(const float* __restrict__ s0, ST* __restrict__ ws_state, const float* __restrict__ ws_gate,
                           int K, int V, int P, ST* __restrict__ ck = nullptr, int ck_r = 1, int ck_P = 1,
@@ -62,7 +62,7 @@ gla_seg_combine_fwd_split(const float* __restrict__ s0, ST* __restrict__ ws_stat
     const long e = ((long)blockIdx.x * 128 + slot) * kCombineVec;
     const long bh = blockIdx.y;
     const int i = (int)(e / V);
-    combine_row_split<false, ST, CKO, STO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
+    combine_row_split<NMAX, false, ST, CKO, STO>(ws_state + bh * P * KV + e, ws_gate + bh * P * (long)K + i, KV, K, P,
                                            s0 ? s0 + bh * KV + e : nullptr, part, &carry[slot],
                                            CKO ? ck + bh * ck_P * KV + e : nullptr, ck_r,
                                            STO ? s_final + bh * KV + e : nullptr);
@@ -627,8 +627,16 @@ static void launch_combine_fwd_v(const FwdLaunch& a, int KD) {
     const int r = CKO ? a.ck_len / a.seg_len : 1;
     if (a.P <= 2 * kSplitMax && KV % (128 * kCombineVec) == 0) {
         dim3 g2((unsigned)(KV / (128 * kCombineVec)), (unsigned)a.BH);
-        GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
-                   (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P, a.s_final);
+        const int nm = split_nmax(a.P);
+        if (nm == 4)
+            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<4, T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P, a.s_final);
+        else if (nm == 8)
+            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<8, T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P, a.s_final);
+        else
+            GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd_split<16, T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, a.ws_gate, KD, a.V, a.P, (T*)a.ckpt, r, a.ck_P, a.s_final);
     } else {
         dim3 g2((unsigned)((KV / kCombineVec + 255) / 256), (unsigned)a.BH);
         GLA_LAUNCH("combine_fwd", (gla_seg_combine_fwd<T, CKO, STO>), g2, dim3(256), a.stream, a.s0,
