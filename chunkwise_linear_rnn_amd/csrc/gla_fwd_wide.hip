@@ -49,7 +49,12 @@ static hipError_t launch_fwd_wide_t(const FwdLaunch& a) {
 
 // Segment combine under general gates: out[0] = S_0, out[p+1] = exp2(GA_p[i] +
 // GB_p[j]) out[p] + in[p], with GA/GB the segment's log2 decays of key row i
-// and value column j.  One thread per 4 adjacent elements of a state row.
+// and value column j.  One thread per 4 adjacent elements of a state row.  The
+// outputs overwrite the inputs in place, so the loop form (any P) reads each
+// segment only after storing the one before; for P <= NMAX every input is read
+// first (NMAX loads per thread, the ones past P - 1 repeating segment 0), then
+// the chain runs from registers.
+template <int NMAX>
 __global__ void __launch_bounds__(256)
 gla_seg_combine_fwd_general(const float* __restrict__ s0, bf16* __restrict__ ws_state,
                             const float* __restrict__ ws_gate, const float* __restrict__ ws_gateb, int K, int V,
@@ -64,6 +69,33 @@ gla_seg_combine_fwd_general(const float* __restrict__ s0, bf16* __restrict__ ws_
     const float* ga = ws_gate + bh * P * (long)K + i;
     const float* gbv = ws_gateb + bh * P * (long)V + j;
     f32x4 cur = s0 ? *reinterpret_cast<const f32x4*>(s0 + bh * KV + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NMAX > 0) {
+        VT in[NMAX];
+        float gr[NMAX];
+        f32x4 gcol[NMAX];
+#pragma unroll
+        for (int u = 0; u < NMAX; ++u) {
+            const int p = u + 1 < P ? u : 0;  // segment P-1 has no state of its own
+            in[u] = *reinterpret_cast<const VT*>(st + p * KV);
+            gr[u] = ga[(long)p * K];
+            gcol[u] = *reinterpret_cast<const f32x4*>(gbv + (long)p * V);
+        }
+#pragma unroll
+        for (int u = 0; u < NMAX; ++u) {
+            if (u < P) {
+                VT o;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[c] = Elem<bf16>::from_f(cur[c]);
+                *reinterpret_cast<VT*>(st + u * KV) = o;
+                if (u + 1 < P) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        cur[c] = exp2f(gr[u] + gcol[u][c]) * cur[c] + Elem<bf16>::to_f(in[u][c]);
+                }
+            }
+        }
+        return;
+    }
     for (int p = 0; p < P; ++p) {
         // segment P-1 has no state of its own: only its initial state is written
         const bool feeds = p + 1 < P;
@@ -126,9 +158,19 @@ static hipError_t launch_fwd_general_kv(const FwdLaunch& a) {
                    (const T*)a.v, (const T*)nullptr, (const float*)nullptr, (T*)nullptr, (float*)nullptr,
                    (T*)a.ws_state, a.ws_gate, a.T, a.H, a.V, a.N, a.P, a.seg_len, nseg, (int)a.BH, a.ws_gateb);
         const long KV = (long)KD * a.V;
-        GLA_LAUNCH("combine_fwd_general", gla_seg_combine_fwd_general, dim3((unsigned)((KV / 4 + 255) / 256), (unsigned)a.BH),
-                   dim3(256), a.stream, a.s0, (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD,
-                   a.V, a.P);
+        const dim3 gc((unsigned)((KV / 4 + 255) / 256), (unsigned)a.BH);
+        if (a.P <= 8)
+            GLA_LAUNCH("combine_fwd_general", gla_seg_combine_fwd_general<8>, gc, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD, a.V, a.P);
+        else if (a.P <= 16)
+            GLA_LAUNCH("combine_fwd_general", gla_seg_combine_fwd_general<16>, gc, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD, a.V, a.P);
+        else if (a.P <= 32)
+            GLA_LAUNCH("combine_fwd_general", gla_seg_combine_fwd_general<32>, gc, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD, a.V, a.P);
+        else
+            GLA_LAUNCH("combine_fwd_general", gla_seg_combine_fwd_general<0>, gc, dim3(256), a.stream, a.s0,
+                       (T*)a.ws_state, (const float*)a.ws_gate, (const float*)a.ws_gateb, KD, a.V, a.P);
     }
     if (a.ws_hs && a.rev)
         GLA_LAUNCH("fwd_general_walk_hs", (gla_fwd_wide_walk<T, KD, BV, true, true, true, true>), gw, dim3(512),
