@@ -45,10 +45,12 @@ def _heads(B, H):
 
 @pytest.mark.parametrize("B,H,T,K,V,s0", [
     (1, 1, 64, 128, 64, "normal0.1"),      # one chunk, one value block
-    (1, 2, 64 * 9, 256, 256, "normal0.1"),  # one chunk per segment, four value blocks
-    (4, 4, 64 * 12, 128, 128, "none"),      # segments of two chunks
+    (1, 2, 64 * 9, 256, 256, "normal0.1"),  # one chunk per segment, two value blocks
+    (4, 4, 64 * 12, 128, 128, "none"),      # 12 segments of one chunk
     (2, 2, 64 * 13, 128, 256, "normal0.1"),  # one chunk per segment, 13 segments
-    (2, 8, 64 * 21, 256, 512, "normal0.1"),  # two segments of 11 and 10 chunks, eight value blocks
+    (2, 8, 64 * 21, 256, 512, "normal0.1"),  # 4 segments (6, 6, 6 and 3 chunks), four value blocks
+    (1, 2, 64 * 20, 256, 256, "none"),      # 20 segments: the combine holds up to 32 segments in registers
+    (1, 1, 64 * 40, 128, 128, "normal0.1"),  # 40 segments: the combine's loop for more than 32
 ])
 def test_fwd_general_heads(B, H, T, K, V, s0):
     w = gi.custom(B, H, T, K, V, dtype="bf16", gate="lowrank", s0=s0, backward=False, seed=1200 + T + V + K)
