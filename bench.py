@@ -178,7 +178,7 @@ def _is_lib(name: str) -> bool:
 def _kernel_base(mangled: str) -> str:
     """The kernel's function name inside namespace gla, e.g. gla_bwd_dq_pipe."""
     import re
-    m = re.search(r"3gla(\d+)", mangled)
+    m = re.search(r"3gla(?:12_GLOBAL__N_1)?(\d+)", mangled)  # also inside an anonymous namespace
     if m:
         n = int(m.group(1))
         return mangled[m.end():m.end() + n]
@@ -483,15 +483,21 @@ def decode_bench(args, torch, gla, gi):
     """gla_decode at serving shape: B sequences, one new token each per call.
 
     The state round-trips through HBM every call (fp32 read and write), so the
-    kernel is HBM-bound: algorithmic bytes per call = B*H*(8*K*V + e*(3K + 2V))."""
+    kernel is HBM-bound: algorithmic bytes per call = B*H*(8*K*V + e*(3K + 2V))
+    with a log gate per key column, e*(2K + 2V + 1) for the scalar gate and
+    e*(3K + 3V) with the value-side gate h of the general form."""
     B, H, K, V = 64, 4, 128, 256
-    w = gi.custom(B, H, 1, K, V, dtype="bf16", gate="lowrank", s0="normal0.1", backward=False, seed=6)
+    sg, gen = args.scalar_gate, args.general_gate
+    w = gi.custom(B, H, 1, K, V, dtype="bf16", gate="scalar" if sg else "lowrank", s0="normal0.1", backward=False,
+                  seed=6)
     cpu = gi.make_inputs(w)
+    if gen:
+        cpu["h"] = gi.make_value_gate(B, 1, H, V, seed=7)
     dev = "cuda:0"
     d = {k: (v.to(dev) if v is not None else None) for k, v in cpu.items()}
     state = d["s0"].clone()
     o = torch.empty(B, 1, H, V, dtype=torch.bfloat16, device=dev)
-    call = lambda: gla.gla_decode_into(d["q"], d["k"], d["v"], d["g"], state, o)
+    call = lambda: gla.gla_decode_into(d["q"], d["k"], d["v"], d["g"], state, o, h=d.get("h"), scalar_gate=sg)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -522,14 +528,15 @@ def decode_bench(args, torch, gla, gi):
     cold = sorted(a.elapsed_time(b_) for a, b_ in evs)
     cold_ms = cold[len(cold) // 2]
     del scrub
-    alg = B * H * (8 * K * V + 2 * (3 * K + 2 * V))
+    alg = B * H * (8 * K * V + 2 * ((2 * K + 2 * V + 1) if sg else (3 * K + 3 * V) if gen else (3 * K + 2 * V)))
+    form = " scalar gate [B,T,H]," if sg else " general gate (g and h [B,T,H,V])," if gen else ""
     achieved = alg / (cold_ms * 1e-3) / 1e9
     line = {"metric": "GLA decode tokens/sec (recurrent form, one token per sequence per call)",
             "value": B / (cold_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "calls": n, "ms_per_call": cold_ms,
             "timing": "cold: median call behind a 512 MiB read; warm: mean of back-to-back calls",
             "ms_per_call_warm": ms, "kernel_us_warm": kern_ms * 1e3, "warm_tokens_per_s": B / (ms * 1e-3),
             "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "decode: B=64 H=4 dk=128 dv=256 bf16, fp32 state, 1 token per call"},
+            "config": {"workload": "decode: B=64 H=4 dk=128 dv=256 bf16,%s fp32 state, 1 token per call" % form},
             "roofline": {"bound": "hbm", "kernel": "decode", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
                          "time": "cold call (HIP events around the single launch)"}}
@@ -539,8 +546,13 @@ def decode_bench(args, torch, gla, gi):
         t0 = time.perf_counter()
         reps = 0
         while time.perf_counter() - t0 < 2.0:
-            oracle.gla_fwd(*(cpu[x].to(torch.float64).numpy() for x in ("q", "k", "v", "g")),
-                           cpu["s0"].to(torch.float64).numpy())
+            f64 = lambda x: cpu[x].to(torch.float64).numpy()
+            if gen:
+                oracle.gla_fwd_general(*(f64(x) for x in ("q", "k", "v", "g", "h", "s0")))
+            elif sg:
+                oracle.gla_fwd_scalar(*(f64(x) for x in ("q", "k", "v", "g", "s0")))
+            else:
+                oracle.gla_fwd(*(f64(x) for x in ("q", "k", "v", "g", "s0")))
             reps += 1
         sec = (time.perf_counter() - t0) / reps
         line["cpu_baseline"] = {"value": B / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
@@ -747,7 +759,8 @@ def main():
                     help="skip measuring the box's attainable copy bandwidth and bf16 GEMM rate")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--decode", action="store_true",
-                    help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead")
+                    help="measure gla_decode (one token per call, B=64 H=4 dk=128 dv=256 bf16) instead; with "
+                         "--scalar-gate or --general-gate gla_decode_scalar or gla_decode_general")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time gla_fwd alone on --workload (also those without backward inputs)")
     ap.add_argument("--dims", default="",
