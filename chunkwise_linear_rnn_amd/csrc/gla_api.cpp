@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -15,6 +16,11 @@
 #include "gla_plan.hpp"
 
 namespace {
+
+// Size limits of the chunked entry points and of decode (see check_shape).
+constexpr int64_t kMaxHeads = (int64_t)1 << 20;
+constexpr int64_t kMaxTokenHeads = (int64_t)1 << 30;
+constexpr int64_t kMaxDecodeGroups = (int64_t)1 << 24;
 
 thread_local std::string g_detail;
 
@@ -62,10 +68,22 @@ gla_status_t check_shape(const gla_shape_t* s, gla::Shape* out, bool backward) {
         return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for %s %s", (long long)s->K,
                     (long long)s->V, bf16 ? "bf16" : "fp32", backward ? "backward" : "forward");
     if (s->T % 64 != 0) return fail(GLA_ERR_SHAPE, "T=%lld is not a multiple of the chunk 64", (long long)s->T);
-    // kernel index arithmetic: per-tensor element counts and the sizes passed as int
+    // kernel index arithmetic: sizes and a chunk's 64 rows of row stride H*D in
+    // int, grids of at most 2^32 work-items (B*H heads), workgroup indices over
+    // chunks and heads (B*H*T token-heads; a shape past that limit would not fit
+    // in device memory anyway)
     const int64_t lim = (int64_t)1 << 31;
-    if (s->T >= lim || s->H >= lim || s->B >= lim || s->B * s->H >= lim)
+    if (s->T >= lim || s->H >= lim || s->B >= lim)
         return fail(GLA_ERR_SHAPE, "size too large for this library");
+    if (s->B * s->H > kMaxHeads)
+        return fail(GLA_ERR_SHAPE, "size too large for this library: B*H=%lld heads (at most %lld)",
+                    (long long)(s->B * s->H), (long long)kMaxHeads);
+    if (s->B * s->H * s->T >= kMaxTokenHeads)
+        return fail(GLA_ERR_SHAPE, "size too large for this library: B*H*T=%lld token-heads (below %lld)",
+                    (long long)(s->B * s->H * s->T), (long long)kMaxTokenHeads);
+    if (s->H * std::max(s->K, s->V) * 64 >= lim)
+        return fail(GLA_ERR_SHAPE, "size too large for this library: H*max(K,V)=%lld (below %lld)",
+                    (long long)(s->H * std::max(s->K, s->V)), (long long)(lim / 64));
     out->B = s->B;
     out->T = s->T;
     out->H = s->H;
@@ -91,9 +109,11 @@ gla_status_t check_decode_shape(const gla_shape_t* s, gla::Shape* out) {
     if (!k_ok || !v_ok)
         return fail(GLA_ERR_UNSUPPORTED, "unsupported head dims K=%lld V=%lld for decode", (long long)s->K,
                     (long long)s->V);
+    // one 256-thread workgroup per head and 64 value columns: at most 2^32 work-items
     const int64_t lim = (int64_t)1 << 31;
-    if (s->T >= lim || s->H >= lim || s->B >= lim || s->B * s->H * (s->V / 64) >= lim)
-        return fail(GLA_ERR_SHAPE, "size too large for this library");
+    if (s->T >= lim || s->H >= lim || s->B >= lim || s->B * s->H * (s->V / 64) >= kMaxDecodeGroups)
+        return fail(GLA_ERR_SHAPE, "size too large for this library: B*H*V/64=%lld workgroups (below %lld)",
+                    (long long)(s->B * s->H * (s->V / 64)), (long long)kMaxDecodeGroups);
     out->B = s->B;
     out->T = s->T;
     out->H = s->H;

@@ -48,6 +48,11 @@
  *      16-bit K = 512 in two slices of 256, fp32 K = 256 and 512 in slices of
  *      128; the slices' outputs and dv add).  B, H >= 0 and T >= 0; B*H == 0 or T == 0
  *      is a valid no-op (s_final is then s0, or zero; ds0 is dht, or zero).
+ *  Size limits (GLA_ERR_SHAPE beyond them; the kernels index in 32 bits):
+ *      B*H <= 2^20 heads, B*H*T < 2^30 token-heads (larger inputs would not
+ *      fit in one GPU's memory), H*max(K, V) < 2^25 (a chunk's 64 rows of
+ *      row stride); decode: B*H*V/64 < 2^24; the output gate: B*H*T < 2^31
+ *      rows.
  */
 #ifndef GLA_H_
 #define GLA_H_
@@ -64,7 +69,8 @@ extern "C" {
 typedef enum {
     GLA_OK = 0,
     GLA_ERR_NULL = 1,        /* a required pointer is NULL                          */
-    GLA_ERR_SHAPE = 2,       /* negative size, or T not a multiple of the chunk     */
+    GLA_ERR_SHAPE = 2,       /* negative size, T not a multiple of the chunk, or a
+                                size past the limits above                          */
     GLA_ERR_UNSUPPORTED = 3, /* K, V, chunk or dtype outside the supported set      */
     GLA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
     GLA_ERR_WORKSPACE = 5,   /* workspace smaller than the *_workspace_size() value */

@@ -113,6 +113,24 @@ def _dec(L, shape, q=P, k=P, v=P, g=P, state=P, o=P):
     return L.gla_decode(ctypes.byref(shape) if shape is not None else None, q, k, v, g, state, o, None)
 
 
+def test_size_limits(L):
+    # past each documented limit the shape check rejects the call before
+    # anything else; just inside it the (pure) size functions accept the shape
+    ok = lambda sh: L.gla_bwd_workspace_size(ctypes.byref(sh)) > 0
+    assert _fwd(L, _shape(B=(1 << 20) + 1, H=1, T=64)) == ERR_SHAPE
+    assert b"heads" in L.gla_last_error_detail()
+    assert ok(_shape(B=1 << 20, H=1, T=64))
+    assert _fwd(L, _shape(B=1, H=1, T=1 << 30)) == ERR_SHAPE
+    assert b"token-heads" in L.gla_last_error_detail()
+    assert ok(_shape(B=1, H=1, T=(1 << 30) - 64))
+    assert _bwd(L, _shape(B=1, H=1 << 16, T=64, K=512, V=64)) == ERR_SHAPE
+    assert b"H*max(K,V)" in L.gla_last_error_detail()
+    assert ok(_shape(B=1, H=(1 << 16) - 1, T=64, K=512, V=64))
+    assert _dec(L, _shape(B=1 << 24, H=1, T=1, V=64)) == ERR_SHAPE
+    assert _dec(L, _shape(B=1 << 22, H=1, T=1, V=256)) == ERR_SHAPE
+    assert b"workgroups" in L.gla_last_error_detail()
+
+
 def test_decode_validation_codes(L):
     # the recurrent form takes any T (no chunk constraint) and needs the state
     assert _dec(L, None) == ERR_NULL
