@@ -479,6 +479,13 @@ def cpu_baseline(inputs, w, n_heads, scalar_gate=False):
     }
 
 
+def device_info(torch, dev):
+    """The GPU and software the line was measured on."""
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+
+
 def decode_bench(args, torch, gla, gi):
     """gla_decode at serving shape: B sequences, one new token each per call.
 
@@ -557,6 +564,7 @@ def decode_bench(args, torch, gla, gi):
         sec = (time.perf_counter() - t0) / reps
         line["cpu_baseline"] = {"value": B / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
                                 "kind": "oracle", "sample": "fp64 oracle, the full call (%d repetitions)" % reps}
+    line["device"] = device_info(torch, "cuda:0")
     print(json.dumps(line), flush=True)
 
 
@@ -622,6 +630,7 @@ def out_gate_bench(args, torch, gla, gi):
         line["cpu_baseline"] = {"value": rows / sec, "unit": "rows/s", "cores": 1, "kind": "oracle",
                                 "sample": "fp64 oracle forward + backward on %d of %d rows (%d repetitions)" % (
                                     rows, R, reps)}
+    line["device"] = device_info(torch, "cuda:0")
     print(json.dumps(line), flush=True)
 
 
@@ -681,6 +690,7 @@ def fwd_only_bench(args, torch, gla, gi):
             "mfma_frac": flops / (ms * 1e-3) / (peak_tf * 1e12),
             "hbm_frac": e * (3 * K + (3 if general else 2) * V) * units / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "kernels": {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}}
+    line["device"] = device_info(torch, "cuda:0")
     print(json.dumps(line), flush=True)
 
 
@@ -743,6 +753,7 @@ def general_step_bench(args, torch, gla, gi):
             "config": {"workload": "%s: B=%d H=%d T=%d dk=%d dv=%d %s, gla_fwd_general_ckpt + gla_bwd_general_ckpt "
                                    "per step" % (w.name, B, H, T, K, V, w.dtype)},
             "kernels": {k: {"launches": c, "avg_us": 1e3 * t / c} for k, (c, t) in kt.items()}}
+    line["device"] = device_info(torch, "cuda:0")
     print(json.dumps(line), flush=True)
 
 
@@ -1029,6 +1040,7 @@ def main():
         "kernels": kern,
         "roofline": roofline,
         "wall_s_timed": wall,
+        "device": device_info(torch, dev),
     }
     if not args.no_attainable:
         out["attainable"] = attainable_peaks(torch, dev)
