@@ -1,14 +1,20 @@
-// Column-slice plumbing of the wide-value paths: the backward at value width 512
-// (16-bit inputs, two slices of 256) and fp32 at value width 256 or 512 (slices
-// of 128, forward and backward).
+// Slice plumbing for heads wider than the kernels, and the small reshapes of the
+// gate forms the kernels do not take directly.
 //
 // The recurrence of Section 4.1, Eq. 3 acts on each value column of the state
-// independently: column j of S_t depends only on column j of v and of S_0.  A
-// head with V = 512 is therefore two heads with V = 256 that share q, k and g;
-// their gradients dv and dS_0 are the two halves side by side, and dq, dk and
-// dg (whose closed form of Section 4.3 is linear in the per-half terms) are the
-// sums of the two halves' values.  These kernels move the halves in and out of
-// contiguous buffers and add them.
+// independently (column j of S_t depends only on column j of v and of S_0), and
+// its diagonal gate scales each state row on its own (row i depends only on
+// column i of k and g, and o_t = q_t S_t sums over the rows).  A head with wide
+// values is therefore several heads that share q, k and g, whose dv and dS_0
+// sit side by side and whose dq, dk and dg (the closed form of Section 4.3 is
+// linear in the per-slice terms) add; a head with wide keys is several heads
+// that share v, whose outputs and dv add.  These kernels gather a slice's
+// columns into contiguous buffers and scatter them back (gla_copy_cols), add a
+// slice's result into another's (gla_add_into), pad 64-wide heads of the
+// general gate to the kernels' 128 with zero columns (gla_pad_cols), repeat a
+// scalar gate over the key columns for the fp32 path (gla_bcast_cols) and sum
+// that path's per-column gate gradient back to one value per token
+// (gla_row_sums).
 #include <hip/hip_runtime.h>
 
 #include "gla_device.hpp"
