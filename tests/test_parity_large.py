@@ -89,6 +89,9 @@ CASES = [
 
 @pytest.mark.parametrize("form,B,H,T,K,V,dtype", CASES)
 def test_past_32bit_offsets(form, B, H, T, K, V, dtype):
+    free, _ = torch.cuda.mem_get_info(0)
+    if free < 120 * 2 ** 30:
+        pytest.skip("needs about 120 GiB of free device memory (%.0f GiB free)" % (free / 2 ** 30))
     heads = [(0, 0), (B - 1, H - 1)]
     n = len(heads)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
