@@ -91,6 +91,7 @@ def test_decode_empty_is_a_no_op():
     (2, 3, 5, 64, 128, "fp32"),
     (1, 2, 70, 128, 256, "bf16"),      # longer than a chunk, not a multiple of it
     (1, 2, 4, 512, 128, "bf16"),
+    (1, 1, 3, 256, 512, "fp32"),
 ])
 def test_decode_scalar_gate_matches_oracle(B, H, T, K, V, dtype):
     # one log gate per token and head, against the oracle's scalar-gate recurrence
@@ -113,6 +114,8 @@ def test_decode_scalar_gate_matches_oracle(B, H, T, K, V, dtype):
     (2, 3, 5, 64, 128, "fp32"),
     (1, 2, 70, 128, 256, "bf16"),
     (1, 1, 3, 256, 512, "bf16"),
+    (1, 2, 4, 512, 64, "bf16"),         # 32 state rows per thread, the value gate staged per 64 columns
+    (1, 1, 3, 512, 512, "fp32"),
 ])
 def test_decode_general_gate_matches_oracle(B, H, T, K, V, dtype):
     # the outer-product gate exp(g)^T exp(h), against the oracle's general recurrence
