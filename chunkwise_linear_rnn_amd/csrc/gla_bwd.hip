@@ -131,13 +131,10 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
 #pragma unroll
         for (int ks = 0; ks < V / 32; ++ks) {
             f32x4& acc = acc2[ks & 1];
-            if (!OUT_ST) {  // D[s][t] = sum_j V[s][j] dO[t][j]
-                acc = mma32(acc, frag_rm<T>(sV, pV, 16 * js, 32 * ks), frag_rm<T>(sV, pV, 16 * js, 32 * ks + 16),
-                            frag_rm<T>(sdO, pV, 16 * is, 32 * ks), frag_rm<T>(sdO, pV, 16 * is, 32 * ks + 16));
-            } else {        // D[t][s] = sum_j dO[t][j] V[s][j]
-                acc = mma32(acc, frag_rm<T>(sdO, pV, 16 * is, 32 * ks), frag_rm<T>(sdO, pV, 16 * is, 32 * ks + 16),
-                            frag_rm<T>(sV, pV, 16 * js, 32 * ks), frag_rm<T>(sV, pV, 16 * js, 32 * ks + 16));
-            }
+            if (!OUT_ST)  // D[s][t] = sum_j V[s][j] dO[t][j]
+                acc = mma32_rr<T>(acc, sV, pV, 16 * js, sdO, pV, 16 * is, 32 * ks);
+            else          // D[t][s] = sum_j dO[t][j] V[s][j]
+                acc = mma32_rr<T>(acc, sdO, pV, 16 * is, sV, pV, 16 * js, 32 * ks);
         }
         f32x4 acc = acc2[0] + acc2[1];
         if (!OUT_ST) {

@@ -131,6 +131,25 @@ __device__ __forceinline__ bf16x4 frag_cm<bf16>(const bf16* base, int pitch, int
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// MFMA k-step with both operands in row-major LDS tiles, contracting columns
+// c0 .. c0+31 of rows ra + l%16 (A) and rb + l%16 (B).  The order in which the
+// 32 contraction indices meet the hardware's k slots is free as long as both
+// operands use the same one: 16-bit tiles hand each lane the 8 consecutive
+// columns c0 + 8*(l/16) .. +7 of each operand as one 16-byte LDS read (rows
+// must start 16-byte aligned); fp32 tiles take the paired 16-column fragments.
+template <typename T>
+__device__ __forceinline__ f32x4 mma32_rr(f32x4 acc, const T* a, int pa, int ra, const T* b, int pb, int rb, int c0) {
+    if constexpr (sizeof(T) == 2) {
+        const int l = lane_id();
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(a + (ra + (l & 15)) * pa + c0 + 8 * (l >> 4));
+        const bf16x8 y = *reinterpret_cast<const bf16x8*>(b + (rb + (l & 15)) * pb + c0 + 8 * (l >> 4));
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+    } else {
+        return mma32(acc, frag_rm<T>(a, pa, ra, c0), frag_rm<T>(a, pa, ra, c0 + 16), frag_rm<T>(b, pb, rb, c0),
+                     frag_rm<T>(b, pb, rb, c0 + 16));
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ vec4_t<T> to_vec4(f32x4 x) {
     vec4_t<T> v;
