@@ -814,6 +814,9 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
     static_assert(CPK % VEC == 0, "wave tiling");
     using Sm = RowPipeSmem<T, BK, V, NW>;
+    // 16-bit V tile in the paired column layout (its only reader is the
+    // V (gamma dS)^T product, whose k-steps pair two dS tiles)
+    constexpr bool VP = sizeof(T) == 2;
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
@@ -860,7 +863,8 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     __syncthreads();
     if (nchunks > 0) {
         row_prep<T, CPK, true>(sm.buf[0], Sm::pK, Sm::pB, rq, rg, kc0);
-        rv.store_lds(sm.Vt, Sm::pV, tid);
+        if constexpr (VP) rv.store_lds_paired(sm.Vt, Sm::pV, tid);
+        else rv.store_lds(sm.Vt, Sm::pV, tid);
         rdo.store_lds(sm.dO, Sm::pV, tid);
         if (nchunks > 1) {
             rq.load(kbase(q, chunk_of(1)), rsK, kc0);
@@ -957,12 +961,20 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 #pragma unroll
                 for (int m = 0; m < RR::NB; ++m) {
                     const int sb = RR::block(m, vs);
-                    own[m] = mma32(own[m], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks),
-                                   frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks + 16));
+                    if constexpr (VP) {
+                        own[m] = mma32_pair(own[m], s0, s1, frag_paired(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks));
+                    } else {
+                        own[m] = mma32(own[m], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks),
+                                       frag_rm<T>(sm.Vt, Sm::pV, 16 * sb, j0 + 32 * ks + 16));
+                    }
                     if (RR::VS > 1) {
                         const int sp = RR::block(m, vs ^ 1);
-                        oth[m] = mma32(oth[m], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks),
-                                       frag_rm<T>(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks + 16));
+                        if constexpr (VP) {
+                            oth[m] = mma32_pair(oth[m], s0, s1, frag_paired(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks));
+                        } else {
+                            oth[m] = mma32(oth[m], s0, s1, frag_rm<T>(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks),
+                                           frag_rm<T>(sm.Vt, Sm::pV, 16 * sp, j0 + 32 * ks + 16));
+                        }
                     }
                 }
             }
@@ -1075,7 +1087,8 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         if (exact) __syncthreads();
         if (tid == 0) cur.flag[0] = 0;  // read by every thread before the phase-1 barrier
         if (more) {
-            rv.store_lds(sm.Vt, Sm::pV, tid);
+            if constexpr (VP) rv.store_lds_paired(sm.Vt, Sm::pV, tid);
+        else rv.store_lds(sm.Vt, Sm::pV, tid);
             rdo.store_lds(sm.dO, Sm::pV, tid);
             if (it + 2 < nchunks) {
                 rv.load(vbase(v, chunk_of(it + 2)), rsV, tid);

@@ -150,6 +150,27 @@ __device__ __forceinline__ f32x4 mma32_rr(f32x4 acc, const T* a, int pa, int ra,
     }
 }
 
+// 16-bit tiles whose columns are interleaved within each 32-column block
+// ("paired" layout): column 32b + c sits at 32b + 8*((c/4)%4) + 4*(c/16) + c%4,
+// so the eight columns c0 + 4*(l/16) .. +3 and c0 + 16 + 4*(l/16) .. +3 that an
+// MFMA k-step pairs with two stacked accumulator tiles (k slots 0-3 from the
+// tile of rows c0..c0+15, 4-7 from the next) are one contiguous 16-byte read.
+__host__ __device__ constexpr int paired_col(int c) { return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3); }
+
+// (lo, hi) fragments of rows r0 + l%16 of a paired tile for k-step columns
+// c0 .. c0+31 (c0 a multiple of 32), as one 16-byte LDS read.
+__device__ __forceinline__ bf16x8 frag_paired(const bf16* base, int pitch, int r0, int c0) {
+    const int l = lane_id();
+    return *reinterpret_cast<const bf16x8*>(base + (r0 + (l & 15)) * pitch + c0 + 8 * (l >> 4));
+}
+
+// k-step of a stacked accumulator tile pair (lo: rows c0..c0+15, hi: the next
+// 16) against a paired-layout fragment read with frag_paired.
+__device__ __forceinline__ f32x4 mma32_pair(f32x4 acc, bf16x4 lo, bf16x4 hi, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), b, acc, 0,
+                                                    0, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ vec4_t<T> to_vec4(f32x4 x) {
     vec4_t<T> v;
@@ -192,6 +213,18 @@ struct TileRegs {
         for (int p = 0; p < PER; ++p)
             if (owns(p, tid))
                 *reinterpret_cast<u32x4*>(s + row_of(p, tid) * pitch + col_of(p, tid)) = r[p];
+    }
+    // 16-bit tiles: store into the paired column layout (two 8-byte halves)
+    __device__ __forceinline__ void store_lds_paired(T* s, int pitch, int tid) const {
+        static_assert(sizeof(T) == 2, "paired layout is for 16-bit tiles");
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+            if (owns(p, tid)) {
+                T* row = s + row_of(p, tid) * pitch;
+                const int c = col_of(p, tid);
+                *reinterpret_cast<uint2*>(row + paired_col(c)) = uint2{r[p][0], r[p][1]};
+                *reinterpret_cast<uint2*>(row + paired_col(c + 4)) = uint2{r[p][2], r[p][3]};
+            }
     }
     // element e (0..VEC-1) of vector p as float
     __device__ __forceinline__ float get(int p, int e) const {
