@@ -670,8 +670,10 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         // S^T <- post * (pre * S^T + V^T Kt); this lane's key column is i0 + l%16
         {
             const float pre = cur.pre[i0 + (l & 15)], post = cur.post[i0 + (l & 15)];
+            // pre is 1 in every column of a chunk inside the basis range
+            if (exact)
 #pragma unroll
-            for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= pre;
+                for (int jb = 0; jb < VW / 16; ++jb) S.s[jb] *= pre;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const vec4_t<T> x0 = frag_cm<T>(cur.K, Sm::pK, 32 * ks, i0);

@@ -548,12 +548,14 @@ gla_fwd_walk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __r
             }
             // S <- post * (pre * S + Kt^T V); slot r of tile (a, cb) is key row 16a + 4(l/16) + r
             auto update = [&]() {
+                // pre is 1 in every column of a chunk inside the basis range
+                if (exact)
 #pragma unroll
-                for (int a = 0; a < KD / 16; ++a) {
-                    const f32x4 pre = *reinterpret_cast<const f32x4*>(cur.pre + 16 * a + 4 * (l >> 4));
+                    for (int a = 0; a < KD / 16; ++a) {
+                        const f32x4 pre = *reinterpret_cast<const f32x4*>(cur.pre + 16 * a + 4 * (l >> 4));
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= pre;
-                }
+                        for (int cb = 0; cb < CB; ++cb) S.s[a][cb] *= pre;
+                    }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
