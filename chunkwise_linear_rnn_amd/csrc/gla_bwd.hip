@@ -1647,10 +1647,7 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks)
-                    acc = mma32(acc, frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks),
-                                frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks + 16),
-                                frag_rm<T>(cur.Kt, Sm::pKt, 16 * js, 32 * ks),
-                                frag_rm<T>(cur.Kt, Sm::pKt, 16 * js, 32 * ks + 16));
+                    acc = mma32_rr<T>(acc, cur.Ql, Sm::pQl, 16 * is, cur.Kt, Sm::pKt, 16 * js, 32 * ks);
                 // slot r: t = 16is + 4(l/16) + r, s = 16js + l%16
                 if (is == js) {
 #pragma unroll
