@@ -389,7 +389,10 @@ template <typename T, int BK, int V, int NW, bool WQ = false>
 struct RowPipeSmem {
     using RR = RowRoles<BK, V, NW>;
     static constexpr int PT = Elem<T>::pad;
-    static constexpr int pV = V + PT;
+    // 16-bit value and d_o rows 8 mod 32 dwords apart keep the four rows of a
+    // transposed read on disjoint banks (the dq walk that forms dS* keeps the
+    // narrower pitch: its LDS is full)
+    static constexpr int pV = V + ((sizeof(T) == 2 && !WQ) ? 16 : PT);
     static constexpr int pP = kChunk + PT;
     // column fragments only: 8 mod 64 dwords keeps a transposed read's four rows apart
     static constexpr int pK = sizeof(T) == 2 ? BK + 16 : BK + 4;
