@@ -390,8 +390,9 @@ struct RowPipeSmem {
     using RR = RowRoles<BK, V, NW>;
     static constexpr int PT = Elem<T>::pad;
     // 16-bit value and d_o rows 8 mod 32 dwords apart keep the four rows of a
-    // transposed read on disjoint banks (the dq walk that forms dS* keeps the
-    // narrower pitch: its LDS is full)
+    // transposed read on disjoint banks, but put two rows of a 16-byte row
+    // read on one bank; the dq walk that forms dS*, whose reads are mostly row
+    // reads, keeps the 4 mod 32 pitch (the wider one measured slower there)
     static constexpr int pV = V + ((sizeof(T) == 2 && !WQ) ? 16 : PT);
     static constexpr int pP = kChunk + PT;
     // column fragments only: 8 mod 64 dwords keeps a transposed read's four rows apart
