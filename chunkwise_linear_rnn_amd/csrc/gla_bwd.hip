@@ -121,7 +121,9 @@ struct RowRoles {
 // the full value width.  OUT_ST = false stores dP row-major [t][s];
 // OUT_ST = true stores dP^T row-major [s][t].
 template <typename T, int V, bool OUT_ST>
-__device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* sP, int pP, int w, int nw) {
+__device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* sP, int pP, int w, int nw,
+                                         int pO = 0) {
+    if (pO == 0) pO = pV;
     const int l = lane_id();
     for (int tile = w; tile < 10; tile += nw) {
         int is, js;  // is: t-block, js: s-block, js <= is
@@ -132,9 +134,9 @@ __device__ __forceinline__ void dp_tiles(const T* sV, const T* sdO, int pV, T* s
         for (int ks = 0; ks < V / 32; ++ks) {
             f32x4& acc = acc2[ks & 1];
             if (!OUT_ST)  // D[s][t] = sum_j V[s][j] dO[t][j]
-                acc = mma32_rr<T>(acc, sV, pV, 16 * js, sdO, pV, 16 * is, 32 * ks);
+                acc = mma32_rr<T>(acc, sV, pV, 16 * js, sdO, pO, 16 * is, 32 * ks);
             else          // D[t][s] = sum_j dO[t][j] V[s][j]
-                acc = mma32_rr<T>(acc, sdO, pV, 16 * is, sV, pV, 16 * js, 32 * ks);
+                acc = mma32_rr<T>(acc, sdO, pO, 16 * is, sV, pV, 16 * js, 32 * ks);
         }
         f32x4 acc = acc2[0] + acc2[1];
         if (!OUT_ST) {
@@ -385,15 +387,17 @@ gla_bwd_dq(const T* __restrict__ k, const T* __restrict__ v, const T* __restrict
 // double-buffered key-side slice of BK columns per chunk (the decayed operand
 // read with column fragments, the fp32 cumulative log gate, the per-column
 // state-update factors).
-template <typename T, int BK, int V, int NW, bool WQ = false>
+template <typename T, int BK, int V, int NW, bool WQ = false, bool WVT = false, bool WDO = false>
 struct RowPipeSmem {
     using RR = RowRoles<BK, V, NW>;
     static constexpr int PT = Elem<T>::pad;
-    // 16-bit value and d_o rows 8 mod 32 dwords apart keep the four rows of a
-    // transposed read on disjoint banks, but put two rows of a 16-byte row
-    // read on one bank; the dq walk that forms dS*, whose reads are mostly row
-    // reads, keeps the 4 mod 32 pitch (the wider one measured slower there)
-    static constexpr int pV = V + ((sizeof(T) == 2 && !WQ) ? 16 : PT);
+    // 16-bit rows 8 mod 32 dwords apart keep the four rows of a transposed read
+    // on disjoint banks but put two rows of a 16-byte row read on one bank; the
+    // 4 mod 32 pitch does the opposite.  The walks widen (WVT, WDO) what
+    // measured faster: the dq walk its value tile (read transposed by the state
+    // update), the dk walk both tiles.
+    static constexpr int pV = V + ((sizeof(T) == 2 && WVT) ? 16 : PT);   // value tile
+    static constexpr int pO = V + ((sizeof(T) == 2 && WDO) ? 16 : PT);   // d_o tile
     static constexpr int pP = kChunk + PT;
     // column fragments only: 8 mod 64 dwords keeps a transposed read's four rows apart
     static constexpr int pK = sizeof(T) == 2 ? BK + 16 : BK + 4;
@@ -409,7 +413,7 @@ struct RowPipeSmem {
     union {
         struct {
             alignas(16) T Vt[kChunk * pV];
-            alignas(16) T dO[kChunk * pV];
+            alignas(16) T dO[kChunk * pO];
         };
         alignas(16) float X[kChunk * BK];  // exact-path intra sums, phase 2 only
     };
@@ -559,7 +563,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
     static_assert(CPK % VEC == 0, "wave tiling");
     static_assert(!DS || BK == 64, "dS* in the dq walk: 64-row key blocks");
-    using Sm = RowPipeSmem<T, BK, V, NW, DS>;
+    using Sm = RowPipeSmem<T, BK, V, NW, DS, true, false>;
     __shared__ Sm sm;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
     const int kq = w % RR::NKQ, vs = w / RR::NKQ;
@@ -627,7 +631,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
     row_prep<T, CPK, false>(sm.buf[c_begin & 1], Sm::pK, Sm::pB, rk, rg, kc0);
     if constexpr (DS) q_prep(sm.buf[c_begin & 1], c_begin);
     rv.store_lds(sm.Vt, Sm::pV, tid);
-    rdo.store_lds(sm.dO, Sm::pV, tid);
+    rdo.store_lds(sm.dO, Sm::pO, tid);
     if (c_begin + 1 < c_end) {
         rk.load(kbase(k, c_begin + 1), rsK, kc0);
         rg.load(gbase(c_begin + 1), rsG, kc0);
@@ -645,7 +649,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         // SIMD one wave's vector work overlaps its partner's dP tiles
         const bool early = RR::VS > 1 && vs == 1;
         if (early && more) row_prep<T, CPK, false>(nxt, Sm::pK, Sm::pB, rk, rg, kc0);
-        dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW);
+        dp_tiles<T, V, false>(sm.Vt, sm.dO, Sm::pV, sm.P, Sm::pP, w, NW, Sm::pO);
         // dq^T[i][t] partial = sum_{j in slice} S^T[j][i] dO[t][j], for this
         // wave's token blocks (own, slot m = block RR::block(m, vs)) and for
         // the partner slice's (oth), which go to LDS in the partner's area
@@ -659,12 +663,12 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
 #pragma unroll
             for (int m = 0; m < RR::NB; ++m) {
                 const int tb = RR::block(m, vs);
-                own[m] = mma32(own[m], s0, s1, frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks),
-                               frag_rm<T>(sm.dO, Sm::pV, 16 * tb, j0 + 32 * ks + 16));
+                own[m] = mma32(own[m], s0, s1, frag_rm<T>(sm.dO, Sm::pO, 16 * tb, j0 + 32 * ks),
+                               frag_rm<T>(sm.dO, Sm::pO, 16 * tb, j0 + 32 * ks + 16));
                 if (RR::VS > 1) {
                     const int tp = RR::block(m, vs ^ 1);
-                    oth[m] = mma32(oth[m], s0, s1, frag_rm<T>(sm.dO, Sm::pV, 16 * tp, j0 + 32 * ks),
-                                   frag_rm<T>(sm.dO, Sm::pV, 16 * tp, j0 + 32 * ks + 16));
+                    oth[m] = mma32(oth[m], s0, s1, frag_rm<T>(sm.dO, Sm::pO, 16 * tp, j0 + 32 * ks),
+                                   frag_rm<T>(sm.dO, Sm::pO, 16 * tp, j0 + 32 * ks + 16));
                 }
             }
         }
@@ -704,8 +708,8 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
                 const vec4_t<T> x1 = frag_cm<T>(sm.Q, Sm::pK, 32 * ks + 16, i0);
 #pragma unroll
                 for (int jb = 0; jb < VW / 16; ++jb)
-                    D.s[jb] = mma32(D.s[jb], frag_cm<T>(sm.dO, Sm::pV, 32 * ks, j0 + 16 * jb),
-                                    frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
+                    D.s[jb] = mma32(D.s[jb], frag_cm<T>(sm.dO, Sm::pO, 32 * ks, j0 + 16 * jb),
+                                    frag_cm<T>(sm.dO, Sm::pO, 32 * ks + 16, j0 + 16 * jb), x0, x1);
             }
             if (l < CPK) dsg += cur.B[(kChunk - 1) * Sm::pB + kc0 + l];
             const int pos = c - c_begin;
@@ -778,7 +782,7 @@ gla_bwd_dq_pipe(const T* __restrict__ k, const T* __restrict__ v, const T* __res
         if (more) {
             if constexpr (DS) q_prep(nxt, c + 1);
             rv.store_lds(sm.Vt, Sm::pV, tid);
-            rdo.store_lds(sm.dO, Sm::pV, tid);
+            rdo.store_lds(sm.dO, Sm::pO, tid);
             if (c + 2 < c_end) {
                 rv.load(vbase(v, c + 2), rsV, tid);
                 rdo.load(vbase(d_o, c + 2), rsV, tid);
@@ -819,7 +823,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     using RR = RowRoles<BK, V, NW>;
     constexpr int VW = RR::VW, CPK = BK / NW, VEC = 16 / (int)sizeof(T);
     static_assert(CPK % VEC == 0, "wave tiling");
-    using Sm = RowPipeSmem<T, BK, V, NW>;
+    using Sm = RowPipeSmem<T, BK, V, NW, false, true, true>;
     // 16-bit V tile in the paired column layout (its only reader is the
     // V (gamma dS)^T product, whose k-steps pair two dS tiles)
     constexpr bool VP = sizeof(T) == 2;
@@ -871,7 +875,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         row_prep<T, CPK, true>(sm.buf[0], Sm::pK, Sm::pB, rq, rg, kc0);
         if constexpr (VP) rv.store_lds_paired(sm.Vt, Sm::pV, tid);
         else rv.store_lds(sm.Vt, Sm::pV, tid);
-        rdo.store_lds(sm.dO, Sm::pV, tid);
+        rdo.store_lds(sm.dO, Sm::pO, tid);
         if (nchunks > 1) {
             rq.load(kbase(q, chunk_of(1)), rsK, kc0);
             rg.load(gbase(chunk_of(1)), rsG, kc0);
@@ -1009,8 +1013,8 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             const vec4_t<T> x1 = frag_cm<T>(cur.K, Sm::pK, 32 * ks + 16, i0);
 #pragma unroll
             for (int jb = 0; jb < VW / 16; ++jb)
-                S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.dO, Sm::pV, 32 * ks, j0 + 16 * jb),
-                                frag_cm<T>(sm.dO, Sm::pV, 32 * ks + 16, j0 + 16 * jb), x0, x1);
+                S.s[jb] = mma32(S.s[jb], frag_cm<T>(sm.dO, Sm::pO, 32 * ks, j0 + 16 * jb),
+                                frag_cm<T>(sm.dO, Sm::pO, 32 * ks + 16, j0 + 16 * jb), x0, x1);
         }
         rp.store_lds(sm.P, Sm::pP, tid);
         if (more) {
@@ -1095,7 +1099,7 @@ gla_bwd_dk_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         if (more) {
             if constexpr (VP) rv.store_lds_paired(sm.Vt, Sm::pV, tid);
         else rv.store_lds(sm.Vt, Sm::pV, tid);
-            rdo.store_lds(sm.dO, Sm::pV, tid);
+            rdo.store_lds(sm.dO, Sm::pO, tid);
             if (it + 2 < nchunks) {
                 rv.load(vbase(v, chunk_of(it + 2)), rsV, tid);
                 rdo.load(vbase(d_o, chunk_of(it + 2)), rsV, tid);
@@ -1924,9 +1928,10 @@ static hipError_t launch_rows_g(const BwdLaunch& a) {
     const long seg_stride = a.P > 1 ? KV : 0;
     const long bh_stride = a.P > 1 ? (long)a.P * KV : KV;
     if constexpr (sizeof(T) == 2) {
-        static_assert(sizeof(RowPipeSmem<T, BK, V, NW>) <= 160 * 1024, "LDS budget");
+        static_assert(sizeof(RowPipeSmem<T, BK, V, NW, false, true, false>) <= 160 * 1024, "LDS budget");
+        static_assert(sizeof(RowPipeSmem<T, BK, V, NW, false, true, true>) <= 160 * 1024, "LDS budget");
         if constexpr (BK == 64) {
-            static_assert(sizeof(RowPipeSmem<T, BK, V, NW, true>) <= 160 * 1024, "LDS budget");
+            static_assert(sizeof(RowPipeSmem<T, BK, V, NW, true, true, false>) <= 160 * 1024, "LDS budget");
             if (a.ds_fused) {
                 // dS* of every half segment formed by the dq walk, then their combine
                 GLA_LAUNCH("bwd_dq_walk", (gla_bwd_dq_pipe<T, BK, V, NW, SG, true>), grid, dim3(NT), a.stream,
