@@ -142,7 +142,10 @@ struct PipeSmem {
     static constexpr int PT = Elem<T>::pad;
     static constexpr int CW = BV / NW;      // value columns per wave
     static constexpr int pQl = tile_pitch<T, KD, QL_COLS>();
-    static constexpr int pKt = tile_pitch<T, KD, false>();
+    // the forward walk reads Kt transposed in its state update: 8 mod 64 dwords
+    // keeps those reads' four rows apart at 2 KB of LDS more
+    static constexpr int pKt =
+        (!QL_COLS && sizeof(T) == 2 && KD <= 128) ? KD + 16 : tile_pitch<T, KD, false>();
     static constexpr int pA = kChunk + PT;
     static constexpr int pF = kChunk + 4;   // fp32 A of exact-path chunks
     // wave-private V slices, read with ds_read_b64_tr_b16: the four rows a
