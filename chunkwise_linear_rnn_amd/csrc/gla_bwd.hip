@@ -1542,6 +1542,9 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 const float* __restrict__ dg_part, int nkb, T* __restrict__ dg, int dsub) {
     constexpr int NT = NW * 64;
     using Sm = PipeSmem<T, KD, BV, NW, true>;  // sm.A holds A^T [s][t]; sm.Vw the d_o slices
+    // 16-bit Kt in the paired column layout: the inter-chunk product reads each
+    // k-step's key fragment as one 16-byte read against the state tile pair
+    constexpr bool KP = sizeof(T) == 2;
     constexpr int CW = Sm::CW, CB = CW / 16, CPK = KD / NW;
     constexpr int VEC = 16 / (int)sizeof(T);
     static_assert(CW % 16 == 0 && CPK % VEC == 0, "wave tiling");
@@ -1632,7 +1635,7 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     }
     __syncthreads();
     if (nchunks > 0) {
-        pipe_prep<T, CPK>(sm.buf[0], Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, NG);
+        pipe_prep<T, CPK, KP>(sm.buf[0], Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, NG);
         rdo.store_lds(dslice(0), Sm::pW, l);
         if (nchunks > 1) {
             load_slabs(chunk_of(1));
@@ -1655,7 +1658,14 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks)
-                    acc = mma32_rr<T>(acc, cur.Ql, Sm::pQl, 16 * is, cur.Kt, Sm::pKt, 16 * js, 32 * ks);
+                    if constexpr (KP)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_shufflevector(frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks),
+                                                    frag_rm<T>(cur.Ql, Sm::pQl, 16 * is, 32 * ks + 16), 0, 1, 2, 3,
+                                                    4, 5, 6, 7),
+                            frag_paired(cur.Kt, Sm::pKt, 16 * js, 32 * ks), acc, 0, 0, 0);
+                    else
+                        acc = mma32_rr<T>(acc, cur.Ql, Sm::pQl, 16 * is, cur.Kt, Sm::pKt, 16 * js, 32 * ks);
                 // slot r: t = 16is + 4(l/16) + r, s = 16js + l%16
                 if (is == js) {
 #pragma unroll
@@ -1699,19 +1709,26 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 }
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb) {
-                    const vec4_t<T> blo = frag_rm<T>(cur.Kt, Sm::pKt, 16 * sb, 32 * ks);
-                    const vec4_t<T> bhi = frag_rm<T>(cur.Kt, Sm::pKt, 16 * sb, 32 * ks + 16);
+                    if constexpr (KP) {
+                        const bf16x8 bk = frag_paired(cur.Kt, Sm::pKt, 16 * sb, 32 * ks);
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) acc[sb][cb] = mma32(acc[sb][cb], sf[cb][0], sf[cb][1], blo, bhi);
+                        for (int cb = 0; cb < CB; ++cb) acc[sb][cb] = mma32_pair(acc[sb][cb], sf[cb][0], sf[cb][1], bk);
+                    } else {
+                        const vec4_t<T> blo = frag_rm<T>(cur.Kt, Sm::pKt, 16 * sb, 32 * ks);
+                        const vec4_t<T> bhi = frag_rm<T>(cur.Kt, Sm::pKt, 16 * sb, 32 * ks + 16);
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[sb][cb] = mma32(acc[sb][cb], sf[cb][0], sf[cb][1], blo, bhi);
+                    }
                 }
             }
         };
         if (w < NW / 2) {
             inter();
             __builtin_amdgcn_sched_barrier(0);
-            if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
+            if (more) pipe_prep<T, CPK, KP>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
         } else {
-            if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
+            if (more) pipe_prep<T, CPK, KP>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, 0, MG);
             __builtin_amdgcn_sched_barrier(0);
             inter();
         }
@@ -1768,9 +1785,9 @@ gla_bwd_dv_pipe(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             if (w < NW / 2) {
                 update();
                 __builtin_amdgcn_sched_barrier(0);
-                if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
+                if (more) pipe_prep<T, CPK, KP>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
             } else {
-                if (more) pipe_prep<T, CPK>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
+                if (more) pipe_prep<T, CPK, KP>(nxt, Sm::pQl, Sm::pKt, rq, rk, rg, kc0, MG, NG);
                 __builtin_amdgcn_sched_barrier(0);
                 update();
             }

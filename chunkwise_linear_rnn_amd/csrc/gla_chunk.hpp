@@ -177,8 +177,8 @@ struct PipeSmem {
 // scans of a group's VEC columns interleave.  A scalar gate (GS::scalar) has
 // one cumulative gate per token: one scan and two exp2 per lane serve every
 // column, and the chunk needs the exact path only if that one decay leaves the
-// basis range.
-template <typename T, int NC, typename Buf, typename GS>
+// basis range.  KP (16-bit only): Kt is written in the paired column layout.
+template <typename T, int NC, bool KP = false, typename Buf, typename GS>
 __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSlab<T, NC>& rq,
                                           const RowSlab<T, NC>& rk, const GS& rg, int kc0, int m0, int m1) {
     constexpr int VEC = 16 / (int)sizeof(T);
@@ -201,7 +201,8 @@ __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSl
                 kt[e] = rk.get(j0 + e) * fk;
             }
             store_vec_lds<T>(bf.Ql + l * pQl + kc0 + j0, ql);
-            store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
+            if constexpr (KP) store_paired8(bf.Kt + l * pKt, kc0 + j0, kt);
+            else store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
         }
         if (l >= m0 * VEC && l < m1 * VEC) {
             const float gm = exp2_fast(bl);
@@ -231,7 +232,8 @@ __device__ __forceinline__ void pipe_prep(Buf& bf, int pQl, int pKt, const RowSl
                 kt[e] = rk.get(j0 + e) * exp2_fast((in ? 0.f : bl) - bt[e]);
             }
             store_vec_lds<T>(bf.Ql + l * pQl + kc0 + j0, ql);
-            store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
+            if constexpr (KP) store_paired8(bf.Kt + l * pKt, kc0 + j0, kt);
+            else store_vec_lds<T>(bf.Kt + l * pKt + kc0 + j0, kt);
         }
         if (l >= m0 * VEC && l < m1 * VEC) {
             const float gm = exp2_fast(last_l);

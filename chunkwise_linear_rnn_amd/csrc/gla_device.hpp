@@ -171,6 +171,19 @@ __device__ __forceinline__ f32x4 mma32_pair(f32x4 acc, bf16x4 lo, bf16x4 hi, bf1
                                                     0, 0);
 }
 
+// Store 8 values of logical columns c .. c+7 (c a multiple of 8) of one row of a
+// paired tile: two 8-byte halves.
+__device__ __forceinline__ void store_paired8(bf16* row, int c, const float* x) {
+    bf16x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a[e] = (bf16)x[e];
+        b[e] = (bf16)x[4 + e];
+    }
+    *reinterpret_cast<bf16x4*>(row + paired_col(c)) = a;
+    *reinterpret_cast<bf16x4*>(row + paired_col(c + 4)) = b;
+}
+
 template <typename T>
 __device__ __forceinline__ vec4_t<T> to_vec4(f32x4 x) {
     vec4_t<T> v;
